@@ -1,0 +1,183 @@
+/*
+ * gd.h -- C ABI of the MI355X (gfx950) KV-cached transformer decode library.
+ *
+ * One library, libgptdecode.so, runs the decode forward pass of a GPT-2-style
+ * decoder (LayerNorm, fused QKV with bias, causal multi-head attention against a
+ * KV cache, output projection, tanh-GELU MLP, residual adds, tied-embedding logits,
+ * greedy argmax) and of a Llama-style variant (RMSNorm, RoPE, grouped-query
+ * attention over a paged KV cache, SiLU-gated MLP, untied head). Every step of the
+ * pass runs in the library's HIP kernels; there is no CPU fallback.
+ *
+ * Sources for what is computed:
+ *   "bare-metal-llm" (GPT-2 on hand-written Metal kernels): "What got built" lists
+ *   the kernels of the pass and the KV cache; "The bug worth telling" is the GELU
+ *   overflow; "What it taught me" asks for one submission per forward pass.
+ *   "batch_forge" README: the op set (layernorm, rmsnorm, rope, gelu with the tanh
+ *   argument clamped to +-15, attention, tiled matmul) and resident weights.
+ *   "rvllm Metal backend" post: "What the kernels do" (the Llama-style layer, the
+ *   paged cache addressed as block = pos / B, slot = pos mod B, GPU argmax returning
+ *   one integer per sequence); "Memory is shared" (never read a buffer the GPU is
+ *   still writing); "Things that were problematic" (-inf masks, NaN-aware argmax,
+ *   tests must not skip when a kernel fails to load).
+ *
+ * Conventions
+ *   - Device memory is owned by the caller (e.g. PyTorch tensors). The library only
+ *     borrows the pointers given to gd_bind_memory / gd_decode_step / gd_prefill;
+ *     they must stay valid while the model uses them.
+ *   - Calls enqueue work on the model's HIP stream and return without waiting,
+ *     except gd_load_weights (waits) and gd_device_errors (waits). Read results on
+ *     the host only after synchronizing that stream.
+ *   - Errors: every call returns a gd_status; gd_last_error() gives a message for
+ *     the calling thread. A HIP failure poisons the model: every later call on it
+ *     returns GD_ERR_HIP. A model is not thread-safe.
+ *   - Activations, accumulation and the KV cache are float32. Weight matrices are
+ *     stored float32 or bfloat16 (weight_dtype); norm parameters and biases float32.
+ */
+#ifndef GD_H
+#define GD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GD_OK = 0,
+  GD_ERR_INVALID = -1,   /* bad argument, shape or token id */
+  GD_ERR_NO_DEVICE = -2, /* no HIP device, or not a gfx950 device */
+  GD_ERR_HIP = -3,       /* a HIP call or kernel launch failed; the model is poisoned */
+  GD_ERR_OOM = -4,       /* bound memory too small */
+  GD_ERR_CTX_FULL = -5,  /* a sequence has no room for another position */
+  GD_ERR_STATE = -6      /* call out of order (e.g. memory not bound, weights not loaded) */
+} gd_status;
+
+#define GD_ARCH_GPT2 0  /* LayerNorm, learned positions, tanh-GELU MLP, biases, tied head */
+#define GD_ARCH_LLAMA 1 /* RMSNorm, RoPE, GQA, SiLU-gated MLP, no biases, untied head */
+
+#define GD_WEIGHT_F32 0
+#define GD_WEIGHT_BF16 1
+
+typedef struct {
+  int32_t arch;           /* GD_ARCH_* */
+  int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab;
+  int32_t n_ctx;          /* positions per sequence (GPT-2: rows of the position table) */
+  float norm_eps;         /* LayerNorm / RMSNorm epsilon */
+  float rope_theta;       /* Llama only */
+  int32_t weight_dtype;   /* GD_WEIGHT_* */
+  int32_t max_seqs;       /* sequence slots 0 .. max_seqs-1 */
+  int32_t max_batch;      /* rows of one decode step (<= 32) */
+  int32_t kv_block_size;  /* 0: contiguous cache, n_ctx positions per slot; else paged */
+  int32_t kv_num_blocks;  /* paged: blocks in the pool */
+} gd_config;
+
+typedef struct gd_model gd_model;
+
+/* Checks the config and the device (must be gfx950) and binds `hip_stream`
+ * (a hipStream_t; NULL = the null stream). Allocates no device memory except a few
+ * bytes of HIP objects. */
+gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model** out);
+
+/* Bytes of device memory the caller must provide: packed weights, KV cache and
+ * scratch (activations, split-K partials, counters, row metadata, block tables). */
+gd_status gd_memory_requirements(const gd_model* m, size_t* weights_bytes, size_t* kv_bytes,
+                                 size_t* scratch_bytes);
+
+/* Binds caller-owned device buffers of at least the required sizes (256-byte aligned).
+ * Clears the scratch counters, the sequence lengths and (contiguous cache) installs
+ * identity block tables. */
+gd_status gd_bind_memory(gd_model* m, void* weights_dev, void* kv_dev, void* scratch_dev);
+
+/* Uploads the weights from one host float32 buffer in the canonical order:
+ *   GPT-2: wte[V][d], wpe[n_ctx][d], then per layer ln1_g[d], ln1_b[d],
+ *          w_qkv[3d][d], b_qkv[3d], w_o[d][d], b_o[d], ln2_g[d], ln2_b[d],
+ *          w_fc[ff][d], b_fc[ff], w_proj[d][ff], b_proj[d]; then lnf_g[d], lnf_b[d].
+ *   Llama: wte[V][d], then per layer rms1[d], w_q[Hq*hd][d], w_k[Hkv*hd][d],
+ *          w_v[Hkv*hd][d], w_o[d][Hq*hd], rms2[d], w_gate[ff][d], w_up[ff][d],
+ *          w_down[d][ff]; then rmsf[d], w_head[V][d].
+ * Matrices are [out][in] (y = x . W^T + b). With GD_WEIGHT_BF16 the matrices are
+ * rounded to bfloat16 (nearest, ties to even). Repacks into the device layout and
+ * waits for the copy. n_floats must equal the canonical count. */
+gd_status gd_load_weights(gd_model* m, const float* host_weights, size_t n_floats);
+
+/* Paged cache only: installs the block table of sequence slot `seq` (n entries,
+ * each in [0, kv_num_blocks)). Position p of the sequence lives in block
+ * blocks[p / kv_block_size], slot p mod kv_block_size. Capacity = n * block size. */
+gd_status gd_set_block_table(gd_model* m, int32_t seq, const int32_t* blocks_host, int32_t n);
+
+/* Empties sequence slot `seq` (length 0). */
+gd_status gd_reset_seq(gd_model* m, int32_t seq);
+
+/* Host-side length of a sequence slot (positions filled, as enqueued). */
+gd_status gd_seq_len(const gd_model* m, int32_t seq, int32_t* len);
+
+/* Runs tokens_host[0..n) of one sequence at positions len .. len+n-1 (causal within
+ * the prompt), appends their K/V, and writes the greedy argmax of the last position
+ * to *next_token_dev (device int32) and, if logits_dev is not NULL, its vocab logits
+ * (device float[vocab]). n >= 1; every id in [0, vocab). */
+gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens_host, int32_t n,
+                     int32_t* next_token_dev, float* logits_dev);
+
+/* One decode step for `batch` sequences: row b runs token tokens_dev[b] (device int32)
+ * of sequence seq_ids_host[b] at its current length, appends K/V, and writes
+ * next_tokens_dev[b] (device int32) and, if logits_dev is not NULL, logits_dev[b][vocab].
+ * seq ids must be distinct. tokens_dev may alias next_tokens_dev (greedy decode fed on
+ * the device). The step is one hipGraph launch (captured on first use for each
+ * (batch, pointers) combination). Token ids produced on the device are checked by the
+ * kernels: an out-of-range id sets a device error flag (gd_device_errors) and is
+ * replaced by 0. */
+gd_status gd_decode_step(gd_model* m, int32_t batch, const int32_t* seq_ids_host,
+                         const int32_t* tokens_dev, int32_t* next_tokens_dev, float* logits_dev);
+
+/* Waits for the stream and returns the device error flags (bit 0: token id out of
+ * range; bit 1: position beyond a sequence's capacity; bit 2: block table entry out
+ * of range), then clears them. */
+gd_status gd_device_errors(gd_model* m, int32_t* flags);
+
+/* Tuning/testing switches. GD_OPT_LINEAR_VARIANT: 0 auto (VALU GEMV for <= 4 rows,
+ * MFMA otherwise), 1 force VALU GEMV, 2 force MFMA. GD_OPT_USE_GRAPH: 1 (default)
+ * capture decode steps in hipGraphs, 0 launch kernels directly. */
+#define GD_OPT_LINEAR_VARIANT 1
+#define GD_OPT_USE_GRAPH 2
+gd_status gd_set_option(gd_model* m, int32_t option, int32_t value);
+
+void gd_destroy(gd_model* m);
+const char* gd_last_error(void);
+
+/* ------------------------------------------------------------------ op level
+ * Single kernels on caller buffers, for kernel tests and tools. All pointers are
+ * device pointers; `hip_stream` is a hipStream_t (NULL = null stream). */
+
+#define GD_NORM_NONE 0
+#define GD_NORM_LAYER 1 /* (x - mean) / sqrt(var + eps) * g + b, biased variance */
+#define GD_NORM_RMS 2   /* x / sqrt(mean(x^2) + eps) * g */
+#define GD_ACT_NONE 0
+#define GD_ACT_GELU 1   /* 0.5 u (1 + tanh(clamp(sqrt(2/pi)(u + 0.044715 u^3), -15, 15))) */
+
+/* Workspace bytes gd_linear needs for (M, N, K) with the given variant. */
+gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, size_t* bytes);
+
+/* y[m][n] = act(norm(x[m]) . W[n]^T + bias[n]) (+ resid[m][n]) for m < M, n < N.
+ * x: float [M][ldx] (K used); W: [N][K] float32 or bf16 bits (weight_dtype); bias,
+ * norm_g, norm_b: float or NULL; resid: float [M][ldr] or NULL; y: float [M][ldy].
+ * 1 <= M <= 32, N >= 1, K >= 8 and K % 8 == 0; W must be 16-byte aligned.
+ * variant: 0 auto, 1 VALU GEMV, 2 MFMA. workspace: gd_linear_workspace bytes, zeroed
+ * once before first use (the kernels leave it zeroed). */
+gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32_t weight_dtype,
+                    const float* bias, int32_t norm, const float* norm_g, const float* norm_b,
+                    float eps, int32_t act, const float* resid, int32_t ldr, float* y, int32_t ldy,
+                    int32_t M, int32_t N, int32_t K, int32_t variant, void* workspace,
+                    size_t workspace_bytes, void* hip_stream);
+
+/* Greedy argmax of each row of logits [rows][vocab] (device) into out[rows] (device
+ * int32). NaN is larger than every number (first NaN wins); ties go to the lowest
+ * index. 1 <= rows <= 32. workspace: gd_argmax_workspace bytes, zeroed once. */
+gd_status gd_argmax_workspace(int32_t rows, int32_t vocab, size_t* bytes);
+gd_status gd_argmax(const float* logits, int32_t rows, int32_t vocab, int32_t* out, void* workspace,
+                    size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

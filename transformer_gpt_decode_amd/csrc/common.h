@@ -1,0 +1,87 @@
+// common.h -- device helpers shared by the decode kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define GD_WG 256          // threads per workgroup for every kernel here (4 waves)
+#define GD_MAX_ROWS 32     // rows (sequences or prompt positions) per forward call
+#define GD_TILE_N 16       // output columns per linear tile
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Device error flag bits (mirrors gd_device_errors).
+#define GD_DERR_TOKEN 1
+#define GD_DERR_POS 2
+#define GD_DERR_BLOCK 4
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight consecutive weights starting at element k of row `row` (16-byte aligned).
+template <int WT>
+__device__ __forceinline__ void load_w8(const void* __restrict__ W, size_t row_off, int k, float w[8]) {
+  if (WT == 0) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(W) + row_off + k);
+    f32x4 a = __builtin_nontemporal_load(p);
+    f32x4 b = __builtin_nontemporal_load(p + 1);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + row_off + k);
+    u32x4 u = __builtin_nontemporal_load(p);
+    w[0] = bf16_lo(u.x); w[1] = bf16_hi(u.x);
+    w[2] = bf16_lo(u.y); w[3] = bf16_hi(u.y);
+    w[4] = bf16_lo(u.z); w[5] = bf16_hi(u.z);
+    w[6] = bf16_lo(u.w); w[7] = bf16_hi(u.w);
+  }
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64); every lane gets the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, G);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Agent-scope (whole device) atomics and fences for the last-arriver reductions.
+__device__ __forceinline__ int atomic_add_acq_rel(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_agent() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent"); }
+
+// tanh-GELU with the tanh argument clamped to [-15, 15] (tanh is +-1 in float there),
+// so that no evaluation path of tanh can overflow to Inf/Inf ("bare-metal-llm",
+// "The bug worth telling"; "batch_forge", the GELU clamp paragraph).
+__device__ __forceinline__ float gelu_clamped(float u) {
+  float a = 0.7978845608028654f * (u + 0.044715f * u * u * u);
+  a = fminf(fmaxf(a, -15.0f), 15.0f);
+  return 0.5f * u * (1.0f + tanhf(a));
+}
+
+// silu(z) = z / (1 + e^-z) ("rvllm Metal backend", "What the kernels do").
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Greedy argmax combine: NaN beats every number, the first NaN wins, ties go to the
+// lower index. Returns true if (vb, ib) should replace (va, ia).
+__device__ __forceinline__ bool am_better(float vb, int ib, float va, int ia) {
+  bool nb = vb != vb, na = va != va;
+  if (na && nb) return ib < ia;
+  if (na) return false;
+  if (nb) return true;
+  if (vb > va) return true;
+  if (vb < va) return false;
+  return ib < ia;
+}
