@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Decode throughput of the HIP KV-cached decode path on one MI355X.
+
+A step is one decode forward of the whole batch (all layers, logits and greedy
+argmax, tokens fed on the device), replayed as one hipGraph. Inputs are the seeded
+synthetic workloads of synth/ (random-init weights of the named shape, random
+prompt ids); prefill is untimed.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value        decode tokens/s of the headline workload (GPT-2 124M shape, batch 1)
+  roofline     the dominant kernel: algorithmic bytes per launch / mean launch time
+               (HIP events around every launch in a profiled eager pass)
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+  batch32      the same measurements for 32 sequences (GPT-2 124M shape, fp32)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def setup(wname: str):
+    import torch
+    import synth
+    import transformer_gpt_decode_amd as gd
+    w = synth.WORKLOADS[wname]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    kw = dict(max_seqs=w.batch, max_batch=w.batch)
+    tables = None
+    if w.kv_block:
+        tables, pool = synth.make_block_tables(w, prompts)
+        kw.update(kv_block_size=w.kv_block, kv_num_blocks=pool)
+    m = gd.Model.from_shape(w.shape, gd.WEIGHT_BF16 if w.init.bf16 else gd.WEIGHT_F32, **kw)
+    m.load_weights(W)
+    if tables is not None:
+        for b in range(w.batch):
+            m.set_block_table(b, tables[b][tables[b] >= 0])
+    dev = torch.device("cuda", 0)
+    tok = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for b, p in enumerate(prompts):
+        m.prefill(b, p, tok[b:b + 1])
+    torch.cuda.synchronize()
+    ttft = time.perf_counter() - t0
+    first = tok.clone()
+    plen = [len(p) for p in prompts]
+    return w, W, prompts, m, tok, first, plen, ttft
+
+
+def rewind(m, tok, first, plen):
+    for b, n in enumerate(plen):
+        m.truncate_seq(b, n)
+    tok.copy_(first)
+
+
+def run_steps(m, tok, first, plen, n_steps, n_decode, seq_ids):
+    """n_steps decode steps; after each full generation (n_decode steps) rewind to the prompt end."""
+    done = 0
+    while done < n_steps:
+        k = min(n_steps - done, n_decode)
+        for _ in range(k):
+            m.decode_step(seq_ids, tok, tok)
+        done += k
+        if done < n_steps:
+            rewind(m, tok, first, plen)
+
+
+def measure(wname: str, steps, warmup: int):
+    import torch
+    import transformer_gpt_decode_amd as gd
+    w, W, prompts, m, tok, first, plen, ttft = setup(wname)
+    n_decode = w.n_generate - 1
+    K = steps if steps else n_decode
+    seq_ids = list(range(w.batch))
+    # warmup (captures the graph), then rewind to the end of the prompts
+    run_steps(m, tok, first, plen, max(1, warmup), n_decode, seq_ids)
+    rewind(m, tok, first, plen)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    run_steps(m, tok, first, plen, K, n_decode, seq_ids)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_step = max(gpu_ms, wall * 1e3) / K
+    assert m.device_errors() == 0
+    # greedy tokens of the first steps after the prompt (for the oracle cross-check)
+    rewind(m, tok, first, plen)
+    hist = [first.cpu().numpy().copy()]
+    for _ in range(min(n_decode, 24)):
+        m.decode_step(seq_ids, tok, tok)
+        hist.append(tok.cpu().numpy().copy())
+    gpu_tokens = np.stack(hist, 1)
+    # profiled eager pass over one generation window: per-kernel time and bytes
+    rewind(m, tok, first, plen)
+    m.set_option(gd.OPT_PROFILE, 1)
+    m.profile_read(reset=True)
+    P = min(K, n_decode)
+    for _ in range(P):
+        m.decode_step(seq_ids, tok, tok)
+    stats = m.profile_read(reset=True)
+    m.set_option(gd.OPT_PROFILE, 0)
+    m.close()
+    torch.cuda.synchronize()
+    return dict(w=w, W=W, prompts=prompts, ms_step=ms_step, K=K, ttft=ttft, stats=stats, P=P,
+                gpu_tokens=gpu_tokens, gpu_ms=gpu_ms, wall_s=wall)
+
+
+def kernel_table(stats, P):
+    by_kernel = {}
+    for s in stats:
+        k = by_kernel.setdefault(s["kernel"], dict(kernel=s["kernel"], roles=[], launches=0, total_us=0.0, bytes=0.0))
+        k["roles"].append(s["role"])
+        k["launches"] += s["launches"]
+        k["total_us"] += s["total_us"]
+        k["bytes"] += s["bytes"]
+    rows = []
+    for k in by_kernel.values():
+        avg_us = k["total_us"] / k["launches"]
+        bpl = k["bytes"] / k["launches"]
+        rows.append(dict(kernel=k["kernel"], roles=sorted(set(k["roles"])), launches_per_step=k["launches"] / P,
+                         avg_us=round(avg_us, 3), bytes_per_launch=bpl, gbps=round(bpl / avg_us / 1e3, 1),
+                         share=0.0, _total=k["total_us"]))
+    tot = sum(r["_total"] for r in rows)
+    for r in rows:
+        r["share"] = round(r.pop("_total") / tot, 4)
+    rows.sort(key=lambda r: -r["share"])
+    step_bytes = sum(s["bytes"] for s in stats) / P
+    return rows, step_bytes, tot / P
+
+
+def roofline(rows):
+    top = rows[0]
+    ach = top["bytes_per_launch"] / (top["avg_us"] * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": top["kernel"], "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+            "bytes_per_launch": round(top["bytes_per_launch"]), "avg_launch_us": top["avg_us"]}
+
+
+def cpu_baseline(res, budget_s: float):
+    """The oracle (single-threaded C) on a bounded sample: prompt prefilled untimed, then
+    single-token decode forwards of sequence 0 until the budget is spent."""
+    import oracle
+    w, W, prompts = res["w"], res["W"], res["prompts"]
+    om = oracle.Model(w.shape, W)
+    p = prompts[0]
+    s = om.new_seq(len(p) + w.n_generate)
+    tok = -1
+    for t in p:
+        tok = s.forward(int(t))
+    toks = [tok]
+    t0 = time.perf_counter()
+    n = 0
+    while n < w.n_generate - 1 and (time.perf_counter() - t0) < budget_s:
+        tok = s.forward(toks[-1])
+        toks.append(tok)
+        n += 1
+    dt = time.perf_counter() - t0
+    g = res["gpu_tokens"][0]
+    k = min(len(g), len(toks))
+    return {"value": round(n / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name}: sequence 0, {len(p)}-id prompt prefilled untimed, then {n} single-token decode "
+                      f"forwards ({dt:.1f} s, 1 thread)",
+            "host_cpus": os.cpu_count(), "tokens_match_gpu": bool(np.array_equal(g[:k], np.array(toks[:k]))),
+            "tokens_compared": int(k)}
+
+
+def summary(res):
+    rows, step_bytes, kern_us = kernel_table(res["stats"], res["P"])
+    w = res["w"]
+    tps = w.batch / (res["ms_step"] * 1e-3)
+    step_gbps = step_bytes / (res["ms_step"] * 1e-3) / 1e9
+    return rows, dict(value=round(tps, 1), ms_per_step=round(res["ms_step"], 4), steps=res["K"],
+                      algo_bytes_per_step=round(step_bytes), step_gbps=round(step_gbps, 1),
+                      step_hbm_frac=round(step_gbps / HBM_PEAK_GBPS, 4),
+                      kernel_us_per_step=round(kern_us, 2), ttft_s=round(res["ttft"], 4))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed decode steps (default: one full generation)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2_b1")
+    ap.add_argument("--batch32", default="gpt2_b32", help="second workload reported beside ('' to skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
+              "would shard); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    log(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps or 'one generation'}")
+    res = measure(args.workload, args.steps, args.warmup)
+    rows, summ = summary(res)
+    log(f"[bench] {args.workload}: {summ['value']} tok/s, {summ['ms_per_step']} ms/step")
+    for r in rows:
+        log(f"  {r['kernel']:<28} {str(r['roles']):<40} {r['launches_per_step']:6.1f}/step {r['avg_us']:9.2f} us "
+            f"{r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
+    out = {"metric": "decode tok/s (GPT-2 124M shape, batch 1)", "value": summ["value"], "unit": "tok/s",
+           "n_gpus": 1, "steps": res["K"], "warmup": args.warmup, "ms_per_step": summ["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": res["w"].name, "batch": res["w"].batch, "prompt_len": res["w"].prompt_len[0],
+                      "n_generate": res["w"].n_generate, "shape": "GPT-2 124M (12x768, 12 heads, ff 3072, "
+                      "vocab 50257)", "weights": "f32"},
+           "roofline": roofline(rows), "step": summ, "kernels": rows}
+    if args.cpu_seconds > 0:
+        log("[bench] oracle CPU baseline ...")
+        out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
+    if args.batch32:
+        log(f"[bench] workload {args.batch32} ...")
+        r32 = measure(args.batch32, 0, args.warmup)
+        rows32, summ32 = summary(r32)
+        log(f"[bench] {args.batch32}: {summ32['value']} tok/s, {summ32['ms_per_step']} ms/step")
+        for r in rows32:
+            log(f"  {r['kernel']:<28} {str(r['roles']):<40} {r['launches_per_step']:6.1f}/step "
+                f"{r['avg_us']:9.2f} us {r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
+        out["batch32"] = dict(workload=r32["w"].name, dtype=r32["w"].weight_dtype, **summ32,
+                              roofline=roofline(rows32), kernels=rows32)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,6 +109,11 @@ gd_status gd_set_block_table(gd_model* m, int32_t seq, const int32_t* blocks_hos
 /* Empties sequence slot `seq` (length 0). */
 gd_status gd_reset_seq(gd_model* m, int32_t seq);
 
+/* Shortens sequence slot `seq` to `len` positions (0 <= len <= current length); the
+ * positions past it are dropped and later overwritten (rewind, e.g. to replay a
+ * generation from the end of its prompt). */
+gd_status gd_truncate_seq(gd_model* m, int32_t seq, int32_t len);
+
 /* Host-side length of a sequence slot (positions filled, as enqueued). */
 gd_status gd_seq_len(const gd_model* m, int32_t seq, int32_t* len);
 
@@ -140,7 +145,24 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
  * capture decode steps in hipGraphs, 0 launch kernels directly. */
 #define GD_OPT_LINEAR_VARIANT 1
 #define GD_OPT_USE_GRAPH 2
+#define GD_OPT_PROFILE 3 /* 1: launch eagerly and time every kernel with a HIP event pair */
 gd_status gd_set_option(gd_model* m, int32_t option, int32_t value);
+
+/* Per-kernel profile gathered while GD_OPT_PROFILE is on ("rvllm Metal backend",
+ * "The matmul pain story": GPU time summed per kernel). Waits for the stream. One
+ * entry per role (e.g. "linear.qkv", "attention"); `kernel` is the HIP kernel it ran;
+ * `bytes` is the algorithmic traffic of those launches (every weight, bias and norm
+ * parameter once, activations in and out, K/V of every attended position once).
+ * Fills up to `max` entries, sets *n to the number of roles, and clears the profile
+ * if reset != 0. */
+typedef struct {
+  char role[32];
+  char kernel[64];
+  int64_t launches;
+  double total_us;
+  double bytes;
+} gd_kernel_stat;
+gd_status gd_profile_read(gd_model* m, gd_kernel_stat* out, int32_t max, int32_t* n, int32_t reset);
 
 void gd_destroy(gd_model* m);
 const char* gd_last_error(void);

@@ -19,14 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libgptdecode.so")
 GD_OK, GD_ERR_INVALID, GD_ERR_NO_DEVICE, GD_ERR_HIP, GD_ERR_OOM, GD_ERR_CTX_FULL, GD_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 ARCH_GPT2, ARCH_LLAMA = 0, 1
 WEIGHT_F32, WEIGHT_BF16 = 0, 1
-OPT_LINEAR_VARIANT, OPT_USE_GRAPH = 1, 2
+OPT_LINEAR_VARIANT, OPT_USE_GRAPH, OPT_PROFILE = 1, 2, 3
 NORM_NONE, NORM_LAYER, NORM_RMS = 0, 1, 2
 ACT_NONE, ACT_GELU = 0, 1
 
 # Symbols declared in include/gd.h.
 EXPORTS = ["gd_create", "gd_memory_requirements", "gd_bind_memory", "gd_load_weights", "gd_set_block_table",
-           "gd_reset_seq", "gd_seq_len", "gd_prefill", "gd_decode_step", "gd_device_errors", "gd_set_option",
-           "gd_destroy", "gd_last_error", "gd_linear_workspace", "gd_linear", "gd_argmax_workspace", "gd_argmax"]
+           "gd_reset_seq", "gd_truncate_seq", "gd_seq_len", "gd_prefill", "gd_decode_step", "gd_device_errors",
+           "gd_set_option", "gd_profile_read", "gd_destroy", "gd_last_error", "gd_linear_workspace", "gd_linear",
+           "gd_argmax_workspace", "gd_argmax"]
 
 
 class GdError(RuntimeError):
@@ -42,6 +43,11 @@ class GdConfig(ctypes.Structure):
                 ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("weight_dtype", ctypes.c_int32),
                 ("max_seqs", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("kv_block_size", ctypes.c_int32),
                 ("kv_num_blocks", ctypes.c_int32)]
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("role", ctypes.c_char * 32), ("kernel", ctypes.c_char * 64), ("launches", ctypes.c_int64),
+                ("total_us", ctypes.c_double), ("bytes", ctypes.c_double)]
 
 
 _lib = None
@@ -65,6 +71,8 @@ def lib() -> ctypes.CDLL:
             "gd_load_weights": [_vp, _vp, ctypes.c_size_t],
             "gd_set_block_table": [_vp, _i32, _i32p, _i32],
             "gd_reset_seq": [_vp, _i32],
+            "gd_truncate_seq": [_vp, _i32, _i32],
+            "gd_profile_read": [_vp, ctypes.POINTER(KernelStat), _i32, _i32p, _i32],
             "gd_seq_len": [_vp, _i32, _i32p],
             "gd_prefill": [_vp, _i32, _i32p, _i32, _vp, _vp],
             "gd_decode_step": [_vp, _i32, _i32p, _vp, _vp, _vp],
@@ -154,6 +162,17 @@ class Model:
 
     def reset_seq(self, seq: int) -> None:
         _check(lib().gd_reset_seq(self._h, seq))
+
+    def truncate_seq(self, seq: int, length: int) -> None:
+        _check(lib().gd_truncate_seq(self._h, seq, length))
+
+    def profile_read(self, reset: bool = True):
+        """Per-kernel profile gathered with OPT_PROFILE on: list of dicts."""
+        arr = (KernelStat * 64)()
+        n = ctypes.c_int32()
+        _check(lib().gd_profile_read(self._h, arr, 64, ctypes.byref(n), 1 if reset else 0))
+        return [dict(role=a.role.decode(), kernel=a.kernel.decode(), launches=a.launches, total_us=a.total_us,
+                     bytes=a.bytes) for a in arr[:min(n.value, 64)]]
 
     def seq_len(self, seq: int) -> int:
         v = ctypes.c_int32()

@@ -1,4 +1,4 @@
-// misc.h -- step plumbing, embedding, RoPE + KV append, standalone argmax.
+// misc.h -- step plumbing, embedding, standalone argmax.
 #pragma once
 #include "common.h"
 
@@ -38,52 +38,6 @@ __global__ __launch_bounds__(GD_WG) void k_embed(const void* __restrict__ wte, c
       else v += bf16_lo(reinterpret_cast<const uint16_t*>(wpe)[(size_t)pos * d + i]);
     }
     x[(size_t)m * ldx + i] = v;
-  }
-}
-
-// RoPE on q and k (Llama style; rotate-half pairs i, i + hd/2 with a cos/sin table
-// [n_pos][hd/2] built once) and the append of k, v at (slot, position) into the cache
-// ("rvllm Metal backend", "What the kernels do": RoPE, then kv_write into the paged
-// cache at block = pos / B, slot = pos mod B).
-__global__ __launch_bounds__(GD_WG) void k_rope_append(float* qkv, int ldq, int Hq, int Hkv, int hd,
-                                                       const float* __restrict__ rope_cs, int n_rope,
-                                                       float* kc, float* vc, const int* __restrict__ table,
-                                                       int max_blocks, int block_size, int nblk,
-                                                       const int* __restrict__ row_seq,
-                                                       const int* __restrict__ row_pos, int* err) {
-  const int m = blockIdx.x;
-  const int seq = row_seq[m], pos = row_pos[m];
-  if (pos < 0) {
-    if (threadIdx.x == 0) atomicOr(err, GD_DERR_POS);
-    return;
-  }
-  float* r = qkv + (size_t)m * ldq;
-  const int half = hd / 2;
-  const int qdim = Hq * hd, kdim = Hkv * hd;
-  if (rope_cs) {
-    const float* cs = rope_cs + (size_t)min(pos, n_rope - 1) * hd;   // [cos(half) | sin(half)]
-    for (int i = threadIdx.x; i < (Hq + Hkv) * half; i += GD_WG) {
-      int h = i / half, j = i % half;
-      float* v = r + h * hd;   // q heads then k heads are contiguous
-      float a = v[j], b = v[j + half];
-      float co = cs[j], si = cs[half + j];
-      v[j] = a * co - b * si;
-      v[j + half] = a * si + b * co;
-    }
-    __syncthreads();
-  }
-  const int bi = pos / block_size;
-  int blk = (bi < max_blocks) ? table[(size_t)seq * max_blocks + bi] : -1;
-  if (blk < 0 || blk >= nblk) {
-    if (threadIdx.x == 0) atomicOr(err, GD_DERR_BLOCK);
-    return;
-  }
-  const int slot = pos - bi * block_size;
-  for (int i = threadIdx.x; i < kdim; i += GD_WG) {
-    int h = i / hd, j = i % hd;
-    size_t off = (((size_t)blk * Hkv + h) * block_size + slot) * hd + j;
-    kc[off] = r[qdim + i];
-    vc[off] = r[qdim + kdim + i];
   }
 }
 

@@ -51,63 +51,124 @@ static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int iceil(int a, int b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------- linear planning
+//
+// var 0: k_gemv, VALU dot products with the weight rows held in registers; at most
+//        GEMV_MAX_ROWS activation rows per launch (more rows run as several launches).
+// var 1: k_mfma, 16-column tiles on the fp32 matrix cores; 1..32 rows per launch.
 
 struct LinPlan {
-  int var, mt, mpad, kc, ksplit, ntw, ntiles, grid;
-  size_t lds;
+  int var;     // 0 gemv, 1 mfma
+  int nc, rw;  // gemv: 16-byte weight chunks per lane and row, weight rows per wave
+  int mt, nw;  // mfma: 16-row activation tiles, waves per workgroup
+  int rows;    // activation rows per launch
+  int grid;
+  size_t lds;  // dynamic LDS bytes (gemv)
 };
 
-static const int kLdsBudget = 48 * 1024;
+static const int kNcChoices[] = {1, 2, 3, 4, 6, 8, 12};
 
-// variant: 0 auto, 1 VALU GEMV, 2 MFMA
-static LinPlan plan_linear(int M, int N, int K, int variant) {
+// Smallest instantiated chunk count covering K (-1: K too long for the gemv kernel).
+static int gemv_nc(int K, int wt) {
+  const int ce = wt == GD_WEIGHT_F32 ? 4 : 8;
+  const int need = iceil(iceil(K, ce), 64);
+  for (int c : kNcChoices)
+    if (c >= need) return c;
+  return -1;
+}
+
+// variant: 0 auto (gemv for <= GEMV_MAX_ROWS rows), 1 gemv, 2 mfma.
+// pair: the epilogue consumes adjacent column pairs (SwiGLU, RoPE'd QKV).
+// stat_floats: per-row LDS floats the prologue needs beyond the rows themselves.
+static LinPlan plan_linear(int M, int N, int K, int wt, int variant, bool pair, int stat_floats_per_row) {
   LinPlan p;
-  p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= 4 ? 0 : 1);
-  p.mpad = p.var == 1 ? (M <= 16 ? 16 : 32) : ((M + 3) & ~3);
-  p.mt = p.var == 1 ? p.mpad / 16 : 1;
-  int kmax = (kLdsBudget / (p.mpad * 4) - 4) & ~31;
-  int K32 = (K + 31) & ~31;
-  int ks = iceil(K32, kmax);
-  int kc = (iceil(K, ks) + 31) & ~31;
-  p.ntiles = iceil(N, GD_TILE_N);
-  // spread narrow layers over more workgroups with split-K
-  while (p.ntiles * ks < 256) {
-    int kc2 = (iceil(K, ks + 1) + 31) & ~31;
-    if (kc2 < 128 || kc2 >= kc) break;
-    ks++;
-    kc = kc2;
+  memset(&p, 0, sizeof(p));
+  p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= GEMV_MAX_ROWS ? 0 : 1);
+  p.nc = gemv_nc(K, wt);
+  if (p.nc < 0) p.var = 1;
+  if (p.var == 0) {
+    p.rw = pair ? 2 : (N >= 16384 ? 4 : 1);
+    p.rows = std::min(M, GEMV_MAX_ROWS);
+    p.grid = iceil(N, 4 * p.rw);
+    const size_t xs = ((size_t)p.rows * K + 3) & ~(size_t)3;
+    p.lds = (xs + (size_t)p.rows * std::max(2, stat_floats_per_row)) * sizeof(float);
+  } else {
+    p.mt = M <= 16 ? 1 : 2;
+    p.nw = K <= 1024 ? 4 : 8;
+    p.rows = M;
+    p.grid = iceil(N, GD_TILE_N);
+    p.lds = 0;
   }
-  p.kc = kc;
-  p.ksplit = iceil(K, kc);
-  p.ntw = std::max(1, std::min(16, p.ntiles * p.ksplit / 512));
-  p.grid = iceil(p.ntiles, p.ntw) * p.ksplit;
-  p.lds = (size_t)p.mpad * (p.kc + 4) * sizeof(float);
   return p;
 }
 
-static size_t plan_part_floats(const LinPlan& p, int M) {
-  return p.ksplit > 1 ? (size_t)p.ntiles * p.ksplit * M * GD_TILE_N : 0;
+template <int WT, int NC>
+static void launch_gemv_nc(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+  if (lp.rw == 1) hipLaunchKernelGGL((k_gemv<WT, NC, 1>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
+  else if (lp.rw == 2) hipLaunchKernelGGL((k_gemv<WT, NC, 2>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
+  else hipLaunchKernelGGL((k_gemv<WT, NC, 4>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
 }
 
 template <int WT>
-static hipError_t launch_linear_wt(const LinPlan& lp, const LinearParams& prm, hipStream_t st) {
+static void launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+  switch (lp.nc) {
+    case 1: launch_gemv_nc<WT, 1>(lp, prm, st); break;
+    case 2: launch_gemv_nc<WT, 2>(lp, prm, st); break;
+    case 3: launch_gemv_nc<WT, 3>(lp, prm, st); break;
+    case 4: launch_gemv_nc<WT, 4>(lp, prm, st); break;
+    case 6: launch_gemv_nc<WT, 6>(lp, prm, st); break;
+    case 8: launch_gemv_nc<WT, 8>(lp, prm, st); break;
+    default: launch_gemv_nc<WT, 12>(lp, prm, st); break;
+  }
+}
+
+template <int WT>
+static void launch_mfma(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+  dim3 g(lp.grid);
+  if (lp.mt == 1 && lp.nw == 4) hipLaunchKernelGGL((k_mfma<WT, 1, 4>), g, dim3(64 * 4), 0, st, prm);
+  else if (lp.mt == 1) hipLaunchKernelGGL((k_mfma<WT, 1, 8>), g, dim3(64 * 8), 0, st, prm);
+  else if (lp.nw == 4) hipLaunchKernelGGL((k_mfma<WT, 2, 4>), g, dim3(64 * 4), 0, st, prm);
+  else hipLaunchKernelGGL((k_mfma<WT, 2, 8>), g, dim3(64 * 8), 0, st, prm);
+}
+
+// One launch of one plan over prm.M rows (prm.M <= lp.rows).
+static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   if (lp.var == 0) {
-    hipLaunchKernelGGL((k_linear<WT, 0, 1>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
-  } else if (lp.mt == 1) {
-    hipLaunchKernelGGL((k_linear<WT, 1, 1>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
+    if (wt == GD_WEIGHT_F32) launch_gemv<0>(lp, prm, st);
+    else launch_gemv<1>(lp, prm, st);
   } else {
-    hipLaunchKernelGGL((k_linear<WT, 1, 2>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
+    if (wt == GD_WEIGHT_F32) launch_mfma<0>(lp, prm, st);
+    else launch_mfma<1>(lp, prm, st);
   }
   return hipGetLastError();
 }
 
-static hipError_t launch_linear(int wt, const LinPlan& lp, LinearParams prm, hipStream_t st) {
-  prm.kc = lp.kc;
-  prm.ksplit = lp.ksplit;
-  prm.ntw = lp.ntw;
-  prm.ntiles = lp.ntiles;
-  prm.mpad = lp.mpad;
-  return wt == GD_WEIGHT_F32 ? launch_linear_wt<0>(lp, prm, st) : launch_linear_wt<1>(lp, prm, st);
+// Runs a linear layer over prm.M rows, as several launches of at most lp.rows rows when
+// needed (every per-row pointer advances with the row group). With EPI_ARGMAX each
+// group's per-workgroup partials are reduced into am_out[rows of the group].
+static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st, int* am_out) {
+  for (int r0 = 0; r0 < prm.M; r0 += lp.rows) {
+    LinParams p = prm;
+    p.M = std::min(lp.rows, prm.M - r0);
+    if (r0) {
+      if (p.x) p.x += (size_t)r0 * p.ldx;
+      if (p.resid) p.resid += (size_t)r0 * p.ldr;
+      if (p.y) p.y += (size_t)r0 * p.ldy;
+      if (p.logits) p.logits += (size_t)r0 * p.ldl;
+      if (p.xres) p.xres += (size_t)r0 * p.K;
+      if (p.row_tok) p.row_tok += r0;
+      if (p.row_seq) p.row_seq += r0;
+      if (p.row_pos) p.row_pos += r0;
+      if (p.apart) p.apart += (size_t)r0 * p.Hq * p.nchunk * (p.hd + 2);
+    }
+    hipError_t e = launch_linear(wt, lp, p, st);
+    if (e != hipSuccess) return e;
+    if (p.epi == EPI_ARGMAX) {
+      hipLaunchKernelGGL(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.grid, p.M,
+                         am_out + r0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------- model
@@ -137,12 +198,12 @@ struct gd_model {
 
   // derived shapes
   int qdim, kdim, qkvdim, fcN, hdim, wt;
-  int nblk, bsize, max_blocks, nchunk, att_chunk;
+  int nblk, bsize, max_blocks, nchunk;
   size_t elt;  // bytes per weight element
 
   // sizes
   size_t w_bytes = 0, kv_bytes = 0, s_bytes = 0;
-  size_t part_floats = 0, ctr_ints = 0, head_tiles = 0;
+  size_t am_parts = 0;  // argmax partials per row (workgroups of the head's widest plan)
 
   // bound memory
   char* w = nullptr;
@@ -155,7 +216,7 @@ struct gd_model {
   std::vector<LayerOff> L;
 
   // scratch offsets (bytes)
-  size_t o_x, o_qkv, o_attn, o_h, o_part, o_ctr, o_amv, o_ami, o_amc, o_apart, o_actr;
+  size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart;
   size_t o_rseq, o_rpos, o_rtok, o_pseq, o_ppos, o_ptok, o_len, o_cap, o_sids, o_table, o_err, o_rope;
 
   // host mirror
@@ -167,6 +228,14 @@ struct gd_model {
   bool staging_pending = false;
 
   std::map<GraphKey, hipGraphExec_t> graphs;
+
+  // per-kernel profiling (GD_OPT_PROFILE)
+  bool profile = false;
+  struct ProfRec { int stat; hipEvent_t a, b; double bytes; };
+  std::vector<hipEvent_t> ev_free;
+  std::vector<ProfRec> prof_pending;
+  std::vector<gd_kernel_stat> prof_stats;
+  std::vector<int> prof_T;   // attended positions per row of the launch being enqueued
 
   template <class T>
   T* sp(size_t off) const { return reinterpret_cast<T*>(s + off); }
@@ -221,8 +290,7 @@ static void layout(gd_model* m) {
     m->nblk = c.max_seqs;
     m->max_blocks = 1;
   }
-  m->att_chunk = 64;
-  m->nchunk = iceil(c.n_ctx, m->att_chunk);
+  m->nchunk = iceil(c.n_ctx, GD_ATT_CHUNK);
 
   // weights
   size_t off = 0;
@@ -254,35 +322,22 @@ static void layout(gd_model* m) {
   // KV cache: K pools for all layers, then V pools
   m->kv_bytes = 2 * (size_t)c.n_layer * m->layer_kv_floats() * sizeof(float);
 
-  // split-K partials / counters: the largest need over every linear shape and row count
-  struct Shp { int N, K; };
-  std::vector<Shp> shapes = {{m->qkvdim, c.d_model}, {c.d_model, m->qdim}, {m->fcN, c.d_model},
-                             {c.d_model, c.d_ff}, {c.vocab, c.d_model}};
-  m->part_floats = 0;
-  m->ctr_ints = 0;
-  for (auto& sh : shapes)
+  // argmax partials: the head's widest grid over both kernels
+  m->am_parts = 0;
+  for (int v = 1; v <= 2; ++v)
     for (int M = 1; M <= GD_MAX_ROWS; ++M)
-      for (int v = 1; v <= 2; ++v) {
-        LinPlan p = plan_linear(M, sh.N, sh.K, v);
-        m->part_floats = std::max(m->part_floats, plan_part_floats(p, M));
-        m->ctr_ints = std::max(m->ctr_ints, (size_t)p.ntiles);
-      }
-  m->head_tiles = iceil(c.vocab, GD_TILE_N);
+      m->am_parts = std::max(m->am_parts, (size_t)plan_linear(M, c.vocab, c.d_model, m->wt, v, false, 2).grid);
 
   // scratch
   off = 0;
   const size_t R = GD_MAX_ROWS;
   m->o_x = take(R * d * 4);
-  m->o_qkv = take(R * m->qkvdim * 4);
+  m->o_q = take(R * m->qdim * 4);
   m->o_attn = take(R * m->qdim * 4);
   m->o_h = take(R * ff * 4);
-  m->o_part = take(m->part_floats * 4);
-  m->o_ctr = take(m->ctr_ints * 4);
-  m->o_amv = take(m->head_tiles * R * 4);
-  m->o_ami = take(m->head_tiles * R * 4);
-  m->o_amc = take(4);
+  m->o_amv = take(m->am_parts * R * 4);
+  m->o_ami = take(m->am_parts * R * 4);
   m->o_apart = take(R * c.n_head * m->nchunk * (c.head_dim + 2) * 4);
-  m->o_actr = take(R * c.n_kv_head * 4);
   m->o_rseq = take(R * 4);
   m->o_rpos = take(R * 4);
   m->o_rtok = take(R * 4);
@@ -338,6 +393,8 @@ extern "C" void gd_destroy(gd_model* m) {
   if (!m) return;
   if (m->stream) (void)hipStreamSynchronize(m->stream);
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& r : m->prof_pending) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+  for (auto e : m->ev_free) (void)hipEventDestroy(e);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   if (m->staging_evt) (void)hipEventDestroy(m->staging_evt);
   if (m->staging) (void)hipHostFree(m->staging);
@@ -467,22 +524,31 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     put_vec(buf, m->o_nfg, p, d); p += d;
     put_vec(buf, m->o_nfb, p, d); p += d;
   } else {
-    const size_t hq = m->qdim, hk = m->kdim;
+    const size_t hq = m->qdim, hk = m->kdim, hd = c.head_dim, half = hd / 2;
+    // q and k rows are stored so that each RoPE pair (i, i + hd/2) of a head sits in
+    // adjacent rows (2i, 2i + 1); q.k is unchanged because both use the same order.
+    auto put_rope_rows = [&](size_t dst, const float* src, size_t heads) {
+      for (size_t h = 0; h < heads; ++h)
+        for (size_t i = 0; i < half; ++i) {
+          put_mat(m, buf, dst + ((h * hd + 2 * i) * d) * e, src + (h * hd + i) * d, d);
+          put_mat(m, buf, dst + ((h * hd + 2 * i + 1) * d) * e, src + (h * hd + half + i) * d, d);
+        }
+    };
     for (int l = 0; l < c.n_layer; ++l) {
       const LayerOff& t = m->L[l];
       put_vec(buf, t.n1g, p, d); p += d;
       // fused [w_q; w_k; w_v]
-      put_mat(m, buf, t.wqkv, p, hq * d); p += hq * d;
-      put_mat(m, buf, t.wqkv + hq * d * e, p, hk * d); p += hk * d;
+      put_rope_rows(t.wqkv, p, c.n_head); p += hq * d;
+      put_rope_rows(t.wqkv + hq * d * e, p, c.n_kv_head); p += hk * d;
       put_mat(m, buf, t.wqkv + (hq + hk) * d * e, p, hk * d); p += hk * d;
       put_mat(m, buf, t.wo, p, d * hq); p += d * hq;
       put_vec(buf, t.n2g, p, d); p += d;
-      // gate/up interleaved per 16-row tile: rows 8j..8j+7 of gate, then of up
+      // gate and up interleaved by row: row 2j = gate j, row 2j + 1 = up j
       const float* g = p;
       const float* u = p + ff * d;
-      for (size_t j = 0; j < ff / 8; ++j) {
-        put_mat(m, buf, t.wfc + (j * 16) * d * e, g + j * 8 * d, 8 * d);
-        put_mat(m, buf, t.wfc + (j * 16 + 8) * d * e, u + j * 8 * d, 8 * d);
+      for (size_t j = 0; j < ff; ++j) {
+        put_mat(m, buf, t.wfc + (2 * j) * d * e, g + j * d, d);
+        put_mat(m, buf, t.wfc + (2 * j + 1) * d * e, u + j * d, d);
       }
       p += 2 * ff * d;
       put_mat(m, buf, t.wproj, p, d * ff); p += d * ff;
@@ -530,6 +596,41 @@ extern "C" gd_status gd_reset_seq(gd_model* m, int32_t seq) {
   return GD_OK;
 }
 
+extern "C" gd_status gd_truncate_seq(gd_model* m, int32_t seq, int32_t len) {
+  if (!m) return set_err(GD_ERR_INVALID, "model is NULL");
+  if (m->poisoned) return set_err(GD_ERR_HIP, "model is poisoned by an earlier HIP error");
+  if (!m->bound) return set_err(GD_ERR_STATE, "memory not bound");
+  if (seq < 0 || seq >= m->c.max_seqs) return set_err(GD_ERR_INVALID, "seq %d out of range", seq);
+  if (len < 0 || len > m->len[seq]) return set_err(GD_ERR_INVALID, "length %d outside 0..%d", len, m->len[seq]);
+  gd_status st = staging_wait(m);
+  if (st != GD_OK) return st;
+  m->staging[0] = len;
+  HIP_TRY(m, hipMemcpyAsync(m->sp<int>(m->o_len) + seq, m->staging, 4, hipMemcpyHostToDevice, m->stream));
+  if ((st = staging_done(m)) != GD_OK) return st;
+  m->len[seq] = len;
+  return GD_OK;
+}
+
+extern "C" gd_status gd_profile_read(gd_model* m, gd_kernel_stat* out, int32_t max, int32_t* n, int32_t reset) {
+  if (!m || !n) return set_err(GD_ERR_INVALID, "NULL argument");
+  HIP_TRY(m, hipStreamSynchronize(m->stream));
+  for (auto& r : m->prof_pending) {
+    float ms = 0.f;
+    HIP_TRY(m, hipEventElapsedTime(&ms, r.a, r.b));
+    gd_kernel_stat& s = m->prof_stats[r.stat];
+    s.launches += 1;
+    s.total_us += ms * 1000.0;
+    s.bytes += r.bytes;
+    m->ev_free.push_back(r.a);
+    m->ev_free.push_back(r.b);
+  }
+  m->prof_pending.clear();
+  *n = (int)m->prof_stats.size();
+  for (int i = 0; i < std::min<int>(max, *n); ++i) out[i] = m->prof_stats[i];
+  if (reset) m->prof_stats.clear();
+  return GD_OK;
+}
+
 extern "C" gd_status gd_seq_len(const gd_model* m, int32_t seq, int32_t* len) {
   if (!m || !len) return set_err(GD_ERR_INVALID, "NULL argument");
   if (seq < 0 || seq >= m->c.max_seqs) return set_err(GD_ERR_INVALID, "seq %d out of range", seq);
@@ -544,6 +645,8 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->variant = v;
   } else if (opt == GD_OPT_USE_GRAPH) {
     m->use_graph = v != 0;
+  } else if (opt == GD_OPT_PROFILE) {
+    m->profile = v != 0;
   } else {
     return set_err(GD_ERR_INVALID, "unknown option %d", opt);
   }
@@ -565,6 +668,90 @@ extern "C" gd_status gd_device_errors(gd_model* m, int32_t* flags) {
 
 // ------------------------------------------------------ forward over rows
 
+static int prof_stat_index(gd_model* m, const char* role, const char* kernel) {
+  for (size_t i = 0; i < m->prof_stats.size(); ++i)
+    if (!strcmp(m->prof_stats[i].role, role) && !strcmp(m->prof_stats[i].kernel, kernel)) return (int)i;
+  gd_kernel_stat s;
+  memset(&s, 0, sizeof(s));
+  snprintf(s.role, sizeof(s.role), "%s", role);
+  snprintf(s.kernel, sizeof(s.kernel), "%s", kernel);
+  m->prof_stats.push_back(s);
+  return (int)m->prof_stats.size() - 1;
+}
+
+static hipEvent_t prof_event(gd_model* m) {
+  if (!m->ev_free.empty()) {
+    hipEvent_t e = m->ev_free.back();
+    m->ev_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  (void)hipEventCreate(&e);
+  return e;
+}
+
+// Brackets one launch with events when profiling; call prof_end after the launch.
+struct ProfScope {
+  gd_model* m;
+  hipStream_t st;
+  int idx = -1;
+  hipEvent_t a = nullptr;
+  double bytes;
+  ProfScope(gd_model* m_, hipStream_t st_, const char* role, const char* kernel, double b) : m(m_), st(st_), bytes(b) {
+    if (!m->profile) return;
+    idx = prof_stat_index(m, role, kernel);
+    a = prof_event(m);
+    (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (idx < 0) return;
+    hipEvent_t b = prof_event(m);
+    (void)hipEventRecord(b, st);
+    m->prof_pending.push_back({idx, a, b, bytes});
+  }
+};
+
+static const char* linear_kernel_name(int wt, const LinPlan& lp, char* buf, size_t n) {
+  const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
+  if (lp.var == 0) snprintf(buf, n, "k_gemv<%d, %d, %d>", w, lp.nc, lp.rw);
+  else snprintf(buf, n, "k_mfma<%d, %d, %d>", w, lp.mt, lp.nw);
+  return buf;
+}
+
+// Algorithmic bytes of one linear layer over p.M rows: every weight, bias and norm
+// parameter once, the activation rows in, the outputs out (and the residual read).
+static double linear_bytes(const gd_model* m, const LinParams& p) {
+  const int n_out = p.epi == EPI_SWIGLU ? p.N / 2 : (p.epi == EPI_ARGMAX ? (p.logits ? p.N : 0) : p.N);
+  double b = (double)p.N * p.K * m->elt + (double)p.M * p.K * 4 + (double)p.M * n_out * 4;
+  if (p.bias) b += (double)p.N * 4;
+  if (p.norm) b += (double)p.K * 4 * (p.nb ? 2 : 1);
+  if (p.resid) b += (double)p.M * p.N * 4;
+  return b;
+}
+
+// Launches one linear layer (profiled when enabled).
+static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, const LinParams& p, int stat_floats,
+                             int* am_out = nullptr) {
+  const bool pair = p.epi == EPI_SWIGLU || (p.epi == EPI_QKV && p.rope_cs);
+  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, pair, stat_floats);
+  char kn[64];
+  ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, kn, sizeof(kn)), m->profile ? linear_bytes(m, p) : 0);
+  return run_linear_rows(m->wt, lp, p, st, am_out);
+}
+
+// Rows handled by the gemv kernel (embedding and attention merge fused into prologues).
+static bool rows_use_gemv(const gd_model* m, int M) {
+  return m->variant == 1 || (m->variant == 0 && M <= GEMV_MAX_ROWS);
+}
+
+template <int HD, int G>
+static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a) {
+  static_assert(HD == 64 || HD == 16, "head_dim");
+  constexpr int PPG = HD == 64 ? 4 : 1;
+  static_assert(GD_WG / (HD / 4) * PPG == GD_ATT_CHUNK, "attention chunk");
+  hipLaunchKernelGGL((k_attention<HD, G, PPG>), grid, dim3(GD_WG), 0, st, a);
+}
+
 // Enqueues the forward pass of M (<= 32) rows with device-resident row metadata.
 // If head_out is not NULL, computes logits/argmax for rows [head_row, head_row + head_rows).
 static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rseq, const int* rpos,
@@ -572,104 +759,153 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rs
   const gd_config& c = m->c;
   const int d = c.d_model, ff = c.d_ff;
   float* x = m->sp<float>(m->o_x);
-  float* qkv = m->sp<float>(m->o_qkv);
+  float* q = m->sp<float>(m->o_q);
   float* attn = m->sp<float>(m->o_attn);
   float* h = m->sp<float>(m->o_h);
+  float* apart = m->sp<float>(m->o_apart);
   int* err = m->sp<int>(m->o_err);
   hipError_t e;
-  if (m->wt == GD_WEIGHT_F32)
-    hipLaunchKernelGGL(k_embed<0>, dim3(M), dim3(GD_WG), 0, st, m->w + m->o_wte,
-                       c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr, c.vocab, c.n_ctx, d, rtok,
-                       rpos, x, d, err);
-  else
-    hipLaunchKernelGGL(k_embed<1>, dim3(M), dim3(GD_WG), 0, st, m->w + m->o_wte,
-                       c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr, c.vocab, c.n_ctx, d, rtok,
-                       rpos, x, d, err);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool gemv = rows_use_gemv(m, M);
+  const bool gpt2 = c.arch == GD_ARCH_GPT2;
+  const int nrm = gpt2 ? NORM_LN : NORM_RMS;
+  const int G = c.n_head / c.n_kv_head;
+  const void* wte = m->w + m->o_wte;
+  const void* wpe = gpt2 ? (const void*)(m->w + m->o_wpe) : nullptr;
 
-  LinearParams base;
+  double kv_pos = 0;  // attended positions summed over rows (profiling only)
+  for (int t : m->prof_T) kv_pos += t;
+
+  if (!gemv) {
+    ProfScope ps(m, st, "embed", m->wt == GD_WEIGHT_F32 ? "k_embed<0>" : "k_embed<1>",
+                 (double)M * d * (m->elt * (gpt2 ? 2 : 1) + 4.0));
+    if (m->wt == GD_WEIGHT_F32)
+      hipLaunchKernelGGL(k_embed<0>, dim3(M), dim3(GD_WG), 0, st, wte, wpe, c.vocab, c.n_ctx, d, rtok, rpos, x, d,
+                         err);
+    else
+      hipLaunchKernelGGL(k_embed<1>, dim3(M), dim3(GD_WG), 0, st, wte, wpe, c.vocab, c.n_ctx, d, rtok, rpos, x, d,
+                         err);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+
+  LinParams base;
   memset(&base, 0, sizeof(base));
   base.eps = c.norm_eps;
-  base.part = m->sp<float>(m->o_part);
-  base.ctr = m->sp<int>(m->o_ctr);
-  const int nrm = c.arch == GD_ARCH_GPT2 ? 1 : 2;
-  const int G = c.n_head / c.n_kv_head;
+  base.err = err;
+  base.vocab = c.vocab;
+  base.n_pos = c.n_ctx;
+  base.hd = c.head_dim;
+  base.Hq = c.n_head;
+  base.nchunk = m->nchunk;
+  base.chunk = GD_ATT_CHUNK;
+  base.row_seq = rseq;
+  base.row_pos = rpos;
+  base.row_tok = rtok;
+  base.M = M;
+  const int att_stat = m->nchunk * c.n_head;  // attention merge weights per row (gemv O-projection)
 
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& t = m->L[l];
-    // QKV (+ pre-norm, + bias)
+    // pre-norm + QKV + bias; q to its buffer, k and v appended to the cache (RoPE first
+    // for the Llama layout); the first layer's rows come from the embedding
     {
-      LinearParams p = base;
-      p.x = x; p.ldx = d; p.w = m->w + t.wqkv;
-      p.bias = t.bqkv ? m->wf(t.bqkv) : nullptr;
+      LinParams p = base;
+      if (gemv && l == 0) {
+        p.pro = PRO_EMBED;
+        p.wte = wte; p.wpe = wpe; p.emb_bf16 = m->wt == GD_WEIGHT_BF16; p.xres = x;
+      } else {
+        p.pro = PRO_COPY;
+      }
+      p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
-      p.act = LIN_ACT_NONE; p.y = qkv; p.ldy = m->qkvdim;
-      p.M = M; p.N = m->qkvdim; p.K = d;
-      if ((e = launch_linear(m->wt, plan_linear(M, p.N, p.K, m->variant), p, st)) != hipSuccess) return e;
+      p.w = m->w + t.wqkv; p.N = m->qkvdim; p.K = d;
+      p.epi = EPI_QKV;
+      p.bias = t.bqkv ? m->wf(t.bqkv) : nullptr;
+      p.y = q; p.ldy = m->qdim;
+      p.qdim = m->qdim; p.kdim = m->kdim;
+      p.rope_cs = gpt2 ? nullptr : m->sp<float>(m->o_rope);
+      p.kc = m->kpool(l); p.vc = m->vpool(l);
+      p.table = m->sp<int>(m->o_table); p.max_blocks = m->max_blocks; p.block_size = m->bsize; p.nblk = m->nblk;
+      if ((e = run_linear(m, st, "linear.qkv", p, 2)) != hipSuccess) return e;
     }
-    // RoPE + KV append
-    hipLaunchKernelGGL(k_rope_append, dim3(M), dim3(GD_WG), 0, st, qkv, m->qkvdim, c.n_head, c.n_kv_head,
-                       c.head_dim, c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rope) : (float*)nullptr, c.n_ctx,
-                       m->kpool(l), m->vpool(l), m->sp<int>(m->o_table), m->max_blocks, m->bsize, m->nblk, rseq,
-                       rpos, err);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // attention
+    // causal attention of every row against its sequence's cache (split-context partials)
     {
       AttnParams a;
-      a.q = qkv; a.ldq = m->qkvdim; a.out = attn; a.ldo = m->qdim;
+      memset(&a, 0, sizeof(a));
+      a.q = q; a.ldq = m->qdim;
       a.kc = m->kpool(l); a.vc = m->vpool(l);
       a.table = m->sp<int>(m->o_table); a.max_blocks = m->max_blocks; a.block_size = m->bsize; a.nblk = m->nblk;
       a.Hq = c.n_head; a.Hkv = c.n_kv_head; a.row_seq = rseq; a.row_pos = rpos;
-      a.M = M; a.nchunk = m->nchunk; a.chunk = m->att_chunk;
+      a.M = M; a.nchunk = m->nchunk;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
-      a.part = m->sp<float>(m->o_apart); a.ctr = m->sp<int>(m->o_actr);
+      a.part = apart;
       dim3 grid(m->nchunk, c.n_kv_head, M);
-      if (c.head_dim == 64 && G == 1) hipLaunchKernelGGL((k_attention<64, 1>), grid, dim3(GD_WG), 0, st, a);
-      else if (c.head_dim == 64 && G == 3) hipLaunchKernelGGL((k_attention<64, 3>), grid, dim3(GD_WG), 0, st, a);
-      else if (c.head_dim == 16 && G == 1) hipLaunchKernelGGL((k_attention<16, 1>), grid, dim3(GD_WG), 0, st, a);
-      else hipLaunchKernelGGL((k_attention<16, 3>), grid, dim3(GD_WG), 0, st, a);
+      char kn[48];
+      snprintf(kn, sizeof(kn), "k_attention<%d, %d>", c.head_dim, G);
+      ProfScope ps(m, st, "attention", kn, kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4);
+      if (c.head_dim == 64 && G == 1) launch_attention<64, 1>(grid, st, a);
+      else if (c.head_dim == 64) launch_attention<64, 3>(grid, st, a);
+      else if (G == 1) launch_attention<16, 1>(grid, st, a);
+      else launch_attention<16, 3>(grid, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // output projection + bias + residual (in place on x)
+    // output projection + bias + residual (in place on x); the gemv kernel merges the
+    // attention partials in its prologue, the mfma path merges them in a kernel first
     {
-      LinearParams p = base;
-      p.x = attn; p.ldx = m->qdim; p.w = m->w + t.wo;
+      LinParams p = base;
+      if (gemv) {
+        p.pro = PRO_ATTN;
+        p.apart = apart;
+      } else {
+        ProfScope ps(m, st, "attn_merge", "k_attn_merge", (double)M * c.n_head * (c.head_dim + 2) * 4.0 * 2);
+        hipLaunchKernelGGL(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, m->nchunk,
+                           GD_ATT_CHUNK, rpos, attn, m->qdim);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        p.pro = PRO_COPY;
+        p.x = attn; p.ldx = m->qdim;
+      }
+      p.w = m->w + t.wo; p.N = d; p.K = m->qdim;
+      p.epi = EPI_PLAIN;
       p.bias = t.bo ? m->wf(t.bo) : nullptr;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
-      p.M = M; p.N = d; p.K = m->qdim;
-      if ((e = launch_linear(m->wt, plan_linear(M, p.N, p.K, m->variant), p, st)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.o", p, att_stat)) != hipSuccess) return e;
     }
-    // MLP up: GPT-2 FC + bias + GELU; Llama gate|up + SiLU gate
+    // pre-norm + MLP up: GPT-2 FC + bias + clamped tanh-GELU; Llama gate|up + SiLU gate
     {
-      LinearParams p = base;
-      p.x = x; p.ldx = d; p.w = m->w + t.wfc;
-      p.bias = t.bfc ? m->wf(t.bfc) : nullptr;
+      LinParams p = base;
+      p.pro = PRO_COPY;
+      p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n2g); p.nb = t.n2b ? m->wf(t.n2b) : nullptr;
-      p.act = c.arch == GD_ARCH_GPT2 ? LIN_ACT_GELU : LIN_ACT_SWIGLU;
+      p.w = m->w + t.wfc; p.N = m->fcN; p.K = d;
+      p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
+      p.bias = t.bfc ? m->wf(t.bfc) : nullptr;
       p.y = h; p.ldy = ff;
-      p.M = M; p.N = m->fcN; p.K = d;
-      if ((e = launch_linear(m->wt, plan_linear(M, p.N, p.K, m->variant), p, st)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.fc", p, 2)) != hipSuccess) return e;
     }
-    // MLP down + bias + residual
+    // MLP down + bias + residual (in place on x)
     {
-      LinearParams p = base;
-      p.x = h; p.ldx = ff; p.w = m->w + t.wproj;
+      LinParams p = base;
+      p.pro = PRO_COPY;
+      p.x = h; p.ldx = ff;
+      p.w = m->w + t.wproj; p.N = d; p.K = ff;
+      p.epi = EPI_PLAIN;
       p.bias = t.bproj ? m->wf(t.bproj) : nullptr;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
-      p.M = M; p.N = d; p.K = ff;
-      if ((e = launch_linear(m->wt, plan_linear(M, p.N, p.K, m->variant), p, st)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.down", p, 2)) != hipSuccess) return e;
     }
   }
   if (head_out) {
-    LinearParams p = base;
+    // final norm + logits (tied embedding or untied head) + greedy argmax partials
+    LinParams p = base;
+    p.pro = PRO_COPY;
     p.x = x + (size_t)head_row * d; p.ldx = d;
-    p.w = m->w + (c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head);
-    p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = c.arch == GD_ARCH_GPT2 ? m->wf(m->o_nfb) : nullptr;
-    p.act = LIN_ACT_ARGMAX;
-    p.M = head_rows; p.N = c.vocab; p.K = d;
-    p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami); p.am_ctr = m->sp<int>(m->o_amc);
-    p.am_out = head_out; p.logits = logits; p.ldl = c.vocab;
-    if ((e = launch_linear(m->wt, plan_linear(head_rows, p.N, p.K, m->variant), p, st)) != hipSuccess) return e;
+    p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
+    p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.N = c.vocab; p.K = d;
+    p.epi = EPI_ARGMAX;
+    p.M = head_rows;
+    p.row_seq = rseq + head_row; p.row_pos = rpos + head_row; p.row_tok = rtok + head_row;
+    p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
+    p.logits = logits; p.ldl = c.vocab;
+    if ((e = run_linear(m, st, "linear.head", p, 2, head_out)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -710,6 +946,9 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
   for (int r0 = 0; r0 < n; r0 += GD_MAX_ROWS) {
     int M = std::min(GD_MAX_ROWS, n - r0);
     bool last = r0 + M == n;
+    m->prof_T.clear();
+    if (m->profile)
+      for (int i = 0; i < M; ++i) m->prof_T.push_back(p0 + r0 + i + 1);
     hipError_t e = enqueue_rows(m, s, M, m->sp<int>(m->o_pseq) + r0, m->sp<int>(m->o_ppos) + r0,
                                 m->sp<int>(m->o_ptok) + r0, M - 1, 1, last ? next_dev : nullptr,
                                 last ? logits_dev : nullptr);
@@ -723,9 +962,11 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
 }
 
 static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, const int* tok, int* next, float* logits) {
+  ProfScope* ps = new ProfScope(m, st, "setup", "k_setup_decode", (double)B * 16);
   hipLaunchKernelGGL(k_setup_decode, dim3(1), dim3(64), 0, st, B, m->sp<int>(m->o_sids), tok, m->sp<int>(m->o_len),
                      m->sp<int>(m->o_cap), m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
                      m->sp<int>(m->o_err));
+  delete ps;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return enqueue_rows(m, st, B, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok), 0, B, next,
@@ -756,7 +997,10 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     if ((st = staging_done(m)) != GD_OK) return st;
     m->last_sids = want;
   }
-  if (m->use_graph) {
+  m->prof_T.clear();
+  if (m->profile)
+    for (int b = 0; b < B; ++b) m->prof_T.push_back(m->len[sids[b]] + 1);
+  if (m->use_graph && !m->profile) {
     GraphKey key{B, tok_dev, next_dev, logits_dev};
     auto it = m->graphs.find(key);
     if (it == m->graphs.end()) {
@@ -791,43 +1035,46 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
 
 // ---------------------------------------------------------------- op level
 
-static gd_status linear_ws(int M, int N, int K, int variant, size_t* bytes, LinPlan* out) {
+static gd_status linear_check(int M, int N, int K, int variant) {
   if (M < 1 || M > GD_MAX_ROWS || N < 1 || K < 8 || K % 8) return set_err(GD_ERR_INVALID, "bad shape M=%d N=%d K=%d", M, N, K);
   if (variant < 0 || variant > 2) return set_err(GD_ERR_INVALID, "bad variant %d", variant);
-  LinPlan p = plan_linear(M, N, K, variant);
-  if (out) *out = p;
-  *bytes = align_up(plan_part_floats(p, M) * 4, 256) + align_up((size_t)p.ntiles * 4, 256);
   return GD_OK;
 }
 
 extern "C" gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, size_t* bytes) {
   if (!bytes) return set_err(GD_ERR_INVALID, "bytes is NULL");
-  return linear_ws(M, N, K, variant, bytes, nullptr);
+  gd_status st = linear_check(M, N, K, variant);
+  if (st != GD_OK) return st;
+  *bytes = 0;  // both kernels reduce inside a workgroup: no cross-workgroup scratch
+  return GD_OK;
 }
 
 extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32_t wdt, const float* bias,
                                int32_t norm, const float* ng, const float* nb, float eps, int32_t act,
                                const float* resid, int32_t ldr, float* y, int32_t ldy, int32_t M, int32_t N, int32_t K,
                                int32_t variant, void* ws, size_t ws_bytes, void* stream) {
-  size_t need;
-  LinPlan lp;
-  gd_status st = linear_ws(M, N, K, variant, &need, &lp);
+  (void)ws;
+  (void)ws_bytes;
+  gd_status st = linear_check(M, N, K, variant);
   if (st != GD_OK) return st;
   if (!x || !W || !y) return set_err(GD_ERR_INVALID, "NULL argument");
   if (wdt != GD_WEIGHT_F32 && wdt != GD_WEIGHT_BF16) return set_err(GD_ERR_INVALID, "bad weight dtype");
   if (norm < 0 || norm > 2 || (norm && !ng) || (norm == 1 && !nb)) return set_err(GD_ERR_INVALID, "bad norm");
+  if (norm && !(eps > 0.f)) return set_err(GD_ERR_INVALID, "eps must be > 0");
   if (act != GD_ACT_NONE && act != GD_ACT_GELU) return set_err(GD_ERR_INVALID, "bad act");
   if (ldx < K || ldx % 4 || ldy < N || (resid && ldr < N)) return set_err(GD_ERR_INVALID, "bad leading dimensions");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(W)) & 15)
     return set_err(GD_ERR_INVALID, "x and W must be 16-byte aligned");
-  if (ws_bytes < need || (need && !ws)) return set_err(GD_ERR_OOM, "workspace %zu < %zu bytes", ws_bytes, need);
-  LinearParams p;
+  LinParams p;
   memset(&p, 0, sizeof(p));
-  p.x = x; p.ldx = ldx; p.w = W; p.bias = bias; p.norm = norm; p.ng = ng; p.nb = nb; p.eps = eps;
-  p.act = act; p.resid = resid; p.ldr = ldr; p.y = y; p.ldy = ldy; p.M = M; p.N = N; p.K = K;
-  p.part = static_cast<float*>(ws);
-  p.ctr = reinterpret_cast<int*>(static_cast<char*>(ws) + align_up(plan_part_floats(lp, M) * 4, 256));
-  hipError_t e = launch_linear(wdt, lp, p, reinterpret_cast<hipStream_t>(stream));
+  p.pro = PRO_COPY;
+  p.norm = norm == GD_NORM_LAYER ? NORM_LN : norm == GD_NORM_RMS ? NORM_RMS : NORM_NONE;
+  p.x = x; p.ldx = ldx; p.ng = ng; p.nb = nb; p.eps = eps;
+  p.w = W; p.M = M; p.N = N; p.K = K;
+  p.epi = act == GD_ACT_GELU ? EPI_GELU : EPI_PLAIN;
+  p.bias = bias; p.resid = resid; p.ldr = ldr; p.y = y; p.ldy = ldy;
+  LinPlan lp = plan_linear(M, N, K, wdt, variant, false, 2);
+  hipError_t e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
   return GD_OK;
 }
