@@ -3,101 +3,133 @@
 // Each row attends to every cached position of its sequence up to and including its
 // own ("bare-metal-llm", "What got built": KV-cached causal attention; "rvllm Metal
 // backend", "What the kernels do": scores Q K^T, mask, softmax, probs V). Positions
-// past the row are never read, so no -inf mask is materialised. The cache is read
-// straight from its blocks: position p of a sequence is block table[p / B], slot
-// p mod B (the paged layout of the same post; a contiguous cache is one block per
-// sequence slot). Query heads h use KV head h / (Hq / Hkv) (grouped-query attention).
+// past the row are never read, so no -inf mask is materialised. Position p of a
+// sequence lives in cache block table[p / B], slot p mod B (the paged layout of the
+// same post); a contiguous cache is one block per sequence slot, addressed directly
+// from the row's slot offset. Query heads h use KV head h / (Hq / Hkv)
+// (grouped-query attention).
 //
-// Decomposition (split context): one workgroup per (row, KV head, chunk of CH
-// positions). Groups of HD/4 lanes take PPG positions each, with every K and V load
-// of the group issued before any arithmetic (float4 per lane). Each group reduces
-// its scores with a max-subtracted softmax; the groups are merged in LDS into one
-// partial (max, sum, weighted V) per query head and chunk. The consumer merges the
-// chunks (the O-projection prologue for few rows, or k_attn_merge).
+// Decomposition (split context): one workgroup per (row, KV head, chunk). A row's
+// T = pos + 1 positions are cut into GD_ATT_NCH chunks of ceil(T / GD_ATT_NCH)
+// positions, so the number of partials per row is fixed and their consumer can load
+// all of them without first reading the row's position. Inside a chunk, groups of
+// HD/4 lanes take one position per step (float4 of K and V per lane, all loads of a
+// step issued before the arithmetic) with an online max-subtracted softmax; the
+// groups are merged in LDS into one partial (max, sum, weighted V) per query head.
+// Empty chunks (T < GD_ATT_NCH) write max = -inf, sum = 0.
 #pragma once
 #include "common.h"
 
 struct AttnParams {
-  const float* q; int ldq;          // [M][ldq]; query head h at h*HD (post-RoPE)
-  const float* kc; const float* vc; // this layer's pools [nblk][Hkv][B][HD]
-  const int* table; int max_blocks; // [slots][max_blocks]
+  const float* q; int ldq;            // [M][ldq]; query head h at h*HD (post-RoPE)
+  const float* kc; const float* vc;   // this layer's pools [nblk][Hkv][B][HD]
+  const int* table; int max_blocks;   // [slots][max_blocks] (paged)
   int block_size, nblk;
   int Hq, Hkv;
   const int* row_seq; const int* row_pos;
-  int M, nchunk;
+  const long long* row_kvoff;         // contiguous: the row's own slot offset
+  int M;
   float scale;
-  float* part;                      // [M][Hq][nchunk][HD + 2]: max, sum, o[HD]
+  float* part;                        // [M][Hq][GD_ATT_NCH][HD + 2]: max, sum, o[HD]
 };
 
-template <int HD, int G, int PPG>
+template <int HD, int G, int PPG, bool PAGED>
 __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
   constexpr int LG = HD / 4;            // lanes per position group
   constexpr int NG = GD_WG / LG;        // position groups per workgroup
-  constexpr int CH = NG * PPG;          // positions per workgroup
+  constexpr int STEP = NG * PPG;        // positions per step
   __shared__ float s_m[NG][G], s_l[NG][G];
   __shared__ __align__(16) float s_o[NG][G][HD];
 
   const int c = blockIdx.x, kh = blockIdx.y, row = blockIdx.z;
   const int tid = threadIdx.x;
   const int grp = tid / LG, gl = tid % LG;
-  const int seq = p.row_seq[row];
-  const int T = p.row_pos[row] + 1;
-  const int nch = (T + CH - 1) / CH;
-  if (c >= nch) return;
-  const int p0 = c * CH, p1 = min(T, p0 + CH);
-  const int* tab = p.table + (size_t)seq * p.max_blocks;
+  const int pos = p.row_pos[row];
+  const int T = pos + 1;
+  const int L = (T + GD_ATT_NCH - 1) / GD_ATT_NCH;
+  const int p0 = min(T, c * L), p1 = min(T, p0 + L);
 
-  f32x4 kv[PPG], vv[PPG];
-  bool ok[PPG];
-#pragma unroll
-  for (int j = 0; j < PPG; ++j) {
-    const int pos = p0 + grp + NG * j;
-    ok[j] = false;
-    kv[j] = vv[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    if (pos < p1) {
-      const int bi = pos / p.block_size;
-      const int blk = tab[bi];
-      if ((unsigned)blk < (unsigned)p.nblk) {
-        const size_t off = (((size_t)blk * p.Hkv + kh) * p.block_size + (pos - bi * p.block_size)) * HD + gl * 4;
-        kv[j] = *reinterpret_cast<const f32x4*>(p.kc + off);
-        vv[j] = *reinterpret_cast<const f32x4*>(p.vc + off);
-        ok[j] = true;
-      }
-    }
-  }
   f32x4 q[G];
 #pragma unroll
   for (int g = 0; g < G; ++g)
     q[g] = *reinterpret_cast<const f32x4*>(p.q + (size_t)row * p.ldq + (kh * G + g) * HD + gl * 4);
+  const float* kbase = nullptr;
+  const float* vbase = nullptr;
+  const int* tab = nullptr;
+  if (PAGED) {
+    tab = p.table + (size_t)p.row_seq[row] * p.max_blocks;
+  } else {
+    const long long base = p.row_kvoff[row] - (long long)pos * HD + (long long)kh * p.block_size * HD;
+    kbase = p.kc + base + gl * 4;
+    vbase = p.vc + base + gl * 4;
+  }
 
+  float mx[G], l[G];
+  f32x4 o[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float s[PPG];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < PPG; ++j) {
-      float d = q[g].x * kv[j].x;
-      d = fmaf(q[g].y, kv[j].y, d);
-      d = fmaf(q[g].z, kv[j].z, d);
-      d = fmaf(q[g].w, kv[j].w, d);
-      s[j] = group_sum<LG>(d) * p.scale;
-      if (ok[j]) mx = fmaxf(mx, s[j]);
-    }
-    float l = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < G; ++g) { mx[g] = -INFINITY; l[g] = 0.f; o[g] = (f32x4){0.f, 0.f, 0.f, 0.f}; }
+
+  for (int s0 = p0; s0 < p1; s0 += STEP) {
+    f32x4 kv[PPG], vv[PPG];
+    bool ok[PPG];
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
-      if (ok[j]) {
-        const float e = expf(s[j] - mx);
-        l += e;
-        o.x = fmaf(e, vv[j].x, o.x);
-        o.y = fmaf(e, vv[j].y, o.y);
-        o.z = fmaf(e, vv[j].z, o.z);
-        o.w = fmaf(e, vv[j].w, o.w);
+      const int ps = s0 + grp + NG * j;
+      ok[j] = false;
+      kv[j] = vv[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (ps < p1) {
+        if (PAGED) {
+          const int bi = ps / p.block_size;
+          const int blk = tab[bi];
+          if ((unsigned)blk < (unsigned)p.nblk) {
+            const size_t off = (((size_t)blk * p.Hkv + kh) * p.block_size + (ps - bi * p.block_size)) * HD + gl * 4;
+            kv[j] = *reinterpret_cast<const f32x4*>(p.kc + off);
+            vv[j] = *reinterpret_cast<const f32x4*>(p.vc + off);
+            ok[j] = true;
+          }
+        } else {
+          kv[j] = *reinterpret_cast<const f32x4*>(kbase + (size_t)ps * HD);
+          vv[j] = *reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
+          ok[j] = true;
+        }
       }
     }
-    if (gl == 0) { s_m[grp][g] = mx; s_l[grp][g] = l; }
-    *reinterpret_cast<f32x4*>(&s_o[grp][g][gl * 4]) = o;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float s[PPG];
+      float smax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < PPG; ++j) {
+        float d = q[g].x * kv[j].x;
+        d = fmaf(q[g].y, kv[j].y, d);
+        d = fmaf(q[g].z, kv[j].z, d);
+        d = fmaf(q[g].w, kv[j].w, d);
+        s[j] = group_sum<LG>(d) * p.scale;
+        if (ok[j]) smax = fmaxf(smax, s[j]);
+      }
+      if (smax == -INFINITY) continue;   // this group saw no position in this step
+      const float nm = fmaxf(mx[g], smax);
+      const float sc = expf(mx[g] - nm);
+      l[g] *= sc;
+      o[g].x *= sc; o[g].y *= sc; o[g].z *= sc; o[g].w *= sc;
+#pragma unroll
+      for (int j = 0; j < PPG; ++j) {
+        if (ok[j]) {
+          const float e = expf(s[j] - nm);
+          l[g] += e;
+          o[g].x = fmaf(e, vv[j].x, o[g].x);
+          o[g].y = fmaf(e, vv[j].y, o[g].y);
+          o[g].z = fmaf(e, vv[j].z, o[g].z);
+          o[g].w = fmaf(e, vv[j].w, o[g].w);
+        }
+      }
+      mx[g] = nm;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (gl == 0) { s_m[grp][g] = mx[g]; s_l[grp][g] = l[g]; }
+    *reinterpret_cast<f32x4*>(&s_o[grp][g][gl * 4]) = o[g];
   }
   __syncthreads();
   // merge the NG groups into the chunk's partial: one thread per (query head g, dim d)
@@ -105,36 +137,52 @@ __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
     const int g = tid / HD, d = tid % HD;
     float m = -INFINITY;
     for (int i = 0; i < NG; ++i) m = fmaxf(m, s_m[i][g]);
-    float l = 0.f, acc = 0.f;
-    for (int i = 0; i < NG; ++i) {
-      if (s_l[i][g] == 0.f) continue;   // group saw no position
-      const float w = expf(s_m[i][g] - m);
-      l = fmaf(s_l[i][g], w, l);
-      acc = fmaf(s_o[i][g][d], w, acc);
+    float ls = 0.f, acc = 0.f;
+    if (m != -INFINITY) {
+      for (int i = 0; i < NG; ++i) {
+        if (s_l[i][g] == 0.f) continue;   // group saw no position
+        const float w = expf(s_m[i][g] - m);
+        ls = fmaf(s_l[i][g], w, ls);
+        acc = fmaf(s_o[i][g][d], w, acc);
+      }
     }
-    float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * p.nchunk + c) * (HD + 2);
+    float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * GD_ATT_NCH + c) * (HD + 2);
     pp[2 + d] = acc;
-    if (d == 0) { pp[0] = m; pp[1] = l; }
+    if (d == 0) { pp[0] = m; pp[1] = ls; }
   }
 }
 
-// Merge of the chunk partials into o[M][Hq*HD] (rows with more than 4 per call).
-__global__ __launch_bounds__(GD_WG) void k_attn_merge(const float* __restrict__ part, int Hq, int hd, int nchunk,
-                                                      int chunk, const int* __restrict__ row_pos, float* out,
+// Merge of the chunk partials of one (row, query head, dim) into o. Chunk 0 always
+// holds at least one position, so the maximum is finite; empty chunks (max = -inf,
+// sum 0, o 0) get weight exp(-inf) = 0. All loads are issued before any arithmetic.
+__device__ __forceinline__ float attn_merge_one(const float* __restrict__ pp, int hd, int d) {
+  const int stride = hd + 2;
+  float mc[GD_ATT_NCH], lc[GD_ATT_NCH], oc[GD_ATT_NCH];
+#pragma unroll
+  for (int c = 0; c < GD_ATT_NCH; ++c) {
+    mc[c] = pp[(size_t)c * stride];
+    lc[c] = pp[(size_t)c * stride + 1];
+    oc[c] = pp[(size_t)c * stride + 2 + d];
+  }
+  float mx = mc[0];
+#pragma unroll
+  for (int c = 1; c < GD_ATT_NCH; ++c) mx = fmaxf(mx, mc[c]);
+  float l = 0.f, o = 0.f;
+#pragma unroll
+  for (int c = 0; c < GD_ATT_NCH; ++c) {
+    const float w = expf(mc[c] - mx);
+    l = fmaf(lc[c], w, l);
+    o = fmaf(oc[c], w, o);
+  }
+  return o / l;
+}
+
+// Merge of the chunk partials into o[M][Hq*HD] (rows handled by the MFMA kernel).
+__global__ __launch_bounds__(GD_WG) void k_attn_merge(const float* __restrict__ part, int Hq, int hd, float* out,
                                                       int ldo) {
   const int m = blockIdx.x;
-  const int nch = (row_pos[m] + chunk) / chunk;
   for (int i = threadIdx.x; i < Hq * hd; i += GD_WG) {
     const int h = i / hd, d = i - h * hd;
-    const float* pp = part + ((size_t)m * Hq + h) * nchunk * (hd + 2);
-    float mx = -INFINITY;
-    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, pp[(size_t)c * (hd + 2)]);
-    float l = 0.f, o = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float w = expf(pp[(size_t)c * (hd + 2)] - mx);
-      l = fmaf(pp[(size_t)c * (hd + 2) + 1], w, l);
-      o = fmaf(pp[(size_t)c * (hd + 2) + 2 + d], w, o);
-    }
-    out[(size_t)m * ldo + i] = o / l;
+    out[(size_t)m * ldo + i] = attn_merge_one(part + ((size_t)m * Hq + h) * GD_ATT_NCH * (hd + 2), hd, d);
   }
 }

@@ -6,7 +6,7 @@
 #define GD_WG 256          // threads per workgroup for every kernel here (4 waves)
 #define GD_MAX_ROWS 32     // rows (sequences or prompt positions) per forward call
 #define GD_TILE_N 16       // output columns per linear tile
-#define GD_ATT_CHUNK 64    // cached positions per attention workgroup (split context)
+#define GD_ATT_NCH 8       // context chunks (attention workgroups) per row and KV head
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -2,43 +2,81 @@
 #pragma once
 #include "common.h"
 
-// Decode step set-up, on the device so the step can be replayed as one graph:
-// row b runs slot seq_ids[b] at its current length, which is then advanced.
-__global__ void k_setup_decode(int B, const int* __restrict__ seq_ids, const int* __restrict__ tokens,
-                               int* len, const int* __restrict__ cap, int* row_seq, int* row_pos,
-                               int* row_tok, int* err) {
-  int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  int s = seq_ids[b];
-  int pos = len[s];
-  if (pos >= cap[s]) { atomicOr(err, GD_DERR_POS); pos = cap[s] - 1; }
-  row_seq[b] = s;
-  row_pos[b] = pos;
-  row_tok[b] = tokens[b];
-  len[s] = pos + 1;
+// Per-row metadata and input embedding shared by decode and prefill.
+struct RowParams {
+  const int* table; int max_blocks, block_size, nblk, Hkv, hd;  // KV cache addressing
+  const void* wte; const void* wpe; int vocab, n_pos, d, emb_bf16;
+  float* x;                                                      // [rows][d]
+  int* row_seq; int* row_pos; int* row_tok; long long* row_kvoff;
+  const float* rope; float* row_cs;   // RoPE table [n_pos][hd] (cos | sin) and each row's copy
+  int* err;
+};
+
+// Element offset of (sequence, position)'s K/V slot inside one layer pool, or -1
+// (position p lives in block table[p / B], slot p mod B: "rvllm Metal backend",
+// "What the kernels do", paged KV cache).
+__device__ __forceinline__ long long kv_slot_offset(const RowParams& r, int seq, int pos) {
+  if (pos < 0) return -1;
+  const int bi = pos / r.block_size;
+  const int blk = bi < r.max_blocks ? r.table[(size_t)seq * r.max_blocks + bi] : -1;
+  if ((unsigned)blk >= (unsigned)r.nblk) return -1;
+  return ((long long)blk * r.Hkv * r.block_size + (pos - bi * r.block_size)) * r.hd;
 }
 
-// x = wte[t] (+ wpe[p]) -- token embedding and learned positions ("bare-metal-llm",
-// "Picking the model" and "What got built": embedding lookup).
-template <int WT>
-__global__ __launch_bounds__(GD_WG) void k_embed(const void* __restrict__ wte, const void* __restrict__ wpe,
-                                                 int vocab, int n_pos, int d, const int* __restrict__ row_tok,
-                                                 const int* __restrict__ row_pos, float* x, int ldx, int* err) {
-  const int m = blockIdx.x;
-  int t = row_tok[m];
-  if (t < 0 || t >= vocab) { if (threadIdx.x == 0) atomicOr(err, GD_DERR_TOKEN); t = 0; }
-  int pos = row_pos[m];
-  if (wpe && (pos < 0 || pos >= n_pos)) { if (threadIdx.x == 0) atomicOr(err, GD_DERR_POS); pos = 0; }
-  for (int i = threadIdx.x; i < d; i += GD_WG) {
-    float v;
-    if (WT == 0) v = reinterpret_cast<const float*>(wte)[(size_t)t * d + i];
-    else v = bf16_lo(reinterpret_cast<const uint16_t*>(wte)[(size_t)t * d + i]);
-    if (wpe) {
-      if (WT == 0) v += reinterpret_cast<const float*>(wpe)[(size_t)pos * d + i];
-      else v += bf16_lo(reinterpret_cast<const uint16_t*>(wpe)[(size_t)pos * d + i]);
-    }
-    x[(size_t)m * ldx + i] = v;
+// Row b's embedding x_b = wte[t] (+ wpe[p]) ("bare-metal-llm", "Picking the model" and
+// "What got built": token and learned position embeddings) and its cache slot.
+// Called by the whole workgroup with the row's sequence, position and token.
+__device__ void row_setup(const RowParams& r, int b, int seq, int pos, int tok) {
+  if (tok < 0 || tok >= r.vocab) { if (threadIdx.x == 0) atomicOr(r.err, GD_DERR_TOKEN); tok = 0; }
+  int ppos = pos;
+  if (r.wpe && (ppos < 0 || ppos >= r.n_pos)) { if (threadIdx.x == 0) atomicOr(r.err, GD_DERR_POS); ppos = 0; }
+  if (threadIdx.x == 0) {
+    const long long off = kv_slot_offset(r, seq, pos);
+    if (off < 0) atomicOr(r.err, GD_DERR_BLOCK);
+    r.row_kvoff[b] = off;
   }
+  for (int i = threadIdx.x; i < r.d; i += GD_WG) {
+    float v;
+    if (!r.emb_bf16) v = reinterpret_cast<const float*>(r.wte)[(size_t)tok * r.d + i];
+    else v = bf16_lo(reinterpret_cast<const uint16_t*>(r.wte)[(size_t)tok * r.d + i]);
+    if (r.wpe) {
+      if (!r.emb_bf16) v += reinterpret_cast<const float*>(r.wpe)[(size_t)ppos * r.d + i];
+      else v += bf16_lo(reinterpret_cast<const uint16_t*>(r.wpe)[(size_t)ppos * r.d + i]);
+    }
+    r.x[(size_t)b * r.d + i] = v;
+  }
+  if (r.rope) {
+    const int rp = min(max(pos, 0), r.n_pos - 1);
+    for (int i = threadIdx.x; i < r.hd; i += GD_WG) r.row_cs[(size_t)b * r.hd + i] = r.rope[(size_t)rp * r.hd + i];
+  }
+}
+
+// Decode step set-up, on the device so the step replays as one graph: row b runs
+// slot seq_ids[b] at its current length, which is then advanced. One workgroup per row.
+__global__ __launch_bounds__(GD_WG) void k_setup_decode(RowParams r, const int* __restrict__ seq_ids,
+                                                        const int* __restrict__ tokens, int* len,
+                                                        const int* __restrict__ cap) {
+  __shared__ int s_pos, s_tok, s_seq;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int s = seq_ids[b];
+    int pos = len[s];
+    if (pos >= cap[s]) { atomicOr(r.err, GD_DERR_POS); pos = cap[s] - 1; }
+    const int tok = tokens[b];
+    r.row_seq[b] = s;
+    r.row_pos[b] = pos;
+    r.row_tok[b] = tok;
+    len[s] = pos + 1;
+    s_pos = pos; s_tok = tok; s_seq = s;
+  }
+  __syncthreads();
+  row_setup(r, b, s_seq, s_pos, s_tok);
+}
+
+// Prefill set-up of rows whose (sequence, position, token) the host has uploaded.
+__global__ __launch_bounds__(GD_WG) void k_setup_rows(RowParams r) {
+  const int b = blockIdx.x;
+  row_setup(r, b, r.row_seq[b], r.row_pos[b], r.row_tok[b]);
 }
 
 // Standalone greedy argmax over rows of logits: per (row, chunk of 4096) partials,

@@ -77,21 +77,31 @@ static int gemv_nc(int K, int wt) {
 }
 
 // variant: 0 auto (gemv for <= GEMV_MAX_ROWS rows), 1 gemv, 2 mfma.
-// pair: the epilogue consumes adjacent column pairs (SwiGLU, RoPE'd QKV).
-// stat_floats: per-row LDS floats the prologue needs beyond the rows themselves.
-static LinPlan plan_linear(int M, int N, int K, int wt, int variant, bool pair, int stat_floats_per_row) {
+// norm: the prologue normalizes the rows (LDS for statistics, gain and shift).
+static int gemv_rows_per_wave(int epi, int N) {
+  if (epi == EPI_SWIGLU || epi == EPI_QKV_ROPE) return 2;   // both rows of a pair in one wave
+  if (epi == EPI_ARGMAX && N >= 16384) return 4;
+  return 1;
+}
+
+static const size_t kGemvLdsMax = 64 * 1024;
+
+static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bool norm) {
   LinPlan p;
   memset(&p, 0, sizeof(p));
   p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= GEMV_MAX_ROWS ? 0 : 1);
   p.nc = gemv_nc(K, wt);
   if (p.nc < 0) p.var = 1;
   if (p.var == 0) {
-    p.rw = pair ? 2 : (N >= 16384 ? 4 : 1);
+    p.rw = gemv_rows_per_wave(epi, N);
     p.rows = std::min(M, GEMV_MAX_ROWS);
     p.grid = iceil(N, 4 * p.rw);
+    // rows, then the norm's gain and shift
     const size_t xs = ((size_t)p.rows * K + 3) & ~(size_t)3;
-    p.lds = (xs + (size_t)p.rows * std::max(2, stat_floats_per_row)) * sizeof(float);
-  } else {
+    p.lds = (xs + (norm ? 2 * (size_t)K : 0)) * sizeof(float);
+    if (p.lds > kGemvLdsMax) p.var = 1;   // rows too long to stage: matrix-core path
+  }
+  if (p.var == 1) {
     p.mt = M <= 16 ? 1 : 2;
     p.nw = K <= 1024 ? 4 : 8;
     p.rows = M;
@@ -103,9 +113,18 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, bool pair, 
 
 template <int WT, int NC>
 static void launch_gemv_nc(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
-  if (lp.rw == 1) hipLaunchKernelGGL((k_gemv<WT, NC, 1>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
-  else if (lp.rw == 2) hipLaunchKernelGGL((k_gemv<WT, NC, 2>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
-  else hipLaunchKernelGGL((k_gemv<WT, NC, 4>), dim3(lp.grid), dim3(GD_WG), lp.lds, st, prm);
+  const dim3 g(lp.grid), b(GD_WG);
+  switch (prm.epi) {
+    case EPI_PLAIN: hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_PLAIN>), g, b, lp.lds, st, prm); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_GELU>), g, b, lp.lds, st, prm); break;
+    case EPI_QKV: hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_QKV>), g, b, lp.lds, st, prm); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<WT, NC, 2, EPI_SWIGLU>), g, b, lp.lds, st, prm); break;
+    case EPI_QKV_ROPE: hipLaunchKernelGGL((k_gemv<WT, NC, 2, EPI_QKV_ROPE>), g, b, lp.lds, st, prm); break;
+    default:
+      if (lp.rw == 4) hipLaunchKernelGGL((k_gemv<WT, NC, 4, EPI_ARGMAX>), g, b, lp.lds, st, prm);
+      else hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_ARGMAX>), g, b, lp.lds, st, prm);
+      break;
+  }
 }
 
 template <int WT>
@@ -151,14 +170,12 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
     p.M = std::min(lp.rows, prm.M - r0);
     if (r0) {
       if (p.x) p.x += (size_t)r0 * p.ldx;
-      if (p.resid) p.resid += (size_t)r0 * p.ldr;
+      p.resid += (size_t)r0 * p.ldr;
       if (p.y) p.y += (size_t)r0 * p.ldy;
       if (p.logits) p.logits += (size_t)r0 * p.ldl;
-      if (p.xres) p.xres += (size_t)r0 * p.K;
-      if (p.row_tok) p.row_tok += r0;
-      if (p.row_seq) p.row_seq += r0;
-      if (p.row_pos) p.row_pos += r0;
-      if (p.apart) p.apart += (size_t)r0 * p.Hq * p.nchunk * (p.hd + 2);
+      if (p.row_kvoff) p.row_kvoff += r0;
+      if (p.rope_cs) p.rope_cs += (size_t)r0 * p.hd;
+      if (p.apart) p.apart += (size_t)r0 * p.Hq * GD_ATT_NCH * (p.hd + 2);
     }
     hipError_t e = launch_linear(wt, lp, p, st);
     if (e != hipSuccess) return e;
@@ -198,7 +215,7 @@ struct gd_model {
 
   // derived shapes
   int qdim, kdim, qkvdim, fcN, hdim, wt;
-  int nblk, bsize, max_blocks, nchunk;
+  int nblk, bsize, max_blocks;
   size_t elt;  // bytes per weight element
 
   // sizes
@@ -216,8 +233,8 @@ struct gd_model {
   std::vector<LayerOff> L;
 
   // scratch offsets (bytes)
-  size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart;
-  size_t o_rseq, o_rpos, o_rtok, o_pseq, o_ppos, o_ptok, o_len, o_cap, o_sids, o_table, o_err, o_rope;
+  size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart, o_zero;
+  size_t o_rseq, o_rpos, o_rtok, o_rkv, o_rcs, o_pseq, o_ppos, o_ptok, o_pkv, o_pcs, o_len, o_cap, o_sids, o_table, o_err, o_rope;
 
   // host mirror
   std::vector<int> len, cap;
@@ -290,7 +307,6 @@ static void layout(gd_model* m) {
     m->nblk = c.max_seqs;
     m->max_blocks = 1;
   }
-  m->nchunk = iceil(c.n_ctx, GD_ATT_CHUNK);
 
   // weights
   size_t off = 0;
@@ -326,7 +342,7 @@ static void layout(gd_model* m) {
   m->am_parts = 0;
   for (int v = 1; v <= 2; ++v)
     for (int M = 1; M <= GD_MAX_ROWS; ++M)
-      m->am_parts = std::max(m->am_parts, (size_t)plan_linear(M, c.vocab, c.d_model, m->wt, v, false, 2).grid);
+      m->am_parts = std::max(m->am_parts, (size_t)plan_linear(M, c.vocab, c.d_model, m->wt, v, EPI_ARGMAX, true).grid);
 
   // scratch
   off = 0;
@@ -337,13 +353,19 @@ static void layout(gd_model* m) {
   m->o_h = take(R * ff * 4);
   m->o_amv = take(m->am_parts * R * 4);
   m->o_ami = take(m->am_parts * R * 4);
-  m->o_apart = take(R * c.n_head * m->nchunk * (c.head_dim + 2) * 4);
+  m->o_apart = take(R * c.n_head * GD_ATT_NCH * (c.head_dim + 2) * 4);
+  // zeros (cleared at bind, never written): the bias or residual of layers that have none
+  m->o_zero = take((size_t)std::max({m->qkvdim, m->fcN, (int)d, (int)ff}) * 4);
   m->o_rseq = take(R * 4);
   m->o_rpos = take(R * 4);
   m->o_rtok = take(R * 4);
+  m->o_rkv = take(R * 8);
+  m->o_rcs = c.arch == GD_ARCH_LLAMA ? take(R * c.head_dim * 4) : 0;
   m->o_pseq = take((size_t)c.n_ctx * 4);
   m->o_ppos = take((size_t)c.n_ctx * 4);
   m->o_ptok = take((size_t)c.n_ctx * 4);
+  m->o_pkv = take((size_t)c.n_ctx * 8);
+  m->o_pcs = c.arch == GD_ARCH_LLAMA ? take((size_t)c.n_ctx * c.head_dim * 4) : 0;
   m->o_len = take((size_t)c.max_seqs * 4);
   m->o_cap = take((size_t)c.max_seqs * 4);
   m->o_sids = take(R * 4);
@@ -382,6 +404,13 @@ extern "C" gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model*
     (void)hipStreamDestroy(m->cap_stream);
     delete m;
     return set_err(GD_ERR_HIP, "pinned staging allocation failed");
+  }
+  if (m->am_parts > (size_t)GD_WG * AM_FIN_PER) {
+    (void)hipHostFree(m->staging);
+    (void)hipEventDestroy(m->staging_evt);
+    (void)hipStreamDestroy(m->cap_stream);
+    delete m;
+    return set_err(GD_ERR_INVALID, "vocab %d too large for the argmax reduction", cfg->vocab);
   }
   m->len.assign(cfg->max_seqs, 0);
   m->cap.assign(cfg->max_seqs, cfg->kv_block_size > 0 ? 0 : cfg->n_ctx);
@@ -723,39 +752,52 @@ static const char* linear_kernel_name(int wt, const LinPlan& lp, char* buf, size
 static double linear_bytes(const gd_model* m, const LinParams& p) {
   const int n_out = p.epi == EPI_SWIGLU ? p.N / 2 : (p.epi == EPI_ARGMAX ? (p.logits ? p.N : 0) : p.N);
   double b = (double)p.N * p.K * m->elt + (double)p.M * p.K * 4 + (double)p.M * n_out * 4;
-  if (p.bias) b += (double)p.N * 4;
+  const float* zero = m->sp<float>(m->o_zero);
+  if (p.bias && p.bias != zero) b += (double)p.N * 4;
   if (p.norm) b += (double)p.K * 4 * (p.nb ? 2 : 1);
-  if (p.resid) b += (double)p.M * p.N * 4;
+  if (p.resid && p.resid != zero) b += (double)p.M * p.N * 4;
   return b;
 }
 
 // Launches one linear layer (profiled when enabled).
-static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, const LinParams& p, int stat_floats,
+static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, const LinParams& p,
                              int* am_out = nullptr) {
-  const bool pair = p.epi == EPI_SWIGLU || (p.epi == EPI_QKV && p.rope_cs);
-  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, pair, stat_floats);
+  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE);
   char kn[64];
   ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, kn, sizeof(kn)), m->profile ? linear_bytes(m, p) : 0);
   return run_linear_rows(m->wt, lp, p, st, am_out);
 }
 
-// Rows handled by the gemv kernel (embedding and attention merge fused into prologues).
-static bool rows_use_gemv(const gd_model* m, int M) {
-  return m->variant == 1 || (m->variant == 0 && M <= GEMV_MAX_ROWS);
-}
-
 template <int HD, int G>
-static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a) {
+static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, bool paged) {
   static_assert(HD == 64 || HD == 16, "head_dim");
   constexpr int PPG = HD == 64 ? 4 : 1;
-  static_assert(GD_WG / (HD / 4) * PPG == GD_ATT_CHUNK, "attention chunk");
-  hipLaunchKernelGGL((k_attention<HD, G, PPG>), grid, dim3(GD_WG), 0, st, a);
+  if (paged) hipLaunchKernelGGL((k_attention<HD, G, PPG, true>), grid, dim3(GD_WG), 0, st, a);
+  else hipLaunchKernelGGL((k_attention<HD, G, PPG, false>), grid, dim3(GD_WG), 0, st, a);
+}
+
+// Row set-up parameters over the row arrays starting at seq/pos/tok/kvoff.
+static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long long* rkv, float* rcs) {
+  const gd_config& c = m->c;
+  RowParams r;
+  memset(&r, 0, sizeof(r));
+  r.table = m->sp<int>(m->o_table); r.max_blocks = m->max_blocks; r.block_size = m->bsize; r.nblk = m->nblk;
+  r.Hkv = c.n_kv_head; r.hd = c.head_dim;
+  r.wte = m->w + m->o_wte;
+  r.wpe = c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr;
+  r.vocab = c.vocab; r.n_pos = c.n_ctx; r.d = c.d_model; r.emb_bf16 = m->wt == GD_WEIGHT_BF16;
+  r.x = m->sp<float>(m->o_x);
+  r.row_seq = rseq; r.row_pos = rpos; r.row_tok = rtok; r.row_kvoff = rkv;
+  r.rope = c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rope) : nullptr;
+  r.row_cs = rcs;
+  r.err = m->sp<int>(m->o_err);
+  return r;
 }
 
 // Enqueues the forward pass of M (<= 32) rows with device-resident row metadata.
 // If head_out is not NULL, computes logits/argmax for rows [head_row, head_row + head_rows).
-static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rseq, const int* rpos,
-                               const int* rtok, int head_row, int head_rows, int* head_out, float* logits) {
+static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp, int M, int head_row, int head_rows,
+                               int* head_out, float* logits) {
   const gd_config& c = m->c;
   const int d = c.d_model, ff = c.d_ff;
   float* x = m->sp<float>(m->o_x);
@@ -763,69 +805,45 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rs
   float* attn = m->sp<float>(m->o_attn);
   float* h = m->sp<float>(m->o_h);
   float* apart = m->sp<float>(m->o_apart);
+  const float* zero = m->sp<float>(m->o_zero);
   int* err = m->sp<int>(m->o_err);
   hipError_t e;
-  const bool gemv = rows_use_gemv(m, M);
+  // the gemv O-projection merges the attention partials in its prologue
+  const bool o_gemv = plan_linear(M, c.d_model, m->qdim, m->wt, m->variant, EPI_PLAIN, false).var == 0;
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
-  const void* wte = m->w + m->o_wte;
-  const void* wpe = gpt2 ? (const void*)(m->w + m->o_wpe) : nullptr;
 
   double kv_pos = 0;  // attended positions summed over rows (profiling only)
   for (int t : m->prof_T) kv_pos += t;
-
-  if (!gemv) {
-    ProfScope ps(m, st, "embed", m->wt == GD_WEIGHT_F32 ? "k_embed<0>" : "k_embed<1>",
-                 (double)M * d * (m->elt * (gpt2 ? 2 : 1) + 4.0));
-    if (m->wt == GD_WEIGHT_F32)
-      hipLaunchKernelGGL(k_embed<0>, dim3(M), dim3(GD_WG), 0, st, wte, wpe, c.vocab, c.n_ctx, d, rtok, rpos, x, d,
-                         err);
-    else
-      hipLaunchKernelGGL(k_embed<1>, dim3(M), dim3(GD_WG), 0, st, wte, wpe, c.vocab, c.n_ctx, d, rtok, rpos, x, d,
-                         err);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
 
   LinParams base;
   memset(&base, 0, sizeof(base));
   base.eps = c.norm_eps;
   base.err = err;
-  base.vocab = c.vocab;
-  base.n_pos = c.n_ctx;
   base.hd = c.head_dim;
   base.Hq = c.n_head;
-  base.nchunk = m->nchunk;
-  base.chunk = GD_ATT_CHUNK;
-  base.row_seq = rseq;
-  base.row_pos = rpos;
-  base.row_tok = rtok;
+  base.row_kvoff = rp.row_kvoff;
   base.M = M;
-  const int att_stat = m->nchunk * c.n_head;  // attention merge weights per row (gemv O-projection)
 
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& t = m->L[l];
     // pre-norm + QKV + bias; q to its buffer, k and v appended to the cache (RoPE first
-    // for the Llama layout); the first layer's rows come from the embedding
+    // for the Llama layout)
     {
       LinParams p = base;
-      if (gemv && l == 0) {
-        p.pro = PRO_EMBED;
-        p.wte = wte; p.wpe = wpe; p.emb_bf16 = m->wt == GD_WEIGHT_BF16; p.xres = x;
-      } else {
-        p.pro = PRO_COPY;
-      }
+      p.pro = PRO_COPY;
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
       p.w = m->w + t.wqkv; p.N = m->qkvdim; p.K = d;
-      p.epi = EPI_QKV;
-      p.bias = t.bqkv ? m->wf(t.bqkv) : nullptr;
+      p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
+      p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
       p.y = q; p.ldy = m->qdim;
       p.qdim = m->qdim; p.kdim = m->kdim;
-      p.rope_cs = gpt2 ? nullptr : m->sp<float>(m->o_rope);
+      p.rope_cs = rp.row_cs;
       p.kc = m->kpool(l); p.vc = m->vpool(l);
-      p.table = m->sp<int>(m->o_table); p.max_blocks = m->max_blocks; p.block_size = m->bsize; p.nblk = m->nblk;
-      if ((e = run_linear(m, st, "linear.qkv", p, 2)) != hipSuccess) return e;
+      p.kv_hstride = m->bsize * c.head_dim;
+      if ((e = run_linear(m, st, "linear.qkv", p)) != hipSuccess) return e;
     }
     // causal attention of every row against its sequence's cache (split-context partials)
     {
@@ -834,40 +852,41 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rs
       a.q = q; a.ldq = m->qdim;
       a.kc = m->kpool(l); a.vc = m->vpool(l);
       a.table = m->sp<int>(m->o_table); a.max_blocks = m->max_blocks; a.block_size = m->bsize; a.nblk = m->nblk;
-      a.Hq = c.n_head; a.Hkv = c.n_kv_head; a.row_seq = rseq; a.row_pos = rpos;
-      a.M = M; a.nchunk = m->nchunk;
+      a.Hq = c.n_head; a.Hkv = c.n_kv_head; a.row_seq = rp.row_seq; a.row_pos = rp.row_pos;
+      a.row_kvoff = rp.row_kvoff;
+      a.M = M;
       a.scale = 1.0f / std::sqrt((float)c.head_dim);
       a.part = apart;
-      dim3 grid(m->nchunk, c.n_kv_head, M);
+      dim3 grid(GD_ATT_NCH, c.n_kv_head, M);
+      const bool paged = c.kv_block_size > 0;
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attention<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attention", kn, kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4);
-      if (c.head_dim == 64 && G == 1) launch_attention<64, 1>(grid, st, a);
-      else if (c.head_dim == 64) launch_attention<64, 3>(grid, st, a);
-      else if (G == 1) launch_attention<16, 1>(grid, st, a);
-      else launch_attention<16, 3>(grid, st, a);
+      if (c.head_dim == 64 && G == 1) launch_attention<64, 1>(grid, st, a, paged);
+      else if (c.head_dim == 64) launch_attention<64, 3>(grid, st, a, paged);
+      else if (G == 1) launch_attention<16, 1>(grid, st, a, paged);
+      else launch_attention<16, 3>(grid, st, a, paged);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // output projection + bias + residual (in place on x); the gemv kernel merges the
     // attention partials in its prologue, the mfma path merges them in a kernel first
     {
       LinParams p = base;
-      if (gemv) {
+      if (o_gemv) {
         p.pro = PRO_ATTN;
         p.apart = apart;
       } else {
         ProfScope ps(m, st, "attn_merge", "k_attn_merge", (double)M * c.n_head * (c.head_dim + 2) * 4.0 * 2);
-        hipLaunchKernelGGL(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, m->nchunk,
-                           GD_ATT_CHUNK, rpos, attn, m->qdim);
+        hipLaunchKernelGGL(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, attn, m->qdim);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.pro = PRO_COPY;
         p.x = attn; p.ldx = m->qdim;
       }
       p.w = m->w + t.wo; p.N = d; p.K = m->qdim;
       p.epi = EPI_PLAIN;
-      p.bias = t.bo ? m->wf(t.bo) : nullptr;
+      p.bias = t.bo ? m->wf(t.bo) : zero;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
-      if ((e = run_linear(m, st, "linear.o", p, att_stat)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.o", p)) != hipSuccess) return e;
     }
     // pre-norm + MLP up: GPT-2 FC + bias + clamped tanh-GELU; Llama gate|up + SiLU gate
     {
@@ -877,9 +896,10 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rs
       p.norm = nrm; p.ng = m->wf(t.n2g); p.nb = t.n2b ? m->wf(t.n2b) : nullptr;
       p.w = m->w + t.wfc; p.N = m->fcN; p.K = d;
       p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
-      p.bias = t.bfc ? m->wf(t.bfc) : nullptr;
+      p.bias = t.bfc ? m->wf(t.bfc) : zero;
+      p.resid = zero; p.ldr = 0;
       p.y = h; p.ldy = ff;
-      if ((e = run_linear(m, st, "linear.fc", p, 2)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.fc", p)) != hipSuccess) return e;
     }
     // MLP down + bias + residual (in place on x)
     {
@@ -888,9 +908,9 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rs
       p.x = h; p.ldx = ff;
       p.w = m->w + t.wproj; p.N = d; p.K = ff;
       p.epi = EPI_PLAIN;
-      p.bias = t.bproj ? m->wf(t.bproj) : nullptr;
+      p.bias = t.bproj ? m->wf(t.bproj) : zero;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
-      if ((e = run_linear(m, st, "linear.down", p, 2)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.down", p)) != hipSuccess) return e;
     }
   }
   if (head_out) {
@@ -902,10 +922,11 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, int M, const int* rs
     p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.N = c.vocab; p.K = d;
     p.epi = EPI_ARGMAX;
     p.M = head_rows;
-    p.row_seq = rseq + head_row; p.row_pos = rpos + head_row; p.row_tok = rtok + head_row;
+    p.row_kvoff = rp.row_kvoff + head_row;
+    p.rope_cs = nullptr;
     p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
     p.logits = logits; p.ldl = c.vocab;
-    if ((e = run_linear(m, st, "linear.head", p, 2, head_out)) != hipSuccess) return e;
+    if ((e = run_linear(m, st, "linear.head", p, head_out)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -949,9 +970,17 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
     m->prof_T.clear();
     if (m->profile)
       for (int i = 0; i < M; ++i) m->prof_T.push_back(p0 + r0 + i + 1);
-    hipError_t e = enqueue_rows(m, s, M, m->sp<int>(m->o_pseq) + r0, m->sp<int>(m->o_ppos) + r0,
-                                m->sp<int>(m->o_ptok) + r0, M - 1, 1, last ? next_dev : nullptr,
-                                last ? logits_dev : nullptr);
+    RowParams rp = row_params(m, m->sp<int>(m->o_pseq) + r0, m->sp<int>(m->o_ppos) + r0,
+                              m->sp<int>(m->o_ptok) + r0, m->sp<long long>(m->o_pkv) + r0,
+                              c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_pcs) + (size_t)r0 * c.head_dim : nullptr);
+    hipError_t e;
+    {
+      ProfScope ps(m, s, "setup", "k_setup_rows", (double)M * c.d_model * (m->elt * 2 + 4));
+      hipLaunchKernelGGL(k_setup_rows, dim3(M), dim3(GD_WG), 0, s, rp);
+      e = hipGetLastError();
+    }
+    if (e == hipSuccess)
+      e = enqueue_rows(m, s, rp, M, M - 1, 1, last ? next_dev : nullptr, last ? logits_dev : nullptr);
     if (e != hipSuccess) {
       m->poisoned = true;
       return set_err(GD_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
@@ -962,15 +991,17 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
 }
 
 static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, const int* tok, int* next, float* logits) {
-  ProfScope* ps = new ProfScope(m, st, "setup", "k_setup_decode", (double)B * 16);
-  hipLaunchKernelGGL(k_setup_decode, dim3(1), dim3(64), 0, st, B, m->sp<int>(m->o_sids), tok, m->sp<int>(m->o_len),
-                     m->sp<int>(m->o_cap), m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
-                     m->sp<int>(m->o_err));
-  delete ps;
+  RowParams rp = row_params(m, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
+                            m->sp<long long>(m->o_rkv),
+                            m->c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rcs) : nullptr);
+  {
+    ProfScope ps(m, st, "setup", "k_setup_decode", (double)B * m->c.d_model * (m->elt * 2 + 4));
+    hipLaunchKernelGGL(k_setup_decode, dim3(B), dim3(GD_WG), 0, st, rp, m->sp<int>(m->o_sids), tok,
+                       m->sp<int>(m->o_len), m->sp<int>(m->o_cap));
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return enqueue_rows(m, st, B, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok), 0, B, next,
-                      logits);
+  return enqueue_rows(m, st, rp, B, 0, B, next, logits);
 }
 
 extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids, const int32_t* tok_dev,
@@ -1041,11 +1072,15 @@ static gd_status linear_check(int M, int N, int K, int variant) {
   return GD_OK;
 }
 
+// The op-level linear reads a zero vector (in the workspace) in place of an absent
+// bias or residual.
+static size_t linear_ws_bytes(int N) { return align_up((size_t)N * 4, 256); }
+
 extern "C" gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, size_t* bytes) {
   if (!bytes) return set_err(GD_ERR_INVALID, "bytes is NULL");
   gd_status st = linear_check(M, N, K, variant);
   if (st != GD_OK) return st;
-  *bytes = 0;  // both kernels reduce inside a workgroup: no cross-workgroup scratch
+  *bytes = linear_ws_bytes(N);
   return GD_OK;
 }
 
@@ -1053,8 +1088,6 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
                                int32_t norm, const float* ng, const float* nb, float eps, int32_t act,
                                const float* resid, int32_t ldr, float* y, int32_t ldy, int32_t M, int32_t N, int32_t K,
                                int32_t variant, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   gd_status st = linear_check(M, N, K, variant);
   if (st != GD_OK) return st;
   if (!x || !W || !y) return set_err(GD_ERR_INVALID, "NULL argument");
@@ -1065,6 +1098,9 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
   if (ldx < K || ldx % 4 || ldy < N || (resid && ldr < N)) return set_err(GD_ERR_INVALID, "bad leading dimensions");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(W)) & 15)
     return set_err(GD_ERR_INVALID, "x and W must be 16-byte aligned");
+  if (!ws || ws_bytes < linear_ws_bytes(N))
+    return set_err(GD_ERR_OOM, "workspace %zu < %zu bytes", ws_bytes, linear_ws_bytes(N));
+  const float* zero = static_cast<const float*>(ws);
   LinParams p;
   memset(&p, 0, sizeof(p));
   p.pro = PRO_COPY;
@@ -1072,8 +1108,11 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
   p.x = x; p.ldx = ldx; p.ng = ng; p.nb = nb; p.eps = eps;
   p.w = W; p.M = M; p.N = N; p.K = K;
   p.epi = act == GD_ACT_GELU ? EPI_GELU : EPI_PLAIN;
-  p.bias = bias; p.resid = resid; p.ldr = ldr; p.y = y; p.ldy = ldy;
-  LinPlan lp = plan_linear(M, N, K, wdt, variant, false, 2);
+  p.bias = bias ? bias : zero;
+  p.resid = resid ? resid : zero;
+  p.ldr = resid ? ldr : 0;
+  p.y = y; p.ldy = ldy;
+  LinPlan lp = plan_linear(M, N, K, wdt, variant, p.epi, p.norm != NORM_NONE);
   hipError_t e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
   return GD_OK;
