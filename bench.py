@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+METRIC = "decode tok/s at GPT-2-124M shape, batch 1 and 32; achieved HBM GB/s"
 
 
 def log(*a):
@@ -202,6 +203,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_b1")
     ap.add_argument("--batch32", default="gpt2_b32", help="second workload reported beside ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a kernel of known traffic that "
+                         "scales the HBM byte counters of a rocprofv3 --pmc run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
@@ -210,6 +214,15 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
 
     log(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps or 'one generation'}")
     res = measure(args.workload, args.steps, args.warmup)
@@ -218,7 +231,7 @@ def main():
     for r in rows:
         log(f"  {r['kernel']:<28} {str(r['roles']):<40} {r['launches_per_step']:6.1f}/step {r['avg_us']:9.2f} us "
             f"{r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
-    out = {"metric": "decode tok/s (GPT-2 124M shape, batch 1)", "value": summ["value"], "unit": "tok/s",
+    out = {"metric": METRIC, "value": summ["value"], "unit": "tok/s",
            "n_gpus": 1, "steps": res["K"], "warmup": args.warmup, "ms_per_step": summ["ms_per_step"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": res["w"].name, "batch": res["w"].batch, "prompt_len": res["w"].prompt_len[0],
