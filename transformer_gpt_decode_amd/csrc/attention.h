@@ -152,37 +152,70 @@ __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
   }
 }
 
-// Merge of the chunk partials of one (row, query head, dim) into o. Chunk 0 always
-// holds at least one position, so the maximum is finite; empty chunks (max = -inf,
-// sum 0, o 0) get weight exp(-inf) = 0. All loads are issued before any arithmetic.
-__device__ __forceinline__ float attn_merge_one(const float* __restrict__ pp, int hd, int d) {
-  const int stride = hd + 2;
-  float mc[GD_ATT_NCH], lc[GD_ATT_NCH], oc[GD_ATT_NCH];
+// Merge of the chunk partials of M rows x Hq heads into dst[m * ldd + h * hd + d]:
+// o = sum_c e^(max_c - max) o_c / sum_c e^(max_c - max) sum_c. Chunk 0 always holds at
+// least one position, so the maximum is finite; empty chunks (max -inf, sum 0, o 0)
+// get weight 0. Each thread first issues the partial outputs of its first EPT elements
+// and the (max, sum) of its (row, head, chunk) entries, so the merge costs one memory
+// round trip; the chunk weights of each (row, head) are formed by 8 adjacent lanes and
+// shared through LDS (s_w: M * Hq * GD_ATT_NCH floats). Called by the whole workgroup
+// (nthr threads, a multiple of 64).
+template <int EPT>
+__device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd, int M, float* dst, int ldd,
+                                float* s_w, int nthr) {
+  static_assert(GD_ATT_NCH == 8, "one chunk per lane of an 8-lane group");
+  const int tid = threadIdx.x, K = Hq * hd, stride = hd + 2;
+  const int total = M * K, npair = M * Hq * GD_ATT_NCH;
+  float oc[EPT][GD_ATT_NCH];
 #pragma unroll
-  for (int c = 0; c < GD_ATT_NCH; ++c) {
-    mc[c] = pp[(size_t)c * stride];
-    lc[c] = pp[(size_t)c * stride + 1];
-    oc[c] = pp[(size_t)c * stride + 2 + d];
+  for (int j = 0; j < EPT; ++j) {
+    const int i = min(tid + nthr * j, total - 1);
+    const int m = i / K, k = i - m * K;
+    const int h = k / hd, d = k - h * hd;
+    const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + 2 + d;
+#pragma unroll
+    for (int c = 0; c < GD_ATT_NCH; ++c) oc[j][c] = pp[(size_t)c * stride];
   }
-  float mx = mc[0];
-#pragma unroll
-  for (int c = 1; c < GD_ATT_NCH; ++c) mx = fmaxf(mx, mc[c]);
-  float l = 0.f, o = 0.f;
-#pragma unroll
-  for (int c = 0; c < GD_ATT_NCH; ++c) {
-    const float w = expf(mc[c] - mx);
-    l = fmaf(lc[c], w, l);
-    o = fmaf(oc[c], w, o);
+  for (int q0 = 0; q0 < npair; q0 += nthr) {   // npair is a multiple of 8: groups never straddle
+    const int q = min(q0 + tid, npair - 1);
+    const float* pp = apart + (size_t)q * stride;   // entry (m, h, c) = q
+    const float mc = pp[0], lc = pp[1];
+    const float mx = group_max<GD_ATT_NCH>(mc);
+    const float e = expf(mc - mx);
+    const float l = group_sum<GD_ATT_NCH>(lc * e);
+    if (q0 + tid < npair) s_w[q0 + tid] = e / l;
   }
-  return o / l;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int i = tid + nthr * j;
+    if (i < total) {
+      const int m = i / K, k = i - m * K;
+      const float* w = s_w + ((size_t)m * Hq + k / hd) * GD_ATT_NCH;
+      float o = 0.f;
+#pragma unroll
+      for (int c = 0; c < GD_ATT_NCH; ++c) o = fmaf(w[c], oc[j][c], o);
+      dst[(size_t)m * ldd + k] = o;
+    }
+  }
+  for (int i = tid + nthr * EPT; i < total; i += nthr) {   // elements beyond the register share
+    const int m = i / K, k = i - m * K;
+    const int h = k / hd, d = k - h * hd;
+    const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + 2 + d;
+    const float* w = s_w + ((size_t)m * Hq + h) * GD_ATT_NCH;
+    float o = 0.f;
+#pragma unroll
+    for (int c = 0; c < GD_ATT_NCH; ++c) o = fmaf(w[c], pp[(size_t)c * stride], o);
+    dst[(size_t)m * ldd + k] = o;
+  }
 }
 
-// Merge of the chunk partials into o[M][Hq*HD] (rows handled by the MFMA kernel).
+// Merge of the chunk partials into o[M][Hq*HD] (rows handled by the matrix-core
+// kernel): one workgroup per row.
 __global__ __launch_bounds__(GD_WG) void k_attn_merge(const float* __restrict__ part, int Hq, int hd, float* out,
                                                       int ldo) {
+  __shared__ float s_w[GD_MAX_HEADS * GD_ATT_NCH];
   const int m = blockIdx.x;
-  for (int i = threadIdx.x; i < Hq * hd; i += GD_WG) {
-    const int h = i / hd, d = i - h * hd;
-    out[(size_t)m * ldo + i] = attn_merge_one(part + ((size_t)m * Hq + h) * GD_ATT_NCH * (hd + 2), hd, d);
-  }
+  attn_merge_rows<4>(part + (size_t)m * Hq * GD_ATT_NCH * (hd + 2), Hq, hd, 1, out + (size_t)m * ldo, ldo, s_w,
+                     GD_WG);
 }

@@ -7,6 +7,7 @@
 #define GD_MAX_ROWS 32     // rows (sequences or prompt positions) per forward call
 #define GD_TILE_N 16       // output columns per linear tile
 #define GD_ATT_NCH 8       // context chunks (attention workgroups) per row and KV head
+#define GD_MAX_HEADS 32    // query heads per layer
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -38,21 +39,56 @@ __device__ __forceinline__ void load_w8(const void* __restrict__ W, size_t row_o
   }
 }
 
-// Sum over aligned groups of G lanes (G a power of two <= 64); every lane gets the sum.
+// Cross-lane reductions with DPP (data-parallel primitives: the lane permutation is
+// part of the VALU instruction, no LDS traffic). Steps: quad_perm (1,0,3,2) and
+// (2,3,0,1) sum pairs then quads, row_half_mirror adds the other quad of each group of
+// 8, row_mirror the other half of each row of 16; the four rows of the wave are
+// combined through readlane. Every lane of a group gets the group's result.
+#define DPP_QUAD_1032 0xB1
+#define DPP_QUAD_2301 0x4E
+#define DPP_ROW_MIRROR 0x140
+#define DPP_ROW_HALF_MIRROR 0x141
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of G lanes (G = 4, 8, 16 or 64); every lane gets the sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, G);
+  static_assert(G == 4 || G == 8 || G == 16 || G == 64, "group size");
+  v += dpp_f<DPP_QUAD_1032>(v);
+  v += dpp_f<DPP_QUAD_2301>(v);
+  if (G >= 8) v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  if (G >= 16) v += dpp_f<DPP_ROW_MIRROR>(v);
+  if (G == 64) {
+    const int b = __float_as_int(v);
+    v = (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+        (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+  }
+  return v;
+}
+
+// Maximum over aligned groups of G lanes (G = 8 or 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(G == 8 || G == 64, "group size");
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  if (G == 64) {
+    v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+    const int b = __float_as_int(v);
+    v = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+              fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+  }
   return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // Agent-scope (whole device) atomics and fences for the last-arriver reductions.
 __device__ __forceinline__ int atomic_add_acq_rel(int* p, int v) {

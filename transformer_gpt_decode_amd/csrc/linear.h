@@ -15,11 +15,8 @@
 //   prologue (a copy or, for the first layer, the token + position embedding, or
 //   the merge of split-context attention partials), then LayerNorm or RMSNorm of
 //   each row. Dot products are reduced across the wave.
-// k_mfma (5..32 rows): v_mfma_f32_16x16x4f32 on a 16-column tile. Lane l holds
-//   W[n0 + l%16][k + 8(l/16) .. +8] and X[m0 + l%16][same k]; step t of 8 feeds
-//   element t of both, so the four k-slots of one instruction are k + 8q + t
-//   (q = l/16) for A and B alike. NW waves split K by 32-element blocks; X fragments
-//   come straight from L2 with the row normalization applied on the fly.
+// k_mm (5..32 rows): fp32 matrix-core tiles of 16 columns over activation rows staged
+//   in LDS; see the MFMA section below.
 //
 // Epilogues: bias, clamped tanh-GELU, residual add; SiLU-gated pairs (gate and up
 // rows interleaved, gate at even rows); QKV scatter (q to a buffer, k and v into the
@@ -202,16 +199,11 @@ __device__ __forceinline__ void block_sum_rows(float v[GEMV_MAX_ROWS], int M, fl
 
 template <int XPT>
 __device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const RowRegs<XPT>& rr,
-                             float (*red)[GD_WG / 64][GEMV_MAX_ROWS]) {
+                             float (*red)[GD_WG / 64][GEMV_MAX_ROWS], float* s_aw) {
   const int tid = threadIdx.x;
   const int M = p.M, K = p.K;
   if (p.pro == PRO_ATTN) {
-    const int hd = p.hd;
-    for (int i = tid; i < M * K; i += GD_WG) {
-      const int m = i / K, k = i - m * K;
-      const int h = k / hd, d = k - h * hd;
-      xs[i] = attn_merge_one(p.apart + ((size_t)m * p.Hq + h) * GD_ATT_NCH * (hd + 2), hd, d);
-    }
+    attn_merge_rows<4>(p.apart, p.Hq, p.hd, M, xs, K, s_aw, GD_WG);
     return;
   }
   const int K4 = K >> 2;
@@ -351,6 +343,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   float* s_gb = xs + ((p.M * p.K + 3) & ~3);
   __shared__ float s_am[GEMV_MAX_ROWS][4 * RW];
   __shared__ float s_red[2][GD_WG / 64][GEMV_MAX_ROWS];
+  __shared__ float s_aw[GEMV_MAX_ROWS * GD_MAX_HEADS * GD_ATT_NCH];   // attention chunk weights
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, N = p.N, K = p.K;
   const int nw0 = (blockIdx.x * 4 + wave) * RW;              // first row of this wave
@@ -381,7 +374,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   const bool own = EPI != EPI_ARGMAX && om < M && (PAIR ? nw0 + 1 < N : (lane < M * RW && on < N));
   EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? on : 0);
   // 3. activations into LDS, normalized
-  stage_finish<XPT>(p, xs, s_gb, rr, s_red);
+  stage_finish<XPT>(p, xs, s_gb, rr, s_red, s_aw);
   __syncthreads();
   // 4. dot products
   float acc[RW][GEMV_MAX_ROWS];
@@ -470,134 +463,353 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
 }
 
 // ------------------------------------------------------------------- MFMA
+//
+// k_mm (1..32 rows): 16-column tiles on v_mfma_f32_16x16x4f32 (bf16 weights widened
+// to fp32 in registers). Grid (G, S): workgroup (g, s) owns the 32-column K blocks
+// [s nb / S, (s + 1) nb / S) and the column tiles g, g + G, g + 2G, ...
+//
+// The activation rows of the workgroup's K range are staged into LDS once (row stride
+// kl + 4 floats, so the 16 rows one instruction reads fall in different banks) and,
+// when the layer has a pre-norm (S == 1, the norm needs whole rows), normalized there.
+// Each of the NW waves takes every NW-th block; all of its weight loads for a tile are
+// issued before its MFMAs, and the loads of the next tile before the current tile's
+// reduction and epilogue. Waves are summed in LDS. With S > 1 (linear epilogue whose
+// output is the residual, updated in place) each split adds its partial sums to the
+// output with float atomics, the bias coming from split 0.
+//
+// Operand layout: lane l holds W[n0 + l%16][kk + 8(l/16) .. +8] and X[m0 + l%16][same];
+// MFMA step t of 8 feeds element t of both, so one instruction contracts the k-values
+// kk + 8q + t (q = l/16) for A and B alike. D[i][j]: lane l holds column j = l%16 and
+// rows 4(l/16) + v.
+
+#define MM_JB 4        // blocks per wave and tile held in registers
+#define MM_KC 1024     // widest K range staged at once (columns)
+#define MM_SB 16       // float4 row loads in flight per thread while staging
+
+template <int WT> struct W8;   // eight consecutive weights of one row, as stored
+template <> struct W8<0> { f32x4 a, b; };
+template <> struct W8<1> { u32x4 a; };
+
+template <int WT>
+__device__ __forceinline__ W8<WT> load_w8raw(const void* __restrict__ W, size_t off) {
+  W8<WT> r;
+  if constexpr (WT == 0) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(W) + off);
+    r.a = __builtin_nontemporal_load(q);
+    r.b = __builtin_nontemporal_load(q + 1);
+  } else {
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + off));
+  }
+  return r;
+}
+
+template <int WT>
+__device__ __forceinline__ float w8_at(const W8<WT>& r, int t) {
+  if constexpr (WT == 0) {
+    const f32x4 v = t < 4 ? r.a : r.b;
+    const int u = t & 3;
+    return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
+  } else {
+    const int u = t >> 1;
+    const uint32_t x = u == 0 ? r.a.x : u == 1 ? r.a.y : u == 2 ? r.a.z : r.a.w;
+    return (t & 1) ? bf16_hi(x) : bf16_lo(x);
+  }
+}
 
 typedef float TileT[GD_MAX_ROWS][GD_TILE_N + 1];
 
+// Epilogue of one reduced 16-column tile (all rows), by the whole workgroup.
 template <int EPI>
-__device__ void mfma_epi(const LinParams& p, TileT& tileT, int n0, int nthr) {
+__device__ void mm_epi(const LinParams& p, const TileT& tt, int n0, int nthr, int S, int s) {
   const int tid = threadIdx.x;
   if (EpiTraits<EPI>::pair) {
     for (int i = tid; i < p.M * (GD_TILE_N / 2); i += nthr) {
       const int m = i >> 3, c = (i & 7) * 2;
       if (n0 + c + 1 < p.N) {
         const EpiOps e = epi_prefetch<EPI>(p, m, n0 + c);
-        epi_store<EPI>(p, e, m, n0 + c, tileT[m][c], tileT[m][c + 1]);
+        epi_store<EPI>(p, e, m, n0 + c, tt[m][c], tt[m][c + 1]);
       }
     }
   } else {
     for (int i = tid; i < p.M * GD_TILE_N; i += nthr) {
       const int m = i >> 4, c = i & 15;
       if (n0 + c < p.N) {
-        const EpiOps e = epi_prefetch<EPI>(p, m, n0 + c);
-        epi_store<EPI>(p, e, m, n0 + c, tileT[m][c], 0.f);
+        if (EPI == EPI_PLAIN && S > 1) {
+          // split-K: the output already holds the residual; add this split's share
+          const float v = tt[m][c] + (s == 0 ? p.bias[n0 + c] : 0.f);
+          __hip_atomic_fetch_add(p.y + (size_t)m * p.ldy + n0 + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          const EpiOps e = epi_prefetch<EPI>(p, m, n0 + c);
+          epi_store<EPI>(p, e, m, n0 + c, tt[m][c], 0.f);
+        }
       }
     }
   }
 }
 
-__device__ void mfma_argmax(const LinParams& p, TileT& tileT, int n0, int nthr) {
+__device__ void mm_argmax(const LinParams& p, const TileT& tt, int t, int n0, int nthr) {
   const int tid = threadIdx.x;
   if (p.logits)
     for (int i = tid; i < p.M * GD_TILE_N; i += nthr) {
       const int m = i >> 4, c = i & 15;
-      if (n0 + c < p.N) p.logits[(size_t)m * p.ldl + n0 + c] = tileT[m][c];
+      if (n0 + c < p.N) p.logits[(size_t)m * p.ldl + n0 + c] = tt[m][c];
     }
   if (tid < p.M) {
-    float bv = tileT[tid][0];
+    float bv = tt[tid][0];
     int bi = n0;
     for (int c = 1; c < GD_TILE_N && n0 + c < p.N; ++c)
-      if (am_better(tileT[tid][c], n0 + c, bv, bi)) { bv = tileT[tid][c]; bi = n0 + c; }
-    p.am_val[(size_t)blockIdx.x * p.M + tid] = bv;
-    p.am_idx[(size_t)blockIdx.x * p.M + tid] = bi;
+      if (am_better(tt[tid][c], n0 + c, bv, bi)) { bv = tt[tid][c]; bi = n0 + c; }
+    p.am_val[(size_t)t * p.M + tid] = bv;
+    p.am_idx[(size_t)t * p.M + tid] = bi;
   }
 }
 
+// Dynamic LDS floats of k_mm for a K range of kl columns (<= MM_KC).
+__host__ __device__ constexpr int mm_lds_floats(int MT, int NW, int kl) {
+  return MT * 16 * (kl + 4) + NW * MT * 16 * 17 + GD_MAX_ROWS * (GD_TILE_N + 1) + 2 * MT * 16 + 2 * MM_KC;
+}
+
 template <int WT, int MT, int NW>
-__global__ __launch_bounds__(64 * NW) void k_mfma(LinParams p) {
-  __shared__ float s_stat[GD_MAX_ROWS * 2];
-  __shared__ float red[NW][GD_MAX_ROWS][GD_TILE_N + 1];
-  __shared__ TileT tileT;
+__global__ __launch_bounds__(64 * NW) void k_mm(LinParams p) {
+  constexpr int R = MT * 16;
+  static_assert(R * (MM_KC / 4) <= 64 * NW * MM_SB, "one staging batch covers a whole chunk");
+  extern __shared__ __align__(16) float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, N = p.N, K = p.K;
-  const int n0 = blockIdx.x * GD_TILE_N;
-  const int n = n0 + (lane & 15);
-  const int q = lane >> 4;
-  const bool norm = p.norm != NORM_NONE;
+  const int S = gridDim.y, s = blockIdx.y;
+  const int nb = (K + 31) >> 5;
+  const int b0 = (int)((long long)s * nb / S), b1 = (int)((long long)(s + 1) * nb / S);
+  const int kr0 = b0 * 32, kr1 = min(K, b1 * 32);
+  const int ntiles = (N + GD_TILE_N - 1) / GD_TILE_N;
+  const int q = lane >> 4, c = lane & 15;
+  const int kl_max = min(kr1 - kr0, MM_KC);
+  const int ldx = kl_max + 4;
+  float* xs = smem;                                   // [R][ldx]
+  float* red = xs + R * ldx;                          // [NW][R][17]
+  TileT& tt = *reinterpret_cast<TileT*>(red + NW * R * 17);
+  float* s_stat = red + NW * R * 17 + GD_MAX_ROWS * (GD_TILE_N + 1);  // [R][2]
+  float* s_g = s_stat + 2 * R;                        // norm gain [MM_KC], then shift [MM_KC]
+  const bool one_chunk = kr1 - kr0 <= MM_KC;
 
-  if (norm) {
-    for (int m = wave; m < M; m += NW) {
-      const float* xr = p.x + (size_t)m * p.ldx;
-      float mean = 0.f;
-      if (p.norm == NORM_LN) {
-        float s = 0.f;
-        for (int k = lane; k < K; k += 64) s += xr[k];
-        mean = wave_sum(s) / (float)K;
+  // Row staging. Loads are issued MM_SB float4 per thread before their LDS stores, so a
+  // batch costs one memory round trip; rows >= M are stored as zeros. For a single
+  // staged chunk (every K range here up to MM_KC columns) stage_issue runs before the
+  // first weight loads, so that waiting for the rows does not wait for the weights
+  // (vector loads complete in issue order), and the norm is applied while the weights
+  // are in flight.
+  const int kq_one = (kr1 - kr0) >> 2;
+  auto stage_issue = [&](int ka, int kq, int base, f32x4 (&v)[MM_SB], f32x4& gv, f32x4& bv) {
+    const int total = R * kq;
+#pragma unroll
+    for (int j = 0; j < MM_SB; ++j) {
+      const int i = min(base + 64 * NW * j, total - 1);
+      const int m = i / kq, k = (i - m * kq) << 2;
+      v[j] = *reinterpret_cast<const f32x4*>(p.x + (size_t)min(m, M - 1) * p.ldx + ka + k);
+    }
+    const float* gsrc = p.ng ? p.ng : p.x;
+    const float* bsrc = p.nb ? p.nb : gsrc;
+    const int kg = min(tid, kq - 1) << 2;
+    gv = *reinterpret_cast<const f32x4*>(gsrc + kg);
+    bv = *reinterpret_cast<const f32x4*>(bsrc + kg);
+  };
+  auto stage_store = [&](int kq, int base, const f32x4 (&v)[MM_SB]) {
+    const int total = R * kq;
+#pragma unroll
+    for (int j = 0; j < MM_SB; ++j) {
+      const int i = base + 64 * NW * j;
+      if (i < total) {
+        const int m = i / kq, k = (i - m * kq) << 2;
+        *reinterpret_cast<f32x4*>(xs + m * ldx + k) = m < M ? v[j] : (f32x4){0.f, 0.f, 0.f, 0.f};
       }
-      float v = 0.f;
-      for (int k = lane; k < K; k += 64) { float t = xr[k] - mean; v = fmaf(t, t, v); }
-      const float var = wave_sum(v) / (float)K;
-      if (lane == 0) { s_stat[2 * m] = mean; s_stat[2 * m + 1] = 1.0f / sqrtf(var + p.eps); }
+    }
+  };
+  // Row moments of rows [0, M) from LDS (the whole row is staged: K <= MM_KC) into
+  // s_stat: each wave takes rows wave, wave + NW, ..., two at a time, with all of a
+  // pair's LDS reads issued before the reductions.
+  auto row_moments = [&]() {
+    for (int m0 = wave; m0 < M; m0 += 2 * NW) {
+      f32x4 v[2][MM_KC / 256];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = min(m0 + h * NW, M - 1);
+#pragma unroll
+        for (int j = 0; j < MM_KC / 256; ++j) {
+          const int k = (lane + 64 * j) * 4;
+          v[h][j] = k < K ? *reinterpret_cast<const f32x4*>(xs + m * ldx + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float mean[2] = {0.f, 0.f}, var[2] = {0.f, 0.f};
+      if (p.norm == NORM_LN) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float t = 0.f;
+#pragma unroll
+          for (int j = 0; j < MM_KC / 256; ++j) t += (v[h][j].x + v[h][j].y) + (v[h][j].z + v[h][j].w);
+          mean[h] = t;
+        }
+        mean[0] = wave_sum(mean[0]) / (float)K;
+        mean[1] = wave_sum(mean[1]) / (float)K;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < MM_KC / 256; ++j) {
+          const int k = (lane + 64 * j) * 4;
+          if (k < K) {
+            const float d0 = v[h][j].x - mean[h], d1 = v[h][j].y - mean[h];
+            const float d2 = v[h][j].z - mean[h], d3 = v[h][j].w - mean[h];
+            var[h] += fmaf(d0, d0, d1 * d1) + fmaf(d2, d2, d3 * d3);
+          }
+        }
+      var[0] = wave_sum(var[0]) / (float)K;
+      var[1] = wave_sum(var[1]) / (float)K;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = m0 + h * NW;
+        if (lane == 0 && m < M) { s_stat[2 * m] = mean[h]; s_stat[2 * m + 1] = 1.0f / sqrtf(var[h] + p.eps); }
+      }
+    }
+  };
+  // Normalizes this thread's staged chunks (still in registers) and stores them.
+  auto normalize_store = [&](int kq, const f32x4 (&xv)[MM_SB]) {
+    const int total = R * kq;
+#pragma unroll
+    for (int j = 0; j < MM_SB; ++j) {
+      const int i = tid + 64 * NW * j;
+      if (i < total) {
+        const int m = i / kq, k = (i - m * kq) << 2;
+        if (m < M) {
+          const float u = s_stat[2 * m], r = s_stat[2 * m + 1];
+          const f32x4 g = *reinterpret_cast<const f32x4*>(s_g + k);
+          f32x4 x = xv[j];
+          if (p.norm == NORM_RMS) {
+            x.x *= r * g.x; x.y *= r * g.y; x.z *= r * g.z; x.w *= r * g.w;
+          } else {
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(s_g + MM_KC + k);
+            x.x = (x.x - u) * r * g.x + bb.x; x.y = (x.y - u) * r * g.y + bb.y;
+            x.z = (x.z - u) * r * g.z + bb.z; x.w = (x.w - u) * r * g.w + bb.w;
+          }
+          *reinterpret_cast<f32x4*>(xs + m * ldx + k) = x;
+        }
+      }
+    }
+  };
+  // General staging of columns [ka, kb) (any number of batches), used when the K range
+  // is staged in several chunks (no norm then).
+  auto stage = [&](int ka, int kb) {
+    const int kq = (kb - ka) >> 2;
+    for (int base = tid; base < R * kq; base += 64 * NW * MM_SB) {
+      f32x4 v[MM_SB], gv, bv;
+      stage_issue(ka, kq, base, v, gv, bv);
+      stage_store(kq, base, v);
     }
     __syncthreads();
-  }
-  f32x4 acc[MT];
+  };
+
+  // Loads this wave's weights of tile t for the blocks jb0 .. jb0 + MM_JB - 1 of its
+  // share of chunk [ka, kb): block index b = ka / 32 + wave + NW * j.
+  auto load = [&](W8<WT> (&w)[MM_JB], int t, int ka, int kb, int jb0) {
+    const int n = min(t * GD_TILE_N + c, N - 1);
+    const int bl = (kb - ka + 31) >> 5;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const int nb = (K + 31) >> 5;
-  for (int b = wave; b < nb; b += NW) {
-    const int kk = b * 32 + q * 8;
-    float w[8];
-    if (n < N && kk < K) load_w8<WT>(p.w, (size_t)n * K, kk, w);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = 0.f;
+    for (int j = 0; j < MM_JB; ++j) {
+      const int bj = min(wave + NW * (jb0 + j), bl - 1);    // clamped: unused blocks are skipped
+      const int kk = min(ka + bj * 32 + 8 * q, K - 8);
+      w[j] = load_w8raw<WT>(p.w, (size_t)n * K + kk);
     }
+  };
+
+  // rows (and norm parameters) first, then the first tile's weights; the rows are
+  // stored and normalized while the weights are in flight
+  W8<WT> w[MM_JB];
+  int t = blockIdx.x;
+  if (one_chunk) {
+    f32x4 xv[MM_SB], gv, bv;
+    stage_issue(kr0, kq_one, tid, xv, gv, bv);
+    // unconditional (clamped tile) so that the compiler can count the loads issued after
+    // the rows and wait for the rows alone
+    load(w, min(t, ntiles - 1), kr0, kr1, 0);
+    stage_store(kq_one, tid, xv);
+    if (p.norm != NORM_NONE && tid < kq_one) {
+      *reinterpret_cast<f32x4*>(s_g + 4 * tid) = gv;
+      *reinterpret_cast<f32x4*>(s_g + MM_KC + 4 * tid) = bv;
+    }
+    __syncthreads();
+    if (p.norm != NORM_NONE) {
+      row_moments();
+      __syncthreads();
+      normalize_store(kq_one, xv);
+      __syncthreads();
+    }
+  }
+  for (; t < ntiles; t += gridDim.x) {
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int ka = kr0; ka < kr1; ka += MM_KC) {
+      const int kb = min(kr1, ka + MM_KC);
+      if (!one_chunk) {
+        __syncthreads();
+        stage(ka, kb);
+        load(w, t, ka, kb, 0);
+      }
+      const int bl = (kb - ka + 31) >> 5;
+      const int nmine = bl > wave ? (bl - wave + NW - 1) / NW : 0;   // this wave's blocks
+      for (int jb0 = 0; jb0 < nmine; jb0 += MM_JB) {
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j) {
+          if (jb0 + j < nmine) {   // wave-uniform: MFMAs run with the whole wave
+            // column within the chunk; a lane past the chunk's end (K % 32 != 0)
+            // contributes zeros, read from a clamped in-range address
+            const int kloc = (wave + NW * (jb0 + j)) * 32 + 8 * q;
+            const bool ok = ka + kloc < kb;
+            const int kread = min(kloc, kb - ka - 8);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const float* xr = xs + (mt * 16 + c) * ldx + kread;
+              const f32x4 xa = *reinterpret_cast<const f32x4*>(xr);
+              const f32x4 xb = *reinterpret_cast<const f32x4*>(xr + 4);
+              float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+              for (int u = 0; u < 8; ++u) {
+                xv[u] = ok ? xv[u] : 0.f;
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u], w8_at<WT>(w[j], u), acc[mt], 0, 0, 0);
+              }
+            }
+          }
+        }
+        if (jb0 + MM_JB < nmine) load(w, t, ka, kb, jb0 + MM_JB);     // more blocks of this tile
+      }
+    }
+    // prefetch the next tile's first blocks (single staged chunk) before the reduction
+    if (one_chunk) load(w, min(t + (int)gridDim.x, ntiles - 1), kr0, kr1, 0);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + (lane & 15);
-      float xv[8];
-      if (m < M && kk < K) {
-        const float* xr = p.x + (size_t)m * p.ldx + kk;
-        f32x4 a = *reinterpret_cast<const f32x4*>(xr), c = *reinterpret_cast<const f32x4*>(xr + 4);
-        xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w; xv[4] = c.x; xv[5] = c.y; xv[6] = c.z; xv[7] = c.w;
-        if (norm) {
-          const float mu = s_stat[2 * m], r = s_stat[2 * m + 1];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            xv[i] = p.norm == NORM_RMS ? xv[i] * r * p.ng[kk + i] : (xv[i] - mu) * r * p.ng[kk + i] + p.nb[kk + i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xv[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i], w[i], acc[mt], 0, 0, 0);
+      float* rw = red + (wave * R + mt * 16 + 4 * q) * 17 + c;
+      rw[0] = acc[mt].x;
+      rw[17] = acc[mt].y;
+      rw[34] = acc[mt].z;
+      rw[51] = acc[mt].w;
     }
-  }
-  // D[i][j]: lane holds column j = lane % 16, rows i = 4q + v
+    __syncthreads();
+    for (int i = tid; i < M * GD_TILE_N; i += 64 * NW) {
+      const int m = i >> 4, cc = i & 15;
+      float v = red[m * 17 + cc];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    red[wave][mt * 16 + 4 * q + 0][lane & 15] = acc[mt].x;
-    red[wave][mt * 16 + 4 * q + 1][lane & 15] = acc[mt].y;
-    red[wave][mt * 16 + 4 * q + 2][lane & 15] = acc[mt].z;
-    red[wave][mt * 16 + 4 * q + 3][lane & 15] = acc[mt].w;
-  }
-  __syncthreads();
-  for (int i = tid; i < M * GD_TILE_N; i += 64 * NW) {
-    const int m = i >> 4, c = i & 15;
-    float s = red[0][m][c];
-#pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) s += red[w2][m][c];
-    tileT[m][c] = s;
-  }
-  __syncthreads();
-  switch (p.epi) {
-    case EPI_ARGMAX: mfma_argmax(p, tileT, n0, 64 * NW); break;
-    case EPI_PLAIN: mfma_epi<EPI_PLAIN>(p, tileT, n0, 64 * NW); break;
-    case EPI_GELU: mfma_epi<EPI_GELU>(p, tileT, n0, 64 * NW); break;
-    case EPI_SWIGLU: mfma_epi<EPI_SWIGLU>(p, tileT, n0, 64 * NW); break;
-    case EPI_QKV: mfma_epi<EPI_QKV>(p, tileT, n0, 64 * NW); break;
-    default: mfma_epi<EPI_QKV_ROPE>(p, tileT, n0, 64 * NW); break;
+      for (int w2 = 1; w2 < NW; ++w2) v += red[(w2 * R + m) * 17 + cc];
+      tt[m][cc] = v;
+    }
+    __syncthreads();
+    const int n0 = t * GD_TILE_N;
+    switch (p.epi) {
+      case EPI_ARGMAX: mm_argmax(p, tt, t, n0, 64 * NW); break;
+      case EPI_PLAIN: mm_epi<EPI_PLAIN>(p, tt, n0, 64 * NW, S, s); break;
+      case EPI_GELU: mm_epi<EPI_GELU>(p, tt, n0, 64 * NW, S, s); break;
+      case EPI_SWIGLU: mm_epi<EPI_SWIGLU>(p, tt, n0, 64 * NW, S, s); break;
+      case EPI_QKV: mm_epi<EPI_QKV>(p, tt, n0, 64 * NW, S, s); break;
+      default: mm_epi<EPI_QKV_ROPE>(p, tt, n0, 64 * NW, S, s); break;
+    }
+    __syncthreads();   // tt and red are reused by the next tile
   }
 }
 

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -54,15 +55,17 @@ static int iceil(int a, int b) { return (a + b - 1) / b; }
 //
 // var 0: k_gemv, VALU dot products with the weight rows held in registers; at most
 //        GEMV_MAX_ROWS activation rows per launch (more rows run as several launches).
-// var 1: k_mfma, 16-column tiles on the fp32 matrix cores; 1..32 rows per launch.
+// var 1: k_mm, 16-column tiles on the fp32 matrix cores; 1..32 rows per launch.
 
 struct LinPlan {
-  int var;     // 0 gemv, 1 mfma
+  int var;     // 0 gemv, 1 mm
   int nc, rw;  // gemv: 16-byte weight chunks per lane and row, weight rows per wave
-  int mt, nw;  // mfma: 16-row activation tiles, waves per workgroup
+  int mt, nw;  // mm: 16-row activation tiles, waves per workgroup
+  int splits;  // mm: K splits (grid.y), > 1 only for in-place residual outputs
   int rows;    // activation rows per launch
   int grid;
-  size_t lds;  // dynamic LDS bytes (gemv)
+  int parts;   // argmax partials per row (gemv: workgroups; mm: column tiles)
+  size_t lds;  // dynamic LDS bytes
 };
 
 static const int kNcChoices[] = {1, 2, 3, 4, 6, 8, 12};
@@ -85,28 +88,41 @@ static int gemv_rows_per_wave(int epi, int N) {
 }
 
 static const size_t kGemvLdsMax = 64 * 1024;
+static const int kMmTargetWgs = 256;   // one matrix-core workgroup per CU
 
-static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bool norm) {
+// splittable: linear epilogue whose output is the residual, updated in place (the
+// K splits are then summed with atomics into it).
+static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bool norm, bool splittable = false) {
   LinPlan p;
   memset(&p, 0, sizeof(p));
   p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= GEMV_MAX_ROWS ? 0 : 1);
   p.nc = gemv_nc(K, wt);
-  if (p.nc < 0) p.var = 1;
+  if (p.var == 1 && norm && K > MM_KC) p.var = 0;   // the norm needs whole rows in LDS
+  if (p.var == 0 && p.nc < 0) p.var = 1;
   if (p.var == 0) {
     p.rw = gemv_rows_per_wave(epi, N);
     p.rows = std::min(M, GEMV_MAX_ROWS);
     p.grid = iceil(N, 4 * p.rw);
+    p.parts = p.grid;
     // rows, then the norm's gain and shift
     const size_t xs = ((size_t)p.rows * K + 3) & ~(size_t)3;
     p.lds = (xs + (norm ? 2 * (size_t)K : 0)) * sizeof(float);
-    if (p.lds > kGemvLdsMax) p.var = 1;   // rows too long to stage: matrix-core path
+    if (p.lds > kGemvLdsMax && !(norm && K > MM_KC)) p.var = 1;   // rows too long to stage
   }
   if (p.var == 1) {
+    const int ntiles = iceil(N, GD_TILE_N), nb = iceil(K, 32);
     p.mt = M <= 16 ? 1 : 2;
-    p.nw = K <= 1024 ? 4 : 8;
+    p.nw = 8;
     p.rows = M;
-    p.grid = iceil(N, GD_TILE_N);
-    p.lds = 0;
+    p.splits = 1;
+    // split K only as far as one workgroup per CU allows (a second round of workgroups
+    // would double the kernel's time)
+    if (splittable && !norm && epi == EPI_PLAIN) p.splits = std::max(1, std::min(nb, kMmTargetWgs / ntiles));
+    // the head streams many tiles per workgroup (rows staged once); others one tile each
+    p.grid = epi == EPI_ARGMAX ? std::min(ntiles, kMmTargetWgs) : ntiles;
+    p.parts = ntiles;
+    const int kl = std::min(iceil(nb, p.splits) * 32, MM_KC);
+    p.lds = (size_t)mm_lds_floats(p.mt, p.nw, kl) * sizeof(float);
   }
   return p;
 }
@@ -141,12 +157,30 @@ static void launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st)
 }
 
 template <int WT>
-static void launch_mfma(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
-  dim3 g(lp.grid);
-  if (lp.mt == 1 && lp.nw == 4) hipLaunchKernelGGL((k_mfma<WT, 1, 4>), g, dim3(64 * 4), 0, st, prm);
-  else if (lp.mt == 1) hipLaunchKernelGGL((k_mfma<WT, 1, 8>), g, dim3(64 * 8), 0, st, prm);
-  else if (lp.nw == 4) hipLaunchKernelGGL((k_mfma<WT, 2, 4>), g, dim3(64 * 4), 0, st, prm);
-  else hipLaunchKernelGGL((k_mfma<WT, 2, 8>), g, dim3(64 * 8), 0, st, prm);
+static void launch_mm(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+  const dim3 g(lp.grid, lp.splits), b(64 * 8);
+  if (lp.mt == 1) hipLaunchKernelGGL((k_mm<WT, 1, 8>), g, b, lp.lds, st, prm);
+  else hipLaunchKernelGGL((k_mm<WT, 2, 8>), g, b, lp.lds, st, prm);
+}
+
+// Lets the matrix-core kernels use more than the default 64 KB of dynamic LDS (once per
+// process).
+static hipError_t mm_allow_lds() {
+  const int bytes = mm_lds_floats(2, 8, MM_KC) * (int)sizeof(float);
+  const void* fns[] = {(const void*)k_mm<0, 1, 8>, (const void*)k_mm<0, 2, 8>, (const void*)k_mm<1, 1, 8>,
+                       (const void*)k_mm<1, 2, 8>};
+  for (const void* f : fns) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static hipError_t mm_allow_lds_once() {
+  static std::once_flag once;
+  static hipError_t result = hipSuccess;
+  std::call_once(once, [] { result = mm_allow_lds(); });
+  return result;
 }
 
 // One launch of one plan over prm.M rows (prm.M <= lp.rows).
@@ -155,8 +189,8 @@ static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm,
     if (wt == GD_WEIGHT_F32) launch_gemv<0>(lp, prm, st);
     else launch_gemv<1>(lp, prm, st);
   } else {
-    if (wt == GD_WEIGHT_F32) launch_mfma<0>(lp, prm, st);
-    else launch_mfma<1>(lp, prm, st);
+    if (wt == GD_WEIGHT_F32) launch_mm<0>(lp, prm, st);
+    else launch_mm<1>(lp, prm, st);
   }
   return hipGetLastError();
 }
@@ -180,7 +214,7 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
     hipError_t e = launch_linear(wt, lp, p, st);
     if (e != hipSuccess) return e;
     if (p.epi == EPI_ARGMAX) {
-      hipLaunchKernelGGL(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.grid, p.M,
+      hipLaunchKernelGGL(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.parts, p.M,
                          am_out + r0);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -275,6 +309,7 @@ static gd_status check_cfg(const gd_config* c) {
   if (c->arch == GD_ARCH_GPT2 && (c->n_kv_head != c->n_head || c->n_head * c->head_dim != c->d_model))
     return set_err(GD_ERR_INVALID, "GPT-2 arch needs n_kv_head == n_head and n_head*head_dim == d_model");
   if (c->n_head % c->n_kv_head) return set_err(GD_ERR_INVALID, "n_head must be a multiple of n_kv_head");
+  if (c->n_head > GD_MAX_HEADS) return set_err(GD_ERR_INVALID, "at most %d query heads", GD_MAX_HEADS);
   int G = c->n_head / c->n_kv_head;
   if (G != 1 && G != 3) return set_err(GD_ERR_INVALID, "query heads per KV head must be 1 or 3");
   if ((c->n_head * c->head_dim) % 8) return set_err(GD_ERR_INVALID, "n_head*head_dim must be a multiple of 8");
@@ -342,7 +377,7 @@ static void layout(gd_model* m) {
   m->am_parts = 0;
   for (int v = 1; v <= 2; ++v)
     for (int M = 1; M <= GD_MAX_ROWS; ++M)
-      m->am_parts = std::max(m->am_parts, (size_t)plan_linear(M, c.vocab, c.d_model, m->wt, v, EPI_ARGMAX, true).grid);
+      m->am_parts = std::max(m->am_parts, (size_t)plan_linear(M, c.vocab, c.d_model, m->wt, v, EPI_ARGMAX, true).parts);
 
   // scratch
   off = 0;
@@ -388,6 +423,7 @@ extern "C" gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model*
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return set_err(GD_ERR_NO_DEVICE, "no device properties");
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return set_err(GD_ERR_NO_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  if (mm_allow_lds_once() != hipSuccess) return set_err(GD_ERR_HIP, "could not raise the LDS limit of k_mm");
   gd_model* m = new gd_model();
   m->c = *cfg;
   m->dev = dev;
@@ -743,7 +779,7 @@ struct ProfScope {
 static const char* linear_kernel_name(int wt, const LinPlan& lp, char* buf, size_t n) {
   const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
   if (lp.var == 0) snprintf(buf, n, "k_gemv<%d, %d, %d>", w, lp.nc, lp.rw);
-  else snprintf(buf, n, "k_mfma<%d, %d, %d>", w, lp.mt, lp.nw);
+  else snprintf(buf, n, "k_mm<%d, %d, %d>", w, lp.mt, lp.nw);
   return buf;
 }
 
@@ -762,7 +798,8 @@ static double linear_bytes(const gd_model* m, const LinParams& p) {
 // Launches one linear layer (profiled when enabled).
 static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, const LinParams& p,
                              int* am_out = nullptr) {
-  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE);
+  const bool inplace = p.resid == p.y && p.ldr == p.ldy;
+  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE, inplace);
   char kn[64];
   ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, kn, sizeof(kn)), m->profile ? linear_bytes(m, p) : 0);
   return run_linear_rows(m->wt, lp, p, st, am_out);
@@ -1112,7 +1149,9 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
   p.resid = resid ? resid : zero;
   p.ldr = resid ? ldr : 0;
   p.y = y; p.ldy = ldy;
-  LinPlan lp = plan_linear(M, N, K, wdt, variant, p.epi, p.norm != NORM_NONE);
+  const bool inplace = resid && resid == y && ldr == ldy;
+  LinPlan lp = plan_linear(M, N, K, wdt, variant, p.epi, p.norm != NORM_NONE, inplace);
+  if (mm_allow_lds_once() != hipSuccess) return set_err(GD_ERR_HIP, "could not raise the LDS limit of k_mm");
   hipError_t e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
   return GD_OK;
