@@ -5,9 +5,11 @@
 // little arithmetic per byte, so both kernels are built around streaming W with
 // 16-byte loads issued before anything that depends on the activations.
 //
-// Cross-workgroup communication happens only at kernel boundaries: an agent-scope
-// fence costs tens of nanoseconds per workgroup and serializes, so no split-K or
-// last-arriver reductions are used here.
+// No workgroup waits for another inside a launch: an agent-scope release costs tens
+// of microseconds per launch here (each workgroup's release writes back its XCD's
+// L2), so there are no last-arriver reductions. The only cross-workgroup sums are
+// the matrix-core kernel's split-K float atomics into an in-place residual, which
+// only the next launch reads.
 //
 // k_gemv (1..4 rows, VALU): each wave owns RW weight rows; lane l holds chunks
 //   c = l + 64 i (16 bytes each: 4 fp32 or 8 bf16 weights) of each row in registers,
@@ -15,8 +17,8 @@
 //   prologue (a copy or, for the first layer, the token + position embedding, or
 //   the merge of split-context attention partials), then LayerNorm or RMSNorm of
 //   each row. Dot products are reduced across the wave.
-// k_mm (5..32 rows): fp32 matrix-core tiles of 16 columns over activation rows staged
-//   in LDS; see the MFMA section below.
+// k_mm (5..32 rows): fp32 matrix-core tiles of 16 columns, activation rows held in
+//   registers in the MFMA operand layout; see the MFMA section below.
 //
 // Epilogues: bias, clamped tanh-GELU, residual add; SiLU-gated pairs (gate and up
 // rows interleaved, gate at even rows); QKV scatter (q to a buffer, k and v into the
@@ -466,25 +468,31 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
 //
 // k_mm (1..32 rows): 16-column tiles on v_mfma_f32_16x16x4f32 (bf16 weights widened
 // to fp32 in registers). Grid (G, S): workgroup (g, s) owns the 32-column K blocks
-// [s nb / S, (s + 1) nb / S) and the column tiles g, g + G, g + 2G, ...
+// [s nb / S, (s + 1) nb / S) and the column tiles g, g + G, g + 2G, ...; S > 1 only for
+// a linear epilogue whose output is the residual, updated in place: each split adds
+// its partial sums to it with float atomics, the bias coming from split 0.
 //
-// The activation rows of the workgroup's K range are staged into LDS once (row stride
-// kl + 4 floats, so the 16 rows one instruction reads fall in different banks) and,
-// when the layer has a pre-norm (S == 1, the norm needs whole rows), normalized there.
-// Each of the NW waves takes every NW-th block; all of its weight loads for a tile are
-// issued before its MFMAs, and the loads of the next tile before the current tile's
-// reduction and epilogue. Waves are summed in LDS. With S > 1 (linear epilogue whose
-// output is the residual, updated in place) each split adds its partial sums to the
-// output with float atomics, the bias coming from split 0.
+// Nothing is staged in LDS. A pass covers up to MM_NW * MM_JB blocks: block
+// b = pass start + wave + MM_NW j is held by the wave in register slot j, for the
+// activation rows (loaded once per pass, so once per launch when the K range fits one
+// pass) and for the weights of the current tile. Load order per lane: rows, the
+// norm's shift values, gain and shift, the tile's weights, the tile's epilogue
+// operands; the row moments and the normalization (in registers, one cross-wave
+// exchange in LDS) run while the weights are in flight. After a tile's MFMAs the
+// next tile's weights are issued, then the waves' partial tiles are summed through a
+// double-buffered LDS array (one barrier per tile) and each thread applies the
+// epilogue to its own output (row tid / 16, column tid % 16). The head's argmax keeps
+// a running best per output thread across tiles and writes one partial per
+// workgroup and row.
 //
 // Operand layout: lane l holds W[n0 + l%16][kk + 8(l/16) .. +8] and X[m0 + l%16][same];
 // MFMA step t of 8 feeds element t of both, so one instruction contracts the k-values
 // kk + 8q + t (q = l/16) for A and B alike. D[i][j]: lane l holds column j = l%16 and
 // rows 4(l/16) + v.
 
-#define MM_JB 4        // blocks per wave and tile held in registers
-#define MM_KC 1024     // widest K range staged at once (columns)
-#define MM_SB 16       // float4 row loads in flight per thread while staging
+#define MM_NW 8                       // waves per workgroup
+#define MM_JB 4                       // K blocks per wave and pass held in registers
+#define MM_KC (MM_NW * MM_JB * 32)    // K columns per pass
 
 template <int WT> struct W8;   // eight consecutive weights of one row, as stored
 template <> struct W8<0> { f32x4 a, b; };
@@ -516,300 +524,241 @@ __device__ __forceinline__ float w8_at(const W8<WT>& r, int t) {
   }
 }
 
-typedef float TileT[GD_MAX_ROWS][GD_TILE_N + 1];
+struct F8 { f32x4 a, b; };   // eight consecutive fp32 values
 
-// Epilogue of one reduced 16-column tile (all rows), by the whole workgroup.
-template <int EPI>
-__device__ void mm_epi(const LinParams& p, const TileT& tt, int n0, int nthr, int S, int s) {
-  const int tid = threadIdx.x;
-  if (EpiTraits<EPI>::pair) {
-    for (int i = tid; i < p.M * (GD_TILE_N / 2); i += nthr) {
-      const int m = i >> 3, c = (i & 7) * 2;
-      if (n0 + c + 1 < p.N) {
-        const EpiOps e = epi_prefetch<EPI>(p, m, n0 + c);
-        epi_store<EPI>(p, e, m, n0 + c, tt[m][c], tt[m][c + 1]);
-      }
-    }
-  } else {
-    for (int i = tid; i < p.M * GD_TILE_N; i += nthr) {
-      const int m = i >> 4, c = i & 15;
-      if (n0 + c < p.N) {
-        if (EPI == EPI_PLAIN && S > 1) {
-          // split-K: the output already holds the residual; add this split's share
-          const float v = tt[m][c] + (s == 0 ? p.bias[n0 + c] : 0.f);
-          __hip_atomic_fetch_add(p.y + (size_t)m * p.ldy + n0 + c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          const EpiOps e = epi_prefetch<EPI>(p, m, n0 + c);
-          epi_store<EPI>(p, e, m, n0 + c, tt[m][c], 0.f);
-        }
-      }
-    }
-  }
+__device__ __forceinline__ F8 load_f8(const float* p) {
+  F8 r;
+  r.a = *reinterpret_cast<const f32x4*>(p);
+  r.b = *reinterpret_cast<const f32x4*>(p + 4);
+  return r;
 }
 
-__device__ void mm_argmax(const LinParams& p, const TileT& tt, int t, int n0, int nthr) {
-  const int tid = threadIdx.x;
-  if (p.logits)
-    for (int i = tid; i < p.M * GD_TILE_N; i += nthr) {
-      const int m = i >> 4, c = i & 15;
-      if (n0 + c < p.N) p.logits[(size_t)m * p.ldl + n0 + c] = tt[m][c];
-    }
-  if (tid < p.M) {
-    float bv = tt[tid][0];
-    int bi = n0;
-    for (int c = 1; c < GD_TILE_N && n0 + c < p.N; ++c)
-      if (am_better(tt[tid][c], n0 + c, bv, bi)) { bv = tt[tid][c]; bi = n0 + c; }
-    p.am_val[(size_t)t * p.M + tid] = bv;
-    p.am_idx[(size_t)t * p.M + tid] = bi;
-  }
+__device__ __forceinline__ float f8_at(const F8& r, int t) {
+  const f32x4 v = t < 4 ? r.a : r.b;
+  const int u = t & 3;
+  return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
 }
 
-// Dynamic LDS floats of k_mm for a K range of kl columns (<= MM_KC).
-__host__ __device__ constexpr int mm_lds_floats(int MT, int NW, int kl) {
-  return MT * 16 * (kl + 4) + NW * MT * 16 * 17 + GD_MAX_ROWS * (GD_TILE_N + 1) + 2 * MT * 16 + 2 * MM_KC;
+__device__ __forceinline__ void f8_set(F8& r, int t, float x) {
+  f32x4& v = t < 4 ? r.a : r.b;
+  const int u = t & 3;
+  if (u == 0) v.x = x; else if (u == 1) v.y = x; else if (u == 2) v.z = x; else v.w = x;
 }
 
-template <int WT, int MT, int NW>
-__global__ __launch_bounds__(64 * NW) void k_mm(LinParams p) {
-  constexpr int R = MT * 16;
-  static_assert(R * (MM_KC / 4) <= 64 * NW * MM_SB, "one staging batch covers a whole chunk");
-  extern __shared__ __align__(16) float smem[];
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// Keeps the loads that produced v in flight no longer than this point: the compiler
+// waits for them here (where they have long arrived) rather than at their use, which
+// may follow loads issued later under a condition.
+__device__ __forceinline__ void settle(float v) { asm volatile("" ::"v"(v)); }
+
+// NRM: the rows are normalized (LayerNorm or RMSNorm by p.norm; S == 1, one pass).
+// MP: the K range of a split may exceed one pass (no norm): rows and weights are then
+// loaded per pass and tile. Without MP every load is unconditional, so the compiler's
+// wait counts stay exact and nothing waits for the next tile's weights.
+template <int WT, int MT, int EPI, bool NRM, bool MP>
+__global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
+  static_assert(!(NRM && MP), "the norm needs whole rows in one pass");
+  constexpr int R = MT * 16;          // activation rows of the tile (rows >= M are padding)
+  constexpr int RS = 17;              // padded row stride of a partial tile in LDS
+  constexpr bool PAIR = EpiTraits<EPI>::pair;
+  __shared__ float s_red[2][MM_NW * R * RS];
+  __shared__ float s_part[MM_NW][R][2];
+  __shared__ float s_mr[R][2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, c = lane & 15;
   const int M = p.M, N = p.N, K = p.K;
-  const int S = gridDim.y, s = blockIdx.y;
+  const int S = gridDim.y, s = blockIdx.y, G = gridDim.x;
   const int nb = (K + 31) >> 5;
   const int b0 = (int)((long long)s * nb / S), b1 = (int)((long long)(s + 1) * nb / S);
-  const int kr0 = b0 * 32, kr1 = min(K, b1 * 32);
   const int ntiles = (N + GD_TILE_N - 1) / GD_TILE_N;
-  const int q = lane >> 4, c = lane & 15;
-  const int kl_max = min(kr1 - kr0, MM_KC);
-  const int ldx = kl_max + 4;
-  float* xs = smem;                                   // [R][ldx]
-  float* red = xs + R * ldx;                          // [NW][R][17]
-  TileT& tt = *reinterpret_cast<TileT*>(red + NW * R * 17);
-  float* s_stat = red + NW * R * 17 + GD_MAX_ROWS * (GD_TILE_N + 1);  // [R][2]
-  float* s_g = s_stat + 2 * R;                        // norm gain [MM_KC], then shift [MM_KC]
-  const bool one_chunk = kr1 - kr0 <= MM_KC;
+  // this thread's output in the epilogue (threads >= R * 16 own none)
+  const int om = tid >> 4, oc = tid & 15;
+  const bool orow = tid < R * 16 && om < M;
 
-  // Row staging. Loads are issued MM_SB float4 per thread before their LDS stores, so a
-  // batch costs one memory round trip; rows >= M are stored as zeros. For a single
-  // staged chunk (every K range here up to MM_KC columns) stage_issue runs before the
-  // first weight loads, so that waiting for the rows does not wait for the weights
-  // (vector loads complete in issue order), and the norm is applied while the weights
-  // are in flight.
-  const int kq_one = (kr1 - kr0) >> 2;
-  auto stage_issue = [&](int ka, int kq, int base, f32x4 (&v)[MM_SB], f32x4& gv, f32x4& bv) {
-    const int total = R * kq;
-#pragma unroll
-    for (int j = 0; j < MM_SB; ++j) {
-      const int i = min(base + 64 * NW * j, total - 1);
-      const int m = i / kq, k = (i - m * kq) << 2;
-      v[j] = *reinterpret_cast<const f32x4*>(p.x + (size_t)min(m, M - 1) * p.ldx + ka + k);
-    }
-    const float* gsrc = p.ng ? p.ng : p.x;
-    const float* bsrc = p.nb ? p.nb : gsrc;
-    const int kg = min(tid, kq - 1) << 2;
-    gv = *reinterpret_cast<const f32x4*>(gsrc + kg);
-    bv = *reinterpret_cast<const f32x4*>(bsrc + kg);
-  };
-  auto stage_store = [&](int kq, int base, const f32x4 (&v)[MM_SB]) {
-    const int total = R * kq;
-#pragma unroll
-    for (int j = 0; j < MM_SB; ++j) {
-      const int i = base + 64 * NW * j;
-      if (i < total) {
-        const int m = i / kq, k = (i - m * kq) << 2;
-        *reinterpret_cast<f32x4*>(xs + m * ldx + k) = m < M ? v[j] : (f32x4){0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-  // Row moments of rows [0, M) from LDS (the whole row is staged: K <= MM_KC) into
-  // s_stat: each wave takes rows wave, wave + NW, ..., two at a time, with all of a
-  // pair's LDS reads issued before the reductions.
-  auto row_moments = [&]() {
-    for (int m0 = wave; m0 < M; m0 += 2 * NW) {
-      f32x4 v[2][MM_KC / 256];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int m = min(m0 + h * NW, M - 1);
-#pragma unroll
-        for (int j = 0; j < MM_KC / 256; ++j) {
-          const int k = (lane + 64 * j) * 4;
-          v[h][j] = k < K ? *reinterpret_cast<const f32x4*>(xs + m * ldx + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
-      }
-      float mean[2] = {0.f, 0.f}, var[2] = {0.f, 0.f};
-      if (p.norm == NORM_LN) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float t = 0.f;
-#pragma unroll
-          for (int j = 0; j < MM_KC / 256; ++j) t += (v[h][j].x + v[h][j].y) + (v[h][j].z + v[h][j].w);
-          mean[h] = t;
-        }
-        mean[0] = wave_sum(mean[0]) / (float)K;
-        mean[1] = wave_sum(mean[1]) / (float)K;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < MM_KC / 256; ++j) {
-          const int k = (lane + 64 * j) * 4;
-          if (k < K) {
-            const float d0 = v[h][j].x - mean[h], d1 = v[h][j].y - mean[h];
-            const float d2 = v[h][j].z - mean[h], d3 = v[h][j].w - mean[h];
-            var[h] += fmaf(d0, d0, d1 * d1) + fmaf(d2, d2, d3 * d3);
-          }
-        }
-      var[0] = wave_sum(var[0]) / (float)K;
-      var[1] = wave_sum(var[1]) / (float)K;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int m = m0 + h * NW;
-        if (lane == 0 && m < M) { s_stat[2 * m] = mean[h]; s_stat[2 * m + 1] = 1.0f / sqrtf(var[h] + p.eps); }
-      }
-    }
-  };
-  // Normalizes this thread's staged chunks (still in registers) and stores them.
-  auto normalize_store = [&](int kq, const f32x4 (&xv)[MM_SB]) {
-    const int total = R * kq;
-#pragma unroll
-    for (int j = 0; j < MM_SB; ++j) {
-      const int i = tid + 64 * NW * j;
-      if (i < total) {
-        const int m = i / kq, k = (i - m * kq) << 2;
-        if (m < M) {
-          const float u = s_stat[2 * m], r = s_stat[2 * m + 1];
-          const f32x4 g = *reinterpret_cast<const f32x4*>(s_g + k);
-          f32x4 x = xv[j];
-          if (p.norm == NORM_RMS) {
-            x.x *= r * g.x; x.y *= r * g.y; x.z *= r * g.z; x.w *= r * g.w;
-          } else {
-            const f32x4 bb = *reinterpret_cast<const f32x4*>(s_g + MM_KC + k);
-            x.x = (x.x - u) * r * g.x + bb.x; x.y = (x.y - u) * r * g.y + bb.y;
-            x.z = (x.z - u) * r * g.z + bb.z; x.w = (x.w - u) * r * g.w + bb.w;
-          }
-          *reinterpret_cast<f32x4*>(xs + m * ldx + k) = x;
-        }
-      }
-    }
-  };
-  // General staging of columns [ka, kb) (any number of batches), used when the K range
-  // is staged in several chunks (no norm then).
-  auto stage = [&](int ka, int kb) {
-    const int kq = (kb - ka) >> 2;
-    for (int base = tid; base < R * kq; base += 64 * NW * MM_SB) {
-      f32x4 v[MM_SB], gv, bv;
-      stage_issue(ka, kq, base, v, gv, bv);
-      stage_store(kq, base, v);
-    }
-    __syncthreads();
-  };
-
-  // Loads this wave's weights of tile t for the blocks jb0 .. jb0 + MM_JB - 1 of its
-  // share of chunk [ka, kb): block index b = ka / 32 + wave + NW * j.
-  auto load = [&](W8<WT> (&w)[MM_JB], int t, int ka, int kb, int jb0) {
-    const int n = min(t * GD_TILE_N + c, N - 1);
-    const int bl = (kb - ka + 31) >> 5;
+  // block held in slot j of the pass starting at cb (clamped: unused slots are skipped)
+  auto slot_block = [&](int cb, int ce, int j) { return min(cb + wave + MM_NW * j, ce - 1); };
+  auto slot_k = [&](int blk) { return min(blk * 32 + 8 * q, K - 8); };
+  auto load_x = [&](F8 (&xr)[MM_JB][MT], int cb, int ce) {
 #pragma unroll
     for (int j = 0; j < MM_JB; ++j) {
-      const int bj = min(wave + NW * (jb0 + j), bl - 1);    // clamped: unused blocks are skipped
-      const int kk = min(ka + bj * 32 + 8 * q, K - 8);
-      w[j] = load_w8raw<WT>(p.w, (size_t)n * K + kk);
+      const int k = slot_k(slot_block(cb, ce, j));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xr[j][mt] = load_f8(p.x + (size_t)min(mt * 16 + c, M - 1) * p.ldx + k);
     }
   };
+  auto load_w = [&](W8<WT> (&w)[MM_JB], int t, int cb, int ce) {
+    const int n = min(t * GD_TILE_N + c, N - 1);
+#pragma unroll
+    for (int j = 0; j < MM_JB; ++j) w[j] = load_w8raw<WT>(p.w, (size_t)n * K + slot_k(slot_block(cb, ce, j)));
+  };
 
-  // rows (and norm parameters) first, then the first tile's weights; the rows are
-  // stored and normalized while the weights are in flight
+  // ---- loads: rows, norm parameters, first tile's weights (one pass)
+  F8 xr[MM_JB][MT];
   W8<WT> w[MM_JB];
   int t = blockIdx.x;
-  if (one_chunk) {
-    f32x4 xv[MM_SB], gv, bv;
-    stage_issue(kr0, kq_one, tid, xv, gv, bv);
-    // unconditional (clamped tile) so that the compiler can count the loads issued after
-    // the rows and wait for the rows alone
-    load(w, min(t, ntiles - 1), kr0, kr1, 0);
-    stage_store(kq_one, tid, xv);
-    if (p.norm != NORM_NONE && tid < kq_one) {
-      *reinterpret_cast<f32x4*>(s_g + 4 * tid) = gv;
-      *reinterpret_cast<f32x4*>(s_g + MM_KC + 4 * tid) = bv;
-    }
-    __syncthreads();
-    if (p.norm != NORM_NONE) {
-      row_moments();
+  if constexpr (!MP) {
+    load_x(xr, b0, b1);
+    if (NRM) {
+      const bool ln = p.norm == NORM_LN;
+      float x0[MT];   // shift of each row's moments: its first element
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) x0[mt] = p.x[(size_t)min(mt * 16 + c, M - 1) * p.ldx];
+      const float* bsrc = ln ? p.nb : p.ng;
+      F8 gg[MM_JB], bb[MM_JB];
+#pragma unroll
+      for (int j = 0; j < MM_JB; ++j) {
+        const int k = slot_k(slot_block(b0, b1, j));
+        gg[j] = load_f8(p.ng + k);
+        bb[j] = load_f8(bsrc + k);
+      }
+      load_w(w, t, b0, b1);
+      // ---- row moments from registers (shifted sums; RMSNorm: plain sum of squares)
+      float s1[MT], s2[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        s1[mt] = s2[mt] = 0.f;
+        const float sh = ln ? x0[mt] : 0.f;
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j) {
+          const int blk = b0 + wave + MM_NW * j;
+          const float okf = (blk < b1 && blk * 32 + 8 * q < K) ? 1.f : 0.f;   // clamped duplicates count 0
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float d = (f8_at(xr[j][mt], u) - sh) * okf;
+            s1[mt] += d;
+            s2[mt] = fmaf(d, d, s2[mt]);
+          }
+        }
+        s1[mt] += __shfl_xor(s1[mt], 16);
+        s1[mt] += __shfl_xor(s1[mt], 32);
+        s2[mt] += __shfl_xor(s2[mt], 16);
+        s2[mt] += __shfl_xor(s2[mt], 32);
+        if (q == 0) {
+          s_part[wave][mt * 16 + c][0] = s1[mt];
+          s_part[wave][mt * 16 + c][1] = s2[mt];
+        }
+      }
       __syncthreads();
-      normalize_store(kq_one, xv);
+      if (tid < R) {   // row tid = 16 q + c, shift x0[q]
+        float a = 0.f, a2 = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < MM_NW; ++w2) { a += s_part[w2][tid][0]; a2 += s_part[w2][tid][1]; }
+        const float sh = ln ? (q == 0 ? x0[0] : x0[MT - 1]) : 0.f;
+        const float md = a / (float)K;   // mean of the shifted values
+        const float var = ln ? fmaxf(a2 / (float)K - md * md, 0.f) : a2 / (float)K;
+        s_mr[tid][0] = ln ? sh + md : 0.f;
+        s_mr[tid][1] = 1.0f / sqrtf(var + p.eps);
+      }
       __syncthreads();
+      const float bsel = ln ? 1.f : 0.f;   // RMSNorm: no shift (and mu = 0)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float mu = s_mr[mt * 16 + c][0], r = s_mr[mt * 16 + c][1];
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            f8_set(xr[j][mt], u, (f8_at(xr[j][mt], u) - mu) * r * f8_at(gg[j], u) + bsel * f8_at(bb[j], u));
+      }
+    } else {
+      load_w(w, t, b0, b1);
     }
   }
-  for (; t < ntiles; t += gridDim.x) {
+
+  float bv = -INFINITY;   // argmax: running best of this thread's columns
+  int bi = 0x7fffffff;
+  for (int it = 0; t < ntiles; t += G, ++it) {
+    // epilogue operands of this thread's output(s) of the tile
+    const int n = t * GD_TILE_N + oc;
+    const bool own = orow && (PAIR ? n + 1 < N : n < N);
+    const EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? n : 0);
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int ka = kr0; ka < kr1; ka += MM_KC) {
-      const int kb = min(kr1, ka + MM_KC);
-      if (!one_chunk) {
-        __syncthreads();
-        stage(ka, kb);
-        load(w, t, ka, kb, 0);
+    for (int cb = b0; cb < b1; cb += MM_NW * MM_JB) {
+      const int ce = min(b1, cb + MM_NW * MM_JB);
+      if constexpr (MP) {
+        load_x(xr, cb, ce);
+        load_w(w, t, cb, ce);
       }
-      const int bl = (kb - ka + 31) >> 5;
-      const int nmine = bl > wave ? (bl - wave + NW - 1) / NW : 0;   // this wave's blocks
-      for (int jb0 = 0; jb0 < nmine; jb0 += MM_JB) {
 #pragma unroll
-        for (int j = 0; j < MM_JB; ++j) {
-          if (jb0 + j < nmine) {   // wave-uniform: MFMAs run with the whole wave
-            // column within the chunk; a lane past the chunk's end (K % 32 != 0)
-            // contributes zeros, read from a clamped in-range address
-            const int kloc = (wave + NW * (jb0 + j)) * 32 + 8 * q;
-            const bool ok = ka + kloc < kb;
-            const int kread = min(kloc, kb - ka - 8);
+      for (int j = 0; j < MM_JB; ++j) {
+        const int blk = cb + wave + MM_NW * j;
+        if (blk < ce) {   // wave-uniform: MFMAs run with the whole wave
+          // a lane past K (K % 32 != 0) holds a clamped duplicate: contribute zeros
+          const bool ok = blk * 32 + 8 * q < K;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const float* xr = xs + (mt * 16 + c) * ldx + kread;
-              const f32x4 xa = *reinterpret_cast<const f32x4*>(xr);
-              const f32x4 xb = *reinterpret_cast<const f32x4*>(xr + 4);
-              float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int u = 0; u < 8; ++u) {
-                xv[u] = ok ? xv[u] : 0.f;
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u], w8_at<WT>(w[j], u), acc[mt], 0, 0, 0);
-              }
-            }
-          }
+            for (int u = 0; u < 8; ++u)
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? f8_at(xr[j][mt], u) : 0.f, w8_at<WT>(w[j], u),
+                                                            acc[mt], 0, 0, 0);
         }
-        if (jb0 + MM_JB < nmine) load(w, t, ka, kb, jb0 + MM_JB);     // more blocks of this tile
       }
     }
-    // prefetch the next tile's first blocks (single staged chunk) before the reduction
-    if (one_chunk) load(w, min(t + (int)gridDim.x, ntiles - 1), kr0, kr1, 0);
+    settle(eo.b0); settle(eo.b1); settle(eo.r0); settle(eo.c); settle(eo.s);
+    settle(__int_as_float((int)eo.kvoff)); settle(__int_as_float((int)(eo.kvoff >> 32)));
+    // the next tile's weights stream while this tile is reduced and stored; after the
+    // last tile every lane reads the same 32 bytes instead (an unconditional load)
+    if constexpr (!MP) {
+      const bool more = t + G < ntiles;
+      const int n = min((t + G) * GD_TILE_N + c, N - 1);
+#pragma unroll
+      for (int j = 0; j < MM_JB; ++j)
+        w[j] = load_w8raw<WT>(p.w, more ? (size_t)n * K + slot_k(slot_block(b0, b1, j)) : 0);
+    }
+    float* red = s_red[it & 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float* rw = red + (wave * R + mt * 16 + 4 * q) * 17 + c;
+      float* rw = red + (wave * R + mt * 16 + 4 * q) * RS + c;
       rw[0] = acc[mt].x;
-      rw[17] = acc[mt].y;
-      rw[34] = acc[mt].z;
-      rw[51] = acc[mt].w;
+      rw[RS] = acc[mt].y;
+      rw[2 * RS] = acc[mt].z;
+      rw[3 * RS] = acc[mt].w;
     }
-    __syncthreads();
-    for (int i = tid; i < M * GD_TILE_N; i += 64 * NW) {
-      const int m = i >> 4, cc = i & 15;
-      float v = red[m * 17 + cc];
+    __syncthreads();   // the other buffer is rewritten only after the next tile's barrier
+    if (tid < R * 16) {
+      float v = 0.f;
 #pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) v += red[(w2 * R + m) * 17 + cc];
-      tt[m][cc] = v;
+      for (int w2 = 0; w2 < MM_NW; ++w2) v += red[(w2 * R + om) * RS + oc];
+      if (EPI == EPI_ARGMAX) {
+        if (own) {
+          if (p.logits) p.logits[(size_t)om * p.ldl + n] = v;
+          if (am_better(v, n, bv, bi)) { bv = v; bi = n; }
+        }
+      } else if (PAIR) {
+        const float v1 = dpp_f<DPP_QUAD_1032>(v);   // the odd neighbour's column
+        if (own && (oc & 1) == 0) epi_store<EPI>(p, eo, om, n, v, v1);
+      } else if (own) {
+        if (EPI == EPI_PLAIN && S > 1)
+          __hip_atomic_fetch_add(p.y + (size_t)om * p.ldy + n, v + (s == 0 ? eo.b0 : 0.f), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        else
+          epi_store<EPI>(p, eo, om, n, v, 0.f);
+      }
     }
-    __syncthreads();
-    const int n0 = t * GD_TILE_N;
-    switch (p.epi) {
-      case EPI_ARGMAX: mm_argmax(p, tt, t, n0, 64 * NW); break;
-      case EPI_PLAIN: mm_epi<EPI_PLAIN>(p, tt, n0, 64 * NW, S, s); break;
-      case EPI_GELU: mm_epi<EPI_GELU>(p, tt, n0, 64 * NW, S, s); break;
-      case EPI_SWIGLU: mm_epi<EPI_SWIGLU>(p, tt, n0, 64 * NW, S, s); break;
-      case EPI_QKV: mm_epi<EPI_QKV>(p, tt, n0, 64 * NW, S, s); break;
-      default: mm_epi<EPI_QKV_ROPE>(p, tt, n0, 64 * NW, S, s); break;
+  }
+  if (EPI == EPI_ARGMAX && tid < R * 16) {
+    // best of the 16 threads of each row (one 16-lane DPP row)
+#define MM_AM_STEP(CTRL)                                   \
+    {                                                      \
+      const float ov = dpp_f<CTRL>(bv);                    \
+      const int oi = dpp_i<CTRL>(bi);                      \
+      if (am_better(ov, oi, bv, bi)) { bv = ov; bi = oi; } \
     }
-    __syncthreads();   // tt and red are reused by the next tile
+    MM_AM_STEP(DPP_QUAD_1032)
+    MM_AM_STEP(DPP_QUAD_2301)
+    MM_AM_STEP(DPP_ROW_HALF_MIRROR)
+    MM_AM_STEP(DPP_ROW_MIRROR)
+#undef MM_AM_STEP
+    if (oc == 0 && om < M) {
+      p.am_val[(size_t)blockIdx.x * M + om] = bv;
+      p.am_idx[(size_t)blockIdx.x * M + om] = bi;
+    }
   }
 }
 

@@ -62,6 +62,7 @@ struct LinPlan {
   int nc, rw;  // gemv: 16-byte weight chunks per lane and row, weight rows per wave
   int mt, nw;  // mm: 16-row activation tiles, waves per workgroup
   int splits;  // mm: K splits (grid.y), > 1 only for in-place residual outputs
+  int passes;  // mm: register passes over the K range of one split (MM_KC columns each)
   int rows;    // activation rows per launch
   int grid;
   int parts;   // argmax partials per row (gemv: workgroups; mm: column tiles)
@@ -97,7 +98,7 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
   memset(&p, 0, sizeof(p));
   p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= GEMV_MAX_ROWS ? 0 : 1);
   p.nc = gemv_nc(K, wt);
-  if (p.var == 1 && norm && K > MM_KC) p.var = 0;   // the norm needs whole rows in LDS
+  if (p.var == 1 && norm && K > MM_KC) p.var = 0;   // the norm needs whole rows in one register pass
   if (p.var == 0 && p.nc < 0) p.var = 1;
   if (p.var == 0) {
     p.rw = gemv_rows_per_wave(epi, N);
@@ -112,17 +113,20 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
   if (p.var == 1) {
     const int ntiles = iceil(N, GD_TILE_N), nb = iceil(K, 32);
     p.mt = M <= 16 ? 1 : 2;
-    p.nw = 8;
+    p.nw = MM_NW;
     p.rows = M;
     p.splits = 1;
     // split K only as far as one workgroup per CU allows (a second round of workgroups
     // would double the kernel's time)
-    if (splittable && !norm && epi == EPI_PLAIN) p.splits = std::max(1, std::min(nb, kMmTargetWgs / ntiles));
-    // the head streams many tiles per workgroup (rows staged once); others one tile each
-    p.grid = epi == EPI_ARGMAX ? std::min(ntiles, kMmTargetWgs) : ntiles;
-    p.parts = ntiles;
-    const int kl = std::min(iceil(nb, p.splits) * 32, MM_KC);
-    p.lds = (size_t)mm_lds_floats(p.mt, p.nw, kl) * sizeof(float);
+    if (splittable && !norm && epi == EPI_PLAIN) {
+      p.splits = std::max(1, std::min(nb, kMmTargetWgs / ntiles));
+      p.splits = std::max(p.splits, iceil(nb, MM_KC / 32));   // one register pass per split
+    }
+    p.passes = iceil(iceil(nb, p.splits) * 32, MM_KC);
+    // at most one workgroup per CU; wider layers stream several tiles per workgroup
+    p.grid = std::min(ntiles, kMmTargetWgs);
+    p.parts = p.grid;
+    p.lds = 0;
   }
   return p;
 }
@@ -156,31 +160,35 @@ static void launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st)
   }
 }
 
-template <int WT>
-static void launch_mm(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
-  const dim3 g(lp.grid, lp.splits), b(64 * 8);
-  if (lp.mt == 1) hipLaunchKernelGGL((k_mm<WT, 1, 8>), g, b, lp.lds, st, prm);
-  else hipLaunchKernelGGL((k_mm<WT, 2, 8>), g, b, lp.lds, st, prm);
-}
-
-// Lets the matrix-core kernels use more than the default 64 KB of dynamic LDS (once per
-// process).
-static hipError_t mm_allow_lds() {
-  const int bytes = mm_lds_floats(2, 8, MM_KC) * (int)sizeof(float);
-  const void* fns[] = {(const void*)k_mm<0, 1, 8>, (const void*)k_mm<0, 2, 8>, (const void*)k_mm<1, 1, 8>,
-                       (const void*)k_mm<1, 2, 8>};
-  for (const void* f : fns) {
-    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
+template <int WT, int MT>
+static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+  const dim3 g(lp.grid, lp.splits), b(64 * MM_NW);
+  const bool nrm = prm.norm != NORM_NONE;
+#define GD_MM(EPI, NRM, MP) hipLaunchKernelGGL((k_mm<WT, MT, EPI, NRM, MP>), g, b, 0, st, prm)
+  if (lp.passes > 1) {   // K range wider than one pass: plain or GELU epilogue, no norm
+    if (nrm) return hipErrorNotSupported;
+    if (prm.epi == EPI_PLAIN) GD_MM(EPI_PLAIN, false, true);
+    else if (prm.epi == EPI_GELU) GD_MM(EPI_GELU, false, true);
+    else return hipErrorNotSupported;
+    return hipSuccess;
   }
+  switch (prm.epi) {
+    case EPI_PLAIN: if (nrm) GD_MM(EPI_PLAIN, true, false); else GD_MM(EPI_PLAIN, false, false); break;
+    case EPI_GELU: if (nrm) GD_MM(EPI_GELU, true, false); else GD_MM(EPI_GELU, false, false); break;
+    // the remaining epilogues always follow a pre-norm
+    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_SWIGLU, true, false); break;
+    case EPI_ARGMAX: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_ARGMAX, true, false); break;
+    case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_QKV, true, false); break;
+    case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_QKV_ROPE, true, false); break;
+    default: return hipErrorNotSupported;
+  }
+#undef GD_MM
   return hipSuccess;
 }
 
-static hipError_t mm_allow_lds_once() {
-  static std::once_flag once;
-  static hipError_t result = hipSuccess;
-  std::call_once(once, [] { result = mm_allow_lds(); });
-  return result;
+template <int WT>
+static hipError_t launch_mm(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+  return lp.mt == 1 ? launch_mm_mt<WT, 1>(lp, prm, st) : launch_mm_mt<WT, 2>(lp, prm, st);
 }
 
 // One launch of one plan over prm.M rows (prm.M <= lp.rows).
@@ -189,8 +197,8 @@ static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm,
     if (wt == GD_WEIGHT_F32) launch_gemv<0>(lp, prm, st);
     else launch_gemv<1>(lp, prm, st);
   } else {
-    if (wt == GD_WEIGHT_F32) launch_mm<0>(lp, prm, st);
-    else launch_mm<1>(lp, prm, st);
+    const hipError_t e = wt == GD_WEIGHT_F32 ? launch_mm<0>(lp, prm, st) : launch_mm<1>(lp, prm, st);
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }
@@ -423,7 +431,6 @@ extern "C" gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model*
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return set_err(GD_ERR_NO_DEVICE, "no device properties");
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return set_err(GD_ERR_NO_DEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
-  if (mm_allow_lds_once() != hipSuccess) return set_err(GD_ERR_HIP, "could not raise the LDS limit of k_mm");
   gd_model* m = new gd_model();
   m->c = *cfg;
   m->dev = dev;
@@ -776,10 +783,11 @@ struct ProfScope {
   }
 };
 
-static const char* linear_kernel_name(int wt, const LinPlan& lp, char* buf, size_t n) {
+static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, char* buf, size_t n) {
   const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
-  if (lp.var == 0) snprintf(buf, n, "k_gemv<%d, %d, %d>", w, lp.nc, lp.rw);
-  else snprintf(buf, n, "k_mm<%d, %d, %d>", w, lp.mt, lp.nw);
+  // as rocprofv3 prints the instantiation
+  if (lp.var == 0) snprintf(buf, n, "k_gemv<%d, %d, %d, %d>", w, lp.nc, lp.rw, epi);
+  else snprintf(buf, n, "k_mm<%d, %d, %d, %s, %s>", w, lp.mt, epi, norm ? "true" : "false", lp.passes > 1 ? "true" : "false");
   return buf;
 }
 
@@ -801,7 +809,7 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
   const bool inplace = p.resid == p.y && p.ldr == p.ldy;
   LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE, inplace);
   char kn[64];
-  ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, kn, sizeof(kn)), m->profile ? linear_bytes(m, p) : 0);
+  ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, kn, sizeof(kn)), m->profile ? linear_bytes(m, p) : 0);
   return run_linear_rows(m->wt, lp, p, st, am_out);
 }
 
@@ -1151,7 +1159,6 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
   p.y = y; p.ldy = ldy;
   const bool inplace = resid && resid == y && ldr == ldy;
   LinPlan lp = plan_linear(M, N, K, wdt, variant, p.epi, p.norm != NORM_NONE, inplace);
-  if (mm_allow_lds_once() != hipSuccess) return set_err(GD_ERR_HIP, "could not raise the LDS limit of k_mm");
   hipError_t e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
   return GD_OK;
