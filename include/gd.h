@@ -185,7 +185,9 @@ gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, 
  * norm_g, norm_b: float or NULL; resid: float [M][ldr] or NULL; y: float [M][ldy].
  * 1 <= M <= 32, N >= 1, K >= 8 and K % 8 == 0; W must be 16-byte aligned.
  * variant: 0 auto, 1 VALU GEMV, 2 MFMA. workspace: gd_linear_workspace bytes, zeroed
- * once before first use (the kernels leave it zeroed). */
+ * once before first use. Its first part (a zero vector) is never written; the rest
+ * receives, on each call that runs the MFMA kernel, the tile-major copy of W that
+ * kernel reads, so calls sharing one workspace must not overlap. */
 gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32_t weight_dtype,
                     const float* bias, int32_t norm, const float* norm_g, const float* norm_b,
                     float eps, int32_t act, const float* resid, int32_t ldr, float* y, int32_t ldy,

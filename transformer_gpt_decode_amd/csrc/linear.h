@@ -57,7 +57,8 @@ struct LinParams {
   int* err;
   const long long* row_kvoff;               // element offset of each row's K/V slot in a layer pool (-1: none)
   // ---- weights
-  const void* w; int M, N, K;
+  const void* w; int M, N, K;               // [N][K] row-major (VALU kernel)
+  const void* wtl;                          // the same, tile-major (matrix-core kernel; see k_pack_tiles)
   // ---- epilogue
   int epi;
   const float* bias;                        // never NULL: a zero vector when the layer has none
@@ -472,41 +473,82 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
 // a linear epilogue whose output is the residual, updated in place: each split adds
 // its partial sums to it with float atomics, the bias coming from split 0.
 //
-// Nothing is staged in LDS. A pass covers up to MM_NW * MM_JB blocks: block
-// b = pass start + wave + MM_NW j is held by the wave in register slot j, for the
-// activation rows (loaded once per pass, so once per launch when the K range fits one
-// pass) and for the weights of the current tile. Load order per lane: rows, the
-// norm's shift values, gain and shift, the tile's weights, the tile's epilogue
-// operands; the row moments and the normalization (in registers, one cross-wave
-// exchange in LDS) run while the weights are in flight. After a tile's MFMAs the
-// next tile's weights are issued, then the waves' partial tiles are summed through a
-// double-buffered LDS array (one barrier per tile) and each thread applies the
-// epilogue to its own output (row tid / 16, column tid % 16). The head's argmax keeps
-// a running best per output thread across tiles and writes one partial per
-// workgroup and row.
+// Operand layout: lane l = 16 q + c holds W[n0 + c][kk + 8q .. +8] and
+// X[m0 + c][kk + 8q .. +8] for the 32-column block kk; MFMA step t of 8 feeds element t
+// of both, so one instruction contracts the k-values kk + 8q + t for A and B alike.
+// D[i][j]: lane l holds column j = l % 16 and rows 4q + v.
 //
-// Operand layout: lane l holds W[n0 + l%16][kk + 8(l/16) .. +8] and X[m0 + l%16][same];
-// MFMA step t of 8 feeds element t of both, so one instruction contracts the k-values
-// kk + 8q + t (q = l/16) for A and B alike. D[i][j]: lane l holds column j = l%16 and
-// rows 4(l/16) + v.
+// Loads are shaped for the memory pipeline rather than for that layout: a load
+// instruction that spreads over 16 rows reaches a CU at well under half the rate of
+// one that reads 1 KB of contiguous bytes. Hence
+//  - the weights are read from a tile-major copy (k_pack_tiles) in which every 16 x 32
+//    block is stored in operand order, so each instruction reads 1 KB contiguously;
+//  - the activation rows of the K range are loaded a whole row per wave (lane l: 16
+//    bytes at 16 l + 1 KB j), normalized there (two-pass mean and variance from
+//    registers), written to LDS once and read back in operand layout; each wave then
+//    keeps its K blocks (block = range start + wave + MM_NW j) in registers for all of
+//    its tiles.
+// Padding is zero on both sides (weight rows past N and columns past K in the packed
+// copy; LDS columns past the K range and rows past M), so no lane needs masking.
+// After a tile's MFMAs the next tile's weights are issued, then the waves' partial
+// tiles are summed through a double-buffered LDS array placed over the (by then
+// unused) row staging area, and each thread applies the epilogue to its own output
+// (row tid / 16, column tid % 16). The head's argmax keeps a running best per output
+// thread across tiles and writes one partial per workgroup and row.
 
 #define MM_NW 8                       // waves per workgroup
 #define MM_JB 4                       // K blocks per wave and pass held in registers
 #define MM_KC (MM_NW * MM_JB * 32)    // K columns per pass
+#define MM_LDX (MM_KC + 4)            // LDS row stride: 16 rows read at one column fall in distinct banks
 
-template <int WT> struct W8;   // eight consecutive weights of one row, as stored
+// Bytes of one packed 16 x 32 block.
+__host__ __device__ constexpr int mm_block_bytes(int wt) { return wt == 0 ? 2048 : 1024; }
+// Bytes of the packed copy of an [N][K] matrix.
+__host__ __device__ inline size_t mm_packed_bytes(int wt, int N, int K) {
+  return (size_t)((N + 15) / 16) * ((K + 31) / 32) * mm_block_bytes(wt);
+}
+
+// Tile-major copy of W [N][K]: block (t, b) (t = column tile of 16 rows, b = 32-column
+// K block) at ((t * nb + b) * block bytes); inside it, fp32: two 1 KB halves h, lane l's
+// 16 bytes at h * 1024 + 16 l hold W[16t + l%16][32b + 8(l/16) + 4h .. +4]; bf16: lane
+// l's 16 bytes at 16 l hold W[16t + l%16][32b + 8(l/16) .. +8]. Rows >= N and columns
+// >= K are zero. One thread per 16-byte unit.
+__global__ __launch_bounds__(GD_WG) void k_pack_tiles(const void* __restrict__ W, int wt, int N, int K,
+                                                      void* __restrict__ dst, size_t units) {
+  const size_t u = (size_t)blockIdx.x * GD_WG + threadIdx.x;
+  if (u >= units) return;
+  const int nb = (K + 31) >> 5;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (wt == 0) {
+    const int l = (int)(u & 63), h = (int)((u >> 6) & 1);
+    const size_t blk = u >> 7;
+    const int t = (int)(blk / nb), b = (int)(blk % nb);
+    const int n = 16 * t + (l & 15), k = 32 * b + 8 * (l >> 4) + 4 * h;
+    if (n < N && k < K) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(W) + (size_t)n * K + k);
+  } else {
+    const int l = (int)(u & 63);
+    const size_t blk = u >> 6;
+    const int t = (int)(blk / nb), b = (int)(blk % nb);
+    const int n = 16 * t + (l & 15), k = 32 * b + 8 * (l >> 4);
+    if (n < N && k < K) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + (size_t)n * K + k);
+  }
+  reinterpret_cast<u32x4*>(dst)[u] = v;
+}
+
+template <int WT> struct W8;   // eight weights of one lane and block, as stored
 template <> struct W8<0> { f32x4 a, b; };
 template <> struct W8<1> { u32x4 a; };
 
+// Lane's eight weights of packed block blk (byte offset blk * block bytes).
 template <int WT>
-__device__ __forceinline__ W8<WT> load_w8raw(const void* __restrict__ W, size_t off) {
+__device__ __forceinline__ W8<WT> load_w8tile(const void* __restrict__ Wt, size_t blk, int lane) {
   W8<WT> r;
+  const char* base = reinterpret_cast<const char*>(Wt) + blk * mm_block_bytes(WT) + 16 * lane;
   if constexpr (WT == 0) {
-    const f32x4* q = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(W) + off);
-    r.a = __builtin_nontemporal_load(q);
-    r.b = __builtin_nontemporal_load(q + 1);
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base));
+    r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base + 1024));
   } else {
-    r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + off));
+    r.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base));
   }
   return r;
 }
@@ -526,23 +568,10 @@ __device__ __forceinline__ float w8_at(const W8<WT>& r, int t) {
 
 struct F8 { f32x4 a, b; };   // eight consecutive fp32 values
 
-__device__ __forceinline__ F8 load_f8(const float* p) {
-  F8 r;
-  r.a = *reinterpret_cast<const f32x4*>(p);
-  r.b = *reinterpret_cast<const f32x4*>(p + 4);
-  return r;
-}
-
 __device__ __forceinline__ float f8_at(const F8& r, int t) {
   const f32x4 v = t < 4 ? r.a : r.b;
   const int u = t & 3;
   return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ void f8_set(F8& r, int t, float x) {
-  f32x4& v = t < 4 ? r.a : r.b;
-  const int u = t & 3;
-  if (u == 0) v.x = x; else if (u == 1) v.y = x; else if (u == 2) v.z = x; else v.w = x;
 }
 
 template <int CTRL>
@@ -552,22 +581,27 @@ __device__ __forceinline__ int dpp_i(int v) {
 
 // Keeps the loads that produced v in flight no longer than this point: the compiler
 // waits for them here (where they have long arrived) rather than at their use, which
-// may follow loads issued later under a condition.
+// may follow loads issued later.
 __device__ __forceinline__ void settle(float v) { asm volatile("" ::"v"(v)); }
+
+__device__ __forceinline__ f32x4 f4_zero() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
+
+// LDS floats of k_mm with R activation rows.
+__host__ __device__ constexpr int mm_lds_floats(int R) { return R * MM_LDX; }
 
 // NRM: the rows are normalized (LayerNorm or RMSNorm by p.norm; S == 1, one pass).
 // MP: the K range of a split may exceed one pass (no norm): rows and weights are then
-// loaded per pass and tile. Without MP every load is unconditional, so the compiler's
-// wait counts stay exact and nothing waits for the next tile's weights.
+// staged per pass and tile. Without MP the weight loads are unconditional, so the
+// compiler's wait counts stay exact and nothing waits for the next tile's weights.
 template <int WT, int MT, int EPI, bool NRM, bool MP>
 __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   static_assert(!(NRM && MP), "the norm needs whole rows in one pass");
-  constexpr int R = MT * 16;          // activation rows of the tile (rows >= M are padding)
+  constexpr int R = MT * 16;          // activation rows of the tile (rows >= M are zero)
+  constexpr int RPW = R / MM_NW;      // rows staged per wave
   constexpr int RS = 17;              // padded row stride of a partial tile in LDS
   constexpr bool PAIR = EpiTraits<EPI>::pair;
-  __shared__ float s_red[2][MM_NW * R * RS];
-  __shared__ float s_part[MM_NW][R][2];
-  __shared__ float s_mr[R][2];
+  static_assert(2 * MM_NW * R * RS <= mm_lds_floats(R), "partial tiles fit over the staging area");
+  __shared__ __align__(16) float xs[mm_lds_floats(R)];   // staged rows [R][MM_LDX], later s_red[2]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c = lane & 15;
   const int M = p.M, N = p.N, K = p.K;
@@ -579,94 +613,113 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   const int om = tid >> 4, oc = tid & 15;
   const bool orow = tid < R * 16 && om < M;
 
-  // block held in slot j of the pass starting at cb (clamped: unused slots are skipped)
-  auto slot_block = [&](int cb, int ce, int j) { return min(cb + wave + MM_NW * j, ce - 1); };
-  auto slot_k = [&](int blk) { return min(blk * 32 + 8 * q, K - 8); };
-  auto load_x = [&](F8 (&xr)[MM_JB][MT], int cb, int ce) {
+  // ---- staging of blocks [cb, ce). stage_issue loads this wave's rows (and the norm's
+  // gain and shift); it runs before the weight loads, so that waiting for the rows does
+  // not wait for the weights (vector loads complete in issue order). stage_finish
+  // normalizes, writes the rows to LDS and reads this wave's operand blocks into xr.
+  F8 xr[MM_JB][MT];
+  f32x4 v[RPW][MM_JB], g[MM_JB], bb[MM_JB];
+  auto stage_issue = [&](int cb, int ce) {
+    const int ka = cb * 32;
+    const int kq = (min(ce * 32, K) - ka) >> 2;   // float4 chunks of real columns per row
+    const int pc = ((ce - cb) * 8 + 63) >> 6;     // chunks per lane (padded range)
+    // lanes past the range read a clamped chunk and keep zeros
 #pragma unroll
-    for (int j = 0; j < MM_JB; ++j) {
-      const int k = slot_k(slot_block(cb, ce, j));
+    for (int i = 0; i < RPW; ++i) {
+      const int m = min(wave + MM_NW * i, M - 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xr[j][mt] = load_f8(p.x + (size_t)min(mt * 16 + c, M - 1) * p.ldx + k);
+      for (int j = 0; j < MM_JB; ++j) {
+        const int ch = lane + 64 * j;
+        const f32x4 t = j < pc ? *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + ka + 4 * min(ch, kq - 1))
+                               : f4_zero();
+        v[i][j] = ch < kq ? t : f4_zero();
+      }
+    }
+    if constexpr (NRM) {
+      const float* bsrc = p.norm == NORM_LN ? p.nb : p.ng;   // RMSNorm: shift 0 (bsel below)
+#pragma unroll
+      for (int j = 0; j < MM_JB; ++j) {
+        const int ch = lane + 64 * j, cc = 4 * min(ch, kq - 1);
+        const f32x4 tg = j < pc ? *reinterpret_cast<const f32x4*>(p.ng + cc) : f4_zero();
+        const f32x4 tb = j < pc ? *reinterpret_cast<const f32x4*>(bsrc + cc) : f4_zero();
+        g[j] = ch < kq ? tg : f4_zero();
+        bb[j] = ch < kq ? tb : f4_zero();
+      }
     }
   };
-  auto load_w = [&](W8<WT> (&w)[MM_JB], int t, int cb, int ce) {
-    const int n = min(t * GD_TILE_N + c, N - 1);
+  auto stage_finish = [&](int cb, int ce) {
+    const int kq = (min(ce * 32, K) - cb * 32) >> 2;
+    const int kqp = (ce - cb) * 8;
+    const int pc = (kqp + 63) >> 6;
+    if constexpr (NRM) {
+      // two-pass moments of each whole row (S == 1: the range is the row)
+      const bool ln = p.norm == NORM_LN;
 #pragma unroll
-    for (int j = 0; j < MM_JB; ++j) w[j] = load_w8raw<WT>(p.w, (size_t)n * K + slot_k(slot_block(cb, ce, j)));
+      for (int i = 0; i < RPW; ++i) {
+        float s1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j) s1 += (v[i][j].x + v[i][j].y) + (v[i][j].z + v[i][j].w);
+        const float mu = ln ? wave_sum(s1) / (float)K : 0.f;
+        float s2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j) {
+          const int ch = lane + 64 * j;
+          if (j < pc && ch < kq) {
+            const float d0 = v[i][j].x - mu, d1 = v[i][j].y - mu, d2 = v[i][j].z - mu, d3 = v[i][j].w - mu;
+            s2 += fmaf(d0, d0, d1 * d1) + fmaf(d2, d2, d3 * d3);
+          }
+        }
+        const float r = 1.0f / sqrtf(wave_sum(s2) / (float)K + p.eps);
+        const float bsel = ln ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j) {
+          v[i][j].x = (v[i][j].x - mu) * r * g[j].x + bsel * bb[j].x;
+          v[i][j].y = (v[i][j].y - mu) * r * g[j].y + bsel * bb[j].y;
+          v[i][j].z = (v[i][j].z - mu) * r * g[j].z + bsel * bb[j].z;
+          v[i][j].w = (v[i][j].w - mu) * r * g[j].w + bsel * bb[j].w;
+        }
+      }
+    }
+    // rows >= M and chunks past K are stored as zeros
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int m = wave + MM_NW * i;
+#pragma unroll
+      for (int j = 0; j < MM_JB; ++j) {
+        const int ch = lane + 64 * j;
+        if (j < pc && ch < kqp) *reinterpret_cast<f32x4*>(xs + m * MM_LDX + 4 * ch) = (m < M && ch < kq) ? v[i][j] : f4_zero();
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < MM_JB; ++j) {
+      // block within the range (clamped: slots past the range are never multiplied)
+      const int blk = min(wave + MM_NW * j, ce - cb - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float* src = xs + (mt * 16 + c) * MM_LDX + blk * 32 + 8 * q;
+        xr[j][mt].a = *reinterpret_cast<const f32x4*>(src);
+        xr[j][mt].b = *reinterpret_cast<const f32x4*>(src + 4);
+      }
+    }
+    __syncthreads();   // the staging area is reused for the partial tiles
+  };
+  // weights of tile t for this wave's blocks of [cb, ce) (unused slots repeat the last
+  // block: loads stay unconditional); more = false reads 16 bytes at the base instead
+  auto load_w = [&](W8<WT> (&w)[MM_JB], int t, int cb, int ce, bool more) {
+#pragma unroll
+    for (int j = 0; j < MM_JB; ++j) {
+      const int blk = min(cb + wave + MM_NW * j, ce - 1);
+      w[j] = load_w8tile<WT>(p.wtl, more ? (size_t)t * nb + blk : 0, more ? lane : 0);
+    }
   };
 
-  // ---- loads: rows, norm parameters, first tile's weights (one pass)
-  F8 xr[MM_JB][MT];
   W8<WT> w[MM_JB];
   int t = blockIdx.x;
   if constexpr (!MP) {
-    load_x(xr, b0, b1);
-    if (NRM) {
-      const bool ln = p.norm == NORM_LN;
-      float x0[MT];   // shift of each row's moments: its first element
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) x0[mt] = p.x[(size_t)min(mt * 16 + c, M - 1) * p.ldx];
-      const float* bsrc = ln ? p.nb : p.ng;
-      F8 gg[MM_JB], bb[MM_JB];
-#pragma unroll
-      for (int j = 0; j < MM_JB; ++j) {
-        const int k = slot_k(slot_block(b0, b1, j));
-        gg[j] = load_f8(p.ng + k);
-        bb[j] = load_f8(bsrc + k);
-      }
-      load_w(w, t, b0, b1);
-      // ---- row moments from registers (shifted sums; RMSNorm: plain sum of squares)
-      float s1[MT], s2[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        s1[mt] = s2[mt] = 0.f;
-        const float sh = ln ? x0[mt] : 0.f;
-#pragma unroll
-        for (int j = 0; j < MM_JB; ++j) {
-          const int blk = b0 + wave + MM_NW * j;
-          const float okf = (blk < b1 && blk * 32 + 8 * q < K) ? 1.f : 0.f;   // clamped duplicates count 0
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float d = (f8_at(xr[j][mt], u) - sh) * okf;
-            s1[mt] += d;
-            s2[mt] = fmaf(d, d, s2[mt]);
-          }
-        }
-        s1[mt] += __shfl_xor(s1[mt], 16);
-        s1[mt] += __shfl_xor(s1[mt], 32);
-        s2[mt] += __shfl_xor(s2[mt], 16);
-        s2[mt] += __shfl_xor(s2[mt], 32);
-        if (q == 0) {
-          s_part[wave][mt * 16 + c][0] = s1[mt];
-          s_part[wave][mt * 16 + c][1] = s2[mt];
-        }
-      }
-      __syncthreads();
-      if (tid < R) {   // row tid = 16 q + c, shift x0[q]
-        float a = 0.f, a2 = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < MM_NW; ++w2) { a += s_part[w2][tid][0]; a2 += s_part[w2][tid][1]; }
-        const float sh = ln ? (q == 0 ? x0[0] : x0[MT - 1]) : 0.f;
-        const float md = a / (float)K;   // mean of the shifted values
-        const float var = ln ? fmaxf(a2 / (float)K - md * md, 0.f) : a2 / (float)K;
-        s_mr[tid][0] = ln ? sh + md : 0.f;
-        s_mr[tid][1] = 1.0f / sqrtf(var + p.eps);
-      }
-      __syncthreads();
-      const float bsel = ln ? 1.f : 0.f;   // RMSNorm: no shift (and mu = 0)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float mu = s_mr[mt * 16 + c][0], r = s_mr[mt * 16 + c][1];
-#pragma unroll
-        for (int j = 0; j < MM_JB; ++j)
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            f8_set(xr[j][mt], u, (f8_at(xr[j][mt], u) - mu) * r * f8_at(gg[j], u) + bsel * f8_at(bb[j], u));
-      }
-    } else {
-      load_w(w, t, b0, b1);
-    }
+    stage_issue(b0, b1);
+    load_w(w, t, b0, b1, true);   // the first tile's weights stream while the rows are staged
+    stage_finish(b0, b1);
   }
 
   float bv = -INFINITY;   // argmax: running best of this thread's columns
@@ -678,40 +731,31 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     const EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? n : 0);
     f32x4 acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_zero();
     for (int cb = b0; cb < b1; cb += MM_NW * MM_JB) {
       const int ce = min(b1, cb + MM_NW * MM_JB);
       if constexpr (MP) {
-        load_x(xr, cb, ce);
-        load_w(w, t, cb, ce);
+        __syncthreads();   // the previous tile's partials have been read
+        stage_issue(cb, ce);
+        load_w(w, t, cb, ce, true);
+        stage_finish(cb, ce);
       }
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
-        const int blk = cb + wave + MM_NW * j;
-        if (blk < ce) {   // wave-uniform: MFMAs run with the whole wave
-          // a lane past K (K % 32 != 0) holds a clamped duplicate: contribute zeros
-          const bool ok = blk * 32 + 8 * q < K;
+        if (cb + wave + MM_NW * j < ce) {   // wave-uniform: MFMAs run with the whole wave
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? f8_at(xr[j][mt], u) : 0.f, w8_at<WT>(w[j], u),
-                                                            acc[mt], 0, 0, 0);
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f8_at(xr[j][mt], u), w8_at<WT>(w[j], u), acc[mt], 0, 0, 0);
         }
       }
     }
     settle(eo.b0); settle(eo.b1); settle(eo.r0); settle(eo.c); settle(eo.s);
     settle(__int_as_float((int)eo.kvoff)); settle(__int_as_float((int)(eo.kvoff >> 32)));
-    // the next tile's weights stream while this tile is reduced and stored; after the
-    // last tile every lane reads the same 32 bytes instead (an unconditional load)
-    if constexpr (!MP) {
-      const bool more = t + G < ntiles;
-      const int n = min((t + G) * GD_TILE_N + c, N - 1);
-#pragma unroll
-      for (int j = 0; j < MM_JB; ++j)
-        w[j] = load_w8raw<WT>(p.w, more ? (size_t)n * K + slot_k(slot_block(b0, b1, j)) : 0);
-    }
-    float* red = s_red[it & 1];
+    // the next tile's weights stream while this tile is reduced and stored
+    if constexpr (!MP) load_w(w, t + G, b0, b1, t + G < ntiles);
+    float* red = xs + (it & 1) * (MM_NW * R * RS);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       float* rw = red + (wave * R + mt * 16 + 4 * q) * RS + c;

@@ -234,6 +234,7 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
 
 struct LayerOff {
   size_t n1g, n1b, wqkv, bqkv, wo, bo, n2g, n2b, wfc, bfc, wproj, bproj;
+  size_t tqkv, to, tfc, tproj;   // tile-major copies of the matrices (matrix-core kernel)
 };
 
 struct GraphKey {
@@ -262,6 +263,7 @@ struct gd_model {
 
   // sizes
   size_t w_bytes = 0, kv_bytes = 0, s_bytes = 0;
+  size_t w_rowmajor_bytes = 0;   // the row-major part of the weights (what the caller's values fill)
   size_t am_parts = 0;  // argmax partials per row (workgroups of the head's widest plan)
 
   // bound memory
@@ -271,7 +273,7 @@ struct gd_model {
   bool bound = false, loaded = false;
 
   // weight offsets (bytes)
-  size_t o_wte = 0, o_wpe = 0, o_nfg = 0, o_nfb = 0, o_head = 0;
+  size_t o_wte = 0, o_wpe = 0, o_nfg = 0, o_nfb = 0, o_head = 0, o_thead = 0;
   std::vector<LayerOff> L;
 
   // scratch offsets (bytes)
@@ -376,6 +378,17 @@ static void layout(gd_model* m) {
   m->o_nfg = take(d * 4);
   if (c.arch == GD_ARCH_GPT2) m->o_nfb = take(d * 4);
   else m->o_head = take(V * d * e);
+  // tile-major copies for the matrix-core kernel (filled from the row-major matrices)
+  m->w_rowmajor_bytes = off;
+  const int wt = m->wt == GD_WEIGHT_F32 ? 0 : 1;
+  for (int l = 0; l < c.n_layer; ++l) {
+    LayerOff& t = m->L[l];
+    t.tqkv = take(mm_packed_bytes(wt, m->qkvdim, (int)d));
+    t.to = take(mm_packed_bytes(wt, (int)d, m->qdim));
+    t.tfc = take(mm_packed_bytes(wt, m->fcN, (int)d));
+    t.tproj = take(mm_packed_bytes(wt, (int)d, (int)ff));
+  }
+  m->o_thead = take(mm_packed_bytes(wt, (int)V, (int)d));
   m->w_bytes = off;
 
   // KV cache: K pools for all layers, then V pools
@@ -556,6 +569,15 @@ static void put_vec(std::vector<char>& dst, size_t off, const float* src, size_t
   memcpy(dst.data() + off, src, n * 4);
 }
 
+// Fills the tile-major copy of an [N][K] matrix (k_pack_tiles).
+static hipError_t launch_pack(const void* W, int wt, int N, int K, void* dst, hipStream_t st) {
+  const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
+  const size_t units = mm_packed_bytes(w, N, K) / 16;
+  hipLaunchKernelGGL(k_pack_tiles, dim3((unsigned)((units + GD_WG - 1) / GD_WG)), dim3(GD_WG), 0, st, W, w, N, K, dst,
+                     units);
+  return hipGetLastError();
+}
+
 static size_t canonical_count(const gd_config& c) {
   size_t d = c.d_model, ff = c.d_ff, V = c.vocab;
   size_t hq = (size_t)c.n_head * c.head_dim, hk = (size_t)c.n_kv_head * c.head_dim;
@@ -571,7 +593,7 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
   const gd_config& c = m->c;
   if (n != canonical_count(c)) return set_err(GD_ERR_INVALID, "weight count %zu, expected %zu", n, canonical_count(c));
   const size_t d = c.d_model, ff = c.d_ff, V = c.vocab, e = m->elt;
-  std::vector<char> buf(m->w_bytes, 0);
+  std::vector<char> buf(m->w_rowmajor_bytes, 0);
   const float* p = hw;
   put_mat(m, buf, m->o_wte, p, V * d);
   p += V * d;
@@ -629,6 +651,17 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     put_mat(m, buf, m->o_head, p, V * d); p += V * d;
   }
   HIP_TRY(m, hipMemcpyAsync(m->w, buf.data(), buf.size(), hipMemcpyHostToDevice, m->stream));
+  auto pack = [&](size_t src, size_t dst, int N, int K) {
+    return launch_pack(m->w + src, m->wt, N, K, m->w + dst, m->stream);
+  };
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& t = m->L[l];
+    HIP_TRY(m, pack(t.wqkv, t.tqkv, m->qkvdim, (int)d));
+    HIP_TRY(m, pack(t.wo, t.to, (int)d, m->qdim));
+    HIP_TRY(m, pack(t.wfc, t.tfc, m->fcN, (int)d));
+    HIP_TRY(m, pack(t.wproj, t.tproj, (int)d, (int)ff));
+  }
+  HIP_TRY(m, pack(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, m->o_thead, (int)V, (int)d));
   HIP_TRY(m, hipStreamSynchronize(m->stream));
   m->loaded = true;
   return GD_OK;
@@ -880,7 +913,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.pro = PRO_COPY;
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
-      p.w = m->w + t.wqkv; p.N = m->qkvdim; p.K = d;
+      p.w = m->w + t.wqkv; p.wtl = m->w + t.tqkv; p.N = m->qkvdim; p.K = d;
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
       p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
       p.y = q; p.ldy = m->qdim;
@@ -927,7 +960,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
         p.pro = PRO_COPY;
         p.x = attn; p.ldx = m->qdim;
       }
-      p.w = m->w + t.wo; p.N = d; p.K = m->qdim;
+      p.w = m->w + t.wo; p.wtl = m->w + t.to; p.N = d; p.K = m->qdim;
       p.epi = EPI_PLAIN;
       p.bias = t.bo ? m->wf(t.bo) : zero;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
@@ -939,7 +972,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.pro = PRO_COPY;
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n2g); p.nb = t.n2b ? m->wf(t.n2b) : nullptr;
-      p.w = m->w + t.wfc; p.N = m->fcN; p.K = d;
+      p.w = m->w + t.wfc; p.wtl = m->w + t.tfc; p.N = m->fcN; p.K = d;
       p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
       p.bias = t.bfc ? m->wf(t.bfc) : zero;
       p.resid = zero; p.ldr = 0;
@@ -951,7 +984,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       LinParams p = base;
       p.pro = PRO_COPY;
       p.x = h; p.ldx = ff;
-      p.w = m->w + t.wproj; p.N = d; p.K = ff;
+      p.w = m->w + t.wproj; p.wtl = m->w + t.tproj; p.N = d; p.K = ff;
       p.epi = EPI_PLAIN;
       p.bias = t.bproj ? m->wf(t.bproj) : zero;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
@@ -964,7 +997,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.pro = PRO_COPY;
     p.x = x + (size_t)head_row * d; p.ldx = d;
     p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
-    p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.N = c.vocab; p.K = d;
+    p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
     p.epi = EPI_ARGMAX;
     p.M = head_rows;
     p.row_kvoff = rp.row_kvoff + head_row;
@@ -1117,15 +1150,17 @@ static gd_status linear_check(int M, int N, int K, int variant) {
   return GD_OK;
 }
 
-// The op-level linear reads a zero vector (in the workspace) in place of an absent
-// bias or residual.
-static size_t linear_ws_bytes(int N) { return align_up((size_t)N * 4, 256); }
+// The op-level linear's workspace: a zero vector read in place of an absent bias or
+// residual, then room for the tile-major copy of W that the matrix-core kernel reads
+// (sized for fp32, filled on every call that uses that kernel).
+static size_t linear_ws_zero_bytes(int N) { return align_up((size_t)N * 4, 256); }
+static size_t linear_ws_bytes(int N, int K) { return linear_ws_zero_bytes(N) + mm_packed_bytes(0, N, K); }
 
 extern "C" gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, size_t* bytes) {
   if (!bytes) return set_err(GD_ERR_INVALID, "bytes is NULL");
   gd_status st = linear_check(M, N, K, variant);
   if (st != GD_OK) return st;
-  *bytes = linear_ws_bytes(N);
+  *bytes = linear_ws_bytes(N, K);
   return GD_OK;
 }
 
@@ -1143,8 +1178,8 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
   if (ldx < K || ldx % 4 || ldy < N || (resid && ldr < N)) return set_err(GD_ERR_INVALID, "bad leading dimensions");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(W)) & 15)
     return set_err(GD_ERR_INVALID, "x and W must be 16-byte aligned");
-  if (!ws || ws_bytes < linear_ws_bytes(N))
-    return set_err(GD_ERR_OOM, "workspace %zu < %zu bytes", ws_bytes, linear_ws_bytes(N));
+  if (!ws || ws_bytes < linear_ws_bytes(N, K))
+    return set_err(GD_ERR_OOM, "workspace %zu < %zu bytes", ws_bytes, linear_ws_bytes(N, K));
   const float* zero = static_cast<const float*>(ws);
   LinParams p;
   memset(&p, 0, sizeof(p));
@@ -1159,7 +1194,14 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
   p.y = y; p.ldy = ldy;
   const bool inplace = resid && resid == y && ldr == ldy;
   LinPlan lp = plan_linear(M, N, K, wdt, variant, p.epi, p.norm != NORM_NONE, inplace);
-  hipError_t e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
+  hipError_t e = hipSuccess;
+  if (lp.var == 1) {
+    void* packed = static_cast<char*>(ws) + linear_ws_zero_bytes(N);
+    e = launch_pack(W, wdt, N, K, packed, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
+    p.wtl = packed;
+  }
+  e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
   return GD_OK;
 }
