@@ -490,9 +490,9 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
 //    its tiles.
 // Padding is zero on both sides (weight rows past N and columns past K in the packed
 // copy; LDS columns past the K range and rows past M), so no lane needs masking.
-// After a tile's MFMAs the next tile's weights are issued, then the waves' partial
-// tiles are summed through a double-buffered LDS array placed over the (by then
-// unused) row staging area, and each thread applies the epilogue to its own output
+// The next tile's weights are issued (into a second register set) before a tile's
+// MFMAs; the waves' partial tiles are summed through a double-buffered LDS array
+// placed over the (by then unused) row staging area, and each thread applies the epilogue to its own output
 // (row tid / 16, column tid % 16). The head's argmax keeps a running best per output
 // thread across tiles and writes one partial per workgroup and row.
 
@@ -714,21 +714,24 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     }
   };
 
-  W8<WT> w[MM_JB];
+  W8<WT> wa[MM_JB], wb[MM_JB];   // this tile's weights and the next tile's
   int t = blockIdx.x;
   if constexpr (!MP) {
     stage_issue(b0, b1);
-    load_w(w, t, b0, b1, true);   // the first tile's weights stream while the rows are staged
+    load_w(wa, t, b0, b1, true);   // the first tile's weights stream while the rows are staged
     stage_finish(b0, b1);
   }
 
   float bv = -INFINITY;   // argmax: running best of this thread's columns
   int bi = 0x7fffffff;
-  for (int it = 0; t < ntiles; t += G, ++it) {
+  // One tile with its weights in w; the next tile's weights go to wn before this tile's
+  // MFMAs (unconditional: past the last tile they read 16 bytes at the base).
+  auto tile = [&](int t, int it, W8<WT> (&w)[MM_JB], W8<WT> (&wn)[MM_JB]) {
     // epilogue operands of this thread's output(s) of the tile
     const int n = t * GD_TILE_N + oc;
     const bool own = orow && (PAIR ? n + 1 < N : n < N);
     const EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? n : 0);
+    if constexpr (!MP) load_w(wn, t + G, b0, b1, t + G < ntiles);
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_zero();
@@ -753,8 +756,6 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     }
     settle(eo.b0); settle(eo.b1); settle(eo.r0); settle(eo.c); settle(eo.s);
     settle(__int_as_float((int)eo.kvoff)); settle(__int_as_float((int)(eo.kvoff >> 32)));
-    // the next tile's weights stream while this tile is reduced and stored
-    if constexpr (!MP) load_w(w, t + G, b0, b1, t + G < ntiles);
     float* red = xs + (it & 1) * (MM_NW * R * RS);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -785,6 +786,14 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
           epi_store<EPI>(p, eo, om, n, v, 0.f);
       }
     }
+  };
+  // the two weight buffers alternate between consecutive tiles
+  for (int it = 0; t < ntiles;) {
+    tile(t, it, wa, wb);
+    t += G; ++it;
+    if (t >= ntiles) break;
+    tile(t, it, wb, wa);
+    t += G; ++it;
   }
   if (EPI == EPI_ARGMAX && tid < R * 16) {
     // best of the 16 threads of each row (one 16-lane DPP row)
