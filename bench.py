@@ -8,8 +8,13 @@ prompt ids); prefill is untimed.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value        decode tokens/s of the headline workload (GPT-2 124M shape, batch 1)
-  roofline     the dominant kernel: algorithmic bytes per launch / mean launch time
-               (HIP events around every launch in a profiled eager pass)
+  roofline     the dominant kernel (largest share of the step's kernel time):
+               algorithmic bytes per launch / mean launch time, from HIP event pairs
+               around every launch of a profiled pass whose steps are each enqueued
+               whole behind a short hold, so host enqueue gaps fall outside the pairs
+  step         achieved algorithmic GB/s of the whole step against 8 TB/s and against a
+               measured device-to-device copy; a synchronous variant (token read back
+               and stream synchronized every step)
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload
   batch32      the same measurements for 32 sequences (GPT-2 124M shape, fp32)
 """
@@ -27,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP32_TFLOPS = 157.3    # dense fp32 matrix peak
+MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix peak
 METRIC = "decode tok/s at GPT-2-124M shape, batch 1 and 32; achieved HBM GB/s"
 
 
@@ -103,6 +110,17 @@ def measure(wname: str, steps, warmup: int):
     gpu_ms = e0.elapsed_time(e1)
     ms_step = max(gpu_ms, wall * 1e3) / K
     assert m.device_errors() == 0
+    # synchronous variant: the new tokens read back and the stream synchronized every step
+    rewind(m, tok, first, plen)
+    S = min(K, n_decode)
+    host = torch.empty(tok.shape, dtype=tok.dtype, pin_memory=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(S):
+        m.decode_step(seq_ids, tok, tok)
+        host.copy_(tok, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+    ms_sync = (time.perf_counter() - t0) * 1e3 / S
     # greedy tokens of the first steps after the prompt (for the oracle cross-check)
     rewind(m, tok, first, plen)
     hist = [first.cpu().numpy().copy()]
@@ -112,7 +130,7 @@ def measure(wname: str, steps, warmup: int):
     gpu_tokens = np.stack(hist, 1)
     # profiled eager pass over one generation window: per-kernel time and bytes
     rewind(m, tok, first, plen)
-    m.set_option(gd.OPT_PROFILE, 1)
+    m.set_option(gd.OPT_PROFILE, 2)
     m.profile_read(reset=True)
     P = min(K, n_decode)
     for _ in range(P):
@@ -122,7 +140,7 @@ def measure(wname: str, steps, warmup: int):
     m.close()
     torch.cuda.synchronize()
     return dict(w=w, W=W, prompts=prompts, ms_step=ms_step, K=K, ttft=ttft, stats=stats, P=P,
-                gpu_tokens=gpu_tokens, gpu_ms=gpu_ms, wall_s=wall)
+                gpu_tokens=gpu_tokens, gpu_ms=gpu_ms, wall_s=wall, ms_sync=ms_sync, S=S)
 
 
 def kernel_table(stats, P):
@@ -146,6 +164,27 @@ def kernel_table(stats, P):
     rows.sort(key=lambda r: -r["share"])
     step_bytes = sum(s["bytes"] for s in stats) / P
     return rows, step_bytes, tot / P
+
+
+def gemm_table(stats, P, w):
+    """Per linear role: 2 M N K flops per launch over the mean launch time, as a fraction of
+    the fp32 matrix peak (the MFMA these kernels issue: bf16 weights are widened to fp32)
+    and of the bf16 peak."""
+    s = w.shape
+    qdim, kdim = s.n_head * s.head_dim, s.n_kv_head * s.head_dim
+    fc_n = s.d_ff if s.arch == 0 else 2 * s.d_ff
+    nk = {"linear.qkv": (qdim + 2 * kdim, s.d_model), "linear.o": (s.d_model, qdim), "linear.fc": (fc_n, s.d_model),
+          "linear.down": (s.d_model, s.d_ff), "linear.head": (s.vocab, s.d_model)}
+    out = []
+    for st in stats:
+        if st["role"] not in nk or st["launches"] == 0:
+            continue
+        n, k = nk[st["role"]]
+        avg_us = st["total_us"] / st["launches"]
+        tf = 2.0 * w.batch * n * k / (avg_us * 1e-6) / 1e12
+        out.append(dict(role=st["role"], kernel=st["kernel"], avg_us=round(avg_us, 3), tflops=round(tf, 2),
+                        frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4), frac_bf16_peak=round(tf / MFMA_BF16_TFLOPS, 5)))
+    return out
 
 
 def roofline(rows):
@@ -192,7 +231,82 @@ def summary(res):
     return rows, dict(value=round(tps, 1), ms_per_step=round(res["ms_step"], 4), steps=res["K"],
                       algo_bytes_per_step=round(step_bytes), step_gbps=round(step_gbps, 1),
                       step_hbm_frac=round(step_gbps / HBM_PEAK_GBPS, 4),
-                      kernel_us_per_step=round(kern_us, 2), ttft_s=round(res["ttft"], 4))
+                      copy_gbps=round(COPY_GBPS[0], 1) if COPY_GBPS[0] else None,
+                      step_copy_frac=round(step_gbps / COPY_GBPS[0], 4) if COPY_GBPS[0] else None,
+                      kernel_us_per_step=round(kern_us, 2), ttft_s=round(res["ttft"], 4),
+                      sync_ms_per_step=round(res["ms_sync"], 4), sync_value=round(w.batch / (res["ms_sync"] * 1e-3), 1))
+
+
+def trace_summary(csv_path: str, bench_json: str | None):
+    """Markdown summary of a rocprofv3 --kernel-trace CSV of a bench.py run: per kernel,
+    the mean execution time of the dispatches of each profiled pass (the steps that
+    follow a k_gate hold; these are the launches bench.py times with events) and, when
+    the bench's JSON line is given, the bench's own figure beside it."""
+    import csv
+    import statistics
+
+    def short(n):
+        n = n.replace("void ", "")
+        return n[:n.index("(")] if "(" in n else n
+
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    gates = [i for i, r in enumerate(rows) if short(r["Kernel_Name"]) == "k_gate"]
+    # a pass: consecutive gated steps (at most a few hundred dispatches apart)
+    passes, cur = [], []
+    for g in gates:
+        if cur and g - cur[-1] > 400:
+            passes.append(cur)
+            cur = []
+        cur.append(g)
+    if cur:
+        passes.append(cur)
+    bench = None
+    if bench_json:
+        with open(bench_json) as f:
+            bench = json.loads(f.read().strip().splitlines()[-1])
+    bench_sets = []
+    if bench:
+        bench_sets.append({k["kernel"]: k for k in bench.get("kernels", [])})
+        if "batch32" in bench:
+            bench_sets.append({k["kernel"]: k for k in bench["batch32"].get("kernels", [])})
+    for pi, pas in enumerate(passes):
+        step = pas[1] - pas[0] if len(pas) > 1 else 0
+        lo, hi = pas[0], pas[-1] + step
+        d = {}
+        for r in rows[lo:hi]:
+            k = short(r["Kernel_Name"])
+            if k == "k_gate" or "at::native" in k or "rocclr" in k:
+                continue
+            d.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        bs = bench_sets[pi] if pi < len(bench_sets) else {}
+        print(f"\nProfiled pass {pi + 1}: {len(pas)} steps, dispatches {lo}..{hi}\n")
+        print("| kernel | dispatches | rocprofv3 mean us | bench.py mean us |")
+        print("|---|---|---|---|")
+        for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+            # bench names drop the instantiation's last template arguments for some kernels
+            b = next((x for name, x in bs.items() if k.startswith(name.rstrip(">"))), None)
+            print(f"| `{k}` | {len(v)} | {statistics.mean(v):.2f} | {b['avg_us'] if b else '-'} |")
+
+
+COPY_GBPS = [None]   # measured device-to-device copy rate (read + write bytes / time)
+
+
+def copy_rate():
+    """Read + write bytes per second of a 1 GiB device-to-device copy (best of 6)."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    best = 1e9
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2.0 * (1 << 30) / (best * 1e-3) / 1e9
 
 
 def main():
@@ -206,7 +320,13 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known traffic that "
                          "scales the HBM byte counters of a rocprofv3 --pmc run)")
+    ap.add_argument("--trace-summary", metavar="CSV", help="print a markdown summary of a rocprofv3 kernel trace "
+                    "of a bench.py run (no GPU needed) and exit")
+    ap.add_argument("--bench-json", metavar="FILE", help="with --trace-summary: the bench's JSON line to compare")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.bench_json)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
               "would shard); use --gpus 1", file=sys.stderr)
@@ -224,6 +344,8 @@ def main():
         log(f"[bench] calibration copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
         del src, dst
 
+    COPY_GBPS[0] = copy_rate()
+    log(f"[bench] device-to-device copy: {COPY_GBPS[0]:.0f} GB/s (read + write)")
     log(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps or 'one generation'}")
     res = measure(args.workload, args.steps, args.warmup)
     rows, summ = summary(res)
@@ -249,8 +371,12 @@ def main():
         for r in rows32:
             log(f"  {r['kernel']:<28} {str(r['roles']):<40} {r['launches_per_step']:6.1f}/step "
                 f"{r['avg_us']:9.2f} us {r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
+        gemms = gemm_table(r32["stats"], r32["P"], r32["w"])
+        for g in gemms:
+            log(f"  {g['role']:<12} {g['avg_us']:8.2f} us {g['tflops']:7.2f} TFLOP/s  "
+                f"{100 * g['frac_fp32_peak']:5.1f}% of fp32 MFMA peak")
         out["batch32"] = dict(workload=r32["w"].name, dtype=r32["w"].weight_dtype, **summ32,
-                              roofline=roofline(rows32), kernels=rows32)
+                              roofline=roofline(rows32), gemm_mfma=gemms, kernels=rows32)
     print(json.dumps(out), flush=True)
 
 

@@ -145,7 +145,11 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
  * capture decode steps in hipGraphs, 0 launch kernels directly. */
 #define GD_OPT_LINEAR_VARIANT 1
 #define GD_OPT_USE_GRAPH 2
-#define GD_OPT_PROFILE 3 /* 1: launch eagerly and time every kernel with a HIP event pair */
+#define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
+                          * 1: as enqueued (host enqueue gaps fall inside short pairs);
+                          * 2: each decode step waits behind a 3 ms hold on a helper
+                          * stream while the host enqueues it whole, so its launches run
+                          * back to back */
 gd_status gd_set_option(gd_model* m, int32_t option, int32_t value);
 
 /* Per-kernel profile gathered while GD_OPT_PROFILE is on ("rvllm Metal backend",

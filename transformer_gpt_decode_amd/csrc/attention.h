@@ -155,18 +155,25 @@ __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
 // Merge of the chunk partials of M rows x Hq heads into dst[m * ldd + h * hd + d]:
 // o = sum_c e^(max_c - max) o_c / sum_c e^(max_c - max) sum_c. Chunk 0 always holds at
 // least one position, so the maximum is finite; empty chunks (max -inf, sum 0, o 0)
-// get weight 0. Each thread first issues the partial outputs of its first EPT elements
-// and the (max, sum) of its (row, head, chunk) entries, so the merge costs one memory
-// round trip; the chunk weights of each (row, head) are formed by 8 adjacent lanes and
-// shared through LDS (s_w: M * Hq * GD_ATT_NCH floats). Called by the whole workgroup
-// (nthr threads, a multiple of 64).
+// get weight 0. attn_merge_issue loads each thread's partial outputs of its first EPT
+// elements and the (max, sum) of its first (row, head, chunk) entry; a caller issues it
+// before unrelated loads (vector loads complete in issue order) and runs
+// attn_merge_finish later, so the merge costs one memory round trip. The chunk
+// weights of each (row, head) are formed by 8 adjacent lanes and shared through LDS
+// (s_w: M * Hq * GD_ATT_NCH floats). Called by the whole workgroup (nthr threads, a
+// multiple of 64).
 template <int EPT>
-__device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd, int M, float* dst, int ldd,
-                                float* s_w, int nthr) {
+struct MergeRegs {
+  float oc[EPT][GD_ATT_NCH];
+  float mc, lc;
+};
+
+template <int EPT>
+__device__ __forceinline__ void attn_merge_issue(const float* __restrict__ apart, int Hq, int hd, int M,
+                                                 MergeRegs<EPT>& r, int nthr) {
   static_assert(GD_ATT_NCH == 8, "one chunk per lane of an 8-lane group");
   const int tid = threadIdx.x, K = Hq * hd, stride = hd + 2;
   const int total = M * K, npair = M * Hq * GD_ATT_NCH;
-  float oc[EPT][GD_ATT_NCH];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int i = min(tid + nthr * j, total - 1);
@@ -174,12 +181,25 @@ __device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd,
     const int h = k / hd, d = k - h * hd;
     const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + 2 + d;
 #pragma unroll
-    for (int c = 0; c < GD_ATT_NCH; ++c) oc[j][c] = pp[(size_t)c * stride];
+    for (int c = 0; c < GD_ATT_NCH; ++c) r.oc[j][c] = pp[(size_t)c * stride];
   }
+  const float* pp = apart + (size_t)min(tid, npair - 1) * stride;   // entry (m, h, c) = tid
+  r.mc = pp[0];
+  r.lc = pp[1];
+}
+
+template <int EPT>
+__device__ void attn_merge_finish(const float* __restrict__ apart, int Hq, int hd, int M, const MergeRegs<EPT>& r,
+                                  float* dst, int ldd, float* s_w, int nthr) {
+  const int tid = threadIdx.x, K = Hq * hd, stride = hd + 2;
+  const int total = M * K, npair = M * Hq * GD_ATT_NCH;
   for (int q0 = 0; q0 < npair; q0 += nthr) {   // npair is a multiple of 8: groups never straddle
-    const int q = min(q0 + tid, npair - 1);
-    const float* pp = apart + (size_t)q * stride;   // entry (m, h, c) = q
-    const float mc = pp[0], lc = pp[1];
+    float mc = r.mc, lc = r.lc;
+    if (q0 > 0) {
+      const float* pp = apart + (size_t)min(q0 + tid, npair - 1) * stride;
+      mc = pp[0];
+      lc = pp[1];
+    }
     const float mx = group_max<GD_ATT_NCH>(mc);
     const float e = expf(mc - mx);
     const float l = group_sum<GD_ATT_NCH>(lc * e);
@@ -194,7 +214,7 @@ __device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd,
       const float* w = s_w + ((size_t)m * Hq + k / hd) * GD_ATT_NCH;
       float o = 0.f;
 #pragma unroll
-      for (int c = 0; c < GD_ATT_NCH; ++c) o = fmaf(w[c], oc[j][c], o);
+      for (int c = 0; c < GD_ATT_NCH; ++c) o = fmaf(w[c], r.oc[j][c], o);
       dst[(size_t)m * ldd + k] = o;
     }
   }
@@ -208,6 +228,14 @@ __device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd,
     for (int c = 0; c < GD_ATT_NCH; ++c) o = fmaf(w[c], pp[(size_t)c * stride], o);
     dst[(size_t)m * ldd + k] = o;
   }
+}
+
+template <int EPT>
+__device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd, int M, float* dst, int ldd,
+                                float* s_w, int nthr) {
+  MergeRegs<EPT> r;
+  attn_merge_issue<EPT>(apart, Hq, hd, M, r, nthr);
+  attn_merge_finish<EPT>(apart, Hq, hd, M, r, dst, ldd, s_w, nthr);
 }
 
 // Merge of the chunk partials into o[M][Hq*HD] (rows handled by the matrix-core

@@ -200,13 +200,20 @@ __device__ __forceinline__ void block_sum_rows(float v[GEMV_MAX_ROWS], int M, fl
   }
 }
 
+// Attention merge prologue: its loads are issued with the other row loads, before the
+// weights.
+__device__ __forceinline__ void stage_issue_attn(const LinParams& p, MergeRegs<4>& ar) {
+  if (p.pro != PRO_ATTN) return;
+  attn_merge_issue<4>(p.apart, p.Hq, p.hd, p.M, ar, GD_WG);
+}
+
 template <int XPT>
-__device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const RowRegs<XPT>& rr,
+__device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const RowRegs<XPT>& rr, const MergeRegs<4>& ar,
                              float (*red)[GD_WG / 64][GEMV_MAX_ROWS], float* s_aw) {
   const int tid = threadIdx.x;
   const int M = p.M, K = p.K;
   if (p.pro == PRO_ATTN) {
-    attn_merge_rows<4>(p.apart, p.Hq, p.hd, M, xs, K, s_aw, GD_WG);
+    attn_merge_finish<4>(p.apart, p.Hq, p.hd, M, ar, xs, K, s_aw, GD_WG);
     return;
   }
   const int K4 = K >> 2;
@@ -355,6 +362,8 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   constexpr int XPT = (NC * CE + 15) / 16;
   RowRegs<XPT> rr;
   stage_issue<XPT>(p, rr);
+  MergeRegs<4> ar;
+  stage_issue_attn(p, ar);
   // 1. weights: they do not depend on anything
   VT w[RW][NC];
 #pragma unroll
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   const bool own = EPI != EPI_ARGMAX && om < M && (PAIR ? nw0 + 1 < N : (lane < M * RW && on < N));
   EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? on : 0);
   // 3. activations into LDS, normalized
-  stage_finish<XPT>(p, xs, s_gb, rr, s_red, s_aw);
+  stage_finish<XPT>(p, xs, s_gb, rr, ar, s_red, s_aw);
   __syncthreads();
   // 4. dot products
   float acc[RW][GEMV_MAX_ROWS];

@@ -132,3 +132,11 @@ __global__ __launch_bounds__(GD_WG) void k_argmax_rows(const float* __restrict__
   }
   out[row] = i0;
 }
+
+// Returns after `ticks` of the 100 MHz real-time counter (bounded by its own clock).
+// A profiled decode step is enqueued behind it whole, so its launches then run back to
+// back with no host enqueue gaps inside the per-launch event pairs.
+__global__ void k_gate(long long ticks) {
+  const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+  while ((long long)__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(64);
+}

@@ -5,6 +5,7 @@
 // then you submit it"). Per-step state (positions, lengths, tokens) lives on the
 // device, so a captured step replays without host work beyond the launch.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -50,6 +51,30 @@ extern "C" const char* gd_last_error(void) { return g_err.c_str(); }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int iceil(int a, int b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------- launch profiling
+//
+// While a profiling scope is open on this thread, every launch takes its own start
+// and stop events (hipExtLaunchKernelGGL): the events carry the kernel's execution
+// timestamps, so a scope's time is the sum of its kernels' execution with no queue or
+// host time in it.
+
+static hipEvent_t prof_event(gd_model* m);
+static thread_local gd_model* t_prof_m = nullptr;
+static thread_local std::vector<std::pair<hipEvent_t, hipEvent_t>>* t_prof_pairs = nullptr;
+// where the argmax finalize launches of a profiled head are timed (their own role)
+static thread_local std::vector<std::pair<hipEvent_t, hipEvent_t>>* t_prof_fin = nullptr;
+
+#define GD_LAUNCH(K, G, B, L, S, ...)                                     \
+  do {                                                                     \
+    if (t_prof_pairs) {                                                    \
+      hipEvent_t a_ = prof_event(t_prof_m), b_ = prof_event(t_prof_m);     \
+      hipExtLaunchKernelGGL(K, G, B, L, S, a_, b_, 0, __VA_ARGS__);        \
+      t_prof_pairs->push_back({a_, b_});                                   \
+    } else {                                                               \
+      hipLaunchKernelGGL(K, G, B, L, S, __VA_ARGS__);                      \
+    }                                                                      \
+  } while (0)
 
 // ---------------------------------------------------------- linear planning
 //
@@ -135,14 +160,14 @@ template <int WT, int NC>
 static void launch_gemv_nc(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   const dim3 g(lp.grid), b(GD_WG);
   switch (prm.epi) {
-    case EPI_PLAIN: hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_PLAIN>), g, b, lp.lds, st, prm); break;
-    case EPI_GELU: hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_GELU>), g, b, lp.lds, st, prm); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_QKV>), g, b, lp.lds, st, prm); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemv<WT, NC, 2, EPI_SWIGLU>), g, b, lp.lds, st, prm); break;
-    case EPI_QKV_ROPE: hipLaunchKernelGGL((k_gemv<WT, NC, 2, EPI_QKV_ROPE>), g, b, lp.lds, st, prm); break;
+    case EPI_PLAIN: GD_LAUNCH((k_gemv<WT, NC, 1, EPI_PLAIN>), g, b, lp.lds, st, prm); break;
+    case EPI_GELU: GD_LAUNCH((k_gemv<WT, NC, 1, EPI_GELU>), g, b, lp.lds, st, prm); break;
+    case EPI_QKV: GD_LAUNCH((k_gemv<WT, NC, 1, EPI_QKV>), g, b, lp.lds, st, prm); break;
+    case EPI_SWIGLU: GD_LAUNCH((k_gemv<WT, NC, 2, EPI_SWIGLU>), g, b, lp.lds, st, prm); break;
+    case EPI_QKV_ROPE: GD_LAUNCH((k_gemv<WT, NC, 2, EPI_QKV_ROPE>), g, b, lp.lds, st, prm); break;
     default:
-      if (lp.rw == 4) hipLaunchKernelGGL((k_gemv<WT, NC, 4, EPI_ARGMAX>), g, b, lp.lds, st, prm);
-      else hipLaunchKernelGGL((k_gemv<WT, NC, 1, EPI_ARGMAX>), g, b, lp.lds, st, prm);
+      if (lp.rw == 4) GD_LAUNCH((k_gemv<WT, NC, 4, EPI_ARGMAX>), g, b, lp.lds, st, prm);
+      else GD_LAUNCH((k_gemv<WT, NC, 1, EPI_ARGMAX>), g, b, lp.lds, st, prm);
       break;
   }
 }
@@ -164,7 +189,7 @@ template <int WT, int MT>
 static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   const dim3 g(lp.grid, lp.splits), b(64 * MM_NW);
   const bool nrm = prm.norm != NORM_NONE;
-#define GD_MM(EPI, NRM, MP) hipLaunchKernelGGL((k_mm<WT, MT, EPI, NRM, MP>), g, b, 0, st, prm)
+#define GD_MM(EPI, NRM, MP) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, MP>), g, b, 0, st, prm)
   if (lp.passes > 1) {   // K range wider than one pass: plain or GELU epilogue, no norm
     if (nrm) return hipErrorNotSupported;
     if (prm.epi == EPI_PLAIN) GD_MM(EPI_PLAIN, false, true);
@@ -222,8 +247,10 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
     hipError_t e = launch_linear(wt, lp, p, st);
     if (e != hipSuccess) return e;
     if (p.epi == EPI_ARGMAX) {
-      hipLaunchKernelGGL(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.parts, p.M,
-                         am_out + r0);
+      auto* keep = t_prof_pairs;
+      if (t_prof_pairs) t_prof_pairs = t_prof_fin;
+      GD_LAUNCH(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.parts, p.M, am_out + r0);
+      t_prof_pairs = keep;
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
@@ -292,7 +319,9 @@ struct gd_model {
 
   // per-kernel profiling (GD_OPT_PROFILE)
   bool profile = false;
-  struct ProfRec { int stat; hipEvent_t a, b; double bytes; };
+  bool profile_gated = false;   // profiled decode steps wait behind k_gate while enqueued
+  hipEvent_t gate_evt = nullptr;
+  struct ProfRec { int stat; std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs; double bytes; };
   std::vector<hipEvent_t> ev_free;
   std::vector<ProfRec> prof_pending;
   std::vector<gd_kernel_stat> prof_stats;
@@ -478,7 +507,9 @@ extern "C" void gd_destroy(gd_model* m) {
   if (!m) return;
   if (m->stream) (void)hipStreamSynchronize(m->stream);
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
-  for (auto& r : m->prof_pending) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+  for (auto& r : m->prof_pending)
+    for (auto& pr : r.pairs) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
+  if (m->gate_evt) (void)hipEventDestroy(m->gate_evt);
   for (auto e : m->ev_free) (void)hipEventDestroy(e);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   if (m->staging_evt) (void)hipEventDestroy(m->staging_evt);
@@ -573,7 +604,7 @@ static void put_vec(std::vector<char>& dst, size_t off, const float* src, size_t
 static hipError_t launch_pack(const void* W, int wt, int N, int K, void* dst, hipStream_t st) {
   const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
   const size_t units = mm_packed_bytes(w, N, K) / 16;
-  hipLaunchKernelGGL(k_pack_tiles, dim3((unsigned)((units + GD_WG - 1) / GD_WG)), dim3(GD_WG), 0, st, W, w, N, K, dst,
+  GD_LAUNCH(k_pack_tiles, dim3((unsigned)((units + GD_WG - 1) / GD_WG)), dim3(GD_WG), 0, st, W, w, N, K, dst,
                      units);
   return hipGetLastError();
 }
@@ -720,14 +751,18 @@ extern "C" gd_status gd_profile_read(gd_model* m, gd_kernel_stat* out, int32_t m
   if (!m || !n) return set_err(GD_ERR_INVALID, "NULL argument");
   HIP_TRY(m, hipStreamSynchronize(m->stream));
   for (auto& r : m->prof_pending) {
-    float ms = 0.f;
-    HIP_TRY(m, hipEventElapsedTime(&ms, r.a, r.b));
+    double us = 0.0;
+    for (auto& pr : r.pairs) {
+      float ms = 0.f;
+      HIP_TRY(m, hipEventElapsedTime(&ms, pr.first, pr.second));
+      us += ms * 1000.0;
+      m->ev_free.push_back(pr.first);
+      m->ev_free.push_back(pr.second);
+    }
     gd_kernel_stat& s = m->prof_stats[r.stat];
     s.launches += 1;
-    s.total_us += ms * 1000.0;
+    s.total_us += us;
     s.bytes += r.bytes;
-    m->ev_free.push_back(r.a);
-    m->ev_free.push_back(r.b);
   }
   m->prof_pending.clear();
   *n = (int)m->prof_stats.size();
@@ -751,7 +786,9 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
   } else if (opt == GD_OPT_USE_GRAPH) {
     m->use_graph = v != 0;
   } else if (opt == GD_OPT_PROFILE) {
+    if (v < 0 || v > 2) return set_err(GD_ERR_INVALID, "profile must be 0, 1 or 2");
     m->profile = v != 0;
+    m->profile_gated = v == 2;
   } else {
     return set_err(GD_ERR_INVALID, "unknown option %d", opt);
   }
@@ -795,24 +832,28 @@ static hipEvent_t prof_event(gd_model* m) {
   return e;
 }
 
-// Brackets one launch with events when profiling; call prof_end after the launch.
+// One profiled unit (a role): the launches made while it is open are timed one by one
+// (GD_LAUNCH) and summed into the role's statistics.
 struct ProfScope {
   gd_model* m;
-  hipStream_t st;
   int idx = -1;
-  hipEvent_t a = nullptr;
   double bytes;
-  ProfScope(gd_model* m_, hipStream_t st_, const char* role, const char* kernel, double b) : m(m_), st(st_), bytes(b) {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs;
+  gd_model* save_m = nullptr;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>>* save_p = nullptr;
+  ProfScope(gd_model* m_, hipStream_t, const char* role, const char* kernel, double b) : m(m_), bytes(b) {
     if (!m->profile) return;
     idx = prof_stat_index(m, role, kernel);
-    a = prof_event(m);
-    (void)hipEventRecord(a, st);
+    save_m = t_prof_m;
+    save_p = t_prof_pairs;
+    t_prof_m = m;
+    t_prof_pairs = &pairs;
   }
   ~ProfScope() {
     if (idx < 0) return;
-    hipEvent_t b = prof_event(m);
-    (void)hipEventRecord(b, st);
-    m->prof_pending.push_back({idx, a, b, bytes});
+    t_prof_m = save_m;
+    t_prof_pairs = save_p;
+    m->prof_pending.push_back({idx, std::move(pairs), bytes});
   }
 };
 
@@ -842,16 +883,27 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
   const bool inplace = p.resid == p.y && p.ldr == p.ldy;
   LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE, inplace);
   char kn[64];
-  ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, kn, sizeof(kn)), m->profile ? linear_bytes(m, p) : 0);
-  return run_linear_rows(m->wt, lp, p, st, am_out);
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> fin;
+  hipError_t e;
+  {
+    ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, kn, sizeof(kn)),
+                 m->profile ? linear_bytes(m, p) : 0);
+    t_prof_fin = &fin;
+    e = run_linear_rows(m->wt, lp, p, st, am_out);
+    t_prof_fin = nullptr;
+  }
+  if (m->profile && !fin.empty())
+    m->prof_pending.push_back({prof_stat_index(m, "argmax", "k_argmax_finalize"), std::move(fin),
+                               (double)lp.parts * p.M * 8 + p.M * 4.0});
+  return e;
 }
 
 template <int HD, int G>
 static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, bool paged) {
   static_assert(HD == 64 || HD == 16, "head_dim");
-  constexpr int PPG = HD == 64 ? 4 : 1;
-  if (paged) hipLaunchKernelGGL((k_attention<HD, G, PPG, true>), grid, dim3(GD_WG), 0, st, a);
-  else hipLaunchKernelGGL((k_attention<HD, G, PPG, false>), grid, dim3(GD_WG), 0, st, a);
+  constexpr int PPG = HD == 64 ? 8 : 1;   // 128 positions per step: one step per chunk up to T = 1024
+  if (paged) GD_LAUNCH((k_attention<HD, G, PPG, true>), grid, dim3(GD_WG), 0, st, a);
+  else GD_LAUNCH((k_attention<HD, G, PPG, false>), grid, dim3(GD_WG), 0, st, a);
 }
 
 // Row set-up parameters over the row arrays starting at seq/pos/tok/kvoff.
@@ -955,7 +1007,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
         p.apart = apart;
       } else {
         ProfScope ps(m, st, "attn_merge", "k_attn_merge", (double)M * c.n_head * (c.head_dim + 2) * 4.0 * 2);
-        hipLaunchKernelGGL(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, attn, m->qdim);
+        GD_LAUNCH(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, attn, m->qdim);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.pro = PRO_COPY;
         p.x = attn; p.ldx = m->qdim;
@@ -1054,7 +1106,7 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
     hipError_t e;
     {
       ProfScope ps(m, s, "setup", "k_setup_rows", (double)M * c.d_model * (m->elt * 2 + 4));
-      hipLaunchKernelGGL(k_setup_rows, dim3(M), dim3(GD_WG), 0, s, rp);
+      GD_LAUNCH(k_setup_rows, dim3(M), dim3(GD_WG), 0, s, rp);
       e = hipGetLastError();
     }
     if (e == hipSuccess)
@@ -1074,7 +1126,7 @@ static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, const int* 
                             m->c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rcs) : nullptr);
   {
     ProfScope ps(m, st, "setup", "k_setup_decode", (double)B * m->c.d_model * (m->elt * 2 + 4));
-    hipLaunchKernelGGL(k_setup_decode, dim3(B), dim3(GD_WG), 0, st, rp, m->sp<int>(m->o_sids), tok,
+    GD_LAUNCH(k_setup_decode, dim3(B), dim3(GD_WG), 0, st, rp, m->sp<int>(m->o_sids), tok,
                        m->sp<int>(m->o_len), m->sp<int>(m->o_cap));
   }
   hipError_t e = hipGetLastError();
@@ -1109,7 +1161,19 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
   m->prof_T.clear();
   if (m->profile)
     for (int b = 0; b < B; ++b) m->prof_T.push_back(m->len[sids[b]] + 1);
-  if (m->use_graph && !m->profile) {
+  if (m->profile && m->profile_gated) {
+    // hold the stream (bounded) while the step is enqueued, then let it run whole
+    if (!m->gate_evt) HIP_TRY(m, hipEventCreateWithFlags(&m->gate_evt, hipEventDisableTiming));
+    hipLaunchKernelGGL(k_gate, dim3(1), dim3(64), 0, m->cap_stream, 300000LL);
+    HIP_TRY(m, hipGetLastError());
+    HIP_TRY(m, hipEventRecord(m->gate_evt, m->cap_stream));
+    HIP_TRY(m, hipStreamWaitEvent(s, m->gate_evt, 0));
+    hipError_t e = enqueue_decode(m, s, B, tok_dev, next_dev, logits_dev);
+    if (e != hipSuccess) {
+      m->poisoned = true;
+      return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    }
+  } else if (m->use_graph && !m->profile) {
     GraphKey key{B, tok_dev, next_dev, logits_dev};
     auto it = m->graphs.find(key);
     if (it == m->graphs.end()) {
@@ -1225,7 +1289,7 @@ extern "C" gd_status gd_argmax(const float* logits, int32_t rows, int32_t vocab,
   float* pv = reinterpret_cast<float*>(b);
   int* pi = reinterpret_cast<int*>(b + align_up((size_t)rows * nch * 4, 256));
   int* ctr = reinterpret_cast<int*>(b + 2 * align_up((size_t)rows * nch * 4, 256));
-  hipLaunchKernelGGL(k_argmax_rows, dim3(nch, rows), dim3(GD_WG), 0, reinterpret_cast<hipStream_t>(stream), logits,
+  GD_LAUNCH(k_argmax_rows, dim3(nch, rows), dim3(GD_WG), 0, reinterpret_cast<hipStream_t>(stream), logits,
                      rows, vocab, nch, pv, pi, ctr, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "argmax launch failed: %s", hipGetErrorString(e));
