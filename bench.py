@@ -187,11 +187,40 @@ def gemm_table(stats, P, w):
     return out
 
 
+def kernel_sources_sha256() -> str:
+    """SHA-256 over the HIP sources of the library (names and contents, sorted)."""
+    import hashlib
+    d = os.path.join(ROOT, "transformer_gpt_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) recorded in
+    profiles/hbm_traffic.json, or None when the kernel sources have changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    k = next((v for name, v in rec.get("kernels", {}).items() if name.startswith(kernel.rstrip(">"))), None)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+
+
 def roofline(rows):
     top = rows[0]
     ach = top["bytes_per_launch"] / (top["avg_us"] * 1e-6) / 1e9
+    tr = measured_traffic(top["kernel"])
     return {"bound": "hbm", "kernel": top["kernel"], "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": round(tr) if tr else None,
             "bytes_per_launch": round(top["bytes_per_launch"]), "avg_launch_us": top["avg_us"]}
 
 
@@ -237,11 +266,14 @@ def summary(res):
                       sync_ms_per_step=round(res["ms_sync"], 4), sync_value=round(w.batch / (res["ms_sync"] * 1e-3), 1))
 
 
-def trace_summary(csv_path: str, bench_json: str | None):
-    """Markdown summary of a rocprofv3 --kernel-trace CSV of a bench.py run: per kernel,
-    the mean execution time of the dispatches of each profiled pass (the steps that
-    follow a k_gate hold; these are the launches bench.py times with events) and, when
-    the bench's JSON line is given, the bench's own figure beside it."""
+def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
+    """Markdown summary of a rocprofv3 CSV of a bench.py run (--kernel-trace, or --pmc with
+    one counter): per kernel, over the dispatches of each profiled pass (the steps that
+    follow a k_gate hold; these are the launches bench.py times), the mean execution time
+    or the mean counter value. A counter in KiB is scaled to bytes by the first
+    __amd_rocclr_copyBuffer dispatch, the copy of calib_mib MiB each way that
+    `bench.py --copy-mib` runs first. With the bench's JSON line, its mean time and
+    algorithmic bytes per launch are shown beside."""
     import csv
     import statistics
 
@@ -250,9 +282,15 @@ def trace_summary(csv_path: str, bench_json: str | None):
         return n[:n.index("(")] if "(" in n else n
 
     rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    counter = rows[0].get("Counter_Name") if rows else None
+    factor = None
+    if counter and calib_mib:
+        cp = next(r for r in rows if "copyBuffer" in r["Kernel_Name"])
+        factor = calib_mib * 1024.0 / float(cp["Counter_Value"])
+        print(f"{counter}: the calibration copy ({calib_mib} MiB read, {calib_mib} MiB written) counts "
+              f"{float(cp['Counter_Value']):.1f} KiB, so bytes = {counter} x {factor:.3f} KiB")
     gates = [i for i, r in enumerate(rows) if short(r["Kernel_Name"]) == "k_gate"]
-    # a pass: consecutive gated steps (at most a few hundred dispatches apart)
-    passes, cur = [], []
+    passes, cur = [], []   # a pass: consecutive gated steps (at most a few hundred dispatches apart)
     for g in gates:
         if cur and g - cur[-1] > 400:
             passes.append(cur)
@@ -260,12 +298,10 @@ def trace_summary(csv_path: str, bench_json: str | None):
         cur.append(g)
     if cur:
         passes.append(cur)
-    bench = None
+    bench_sets = []
     if bench_json:
         with open(bench_json) as f:
             bench = json.loads(f.read().strip().splitlines()[-1])
-    bench_sets = []
-    if bench:
         bench_sets.append({k["kernel"]: k for k in bench.get("kernels", [])})
         if "batch32" in bench:
             bench_sets.append({k["kernel"]: k for k in bench["batch32"].get("kernels", [])})
@@ -277,15 +313,27 @@ def trace_summary(csv_path: str, bench_json: str | None):
             k = short(r["Kernel_Name"])
             if k == "k_gate" or "at::native" in k or "rocclr" in k:
                 continue
-            d.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+            v = float(r["Counter_Value"]) if counter else (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            d.setdefault(k, []).append(v)
         bs = bench_sets[pi] if pi < len(bench_sets) else {}
         print(f"\nProfiled pass {pi + 1}: {len(pas)} steps, dispatches {lo}..{hi}\n")
-        print("| kernel | dispatches | rocprofv3 mean us | bench.py mean us |")
-        print("|---|---|---|---|")
+        if counter:
+            print(f"| kernel | dispatches | mean {counter} KiB | MB per dispatch | bench.py algorithmic MB | ratio |")
+            print("|---|---|---|---|---|---|")
+        else:
+            print("| kernel | dispatches | rocprofv3 mean us | bench.py mean us |")
+            print("|---|---|---|---|")
         for k, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
-            # bench names drop the instantiation's last template arguments for some kernels
             b = next((x for name, x in bs.items() if k.startswith(name.rstrip(">"))), None)
-            print(f"| `{k}` | {len(v)} | {statistics.mean(v):.2f} | {b['avg_us'] if b else '-'} |")
+            mean = statistics.mean(v)
+            if counter:
+                mb = mean * factor * 1024 / 1e6 if factor else None
+                alg = b["bytes_per_launch"] / 1e6 if b else None
+                ratio = f"{mb / alg:.3f}" if (mb and alg) else "-"
+                print(f"| `{k}` | {len(v)} | {mean:.1f} | {f'{mb:.3f}' if mb else '-'} | "
+                      f"{f'{alg:.3f}' if alg else '-'} | {ratio} |")
+            else:
+                print(f"| `{k}` | {len(v)} | {mean:.2f} | {b['avg_us'] if b else '-'} |")
 
 
 COPY_GBPS = [None]   # measured device-to-device copy rate (read + write bytes / time)
@@ -323,9 +371,11 @@ def main():
     ap.add_argument("--trace-summary", metavar="CSV", help="print a markdown summary of a rocprofv3 kernel trace "
                     "of a bench.py run (no GPU needed) and exit")
     ap.add_argument("--bench-json", metavar="FILE", help="with --trace-summary: the bench's JSON line to compare")
+    ap.add_argument("--calib-mib", type=int, default=0, help="with --trace-summary of a --pmc CSV: the size of the "
+                    "--copy-mib calibration copy")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.bench_json)
+        trace_summary(args.trace_summary, args.bench_json, args.calib_mib)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
