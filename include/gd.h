@@ -145,6 +145,9 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
  * capture decode steps in hipGraphs, 0 launch kernels directly. */
 #define GD_OPT_LINEAR_VARIANT 1
 #define GD_OPT_USE_GRAPH 2
+#define GD_OPT_FUSE_ATTN_O 4 /* 1 (default): up to 4 rows whose contexts all hold at most
+                              * 256 positions run attention fused with the output
+                              * projection; 0: always split-context attention */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

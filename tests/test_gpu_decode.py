@@ -17,6 +17,8 @@ from tests.gpu_util import compare_generation, device, gd_model, gpu_generate, o
 pytestmark = pytest.mark.gpu
 
 TINY_LLAMA = synth.Shape(synth.ARCH_LLAMA, 2, 96, 6, 2, 16, 128, 300, 64, 1e-5, 1e4)
+# head_dim 64 with 3 query heads per KV head (the C5 attention shape) in a small model
+LLAMA_HD64 = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 320, 1e-5, 1e5)
 
 
 def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, pool=None, max_seqs=None):
@@ -59,6 +61,28 @@ def test_tiny_llama_paged(shuffled):
     prompts = synth.make_prompts(w)
     tab, pool = (synth.make_block_tables if shuffled else synth.identity_block_tables)(w, prompts)
     _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool)
+
+
+@pytest.mark.parametrize("batch", [2, 6], ids=["fused_attn_o", "split_context"])
+def test_llama_hd64_gqa_paged(batch):
+    """Up to 4 rows at contexts of at most 256 positions run attention fused with the
+    output projection; more rows run split-context attention, a merge and the MFMA
+    projection. Both at head_dim 64, 3 query heads per KV head, paged, bf16 weights."""
+    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 11, batch, (5, 60), 10, kv_block=16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool)
+
+
+def test_context_crosses_fused_limit():
+    """A batch-1 generation whose context grows past 256 positions: the decode graph
+    switches from the fused attention + output projection to split-context attention."""
+    shape = dataclasses.replace(synth.WORKLOADS["tiny"].shape, n_ctx=400)
+    w = synth.Workload("tiny_long", shape, synth.Init(), 5, 1, (248, 248), 20)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    _run_and_compare(w, W, prompts, 1e-3)
 
 
 def test_gpt2_124m_batch1():

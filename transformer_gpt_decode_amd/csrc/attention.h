@@ -16,7 +16,9 @@
 // HD/4 lanes take one position per step (float4 of K and V per lane, all loads of a
 // step issued before the arithmetic) with an online max-subtracted softmax; the
 // groups are merged in LDS into one partial (max, sum, weighted V) per query head.
-// Empty chunks (T < GD_ATT_NCH) write max = -inf, sum = 0.
+// Empty chunks (T < GD_ATT_NCH) write max = -inf, sum = 0. For a few rows at short
+// contexts, k_attn_o instead scans each row's whole context and applies the output
+// projection in the same launch (see there).
 #pragma once
 #include "common.h"
 
@@ -33,21 +35,29 @@ struct AttnParams {
   float* part;                        // [M][Hq][GD_ATT_NCH][HD + 2]: max, sum, o[HD]
 };
 
+// Online softmax of the G query heads of KV head kh of `row` over positions [p0, p1):
+// groups of HD/4 lanes take one position per step (float4 of K and V per lane, all
+// loads of a step issued before the arithmetic), each keeping a running max, sum and
+// weighted V per query head; the groups are then merged in LDS. On return (after a
+// barrier) thread tid < G * HD holds, for query head g = tid / HD and dimension
+// d = tid % HD, the range's max, sum and weighted V (max -inf and zeros for an empty
+// range).
+template <int HD, int G, int PPG>
+struct AttnScanLds {
+  static constexpr int LG = HD / 4, NG = GD_WG / LG;
+  float m[NG][G], l[NG][G];
+  __align__(16) float o[NG][G][HD];
+};
+
 template <int HD, int G, int PPG, bool PAGED>
-__global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
+__device__ void attn_scan(const AttnParams& p, int row, int kh, int p0, int p1, AttnScanLds<HD, G, PPG>& sh,
+                          float& m_out, float& l_out, float& o_out) {
   constexpr int LG = HD / 4;            // lanes per position group
   constexpr int NG = GD_WG / LG;        // position groups per workgroup
   constexpr int STEP = NG * PPG;        // positions per step
-  __shared__ float s_m[NG][G], s_l[NG][G];
-  __shared__ __align__(16) float s_o[NG][G][HD];
-
-  const int c = blockIdx.x, kh = blockIdx.y, row = blockIdx.z;
   const int tid = threadIdx.x;
   const int grp = tid / LG, gl = tid % LG;
   const int pos = p.row_pos[row];
-  const int T = pos + 1;
-  const int L = (T + GD_ATT_NCH - 1) / GD_ATT_NCH;
-  const int p0 = min(T, c * L), p1 = min(T, p0 + L);
 
   f32x4 q[G];
 #pragma unroll
@@ -128,27 +138,112 @@ __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if (gl == 0) { s_m[grp][g] = mx[g]; s_l[grp][g] = l[g]; }
-    *reinterpret_cast<f32x4*>(&s_o[grp][g][gl * 4]) = o[g];
+    if (gl == 0) { sh.m[grp][g] = mx[g]; sh.l[grp][g] = l[g]; }
+    *reinterpret_cast<f32x4*>(&sh.o[grp][g][gl * 4]) = o[g];
   }
   __syncthreads();
-  // merge the NG groups into the chunk's partial: one thread per (query head g, dim d)
+  // merge the NG groups: one thread per (query head g, dim d)
+  m_out = -INFINITY;
+  l_out = o_out = 0.f;
   if (tid < G * HD) {
     const int g = tid / HD, d = tid % HD;
     float m = -INFINITY;
-    for (int i = 0; i < NG; ++i) m = fmaxf(m, s_m[i][g]);
+    for (int i = 0; i < NG; ++i) m = fmaxf(m, sh.m[i][g]);
     float ls = 0.f, acc = 0.f;
     if (m != -INFINITY) {
       for (int i = 0; i < NG; ++i) {
-        if (s_l[i][g] == 0.f) continue;   // group saw no position
-        const float w = expf(s_m[i][g] - m);
-        ls = fmaf(s_l[i][g], w, ls);
-        acc = fmaf(s_o[i][g][d], w, acc);
+        if (sh.l[i][g] == 0.f) continue;   // group saw no position
+        const float w = expf(sh.m[i][g] - m);
+        ls = fmaf(sh.l[i][g], w, ls);
+        acc = fmaf(sh.o[i][g][d], w, acc);
       }
     }
+    m_out = m;
+    l_out = ls;
+    o_out = acc;
+  }
+}
+
+template <int HD, int G, int PPG, bool PAGED>
+__global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
+  __shared__ AttnScanLds<HD, G, PPG> sh;
+  const int c = blockIdx.x, kh = blockIdx.y, row = blockIdx.z;
+  const int T = p.row_pos[row] + 1;
+  const int L = (T + GD_ATT_NCH - 1) / GD_ATT_NCH;
+  const int p0 = min(T, c * L), p1 = min(T, p0 + L);
+  float m, l, o;
+  attn_scan<HD, G, PPG, PAGED>(p, row, kh, p0, p1, sh, m, l, o);
+  if (threadIdx.x < G * HD) {
+    const int g = threadIdx.x / HD, d = threadIdx.x % HD;
     float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * GD_ATT_NCH + c) * (HD + 2);
-    pp[2 + d] = acc;
-    if (d == 0) { pp[0] = m; pp[1] = ls; }
+    pp[2 + d] = o;
+    if (d == 0) { pp[0] = m; pp[1] = l; }
+  }
+}
+
+// Attention fused with the output projection, for a few rows at short contexts.
+// Workgroup (slice s, KV head kh, row) scans the whole context of its G query heads
+// (the attention is recomputed by every slice of the head: at short contexts its K/V
+// come from cache), normalizes them, and adds their share of the projection,
+// sum over g, d of o[g][d] W[n][(kh G + g) HD + d], to the residual rows n of its
+// slice with float atomics (the bias from kh == 0). A slice is ROWS consecutive n; its
+// weights (HD/4 lanes per row, float4 or four bf16 each) are loaded before the scan.
+struct AttnOParams {
+  const void* w;          // W_o [N][K] (K = Hq * HD), fp32 or bf16 bits
+  const float* bias;      // never NULL
+  float* y; int ldy;      // residual rows, updated in place
+  int N, K;
+};
+
+template <int HD>
+struct AttnORows { static constexpr int LG = HD / 4, PER_PASS = GD_WG / LG, PASSES = HD == 64 ? 3 : 1,
+                   ROWS = PER_PASS * PASSES; };
+
+template <int HD, int G, int PPG, bool PAGED, int WT>
+__global__ __launch_bounds__(GD_WG) void k_attn_o(AttnParams p, AttnOParams po) {
+  using RT = AttnORows<HD>;
+  __shared__ AttnScanLds<HD, G, PPG> sh;
+  __shared__ __align__(16) float s_o[G][HD];
+  const int kh = blockIdx.y, row = blockIdx.z;
+  const int tid = threadIdx.x, grp = tid / RT::LG, gl = tid % RT::LG;
+  const int n0 = blockIdx.x * RT::ROWS;
+  // the slice's weights first: they depend on nothing
+  f32x4 wv[RT::PASSES][G];
+#pragma unroll
+  for (int ps = 0; ps < RT::PASSES; ++ps) {
+    const int n = min(n0 + ps * RT::PER_PASS + grp, po.N - 1);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const size_t off = (size_t)n * po.K + (kh * G + g) * HD + gl * 4;
+      if constexpr (WT == 0) {
+        wv[ps][g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(po.w) + off);
+      } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(po.w) + off);
+        wv[ps][g] = (f32x4){bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+      }
+    }
+  }
+  const int T = p.row_pos[row] + 1;
+  float m, l, o;
+  attn_scan<HD, G, PPG, PAGED>(p, row, kh, 0, T, sh, m, l, o);
+  if (tid < G * HD) s_o[tid / HD][tid % HD] = l > 0.f ? o / l : 0.f;
+  __syncthreads();
+#pragma unroll
+  for (int ps = 0; ps < RT::PASSES; ++ps) {
+    const int n = n0 + ps * RT::PER_PASS + grp;
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const f32x4 ov = *reinterpret_cast<const f32x4*>(&s_o[g][gl * 4]);
+      acc = fmaf(wv[ps][g].x, ov.x, acc);
+      acc = fmaf(wv[ps][g].y, ov.y, acc);
+      acc = fmaf(wv[ps][g].z, ov.z, acc);
+      acc = fmaf(wv[ps][g].w, ov.w, acc);
+    }
+    acc = group_sum<RT::LG>(acc);
+    if (gl == 0 && n < po.N)
+      __hip_atomic_fetch_add(po.y + (size_t)row * po.ldy + n, acc + (kh == 0 ? po.bias[n] : 0.f), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

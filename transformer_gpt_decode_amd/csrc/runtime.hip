@@ -269,10 +269,15 @@ struct GraphKey {
   const void* tok;
   void* next;
   void* logits;
+  bool short_ctx;   // every row attends to at most kFusedAttnOMaxT positions
   bool operator<(const GraphKey& o) const {
-    return std::tie(batch, tok, next, logits) < std::tie(o.batch, o.tok, o.next, o.logits);
+    return std::tie(batch, tok, next, logits, short_ctx) < std::tie(o.batch, o.tok, o.next, o.logits, o.short_ctx);
   }
 };
+
+// Rows of at most this many positions (and few rows) run attention fused with the output
+// projection: every projection slice recomputes the attention from K/V in cache.
+static const int kFusedAttnOMaxT = 256;
 
 struct gd_model {
   gd_config c;
@@ -281,6 +286,7 @@ struct gd_model {
   bool poisoned = false;
   int variant = 0;
   bool use_graph = true;
+  bool fuse_attn_o = true;
   int dev = 0;
 
   // derived shapes
@@ -785,6 +791,8 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->variant = v;
   } else if (opt == GD_OPT_USE_GRAPH) {
     m->use_graph = v != 0;
+  } else if (opt == GD_OPT_FUSE_ATTN_O) {
+    m->fuse_attn_o = v != 0;
   } else if (opt == GD_OPT_PROFILE) {
     if (v < 0 || v > 2) return set_err(GD_ERR_INVALID, "profile must be 0, 1 or 2");
     m->profile = v != 0;
@@ -899,6 +907,20 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
 }
 
 template <int HD, int G>
+static void launch_attn_o(hipStream_t st, const AttnParams& a, const AttnOParams& po, bool paged, int wt, int M,
+                          int Hkv) {
+  constexpr int PPG = HD == 64 ? 8 : 1;
+  const dim3 grid(iceil(po.N, AttnORows<HD>::ROWS), Hkv, M), b(GD_WG);
+  if (paged) {
+    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, true, 0>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_o<HD, G, PPG, true, 1>), grid, b, 0, st, a, po);
+  } else {
+    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, false, 0>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_o<HD, G, PPG, false, 1>), grid, b, 0, st, a, po);
+  }
+}
+
+template <int HD, int G>
 static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, bool paged) {
   static_assert(HD == 64 || HD == 16, "head_dim");
   constexpr int PPG = HD == 64 ? 8 : 1;   // 128 positions per step: one step per chunk up to T = 1024
@@ -926,8 +948,8 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
 
 // Enqueues the forward pass of M (<= 32) rows with device-resident row metadata.
 // If head_out is not NULL, computes logits/argmax for rows [head_row, head_row + head_rows).
-static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp, int M, int head_row, int head_rows,
-                               int* head_out, float* logits) {
+static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp, int M, int max_T, int head_row,
+                               int head_rows, int* head_out, float* logits) {
   const gd_config& c = m->c;
   const int d = c.d_model, ff = c.d_ff;
   float* x = m->sp<float>(m->o_x);
@@ -940,6 +962,8 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   hipError_t e;
   // the gemv O-projection merges the attention partials in its prologue
   const bool o_gemv = plan_linear(M, c.d_model, m->qdim, m->wt, m->variant, EPI_PLAIN, false).var == 0;
+  // few rows at short contexts: attention fused with the output projection
+  const bool fuse_ao = m->fuse_attn_o && o_gemv && max_T <= kFusedAttnOMaxT;
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
@@ -975,20 +999,35 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.kv_hstride = m->bsize * c.head_dim;
       if ((e = run_linear(m, st, "linear.qkv", p)) != hipSuccess) return e;
     }
-    // causal attention of every row against its sequence's cache (split-context partials)
-    {
-      AttnParams a;
-      memset(&a, 0, sizeof(a));
-      a.q = q; a.ldq = m->qdim;
-      a.kc = m->kpool(l); a.vc = m->vpool(l);
-      a.table = m->sp<int>(m->o_table); a.max_blocks = m->max_blocks; a.block_size = m->bsize; a.nblk = m->nblk;
-      a.Hq = c.n_head; a.Hkv = c.n_kv_head; a.row_seq = rp.row_seq; a.row_pos = rp.row_pos;
-      a.row_kvoff = rp.row_kvoff;
-      a.M = M;
-      a.scale = 1.0f / std::sqrt((float)c.head_dim);
-      a.part = apart;
+    AttnParams a;
+    memset(&a, 0, sizeof(a));
+    a.q = q; a.ldq = m->qdim;
+    a.kc = m->kpool(l); a.vc = m->vpool(l);
+    a.table = m->sp<int>(m->o_table); a.max_blocks = m->max_blocks; a.block_size = m->bsize; a.nblk = m->nblk;
+    a.Hq = c.n_head; a.Hkv = c.n_kv_head; a.row_seq = rp.row_seq; a.row_pos = rp.row_pos;
+    a.row_kvoff = rp.row_kvoff;
+    a.M = M;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    a.part = apart;
+    const bool paged = c.kv_block_size > 0;
+    if (fuse_ao) {
+      // attention + output projection + bias + residual (in place on x), one launch
+      AttnOParams po;
+      po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
+      po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
+      char kn[48];
+      snprintf(kn, sizeof(kn), "k_attn_o<%d, %d>", c.head_dim, G);
+      ProfScope ps(m, st, "attn_o", kn,
+                   kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4 +
+                       (double)d * m->qdim * m->elt + (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
+      if (c.head_dim == 64 && G == 1) launch_attn_o<64, 1>(st, a, po, paged, m->wt, M, c.n_kv_head);
+      else if (c.head_dim == 64) launch_attn_o<64, 3>(st, a, po, paged, m->wt, M, c.n_kv_head);
+      else if (G == 1) launch_attn_o<16, 1>(st, a, po, paged, m->wt, M, c.n_kv_head);
+      else launch_attn_o<16, 3>(st, a, po, paged, m->wt, M, c.n_kv_head);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      // causal attention of every row against its sequence's cache (split-context partials)
       dim3 grid(GD_ATT_NCH, c.n_kv_head, M);
-      const bool paged = c.kv_block_size > 0;
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attention<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attention", kn, kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4);
@@ -1000,7 +1039,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     }
     // output projection + bias + residual (in place on x); the gemv kernel merges the
     // attention partials in its prologue, the mfma path merges them in a kernel first
-    {
+    if (!fuse_ao) {
       LinParams p = base;
       if (o_gemv) {
         p.pro = PRO_ATTN;
@@ -1110,7 +1149,7 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
       e = hipGetLastError();
     }
     if (e == hipSuccess)
-      e = enqueue_rows(m, s, rp, M, M - 1, 1, last ? next_dev : nullptr, last ? logits_dev : nullptr);
+      e = enqueue_rows(m, s, rp, M, p0 + r0 + M, M - 1, 1, last ? next_dev : nullptr, last ? logits_dev : nullptr);
     if (e != hipSuccess) {
       m->poisoned = true;
       return set_err(GD_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
@@ -1120,7 +1159,8 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
   return GD_OK;
 }
 
-static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, const int* tok, int* next, float* logits) {
+static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, int max_T, const int* tok, int* next,
+                                 float* logits) {
   RowParams rp = row_params(m, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
                             m->sp<long long>(m->o_rkv),
                             m->c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rcs) : nullptr);
@@ -1131,7 +1171,7 @@ static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, const int* 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return enqueue_rows(m, st, rp, B, 0, B, next, logits);
+  return enqueue_rows(m, st, rp, B, max_T, 0, B, next, logits);
 }
 
 extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids, const int32_t* tok_dev,
@@ -1161,6 +1201,8 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
   m->prof_T.clear();
   if (m->profile)
     for (int b = 0; b < B; ++b) m->prof_T.push_back(m->len[sids[b]] + 1);
+  int max_T = 0;   // attended positions of the longest row
+  for (int b = 0; b < B; ++b) max_T = std::max(max_T, m->len[sids[b]] + 1);
   if (m->profile && m->profile_gated) {
     // hold the stream (bounded) while the step is enqueued, then let it run whole
     if (!m->gate_evt) HIP_TRY(m, hipEventCreateWithFlags(&m->gate_evt, hipEventDisableTiming));
@@ -1168,18 +1210,18 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     HIP_TRY(m, hipGetLastError());
     HIP_TRY(m, hipEventRecord(m->gate_evt, m->cap_stream));
     HIP_TRY(m, hipStreamWaitEvent(s, m->gate_evt, 0));
-    hipError_t e = enqueue_decode(m, s, B, tok_dev, next_dev, logits_dev);
+    hipError_t e = enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
     if (e != hipSuccess) {
       m->poisoned = true;
       return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     }
   } else if (m->use_graph && !m->profile) {
-    GraphKey key{B, tok_dev, next_dev, logits_dev};
+    GraphKey key{B, tok_dev, next_dev, logits_dev, max_T <= kFusedAttnOMaxT};
     auto it = m->graphs.find(key);
     if (it == m->graphs.end()) {
       hipGraph_t g;
       HIP_TRY(m, hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
-      hipError_t e = enqueue_decode(m, m->cap_stream, B, tok_dev, next_dev, logits_dev);
+      hipError_t e = enqueue_decode(m, m->cap_stream, B, max_T, tok_dev, next_dev, logits_dev);
       hipError_t e2 = hipStreamEndCapture(m->cap_stream, &g);
       if (e != hipSuccess || e2 != hipSuccess) {
         m->poisoned = true;
@@ -1196,7 +1238,7 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     }
     HIP_TRY(m, hipGraphLaunch(it->second, s));
   } else {
-    hipError_t e = enqueue_decode(m, s, B, tok_dev, next_dev, logits_dev);
+    hipError_t e = enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
     if (e != hipSuccess) {
       m->poisoned = true;
       return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
