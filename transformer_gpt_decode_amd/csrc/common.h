@@ -88,6 +88,26 @@ __device__ __forceinline__ float group_max(float v) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// Wave sums of NV values at once: each DPP step is applied to all of them, so the
+// reductions overlap instead of running one after another.
+template <int NV>
+__device__ __forceinline__ void wave_sum_n(float (&v)[NV]) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += dpp_f<DPP_QUAD_1032>(v[k]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += dpp_f<DPP_QUAD_2301>(v[k]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += dpp_f<DPP_ROW_HALF_MIRROR>(v[k]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] += dpp_f<DPP_ROW_MIRROR>(v[k]);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int b = __float_as_int(v[k]);
+    v[k] = (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+           (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+  }
+}
+
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // Agent-scope (whole device) atomics and fences for the last-arriver reductions.

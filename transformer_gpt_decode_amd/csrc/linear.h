@@ -207,6 +207,44 @@ __device__ __forceinline__ void stage_issue_attn(const LinParams& p, MergeRegs<4
   attn_merge_issue<4>(p.apart, p.Hq, p.hd, p.M, ar, GD_WG);
 }
 
+// Both sums of the register LayerNorm path in one workgroup exchange (one barrier).
+__device__ __forceinline__ void block_sum_rows2(float a[GEMV_MAX_ROWS], float b[GEMV_MAX_ROWS], int M,
+                                                float (*red)[GD_WG / 64][GEMV_MAX_ROWS]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float v[2 * GEMV_MAX_ROWS];
+  if (M == 1) {   // the batch-1 case: two sums only
+    float v1[2] = {a[0], b[0]};
+    wave_sum_n<2>(v1);
+    v[0] = v1[0];
+    v[GEMV_MAX_ROWS] = v1[1];
+#pragma unroll
+    for (int m = 1; m < GEMV_MAX_ROWS; ++m) v[m] = v[GEMV_MAX_ROWS + m] = 0.f;
+  } else {
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+      v[m] = m < M ? a[m] : 0.f;
+      v[GEMV_MAX_ROWS + m] = m < M ? b[m] : 0.f;
+    }
+    wave_sum_n<2 * GEMV_MAX_ROWS>(v);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+      red[0][wave][m] = v[m];
+      red[1][wave][m] = v[GEMV_MAX_ROWS + m];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+    float ta = 0.f, tb = 0.f;
+#pragma unroll
+    for (int w = 0; w < GD_WG / 64; ++w) { ta += red[0][w][m]; tb += red[1][w][m]; }
+    a[m] = ta;
+    b[m] = tb;
+  }
+}
+
 template <int XPT>
 __device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const RowRegs<XPT>& rr, const MergeRegs<4>& ar,
                              float (*red)[GD_WG / 64][GEMV_MAX_ROWS], float* s_aw) {
@@ -242,8 +280,7 @@ __device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const R
           }
       }
     }
-    block_sum_rows(s1, M, red[0]);
-    block_sum_rows(s2, M, red[1]);
+    block_sum_rows2(s1, s2, M, red);
     float mu[GEMV_MAX_ROWS], rs[GEMV_MAX_ROWS];
 #pragma unroll
     for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
