@@ -137,7 +137,8 @@ gd_status gd_decode_step(gd_model* m, int32_t batch, const int32_t* seq_ids_host
 
 /* Waits for the stream and returns the device error flags (bit 0: token id out of
  * range; bit 1: position beyond a sequence's capacity; bit 2: block table entry out
- * of range), then clears them. */
+ * of range; bit 3: a single-launch decode step timed out waiting for one of its own
+ * phases and was abandoned, its outputs are invalid), then clears them. */
 gd_status gd_device_errors(gd_model* m, int32_t* flags);
 
 /* Tuning/testing switches. GD_OPT_LINEAR_VARIANT: 0 auto (VALU GEMV for <= 4 rows,
@@ -148,6 +149,14 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
 #define GD_OPT_FUSE_ATTN_O 4 /* 1 (default): up to 4 rows whose contexts all hold at most
                               * 256 positions run attention fused with the output
                               * projection; 0: always split-context attention */
+#define GD_OPT_PERSISTENT 5 /* 1: a one-sequence decode step of the GPT-2 layout runs as
+                             * one launch with one workgroup per CU (phases hand over
+                             * through tagged words in device memory) for the GPT-2 124M
+                             * and tiny shapes (n_ctx <= 1024); 0 (default): the kernel
+                             * chain, which measures faster on this GPU */
+#define GD_OPT_PERSISTENT_SPIN_US 6 /* bound of every wait inside the single-launch step, in
+                                     * microseconds (default 20000); a step that exceeds it is
+                                     * abandoned and flagged (device error bit 3) */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

@@ -15,7 +15,7 @@ def device():
     return torch.device("cuda", 0)
 
 
-def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True):
+def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True, persistent=False):
     import transformer_gpt_decode_amd as gd
     s = workload.shape
     kw = dict(max_seqs=max_seqs or workload.batch, max_batch=max_batch or workload.batch)
@@ -25,6 +25,7 @@ def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, varia
     m.load_weights(W)
     m.set_option(gd.OPT_LINEAR_VARIANT, variant)
     m.set_option(gd.OPT_USE_GRAPH, 1 if graph else 0)
+    m.set_option(gd.OPT_PERSISTENT, 1 if persistent else 0)
     return m
 
 

@@ -21,9 +21,10 @@ TINY_LLAMA = synth.Shape(synth.ARCH_LLAMA, 2, 96, 6, 2, 16, 128, 300, 64, 1e-5, 
 LLAMA_HD64 = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 320, 1e-5, 1e5)
 
 
-def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, pool=None, max_seqs=None):
+def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, pool=None, max_seqs=None,
+                     persistent=False):
     ref_tok, ref_lg = oracle_generate(w, W, prompts)
-    m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph)
+    m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph, persistent=persistent)
     tok, lg = gpu_generate(m, prompts, w.n_generate, tables=tables)
     assert m.device_errors() == 0
     rep = compare_generation(tok, lg, ref_tok, ref_lg, tol)
@@ -85,12 +86,13 @@ def test_context_crosses_fused_limit():
     _run_and_compare(w, W, prompts, 1e-3)
 
 
-def test_gpt2_124m_batch1():
+@pytest.mark.parametrize("persistent", [True, False], ids=["single_launch", "chain"])
+def test_gpt2_124m_batch1(persistent):
     """GPT-2 124M shape, batch 1, 8 prompt ids, 128 generated tokens (fp32)."""
     w = synth.WORKLOADS["gpt2_b1"]
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
-    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, persistent=persistent)
     print("gpt2_b1", rep)
 
 

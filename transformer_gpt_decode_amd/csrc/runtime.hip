@@ -23,6 +23,7 @@
 #include "linear.h"
 #include "attention.h"
 #include "misc.h"
+#include "persistent.h"
 
 // ------------------------------------------------------------------ errors
 
@@ -287,7 +288,10 @@ struct gd_model {
   int variant = 0;
   bool use_graph = true;
   bool fuse_attn_o = true;
+  bool use_pk = false;  // single-launch decode step for one sequence (GD_OPT_PERSISTENT; measured slower)
+  long long pk_spin_us = 20000;   // bound of its waits (GD_OPT_PERSISTENT_SPIN_US)
   int dev = 0;
+  int n_cu = 0;         // compute units: workgroups of the single-launch step
 
   // derived shapes
   int qdim, kdim, qkvdim, fcN, hdim, wt;
@@ -311,6 +315,12 @@ struct gd_model {
 
   // scratch offsets (bytes)
   size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart, o_zero;
+  // single-launch decode step: exchange words, layer table, abort tag
+  bool pk_ok = false;
+  unsigned pk_tag = 0;
+  size_t o_xb = 0, o_pkabort = 0;
+  long long pk_xl = 0, pk_att = 0, pk_xo = 0, pk_h = 0, pk_xd = 0, pk_rs_att = 0, pk_rs_d = 0, pk_rs_h = 0, pk_arg = 0;
+  size_t pk_words = 0;
   size_t o_rseq, o_rpos, o_rtok, o_rkv, o_rcs, o_pseq, o_ppos, o_ptok, o_pkv, o_pcs, o_len, o_cap, o_sids, o_table, o_err, o_rope;
 
   // host mirror
@@ -366,6 +376,35 @@ static gd_status check_cfg(const gd_config* c) {
     return set_err(GD_ERR_INVALID, "bad paged cache sizes");
   if (!(c->norm_eps > 0.f)) return set_err(GD_ERR_INVALID, "norm_eps must be > 0");
   return GD_OK;
+}
+
+// Weight chunks (16 bytes) per lane of a K-long row in the single-launch step.
+static int pk_chunks(int K, int wt) { return iceil(K, 64 * (wt == GD_WEIGHT_F32 ? 4 : 8)); }
+
+// The single-launch decode step handles one sequence of the GPT-2 layout whose shapes
+// match an instantiated kernel and fit its LDS staging.
+static bool pk_supported(const gd_model* m) {
+  const gd_config& c = m->c;
+  if (c.arch != GD_ARCH_GPT2 || m->n_cu < 1 || m->n_cu > PK_MAXWG) return false;
+  if (c.d_model > PK_DMAX || c.d_model % 64 || c.d_ff > PK_INMAX || c.n_ctx > PK_ACH * PK_MAXNCH) return false;
+  if (c.n_head * PK_MAXNCH * (c.head_dim + 2) > PK_INMAX || c.n_head * PK_MAXNCH > m->n_cu) return false;
+  if (iceil(m->qkvdim, m->n_cu) > 2 * PK_CW || iceil(c.d_ff, m->n_cu) > 2 * PK_CW || iceil(c.d_model, m->n_cu) > PK_CW)
+    return false;
+  if (c.kv_block_size > 0 && (c.kv_block_size & (c.kv_block_size - 1))) return false;   // power-of-two blocks
+  if (m->layer_kv_floats() * 4 >= (1ull << 31)) return false;   // 32-bit byte offsets in a pool
+  // every layer's tensors at a constant stride from layer 0's (the kernel adds l x stride)
+  for (int l = 1; l < c.n_layer; ++l) {
+    const LayerOff &a = m->L[l], &z = m->L[0];
+    const size_t st = m->L[1].n1g - z.n1g;
+    const size_t d = (size_t)l * st;
+    if (a.n1g != z.n1g + d || a.n1b != z.n1b + d || a.wqkv != z.wqkv + d || a.bqkv != z.bqkv + d || a.wo != z.wo + d ||
+        a.bo != z.bo + d || a.n2g != z.n2g + d || a.n2b != z.n2b + d || a.wfc != z.wfc + d || a.bfc != z.bfc + d ||
+        a.wproj != z.wproj + d || a.bproj != z.bproj + d)
+      return false;
+  }
+  // instantiated shapes: GPT-2 124M and the tiny decoder
+  return (c.d_model == 768 && c.d_ff == 3072 && c.head_dim == 64) ||
+         (c.d_model == 64 && c.d_ff == 256 && c.head_dim == 16);
 }
 
 static void layout(gd_model* m) {
@@ -463,6 +502,24 @@ static void layout(gd_model* m) {
   m->o_table = take((size_t)c.max_seqs * m->max_blocks * 4);
   m->o_err = take(4);
   m->o_rope = c.arch == GD_ARCH_LLAMA ? take((size_t)c.n_ctx * c.head_dim * 4) : 0;
+  // single-launch decode step (one sequence, GPT-2 layout): exchange regions per layer
+  m->pk_ok = pk_supported(m);
+  if (m->pk_ok) {
+    auto r64 = [](long long w) { return (w + 63) / 64 * 64; };   // 512-byte granules
+    const long long d = c.d_model, hd = c.head_dim, H = c.n_head;
+    m->pk_rs_att = r64(H * PK_MAXNCH * (hd + 2));
+    m->pk_rs_d = r64(d);
+    m->pk_rs_h = r64(c.d_ff);
+    m->pk_att = r64(m->qkvdim);
+    m->pk_xo = m->pk_att + PK_NREP * m->pk_rs_att;
+    m->pk_h = m->pk_xo + PK_NREP * m->pk_rs_d;
+    m->pk_xd = m->pk_h + PK_NREP * m->pk_rs_h;
+    m->pk_xl = m->pk_xd + PK_NREP * m->pk_rs_d;
+    m->pk_arg = m->pk_xl * c.n_layer;
+    m->pk_words = (size_t)(m->pk_arg + r64(2 * PK_MAXWG));
+    m->o_xb = take(m->pk_words * 8);
+    m->o_pkabort = take(4);
+  }
   m->s_bytes = off;
 }
 
@@ -482,6 +539,7 @@ extern "C" gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model*
   gd_model* m = new gd_model();
   m->c = *cfg;
   m->dev = dev;
+  m->n_cu = prop.multiProcessorCount;
   m->stream = reinterpret_cast<hipStream_t>(hip_stream);
   layout(m);
   if (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess ||
@@ -575,6 +633,7 @@ extern "C" gd_status gd_bind_memory(gd_model* m, void* wdev, void* kvdev, void* 
       }
     HIP_TRY(m, hipMemcpyAsync(m->sp<float>(m->o_rope), cs.data(), cs.size() * 4, hipMemcpyHostToDevice, m->stream));
   }
+  m->pk_tag = 0;   // the exchange words were just cleared (tag 0)
   HIP_TRY(m, hipStreamSynchronize(m->stream));
   std::fill(m->len.begin(), m->len.end(), 0);
   m->last_sids.clear();
@@ -793,6 +852,11 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->use_graph = v != 0;
   } else if (opt == GD_OPT_FUSE_ATTN_O) {
     m->fuse_attn_o = v != 0;
+  } else if (opt == GD_OPT_PERSISTENT) {
+    m->use_pk = v != 0;
+  } else if (opt == GD_OPT_PERSISTENT_SPIN_US) {
+    if (v < 0) return set_err(GD_ERR_INVALID, "spin bound must be >= 0");
+    m->pk_spin_us = v;
   } else if (opt == GD_OPT_PROFILE) {
     if (v < 0 || v > 2) return set_err(GD_ERR_INVALID, "profile must be 0, 1 or 2");
     m->profile = v != 0;
@@ -1159,6 +1223,88 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
   return GD_OK;
 }
 
+// ------------------------------------------------- single-launch decode step
+
+template <int WT, int D, int FF, int HD>
+static hipError_t launch_pk(gd_model* m, hipStream_t st, const PKParams& p) {
+  static bool lds_set = false;
+  if (!lds_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode1<WT, D, FF, HD>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, PK_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  GD_LAUNCH((k_decode1<WT, D, FF, HD>), dim3(m->n_cu), dim3(PK_WG), PK_LDS_BYTES, st, p);
+  return hipGetLastError();
+}
+
+// Algorithmic bytes of one single-launch step at T attended positions, counted as the
+// kernel chain counts its launches: every weight, bias and norm parameter once, the
+// K/V of every attended position once, activations in and out.
+static double pk_step_bytes(const gd_model* m, int T, bool logits) {
+  const gd_config& c = m->c;
+  const double d = c.d_model, ff = c.d_ff, q = m->qkvdim, e = (double)m->elt, V = c.vocab;
+  double b = d * (2 * e + 4);
+  const double layer = (q * d * e + d * 4 + q * 4 + q * 4 + 2 * d * 4) +
+                       ((double)T * c.n_head * c.head_dim * 8 + 2 * d * 4 + d * d * e + d * 4 + 2 * d * 4) +
+                       (ff * d * e + d * 4 + ff * 4 + ff * 4 + 2 * d * 4) + (d * ff * e + ff * 4 + 3 * d * 4);
+  b += layer * c.n_layer;
+  b += V * d * e + d * 4 + (logits ? V * 4 : 0) + 2 * d * 4 + m->n_cu * 8.0 + 4;
+  return b;
+}
+
+// One decode step of sequence `seq` as a single launch (k_decode1).
+static hipError_t enqueue_pk(gd_model* m, hipStream_t st, int seq, const int* tok, int* next, float* logits) {
+  const gd_config& c = m->c;
+  if (m->pk_tag == 0xffffffffu) {   // tags are about to wrap: clear every exchange word
+    const hipError_t e = hipMemsetAsync(m->s + m->o_xb, 0, m->pk_words * 8, st);
+    if (e != hipSuccess) return e;
+    m->pk_tag = 0;
+  }
+  PKParams p;
+  memset(&p, 0, sizeof(p));
+  {
+    const LayerOff& t = m->L[0];
+    PKLayer& q = p.L0;
+    q.n1g = m->wf(t.n1g); q.n1b = m->wf(t.n1b);
+    q.wqkv = m->w + t.wqkv; q.bqkv = m->wf(t.bqkv);
+    q.wo = m->w + t.wo; q.bo = m->wf(t.bo);
+    q.n2g = m->wf(t.n2g); q.n2b = m->wf(t.n2b);
+    q.wfc = m->w + t.wfc; q.bfc = m->wf(t.bfc);
+    q.wproj = m->w + t.wproj; q.bproj = m->wf(t.bproj);
+    q.kc = m->kpool(0); q.vc = m->vpool(0);
+    p.w_stride = c.n_layer > 1 ? (long long)(m->L[1].n1g - m->L[0].n1g) : 0;
+    p.kv_stride = (long long)m->layer_kv_floats();
+  }
+  p.n_layer = c.n_layer; p.d = c.d_model; p.H = c.n_head; p.ff = c.d_ff; p.vocab = c.vocab; p.qkv = m->qkvdim;
+  p.eps = c.norm_eps; p.scale = 1.0f / std::sqrt((float)c.head_dim);
+  p.wte = m->w + m->o_wte; p.wpe = m->w + m->o_wpe; p.nfg = m->wf(m->o_nfg); p.nfb = m->wf(m->o_nfb);
+  p.paged = c.kv_block_size > 0;
+  p.hd = c.head_dim;
+  p.kv0 = (int)((size_t)seq * c.n_kv_head * m->bsize * c.head_dim);   // contiguous: the sequence's block
+  p.table = m->sp<int>(m->o_table); p.max_blocks = m->max_blocks; p.nblk = m->nblk;
+  p.bs_shift = 0;
+  while ((1 << p.bs_shift) < m->bsize) ++p.bs_shift;
+  p.kv_hstride = m->bsize * c.head_dim;
+  p.seq = seq; p.pos = m->len[seq]; p.nch = iceil(p.pos + 1, PK_ACH);
+  p.tag = ++m->pk_tag;
+  p.spin_ticks = m->pk_spin_us * 100;   // the real-time counter runs at 100 MHz
+  p.tok = tok; p.next = next; p.logits = logits;
+  p.len = m->sp<int>(m->o_len); p.err = m->sp<int>(m->o_err);
+  p.xb = m->sp<uint64_t>(m->o_xb); p.abort_tag = m->sp<unsigned>(m->o_pkabort);
+  p.xl = m->pk_xl; p.x_att = m->pk_att; p.x_xo = m->pk_xo; p.x_h = m->pk_h; p.x_xd = m->pk_xd;
+  p.rs_att = m->pk_rs_att; p.rs_d = m->pk_rs_d; p.rs_h = m->pk_rs_h; p.x_arg = m->pk_arg;
+  char kn[48];
+  snprintf(kn, sizeof(kn), "k_decode1<%d, %d, %d, %d>", m->wt == GD_WEIGHT_F32 ? 0 : 1, c.d_model, c.d_ff, c.head_dim);
+  ProfScope ps(m, st, "decode1", kn, m->profile ? pk_step_bytes(m, p.pos + 1, logits != nullptr) : 0);
+  if (c.head_dim == 16) {
+    if (m->wt == GD_WEIGHT_F32) return launch_pk<0, 64, 256, 16>(m, st, p);
+    return launch_pk<1, 64, 256, 16>(m, st, p);
+  }
+  if (m->wt == GD_WEIGHT_F32) return launch_pk<0, 768, 3072, 64>(m, st, p);
+  return launch_pk<1, 768, 3072, 64>(m, st, p);
+}
+
 static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, int max_T, const int* tok, int* next,
                                  float* logits) {
   RowParams rp = row_params(m, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
@@ -1203,6 +1349,8 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     for (int b = 0; b < B; ++b) m->prof_T.push_back(m->len[sids[b]] + 1);
   int max_T = 0;   // attended positions of the longest row
   for (int b = 0; b < B; ++b) max_T = std::max(max_T, m->len[sids[b]] + 1);
+  // one sequence of the GPT-2 layout: the whole step as one launch
+  const bool single = B == 1 && m->use_pk && m->pk_ok;
   if (m->profile && m->profile_gated) {
     // hold the stream (bounded) while the step is enqueued, then let it run whole
     if (!m->gate_evt) HIP_TRY(m, hipEventCreateWithFlags(&m->gate_evt, hipEventDisableTiming));
@@ -1210,7 +1358,15 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     HIP_TRY(m, hipGetLastError());
     HIP_TRY(m, hipEventRecord(m->gate_evt, m->cap_stream));
     HIP_TRY(m, hipStreamWaitEvent(s, m->gate_evt, 0));
-    hipError_t e = enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
+    hipError_t e = single ? enqueue_pk(m, s, sids[0], tok_dev, next_dev, logits_dev)
+                          : enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
+    if (e != hipSuccess) {
+      m->poisoned = true;
+      return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    }
+  } else if (single) {
+    // the step's tag changes every step, so it is launched directly (one launch anyway)
+    hipError_t e = enqueue_pk(m, s, sids[0], tok_dev, next_dev, logits_dev);
     if (e != hipSuccess) {
       m->poisoned = true;
       return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
