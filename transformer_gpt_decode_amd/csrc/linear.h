@@ -148,174 +148,49 @@ __device__ __forceinline__ void epi_store(const LinParams& p, const EpiOps& e, i
   }
 }
 
-// Activation rows are staged into LDS xs[m * K + k] in two parts. stage_issue loads
-// the first XPT float4 chunks of this thread (rows, and the norm's gain and shift)
-// into registers; it runs before the weight loads, so that waiting for the rows
-// does not wait for the weight stream (vector loads complete in issue order).
-// stage_finish stores them, loads any remaining chunks, and normalizes the rows.
+// Activation rows are staged into LDS xs[m * K + k] as they are. stage_issue loads
+// the first XPT float4 chunks of this thread; it runs before the weight loads, so that
+// waiting for the rows does not wait for the weight stream (vector loads complete in
+// issue order). stage_finish stores them and copies any remaining chunks. A pre-norm
+// is applied later, in the dot products (k_gemv).
 template <int XPT>
 struct RowRegs {
-  f32x4 x[XPT], g[XPT], b[XPT];
-  float x0[GEMV_MAX_ROWS];   // first element of each row (shift of the one-pass moments)
+  f32x4 x[XPT];
 };
 
-template <int XPT>
+template <int XPT, int PRO>
 __device__ __forceinline__ void stage_issue(const LinParams& p, RowRegs<XPT>& rr) {
   // Loads are unconditional (clamped to the last valid chunk; stage_finish stores only
-  // valid ones), so the compiler can count them and wait for these alone later.
-  if (p.pro != PRO_COPY) return;
+  // valid ones) and the prologue is fixed at compile time, so the compiler can count
+  // them and wait for these alone later, not for the weight loads issued after them.
+  if (PRO != PRO_COPY) return;
   const int tid = threadIdx.x, K4 = p.K >> 2;
-  const float* gsrc = p.ng ? p.ng : p.x;
-  const float* bsrc = p.nb ? p.nb : gsrc;
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
     const int i = min(tid + GD_WG * j, p.M * K4 - 1);
     const int m = i / K4, k = (i - m * K4) << 2;
     rr.x[j] = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + k);
-    const int kg = min(tid + GD_WG * j, K4 - 1) << 2;
-    rr.g[j] = *reinterpret_cast<const f32x4*>(gsrc + kg);
-    rr.b[j] = *reinterpret_cast<const f32x4*>(bsrc + kg);
-  }
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m) rr.x0[m] = p.x[(size_t)min(m, p.M - 1) * p.ldx];
-}
-
-// Sum over the workgroup of one value per row (rows < M), for every thread.
-__device__ __forceinline__ void block_sum_rows(float v[GEMV_MAX_ROWS], int M, float (*red)[GEMV_MAX_ROWS]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m)
-    if (m < M) v[m] = wave_sum(v[m]);
-  if (lane == 0) {
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m) red[wave][m] = v[m];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < GD_WG / 64; ++w) t += red[w][m];
-    v[m] = t;
   }
 }
 
 // Attention merge prologue: its loads are issued with the other row loads, before the
 // weights.
+template <int PRO>
 __device__ __forceinline__ void stage_issue_attn(const LinParams& p, MergeRegs<4>& ar) {
-  if (p.pro != PRO_ATTN) return;
+  if (PRO != PRO_ATTN) return;
   attn_merge_issue<4>(p.apart, p.Hq, p.hd, p.M, ar, GD_WG);
 }
 
-// Both sums of the register LayerNorm path in one workgroup exchange (one barrier).
-__device__ __forceinline__ void block_sum_rows2(float a[GEMV_MAX_ROWS], float b[GEMV_MAX_ROWS], int M,
-                                                float (*red)[GD_WG / 64][GEMV_MAX_ROWS]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float v[2 * GEMV_MAX_ROWS];
-  if (M == 1) {   // the batch-1 case: two sums only
-    float v1[2] = {a[0], b[0]};
-    wave_sum_n<2>(v1);
-    v[0] = v1[0];
-    v[GEMV_MAX_ROWS] = v1[1];
-#pragma unroll
-    for (int m = 1; m < GEMV_MAX_ROWS; ++m) v[m] = v[GEMV_MAX_ROWS + m] = 0.f;
-  } else {
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-      v[m] = m < M ? a[m] : 0.f;
-      v[GEMV_MAX_ROWS + m] = m < M ? b[m] : 0.f;
-    }
-    wave_sum_n<2 * GEMV_MAX_ROWS>(v);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-      red[0][wave][m] = v[m];
-      red[1][wave][m] = v[GEMV_MAX_ROWS + m];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-    float ta = 0.f, tb = 0.f;
-#pragma unroll
-    for (int w = 0; w < GD_WG / 64; ++w) { ta += red[0][w][m]; tb += red[1][w][m]; }
-    a[m] = ta;
-    b[m] = tb;
-  }
-}
-
-template <int XPT>
-__device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const RowRegs<XPT>& rr, const MergeRegs<4>& ar,
-                             float (*red)[GD_WG / 64][GEMV_MAX_ROWS], float* s_aw) {
+template <int XPT, int PRO>
+__device__ __forceinline__ void stage_finish(const LinParams& p, float* xs, const RowRegs<XPT>& rr,
+                                             const MergeRegs<4>& ar, float* s_aw) {
   const int tid = threadIdx.x;
   const int M = p.M, K = p.K;
-  if (p.pro == PRO_ATTN) {
+  if (PRO == PRO_ATTN) {
     attn_merge_finish<4>(p.apart, p.Hq, p.hd, M, ar, xs, K, s_aw, GD_WG);
     return;
   }
   const int K4 = K >> 2;
-  float* s_g = s_gb;
-  float* s_b = s_gb + K;
-  if (p.norm != NORM_NONE && M * K4 <= GD_WG * XPT) {
-    // Every row is in registers: moments from registers with one workgroup reduction,
-    // shifted by the row's first element (sum d and sum d^2 with d = x - x0), then
-    // normalize in registers and store. RMSNorm uses the unshifted sum of squares.
-    float s1[GEMV_MAX_ROWS], s2[GEMV_MAX_ROWS];
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m) s1[m] = s2[m] = 0.f;
-    const bool ln = p.norm == NORM_LN;
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int i = tid + GD_WG * j;
-      if (i < M * K4) {
-        const int m = i / K4;
-#pragma unroll
-        for (int mm = 0; mm < GEMV_MAX_ROWS; ++mm)
-          if (mm == m) {
-            const float sh = ln ? rr.x0[mm] : 0.f;
-            const float d0 = rr.x[j].x - sh, d1 = rr.x[j].y - sh, d2 = rr.x[j].z - sh, d3 = rr.x[j].w - sh;
-            s1[mm] += (d0 + d1) + (d2 + d3);
-            s2[mm] += fmaf(d0, d0, d1 * d1) + fmaf(d2, d2, d3 * d3);
-          }
-      }
-    }
-    block_sum_rows2(s1, s2, M, red);
-    float mu[GEMV_MAX_ROWS], rs[GEMV_MAX_ROWS];
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-      const float a = s1[m] / (float)K;                  // mean of d
-      const float var = ln ? fmaxf(s2[m] / (float)K - a * a, 0.f) : s2[m] / (float)K;
-      mu[m] = ln ? rr.x0[m] + a : 0.f;
-      rs[m] = 1.0f / sqrtf(var + p.eps);
-    }
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int i = tid + GD_WG * j;
-      if (i < M * K4) {
-        const int m = i / K4, k = (i - m * K4) << 2;
-        float u = 0.f, r = 0.f;
-#pragma unroll
-        for (int mm = 0; mm < GEMV_MAX_ROWS; ++mm)
-          if (mm == m) { u = mu[mm]; r = rs[mm]; }
-        f32x4 v = rr.x[j];
-        f32x4 gg, bb;
-        if (m == 0) { gg = rr.g[j]; bb = rr.b[j]; }   // this thread's gain/shift chunk is column k
-        else {
-          gg = *reinterpret_cast<const f32x4*>(p.ng + k);
-          bb = ln ? *reinterpret_cast<const f32x4*>(p.nb + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
-        if (ln) {
-          v.x = (v.x - u) * r * gg.x + bb.x; v.y = (v.y - u) * r * gg.y + bb.y;
-          v.z = (v.z - u) * r * gg.z + bb.z; v.w = (v.w - u) * r * gg.w + bb.w;
-        } else {
-          v.x = v.x * r * gg.x; v.y = v.y * r * gg.y; v.z = v.z * r * gg.z; v.w = v.w * r * gg.w;
-        }
-        *reinterpret_cast<f32x4*>(xs + m * K + k) = v;
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
     const int i = tid + GD_WG * j;
@@ -323,54 +198,11 @@ __device__ void stage_finish(const LinParams& p, float* xs, float* s_gb, const R
       const int m = i / K4, k = (i - m * K4) << 2;
       *reinterpret_cast<f32x4*>(xs + m * K + k) = rr.x[j];
     }
-    if (p.norm != NORM_NONE && i < K4) {
-      *reinterpret_cast<f32x4*>(s_g + 4 * i) = rr.g[j];
-      if (p.norm == NORM_LN) *reinterpret_cast<f32x4*>(s_b + 4 * i) = rr.b[j];
-    }
   }
   for (int i = tid + GD_WG * XPT; i < M * K4; i += GD_WG) {   // rows beyond the register share
     const int m = i / K4, k = (i - m * K4) << 2;
     *reinterpret_cast<f32x4*>(xs + m * K + k) = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + k);
-    if (p.norm != NORM_NONE && i < K4) {
-      *reinterpret_cast<f32x4*>(s_g + 4 * i) = *reinterpret_cast<const f32x4*>(p.ng + 4 * i);
-      if (p.norm == NORM_LN) *reinterpret_cast<f32x4*>(s_b + 4 * i) = *reinterpret_cast<const f32x4*>(p.nb + 4 * i);
-    }
   }
-  if (p.norm == NORM_NONE) return;
-  __syncthreads();
-  // row statistics over the whole workgroup: mean, then the mean of squared deviations
-  float mean[GEMV_MAX_ROWS], var[GEMV_MAX_ROWS];
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m) mean[m] = 0.f;
-  if (p.norm == NORM_LN) {
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m)
-      if (m < M)
-        for (int k = tid; k < K; k += GD_WG) mean[m] += xs[m * K + k];
-    block_sum_rows(mean, M, red[0]);
-#pragma unroll
-    for (int m = 0; m < GEMV_MAX_ROWS; ++m) mean[m] /= (float)K;
-  }
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-    var[m] = 0.f;
-    if (m < M)
-      for (int k = tid; k < K; k += GD_WG) {
-        const float t = xs[m * K + k] - mean[m];
-        var[m] = fmaf(t, t, var[m]);
-      }
-  }
-  block_sum_rows(var, M, red[1]);
-  float rs[GEMV_MAX_ROWS];
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m) rs[m] = 1.0f / sqrtf(var[m] / (float)K + p.eps);
-#pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m)
-    if (m < M)
-      for (int k = tid; k < K; k += GD_WG) {
-        const float v = xs[m * K + k];
-        xs[m * K + k] = p.norm == NORM_RMS ? v * rs[m] * s_g[k] : (v - mean[m]) * rs[m] * s_g[k] + s_b[k];
-      }
 }
 
 template <int WT>
@@ -382,14 +214,15 @@ struct WChunk<1> { typedef u32x4 T; static constexpr int CE = 8; };
 
 // ------------------------------------------------------------------ GEMV
 
-template <int WT, int NC, int RW, int EPI>
+// PRO: source of the rows (PRO_COPY or PRO_ATTN); NRM: the rows are normalized
+// (p.norm: LayerNorm or RMSNorm). Both are compile-time so that every path issues a
+// fixed number of loads and the waits for the rows do not cover the weight stream.
+template <int WT, int NC, int RW, int EPI, int PRO, bool NRM>
 __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   typedef typename WChunk<WT>::T VT;
   constexpr int CE = WChunk<WT>::CE;
-  extern __shared__ __align__(16) float xs[];   // [M][K] rows, then the norm's gain and shift [2][K]
-  float* s_gb = xs + ((p.M * p.K + 3) & ~3);
+  extern __shared__ __align__(16) float xs[];   // [M][K] rows
   __shared__ float s_am[GEMV_MAX_ROWS][4 * RW];
-  __shared__ float s_red[2][GD_WG / 64][GEMV_MAX_ROWS];
   __shared__ float s_aw[GEMV_MAX_ROWS * GD_MAX_HEADS * GD_ATT_NCH];   // attention chunk weights
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, N = p.N, K = p.K;
@@ -398,9 +231,24 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   // 0. this thread's share of the activation rows (M = 1 rows fit entirely)
   constexpr int XPT = (NC * CE + 15) / 16;
   RowRegs<XPT> rr;
-  stage_issue<XPT>(p, rr);
+  stage_issue<XPT, PRO>(p, rr);
   MergeRegs<4> ar;
-  stage_issue_attn(p, ar);
+  stage_issue_attn<PRO>(p, ar);
+  // the norm's gain and shift at this lane's chunks (RMSNorm: no shift; the gain is
+  // loaded in its place so that the number of loads stays fixed)
+  f32x4 gn[NC][CE / 4], bn[NC][CE / 4];
+  if constexpr (NRM) {
+    const float* bsrc = p.nb ? p.nb : p.ng;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int k = min((lane + 64 * i) * CE, K - CE);
+#pragma unroll
+      for (int h = 0; h < CE / 4; ++h) {
+        gn[i][h] = *reinterpret_cast<const f32x4*>(p.ng + k + 4 * h);
+        bn[i][h] = *reinterpret_cast<const f32x4*>(bsrc + k + 4 * h);
+      }
+    }
+  }
   // 1. weights: they do not depend on anything
   VT w[RW][NC];
 #pragma unroll
@@ -422,47 +270,137 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   const int on = nw0 + orr;
   const bool own = EPI != EPI_ARGMAX && om < M && (PAIR ? nw0 + 1 < N : (lane < M * RW && on < N));
   EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? on : 0);
-  // 3. activations into LDS, normalized
-  stage_finish<XPT>(p, xs, s_gb, rr, ar, s_red, s_aw);
+  // 3. activation rows into LDS
+  stage_finish<XPT, PRO>(p, xs, rr, ar, s_aw);
   __syncthreads();
-  // 4. dot products
+  // 4. dot products. With NRM every row is normalized on the fly: the lanes of a wave
+  //    hold the row's whole K range (chunks lane + 64 i), so each wave forms the row's
+  //    statistics itself (one-pass moments shifted by the row's first element, summed
+  //    with wave-level reductions) and no workgroup exchange is needed.
   float acc[RW][GEMV_MAX_ROWS];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int m = 0; m < GEMV_MAX_ROWS; ++m) acc[r][m] = 0.f;
+  // acc[.][m] += w . xv over this lane's chunks (xv: the row's chunks in registers)
+  auto dot_row = [&](int m, const f32x4 (&xv)[NC][CE / 4]) {
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int k = (lane + 64 * i) * CE;
-    if (k < K) {
+    for (int i = 0; i < NC; ++i) {
+      if ((lane + 64 * i) * CE < K) {
+        const f32x4 a = xv[i][0];
 #pragma unroll
-      for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-        if (m < M) {
-          const float* xr = xs + m * K + k;
-          f32x4 a = *reinterpret_cast<const f32x4*>(xr);
+        for (int r = 0; r < RW; ++r) {
+          float s = acc[r][m];
+          if (WT == 0) {
+            s = fmaf(w[r][i].x, a.x, s); s = fmaf(w[r][i].y, a.y, s);
+            s = fmaf(w[r][i].z, a.z, s); s = fmaf(w[r][i].w, a.w, s);
+          } else {
+            s = fmaf(bf16_lo(w[r][i].x), a.x, s); s = fmaf(bf16_hi(w[r][i].x), a.y, s);
+            s = fmaf(bf16_lo(w[r][i].y), a.z, s); s = fmaf(bf16_hi(w[r][i].y), a.w, s);
+          }
+          acc[r][m] = s;
+        }
+        if constexpr (WT == 1) {
+          const f32x4 b = xv[i][CE / 4 - 1];
 #pragma unroll
           for (int r = 0; r < RW; ++r) {
             float s = acc[r][m];
-            if (WT == 0) {
-              s = fmaf(w[r][i].x, a.x, s); s = fmaf(w[r][i].y, a.y, s);
-              s = fmaf(w[r][i].z, a.z, s); s = fmaf(w[r][i].w, a.w, s);
-            } else {
-              s = fmaf(bf16_lo(w[r][i].x), a.x, s); s = fmaf(bf16_hi(w[r][i].x), a.y, s);
-              s = fmaf(bf16_lo(w[r][i].y), a.z, s); s = fmaf(bf16_hi(w[r][i].y), a.w, s);
-            }
+            s = fmaf(bf16_lo(w[r][i].z), b.x, s); s = fmaf(bf16_hi(w[r][i].z), b.y, s);
+            s = fmaf(bf16_lo(w[r][i].w), b.z, s); s = fmaf(bf16_hi(w[r][i].w), b.w, s);
             acc[r][m] = s;
           }
-          if (WT == 1) {
-            f32x4 b = *reinterpret_cast<const f32x4*>(xr + 4);
+        }
+      }
+    }
+  };
+  // the row's chunks from LDS into registers (zeros past K)
+  auto load_row = [&](int m, f32x4 (&xv)[NC][CE / 4]) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int k = (lane + 64 * i) * CE;
+#pragma unroll
+      for (int h = 0; h < CE / 4; ++h)
+        xv[i][h] = k < K ? *reinterpret_cast<const f32x4*>(xs + m * K + k + 4 * h) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (!NRM && M > 1) {
+    // several rows as staged: chunk-outer, so that each weight chunk meets every row
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int k = (lane + 64 * i) * CE;
+      if (k < K) {
+#pragma unroll
+        for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+          if (m < M) {
+            const float* xr = xs + m * K + k;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(xr);
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
               float s = acc[r][m];
-              s = fmaf(bf16_lo(w[r][i].z), b.x, s); s = fmaf(bf16_hi(w[r][i].z), b.y, s);
-              s = fmaf(bf16_lo(w[r][i].w), b.z, s); s = fmaf(bf16_hi(w[r][i].w), b.w, s);
+              if (WT == 0) {
+                s = fmaf(w[r][i].x, a.x, s); s = fmaf(w[r][i].y, a.y, s);
+                s = fmaf(w[r][i].z, a.z, s); s = fmaf(w[r][i].w, a.w, s);
+              } else {
+                s = fmaf(bf16_lo(w[r][i].x), a.x, s); s = fmaf(bf16_hi(w[r][i].x), a.y, s);
+                s = fmaf(bf16_lo(w[r][i].y), a.z, s); s = fmaf(bf16_hi(w[r][i].y), a.w, s);
+              }
               acc[r][m] = s;
+            }
+            if constexpr (WT == 1) {
+              const f32x4 b = *reinterpret_cast<const f32x4*>(xr + 4);
+#pragma unroll
+              for (int r = 0; r < RW; ++r) {
+                float s = acc[r][m];
+                s = fmaf(bf16_lo(w[r][i].z), b.x, s); s = fmaf(bf16_hi(w[r][i].z), b.y, s);
+                s = fmaf(bf16_lo(w[r][i].w), b.z, s); s = fmaf(bf16_hi(w[r][i].w), b.w, s);
+                acc[r][m] = s;
+              }
             }
           }
         }
+      }
+    }
+  } else {
+    // row by row with the row's chunks in registers (a single row, or a pre-norm that
+    // needs each row's statistics before its products)
+#pragma unroll
+    for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+      if (m < M) {
+        f32x4 xv[NC][CE / 4];
+        load_row(m, xv);
+        if constexpr (NRM) {
+          const bool ln = p.norm == NORM_LN;
+          const float sh = ln ? xs[m * K] : 0.f;
+          float st[2] = {0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            if ((lane + 64 * i) * CE < K) {
+#pragma unroll
+              for (int h = 0; h < CE / 4; ++h) {
+                const float d0 = xv[i][h].x - sh, d1 = xv[i][h].y - sh, d2 = xv[i][h].z - sh, d3 = xv[i][h].w - sh;
+                st[0] += (d0 + d1) + (d2 + d3);
+                st[1] += fmaf(d0, d0, d1 * d1) + fmaf(d2, d2, d3 * d3);
+              }
+            }
+          }
+          wave_sum_n<2>(st);
+          const float a = st[0] / (float)K;   // mean of the shifted values
+          const float var = ln ? fmaxf(st[1] / (float)K - a * a, 0.f) : st[1] / (float)K;
+          const float mu = ln ? sh + a : 0.f;
+          const float rs = 1.0f / sqrtf(var + p.eps);
+          const float bs = ln ? 1.f : 0.f;
+#pragma unroll
+          for (int i = 0; i < NC; ++i)
+#pragma unroll
+            for (int h = 0; h < CE / 4; ++h) {
+              f32x4& v = xv[i][h];
+              v.x = (v.x - mu) * rs * gn[i][h].x + bs * bn[i][h].x;
+              v.y = (v.y - mu) * rs * gn[i][h].y + bs * bn[i][h].y;
+              v.z = (v.z - mu) * rs * gn[i][h].z + bs * bn[i][h].z;
+              v.w = (v.w - mu) * rs * gn[i][h].w + bs * bn[i][h].w;
+            }
+        }
+        dot_row(m, xv);
       }
     }
   }

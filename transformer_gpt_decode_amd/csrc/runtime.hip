@@ -131,9 +131,9 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
     p.rows = std::min(M, GEMV_MAX_ROWS);
     p.grid = iceil(N, 4 * p.rw);
     p.parts = p.grid;
-    // rows, then the norm's gain and shift
+    // the activation rows (a pre-norm is applied in registers)
     const size_t xs = ((size_t)p.rows * K + 3) & ~(size_t)3;
-    p.lds = (xs + (norm ? 2 * (size_t)K : 0)) * sizeof(float);
+    p.lds = xs * sizeof(float);
     if (p.lds > kGemvLdsMax && !(norm && K > MM_KC)) p.var = 1;   // rows too long to stage
   }
   if (p.var == 1) {
@@ -158,31 +158,42 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
 }
 
 template <int WT, int NC>
-static void launch_gemv_nc(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   const dim3 g(lp.grid), b(GD_WG);
+  const bool nrm = prm.norm != NORM_NONE;
+#define GD_GEMV(RW, EPI, PRO, NRM) GD_LAUNCH((k_gemv<WT, NC, RW, EPI, PRO, NRM>), g, b, lp.lds, st, prm)
+  if (prm.pro == PRO_ATTN) {   // the output projection behind split-context attention
+    if (prm.epi != EPI_PLAIN || nrm) return hipErrorNotSupported;
+    GD_GEMV(1, EPI_PLAIN, PRO_ATTN, false);
+    return hipSuccess;
+  }
   switch (prm.epi) {
-    case EPI_PLAIN: GD_LAUNCH((k_gemv<WT, NC, 1, EPI_PLAIN>), g, b, lp.lds, st, prm); break;
-    case EPI_GELU: GD_LAUNCH((k_gemv<WT, NC, 1, EPI_GELU>), g, b, lp.lds, st, prm); break;
-    case EPI_QKV: GD_LAUNCH((k_gemv<WT, NC, 1, EPI_QKV>), g, b, lp.lds, st, prm); break;
-    case EPI_SWIGLU: GD_LAUNCH((k_gemv<WT, NC, 2, EPI_SWIGLU>), g, b, lp.lds, st, prm); break;
-    case EPI_QKV_ROPE: GD_LAUNCH((k_gemv<WT, NC, 2, EPI_QKV_ROPE>), g, b, lp.lds, st, prm); break;
+    case EPI_PLAIN: if (nrm) GD_GEMV(1, EPI_PLAIN, PRO_COPY, true); else GD_GEMV(1, EPI_PLAIN, PRO_COPY, false); break;
+    case EPI_GELU: if (nrm) GD_GEMV(1, EPI_GELU, PRO_COPY, true); else GD_GEMV(1, EPI_GELU, PRO_COPY, false); break;
+    // the remaining epilogues always follow a pre-norm
+    case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_GEMV(1, EPI_QKV, PRO_COPY, true); break;
+    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_GEMV(2, EPI_SWIGLU, PRO_COPY, true); break;
+    case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_GEMV(2, EPI_QKV_ROPE, PRO_COPY, true); break;
     default:
-      if (lp.rw == 4) GD_LAUNCH((k_gemv<WT, NC, 4, EPI_ARGMAX>), g, b, lp.lds, st, prm);
-      else GD_LAUNCH((k_gemv<WT, NC, 1, EPI_ARGMAX>), g, b, lp.lds, st, prm);
+      if (!nrm) return hipErrorNotSupported;
+      if (lp.rw == 4) GD_GEMV(4, EPI_ARGMAX, PRO_COPY, true);
+      else GD_GEMV(1, EPI_ARGMAX, PRO_COPY, true);
       break;
   }
+#undef GD_GEMV
+  return hipSuccess;
 }
 
 template <int WT>
-static void launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+static hipError_t launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   switch (lp.nc) {
-    case 1: launch_gemv_nc<WT, 1>(lp, prm, st); break;
-    case 2: launch_gemv_nc<WT, 2>(lp, prm, st); break;
-    case 3: launch_gemv_nc<WT, 3>(lp, prm, st); break;
-    case 4: launch_gemv_nc<WT, 4>(lp, prm, st); break;
-    case 6: launch_gemv_nc<WT, 6>(lp, prm, st); break;
-    case 8: launch_gemv_nc<WT, 8>(lp, prm, st); break;
-    default: launch_gemv_nc<WT, 12>(lp, prm, st); break;
+    case 1: return launch_gemv_nc<WT, 1>(lp, prm, st);
+    case 2: return launch_gemv_nc<WT, 2>(lp, prm, st);
+    case 3: return launch_gemv_nc<WT, 3>(lp, prm, st);
+    case 4: return launch_gemv_nc<WT, 4>(lp, prm, st);
+    case 6: return launch_gemv_nc<WT, 6>(lp, prm, st);
+    case 8: return launch_gemv_nc<WT, 8>(lp, prm, st);
+    default: return launch_gemv_nc<WT, 12>(lp, prm, st);
   }
 }
 
@@ -220,8 +231,8 @@ static hipError_t launch_mm(const LinPlan& lp, const LinParams& prm, hipStream_t
 // One launch of one plan over prm.M rows (prm.M <= lp.rows).
 static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   if (lp.var == 0) {
-    if (wt == GD_WEIGHT_F32) launch_gemv<0>(lp, prm, st);
-    else launch_gemv<1>(lp, prm, st);
+    const hipError_t e = wt == GD_WEIGHT_F32 ? launch_gemv<0>(lp, prm, st) : launch_gemv<1>(lp, prm, st);
+    if (e != hipSuccess) return e;
   } else {
     const hipError_t e = wt == GD_WEIGHT_F32 ? launch_mm<0>(lp, prm, st) : launch_mm<1>(lp, prm, st);
     if (e != hipSuccess) return e;
@@ -929,10 +940,11 @@ struct ProfScope {
   }
 };
 
-static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, char* buf, size_t n) {
+static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, int pro, char* buf, size_t n) {
   const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
   // as rocprofv3 prints the instantiation
-  if (lp.var == 0) snprintf(buf, n, "k_gemv<%d, %d, %d, %d>", w, lp.nc, lp.rw, epi);
+  if (lp.var == 0)
+    snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %s>", w, lp.nc, lp.rw, epi, pro, norm ? "true" : "false");
   else snprintf(buf, n, "k_mm<%d, %d, %d, %s, %s>", w, lp.mt, epi, norm ? "true" : "false", lp.passes > 1 ? "true" : "false");
   return buf;
 }
@@ -958,7 +970,7 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
   std::vector<std::pair<hipEvent_t, hipEvent_t>> fin;
   hipError_t e;
   {
-    ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, kn, sizeof(kn)),
+    ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, p.pro, kn, sizeof(kn)),
                  m->profile ? linear_bytes(m, p) : 0);
     t_prof_fin = &fin;
     e = run_linear_rows(m->wt, lp, p, st, am_out);
