@@ -266,6 +266,60 @@ def summary(res):
                       sync_ms_per_step=round(res["ms_sync"], 4), sync_value=round(w.batch / (res["ms_sync"] * 1e-3), 1))
 
 
+def counter_means(csv_path: str, calib_mib: int):
+    """Per profiled pass of a rocprofv3 --pmc CSV of a bench.py run: {kernel: mean bytes
+    per dispatch}, the counter scaled by the calibration copy (see trace_summary)."""
+    import csv
+    import statistics
+
+    def short(n):
+        n = n.replace("void ", "")
+        return n[:n.index("(")] if "(" in n else n
+
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    cp = next(r for r in rows if "copyBuffer" in r["Kernel_Name"])
+    factor = calib_mib * 1024.0 / float(cp["Counter_Value"])
+    gates = [i for i, r in enumerate(rows) if short(r["Kernel_Name"]) == "k_gate"]
+    passes, cur = [], []
+    for g in gates:
+        if cur and g - cur[-1] > 400:
+            passes.append(cur)
+            cur = []
+        cur.append(g)
+    if cur:
+        passes.append(cur)
+    out = []
+    for pas in passes:
+        step = pas[1] - pas[0] if len(pas) > 1 else 0
+        d = {}
+        for r in rows[pas[0]:pas[-1] + step]:
+            k = short(r["Kernel_Name"])
+            if k == "k_gate" or "at::native" in k or "rocclr" in k:
+                continue
+            d.setdefault(k, []).append(float(r["Counter_Value"]) * factor * 1024.0)
+        out.append({k: statistics.mean(v) for k, v in d.items()})
+    return out, factor
+
+
+def traffic_json(fetch_csv: str, write_csv: str, calib_mib: int, commands):
+    """profiles/hbm_traffic.json from the FETCH_SIZE and WRITE_SIZE runs: HBM bytes per
+    dispatch of each kernel of the first profiled pass, with the hash of the kernel
+    sources they were measured on."""
+    f, ff = counter_means(fetch_csv, calib_mib)
+    w, wf = counter_means(write_csv, calib_mib)
+    rec = {"sources_sha256": kernel_sources_sha256(),
+           "workload": "gpt2_b1 (GPT-2 124M shape, batch 1, fp32 weights), profiled pass of bench.py --steps 32",
+           "commands": list(commands),
+           "calibration": {"copy_mib_each_way": calib_mib, "fetch_kib_factor": round(ff, 4),
+                           "write_kib_factor": round(wf, 4)},
+           "kernels": {k: {"fetch_bytes": round(f[0][k]), "write_bytes": round(w[0].get(k, 0.0))}
+                       for k in sorted(f[0])}}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(f"wrote {path}: {len(rec['kernels'])} kernels")
+
+
 def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
     """Markdown summary of a rocprofv3 CSV of a bench.py run (--kernel-trace, or --pmc with
     one counter): per kernel, over the dispatches of each profiled pass (the steps that
@@ -373,7 +427,13 @@ def main():
     ap.add_argument("--bench-json", metavar="FILE", help="with --trace-summary: the bench's JSON line to compare")
     ap.add_argument("--calib-mib", type=int, default=0, help="with --trace-summary of a --pmc CSV: the size of the "
                     "--copy-mib calibration copy")
+    ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.json from the two --pmc CSVs (with --calib-mib) and exit")
+    ap.add_argument("--traffic-cmd", action="append", default=[], help="with --traffic-json: a command to record")
     args = ap.parse_args()
+    if args.traffic_json:
+        traffic_json(args.traffic_json[0], args.traffic_json[1], args.calib_mib, args.traffic_cmd)
+        return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json, args.calib_mib)
         return
