@@ -157,6 +157,11 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
 #define GD_OPT_PERSISTENT_SPIN_US 6 /* bound of every wait inside the single-launch step, in
                                      * microseconds (default 20000); a step that exceeds it is
                                      * abandoned and flagged (device error bit 3) */
+#define GD_OPT_FOLD_NORM 7 /* 1 (default): with fp32 weights the VALU GEMV of a layer
+                           * behind a pre-norm (QKV, MLP up, head) reads a copy of its
+                           * weights with the norm's gain folded in (and the shift in
+                           * its bias), made at gd_load_weights; 0: it applies the
+                           * norm's gain and shift to the row */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

@@ -15,7 +15,8 @@ def device():
     return torch.device("cuda", 0)
 
 
-def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True, persistent=False):
+def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True, persistent=False,
+             fold=True):
     import transformer_gpt_decode_amd as gd
     s = workload.shape
     kw = dict(max_seqs=max_seqs or workload.batch, max_batch=max_batch or workload.batch)
@@ -26,7 +27,25 @@ def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, varia
     m.set_option(gd.OPT_LINEAR_VARIANT, variant)
     m.set_option(gd.OPT_USE_GRAPH, 1 if graph else 0)
     m.set_option(gd.OPT_PERSISTENT, 1 if persistent else 0)
+    m.set_option(gd.OPT_FOLD_NORM, 1 if fold else 0)
     return m
+
+
+def perturb_norms_and_biases(shape, W, seed):
+    """A copy of W whose norm gains are 1 + 0.2 N(0, 1) and whose norm shifts and
+    biases are 0.1 N(0, 1) (synth draws them constant: 1 and 0)."""
+    import synth
+    rng = np.random.default_rng(seed)
+    W = W.copy()
+    off = 0
+    for name, shp, kind in synth.tensor_list(shape):
+        n = int(np.prod(shp))
+        if kind == "g":
+            W[off:off + n] = 1.0 + 0.2 * rng.standard_normal(n, dtype=np.float32)
+        elif kind == "b":
+            W[off:off + n] = 0.1 * rng.standard_normal(n, dtype=np.float32)
+        off += n
+    return W
 
 
 def gpu_generate(m, prompts, n_generate, tables=None, want_logits=True, forced=None):

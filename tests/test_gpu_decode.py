@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import compare_generation, device, gd_model, gpu_generate, oracle_generate
+from tests.gpu_util import (compare_generation, device, gd_model, gpu_generate, oracle_generate,
+                             perturb_norms_and_biases)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,9 +23,10 @@ LLAMA_HD64 = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 320, 1e-5
 
 
 def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, pool=None, max_seqs=None,
-                     persistent=False):
+                     persistent=False, fold=True):
     ref_tok, ref_lg = oracle_generate(w, W, prompts)
-    m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph, persistent=persistent)
+    m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph, persistent=persistent,
+                 fold=fold)
     tok, lg = gpu_generate(m, prompts, w.n_generate, tables=tables)
     assert m.device_errors() == 0
     rep = compare_generation(tok, lg, ref_tok, ref_lg, tol)
@@ -86,14 +88,38 @@ def test_context_crosses_fused_limit():
     _run_and_compare(w, W, prompts, 1e-3)
 
 
-@pytest.mark.parametrize("persistent", [True, False], ids=["single_launch", "chain"])
-def test_gpt2_124m_batch1(persistent):
+@pytest.mark.parametrize("mode", ["single_launch", "chain", "chain_norm_applied"])
+def test_gpt2_124m_batch1(mode):
     """GPT-2 124M shape, batch 1, 8 prompt ids, 128 generated tokens (fp32)."""
     w = synth.WORKLOADS["gpt2_b1"]
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
-    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, persistent=persistent)
-    print("gpt2_b1", rep)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, persistent=mode == "single_launch",
+                                 fold=mode != "chain_norm_applied")
+    print("gpt2_b1", mode, rep)
+
+
+@pytest.mark.parametrize("fold", [True, False], ids=["folded", "applied"])
+@pytest.mark.parametrize("variant", [0, 2], ids=["auto", "mfma"])
+def test_tiny_gpt2_random_norms_and_biases(variant, fold):
+    """Norm gains and shifts and every bias drawn at random (the workloads hold them at
+    1 and 0): the pre-norm folded into the weights (gain) and the bias (shift), or
+    applied to the row, must match the oracle, on the GEMV and the MFMA paths."""
+    w = dataclasses.replace(synth.WORKLOADS["tiny"], batch=3, prompt_len=(1, 30), n_generate=16)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 101)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, variant, fold=fold)
+    assert not rep["near_ties"]
+
+
+def test_gpt2_124m_random_norms_and_biases():
+    """GPT-2 124M shape, batch 1, random norm parameters and biases, folded pre-norms
+    (the head's folded bias carries the final norm's shift through the tied embedding)."""
+    w = dataclasses.replace(synth.WORKLOADS["gpt2_b1"], n_generate=24)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 102)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3)
+    print("gpt2_b1 random norms", rep)
 
 
 @pytest.mark.parametrize("wdt", ["f32", "bf16"])

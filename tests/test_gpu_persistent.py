@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 
 import synth
-from tests.gpu_util import compare_generation, device, gd_model, gpu_generate, oracle_generate
+from tests.gpu_util import (compare_generation, device, gd_model, gpu_generate, oracle_generate,
+                             perturb_norms_and_biases)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +39,14 @@ def test_tiny():
     w = synth.WORKLOADS["tiny"]
     W = synth.make_weights(w.shape, w.init, w.seed)
     print("tiny", _check(w, W, synth.make_prompts(w), 1e-3))
+
+
+def test_tiny_random_norms_and_biases():
+    """Norm gains and shifts and every bias drawn at random (the workloads hold them at
+    1 and 0)."""
+    w = synth.WORKLOADS["tiny"]
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 103)
+    print("tiny random norms", _check(w, W, synth.make_prompts(w), 1e-3))
 
 
 def test_tiny_long_context_chunks():

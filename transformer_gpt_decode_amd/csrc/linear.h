@@ -14,9 +14,10 @@
 // k_gemv (1..4 rows, VALU): each wave owns RW weight rows; lane l holds chunks
 //   c = l + 64 i (16 bytes each: 4 fp32 or 8 bf16 weights) of each row in registers,
 //   loaded first. Meanwhile the workgroup stages the activation rows in LDS through a
-//   prologue (a copy or, for the first layer, the token + position embedding, or
-//   the merge of split-context attention partials), then LayerNorm or RMSNorm of
-//   each row. Dot products are reduced across the wave.
+//   prologue (a copy, or the merge of split-context attention partials). A pre-norm
+//   (LayerNorm or RMSNorm) is taken per wave in registers, either applied to the row
+//   (gain and shift loaded) or folded into the weights (see NRM_FOLDED). Dot products
+//   are reduced across the wave.
 // k_mm (5..32 rows): fp32 matrix-core tiles of 16 columns, activation rows held in
 //   registers in the MFMA operand layout; see the MFMA section below.
 //
@@ -36,6 +37,11 @@
 #define NORM_NONE 0
 #define NORM_LN 1    // (x - mean) / sqrt(var + eps) * g + b, biased variance
 #define NORM_RMS 2   // x / sqrt(mean(x^2) + eps) * g
+
+// How k_gemv applies a pre-norm.
+#define NRM_NONE 0
+#define NRM_EXPLICIT 1   // gain and shift loaded and applied to the row
+#define NRM_FOLDED 2     // gain and shift folded into W, bias and row sums (LinParams::fs)
 
 // Epilogues (a template parameter of the kernels, so that the loads of their
 // operands compile to straight-line code).
@@ -59,6 +65,10 @@ struct LinParams {
   // ---- weights
   const void* w; int M, N, K;               // [N][K] row-major (VALU kernel)
   const void* wtl;                          // the same, tile-major (matrix-core kernel; see k_pack_tiles)
+  // ---- the pre-norm folded into the layer (fp32 weights; NULL: not available). With
+  // LN(x)_k = (x_k - mu) r g_k + b_k the layer is y_n = r sum_k (x_k - mu) g_k W_nk +
+  // (bias_n + sum_k b_k W_nk): wf holds g_k W_nk, bf the bracket, fs the row sums of wf.
+  const void* wf; const float* bf; const float* fs;
   // ---- epilogue
   int epi;
   const float* bias;                        // never NULL: a zero vector when the layer has none
@@ -94,14 +104,21 @@ struct EpiTraits { static constexpr bool pair = EPI == EPI_SWIGLU || EPI == EPI_
 // that depends on a loaded value is taken in epi_store.
 struct EpiOps {
   float b0, b1, r0;   // bias of n and n + 1, residual of n
+  float f0, f1;       // row sums of the folded weights of n and n + 1 (NRM_FOLDED)
   float c, s;         // RoPE cos/sin of the pair
   long long kvoff;    // the row's cache slot (QKV)
 };
 
-template <int EPI>
+template <int EPI, bool FOLD = false>
 __device__ __forceinline__ EpiOps epi_prefetch(const LinParams& p, int m, int n) {
   EpiOps e;
   e.b0 = e.b1 = e.r0 = 0.f;
+  e.f0 = e.f1 = 0.f;
+  if (FOLD) {
+    e.f0 = p.fs[n];
+    if (EpiTraits<EPI>::pair) e.f1 = p.fs[n + 1];
+    if (EPI == EPI_ARGMAX) e.b0 = p.bias[n];
+  }
   e.c = 1.f; e.s = 0.f;
   e.kvoff = 0;
   if (EPI == EPI_PLAIN || EPI == EPI_GELU) {
@@ -190,14 +207,15 @@ __device__ __forceinline__ void stage_finish(const LinParams& p, float* xs, cons
     attn_merge_finish<4>(p.apart, p.Hq, p.hd, M, ar, xs, K, s_aw, GD_WG);
     return;
   }
+  // Every thread stores its (clamped) chunks: threads past the rows rewrite the last
+  // chunk with the value its owner writes. A conditional store would let the compiler
+  // sink the row loads into the branch, behind the weight loads, and wait for those.
   const int K4 = K >> 2;
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
-    const int i = tid + GD_WG * j;
-    if (i < M * K4) {
-      const int m = i / K4, k = (i - m * K4) << 2;
-      *reinterpret_cast<f32x4*>(xs + m * K + k) = rr.x[j];
-    }
+    const int i = min(tid + GD_WG * j, M * K4 - 1);
+    const int m = i / K4, k = (i - m * K4) << 2;
+    *reinterpret_cast<f32x4*>(xs + m * K + k) = rr.x[j];
   }
   for (int i = tid + GD_WG * XPT; i < M * K4; i += GD_WG) {   // rows beyond the register share
     const int m = i / K4, k = (i - m * K4) << 2;
@@ -214,10 +232,17 @@ struct WChunk<1> { typedef u32x4 T; static constexpr int CE = 8; };
 
 // ------------------------------------------------------------------ GEMV
 
-// PRO: source of the rows (PRO_COPY or PRO_ATTN); NRM: the rows are normalized
-// (p.norm: LayerNorm or RMSNorm). Both are compile-time so that every path issues a
-// fixed number of loads and the waits for the rows do not cover the weight stream.
-template <int WT, int NC, int RW, int EPI, int PRO, bool NRM>
+// PRO: source of the rows (PRO_COPY or PRO_ATTN); NRM: how a pre-norm (p.norm:
+// LayerNorm or RMSNorm) is applied (NRM_NONE, NRM_EXPLICIT, NRM_FOLDED). Both are
+// compile-time so that every path issues a fixed number of loads and the waits for the
+// rows do not cover the weight stream.
+//
+// NRM_FOLDED (fp32 weights): p.w holds g_k W_nk, p.bias the folded bias, p.fs the row
+// sums of p.w. A wave shifts its row by the row's first element, d = x - x_0, and
+// forms the moments of d; the dot products use d as is, so they do not wait for the
+// statistics, and the result is r (d . w_n - a s_n) + bias_n with a = mean(d) (this
+// equals r (x - mu) . w_n) and r = 1 / sqrt(var + eps). RMSNorm: no shift, a = 0.
+template <int WT, int NC, int RW, int EPI, int PRO, int NRM>
 __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   typedef typename WChunk<WT>::T VT;
   constexpr int CE = WChunk<WT>::CE;
@@ -237,7 +262,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   // the norm's gain and shift at this lane's chunks (RMSNorm: no shift; the gain is
   // loaded in its place so that the number of loads stays fixed)
   f32x4 gn[NC][CE / 4], bn[NC][CE / 4];
-  if constexpr (NRM) {
+  if constexpr (NRM == NRM_EXPLICIT) {
     const float* bsrc = p.nb ? p.nb : p.ng;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -269,14 +294,17 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   const int om = PAIR ? lane : lane / RW, orr = PAIR ? 0 : lane % RW;
   const int on = nw0 + orr;
   const bool own = EPI != EPI_ARGMAX && om < M && (PAIR ? nw0 + 1 < N : (lane < M * RW && on < N));
-  EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? on : 0);
+  // argmax: lane m * RW + r finishes output (m, nw0 + r)
+  const int an = min(nw0 + lane % RW, N - 1);
+  EpiOps eo = EPI == EPI_ARGMAX ? epi_prefetch<EPI, NRM == NRM_FOLDED>(p, 0, an)
+                                : epi_prefetch<EPI, NRM == NRM_FOLDED>(p, own ? om : 0, own ? on : 0);
   // 3. activation rows into LDS
   stage_finish<XPT, PRO>(p, xs, rr, ar, s_aw);
   __syncthreads();
-  // 4. dot products. With NRM every row is normalized on the fly: the lanes of a wave
-  //    hold the row's whole K range (chunks lane + 64 i), so each wave forms the row's
-  //    statistics itself (one-pass moments shifted by the row's first element, summed
-  //    with wave-level reductions) and no workgroup exchange is needed.
+  // 4. dot products. With a pre-norm every row is normalized on the fly: the lanes of a
+  //    wave hold the row's whole K range (chunks lane + 64 i), so each wave forms the
+  //    row's statistics itself (one-pass moments shifted by the row's first element,
+  //    summed with wave-level reductions) and no workgroup exchange is needed.
   float acc[RW][GEMV_MAX_ROWS];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -323,7 +351,9 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
         xv[i][h] = k < K ? *reinterpret_cast<const f32x4*>(xs + m * K + k + 4 * h) : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   };
-  if (!NRM && M > 1) {
+  float rsv[GEMV_MAX_ROWS], av[GEMV_MAX_ROWS];   // NRM_FOLDED: per-row 1/sqrt(var + eps), mean of d
+  const float invK = 1.0f / (float)K;
+  if (NRM == NRM_NONE && M > 1) {
     // several rows as staged: chunk-outer, so that each weight chunk meets every row
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
@@ -368,7 +398,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
       if (m < M) {
         f32x4 xv[NC][CE / 4];
         load_row(m, xv);
-        if constexpr (NRM) {
+        if constexpr (NRM != NRM_NONE) {
           const bool ln = p.norm == NORM_LN;
           const float sh = ln ? xs[m * K] : 0.f;
           float st[2] = {0.f, 0.f};
@@ -377,28 +407,34 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
             if ((lane + 64 * i) * CE < K) {
 #pragma unroll
               for (int h = 0; h < CE / 4; ++h) {
-                const float d0 = xv[i][h].x - sh, d1 = xv[i][h].y - sh, d2 = xv[i][h].z - sh, d3 = xv[i][h].w - sh;
-                st[0] += (d0 + d1) + (d2 + d3);
-                st[1] += fmaf(d0, d0, d1 * d1) + fmaf(d2, d2, d3 * d3);
+                f32x4& v = xv[i][h];
+                v.x -= sh; v.y -= sh; v.z -= sh; v.w -= sh;
+                st[0] += (v.x + v.y) + (v.z + v.w);
+                st[1] += fmaf(v.x, v.x, v.y * v.y) + fmaf(v.z, v.z, v.w * v.w);
               }
             }
           }
           wave_sum_n<2>(st);
-          const float a = st[0] / (float)K;   // mean of the shifted values
-          const float var = ln ? fmaxf(st[1] / (float)K - a * a, 0.f) : st[1] / (float)K;
-          const float mu = ln ? sh + a : 0.f;
-          const float rs = 1.0f / sqrtf(var + p.eps);
-          const float bs = ln ? 1.f : 0.f;
+          const float a = ln ? st[0] * invK : 0.f;   // mean of the shifted values
+          const float var = fmaxf(st[1] * invK - a * a, 0.f);
+          const float rs = rsqrtf(var + p.eps);
+          if constexpr (NRM == NRM_FOLDED) {
+            rsv[m] = rs;
+            av[m] = a;
+          } else {
+            // (x - mu) r g + b with x - mu = d - a
 #pragma unroll
-          for (int i = 0; i < NC; ++i)
+            for (int i = 0; i < NC; ++i)
 #pragma unroll
-            for (int h = 0; h < CE / 4; ++h) {
-              f32x4& v = xv[i][h];
-              v.x = (v.x - mu) * rs * gn[i][h].x + bs * bn[i][h].x;
-              v.y = (v.y - mu) * rs * gn[i][h].y + bs * bn[i][h].y;
-              v.z = (v.z - mu) * rs * gn[i][h].z + bs * bn[i][h].z;
-              v.w = (v.w - mu) * rs * gn[i][h].w + bs * bn[i][h].w;
-            }
+              for (int h = 0; h < CE / 4; ++h) {
+                f32x4& v = xv[i][h];
+                const f32x4 g = gn[i][h], b = bn[i][h];
+                v.x = fmaf((v.x - a) * rs, g.x, ln ? b.x : 0.f);
+                v.y = fmaf((v.y - a) * rs, g.y, ln ? b.y : 0.f);
+                v.z = fmaf((v.z - a) * rs, g.z, ln ? b.z : 0.f);
+                v.w = fmaf((v.w - a) * rs, g.w, ln ? b.w : 0.f);
+              }
+          }
         }
         dot_row(m, xv);
       }
@@ -411,19 +447,19 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
       if (m < M) acc[r][m] = wave_sum(acc[r][m]);
   // 5. epilogue
   if (EPI == EPI_ARGMAX) {
-    if (lane == 0) {
+    if (lane < M * RW) {
+      const int am = lane / RW, ar = lane % RW;
+      float v = 0.f;
 #pragma unroll
       for (int m = 0; m < GEMV_MAX_ROWS; ++m)
 #pragma unroll
         for (int r = 0; r < RW; ++r)
-          if (m < M) s_am[m][wave * RW + r] = acc[r][m];
-    }
-    if (p.logits && lane < M * RW) {
-#pragma unroll
-      for (int m = 0; m < GEMV_MAX_ROWS; ++m)
-#pragma unroll
-        for (int r = 0; r < RW; ++r)
-          if (lane == m * RW + r && nw0 + r < N) p.logits[(size_t)m * p.ldl + nw0 + r] = acc[r][m];
+          if (m == am && r == ar) {
+            v = acc[r][m];
+            if (NRM == NRM_FOLDED) v = fmaf(rsv[m], v - av[m] * eo.f0, eo.b0);
+          }
+      s_am[am][wave * RW + ar] = v;
+      if (p.logits && nw0 + ar < N) p.logits[(size_t)am * p.ldl + nw0 + ar] = v;
     }
     __syncthreads();
     if (tid < M) {
@@ -440,12 +476,17 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   if (!own) return;
   float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-  for (int m = 0; m < GEMV_MAX_ROWS; ++m)
+  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       if (m == om && r == orr) v0 = acc[r][m];
       if (m == om && r == orr + 1) v1 = acc[r][m];
     }
+    if (NRM == NRM_FOLDED && m == om) {
+      v0 = rsv[m] * (v0 - av[m] * eo.f0);
+      v1 = rsv[m] * (v1 - av[m] * eo.f1);
+    }
+  }
   epi_store<EPI>(p, eo, om, on, v0, v1);
 }
 

@@ -157,29 +157,43 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
   return p;
 }
 
+// With a pre-norm whose folded form is given (fp32 weights, prm.wf), the folded
+// weights, bias and row sums replace the layer's own (NRM_FOLDED).
 template <int WT, int NC>
-static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipStream_t st) {
   const dim3 g(lp.grid), b(GD_WG);
-  const bool nrm = prm.norm != NORM_NONE;
+  const bool nrm = prm0.norm != NORM_NONE;
+  const bool fold = WT == 0 && nrm && prm0.wf;
+  LinParams prm = prm0;
+  if (fold) {
+    prm.w = prm0.wf;
+    prm.bias = prm0.bf;
+  }
 #define GD_GEMV(RW, EPI, PRO, NRM) GD_LAUNCH((k_gemv<WT, NC, RW, EPI, PRO, NRM>), g, b, lp.lds, st, prm)
+#define GD_GEMV_N(RW, EPI)                                                   \
+  do {                                                                       \
+    if (fold) GD_GEMV(RW, EPI, PRO_COPY, NRM_FOLDED);                        \
+    else GD_GEMV(RW, EPI, PRO_COPY, NRM_EXPLICIT);                           \
+  } while (0)
   if (prm.pro == PRO_ATTN) {   // the output projection behind split-context attention
     if (prm.epi != EPI_PLAIN || nrm) return hipErrorNotSupported;
-    GD_GEMV(1, EPI_PLAIN, PRO_ATTN, false);
+    GD_GEMV(1, EPI_PLAIN, PRO_ATTN, NRM_NONE);
     return hipSuccess;
   }
   switch (prm.epi) {
-    case EPI_PLAIN: if (nrm) GD_GEMV(1, EPI_PLAIN, PRO_COPY, true); else GD_GEMV(1, EPI_PLAIN, PRO_COPY, false); break;
-    case EPI_GELU: if (nrm) GD_GEMV(1, EPI_GELU, PRO_COPY, true); else GD_GEMV(1, EPI_GELU, PRO_COPY, false); break;
+    case EPI_PLAIN: if (nrm) GD_GEMV_N(1, EPI_PLAIN); else GD_GEMV(1, EPI_PLAIN, PRO_COPY, NRM_NONE); break;
+    case EPI_GELU: if (nrm) GD_GEMV_N(1, EPI_GELU); else GD_GEMV(1, EPI_GELU, PRO_COPY, NRM_NONE); break;
     // the remaining epilogues always follow a pre-norm
-    case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_GEMV(1, EPI_QKV, PRO_COPY, true); break;
-    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_GEMV(2, EPI_SWIGLU, PRO_COPY, true); break;
-    case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_GEMV(2, EPI_QKV_ROPE, PRO_COPY, true); break;
+    case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_GEMV_N(1, EPI_QKV); break;
+    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_GEMV_N(2, EPI_SWIGLU); break;
+    case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_GEMV_N(2, EPI_QKV_ROPE); break;
     default:
       if (!nrm) return hipErrorNotSupported;
-      if (lp.rw == 4) GD_GEMV(4, EPI_ARGMAX, PRO_COPY, true);
-      else GD_GEMV(1, EPI_ARGMAX, PRO_COPY, true);
+      if (lp.rw == 4) GD_GEMV_N(4, EPI_ARGMAX);
+      else GD_GEMV_N(1, EPI_ARGMAX);
       break;
   }
+#undef GD_GEMV_N
 #undef GD_GEMV
   return hipSuccess;
 }
@@ -274,6 +288,8 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
 struct LayerOff {
   size_t n1g, n1b, wqkv, bqkv, wo, bo, n2g, n2b, wfc, bfc, wproj, bproj;
   size_t tqkv, to, tfc, tproj;   // tile-major copies of the matrices (matrix-core kernel)
+  // pre-norm folded into QKV and MLP-up (fp32): weights, bias, row sums (0: none)
+  size_t fqkv, fqkv_b, fqkv_s, ffc, ffc_b, ffc_s;
 };
 
 struct GraphKey {
@@ -299,6 +315,7 @@ struct gd_model {
   int variant = 0;
   bool use_graph = true;
   bool fuse_attn_o = true;
+  bool use_fold = true;  // GEMV pre-norms folded into the weights when available (GD_OPT_FOLD_NORM)
   bool use_pk = false;  // single-launch decode step for one sequence (GD_OPT_PERSISTENT; measured slower)
   long long pk_spin_us = 20000;   // bound of its waits (GD_OPT_PERSISTENT_SPIN_US)
   int dev = 0;
@@ -322,6 +339,8 @@ struct gd_model {
 
   // weight offsets (bytes)
   size_t o_wte = 0, o_wpe = 0, o_nfg = 0, o_nfb = 0, o_head = 0, o_thead = 0;
+  size_t o_fhead = 0, o_fhead_b = 0, o_fhead_s = 0, o_fold = 0;   // folded final norm + head
+  bool folded = false;   // the folded copies exist (fp32 weights)
   std::vector<LayerOff> L;
 
   // scratch offsets (bytes)
@@ -390,7 +409,6 @@ static gd_status check_cfg(const gd_config* c) {
 }
 
 // Weight chunks (16 bytes) per lane of a K-long row in the single-launch step.
-static int pk_chunks(int K, int wt) { return iceil(K, 64 * (wt == GD_WEIGHT_F32 ? 4 : 8)); }
 
 // The single-launch decode step handles one sequence of the GPT-2 layout whose shapes
 // match an instantiated kernel and fit its LDS staging.
@@ -474,6 +492,24 @@ static void layout(gd_model* m) {
     t.tproj = take(mm_packed_bytes(wt, (int)d, (int)ff));
   }
   m->o_thead = take(mm_packed_bytes(wt, (int)V, (int)d));
+  // the pre-norms folded into the layers that follow them (fp32 weights only: a bf16
+  // copy of g_k W_nk would round the weights a second time)
+  m->folded = m->wt == GD_WEIGHT_F32;
+  m->o_fold = off;
+  if (m->folded) {
+    for (int l = 0; l < c.n_layer; ++l) {
+      LayerOff& t = m->L[l];
+      t.fqkv = take((size_t)m->qkvdim * d * 4);
+      t.fqkv_b = take((size_t)m->qkvdim * 4);
+      t.fqkv_s = take((size_t)m->qkvdim * 4);
+      t.ffc = take((size_t)m->fcN * d * 4);
+      t.ffc_b = take((size_t)m->fcN * 4);
+      t.ffc_s = take((size_t)m->fcN * 4);
+    }
+    m->o_fhead = take(V * d * 4);
+    m->o_fhead_b = take(V * 4);
+    m->o_fhead_s = take(V * 4);
+  }
   m->w_bytes = off;
 
   // KV cache: K pools for all layers, then V pools
@@ -758,6 +794,43 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     put_mat(m, buf, m->o_head, p, V * d); p += V * d;
   }
   HIP_TRY(m, hipMemcpyAsync(m->w, buf.data(), buf.size(), hipMemcpyHostToDevice, m->stream));
+  std::vector<char> fbuf;
+  if (m->folded) {
+    // W'_nk = g_k W_nk (one fp32 product), s_n = sum_k W'_nk, bias'_n = bias_n +
+    // sum_k b_k W_nk, from the row-major matrices as stored (sums in double)
+    fbuf.assign(m->w_bytes - m->o_fold, 0);
+    auto rf = [&](size_t off) { return reinterpret_cast<const float*>(buf.data() + off); };
+    auto wf = [&](size_t off) { return reinterpret_cast<float*>(fbuf.data() + (off - m->o_fold)); };
+    auto fold = [&](size_t w, int N, size_t g, size_t b, size_t bias, size_t fw, size_t fb, size_t fs) {
+      const float* W = rf(w);
+      const float* G = rf(g);
+      const float* B = b ? rf(b) : nullptr;
+      const float* bi = bias ? rf(bias) : nullptr;
+      float* Wf = wf(fw);
+      float* Bf = wf(fb);
+      float* Sf = wf(fs);
+      for (size_t n = 0; n < (size_t)N; ++n) {
+        double sn = 0.0, bn = bi ? (double)bi[n] : 0.0;
+        for (size_t k = 0; k < d; ++k) {
+          const float v = W[n * d + k];
+          const float f = G[k] * v;
+          Wf[n * d + k] = f;
+          sn += (double)f;
+          if (B) bn += (double)B[k] * (double)v;
+        }
+        Sf[n] = (float)sn;
+        Bf[n] = (float)bn;
+      }
+    };
+    for (int l = 0; l < c.n_layer; ++l) {
+      const LayerOff& t = m->L[l];
+      fold(t.wqkv, m->qkvdim, t.n1g, t.n1b, t.bqkv, t.fqkv, t.fqkv_b, t.fqkv_s);
+      fold(t.wfc, m->fcN, t.n2g, t.n2b, t.bfc, t.ffc, t.ffc_b, t.ffc_s);
+    }
+    fold(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, (int)V, m->o_nfg, m->o_nfb, 0, m->o_fhead, m->o_fhead_b,
+         m->o_fhead_s);
+    HIP_TRY(m, hipMemcpyAsync(m->w + m->o_fold, fbuf.data(), fbuf.size(), hipMemcpyHostToDevice, m->stream));
+  }
   auto pack = [&](size_t src, size_t dst, int N, int K) {
     return launch_pack(m->w + src, m->wt, N, K, m->w + dst, m->stream);
   };
@@ -863,6 +936,8 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->use_graph = v != 0;
   } else if (opt == GD_OPT_FUSE_ATTN_O) {
     m->fuse_attn_o = v != 0;
+  } else if (opt == GD_OPT_FOLD_NORM) {
+    m->use_fold = v != 0;
   } else if (opt == GD_OPT_PERSISTENT) {
     m->use_pk = v != 0;
   } else if (opt == GD_OPT_PERSISTENT_SPIN_US) {
@@ -940,11 +1015,13 @@ struct ProfScope {
   }
 };
 
-static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, int pro, char* buf, size_t n) {
+static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, bool fold, int pro, char* buf,
+                                      size_t n) {
   const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
   // as rocprofv3 prints the instantiation
   if (lp.var == 0)
-    snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %s>", w, lp.nc, lp.rw, epi, pro, norm ? "true" : "false");
+    snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %d>", w, lp.nc, lp.rw, epi, pro,
+             !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT);
   else snprintf(buf, n, "k_mm<%d, %d, %d, %s, %s>", w, lp.mt, epi, norm ? "true" : "false", lp.passes > 1 ? "true" : "false");
   return buf;
 }
@@ -970,7 +1047,8 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
   std::vector<std::pair<hipEvent_t, hipEvent_t>> fin;
   hipError_t e;
   {
-    ProfScope ps(m, st, role, linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, p.pro, kn, sizeof(kn)),
+    ProfScope ps(m, st, role,
+                 linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, p.wf != nullptr, p.pro, kn, sizeof(kn)),
                  m->profile ? linear_bytes(m, p) : 0);
     t_prof_fin = &fin;
     e = run_linear_rows(m->wt, lp, p, st, am_out);
@@ -1043,6 +1121,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
+  const bool fold = m->folded && m->use_fold;   // used by the GEMV path only
 
   double kv_pos = 0;  // attended positions summed over rows (profiling only)
   for (int t : m->prof_T) kv_pos += t;
@@ -1066,6 +1145,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
       p.w = m->w + t.wqkv; p.wtl = m->w + t.tqkv; p.N = m->qkvdim; p.K = d;
+      if (fold) { p.wf = m->w + t.fqkv; p.bf = m->wf(t.fqkv_b); p.fs = m->wf(t.fqkv_s); }
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
       p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
       p.y = q; p.ldy = m->qdim;
@@ -1140,6 +1220,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n2g); p.nb = t.n2b ? m->wf(t.n2b) : nullptr;
       p.w = m->w + t.wfc; p.wtl = m->w + t.tfc; p.N = m->fcN; p.K = d;
+      if (fold) { p.wf = m->w + t.ffc; p.bf = m->wf(t.ffc_b); p.fs = m->wf(t.ffc_s); }
       p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
       p.bias = t.bfc ? m->wf(t.bfc) : zero;
       p.resid = zero; p.ldr = 0;
@@ -1165,6 +1246,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.x = x + (size_t)head_row * d; p.ldx = d;
     p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
     p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
+    if (fold) { p.wf = m->w + m->o_fhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s); }
     p.epi = EPI_ARGMAX;
     p.M = head_rows;
     p.row_kvoff = rp.row_kvoff + head_row;
