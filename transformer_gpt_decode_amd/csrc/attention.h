@@ -38,38 +38,69 @@ struct AttnParams {
 // Online softmax of the G query heads of KV head kh of `row` over positions [p0, p1):
 // groups of HD/4 lanes take one position per step (float4 of K and V per lane, all
 // loads of a step issued before the arithmetic), each keeping a running max, sum and
-// weighted V per query head; the groups are then merged in LDS. On return (after a
-// barrier) thread tid < G * HD holds, for query head g = tid / HD and dimension
-// d = tid % HD, the range's max, sum and weighted V (max -inf and zeros for an empty
-// range).
+// weighted V per query head. The groups of a wave are then merged with cross-lane
+// exchanges and the waves through LDS. On return (after a barrier) thread
+// tid < G * HD holds, for query head g = tid / HD and dimension d = tid % HD, the
+// range's max, sum and weighted V (max -inf and zeros for an empty range).
 template <int HD, int G, int PPG>
 struct AttnScanLds {
-  static constexpr int LG = HD / 4, NG = GD_WG / LG;
-  float m[NG][G], l[NG][G];
-  __align__(16) float o[NG][G][HD];
+  static constexpr int NW = GD_WG / 64;
+  float m[NW][G], l[NW][G];
+  __align__(16) float o[NW][G][HD];
 };
 
-template <int HD, int G, int PPG, bool PAGED>
-__device__ void attn_scan(const AttnParams& p, int row, int kh, int p0, int p1, AttnScanLds<HD, G, PPG>& sh,
-                          float& m_out, float& l_out, float& o_out) {
-  constexpr int LG = HD / 4;            // lanes per position group
-  constexpr int NG = GD_WG / LG;        // position groups per workgroup
-  constexpr int STEP = NG * PPG;        // positions per step
-  const int tid = threadIdx.x;
-  const int grp = tid / LG, gl = tid % LG;
-  const int pos = p.row_pos[row];
-
-  f32x4 q[G];
+// This lane's query values (lanes gl of every position group: dims 4 gl .. 4 gl + 3
+// of each query head of KV head kh).
+template <int HD, int G>
+__device__ __forceinline__ void attn_load_q(const AttnParams& p, int row, int kh, f32x4 (&q)[G]) {
+  const int gl = threadIdx.x % (HD / 4);
 #pragma unroll
   for (int g = 0; g < G; ++g)
     q[g] = *reinterpret_cast<const f32x4*>(p.q + (size_t)row * p.ldq + (kh * G + g) * HD + gl * 4);
+}
+
+// A row's metadata, read with scalar loads (row is uniform over the workgroup), so that
+// waiting for them does not wait for vector loads issued earlier; the empty asm takes
+// them all as operands, so they are issued together and waited for once.
+struct AttnRow {
+  int pos, seq;
+  long long kvoff;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ AttnRow attn_row(const AttnParams& p, int row) {
+  AttnRow r;
+  r.pos = *(const __attribute__((address_space(4))) int*)(p.row_pos + row);
+  r.seq = PAGED ? *(const __attribute__((address_space(4))) int*)(p.row_seq + row) : 0;
+  r.kvoff = PAGED ? 0 : *(const __attribute__((address_space(4))) long long*)(p.row_kvoff + row);
+  asm volatile("" ::"s"(r.pos), "s"(r.seq), "s"(r.kvoff));
+  return r;
+}
+
+// Weight of a partial with max m in a merge whose max is mm (0 when both are -inf).
+__device__ __forceinline__ float attn_rescale(float m, float mm) { return mm == -INFINITY ? 0.f : expf(m - mm); }
+
+// Loads are unconditional (a position past the range is clamped to its last position,
+// an invalid cache block to block 0) and masked afterwards, so that the compiler keeps
+// them where they are issued instead of sinking them into branches.
+template <int HD, int G, int PPG, bool PAGED>
+__device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0, int p1, const f32x4 (&q)[G],
+                          AttnScanLds<HD, G, PPG>& sh, float& m_out, float& l_out, float& o_out) {
+  constexpr int LG = HD / 4;            // lanes per position group
+  constexpr int NG = GD_WG / LG;        // position groups per workgroup
+  constexpr int STEP = NG * PPG;        // positions per step
+  constexpr int NW = GD_WG / 64;
+  const int tid = threadIdx.x;
+  const int grp = tid / LG, gl = tid % LG;
+  const int pos = rm.pos;
+
   const float* kbase = nullptr;
   const float* vbase = nullptr;
   const int* tab = nullptr;
   if (PAGED) {
-    tab = p.table + (size_t)p.row_seq[row] * p.max_blocks;
+    tab = p.table + (size_t)rm.seq * p.max_blocks;
   } else {
-    const long long base = p.row_kvoff[row] - (long long)pos * HD + (long long)kh * p.block_size * HD;
+    const long long base = rm.kvoff - (long long)pos * HD + (long long)kh * p.block_size * HD;
     kbase = p.kc + base + gl * 4;
     vbase = p.vc + base + gl * 4;
   }
@@ -79,31 +110,30 @@ __device__ void attn_scan(const AttnParams& p, int row, int kh, int p0, int p1, 
 #pragma unroll
   for (int g = 0; g < G; ++g) { mx[g] = -INFINITY; l[g] = 0.f; o[g] = (f32x4){0.f, 0.f, 0.f, 0.f}; }
 
-  for (int s0 = p0; s0 < p1; s0 += STEP) {
-    f32x4 kv[PPG], vv[PPG];
-    bool ok[PPG];
+  f32x4 kv[PPG], vv[PPG];
+  bool ok[PPG];
+  auto issue = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
-      const int ps = s0 + grp + NG * j;
-      ok[j] = false;
-      kv[j] = vv[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (ps < p1) {
-        if (PAGED) {
-          const int bi = ps / p.block_size;
-          const int blk = tab[bi];
-          if ((unsigned)blk < (unsigned)p.nblk) {
-            const size_t off = (((size_t)blk * p.Hkv + kh) * p.block_size + (ps - bi * p.block_size)) * HD + gl * 4;
-            kv[j] = *reinterpret_cast<const f32x4*>(p.kc + off);
-            vv[j] = *reinterpret_cast<const f32x4*>(p.vc + off);
-            ok[j] = true;
-          }
-        } else {
-          kv[j] = *reinterpret_cast<const f32x4*>(kbase + (size_t)ps * HD);
-          vv[j] = *reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
-          ok[j] = true;
-        }
+      const int pr = s0 + grp + NG * j;
+      const int ps = min(pr, p1 - 1);
+      ok[j] = pr < p1;
+      size_t off;
+      if (PAGED) {
+        const int bi = ps / p.block_size;
+        const int blk = tab[bi];
+        const bool valid = (unsigned)blk < (unsigned)p.nblk;
+        ok[j] = ok[j] && valid;
+        off = (((size_t)(valid ? blk : 0) * p.Hkv + kh) * p.block_size + (ps - bi * p.block_size)) * HD + gl * 4;
+        kv[j] = *reinterpret_cast<const f32x4*>(p.kc + off);
+        vv[j] = *reinterpret_cast<const f32x4*>(p.vc + off);
+      } else {
+        kv[j] = *reinterpret_cast<const f32x4*>(kbase + (size_t)ps * HD);
+        vv[j] = *reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
       }
     }
+  };
+  auto consume = [&]() {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s[PPG];
@@ -114,51 +144,76 @@ __device__ void attn_scan(const AttnParams& p, int row, int kh, int p0, int p1, 
         d = fmaf(q[g].y, kv[j].y, d);
         d = fmaf(q[g].z, kv[j].z, d);
         d = fmaf(q[g].w, kv[j].w, d);
-        s[j] = group_sum<LG>(d) * p.scale;
-        if (ok[j]) smax = fmaxf(smax, s[j]);
+        // computed for every position and masked after: a conditional here would let
+        // the compiler sink the K load into the branch, behind later loads
+        const float sj = group_sum<LG>(d) * p.scale;
+        s[j] = ok[j] ? sj : -INFINITY;
+        smax = fmaxf(smax, s[j]);
       }
-      if (smax == -INFINITY) continue;   // this group saw no position in this step
-      const float nm = fmaxf(mx[g], smax);
-      const float sc = expf(mx[g] - nm);
+      const float nm = fmaxf(mx[g], smax);   // -inf only if this group has seen no position yet
+      const float sc = attn_rescale(mx[g], nm);
       l[g] *= sc;
       o[g].x *= sc; o[g].y *= sc; o[g].z *= sc; o[g].w *= sc;
 #pragma unroll
       for (int j = 0; j < PPG; ++j) {
-        if (ok[j]) {
-          const float e = expf(s[j] - nm);
-          l[g] += e;
-          o[g].x = fmaf(e, vv[j].x, o[g].x);
-          o[g].y = fmaf(e, vv[j].y, o[g].y);
-          o[g].z = fmaf(e, vv[j].z, o[g].z);
-          o[g].w = fmaf(e, vv[j].w, o[g].w);
-        }
+        const float ej = expf(s[j] - nm);
+        const float e = ok[j] ? ej : 0.f;
+        l[g] += e;
+        o[g].x = fmaf(e, vv[j].x, o[g].x);
+        o[g].y = fmaf(e, vv[j].y, o[g].y);
+        o[g].z = fmaf(e, vv[j].z, o[g].z);
+        o[g].w = fmaf(e, vv[j].w, o[g].w);
       }
       mx[g] = nm;
     }
+  };
+  for (int s0 = p0; s0 < p1; s0 += STEP) {
+    issue(s0);
+    consume();
   }
+  // merge the groups of each wave (lanes gl + LG r) by exchanges between lanes
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if (gl == 0) { sh.m[grp][g] = mx[g]; sh.l[grp][g] = l[g]; }
-    *reinterpret_cast<f32x4*>(&sh.o[grp][g][gl * 4]) = o[g];
+#pragma unroll
+    for (int off = LG; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(mx[g], off), l2 = __shfl_xor(l[g], off);
+      f32x4 o2;
+      o2.x = __shfl_xor(o[g].x, off); o2.y = __shfl_xor(o[g].y, off);
+      o2.z = __shfl_xor(o[g].z, off); o2.w = __shfl_xor(o[g].w, off);
+      const float mm = fmaxf(mx[g], m2);
+      const float s1 = attn_rescale(mx[g], mm), s2 = attn_rescale(m2, mm);
+      l[g] = fmaf(l[g], s1, l2 * s2);
+      o[g].x = fmaf(o[g].x, s1, o2.x * s2); o[g].y = fmaf(o[g].y, s1, o2.y * s2);
+      o[g].z = fmaf(o[g].z, s1, o2.z * s2); o[g].w = fmaf(o[g].w, s1, o2.w * s2);
+      mx[g] = mm;
+    }
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  if (lane < LG) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (lane == 0) { sh.m[wave][g] = mx[g]; sh.l[wave][g] = l[g]; }
+      *reinterpret_cast<f32x4*>(&sh.o[wave][g][lane * 4]) = o[g];
+    }
   }
   __syncthreads();
-  // merge the NG groups: one thread per (query head g, dim d)
+  // merge the waves: one thread per (query head g, dim d)
   m_out = -INFINITY;
   l_out = o_out = 0.f;
   if (tid < G * HD) {
     const int g = tid / HD, d = tid % HD;
-    float m = -INFINITY;
-    for (int i = 0; i < NG; ++i) m = fmaxf(m, sh.m[i][g]);
+    float mw[NW];
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { mw[w] = sh.m[w][g]; mm = fmaxf(mm, mw[w]); }
     float ls = 0.f, acc = 0.f;
-    if (m != -INFINITY) {
-      for (int i = 0; i < NG; ++i) {
-        if (sh.l[i][g] == 0.f) continue;   // group saw no position
-        const float w = expf(sh.m[i][g] - m);
-        ls = fmaf(sh.l[i][g], w, ls);
-        acc = fmaf(sh.o[i][g][d], w, acc);
-      }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float s = attn_rescale(mw[w], mm);
+      ls = fmaf(sh.l[w][g], s, ls);
+      acc = fmaf(sh.o[w][g][d], s, acc);
     }
-    m_out = m;
+    m_out = mm;
     l_out = ls;
     o_out = acc;
   }
@@ -168,11 +223,14 @@ template <int HD, int G, int PPG, bool PAGED>
 __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
   __shared__ AttnScanLds<HD, G, PPG> sh;
   const int c = blockIdx.x, kh = blockIdx.y, row = blockIdx.z;
-  const int T = p.row_pos[row] + 1;
+  const AttnRow rm = attn_row<PAGED>(p, row);
+  f32x4 q[G];
+  attn_load_q<HD, G>(p, row, kh, q);
+  const int T = rm.pos + 1;
   const int L = (T + GD_ATT_NCH - 1) / GD_ATT_NCH;
   const int p0 = min(T, c * L), p1 = min(T, p0 + L);
   float m, l, o;
-  attn_scan<HD, G, PPG, PAGED>(p, row, kh, p0, p1, sh, m, l, o);
+  attn_scan<HD, G, PPG, PAGED>(p, rm, kh, p0, p1, q, sh, m, l, o);
   if (threadIdx.x < G * HD) {
     const int g = threadIdx.x / HD, d = threadIdx.x % HD;
     float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * GD_ATT_NCH + c) * (HD + 2);
@@ -187,7 +245,10 @@ __global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
 // come from cache), normalizes them, and adds their share of the projection,
 // sum over g, d of o[g][d] W[n][(kh G + g) HD + d], to the residual rows n of its
 // slice with float atomics (the bias from kh == 0). A slice is ROWS consecutive n; its
-// weights (HD/4 lanes per row, float4 or four bf16 each) are loaded before the scan.
+// weights (HD/4 lanes per row, float4 or four bf16 each) and bias are loaded first.
+// The atomics of all passes go out together at the end, after the last wait (vector
+// memory operations of a wave complete in issue order: an atomic issued before a later
+// wait would be waited for).
 struct AttnOParams {
   const void* w;          // W_o [N][K] (K = Hq * HD), fp32 or bf16 bits
   const float* bias;      // never NULL
@@ -200,15 +261,25 @@ struct AttnORows { static constexpr int LG = HD / 4, PER_PASS = GD_WG / LG, PASS
                    ROWS = PER_PASS * PASSES; };
 
 template <int HD, int G, int PPG, bool PAGED, int WT>
-__global__ __launch_bounds__(GD_WG) void k_attn_o(AttnParams p, AttnOParams po) {
+__global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_o(AttnParams p, AttnOParams po) {
   using RT = AttnORows<HD>;
   __shared__ AttnScanLds<HD, G, PPG> sh;
   __shared__ __align__(16) float s_o[G][HD];
   const int kh = blockIdx.y, row = blockIdx.z;
   const int tid = threadIdx.x, grp = tid / RT::LG, gl = tid % RT::LG;
   const int n0 = blockIdx.x * RT::ROWS;
-  // the slice's weights first: they depend on nothing
+  // Every kernel argument the launch reads, loaded at once: left to itself the compiler
+  // loads each just before its first use, a chain of scalar round trips ahead of the
+  // metadata, query and K/V loads.
+  asm volatile("" ::"s"(p.q), "s"(p.kc), "s"(p.vc), "s"(p.row_pos), "s"(p.row_kvoff), "s"(p.row_seq), "s"(p.table),
+               "s"(po.w), "s"(po.bias), "s"(po.y), "s"(p.ldq), "s"(p.max_blocks), "s"(p.block_size), "s"(p.nblk),
+               "s"(p.Hkv), "s"(p.scale), "s"(po.ldy), "s"(po.N), "s"(po.K));
+  // Then, in this order: the slice's weights and bias (vector loads that depend on
+  // nothing), the row's metadata (scalar loads, waited for at once), the query and the
+  // K/V loads. Vector loads complete in issue order, so the weights, needed last,
+  // arrive first and the wait for the K/V covers them at no cost.
   f32x4 wv[RT::PASSES][G];
+  float bv[RT::PASSES];
 #pragma unroll
   for (int ps = 0; ps < RT::PASSES; ++ps) {
     const int n = min(n0 + ps * RT::PER_PASS + grp, po.N - 1);
@@ -222,28 +293,38 @@ __global__ __launch_bounds__(GD_WG) void k_attn_o(AttnParams p, AttnOParams po) 
         wv[ps][g] = (f32x4){bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
       }
     }
+    bv[ps] = po.bias[n];
   }
-  const int T = p.row_pos[row] + 1;
+  const AttnRow rm = attn_row<PAGED>(p, row);
+  f32x4 q[G];
+  attn_load_q<HD, G>(p, row, kh, q);
   float m, l, o;
-  attn_scan<HD, G, PPG, PAGED>(p, row, kh, 0, T, sh, m, l, o);
+  attn_scan<HD, G, PPG, PAGED>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
   if (tid < G * HD) s_o[tid / HD][tid % HD] = l > 0.f ? o / l : 0.f;
   __syncthreads();
+  float acc[RT::PASSES];
 #pragma unroll
   for (int ps = 0; ps < RT::PASSES; ++ps) {
-    const int n = n0 + ps * RT::PER_PASS + grp;
-    float acc = 0.f;
+    float a = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const f32x4 ov = *reinterpret_cast<const f32x4*>(&s_o[g][gl * 4]);
-      acc = fmaf(wv[ps][g].x, ov.x, acc);
-      acc = fmaf(wv[ps][g].y, ov.y, acc);
-      acc = fmaf(wv[ps][g].z, ov.z, acc);
-      acc = fmaf(wv[ps][g].w, ov.w, acc);
+      a = fmaf(wv[ps][g].x, ov.x, a);
+      a = fmaf(wv[ps][g].y, ov.y, a);
+      a = fmaf(wv[ps][g].z, ov.z, a);
+      a = fmaf(wv[ps][g].w, ov.w, a);
     }
-    acc = group_sum<RT::LG>(acc);
+    acc[ps] = group_sum<RT::LG>(a) + (kh == 0 ? bv[ps] : 0.f);
+  }
+  // every sum complete before the first atomic (the empty asm takes them as operands):
+  // a wait placed after an atomic would wait for that atomic too
+#pragma unroll
+  for (int ps = 0; ps < RT::PASSES; ++ps) asm volatile("" ::"v"(acc[ps]));
+#pragma unroll
+  for (int ps = 0; ps < RT::PASSES; ++ps) {
+    const int n = n0 + ps * RT::PER_PASS + grp;
     if (gl == 0 && n < po.N)
-      __hip_atomic_fetch_add(po.y + (size_t)row * po.ldy + n, acc + (kh == 0 ? po.bias[n] : 0.f), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(po.y + (size_t)row * po.ldy + n, acc[ps], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
