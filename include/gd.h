@@ -61,7 +61,7 @@ typedef enum {
 
 typedef struct {
   int32_t arch;           /* GD_ARCH_* */
-  int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab;
+  int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab;   /* d_model, d_ff: multiples of 8, <= 2^20 */
   int32_t n_ctx;          /* positions per sequence (GPT-2: rows of the position table) */
   float norm_eps;         /* LayerNorm / RMSNorm epsilon */
   float rope_theta;       /* Llama only */
@@ -157,11 +157,12 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
 #define GD_OPT_PERSISTENT_SPIN_US 6 /* bound of every wait inside the single-launch step, in
                                      * microseconds (default 20000); a step that exceeds it is
                                      * abandoned and flagged (device error bit 3) */
-#define GD_OPT_FOLD_NORM 7 /* 1 (default): with fp32 weights the VALU GEMV of a layer
-                           * behind a pre-norm (QKV, MLP up, head) reads a copy of its
-                           * weights with the norm's gain folded in (and the shift in
-                           * its bias), made at gd_load_weights; 0: it applies the
-                           * norm's gain and shift to the row */
+#define GD_OPT_FOLD_NORM 7 /* 1 (default): with fp32 weights a layer behind a pre-norm
+                           * (QKV, MLP up, head) reads copies of its weights with the
+                           * norm's gain folded in (and the shift in its bias), made at
+                           * gd_load_weights, and applies the row statistics in its
+                           * epilogue; 0: the norm's gain and shift are applied to the
+                           * row first */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper
@@ -204,7 +205,7 @@ gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, 
 /* y[m][n] = act(norm(x[m]) . W[n]^T + bias[n]) (+ resid[m][n]) for m < M, n < N.
  * x: float [M][ldx] (K used); W: [N][K] float32 or bf16 bits (weight_dtype); bias,
  * norm_g, norm_b: float or NULL; resid: float [M][ldr] or NULL; y: float [M][ldy].
- * 1 <= M <= 32, N >= 1, K >= 8 and K % 8 == 0; W must be 16-byte aligned.
+ * 1 <= M <= 32, N >= 1, 8 <= K <= 2^20 and K % 8 == 0; W must be 16-byte aligned.
  * variant: 0 auto, 1 VALU GEMV, 2 MFMA. workspace: gd_linear_workspace bytes, zeroed
  * once before first use. Its first part (a zero vector) is never written; the rest
  * receives, on each call that runs the MFMA kernel, the tile-major copy of W that

@@ -132,6 +132,7 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
         vv[j] = *reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // all of this step's loads go out before any arithmetic
   };
   auto consume = [&]() {
 #pragma unroll

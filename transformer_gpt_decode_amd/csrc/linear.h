@@ -69,6 +69,7 @@ struct LinParams {
   // LN(x)_k = (x_k - mu) r g_k + b_k the layer is y_n = r sum_k (x_k - mu) g_k W_nk +
   // (bias_n + sum_k b_k W_nk): wf holds g_k W_nk, bf the bracket, fs the row sums of wf.
   const void* wf; const float* bf; const float* fs;
+  const void* wfl;                          // wf, tile-major (matrix-core kernel)
   // ---- epilogue
   int epi;
   const float* bias;                        // never NULL: a zero vector when the layer has none
@@ -298,6 +299,9 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   const int an = min(nw0 + lane % RW, N - 1);
   EpiOps eo = EPI == EPI_ARGMAX ? epi_prefetch<EPI, NRM == NRM_FOLDED>(p, 0, an)
                                 : epi_prefetch<EPI, NRM == NRM_FOLDED>(p, own ? om : 0, own ? on : 0);
+  // every load above is issued here, in this order: the scheduler may not move any of
+  // them below the waits for the rows
+  __builtin_amdgcn_sched_barrier(0);
   // 3. activation rows into LDS
   stage_finish<XPT, PRO>(p, xs, rr, ar, s_aw);
   __syncthreads();
@@ -524,6 +528,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
 #define MM_NW 8                       // waves per workgroup
 #define MM_JB 4                       // K blocks per wave and pass held in registers
 #define MM_KC (MM_NW * MM_JB * 32)    // K columns per pass
+static_assert(64 * MM_JB * 4 <= MM_KC, "a lane's staging slots stay inside a row's MM_KC columns");
 #define MM_LDX (MM_KC + 4)            // LDS row stride: 16 rows read at one column fall in distinct banks
 
 // Bytes of one packed 16 x 32 block.
@@ -614,25 +619,35 @@ __device__ __forceinline__ f32x4 f4_zero() { return (f32x4){0.f, 0.f, 0.f, 0.f};
 // LDS floats of k_mm with R activation rows.
 __host__ __device__ constexpr int mm_lds_floats(int R) { return R * MM_LDX; }
 
-// NRM: the rows are normalized (LayerNorm or RMSNorm by p.norm; S == 1, one pass).
+// NRM: how a pre-norm (LayerNorm or RMSNorm by p.norm; S == 1, one pass) is applied,
+// as in k_gemv: NRM_EXPLICIT normalizes the staged rows with the loaded gain and shift;
+// NRM_FOLDED (fp32) stages the rows shifted by their first element, d = x - x_0, keeps
+// each row's r = 1 / sqrt(var + eps) and a = mean(d) in LDS and applies
+// r (acc - a s_n) + bias_n in the epilogue, with the folded weights, row sums and bias.
 // MP: the K range of a split may exceed one pass (no norm): rows and weights are then
 // staged per pass and tile. Without MP the weight loads are unconditional, so the
 // compiler's wait counts stay exact and nothing waits for the next tile's weights.
-template <int WT, int MT, int EPI, bool NRM, bool MP>
+//
+// Staging costs VALU time (two waves per SIMD hide little), so only NRM_EXPLICIT masks
+// element by element. Elsewhere the slots past a row's range hold a copy of its last
+// chunk, which only ever meets zero weight columns (the packed copy is zero past K), and
+// rows >= M hold copies of row M - 1, whose outputs are never stored.
+template <int WT, int MT, int EPI, int NRM, bool MP>
 __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
-  static_assert(!(NRM && MP), "the norm needs whole rows in one pass");
-  constexpr int R = MT * 16;          // activation rows of the tile (rows >= M are zero)
+  static_assert(!(NRM != NRM_NONE && MP), "the norm needs whole rows in one pass");
+  constexpr int R = MT * 16;          // activation rows of the tile (rows >= M discarded)
   constexpr int RPW = R / MM_NW;      // rows staged per wave
   constexpr int RS = 17;              // padded row stride of a partial tile in LDS
   constexpr bool PAIR = EpiTraits<EPI>::pair;
   static_assert(2 * MM_NW * R * RS <= mm_lds_floats(R), "partial tiles fit over the staging area");
   __shared__ __align__(16) float xs[mm_lds_floats(R)];   // staged rows [R][MM_LDX], later s_red[2]
+  __shared__ float s_rs[R], s_mu[R];   // NRM_FOLDED: each row's r and a
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c = lane & 15;
   const int M = p.M, N = p.N, K = p.K;
   const int S = gridDim.y, s = blockIdx.y, G = gridDim.x;
   const int nb = (K + 31) >> 5;
-  const int b0 = (int)((long long)s * nb / S), b1 = (int)((long long)(s + 1) * nb / S);
+  const int b0 = s * nb / S, b1 = (s + 1) * nb / S;   // 32-bit: S <= 256, nb <= 2^16
   const int ntiles = (N + GD_TILE_N - 1) / GD_TILE_N;
   // this thread's output in the epilogue (threads >= R * 16 own none)
   const int om = tid >> 4, oc = tid & 15;
@@ -648,27 +663,36 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     const int ka = cb * 32;
     const int kq = (min(ce * 32, K) - ka) >> 2;   // float4 chunks of real columns per row
     const int pc = ((ce - cb) * 8 + 63) >> 6;     // chunks per lane (padded range)
-    // lanes past the range read a clamped chunk and keep zeros
+    // Every lane loads every slot (past the range a clamped chunk of the same row):
+    // a load under a condition would be compiled as a branch of its own, waiting for
+    // everything issued before it. NRM_EXPLICIT zeroes the slots past the range (by a
+    // product: a select would let the compiler move the load into a branch again).
+    (void)pc;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int m = min(wave + MM_NW * i, M - 1);
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
         const int ch = lane + 64 * j;
-        const f32x4 t = j < pc ? *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + ka + 4 * min(ch, kq - 1))
-                               : f4_zero();
-        v[i][j] = ch < kq ? t : f4_zero();
+        const f32x4 t = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + ka + 4 * min(ch, kq - 1));
+        if constexpr (NRM == NRM_EXPLICIT) {
+          const float keep = ch < kq ? 1.f : 0.f;
+          v[i][j] = (f32x4){t.x * keep, t.y * keep, t.z * keep, t.w * keep};
+        } else {
+          v[i][j] = t;
+        }
       }
     }
-    if constexpr (NRM) {
+    if constexpr (NRM == NRM_EXPLICIT) {
       const float* bsrc = p.norm == NORM_LN ? p.nb : p.ng;   // RMSNorm: shift 0 (bsel below)
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
         const int ch = lane + 64 * j, cc = 4 * min(ch, kq - 1);
-        const f32x4 tg = j < pc ? *reinterpret_cast<const f32x4*>(p.ng + cc) : f4_zero();
-        const f32x4 tb = j < pc ? *reinterpret_cast<const f32x4*>(bsrc + cc) : f4_zero();
-        g[j] = ch < kq ? tg : f4_zero();
-        bb[j] = ch < kq ? tb : f4_zero();
+        const float keep = ch < kq ? 1.f : 0.f;
+        const f32x4 tg = *reinterpret_cast<const f32x4*>(p.ng + cc);
+        const f32x4 tb = *reinterpret_cast<const f32x4*>(bsrc + cc);
+        g[j] = (f32x4){tg.x * keep, tg.y * keep, tg.z * keep, tg.w * keep};
+        bb[j] = (f32x4){tb.x * keep, tb.y * keep, tb.z * keep, tb.w * keep};
       }
     }
   };
@@ -676,7 +700,33 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     const int kq = (min(ce * 32, K) - cb * 32) >> 2;
     const int kqp = (ce - cb) * 8;
     const int pc = (kqp + 63) >> 6;
-    if constexpr (NRM) {
+    if constexpr (NRM == NRM_FOLDED) {
+      // shift each row by its first element (lane 0, slot 0) and form its moments; the
+      // shifted row is what the MFMAs see
+      const bool ln = p.norm == NORM_LN;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const float shf = ln ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[i][0].x))) : 0.f;
+        float st[2] = {0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < MM_JB; ++j) {
+          f32x4& d = v[i][j];
+          d.x -= shf; d.y -= shf; d.z -= shf; d.w -= shf;
+          const float keep = (j < pc && lane + 64 * j < kq) ? 1.f : 0.f;
+          st[0] = fmaf(keep, (d.x + d.y) + (d.z + d.w), st[0]);
+          st[1] = fmaf(keep, fmaf(d.x, d.x, d.y * d.y) + fmaf(d.z, d.z, d.w * d.w), st[1]);
+        }
+        wave_sum_n<2>(st);
+        const float invK = 1.0f / (float)K;
+        const float a = ln ? st[0] * invK : 0.f;
+        const float var = fmaxf(st[1] * invK - a * a, 0.f);
+        if (lane == 0) {
+          s_rs[wave + MM_NW * i] = rsqrtf(var + p.eps);
+          s_mu[wave + MM_NW * i] = a;
+        }
+      }
+    }
+    if constexpr (NRM == NRM_EXPLICIT) {
       // two-pass moments of each whole row (S == 1: the range is the row)
       const bool ln = p.norm == NORM_LN;
 #pragma unroll
@@ -705,16 +755,19 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
         }
       }
     }
-    // rows >= M and chunks past K are stored as zeros
+    // Slots of the range's padded 32-column blocks are stored, the rest skipped by a
+    // wave-uniform test (the loads cannot sink into it: a scheduling barrier separates
+    // them). Slots past the range are never read as operands.
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int m = wave + MM_NW * i;
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
         const int ch = lane + 64 * j;
-        if (j < pc && ch < kqp) *reinterpret_cast<f32x4*>(xs + m * MM_LDX + 4 * ch) = (m < M && ch < kq) ? v[i][j] : f4_zero();
+        if (j < pc) *reinterpret_cast<f32x4*>(xs + m * MM_LDX + 4 * ch) = v[i][j];
       }
     }
+    (void)kqp;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < MM_JB; ++j) {
@@ -739,11 +792,18 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     }
   };
 
+  // every kernel argument the launch reads, loaded at once (left to itself the compiler
+  // loads each just before its first use, inside the branch that uses it)
+  asm volatile("" ::"s"(p.x), "s"(p.ldx), "s"(p.ng), "s"(p.nb), "s"(p.norm), "s"(p.eps), "s"(p.wtl), "s"(p.bias),
+               "s"(p.resid), "s"(p.ldr), "s"(p.y), "s"(p.ldy));
   W8<WT> wa[MM_JB], wb[MM_JB];   // this tile's weights and the next tile's
   int t = blockIdx.x;
   if constexpr (!MP) {
     stage_issue(b0, b1);
     load_w(wa, t, b0, b1, true);   // the first tile's weights stream while the rows are staged
+    // keep every load above issued here: the scheduler would otherwise move the weight
+    // loads below the waits for the rows, adding a memory round trip
+    __builtin_amdgcn_sched_barrier(0);
     stage_finish(b0, b1);
   }
 
@@ -755,8 +815,9 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     // epilogue operands of this thread's output(s) of the tile
     const int n = t * GD_TILE_N + oc;
     const bool own = orow && (PAIR ? n + 1 < N : n < N);
-    const EpiOps eo = epi_prefetch<EPI>(p, own ? om : 0, own ? n : 0);
+    const EpiOps eo = epi_prefetch<EPI, NRM == NRM_FOLDED>(p, own ? om : 0, own ? n : 0);
     if constexpr (!MP) load_w(wn, t + G, b0, b1, t + G < ntiles);
+    __builtin_amdgcn_sched_barrier(0);   // the loads above go out before this tile's MFMAs
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f4_zero();
@@ -779,7 +840,7 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
         }
       }
     }
-    settle(eo.b0); settle(eo.b1); settle(eo.r0); settle(eo.c); settle(eo.s);
+    settle(eo.b0); settle(eo.b1); settle(eo.r0); settle(eo.c); settle(eo.s); settle(eo.f0);
     settle(__int_as_float((int)eo.kvoff)); settle(__int_as_float((int)(eo.kvoff >> 32)));
     float* red = xs + (it & 1) * (MM_NW * R * RS);
 #pragma unroll
@@ -795,6 +856,10 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
       float v = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < MM_NW; ++w2) v += red[(w2 * R + om) * RS + oc];
+      if (NRM == NRM_FOLDED) {
+        v = s_rs[om] * (v - s_mu[om] * eo.f0);
+        if (EPI == EPI_ARGMAX) v += eo.b0;   // the folded bias (other epilogues add it)
+      }
       if (EPI == EPI_ARGMAX) {
         if (own) {
           if (p.logits) p.logits[(size_t)om * p.ldl + n] = v;

@@ -115,6 +115,9 @@ static int gemv_rows_per_wave(int epi, int N) {
 }
 
 static const size_t kGemvLdsMax = 64 * 1024;
+// Widest reduction (K) of a linear layer: keeps the matrix-core kernel's split bounds
+// (split index x 32-column blocks) in 32-bit arithmetic.
+static const int kMaxK = 1 << 20;
 static const int kMmTargetWgs = 256;   // one matrix-core workgroup per CU
 
 // splittable: linear epilogue whose output is the residual, updated in place (the
@@ -211,28 +214,42 @@ static hipError_t launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream
   }
 }
 
+// A pre-norm whose folded form is given (fp32 weights, prm.wfl) runs as NRM_FOLDED on
+// the folded tile-major weights, bias and row sums.
 template <int WT, int MT>
-static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm0, hipStream_t st) {
   const dim3 g(lp.grid, lp.splits), b(64 * MM_NW);
-  const bool nrm = prm.norm != NORM_NONE;
+  const bool nrm = prm0.norm != NORM_NONE;
+  const bool fold = WT == 0 && nrm && prm0.wfl;
+  LinParams prm = prm0;
+  if (fold) {
+    prm.wtl = prm0.wfl;
+    prm.bias = prm0.bf;
+  }
 #define GD_MM(EPI, NRM, MP) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, MP>), g, b, 0, st, prm)
+#define GD_MM_N(EPI)                                   \
+  do {                                                 \
+    if (fold) GD_MM(EPI, NRM_FOLDED, false);           \
+    else GD_MM(EPI, NRM_EXPLICIT, false);              \
+  } while (0)
   if (lp.passes > 1) {   // K range wider than one pass: plain or GELU epilogue, no norm
     if (nrm) return hipErrorNotSupported;
-    if (prm.epi == EPI_PLAIN) GD_MM(EPI_PLAIN, false, true);
-    else if (prm.epi == EPI_GELU) GD_MM(EPI_GELU, false, true);
+    if (prm.epi == EPI_PLAIN) GD_MM(EPI_PLAIN, NRM_NONE, true);
+    else if (prm.epi == EPI_GELU) GD_MM(EPI_GELU, NRM_NONE, true);
     else return hipErrorNotSupported;
     return hipSuccess;
   }
   switch (prm.epi) {
-    case EPI_PLAIN: if (nrm) GD_MM(EPI_PLAIN, true, false); else GD_MM(EPI_PLAIN, false, false); break;
-    case EPI_GELU: if (nrm) GD_MM(EPI_GELU, true, false); else GD_MM(EPI_GELU, false, false); break;
+    case EPI_PLAIN: if (nrm) GD_MM_N(EPI_PLAIN); else GD_MM(EPI_PLAIN, NRM_NONE, false); break;
+    case EPI_GELU: if (nrm) GD_MM_N(EPI_GELU); else GD_MM(EPI_GELU, NRM_NONE, false); break;
     // the remaining epilogues always follow a pre-norm
-    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_SWIGLU, true, false); break;
-    case EPI_ARGMAX: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_ARGMAX, true, false); break;
-    case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_QKV, true, false); break;
-    case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_MM(EPI_QKV_ROPE, true, false); break;
+    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_SWIGLU); break;
+    case EPI_ARGMAX: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_ARGMAX); break;
+    case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_QKV); break;
+    case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_QKV_ROPE); break;
     default: return hipErrorNotSupported;
   }
+#undef GD_MM_N
 #undef GD_MM
   return hipSuccess;
 }
@@ -290,6 +307,7 @@ struct LayerOff {
   size_t tqkv, to, tfc, tproj;   // tile-major copies of the matrices (matrix-core kernel)
   // pre-norm folded into QKV and MLP-up (fp32): weights, bias, row sums (0: none)
   size_t fqkv, fqkv_b, fqkv_s, ffc, ffc_b, ffc_s;
+  size_t tfqkv, tffc;   // their tile-major copies
 };
 
 struct GraphKey {
@@ -340,6 +358,7 @@ struct gd_model {
   // weight offsets (bytes)
   size_t o_wte = 0, o_wpe = 0, o_nfg = 0, o_nfb = 0, o_head = 0, o_thead = 0;
   size_t o_fhead = 0, o_fhead_b = 0, o_fhead_s = 0, o_fold = 0;   // folded final norm + head
+  size_t o_tfhead = 0, o_fold_end = 0;   // tile-major folded head; end of the row-major folded part
   bool folded = false;   // the folded copies exist (fp32 weights)
   std::vector<LayerOff> L;
 
@@ -391,6 +410,7 @@ static gd_status check_cfg(const gd_config* c) {
     return set_err(GD_ERR_INVALID, "bad model sizes");
   if (c->head_dim != 16 && c->head_dim != 64) return set_err(GD_ERR_INVALID, "head_dim must be 16 or 64");
   if (c->d_model % 8 || c->d_ff % 8) return set_err(GD_ERR_INVALID, "d_model and d_ff must be multiples of 8");
+  if (c->d_model > kMaxK || c->d_ff > kMaxK) return set_err(GD_ERR_INVALID, "d_model and d_ff must be at most %d", kMaxK);
   if (c->arch == GD_ARCH_GPT2 && (c->n_kv_head != c->n_head || c->n_head * c->head_dim != c->d_model))
     return set_err(GD_ERR_INVALID, "GPT-2 arch needs n_kv_head == n_head and n_head*head_dim == d_model");
   if (c->n_head % c->n_kv_head) return set_err(GD_ERR_INVALID, "n_head must be a multiple of n_kv_head");
@@ -509,6 +529,15 @@ static void layout(gd_model* m) {
     m->o_fhead = take(V * d * 4);
     m->o_fhead_b = take(V * 4);
     m->o_fhead_s = take(V * 4);
+  }
+  m->o_fold_end = off;   // the host fills [o_fold, o_fold_end); k_pack_tiles the rest
+  if (m->folded) {
+    for (int l = 0; l < c.n_layer; ++l) {
+      LayerOff& t = m->L[l];
+      t.tfqkv = take(mm_packed_bytes(0, m->qkvdim, (int)d));
+      t.tffc = take(mm_packed_bytes(0, m->fcN, (int)d));
+    }
+    m->o_tfhead = take(mm_packed_bytes(0, (int)V, (int)d));
   }
   m->w_bytes = off;
 
@@ -798,7 +827,7 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
   if (m->folded) {
     // W'_nk = g_k W_nk (one fp32 product), s_n = sum_k W'_nk, bias'_n = bias_n +
     // sum_k b_k W_nk, from the row-major matrices as stored (sums in double)
-    fbuf.assign(m->w_bytes - m->o_fold, 0);
+    fbuf.assign(m->o_fold_end - m->o_fold, 0);
     auto rf = [&](size_t off) { return reinterpret_cast<const float*>(buf.data() + off); };
     auto wf = [&](size_t off) { return reinterpret_cast<float*>(fbuf.data() + (off - m->o_fold)); };
     auto fold = [&](size_t w, int N, size_t g, size_t b, size_t bias, size_t fw, size_t fb, size_t fs) {
@@ -842,6 +871,14 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     HIP_TRY(m, pack(t.wproj, t.tproj, (int)d, (int)ff));
   }
   HIP_TRY(m, pack(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, m->o_thead, (int)V, (int)d));
+  if (m->folded) {
+    for (int l = 0; l < c.n_layer; ++l) {
+      const LayerOff& t = m->L[l];
+      HIP_TRY(m, pack(t.fqkv, t.tfqkv, m->qkvdim, (int)d));
+      HIP_TRY(m, pack(t.ffc, t.tffc, m->fcN, (int)d));
+    }
+    HIP_TRY(m, pack(m->o_fhead, m->o_tfhead, (int)V, (int)d));
+  }
   HIP_TRY(m, hipStreamSynchronize(m->stream));
   m->loaded = true;
   return GD_OK;
@@ -1022,7 +1059,9 @@ static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool n
   if (lp.var == 0)
     snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %d>", w, lp.nc, lp.rw, epi, pro,
              !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT);
-  else snprintf(buf, n, "k_mm<%d, %d, %d, %s, %s>", w, lp.mt, epi, norm ? "true" : "false", lp.passes > 1 ? "true" : "false");
+  else
+    snprintf(buf, n, "k_mm<%d, %d, %d, %d, %s>", w, lp.mt, epi,
+             !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT, lp.passes > 1 ? "true" : "false");
   return buf;
 }
 
@@ -1121,7 +1160,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
-  const bool fold = m->folded && m->use_fold;   // used by the GEMV path only
+  const bool fold = m->folded && m->use_fold;   // pre-norms folded into QKV, MLP up and the head
 
   double kv_pos = 0;  // attended positions summed over rows (profiling only)
   for (int t : m->prof_T) kv_pos += t;
@@ -1145,7 +1184,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
       p.w = m->w + t.wqkv; p.wtl = m->w + t.tqkv; p.N = m->qkvdim; p.K = d;
-      if (fold) { p.wf = m->w + t.fqkv; p.bf = m->wf(t.fqkv_b); p.fs = m->wf(t.fqkv_s); }
+      if (fold) { p.wf = m->w + t.fqkv; p.wfl = m->w + t.tfqkv; p.bf = m->wf(t.fqkv_b); p.fs = m->wf(t.fqkv_s); }
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
       p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
       p.y = q; p.ldy = m->qdim;
@@ -1220,7 +1259,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n2g); p.nb = t.n2b ? m->wf(t.n2b) : nullptr;
       p.w = m->w + t.wfc; p.wtl = m->w + t.tfc; p.N = m->fcN; p.K = d;
-      if (fold) { p.wf = m->w + t.ffc; p.bf = m->wf(t.ffc_b); p.fs = m->wf(t.ffc_s); }
+      if (fold) { p.wf = m->w + t.ffc; p.wfl = m->w + t.tffc; p.bf = m->wf(t.ffc_b); p.fs = m->wf(t.ffc_s); }
       p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
       p.bias = t.bfc ? m->wf(t.bfc) : zero;
       p.resid = zero; p.ldr = 0;
@@ -1246,7 +1285,9 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.x = x + (size_t)head_row * d; p.ldx = d;
     p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
     p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
-    if (fold) { p.wf = m->w + m->o_fhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s); }
+    if (fold) {
+      p.wf = m->w + m->o_fhead; p.wfl = m->w + m->o_tfhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s);
+    }
     p.epi = EPI_ARGMAX;
     p.M = head_rows;
     p.row_kvoff = rp.row_kvoff + head_row;
@@ -1501,7 +1542,8 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
 // ---------------------------------------------------------------- op level
 
 static gd_status linear_check(int M, int N, int K, int variant) {
-  if (M < 1 || M > GD_MAX_ROWS || N < 1 || K < 8 || K % 8) return set_err(GD_ERR_INVALID, "bad shape M=%d N=%d K=%d", M, N, K);
+  if (M < 1 || M > GD_MAX_ROWS || N < 1 || K < 8 || K % 8 || K > kMaxK)
+    return set_err(GD_ERR_INVALID, "bad shape M=%d N=%d K=%d", M, N, K);
   if (variant < 0 || variant > 2) return set_err(GD_ERR_INVALID, "bad variant %d", variant);
   return GD_OK;
 }
