@@ -663,23 +663,27 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     const int ka = cb * 32;
     const int kq = (min(ce * 32, K) - ka) >> 2;   // float4 chunks of real columns per row
     const int pc = ((ce - cb) * 8 + 63) >> 6;     // chunks per lane (padded range)
-    // Every lane loads every slot (past the range a clamped chunk of the same row):
-    // a load under a condition would be compiled as a branch of its own, waiting for
-    // everything issued before it. NRM_EXPLICIT zeroes the slots past the range (by a
-    // product: a select would let the compiler move the load into a branch again).
-    (void)pc;
+    // Without a norm only the slots of the range's padded blocks are loaded (j < pc, a
+    // wave-uniform test: the load pipeline of a CU is the bottleneck there); with a
+    // norm every slot is, which keeps the statistics free of branches. Lanes past the
+    // range read a clamped chunk of the same row. No load is under a per-lane
+    // condition: such a load would be compiled as a branch of its own, waiting for
+    // everything issued before it. NRM_EXPLICIT zeroes the lanes past the range (by a
+    // product: a select would let the compiler sink the load again).
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int m = min(wave + MM_NW * i, M - 1);
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
-        const int ch = lane + 64 * j;
-        const f32x4 t = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + ka + 4 * min(ch, kq - 1));
-        if constexpr (NRM == NRM_EXPLICIT) {
-          const float keep = ch < kq ? 1.f : 0.f;
-          v[i][j] = (f32x4){t.x * keep, t.y * keep, t.z * keep, t.w * keep};
-        } else {
-          v[i][j] = t;
+        if (NRM != NRM_NONE || j < pc) {
+          const int ch = lane + 64 * j;
+          const f32x4 t = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + ka + 4 * min(ch, kq - 1));
+          if constexpr (NRM == NRM_EXPLICIT) {
+            const float keep = ch < kq ? 1.f : 0.f;
+            v[i][j] = (f32x4){t.x * keep, t.y * keep, t.z * keep, t.w * keep};
+          } else {
+            v[i][j] = t;
+          }
         }
       }
     }
@@ -696,35 +700,52 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
       }
     }
   };
+  // NRM_FOLDED: each staged row's r = 1 / sqrt(var + eps) and a = mean of the shifted
+  // row, into LDS (read by the epilogue after the partial-tile barrier). Lanes past the
+  // range are masked by selects (no branches).
+  auto fold_stats = [&](int pc, int kq) {
+    (void)pc;
+    const bool ln = p.norm == NORM_LN;
+    const float invK = 1.0f / (float)K;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      float st[2] = {0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < MM_JB; ++j) {
+        const f32x4 d = v[i][j];
+        const bool in = lane + 64 * j < kq;
+        const float cs = (d.x + d.y) + (d.z + d.w);
+        const float cq = fmaf(d.x, d.x, d.y * d.y) + fmaf(d.z, d.z, d.w * d.w);
+        st[0] += in ? cs : 0.f;
+        st[1] += in ? cq : 0.f;
+      }
+      wave_sum_n<2>(st);
+      const float a = ln ? st[0] * invK : 0.f;
+      const float var = fmaxf(st[1] * invK - a * a, 0.f);
+      if (lane == 0) {
+        s_rs[wave + MM_NW * i] = rsqrtf(var + p.eps);
+        s_mu[wave + MM_NW * i] = a;
+      }
+    }
+  };
   auto stage_finish = [&](int cb, int ce) {
     const int kq = (min(ce * 32, K) - cb * 32) >> 2;
     const int kqp = (ce - cb) * 8;
     const int pc = (kqp + 63) >> 6;
     if constexpr (NRM == NRM_FOLDED) {
-      // shift each row by its first element (lane 0, slot 0) and form its moments; the
-      // shifted row is what the MFMAs see
-      const bool ln = p.norm == NORM_LN;
+      // shift each row by its first element (lane 0, slot 0): the shifted row is what the
+      // MFMAs see; then its moments
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
-        const float shf = ln ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[i][0].x))) : 0.f;
-        float st[2] = {0.f, 0.f};
+        const float shf =
+            p.norm == NORM_LN ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[i][0].x))) : 0.f;
 #pragma unroll
         for (int j = 0; j < MM_JB; ++j) {
           f32x4& d = v[i][j];
           d.x -= shf; d.y -= shf; d.z -= shf; d.w -= shf;
-          const float keep = (j < pc && lane + 64 * j < kq) ? 1.f : 0.f;
-          st[0] = fmaf(keep, (d.x + d.y) + (d.z + d.w), st[0]);
-          st[1] = fmaf(keep, fmaf(d.x, d.x, d.y * d.y) + fmaf(d.z, d.z, d.w * d.w), st[1]);
-        }
-        wave_sum_n<2>(st);
-        const float invK = 1.0f / (float)K;
-        const float a = ln ? st[0] * invK : 0.f;
-        const float var = fmaxf(st[1] * invK - a * a, 0.f);
-        if (lane == 0) {
-          s_rs[wave + MM_NW * i] = rsqrtf(var + p.eps);
-          s_mu[wave + MM_NW * i] = a;
         }
       }
+      fold_stats(pc, kq);
     }
     if constexpr (NRM == NRM_EXPLICIT) {
       // two-pass moments of each whole row (S == 1: the range is the row)
@@ -733,7 +754,7 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
       for (int i = 0; i < RPW; ++i) {
         float s1 = 0.f;
 #pragma unroll
-        for (int j = 0; j < MM_JB; ++j) s1 += (v[i][j].x + v[i][j].y) + (v[i][j].z + v[i][j].w);
+        for (int j = 0; j < MM_JB; ++j) s1 += (v[i][j].x + v[i][j].y) + (v[i][j].z + v[i][j].w);   // zeros past K
         const float mu = ln ? wave_sum(s1) / (float)K : 0.f;
         float s2 = 0.f;
 #pragma unroll
