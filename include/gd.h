@@ -163,6 +163,12 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                            * gd_load_weights, and applies the row statistics in its
                            * epilogue; 0: the norm's gain and shift are applied to the
                            * row first */
+#define GD_OPT_FUSE_MLP 8 /* 1: with folded pre-norms (GD_OPT_FOLD_NORM, fp32), the
+                          * GPT-2 124M or tiny shape, up to 4 rows and attention fused
+                          * with the output projection, the MLP block runs as one launch
+                          * whose workgroups each add a hidden slice's share of the
+                          * down-projection with atomics; 0 (default): two launches,
+                          * which measure faster on this GPU */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

@@ -23,10 +23,10 @@ LLAMA_HD64 = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 320, 1e-5
 
 
 def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, pool=None, max_seqs=None,
-                     persistent=False, fold=True):
+                     persistent=False, fold=True, mlp=False):
     ref_tok, ref_lg = oracle_generate(w, W, prompts)
     m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph, persistent=persistent,
-                 fold=fold)
+                 fold=fold, mlp=mlp)
     tok, lg = gpu_generate(m, prompts, w.n_generate, tables=tables)
     assert m.device_errors() == 0
     rep = compare_generation(tok, lg, ref_tok, ref_lg, tol)
@@ -88,15 +88,54 @@ def test_context_crosses_fused_limit():
     _run_and_compare(w, W, prompts, 1e-3)
 
 
-@pytest.mark.parametrize("mode", ["single_launch", "chain", "chain_norm_applied"])
+@pytest.mark.parametrize("mode", ["single_launch", "chain", "chain_one_launch_mlp", "chain_norm_applied"])
 def test_gpt2_124m_batch1(mode):
-    """GPT-2 124M shape, batch 1, 8 prompt ids, 128 generated tokens (fp32)."""
+    """GPT-2 124M shape, batch 1, 8 prompt ids, 128 generated tokens (fp32). "chain" runs
+    the MLP block as two GEMVs, "chain_one_launch_mlp" as one launch (k_mlp)."""
     w = synth.WORKLOADS["gpt2_b1"]
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
     rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, persistent=mode == "single_launch",
-                                 fold=mode != "chain_norm_applied")
+                                 fold=mode != "chain_norm_applied", mlp=mode == "chain_one_launch_mlp")
     print("gpt2_b1", mode, rep)
+
+
+@pytest.mark.parametrize("mlp", [True, False], ids=["mlp_one_launch", "mlp_two_launches"])
+def test_tiny_gpt2_mlp_modes_across_batch_sizes(mlp):
+    """Random norm parameters and biases; three sequences decoded in batches of 1, 3 and
+    then 2 (slots interleaved), so steps with and without the one-launch MLP block (its
+    accumulators) follow each other on the same model."""
+    import torch
+    w = dataclasses.replace(synth.WORKLOADS["tiny"], batch=3, prompt_len=(3, 20), n_generate=12)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 104)
+    prompts = synth.make_prompts(w)
+    ref_tok, ref_lg = oracle_generate(w, W, prompts)
+    m = gd_model(w, W, mlp=mlp)
+    dev = device()
+    V = w.shape.vocab
+    tok = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    out = torch.zeros((w.batch, w.n_generate), dtype=torch.int32, device=dev)
+    lg = torch.empty((w.batch, w.n_generate, V), dtype=torch.float32, device=dev)
+    for b, p in enumerate(prompts):
+        m.reset_seq(b)
+        m.prefill(b, p, tok[b:b + 1], lg[b, 0])
+        out[b, 0] = tok[b]
+    step_lg = torch.empty((w.batch, V), dtype=torch.float32, device=dev)
+    for i in range(1, w.n_generate):
+        groups = [[0], [1], [2]] if i % 3 == 0 else ([[0, 1, 2]] if i % 3 == 1 else [[2, 0], [1]])
+        for g in groups:
+            t_in = torch.stack([tok[b] for b in g])
+            t_out = torch.zeros(len(g), dtype=torch.int32, device=dev)
+            m.decode_step(g, t_in, t_out, step_lg[:len(g)])
+            for k, b in enumerate(g):
+                tok[b] = t_out[k]
+                out[b, i] = t_out[k]
+                lg[b, i] = step_lg[k]
+    torch.cuda.synchronize()
+    assert m.device_errors() == 0
+    rep = compare_generation(out.cpu().numpy(), lg.cpu().numpy(), ref_tok, ref_lg, 1e-3)
+    assert not rep["near_ties"], rep
+    m.close()
 
 
 @pytest.mark.parametrize("fold", [True, False], ids=["folded", "applied"])

@@ -24,6 +24,7 @@
 #include "attention.h"
 #include "misc.h"
 #include "persistent.h"
+#include "mlp.h"
 
 // ------------------------------------------------------------------ errors
 
@@ -183,6 +184,17 @@ static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipSt
     GD_GEMV(1, EPI_PLAIN, PRO_ATTN, NRM_NONE);
     return hipSuccess;
   }
+  if (prm.pro == PRO_SUM2) {   // the residual plus the fused MLP's accumulator (fp32, folded norm)
+    if constexpr (WT == 0) {
+      if (!fold) return hipErrorNotSupported;
+      if (prm.epi == EPI_QKV) GD_GEMV(1, EPI_QKV, PRO_SUM2, NRM_FOLDED);
+      else if (prm.epi == EPI_ARGMAX && lp.rw == 4) GD_GEMV(4, EPI_ARGMAX, PRO_SUM2, NRM_FOLDED);
+      else if (prm.epi == EPI_ARGMAX) GD_GEMV(1, EPI_ARGMAX, PRO_SUM2, NRM_FOLDED);
+      else return hipErrorNotSupported;
+      return hipSuccess;
+    }
+    return hipErrorNotSupported;
+  }
   switch (prm.epi) {
     case EPI_PLAIN: if (nrm) GD_GEMV_N(1, EPI_PLAIN); else GD_GEMV(1, EPI_PLAIN, PRO_COPY, NRM_NONE); break;
     case EPI_GELU: if (nrm) GD_GEMV_N(1, EPI_GELU); else GD_GEMV(1, EPI_GELU, PRO_COPY, NRM_NONE); break;
@@ -280,6 +292,7 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
     p.M = std::min(lp.rows, prm.M - r0);
     if (r0) {
       if (p.x) p.x += (size_t)r0 * p.ldx;
+      if (p.x2) p.x2 += (size_t)r0 * p.ldx;
       p.resid += (size_t)r0 * p.ldr;
       if (p.y) p.y += (size_t)r0 * p.ldy;
       if (p.logits) p.logits += (size_t)r0 * p.ldl;
@@ -308,6 +321,7 @@ struct LayerOff {
   // pre-norm folded into QKV and MLP-up (fp32): weights, bias, row sums (0: none)
   size_t fqkv, fqkv_b, fqkv_s, ffc, ffc_b, ffc_s;
   size_t tfqkv, tffc;   // their tile-major copies
+  size_t pproj;         // W_proj packed for k_mlp (0: none)
 };
 
 struct GraphKey {
@@ -334,6 +348,8 @@ struct gd_model {
   bool use_graph = true;
   bool fuse_attn_o = true;
   bool use_fold = true;  // GEMV pre-norms folded into the weights when available (GD_OPT_FOLD_NORM)
+  bool use_mlp = false;  // the MLP block of <= 4 rows in one launch (GD_OPT_FUSE_MLP; measured slower)
+  bool mlp_ok = false;   // k_mlp has an instance for this shape (and the weights are folded)
   bool use_pk = false;  // single-launch decode step for one sequence (GD_OPT_PERSISTENT; measured slower)
   long long pk_spin_us = 20000;   // bound of its waits (GD_OPT_PERSISTENT_SPIN_US)
   int dev = 0;
@@ -364,6 +380,7 @@ struct gd_model {
 
   // scratch offsets (bytes)
   size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart, o_zero;
+  size_t o_z[2];   // k_mlp accumulators (alternating layers)
   // single-launch decode step: exchange words, layer table, abort tag
   bool pk_ok = false;
   unsigned pk_tag = 0;
@@ -529,6 +546,10 @@ static void layout(gd_model* m) {
     m->o_fhead = take(V * d * 4);
     m->o_fhead_b = take(V * 4);
     m->o_fhead_s = take(V * 4);
+    // k_mlp instances: GPT-2 124M (768, 3072) and the tiny decoder (64, 256)
+    m->mlp_ok = c.arch == GD_ARCH_GPT2 && ((d == 768 && ff == 3072) || (d == 64 && ff == 256));
+    if (m->mlp_ok)
+      for (int l = 0; l < c.n_layer; ++l) m->L[l].pproj = take(d * ff * 4);
   }
   m->o_fold_end = off;   // the host fills [o_fold, o_fold_end); k_pack_tiles the rest
   if (m->folded) {
@@ -560,6 +581,8 @@ static void layout(gd_model* m) {
   m->o_amv = take(m->am_parts * R * 4);
   m->o_ami = take(m->am_parts * R * 4);
   m->o_apart = take(R * c.n_head * GD_ATT_NCH * (c.head_dim + 2) * 4);
+  m->o_z[0] = take(R * d * 4);
+  m->o_z[1] = take(R * d * 4);
   // zeros (cleared at bind, never written): the bias or residual of layers that have none
   m->o_zero = take((size_t)std::max({m->qkvdim, m->fcN, (int)d, (int)ff}) * 4);
   m->o_rseq = take(R * 4);
@@ -858,6 +881,21 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     }
     fold(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, (int)V, m->o_nfg, m->o_nfb, 0, m->o_fhead, m->o_fhead_b,
          m->o_fhead_s);
+    if (m->mlp_ok) {
+      // W_proj for k_mlp: float4 c of output nl of slice (js, ns) holds
+      // W_proj[ns NSL + nl][js J + 4c .. 4c + 3]
+      const size_t J = ff / 64, CJ = J / 4, NSL = d / MLP_NS;
+      for (int l = 0; l < c.n_layer; ++l) {
+        const float* Wp = rf(m->L[l].wproj);
+        float* P = wf(m->L[l].pproj);
+        for (size_t js = 0; js < 64; ++js)
+          for (size_t ns = 0; ns < MLP_NS; ++ns)
+            for (size_t cc = 0; cc < CJ; ++cc)
+              for (size_t nl = 0; nl < NSL; ++nl)
+                for (size_t q = 0; q < 4; ++q)
+                  P[((((js * MLP_NS + ns) * CJ + cc) * NSL + nl) << 2) + q] = Wp[(ns * NSL + nl) * ff + js * J + 4 * cc + q];
+      }
+    }
     HIP_TRY(m, hipMemcpyAsync(m->w + m->o_fold, fbuf.data(), fbuf.size(), hipMemcpyHostToDevice, m->stream));
   }
   auto pack = [&](size_t src, size_t dst, int N, int K) {
@@ -975,6 +1013,8 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->fuse_attn_o = v != 0;
   } else if (opt == GD_OPT_FOLD_NORM) {
     m->use_fold = v != 0;
+  } else if (opt == GD_OPT_FUSE_MLP) {
+    m->use_mlp = v != 0;
   } else if (opt == GD_OPT_PERSISTENT) {
     m->use_pk = v != 0;
   } else if (opt == GD_OPT_PERSISTENT_SPIN_US) {
@@ -1121,6 +1161,22 @@ static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, boo
   else GD_LAUNCH((k_attention<HD, G, PPG, false>), grid, dim3(GD_WG), 0, st, a);
 }
 
+// The MLP block of M <= 4 rows (k_mlp): reads the residual rows x, adds into z.
+static hipError_t launch_mlp(gd_model* m, hipStream_t st, int l, int M, const float* x, float* z) {
+  const gd_config& c = m->c;
+  const LayerOff& t = m->L[l];
+  MlpParams p;
+  p.x = x; p.ldx = c.d_model; p.M = M; p.K = c.d_model; p.eps = c.norm_eps;
+  p.wfc = m->wf(t.ffc); p.bfc = m->wf(t.ffc_b); p.sfc = m->wf(t.ffc_s);
+  p.wpk = m->wf(t.pproj); p.bproj = m->wf(t.bproj);
+  p.z = z; p.ldz = c.d_model;
+  p.J = c.d_ff / 64; p.JS = 64; p.NSL = c.d_model / MLP_NS;
+  const dim3 g(64 * MLP_NS), b(MLP_WG);
+  if (c.d_model == 768) GD_LAUNCH((k_mlp<3, 6, 12>), g, b, 0, st, p);
+  else GD_LAUNCH((k_mlp<1, 1, 1>), g, b, 0, st, p);
+  return hipGetLastError();
+}
+
 // Row set-up parameters over the row arrays starting at seq/pos/tok/kvoff.
 static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long long* rkv, float* rcs) {
   const gd_config& c = m->c;
@@ -1132,6 +1188,7 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
   r.wpe = c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr;
   r.vocab = c.vocab; r.n_pos = c.n_ctx; r.d = c.d_model; r.emb_bf16 = m->wt == GD_WEIGHT_BF16;
   r.x = m->sp<float>(m->o_x);
+  if (m->mlp_ok) { r.z0 = m->sp<float>(m->o_z[0]); r.z1 = m->sp<float>(m->o_z[1]); }
   r.row_seq = rseq; r.row_pos = rpos; r.row_tok = rtok; r.row_kvoff = rkv;
   r.rope = c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rope) : nullptr;
   r.row_cs = rcs;
@@ -1161,6 +1218,13 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
   const bool fold = m->folded && m->use_fold;   // pre-norms folded into QKV, MLP up and the head
+  // The MLP block in one launch (k_mlp) adds its output into accumulator z[l % 2]
+  // instead of the residual x, which its own workgroups read for the norm. Layer l + 1
+  // then reads x + z[l % 2] (QKV prologue), and its fused attention + output projection
+  // folds z[l % 2] into x and clears it for layer l + 2; the head reads x + z[L-1 % 2].
+  // The row set-up clears both accumulators.
+  const bool fmlp = m->mlp_ok && m->use_mlp && fold && fuse_ao && M <= GEMV_MAX_ROWS;
+  float* zacc[2] = {m->sp<float>(m->o_z[0]), m->sp<float>(m->o_z[1])};
 
   double kv_pos = 0;  // attended positions summed over rows (profiling only)
   for (int t : m->prof_T) kv_pos += t;
@@ -1183,6 +1247,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.pro = PRO_COPY;
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
+      if (fmlp && l > 0) { p.pro = PRO_SUM2; p.x2 = zacc[(l - 1) & 1]; }
       p.w = m->w + t.wqkv; p.wtl = m->w + t.tqkv; p.N = m->qkvdim; p.K = d;
       if (fold) { p.wf = m->w + t.fqkv; p.wfl = m->w + t.tfqkv; p.bf = m->wf(t.fqkv_b); p.fs = m->wf(t.fqkv_s); }
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
@@ -1210,6 +1275,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       AttnOParams po;
       po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
       po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
+      po.zf = fmlp && l > 0 ? zacc[(l - 1) & 1] : nullptr;
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attn_o<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attn_o", kn,
@@ -1252,6 +1318,13 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
       if ((e = run_linear(m, st, "linear.o", p)) != hipSuccess) return e;
     }
+    if (fmlp) {
+      // pre-norm + FC + GELU + down-projection + bias, added into z[l % 2]
+      ProfScope ps(m, st, "mlp", c.d_model == 768 ? "k_mlp<3, 6, 12>" : "k_mlp<1, 1, 1>",
+                   2.0 * d * ff * 4 + 2.0 * ff * 4 + d * 4.0 + 2.0 * M * d * 4);
+      if ((e = launch_mlp(m, st, l, M, x, zacc[l & 1])) != hipSuccess) return e;
+      continue;
+    }
     // pre-norm + MLP up: GPT-2 FC + bias + clamped tanh-GELU; Llama gate|up + SiLU gate
     {
       LinParams p = base;
@@ -1284,6 +1357,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.pro = PRO_COPY;
     p.x = x + (size_t)head_row * d; p.ldx = d;
     p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
+    if (fmlp) { p.pro = PRO_SUM2; p.x2 = zacc[(c.n_layer - 1) & 1] + (size_t)head_row * d; }
     p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
     if (fold) {
       p.wf = m->w + m->o_fhead; p.wfl = m->w + m->o_tfhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s);
