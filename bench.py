@@ -168,23 +168,41 @@ def kernel_table(stats, P):
 
 def gemm_table(stats, P, w):
     """Per linear role: 2 M N K flops per launch over the mean launch time, as a fraction of
-    the fp32 matrix peak (the MFMA these kernels issue: bf16 weights are widened to fp32)
-    and of the bf16 peak."""
+    the fp32 matrix peak (the MFMA these kernels issue: bf16 weights are widened to fp32),
+    of the bf16 peak, and of the attainable min(fp32 peak, intensity x 8 TB/s)."""
     s = w.shape
     qdim, kdim = s.n_head * s.head_dim, s.n_kv_head * s.head_dim
     fc_n = s.d_ff if s.arch == 0 else 2 * s.d_ff
     nk = {"linear.qkv": (qdim + 2 * kdim, s.d_model), "linear.o": (s.d_model, qdim), "linear.fc": (fc_n, s.d_model),
           "linear.down": (s.d_model, s.d_ff), "linear.head": (s.vocab, s.d_model)}
+    elt = 2 if w.init.bf16 else 4
     out = []
     for st in stats:
         if st["role"] not in nk or st["launches"] == 0:
             continue
         n, k = nk[st["role"]]
         avg_us = st["total_us"] / st["launches"]
-        tf = 2.0 * w.batch * n * k / (avg_us * 1e-6) / 1e12
-        out.append(dict(role=st["role"], kernel=st["kernel"], avg_us=round(avg_us, 3), tflops=round(tf, 2),
-                        frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4), frac_bf16_peak=round(tf / MFMA_BF16_TFLOPS, 5)))
+        flops = 2.0 * w.batch * n * k
+        tf = flops / (avg_us * 1e-6) / 1e12
+        # attainable: min(fp32 matrix peak, arithmetic intensity x 8 TB/s), with the weights
+        # and the activation rows in and out as the bytes
+        ai = flops / (n * k * elt + 4.0 * w.batch * (n + k))
+        attain = min(MFMA_FP32_TFLOPS, ai * HBM_PEAK_GBPS / 1e3)
+        out.append(dict(role=st["role"], kernel=st["kernel"], launches_per_step=round(st["launches"] / P, 2),
+                        avg_us=round(avg_us, 3), tflops=round(tf, 2),
+                        frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4), frac_bf16_peak=round(tf / MFMA_BF16_TFLOPS, 5),
+                        attainable_tflops=round(attain, 1), frac_attainable=round(tf / attain, 4)))
     return out
+
+
+def gemm_step(gemms, w):
+    """All linear layers of one step: their summed kernel time and the step's GEMM flops
+    (2 B x linear and head parameters) over it."""
+    us = sum(g["launches_per_step"] * g["avg_us"] for g in gemms)
+    flops = sum(g["launches_per_step"] * g["tflops"] * 1e12 * g["avg_us"] * 1e-6 for g in gemms)
+    tf = flops / (us * 1e-6) / 1e12 if us else 0.0
+    return dict(us_per_step=round(us, 1), gflop_per_step=round(flops / 1e9, 3), tflops=round(tf, 2),
+                frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4))
 
 
 def kernel_sources_sha256() -> str:
@@ -484,9 +502,10 @@ def main():
         gemms = gemm_table(r32["stats"], r32["P"], r32["w"])
         for g in gemms:
             log(f"  {g['role']:<12} {g['avg_us']:8.2f} us {g['tflops']:7.2f} TFLOP/s  "
-                f"{100 * g['frac_fp32_peak']:5.1f}% of fp32 MFMA peak")
+                f"{100 * g['frac_fp32_peak']:5.1f}% of fp32 MFMA peak, {100 * g['frac_attainable']:5.1f}% of attainable")
         out["batch32"] = dict(workload=r32["w"].name, dtype=r32["w"].weight_dtype, **summ32,
-                              roofline=roofline(rows32), gemm_mfma=gemms, kernels=rows32)
+                              roofline=roofline(rows32), gemm_mfma=gemms, gemm_step=gemm_step(gemms, r32["w"]),
+                              kernels=rows32)
     print(json.dumps(out), flush=True)
 
 

@@ -1188,7 +1188,7 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
   r.wpe = c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr;
   r.vocab = c.vocab; r.n_pos = c.n_ctx; r.d = c.d_model; r.emb_bf16 = m->wt == GD_WEIGHT_BF16;
   r.x = m->sp<float>(m->o_x);
-  if (m->mlp_ok) { r.z0 = m->sp<float>(m->o_z[0]); r.z1 = m->sp<float>(m->o_z[1]); }
+  if (m->mlp_ok && m->use_mlp) { r.z0 = m->sp<float>(m->o_z[0]); r.z1 = m->sp<float>(m->o_z[1]); }
   r.row_seq = rseq; r.row_pos = rpos; r.row_tok = rtok; r.row_kvoff = rkv;
   r.rope = c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rope) : nullptr;
   r.row_cs = rcs;
