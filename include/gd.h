@@ -169,6 +169,13 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                           * whose workgroups each add a hidden slice's share of the
                           * down-projection with atomics; 0 (default): two launches,
                           * which measure faster on this GPU */
+#define GD_OPT_ATTN_CHUNKS 9 /* context chunks per row of the split-context attention
+                             * (rows that do not take the fused attention + output
+                             * projection): 1 (one workgroup per row and KV head,
+                             * normalized output written directly) or 8 (partials merged
+                             * by the output projection or a merge launch); 0 (default):
+                             * 1 when rows x KV heads >= the CU count and the output
+                             * projection is a matrix-core launch, else 8 */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

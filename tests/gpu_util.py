@@ -16,7 +16,7 @@ def device():
 
 
 def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True, persistent=False,
-             fold=True, mlp=False):
+             fold=True, mlp=False, chunks=0):
     import transformer_gpt_decode_amd as gd
     s = workload.shape
     kw = dict(max_seqs=max_seqs or workload.batch, max_batch=max_batch or workload.batch)
@@ -29,6 +29,7 @@ def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, varia
     m.set_option(gd.OPT_PERSISTENT, 1 if persistent else 0)
     m.set_option(gd.OPT_FOLD_NORM, 1 if fold else 0)
     m.set_option(gd.OPT_FUSE_MLP, 1 if mlp else 0)
+    m.set_option(gd.OPT_ATTN_CHUNKS, chunks)
     return m
 
 

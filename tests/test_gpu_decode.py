@@ -23,10 +23,10 @@ LLAMA_HD64 = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 320, 1e-5
 
 
 def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, pool=None, max_seqs=None,
-                     persistent=False, fold=True, mlp=False):
+                     persistent=False, fold=True, mlp=False, chunks=0):
     ref_tok, ref_lg = oracle_generate(w, W, prompts)
     m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph, persistent=persistent,
-                 fold=fold, mlp=mlp)
+                 fold=fold, mlp=mlp, chunks=chunks)
     tok, lg = gpu_generate(m, prompts, w.n_generate, tables=tables)
     assert m.device_errors() == 0
     rep = compare_generation(tok, lg, ref_tok, ref_lg, tol)
@@ -86,6 +86,24 @@ def test_context_crosses_fused_limit():
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
     _run_and_compare(w, W, prompts, 1e-3)
+
+
+# head_dim 64 (64 positions per load round of the attention scan) at contexts of up to
+# 1024 positions, small enough for the oracle
+GPT2_HD64_LONG = synth.Shape(synth.ARCH_GPT2, 2, 128, 2, 2, 64, 256, 300, 1024)
+
+
+@pytest.mark.parametrize("chunks", [0, 1, 8], ids=["auto", "one_chunk", "eight_chunks"])
+@pytest.mark.parametrize("variant", [1, 2], ids=["gemv", "mfma"])
+def test_long_contexts_attention_chunks(variant, chunks):
+    """Ragged contexts of 1..~900 positions: the scan runs 1..15 load rounds of 64
+    positions, odd and even counts. With the matrix-core output projection and one
+    chunk per row the attention writes its normalized output itself; with eight chunks
+    the partials are merged (the gemv projection always merges eight)."""
+    w = synth.Workload("gpt2_hd64_long", GPT2_HD64_LONG, synth.Init(), 13, 5, (1, 880), 6)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    _run_and_compare(w, W, prompts, 1e-3, variant, chunks=chunks)
 
 
 @pytest.mark.parametrize("mode", ["single_launch", "chain", "chain_one_launch_mlp", "chain_norm_applied"])

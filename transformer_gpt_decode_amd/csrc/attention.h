@@ -10,15 +10,18 @@
 // (grouped-query attention).
 //
 // Decomposition (split context): one workgroup per (row, KV head, chunk). A row's
-// T = pos + 1 positions are cut into GD_ATT_NCH chunks of ceil(T / GD_ATT_NCH)
-// positions, so the number of partials per row is fixed and their consumer can load
-// all of them without first reading the row's position. Inside a chunk, groups of
-// HD/4 lanes take one position per step (float4 of K and V per lane, all loads of a
-// step issued before the arithmetic) with an online max-subtracted softmax; the
-// groups are merged in LDS into one partial (max, sum, weighted V) per query head.
-// Empty chunks (T < GD_ATT_NCH) write max = -inf, sum = 0. For a few rows at short
-// contexts, k_attn_o instead scans each row's whole context and applies the output
-// projection in the same launch (see there).
+// T = pos + 1 positions are cut into C <= GD_ATT_NCH chunks of ceil(T / C) positions
+// (C = the grid's x extent), so the number of partials per row is fixed and their
+// consumer can load all of them without first reading the row's position. Inside a
+// chunk, groups of HD/4 lanes take one position per step (float4 of K and V per lane,
+// all loads of a step issued before the arithmetic; with a contiguous cache the next
+// step's loads are issued before the current step's arithmetic) with an online
+// max-subtracted softmax; the groups are merged into one partial (max, sum, weighted V)
+// per query head. Empty chunks (T < C) write max = -inf, sum = 0. With one chunk per
+// row (enough rows and heads to fill the GPU) the kernel writes the normalized output
+// itself and no merge follows. For a few rows at short contexts, k_attn_o instead scans
+// each row's whole context and applies the output projection in the same launch (see
+// there).
 #pragma once
 #include "common.h"
 
@@ -33,6 +36,7 @@ struct AttnParams {
   int M;
   float scale;
   float* part;                        // [M][Hq][GD_ATT_NCH][HD + 2]: max, sum, o[HD]
+  float* out; int ldo;                // one chunk per row: the normalized output [M][ldo]
 };
 
 // Online softmax of the G query heads of KV head kh of `row` over positions [p0, p1):
@@ -42,9 +46,9 @@ struct AttnParams {
 // exchanges and the waves through LDS. On return (after a barrier) thread
 // tid < G * HD holds, for query head g = tid / HD and dimension d = tid % HD, the
 // range's max, sum and weighted V (max -inf and zeros for an empty range).
-template <int HD, int G, int PPG>
+template <int HD, int G, int PPG, int NT = GD_WG>
 struct AttnScanLds {
-  static constexpr int NW = GD_WG / 64;
+  static constexpr int NW = NT / 64;
   float m[NW][G], l[NW][G];
   __align__(16) float o[NW][G][HD];
 };
@@ -83,13 +87,13 @@ __device__ __forceinline__ float attn_rescale(float m, float mm) { return mm == 
 // Loads are unconditional (a position past the range is clamped to its last position,
 // an invalid cache block to block 0) and masked afterwards, so that the compiler keeps
 // them where they are issued instead of sinking them into branches.
-template <int HD, int G, int PPG, bool PAGED>
+template <int HD, int G, int PPG, bool PAGED, int NT = GD_WG>
 __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0, int p1, const f32x4 (&q)[G],
-                          AttnScanLds<HD, G, PPG>& sh, float& m_out, float& l_out, float& o_out) {
+                          AttnScanLds<HD, G, PPG, NT>& sh, float& m_out, float& l_out, float& o_out) {
   constexpr int LG = HD / 4;            // lanes per position group
-  constexpr int NG = GD_WG / LG;        // position groups per workgroup
+  constexpr int NG = NT / LG;           // position groups per workgroup
   constexpr int STEP = NG * PPG;        // positions per step
-  constexpr int NW = GD_WG / 64;
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int grp = tid / LG, gl = tid % LG;
   const int pos = rm.pos;
@@ -110,9 +114,9 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
 #pragma unroll
   for (int g = 0; g < G; ++g) { mx[g] = -INFINITY; l[g] = 0.f; o[g] = (f32x4){0.f, 0.f, 0.f, 0.f}; }
 
-  f32x4 kv[PPG], vv[PPG];
-  bool ok[PPG];
-  auto issue = [&](int s0) {
+  f32x4 kv[PPG], vv[PPG], kv2[PPG], vv2[PPG];
+  bool ok[PPG], ok2[PPG];
+  auto issue = [&](int s0, f32x4 (&kv)[PPG], f32x4 (&vv)[PPG], bool (&ok)[PPG]) {
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
       const int pr = s0 + grp + NG * j;
@@ -134,7 +138,7 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
     }
     __builtin_amdgcn_sched_barrier(0);   // all of this step's loads go out before any arithmetic
   };
-  auto consume = [&]() {
+  auto consume = [&](const f32x4 (&kv)[PPG], const f32x4 (&vv)[PPG], const bool (&ok)[PPG]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s[PPG];
@@ -168,9 +172,39 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
       mx[g] = nm;
     }
   };
-  for (int s0 = p0; s0 < p1; s0 += STEP) {
-    issue(s0);
-    consume();
+  if constexpr (PAGED) {
+    // the block-table read of a step feeds its own K/V addresses, so a step is waited
+    // for before the next one is issued
+    for (int s0 = p0; s0 < p1; s0 += STEP) {
+      issue(s0, kv, vv, ok);
+      consume(kv, vv, ok);
+    }
+  } else if (p0 < p1) {
+    // Two register sets: step i + 1 is in flight while step i is consumed (the wait
+    // before a consume covers only the older set: loads complete in issue order). Every
+    // path into the loop head has exactly the newer set in flight (an issue or exit
+    // between the halves would make the compiler wait for every load there); the last
+    // one or two steps are peeled off below the loop, so no load is issued past the range.
+    const int n = (p1 - p0 + STEP - 1) / STEP;
+    issue(p0, kv, vv, ok);
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+      issue(p0 + (i + 1) * STEP, kv2, vv2, ok2);
+      consume(kv, vv, ok);
+      issue(p0 + (i + 2) * STEP, kv, vv, ok);
+      consume(kv2, vv2, ok2);
+    }
+    if (i + 1 < n) {
+      issue(p0 + (i + 1) * STEP, kv2, vv2, ok2);
+      // passing the older set through empty asm makes this branch's arithmetic differ
+      // from the other's, which the compiler would otherwise hoist above the issue
+#pragma unroll
+      for (int j = 0; j < PPG; ++j) asm volatile("" : "+v"(kv[j]), "+v"(vv[j]));
+      consume(kv, vv, ok);
+      consume(kv2, vv2, ok2);
+    } else {
+      consume(kv, vv, ok);
+    }
   }
   // merge the groups of each wave (lanes gl + LG r) by exchanges between lanes
 #pragma unroll
@@ -220,23 +254,29 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
   }
 }
 
-template <int HD, int G, int PPG, bool PAGED>
-__global__ __launch_bounds__(GD_WG) void k_attention(AttnParams p) {
-  __shared__ AttnScanLds<HD, G, PPG> sh;
+// NT threads: 512 for one chunk per row, so that a long context scanned by one
+// workgroup keeps twice the positions in flight.
+template <int HD, int G, int PPG, bool PAGED, int NT>
+__global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
+  __shared__ AttnScanLds<HD, G, PPG, NT> sh;
   const int c = blockIdx.x, kh = blockIdx.y, row = blockIdx.z;
   const AttnRow rm = attn_row<PAGED>(p, row);
   f32x4 q[G];
   attn_load_q<HD, G>(p, row, kh, q);
-  const int T = rm.pos + 1;
-  const int L = (T + GD_ATT_NCH - 1) / GD_ATT_NCH;
+  const int T = rm.pos + 1, C = gridDim.x;
+  const int L = (T + C - 1) / C;
   const int p0 = min(T, c * L), p1 = min(T, p0 + L);
   float m, l, o;
-  attn_scan<HD, G, PPG, PAGED>(p, rm, kh, p0, p1, q, sh, m, l, o);
+  attn_scan<HD, G, PPG, PAGED, NT>(p, rm, kh, p0, p1, q, sh, m, l, o);
   if (threadIdx.x < G * HD) {
     const int g = threadIdx.x / HD, d = threadIdx.x % HD;
-    float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * GD_ATT_NCH + c) * (HD + 2);
-    pp[2 + d] = o;
-    if (d == 0) { pp[0] = m; pp[1] = l; }
+    if (C == 1) {   // the whole context: l > 0 (the row's own position is in it)
+      p.out[(size_t)row * p.ldo + (kh * G + g) * HD + d] = o / l;
+    } else {
+      float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * GD_ATT_NCH + c) * (HD + 2);
+      pp[2 + d] = o;
+      if (d == 0) { pp[0] = m; pp[1] = l; }
+    }
   }
 }
 

@@ -347,6 +347,7 @@ struct gd_model {
   int variant = 0;
   bool use_graph = true;
   bool fuse_attn_o = true;
+  int attn_chunks = 0;   // split-context chunks per row: 0 auto, 1 or GD_ATT_NCH (GD_OPT_ATTN_CHUNKS)
   bool use_fold = true;  // GEMV pre-norms folded into the weights when available (GD_OPT_FOLD_NORM)
   bool use_mlp = false;  // the MLP block of <= 4 rows in one launch (GD_OPT_FUSE_MLP; measured slower)
   bool mlp_ok = false;   // k_mlp has an instance for this shape (and the weights are folded)
@@ -1020,6 +1021,9 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
   } else if (opt == GD_OPT_PERSISTENT_SPIN_US) {
     if (v < 0) return set_err(GD_ERR_INVALID, "spin bound must be >= 0");
     m->pk_spin_us = v;
+  } else if (opt == GD_OPT_ATTN_CHUNKS) {
+    if (v != 0 && v != 1 && v != GD_ATT_NCH) return set_err(GD_ERR_INVALID, "attention chunks must be 0, 1 or %d", GD_ATT_NCH);
+    m->attn_chunks = v;
   } else if (opt == GD_OPT_PROFILE) {
     if (v < 0 || v > 2) return set_err(GD_ERR_INVALID, "profile must be 0, 1 or 2");
     m->profile = v != 0;
@@ -1158,9 +1162,11 @@ static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, boo
   static_assert(HD == 64 || HD == 16, "head_dim");
   // 64 positions per load round: at batch 32 the kernel runs 40 % faster than with 128
   // (fewer registers, more workgroups resident per CU); 32 and 16 measure slightly slower
+  // One chunk per row: 512 threads, twice the positions in flight for the longest rows.
   constexpr int PPG = HD == 64 ? 4 : 1;
-  if (paged) GD_LAUNCH((k_attention<HD, G, PPG, true>), grid, dim3(GD_WG), 0, st, a);
-  else GD_LAUNCH((k_attention<HD, G, PPG, false>), grid, dim3(GD_WG), 0, st, a);
+  if (grid.x == 1 && !paged) GD_LAUNCH((k_attention<HD, G, PPG, false, 2 * GD_WG>), grid, dim3(2 * GD_WG), 0, st, a);
+  else if (paged) GD_LAUNCH((k_attention<HD, G, PPG, true, GD_WG>), grid, dim3(GD_WG), 0, st, a);
+  else GD_LAUNCH((k_attention<HD, G, PPG, false, GD_WG>), grid, dim3(GD_WG), 0, st, a);
 }
 
 // The MLP block of M <= 4 rows (k_mlp): reads the residual rows x, adds into z.
@@ -1216,6 +1222,12 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const bool o_gemv = plan_linear(M, c.d_model, m->qdim, m->wt, m->variant, EPI_PLAIN, false).var == 0;
   // few rows at short contexts: attention fused with the output projection
   const bool fuse_ao = m->fuse_attn_o && o_gemv && max_T <= kFusedAttnOMaxT;
+  // Split-context chunks per row: one when the rows and KV heads alone give every CU a
+  // workgroup (the kernel then writes the normalized output and no merge launch
+  // follows); the gemv O-projection's prologue merges GD_ATT_NCH partials.
+  const int nch = o_gemv ? GD_ATT_NCH
+                  : m->attn_chunks ? m->attn_chunks
+                  : (M * c.n_kv_head >= m->n_cu ? 1 : GD_ATT_NCH);
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
@@ -1271,6 +1283,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     a.M = M;
     a.scale = 1.0f / std::sqrt((float)c.head_dim);
     a.part = apart;
+    a.out = attn; a.ldo = m->qdim;
     const bool paged = c.kv_block_size > 0;
     if (fuse_ao) {
       // attention + output projection + bias + residual (in place on x), one launch
@@ -1290,7 +1303,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
       // causal attention of every row against its sequence's cache (split-context partials)
-      dim3 grid(GD_ATT_NCH, c.n_kv_head, M);
+      dim3 grid(nch, c.n_kv_head, M);
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attention<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attention", kn, kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4);
@@ -1308,9 +1321,11 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
         p.pro = PRO_ATTN;
         p.apart = apart;
       } else {
-        ProfScope ps(m, st, "attn_merge", "k_attn_merge", (double)M * c.n_head * (c.head_dim + 2) * 4.0 * 2);
-        GD_LAUNCH(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, attn, m->qdim);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (nch > 1) {
+          ProfScope ps(m, st, "attn_merge", "k_attn_merge", (double)M * c.n_head * (c.head_dim + 2) * 4.0 * 2);
+          GD_LAUNCH(k_attn_merge, dim3(M), dim3(GD_WG), 0, st, apart, c.n_head, c.head_dim, attn, m->qdim);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         p.pro = PRO_COPY;
         p.x = attn; p.ldx = m->qdim;
       }
