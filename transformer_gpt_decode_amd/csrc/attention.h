@@ -380,6 +380,74 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   }
 }
 
+// Attention of one whole context per workgroup fused with the output projection, for
+// many rows (rows x KV heads fill the GPU): workgroup (KV head kh, row) scans the row's
+// context (as k_attention with one chunk), normalizes o, and adds o . W_o[n][kh HD ..]
+// for every output n (plus the bias from kh == 0) to the residual row with float
+// atomics: Hkv contributions per address. Against the split-context kernel followed by
+// a matrix-core projection launch it costs each workgroup its head's W_o columns
+// (N x HD, from L2 after the first workgroup of the head) and one extra round trip,
+// and saves the projection launch. One query head per KV head (G = 1); the projection
+// reads its weights in groups of HD/4 lanes per output (float4 or four bf16 each), NP
+// passes of NT / (HD/4) outputs, all issued at once after the scan; the sums go
+// through LDS so that every atomic is issued after the last wait.
+template <int HD, bool PAGED, int WT, int NT, int NP>
+__global__ __launch_bounds__(NT) void k_attn_proj(AttnParams p, AttnOParams po) {
+  constexpr int PPG = 4, LG = HD / 4, RPP = NT / LG;
+  static_assert(HD == 64, "head_dim 64");
+  static_assert(NP * RPP <= 2 * NT, "two outputs per thread at most");
+  __shared__ AttnScanLds<HD, 1, PPG, NT> sh;
+  __shared__ __align__(16) float s_o[HD];
+  __shared__ float s_acc[NP * RPP];
+  const int kh = blockIdx.y, row = blockIdx.z, tid = threadIdx.x;
+  const int grp = tid / LG, gl = tid % LG;
+  asm volatile("" ::"s"(p.q), "s"(p.kc), "s"(p.vc), "s"(p.row_pos), "s"(p.row_kvoff), "s"(p.row_seq), "s"(p.table),
+               "s"(po.w), "s"(po.bias), "s"(po.y), "s"(p.ldq), "s"(p.max_blocks), "s"(p.block_size), "s"(p.nblk),
+               "s"(p.Hkv), "s"(p.scale), "s"(po.ldy), "s"(po.N), "s"(po.K));
+  // the bias (added by kh == 0) of this thread's two outputs tid, tid + NT (N <= 2 NT)
+  float bq[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bq[j] = kh == 0 ? po.bias[min(tid + NT * j, po.N - 1)] : 0.f;
+  const AttnRow rm = attn_row<PAGED>(p, row);
+  f32x4 q[1];
+  attn_load_q<HD, 1>(p, row, kh, q);
+  float m, l, o;
+  attn_scan<HD, 1, PPG, PAGED, NT>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
+  if (tid < HD) s_o[tid] = o / l;   // l > 0: the row's own position is in its context
+  // this head's weight columns, every pass at once (clamped rows past N are never added)
+  f32x4 wv[NP];
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int n = min(ps * RPP + grp, po.N - 1);
+    const size_t off = (size_t)n * po.K + kh * HD + gl * 4;
+    if constexpr (WT == 0) {
+      wv[ps] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(po.w) + off);
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(po.w) + off);
+      wv[ps] = (f32x4){bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+    }
+  }
+  __syncthreads();
+  const f32x4 ov = *reinterpret_cast<const f32x4*>(&s_o[gl * 4]);
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    float a = wv[ps].x * ov.x;
+    a = fmaf(wv[ps].y, ov.y, a);
+    a = fmaf(wv[ps].z, ov.z, a);
+    a = fmaf(wv[ps].w, ov.w, a);
+    a = group_sum<LG>(a);
+    if (gl == 0) s_acc[ps * RPP + grp] = a;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = tid + NT * j;
+    if (n < po.N)
+      __hip_atomic_fetch_add(po.y + (size_t)row * po.ldy + n, s_acc[n] + bq[j], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Merge of the chunk partials of M rows x Hq heads into dst[m * ldd + h * hd + d]:
 // o = sum_c e^(max_c - max) o_c / sum_c e^(max_c - max) sum_c. Chunk 0 always holds at
 // least one position, so the maximum is finite; empty chunks (max -inf, sum 0, o 0)

@@ -1157,6 +1157,15 @@ static void launch_attn_o(hipStream_t st, const AttnParams& a, const AttnOParams
   }
 }
 
+// Outputs of k_attn_proj: NP passes of 32 (512 threads, 16 lanes per output).
+static const int kAttnProjPasses = 24;
+
+static void launch_attn_proj(hipStream_t st, const AttnParams& a, const AttnOParams& po, int wt, int M, int Hkv) {
+  const dim3 grid(1, Hkv, M), b(2 * GD_WG);
+  if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_proj<64, false, 0, 2 * GD_WG, kAttnProjPasses>), grid, b, 0, st, a, po);
+  else GD_LAUNCH((k_attn_proj<64, false, 1, 2 * GD_WG, kAttnProjPasses>), grid, b, 0, st, a, po);
+}
+
 template <int HD, int G>
 static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, bool paged) {
   static_assert(HD == 64 || HD == 16, "head_dim");
@@ -1228,6 +1237,10 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const int nch = o_gemv ? GD_ATT_NCH
                   : m->attn_chunks ? m->attn_chunks
                   : (M * c.n_kv_head >= m->n_cu ? 1 : GD_ATT_NCH);
+  // With one chunk per row (contiguous cache, head_dim 64, one query head per KV head,
+  // d_model <= 768) the attention workgroups also apply the output projection.
+  const bool fuse_ap = m->fuse_attn_o && !fuse_ao && nch == 1 && c.kv_block_size == 0 && c.head_dim == 64 &&
+                       c.n_head == c.n_kv_head && c.d_model <= kAttnProjPasses * 32;
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
@@ -1301,6 +1314,18 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       else if (G == 1) launch_attn_o<16, 1>(st, a, po, paged, m->wt, M, c.n_kv_head);
       else launch_attn_o<16, 3>(st, a, po, paged, m->wt, M, c.n_kv_head);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (fuse_ap) {
+      // attention + output projection + bias + residual (in place on x), one workgroup
+      // per (KV head, row)
+      AttnOParams po;
+      po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
+      po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
+      po.zf = nullptr;
+      ProfScope ps(m, st, "attn_proj", "k_attn_proj<64>",
+                   kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + M * m->qdim * 4.0 + (double)d * m->qdim * m->elt +
+                       (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
+      launch_attn_proj(st, a, po, m->wt, M, c.n_kv_head);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
       // causal attention of every row against its sequence's cache (split-context partials)
       dim3 grid(nch, c.n_kv_head, M);
@@ -1315,7 +1340,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     }
     // output projection + bias + residual (in place on x); the gemv kernel merges the
     // attention partials in its prologue, the mfma path merges them in a kernel first
-    if (!fuse_ao) {
+    if (!fuse_ao && !fuse_ap) {
       LinParams p = base;
       if (o_gemv) {
         p.pro = PRO_ATTN;
