@@ -218,25 +218,33 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) recorded in
-    profiles/hbm_traffic.json, or None when the kernel sources have changed since."""
+def load_traffic_record():
+    """profiles/hbm_traffic.json, or None when absent or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except OSError:
         return None
-    if rec.get("sources_sha256") != kernel_sources_sha256():
+    return rec if rec.get("sources_sha256") == kernel_sources_sha256() else None
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) of a kernel in a
+    workload, recorded in profiles/hbm_traffic.json, or None when not recorded or when
+    the kernel sources have changed since."""
+    rec = load_traffic_record()
+    if rec is None:
         return None
-    k = next((v for name, v in rec.get("kernels", {}).items() if name.startswith(kernel.rstrip(">"))), None)
+    ks = rec.get("workloads", {}).get(workload, {}).get("kernels", {})
+    k = next((v for name, v in ks.items() if name.startswith(kernel.rstrip(">"))), None)
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
-def roofline(rows):
+def roofline(rows, workload: str):
     top = rows[0]
     ach = top["bytes_per_launch"] / (top["avg_us"] * 1e-6) / 1e9
-    tr = measured_traffic(top["kernel"])
+    tr = measured_traffic(top["kernel"], workload)
     return {"bound": "hbm", "kernel": top["kernel"], "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": round(tr) if tr else None,
             "bytes_per_launch": round(top["bytes_per_launch"]), "avg_launch_us": top["avg_us"]}
@@ -284,34 +292,49 @@ def summary(res):
                       sync_ms_per_step=round(res["ms_sync"], 4), sync_value=round(w.batch / (res["ms_sync"] * 1e-3), 1))
 
 
+def _short_name(n: str) -> str:
+    n = n.replace("void ", "")
+    return n[:n.index("(")] if "(" in n else n
+
+
+def profiled_regions(rows, steps_per_pass=None):
+    """Row ranges [lo, hi) of the profiled passes in a rocprofv3 CSV of a bench.py run,
+    rows in dispatch order. Every profiled step is held by one k_gate and ends with one
+    k_argmax_finalize; the gates of a pass need not sit beside their steps (the helper
+    stream that holds them runs ahead of the host's enqueues), so a pass is taken as its
+    K gates in order and spans from its first gate to the K-th finalize after it.
+    steps_per_pass gives K for each pass; without it all gates form one pass."""
+    gates = [i for i, r in enumerate(rows) if _short_name(r["Kernel_Name"]) == "k_gate"]
+    fins = [i for i, r in enumerate(rows) if _short_name(r["Kernel_Name"]) == "k_argmax_finalize"]
+    counts = list(steps_per_pass) if steps_per_pass else [len(gates)]
+    regions, gi = [], 0
+    for k in counts:
+        if k <= 0 or gi + k > len(gates):
+            break
+        lo = gates[gi]
+        after = [i for i in fins if i > lo]
+        if len(after) < k:
+            break
+        regions.append((lo, after[k - 1] + 1, k))
+        gi += k
+    return regions
+
+
 def counter_means(csv_path: str, calib_mib: int):
-    """Per profiled pass of a rocprofv3 --pmc CSV of a bench.py run: {kernel: mean bytes
-    per dispatch}, the counter scaled by the calibration copy (see trace_summary)."""
+    """The profiled pass of a rocprofv3 --pmc CSV of a bench.py run with one workload:
+    {kernel: mean bytes per dispatch}, the counter scaled by the calibration copy (see
+    trace_summary)."""
     import csv
     import statistics
 
-    def short(n):
-        n = n.replace("void ", "")
-        return n[:n.index("(")] if "(" in n else n
-
-    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Dispatch_Id"]))
     cp = next(r for r in rows if "copyBuffer" in r["Kernel_Name"])
     factor = calib_mib * 1024.0 / float(cp["Counter_Value"])
-    gates = [i for i, r in enumerate(rows) if short(r["Kernel_Name"]) == "k_gate"]
-    passes, cur = [], []
-    for g in gates:
-        if cur and g - cur[-1] > 400:
-            passes.append(cur)
-            cur = []
-        cur.append(g)
-    if cur:
-        passes.append(cur)
     out = []
-    for pas in passes:
-        step = pas[1] - pas[0] if len(pas) > 1 else 0
+    for lo, hi, _ in profiled_regions(rows):
         d = {}
-        for r in rows[pas[0]:pas[-1] + step]:
-            k = short(r["Kernel_Name"])
+        for r in rows[lo:hi]:
+            k = _short_name(r["Kernel_Name"])
             if k == "k_gate" or "at::native" in k or "rocclr" in k:
                 continue
             d.setdefault(k, []).append(float(r["Counter_Value"]) * factor * 1024.0)
@@ -319,23 +342,24 @@ def counter_means(csv_path: str, calib_mib: int):
     return out, factor
 
 
-def traffic_json(fetch_csv: str, write_csv: str, calib_mib: int, commands):
-    """profiles/hbm_traffic.json from the FETCH_SIZE and WRITE_SIZE runs: HBM bytes per
-    dispatch of each kernel of the first profiled pass, with the hash of the kernel
-    sources they were measured on."""
+def traffic_json(fetch_csv: str, write_csv: str, calib_mib: int, commands, workload: str):
+    """Records in profiles/hbm_traffic.json, under the workload's name, the HBM bytes
+    per dispatch of each kernel of the first profiled pass of the FETCH_SIZE and
+    WRITE_SIZE runs (the bench's main workload), with the hash of the kernel sources they
+    were measured on; records of other workloads on the same sources are kept."""
     f, ff = counter_means(fetch_csv, calib_mib)
     w, wf = counter_means(write_csv, calib_mib)
-    rec = {"sources_sha256": kernel_sources_sha256(),
-           "workload": "gpt2_b1 (GPT-2 124M shape, batch 1, fp32 weights), profiled pass of bench.py --steps 32",
-           "commands": list(commands),
-           "calibration": {"copy_mib_each_way": calib_mib, "fetch_kib_factor": round(ff, 4),
-                           "write_kib_factor": round(wf, 4)},
-           "kernels": {k: {"fetch_bytes": round(f[0][k]), "write_bytes": round(w[0].get(k, 0.0))}
-                       for k in sorted(f[0])}}
+    rec = load_traffic_record() or {"sources_sha256": kernel_sources_sha256(), "workloads": {}}
+    rec.setdefault("workloads", {})[workload] = {
+        "pass": "the profiled pass of bench.py (see commands)",
+        "commands": list(commands),
+        "calibration": {"copy_mib_each_way": calib_mib, "fetch_kib_factor": round(ff, 4),
+                        "write_kib_factor": round(wf, 4)},
+        "kernels": {k: {"fetch_bytes": round(f[0][k]), "write_bytes": round(w[0].get(k, 0.0))} for k in sorted(f[0])}}
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
-    print(f"wrote {path}: {len(rec['kernels'])} kernels")
+    print(f"wrote {path}: {workload}, {len(rec['workloads'][workload]['kernels'])} kernels")
 
 
 def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
@@ -349,11 +373,9 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
     import csv
     import statistics
 
-    def short(n):
-        n = n.replace("void ", "")
-        return n[:n.index("(")] if "(" in n else n
-
-    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Start_Timestamp"]))
+    # dispatch order (under counter collection the start times of a held kernel and
+    # of the launches queued behind it do not follow it)
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Dispatch_Id"]))
     counter = rows[0].get("Counter_Name") if rows else None
     factor = None
     if counter and calib_mib:
@@ -361,34 +383,25 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
         factor = calib_mib * 1024.0 / float(cp["Counter_Value"])
         print(f"{counter}: the calibration copy ({calib_mib} MiB read, {calib_mib} MiB written) counts "
               f"{float(cp['Counter_Value']):.1f} KiB, so bytes = {counter} x {factor:.3f} KiB")
-    gates = [i for i, r in enumerate(rows) if short(r["Kernel_Name"]) == "k_gate"]
-    passes, cur = [], []   # a pass: consecutive gated steps (at most a few hundred dispatches apart)
-    for g in gates:
-        if cur and g - cur[-1] > 400:
-            passes.append(cur)
-            cur = []
-        cur.append(g)
-    if cur:
-        passes.append(cur)
-    bench_sets = []
+    bench_sets, steps = [], None
     if bench_json:
         with open(bench_json) as f:
             bench = json.loads(f.read().strip().splitlines()[-1])
         bench_sets.append({k["kernel"]: k for k in bench.get("kernels", [])})
+        steps = [bench["steps"]]
         if "batch32" in bench:
             bench_sets.append({k["kernel"]: k for k in bench["batch32"].get("kernels", [])})
-    for pi, pas in enumerate(passes):
-        step = pas[1] - pas[0] if len(pas) > 1 else 0
-        lo, hi = pas[0], pas[-1] + step
+            steps.append(bench["batch32"]["steps"])
+    for pi, (lo, hi, nsteps) in enumerate(profiled_regions(rows, steps)):
         d = {}
         for r in rows[lo:hi]:
-            k = short(r["Kernel_Name"])
+            k = _short_name(r["Kernel_Name"])
             if k == "k_gate" or "at::native" in k or "rocclr" in k:
                 continue
             v = float(r["Counter_Value"]) if counter else (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
             d.setdefault(k, []).append(v)
         bs = bench_sets[pi] if pi < len(bench_sets) else {}
-        print(f"\nProfiled pass {pi + 1}: {len(pas)} steps, dispatches {lo}..{hi}\n")
+        print(f"\nProfiled pass {pi + 1}: {nsteps} steps, dispatches {lo}..{hi}\n")
         if counter:
             print(f"| kernel | dispatches | mean {counter} KiB | MB per dispatch | bench.py algorithmic MB | ratio |")
             print("|---|---|---|---|---|---|")
@@ -448,9 +461,11 @@ def main():
     ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from the two --pmc CSVs (with --calib-mib) and exit")
     ap.add_argument("--traffic-cmd", action="append", default=[], help="with --traffic-json: a command to record")
+    ap.add_argument("--traffic-workload", default="gpt2_b1", help="with --traffic-json: the profiled workload")
     args = ap.parse_args()
     if args.traffic_json:
-        traffic_json(args.traffic_json[0], args.traffic_json[1], args.calib_mib, args.traffic_cmd)
+        traffic_json(args.traffic_json[0], args.traffic_json[1], args.calib_mib, args.traffic_cmd,
+                     args.traffic_workload)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json, args.calib_mib)
@@ -487,7 +502,7 @@ def main():
            "config": {"workload": res["w"].name, "batch": res["w"].batch, "prompt_len": res["w"].prompt_len[0],
                       "n_generate": res["w"].n_generate, "shape": "GPT-2 124M (12x768, 12 heads, ff 3072, "
                       "vocab 50257)", "weights": "f32"},
-           "roofline": roofline(rows), "step": summ, "kernels": rows}
+           "roofline": roofline(rows, res["w"].name), "step": summ, "kernels": rows}
     if args.cpu_seconds > 0:
         log("[bench] oracle CPU baseline ...")
         out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
@@ -504,7 +519,7 @@ def main():
             log(f"  {g['role']:<12} {g['avg_us']:8.2f} us {g['tflops']:7.2f} TFLOP/s  "
                 f"{100 * g['frac_fp32_peak']:5.1f}% of fp32 MFMA peak, {100 * g['frac_attainable']:5.1f}% of attainable")
         out["batch32"] = dict(workload=r32["w"].name, dtype=r32["w"].weight_dtype, **summ32,
-                              roofline=roofline(rows32), gemm_mfma=gemms, gemm_step=gemm_step(gemms, r32["w"]),
+                              roofline=roofline(rows32, r32["w"].name), gemm_mfma=gemms, gemm_step=gemm_step(gemms, r32["w"]),
                               kernels=rows32)
     print(json.dumps(out), flush=True)
 

@@ -308,9 +308,18 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   using RT = AttnORows<HD>;
   __shared__ AttnScanLds<HD, G, PPG> sh;
   __shared__ __align__(16) float s_o[G][HD];
-  const int kh = blockIdx.y, row = blockIdx.z;
+  // Workgroups are placed round-robin over the 8 XCDs in launch order, and the slices
+  // of one (KV head, row) read the same K/V: launch index L is renumbered so that
+  // consecutive slices share an XCD and its L2 (the K/V then come from HBM about once
+  // rather than once per XCD). L = 8 k + x with x < 8 becomes j = x per + k for the
+  // first 8 per indices (per = total / 8); the remainder keeps its index.
+  const int S = gridDim.x, total = S * gridDim.y * gridDim.z;
+  const int L = blockIdx.x + S * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int per = total >> 3;
+  const int j = L < 8 * per ? (L & 7) * per + (L >> 3) : L;
+  const int slice = j % S, kh = (j / S) % gridDim.y, row = j / (S * gridDim.y);
   const int tid = threadIdx.x, grp = tid / RT::LG, gl = tid % RT::LG;
-  const int n0 = blockIdx.x * RT::ROWS;
+  const int n0 = slice * RT::ROWS;
   // Every kernel argument the launch reads, loaded at once: left to itself the compiler
   // loads each just before its first use, a chain of scalar round trips ahead of the
   // metadata, query and K/V loads.
