@@ -653,7 +653,17 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c = lane & 15;
   const int M = p.M, N = p.N, K = p.K;
-  const int S = gridDim.y, s = blockIdx.y, G = gridDim.x;
+  // Workgroups are placed round-robin over the 8 XCDs in launch order; the G column
+  // tiles of one K split read the same slice of the activation rows, so the launch index
+  // is renumbered to put consecutive tiles of a split on one XCD (the slice then comes
+  // from HBM about once per split rather than once per XCD): L = 8 k + x (x < 8) becomes
+  // x per + k for the first 8 per indices, per = total / 8; the remainder keeps its index.
+  const int S = gridDim.y, G = gridDim.x;
+  const int wgid = [&] {
+    const int total = G * S, L = blockIdx.x + G * blockIdx.y, per = total >> 3;
+    return L < 8 * per ? (L & 7) * per + (L >> 3) : L;
+  }();
+  const int s = wgid / G, wg = wgid - s * G;
   const int nb = (K + 31) >> 5;
   const int b0 = s * nb / S, b1 = (s + 1) * nb / S;   // 32-bit: S <= 256, nb <= 2^16
   const int ntiles = (N + GD_TILE_N - 1) / GD_TILE_N;
@@ -826,7 +836,7 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   asm volatile("" ::"s"(p.x), "s"(p.ldx), "s"(p.ng), "s"(p.nb), "s"(p.norm), "s"(p.eps), "s"(p.wtl), "s"(p.bias),
                "s"(p.resid), "s"(p.ldr), "s"(p.y), "s"(p.ldy));
   W8<WT> wa[MM_JB], wb[MM_JB];   // this tile's weights and the next tile's
-  int t = blockIdx.x;
+  int t = wg;
   if constexpr (!MP) {
     stage_issue(b0, b1);
     load_w(wa, t, b0, b1, true);   // the first tile's weights stream while the rows are staged
@@ -928,8 +938,8 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     MM_AM_STEP(DPP_ROW_MIRROR)
 #undef MM_AM_STEP
     if (oc == 0 && om < M) {
-      p.am_val[(size_t)blockIdx.x * M + om] = bv;
-      p.am_idx[(size_t)blockIdx.x * M + om] = bi;
+      p.am_val[(size_t)wg * M + om] = bv;
+      p.am_idx[(size_t)wg * M + om] = bi;
     }
   }
 }
