@@ -130,7 +130,7 @@ def measure(wname: str, steps, warmup: int):
     gpu_tokens = np.stack(hist, 1)
     # profiled eager pass over one generation window: per-kernel time and bytes
     rewind(m, tok, first, plen)
-    m.set_option(gd.OPT_PROFILE, 2)
+    m.set_option(gd.OPT_PROFILE, PROFILE_MODE[0])
     m.profile_read(reset=True)
     P = min(K, n_decode)
     for _ in range(P):
@@ -306,6 +306,13 @@ def profiled_regions(rows, steps_per_pass=None):
     steps_per_pass gives K for each pass; without it all gates form one pass."""
     gates = [i for i, r in enumerate(rows) if _short_name(r["Kernel_Name"]) == "k_gate"]
     fins = [i for i, r in enumerate(rows) if _short_name(r["Kernel_Name"]) == "k_argmax_finalize"]
+    if not gates:
+        # ungated profiling (--profile-mode 1): one workload, whose profiled pass is the
+        # last thing the run does, its K steps end with the last K finalizes
+        k = steps_per_pass[0] if steps_per_pass else 0
+        if k <= 0 or len(fins) <= k:
+            return []
+        return [(fins[-k - 1] + 1, fins[-1] + 1, k)]
     counts = list(steps_per_pass) if steps_per_pass else [len(gates)]
     regions, gi = [], 0
     for k in counts:
@@ -320,10 +327,10 @@ def profiled_regions(rows, steps_per_pass=None):
     return regions
 
 
-def counter_means(csv_path: str, calib_mib: int):
-    """The profiled pass of a rocprofv3 --pmc CSV of a bench.py run with one workload:
-    {kernel: mean bytes per dispatch}, the counter scaled by the calibration copy (see
-    trace_summary)."""
+def counter_means(csv_path: str, calib_mib: int, steps=None):
+    """The profiled pass (of `steps` steps; required when the run was not gated) of a
+    rocprofv3 --pmc CSV of a bench.py run with one workload: {kernel: mean bytes per
+    dispatch}, the counter scaled by the calibration copy (see trace_summary)."""
     import csv
     import statistics
 
@@ -331,7 +338,7 @@ def counter_means(csv_path: str, calib_mib: int):
     cp = next(r for r in rows if "copyBuffer" in r["Kernel_Name"])
     factor = calib_mib * 1024.0 / float(cp["Counter_Value"])
     out = []
-    for lo, hi, _ in profiled_regions(rows):
+    for lo, hi, _ in profiled_regions(rows, [steps] if steps else None):
         d = {}
         for r in rows[lo:hi]:
             k = _short_name(r["Kernel_Name"])
@@ -342,13 +349,13 @@ def counter_means(csv_path: str, calib_mib: int):
     return out, factor
 
 
-def traffic_json(fetch_csv: str, write_csv: str, calib_mib: int, commands, workload: str):
+def traffic_json(fetch_csv: str, write_csv: str, calib_mib: int, commands, workload: str, steps=None):
     """Records in profiles/hbm_traffic.json, under the workload's name, the HBM bytes
     per dispatch of each kernel of the first profiled pass of the FETCH_SIZE and
     WRITE_SIZE runs (the bench's main workload), with the hash of the kernel sources they
     were measured on; records of other workloads on the same sources are kept."""
-    f, ff = counter_means(fetch_csv, calib_mib)
-    w, wf = counter_means(write_csv, calib_mib)
+    f, ff = counter_means(fetch_csv, calib_mib, steps)
+    w, wf = counter_means(write_csv, calib_mib, steps)
     rec = load_traffic_record() or {"sources_sha256": kernel_sources_sha256(), "workloads": {}}
     rec.setdefault("workloads", {})[workload] = {
         "pass": "the profiled pass of bench.py (see commands)",
@@ -422,6 +429,7 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
 
 
 COPY_GBPS = [None]   # measured device-to-device copy rate (read + write bytes / time)
+PROFILE_MODE = [2]   # GD_OPT_PROFILE of the per-kernel pass (--profile-mode)
 
 
 def copy_rate():
@@ -462,10 +470,18 @@ def main():
                     help="write profiles/hbm_traffic.json from the two --pmc CSVs (with --calib-mib) and exit")
     ap.add_argument("--traffic-cmd", action="append", default=[], help="with --traffic-json: a command to record")
     ap.add_argument("--traffic-workload", default="gpt2_b1", help="with --traffic-json: the profiled workload")
+    ap.add_argument("--profile-mode", type=int, choices=(1, 2), default=2,
+                    help="per-kernel timing pass: 2 holds each step behind a gate kernel on a helper stream so "
+                         "that its launches run back to back (timing); 1 launches as enqueued, with no "
+                         "cross-stream wait (for counter collection, which serializes dispatches)")
     args = ap.parse_args()
     if args.traffic_json:
+        steps = None
+        if args.bench_json:
+            with open(args.bench_json) as f:
+                steps = json.loads(f.read().strip().splitlines()[-1])["steps"]
         traffic_json(args.traffic_json[0], args.traffic_json[1], args.calib_mib, args.traffic_cmd,
-                     args.traffic_workload)
+                     args.traffic_workload, steps)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json, args.calib_mib)
@@ -487,6 +503,7 @@ def main():
         log(f"[bench] calibration copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
         del src, dst
 
+    PROFILE_MODE[0] = args.profile_mode
     COPY_GBPS[0] = copy_rate()
     log(f"[bench] device-to-device copy: {COPY_GBPS[0]:.0f} GB/s (read + write)")
     log(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps or 'one generation'}")
