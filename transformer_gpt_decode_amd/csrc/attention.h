@@ -87,7 +87,10 @@ __device__ __forceinline__ float attn_rescale(float m, float mm) { return mm == 
 // Loads are unconditional (a position past the range is clamped to its last position,
 // an invalid cache block to block 0) and masked afterwards, so that the compiler keeps
 // them where they are issued instead of sinking them into branches.
-template <int HD, int G, int PPG, bool PAGED, int NT = GD_WG>
+// STREAM: each K/V element is read by one workgroup of the launch, so the contiguous
+// loads carry the non-temporal hint (they then displace less of what other workgroups
+// share in L2: the output projection's weights, the query rows).
+template <int HD, int G, int PPG, bool PAGED, int NT = GD_WG, bool STREAM = false>
 __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0, int p1, const f32x4 (&q)[G],
                           AttnScanLds<HD, G, PPG, NT>& sh, float& m_out, float& l_out, float& o_out) {
   constexpr int LG = HD / 4;            // lanes per position group
@@ -132,8 +135,15 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
         kv[j] = *reinterpret_cast<const f32x4*>(p.kc + off);
         vv[j] = *reinterpret_cast<const f32x4*>(p.vc + off);
       } else {
-        kv[j] = *reinterpret_cast<const f32x4*>(kbase + (size_t)ps * HD);
-        vv[j] = *reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
+        const f32x4* kp = reinterpret_cast<const f32x4*>(kbase + (size_t)ps * HD);
+        const f32x4* vp = reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
+        if constexpr (STREAM) {
+          kv[j] = __builtin_nontemporal_load(kp);
+          vv[j] = __builtin_nontemporal_load(vp);
+        } else {
+          kv[j] = *kp;
+          vv[j] = *vp;
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // all of this step's loads go out before any arithmetic
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
   const int L = (T + C - 1) / C;
   const int p0 = min(T, c * L), p1 = min(T, p0 + L);
   float m, l, o;
-  attn_scan<HD, G, PPG, PAGED, NT>(p, rm, kh, p0, p1, q, sh, m, l, o);
+  attn_scan<HD, G, PPG, PAGED, NT, true>(p, rm, kh, p0, p1, q, sh, m, l, o);
   if (threadIdx.x < G * HD) {
     const int g = threadIdx.x / HD, d = threadIdx.x % HD;
     if (C == 1) {   // the whole context: l > 0 (the row's own position is in it)
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(NT) void k_attn_proj(AttnParams p, AttnOParams po) 
   f32x4 q[1];
   attn_load_q<HD, 1>(p, row, kh, q);
   float m, l, o;
-  attn_scan<HD, 1, PPG, PAGED, NT>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
+  attn_scan<HD, 1, PPG, PAGED, NT, true>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
   if (tid < HD) s_o[tid] = o / l;   // l > 0: the row's own position is in its context
   // this head's weight columns, every pass at once (clamped rows past N are never added)
   f32x4 wv[NP];
