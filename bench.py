@@ -93,6 +93,7 @@ def measure(wname: str, steps, warmup: int):
     import torch
     import transformer_gpt_decode_amd as gd
     w, W, prompts, m, tok, first, plen, ttft = setup(wname)
+    log(f"[bench] {wname}: prompts prefilled")
     n_decode = w.n_generate - 1
     K = steps if steps else n_decode
     seq_ids = list(range(w.batch))
@@ -100,6 +101,7 @@ def measure(wname: str, steps, warmup: int):
     run_steps(m, tok, first, plen, max(1, warmup), n_decode, seq_ids)
     rewind(m, tok, first, plen)
     torch.cuda.synchronize()
+    log(f"[bench] {wname}: warm-up done")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
@@ -110,6 +112,7 @@ def measure(wname: str, steps, warmup: int):
     gpu_ms = e0.elapsed_time(e1)
     ms_step = max(gpu_ms, wall * 1e3) / K
     assert m.device_errors() == 0
+    log(f"[bench] {wname}: timed run done ({K} steps)")
     # synchronous variant: the new tokens read back and the stream synchronized every step
     rewind(m, tok, first, plen)
     S = min(K, n_decode)
@@ -121,6 +124,7 @@ def measure(wname: str, steps, warmup: int):
         host.copy_(tok, non_blocking=True)
         torch.cuda.current_stream().synchronize()
     ms_sync = (time.perf_counter() - t0) * 1e3 / S
+    log(f"[bench] {wname}: synchronous run done")
     # greedy tokens of the first steps after the prompt (for the oracle cross-check)
     rewind(m, tok, first, plen)
     hist = [first.cpu().numpy().copy()]
@@ -136,6 +140,7 @@ def measure(wname: str, steps, warmup: int):
     for _ in range(P):
         m.decode_step(seq_ids, tok, tok)
     stats = m.profile_read(reset=True)
+    log(f"[bench] {wname}: profiled pass done ({P} steps)")
     m.set_option(gd.OPT_PROFILE, 0)
     m.close()
     torch.cuda.synchronize()
