@@ -94,6 +94,10 @@ def measure(wname: str, steps, warmup: int):
     import transformer_gpt_decode_amd as gd
     w, W, prompts, m, tok, first, plen, ttft = setup(wname)
     log(f"[bench] {wname}: prompts prefilled")
+    if PROFILE_MODE[0] == 1:
+        # counter runs: every step launched eagerly (under counter collection, runs stalled
+        # inside back-to-back graph replays)
+        m.set_option(gd.OPT_USE_GRAPH, 0)
     n_decode = w.n_generate - 1
     K = steps if steps else n_decode
     seq_ids = list(range(w.batch))
@@ -478,7 +482,8 @@ def main():
     ap.add_argument("--profile-mode", type=int, choices=(1, 2), default=2,
                     help="per-kernel timing pass: 2 holds each step behind a gate kernel on a helper stream so "
                          "that its launches run back to back (timing); 1 launches as enqueued, with no "
-                         "cross-stream wait (for counter collection, which serializes dispatches)")
+                         "cross-stream wait and no graphs in any pass (for counter collection, which "
+                         "serializes dispatches; its step times are not representative)")
     args = ap.parse_args()
     if args.traffic_json:
         steps = None
