@@ -497,8 +497,8 @@ def main():
         trace_summary(args.trace_summary, args.bench_json, args.calib_mib)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
-              "would shard); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the decode path has no multi-GPU code (decode would shard "
+              "by sequence, one weight copy per GPU); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

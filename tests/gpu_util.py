@@ -9,7 +9,7 @@ import synth
 
 def device():
     import torch
-    assert torch.cuda.is_available(), "GPU tests need an MI355X; run them with -m gpu on the GPU box"
+    assert torch.cuda.is_available(), "GPU tests need an MI355X (gfx950) device; select them with -m gpu"
     import transformer_gpt_decode_amd as gd
     gd.lib()   # fails loudly if the HIP library is missing
     return torch.device("cuda", 0)
