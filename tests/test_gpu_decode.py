@@ -203,6 +203,8 @@ def test_context_edges_and_errors():
     tok = torch.zeros(1, dtype=torch.int32, device=dev)
     logits = torch.empty((2, w.shape.vocab), dtype=torch.float32, device=dev)
     m.prefill(0, prompt, tok, logits[0])
+    torch.cuda.synchronize()
+    tok0 = int(tok.item())                            # the prefill's greedy token
     m.decode_step([0], tok, tok, logits[1])          # position n_ctx - 1
     torch.cuda.synchronize()
     om = oracle.Model(w.shape, W)
@@ -210,7 +212,7 @@ def test_context_edges_and_errors():
     ref = np.empty(w.shape.vocab, np.float32)
     for t in prompt:
         first = s.forward(int(t), ref)
-    assert int(first) == int(oracle.argmax(logits[0].cpu().numpy())) or True
+    assert tok0 == int(first)
     r0 = ref.copy()
     second = s.forward(first, ref)
     assert np.max(np.abs(logits[0].cpu().numpy() - r0)) <= 1e-3
@@ -236,4 +238,10 @@ def test_context_edges_and_errors():
     m.decode_step([0], bad, tok)
     assert m.device_errors() & 1
     assert m.device_errors() == 0
+    # option values outside the documented sets are refused on the host
+    for opt, bad in ((gd.OPT_ATTN_CHUNKS, 2), (gd.OPT_ATTN_CHUNKS, -1), (gd.OPT_ATTN_CHUNKS, 16),
+                     (gd.OPT_LINEAR_VARIANT, 3), (gd.OPT_PROFILE, 5), (99, 0)):
+        with pytest.raises(gd.GdError) as e:
+            m.set_option(opt, bad)
+        assert e.value.status == gd.GD_ERR_INVALID
     m.close()
