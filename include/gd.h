@@ -146,9 +146,13 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
  * capture decode steps in hipGraphs, 0 launch kernels directly. */
 #define GD_OPT_LINEAR_VARIANT 1
 #define GD_OPT_USE_GRAPH 2
-#define GD_OPT_FUSE_ATTN_O 4 /* 1 (default): up to 4 rows whose contexts all hold at most
-                              * 256 positions run attention fused with the output
-                              * projection; 0: always split-context attention */
+#define GD_OPT_FUSE_ATTN_O 4 /* 1 (default): attention runs fused with the output
+                              * projection (+ bias + residual) for up to 4 rows whose
+                              * contexts all hold at most 256 positions, and for the
+                              * one-chunk split-context case (GD_OPT_ATTN_CHUNKS) with a
+                              * contiguous cache, head_dim 64, one query head per KV head
+                              * and d_model <= 768; 0: attention and projection always run
+                              * as separate launches */
 #define GD_OPT_PERSISTENT 5 /* 1: a one-sequence decode step of the GPT-2 layout runs as
                              * one launch with one workgroup per CU (phases hand over
                              * through tagged words in device memory) for the GPT-2 124M
@@ -170,12 +174,14 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                           * down-projection with atomics; 0 (default): two launches,
                           * which measure faster on this GPU */
 #define GD_OPT_ATTN_CHUNKS 9 /* context chunks per row of the split-context attention
-                             * (rows that do not take the fused attention + output
-                             * projection): 1 (one workgroup per row and KV head,
-                             * normalized output written directly) or 8 (partials merged
-                             * by the output projection or a merge launch); 0 (default):
-                             * 1 when rows x KV heads >= the CU count and the output
-                             * projection is a matrix-core launch, else 8 */
+                             * (rows that do not take the short-context fused attention):
+                             * 1 (one workgroup per row and KV head over the whole context:
+                             * normalized output written directly, or the output
+                             * projection applied in the same launch, see
+                             * GD_OPT_FUSE_ATTN_O) or 8 (partials merged by the output
+                             * projection's prologue or a merge launch); 0 (default): 1
+                             * when rows x KV heads >= the CU count and the output
+                             * projection would be a matrix-core launch, else 8 */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper
