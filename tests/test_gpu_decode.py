@@ -78,6 +78,17 @@ def test_llama_hd64_gqa_paged(batch):
     _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool)
 
 
+def test_llama_hd64_gqa_paged_one_chunk():
+    """The one-chunk split-context attention (one workgroup per row and KV head writes the
+    normalized output) on a shuffled paged cache with 3 query heads per KV head, followed
+    by the matrix-core output projection."""
+    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 12, 6, (5, 200), 10, kv_block=16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    _run_and_compare(w, W, prompts, 2e-2, variant=2, tables=tab, pool=pool, chunks=1)
+
+
 def test_context_crosses_fused_limit():
     """A batch-1 generation whose context grows past 256 positions: the decode graph
     switches from the fused attention + output projection to split-context attention."""
