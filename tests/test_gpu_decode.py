@@ -89,6 +89,16 @@ def test_llama_hd64_gqa_paged_one_chunk():
     _run_and_compare(w, W, prompts, 2e-2, variant=2, tables=tab, pool=pool, chunks=1)
 
 
+@pytest.mark.parametrize("chunks", [1, 8], ids=["one_chunk", "eight_chunks"])
+def test_llama_hd64_gqa_contiguous(chunks):
+    """3 query heads per KV head on a contiguous cache (no block table), split-context
+    attention with one or eight chunks per row and the matrix-core output projection."""
+    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 14, 6, (5, 200), 10)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    _run_and_compare(w, W, prompts, 2e-2, variant=2, chunks=chunks)
+
+
 def test_context_crosses_fused_limit():
     """A batch-1 generation whose context grows past 256 positions: the decode graph
     switches from the fused attention + output projection to split-context attention."""
