@@ -89,14 +89,18 @@ def test_llama_hd64_gqa_paged_one_chunk():
     _run_and_compare(w, W, prompts, 2e-2, variant=2, tables=tab, pool=pool, chunks=1)
 
 
-@pytest.mark.parametrize("chunks", [1, 8], ids=["one_chunk", "eight_chunks"])
-def test_llama_hd64_gqa_contiguous(chunks):
-    """3 query heads per KV head on a contiguous cache (no block table), split-context
+@pytest.mark.parametrize("mode", ["fused_attn_o", "one_chunk", "eight_chunks"])
+def test_llama_hd64_gqa_contiguous(mode):
+    """3 query heads per KV head on a contiguous cache (no block table): 2 rows at short
+    contexts take the fused attention + output projection; 6 rows run split-context
     attention with one or eight chunks per row and the matrix-core output projection."""
-    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 14, 6, (5, 200), 10)
+    fused = mode == "fused_attn_o"
+    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 14, 2 if fused else 6,
+                       (5, 120 if fused else 200), 10)
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
-    _run_and_compare(w, W, prompts, 2e-2, variant=2, chunks=chunks)
+    _run_and_compare(w, W, prompts, 2e-2, variant=0 if fused else 2, chunks=8 if mode == "eight_chunks" else
+                     (1 if mode == "one_chunk" else 0))
 
 
 def test_context_crosses_fused_limit():
