@@ -181,7 +181,9 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                              * GD_OPT_FUSE_ATTN_O) or 8 (partials merged by the output
                              * projection's prologue or a merge launch); 0 (default): 1
                              * when rows x KV heads >= the CU count and the output
-                             * projection would be a matrix-core launch, else 8 */
+                             * projection would be a matrix-core launch, else 8. Launches
+                             * of at most 4 rows whose output projection is the VALU GEMV
+                             * always use 8 (its prologue merges them) */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper
