@@ -76,20 +76,37 @@ typedef struct gd_model gd_model;
 
 /* Checks the config and the device (must be gfx950) and binds `hip_stream`
  * (a hipStream_t; NULL = the null stream). Allocates no device memory except a few
- * bytes of HIP objects. */
+ * bytes of HIP objects.
+ * Defines: the model shapes this engine runs -- GPT-2 with LayerNorm, learned positions
+ * and plain multi-head attention ("bare-metal-llm", "Picking the model") and the
+ * Llama-style layer with RMSNorm, RoPE, grouped K/V heads and a gated MLP ("rvllm Metal
+ * backend", "What the kernels do").
+ * Errors: GD_ERR_INVALID for a bad config (nothing created); GD_ERR_NO_DEVICE when no
+ * gfx950 device is present -- a backend that is asked for and missing is an error, never
+ * a silent fallback ("batch_forge" README, the generate binary's usage notes). *out
+ * is NULL on any error. */
 gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model** out);
 
 /* Bytes of device memory the caller must provide: packed weights, KV cache and
- * scratch (activations, split-K partials, counters, row metadata, block tables). */
+ * scratch (activations, attention partials, argmax partials, row metadata, block
+ * tables). The weights stay resident in the first buffer for the model's life
+ * ("batch_forge" README, roadmap: resident weights instead of a re-upload per call).
+ * Errors: GD_ERR_INVALID if m is NULL; NULL size pointers are skipped. */
 gd_status gd_memory_requirements(const gd_model* m, size_t* weights_bytes, size_t* kv_bytes,
                                  size_t* scratch_bytes);
 
 /* Binds caller-owned device buffers of at least the required sizes (256-byte aligned).
- * Clears the scratch counters, the sequence lengths and (contiguous cache) installs
- * identity block tables. */
+ * Clears the scratch, the sequence lengths and (contiguous cache) installs identity
+ * block tables; waits for that. The caller keeps ownership and must keep the buffers
+ * alive while the model uses them ("rvllm Metal backend", "Memory is shared": buffers
+ * are the caller's, read only after the GPU is done with them).
+ * Errors: GD_ERR_INVALID (NULL or misaligned pointer), GD_ERR_HIP. Unloads any weights
+ * loaded before (GD_ERR_STATE until gd_load_weights runs again). */
 gd_status gd_bind_memory(gd_model* m, void* weights_dev, void* kv_dev, void* scratch_dev);
 
-/* Uploads the weights from one host float32 buffer in the canonical order:
+/* Uploads the weights from one host float32 buffer in the canonical order (resident
+ * weights: "batch_forge" README, roadmap; the tied output head reads wte transposed:
+ * "bare-metal-llm", "What got built"):
  *   GPT-2: wte[V][d], wpe[n_ctx][d], then per layer ln1_g[d], ln1_b[d],
  *          w_qkv[3d][d], b_qkv[3d], w_o[d][d], b_o[d], ln2_g[d], ln2_b[d],
  *          w_fc[ff][d], b_fc[ff], w_proj[d][ff], b_proj[d]; then lnf_g[d], lnf_b[d].
@@ -98,81 +115,87 @@ gd_status gd_bind_memory(gd_model* m, void* weights_dev, void* kv_dev, void* scr
  *          w_down[d][ff]; then rmsf[d], w_head[V][d].
  * Matrices are [out][in] (y = x . W^T + b). With GD_WEIGHT_BF16 the matrices are
  * rounded to bfloat16 (nearest, ties to even). Repacks into the device layout and
- * waits for the copy. n_floats must equal the canonical count. */
+ * waits for the copy. n_floats must equal the canonical count (else GD_ERR_INVALID);
+ * GD_ERR_STATE before gd_bind_memory. The host buffer is only read during the call. */
 gd_status gd_load_weights(gd_model* m, const float* host_weights, size_t n_floats);
 
 /* Paged cache only: installs the block table of sequence slot `seq` (n entries,
  * each in [0, kv_num_blocks)). Position p of the sequence lives in block
- * blocks[p / kv_block_size], slot p mod kv_block_size. Capacity = n * block size. */
+ * blocks[p / kv_block_size], slot p mod kv_block_size ("rvllm Metal backend", "What the
+ * kernels do": the paged cache addressed by integer division and modulo). Capacity =
+ * min(n * block size, n_ctx). Errors: GD_ERR_STATE for a contiguous cache,
+ * GD_ERR_INVALID for an entry out of range. The host array is copied before return. */
 gd_status gd_set_block_table(gd_model* m, int32_t seq, const int32_t* blocks_host, int32_t n);
 
-/* Empties sequence slot `seq` (length 0). */
+/* Empties sequence slot `seq` (length 0): the KV cache of a sequence holds only what
+ * it has run ("bare-metal-llm", "What got built": a real KV cache, each step computes
+ * only the new token). GD_ERR_INVALID for a slot out of range. */
 gd_status gd_reset_seq(gd_model* m, int32_t seq);
 
 /* Shortens sequence slot `seq` to `len` positions (0 <= len <= current length); the
  * positions past it are dropped and later overwritten (rewind, e.g. to replay a
- * generation from the end of its prompt). */
+ * generation from the end of its prompt, as the same KV cache of "bare-metal-llm",
+ * "What got built"). GD_ERR_INVALID outside 0..length. */
 gd_status gd_truncate_seq(gd_model* m, int32_t seq, int32_t len);
 
-/* Host-side length of a sequence slot (positions filled, as enqueued). */
+/* Host-side length of a sequence slot (positions filled, as enqueued; the device copy
+ * is advanced by the decode step itself). GD_ERR_INVALID for a bad slot. */
 gd_status gd_seq_len(const gd_model* m, int32_t seq, int32_t* len);
 
 /* Runs tokens_host[0..n) of one sequence at positions len .. len+n-1 (causal within
  * the prompt), appends their K/V, and writes the greedy argmax of the last position
  * to *next_token_dev (device int32) and, if logits_dev is not NULL, its vocab logits
- * (device float[vocab]). n >= 1; every id in [0, vocab). */
+ * (device float[vocab]) ("rvllm Metal backend", "Numbers": the prompt is processed
+ * before the first token; "bare-metal-llm", "What got built": the KV cache filled for
+ * later steps). n >= 1 and every id in [0, vocab), else GD_ERR_INVALID; GD_ERR_CTX_FULL
+ * past the slot's capacity. Enqueued, not waited for. */
 gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens_host, int32_t n,
                      int32_t* next_token_dev, float* logits_dev);
 
-/* One decode step for `batch` sequences: row b runs token tokens_dev[b] (device int32)
+/* One decode step for `batch` sequences ("bare-metal-llm", "What got built" and "What
+ * it taught me": one token per step against the KV cache, the whole forward pass in
+ * one submission; "rvllm Metal backend", "What the kernels do": the GPU argmax returns
+ * one integer per sequence). Row b runs token tokens_dev[b] (device int32)
  * of sequence seq_ids_host[b] at its current length, appends K/V, and writes
  * next_tokens_dev[b] (device int32) and, if logits_dev is not NULL, logits_dev[b][vocab].
  * seq ids must be distinct. tokens_dev may alias next_tokens_dev (greedy decode fed on
- * the device). The step is one hipGraph launch (captured on first use for each
- * (batch, pointers) combination). Token ids produced on the device are checked by the
- * kernels: an out-of-range id sets a device error flag (gd_device_errors) and is
- * replaced by 0. */
+ * the device). The step is one hipGraph launch, captured on first use for each
+ * (batch, pointers, short/long context) combination; the 16 most recently used graphs
+ * are kept (an evicted graph costs one stream synchronization). Token ids produced on
+ * the device are checked by the kernels: an out-of-range id sets a device error flag
+ * (gd_device_errors) and is replaced by 0. Host-checked errors: GD_ERR_INVALID (batch,
+ * ids), GD_ERR_STATE (an empty sequence), GD_ERR_CTX_FULL (a full one). */
 gd_status gd_decode_step(gd_model* m, int32_t batch, const int32_t* seq_ids_host,
                          const int32_t* tokens_dev, int32_t* next_tokens_dev, float* logits_dev);
 
 /* Waits for the stream and returns the device error flags (bit 0: token id out of
  * range; bit 1: position beyond a sequence's capacity; bit 2: block table entry out
- * of range; bit 3: a single-launch decode step timed out waiting for one of its own
- * phases and was abandoned, its outputs are invalid), then clears them. */
+ * of range), then clears them. Waiting first is the rule of "rvllm Metal backend",
+ * "Memory is shared": no buffer is read while the GPU may still write it. */
 gd_status gd_device_errors(gd_model* m, int32_t* flags);
 
-/* Tuning/testing switches. GD_OPT_LINEAR_VARIANT: 0 auto (VALU GEMV for <= 4 rows,
- * MFMA otherwise), 1 force VALU GEMV, 2 force MFMA. GD_OPT_USE_GRAPH: 1 (default)
- * capture decode steps in hipGraphs, 0 launch kernels directly. */
+/* Tuning/testing switches (per shape, the pages' engines pick among kernel variants:
+ * "bare-metal-llm", "What it taught me"; "rvllm Metal backend", "The matmul pain story").
+ * GD_OPT_LINEAR_VARIANT: 0 auto (VALU GEMV for <= 4 rows, MFMA otherwise), 1 force VALU
+ * GEMV, 2 force MFMA. GD_OPT_USE_GRAPH: 1 (default) capture decode steps in hipGraphs,
+ * 0 launch kernels directly. Every call drops the captured graphs. GD_ERR_INVALID for
+ * an unknown option or a value outside its set. */
 #define GD_OPT_LINEAR_VARIANT 1
 #define GD_OPT_USE_GRAPH 2
 #define GD_OPT_FUSE_ATTN_O 4 /* 1 (default): attention runs fused with the output
-                              * projection (+ bias + residual) for up to 4 rows whose
-                              * contexts all hold at most 256 positions, and for the
-                              * one-chunk split-context case (GD_OPT_ATTN_CHUNKS) with a
-                              * contiguous cache, head_dim 64, one query head per KV head
-                              * and d_model <= 768; 0: attention and projection always run
-                              * as separate launches */
-#define GD_OPT_PERSISTENT 5 /* 1: a one-sequence decode step of the GPT-2 layout runs as
-                             * one launch with one workgroup per CU (phases hand over
-                             * through tagged words in device memory) for the GPT-2 124M
-                             * and tiny shapes (n_ctx <= 1024); 0 (default): the kernel
-                             * chain, which measures faster on this GPU */
-#define GD_OPT_PERSISTENT_SPIN_US 6 /* bound of every wait inside the single-launch step, in
-                                     * microseconds (default 20000); a step that exceeds it is
-                                     * abandoned and flagged (device error bit 3) */
+                              * projection (+ bias + residual) when the projection is the
+                              * VALU GEMV (up to 4 rows by default, any row count with
+                              * GD_OPT_LINEAR_VARIANT = 1) and every context holds at most
+                              * 256 positions, and for the one-chunk split-context case
+                              * (GD_OPT_ATTN_CHUNKS) with a contiguous cache, head_dim 64,
+                              * one query head per KV head and d_model <= 768; 0: attention
+                              * and projection always run as separate launches */
 #define GD_OPT_FOLD_NORM 7 /* 1 (default): with fp32 weights a layer behind a pre-norm
                            * (QKV, MLP up, head) reads copies of its weights with the
                            * norm's gain folded in (and the shift in its bias), made at
                            * gd_load_weights, and applies the row statistics in its
                            * epilogue; 0: the norm's gain and shift are applied to the
                            * row first */
-#define GD_OPT_FUSE_MLP 8 /* 1: with folded pre-norms (GD_OPT_FOLD_NORM, fp32), the
-                          * GPT-2 124M or tiny shape, up to 4 rows and attention fused
-                          * with the output projection, the MLP block runs as one launch
-                          * whose workgroups each add a hidden slice's share of the
-                          * down-projection with atomics; 0 (default): two launches,
-                          * which measure faster on this GPU */
 #define GD_OPT_ATTN_CHUNKS 9 /* context chunks per row of the split-context attention
                              * (rows that do not take the short-context fused attention):
                              * 1 (one workgroup per row and KV head over the whole context:
@@ -181,9 +204,10 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                              * GD_OPT_FUSE_ATTN_O) or 8 (partials merged by the output
                              * projection's prologue or a merge launch); 0 (default): 1
                              * when rows x KV heads >= the CU count and the output
-                             * projection would be a matrix-core launch, else 8. Launches
-                             * of at most 4 rows whose output projection is the VALU GEMV
-                             * always use 8 (its prologue merges them) */
+                             * projection would be a matrix-core launch, else 8. When the
+                             * output projection is the VALU GEMV (at most 4 rows, or any
+                             * row count with GD_OPT_LINEAR_VARIANT = 1) the split-context
+                             * attention always uses 8 (the GEMV's prologue merges them) */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper
@@ -192,7 +216,8 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
 gd_status gd_set_option(gd_model* m, int32_t option, int32_t value);
 
 /* Per-kernel profile gathered while GD_OPT_PROFILE is on ("rvllm Metal backend",
- * "The matmul pain story": GPU time summed per kernel). Waits for the stream. One
+ * "The matmul pain story": GPU time summed per kernel). Waits for the stream
+ * ("Memory is shared": read only after the GPU is done). One
  * entry per role (e.g. "linear.qkv", "attention"); `kernel` is the HIP kernel it ran;
  * `bytes` is the algorithmic traffic of those launches (every weight, bias and norm
  * parameter once, activations in and out, K/V of every attended position once).
@@ -207,7 +232,13 @@ typedef struct {
 } gd_kernel_stat;
 gd_status gd_profile_read(gd_model* m, gd_kernel_stat* out, int32_t max, int32_t* n, int32_t reset);
 
+/* Waits for the model's stream, releases its graphs, events and pinned staging; the
+ * caller's device buffers are untouched. NULL is ignored. */
 void gd_destroy(gd_model* m);
+/* Message of the calling thread's last error (empty if none). A kernel that fails to
+ * load or launch is reported as GD_ERR_HIP with this message and poisons the model --
+ * a hard failure, never a quiet skip ("rvllm Metal backend", "Things that were
+ * problematic"). The string is valid until the thread's next call. */
 const char* gd_last_error(void);
 
 /* ------------------------------------------------------------------ op level
@@ -220,10 +251,14 @@ const char* gd_last_error(void);
 #define GD_ACT_NONE 0
 #define GD_ACT_GELU 1   /* 0.5 u (1 + tanh(clamp(sqrt(2/pi)(u + 0.044715 u^3), -15, 15))) */
 
-/* Workspace bytes gd_linear needs for (M, N, K) with the given variant. */
+/* Workspace bytes gd_linear needs for (M, N, K) with the given variant.
+ * GD_ERR_INVALID for shapes gd_linear refuses. */
 gd_status gd_linear_workspace(int32_t M, int32_t N, int32_t K, int32_t variant, size_t* bytes);
 
-/* y[m][n] = act(norm(x[m]) . W[n]^T + bias[n]) (+ resid[m][n]) for m < M, n < N.
+/* One linear layer y = x . W^T with W stored [out][in] ("rvllm Metal backend", "The
+ * matmul pain story"), with its pre-norm and epilogue ("batch_forge" README: layernorm,
+ * rmsnorm and gelu with the tanh argument clamped to +-15):
+ * y[m][n] = act(norm(x[m]) . W[n]^T + bias[n]) (+ resid[m][n]) for m < M, n < N.
  * x: float [M][ldx] (K used); W: [N][K] float32 or bf16 bits (weight_dtype); bias,
  * norm_g, norm_b: float or NULL; resid: float [M][ldr] or NULL; y: float [M][ldy].
  * 1 <= M <= 32, N >= 1, 8 <= K <= 2^20 and K % 8 == 0; W must be 16-byte aligned.
@@ -238,8 +273,11 @@ gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32_t weight_d
                     size_t workspace_bytes, void* hip_stream);
 
 /* Greedy argmax of each row of logits [rows][vocab] (device) into out[rows] (device
- * int32). NaN is larger than every number (first NaN wins); ties go to the lowest
- * index. 1 <= rows <= 32. workspace: gd_argmax_workspace bytes, zeroed once. */
+ * int32), on the GPU so that one integer per row comes back ("rvllm Metal backend",
+ * "What the kernels do"). NaN is larger than every number (first NaN wins; the
+ * argmax is defined by its NaN handling: "Things that were problematic"); ties go to
+ * the lowest index. 1 <= rows <= 32, else GD_ERR_INVALID. workspace:
+ * gd_argmax_workspace bytes, zeroed once; calls sharing one workspace must not overlap. */
 gd_status gd_argmax_workspace(int32_t rows, int32_t vocab, size_t* bytes);
 gd_status gd_argmax(const float* logits, int32_t rows, int32_t vocab, int32_t* out, void* workspace,
                     size_t workspace_bytes, void* hip_stream);

@@ -15,8 +15,8 @@ def device():
     return torch.device("cuda", 0)
 
 
-def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True, persistent=False,
-             fold=True, mlp=False, chunks=0):
+def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, variant=0, graph=True, fold=True,
+             chunks=0):
     import transformer_gpt_decode_amd as gd
     s = workload.shape
     kw = dict(max_seqs=max_seqs or workload.batch, max_batch=max_batch or workload.batch)
@@ -26,9 +26,7 @@ def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, varia
     m.load_weights(W)
     m.set_option(gd.OPT_LINEAR_VARIANT, variant)
     m.set_option(gd.OPT_USE_GRAPH, 1 if graph else 0)
-    m.set_option(gd.OPT_PERSISTENT, 1 if persistent else 0)
     m.set_option(gd.OPT_FOLD_NORM, 1 if fold else 0)
-    m.set_option(gd.OPT_FUSE_MLP, 1 if mlp else 0)
     m.set_option(gd.OPT_ATTN_CHUNKS, chunks)
     return m
 
@@ -50,11 +48,15 @@ def perturb_norms_and_biases(shape, W, seed):
     return W
 
 
-def gpu_generate(m, prompts, n_generate, tables=None, want_logits=True, forced=None):
+def gpu_generate(m, prompts, n_generate, tables=None, want_logits=True, forced=None, logits_slices=False):
     """Prefill each sequence, then n_generate-1 batched greedy decode steps fed on the device.
 
     Returns tokens [B][n_generate] and (optionally) logits [B][n_generate][V] as numpy.
     With ``forced`` ([B][n_generate]) the fed tokens are forced[b][i-1] (teacher forcing).
+    The steps write their logits into one buffer (one captured graph replayed every
+    step) that is copied out after each step; with ``logits_slices`` each step writes
+    straight into its own slice of the result (a new graph per step, so the library's
+    graph cache evicts).
     """
     import torch
     dev = device()
@@ -65,6 +67,7 @@ def gpu_generate(m, prompts, n_generate, tables=None, want_logits=True, forced=N
             m.set_block_table(b, tables[b][tables[b] >= 0])
     tok = torch.zeros(B, dtype=torch.int32, device=dev)
     logits = torch.empty((n_generate, B, V), dtype=torch.float32, device=dev) if want_logits else None
+    step_lg = torch.empty((B, V), dtype=torch.float32, device=dev) if want_logits and not logits_slices else None
     for b, p in enumerate(prompts):
         m.reset_seq(b)
         m.prefill(b, p, tok[b:b + 1], logits[0, b] if want_logits else None)
@@ -74,11 +77,14 @@ def gpu_generate(m, prompts, n_generate, tables=None, want_logits=True, forced=N
         forced_dev = torch.as_tensor(np.ascontiguousarray(np.asarray(forced, np.int32).T), device=dev)
     feed = torch.zeros(B, dtype=torch.int32, device=dev)
     for i in range(1, n_generate):
+        out_lg = None if not want_logits else (logits[i] if logits_slices else step_lg)
         if forced_dev is not None:
             feed.copy_(forced_dev[i - 1])
-            m.decode_step(list(range(B)), feed, tok, logits[i] if want_logits else None)
+            m.decode_step(list(range(B)), feed, tok, out_lg)
         else:
-            m.decode_step(list(range(B)), tok, tok, logits[i] if want_logits else None)
+            m.decode_step(list(range(B)), tok, tok, out_lg)
+        if step_lg is not None:
+            logits[i].copy_(step_lg)
         toks.append(tok.clone())
     torch.cuda.synchronize()
     t = torch.stack(toks, 1).cpu().numpy()
@@ -102,25 +108,73 @@ def top2_margin(logits: np.ndarray) -> float:
     return float(s[-1] - s[-2])
 
 
-def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol):
-    """Parity bar: identical greedy tokens and |dlogit| <= tol at every step of every
-    sequence. A token flip is tolerated only as a near tie: the oracle's top-2 margin at
-    that step is at most twice the max |dlogit| seen up to it. Returns a report dict."""
+def token_checksum(tokens: np.ndarray) -> str:
+    """First 16 hex digits of SHA-256 over the int32 tokens [B][n] (row-major): one
+    number per run that the GPU and the oracle must share ("rvllm Metal backend",
+    "How I know it's correct": a checksum of every generated token per run)."""
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(tokens, dtype=np.int32).tobytes()).hexdigest()[:16]
+
+
+# A greedy token may flip only at a step whose oracle top-2 margin is below this, the
+# known near ties (every such step of the full-size workloads is listed in DESIGN.md),
+# and at most twice the largest logit difference seen so far in the sequence. The GPU
+# logits of every configuration differ from the oracle's by well under 5e-5 (fp32
+# sums in another order), so a wider gap cannot flip a token.
+NEAR_TIE_MARGIN = 1e-4
+
+# Parity records of the end-to-end runs of this session (printed in the terminal
+# summary by conftest.py).
+RECORDS = []
+
+
+def new_record(config: str, B: int, n: int, tol: float) -> dict:
+    rec = {"config": config, "seqs": B, "steps": n, "tol": tol, "flips": [], "max_dlogit": 0.0,
+           "max_dlogit_full": 0.0, "full_rows": 0, "sampled_rows": 0, "tok_gpu": "", "tok_ref": "",
+           "forced_max_dlogit": None}
+    RECORDS.append(rec)
+    return rec
+
+
+def format_record(r: dict) -> str:
+    flips = ", ".join(f"seq {b} step {i} (margin {m:.2e})" for b, i, m, _ in r["flips"]) or "none"
+    forced = "" if r["forced_max_dlogit"] is None else f"; teacher-forced max |dlogit| {r['forced_max_dlogit']:.2e}"
+    same = "identical" if r["tok_gpu"] == r["tok_ref"] else "differ"
+    return (f"{r['config']}: {r['seqs']} seq x {r['steps']} steps; tokens {same} (GPU {r['tok_gpu']}, oracle "
+            f"{r['tok_ref']}); flips: {flips}; max |dlogit| {r['max_dlogit']:.2e} (tol {r['tol']:g}) over "
+            f"{r['full_rows']} whole rows and {r['sampled_rows']} sampled rows{forced}")
+
+
+def check_flip(rec: dict, b: int, i: int, margin: float, seen: float, gpu_t: int, ref_t: int) -> None:
+    """A flipped greedy token passes only as a known near tie (see NEAR_TIE_MARGIN)."""
+    assert margin <= NEAR_TIE_MARGIN and margin <= 2 * seen, (
+        f"{rec['config']} seq {b} step {i}: token {gpu_t} != oracle {ref_t} with oracle top-2 margin "
+        f"{margin:.3e} (known near ties are below {NEAR_TIE_MARGIN:g}; twice the max |dlogit| so far is "
+        f"{2 * seen:.3e})")
+    rec["flips"].append((b, i, margin, seen))
+
+
+def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run"):
+    """Parity bar: identical greedy tokens and |dlogit| <= tol over every vocabulary
+    entry at every step of every sequence. A flip passes only as a known near tie
+    (check_flip); the caller then compares that sequence teacher-forced. Returns the
+    parity record (also kept in RECORDS)."""
     B, n = ref_tok.shape
-    rep = {"max_dlogit": 0.0, "near_ties": [], "first_divergence": None}
+    rec = new_record(config, B, n, tol)
+    rec["tok_gpu"], rec["tok_ref"] = token_checksum(gpu_tok), token_checksum(ref_tok)
     for b in range(B):
         seen = 0.0
         for i in range(n):
+            assert np.all(np.isfinite(gpu_lg[b, i])), f"non-finite logits seq {b} step {i}"
             d = float(np.max(np.abs(gpu_lg[b, i] - ref_lg[b, i])))
             seen = max(seen, d)
-            rep["max_dlogit"] = max(rep["max_dlogit"], d)
-            assert np.all(np.isfinite(gpu_lg[b, i])), f"non-finite logits seq {b} step {i}"
+            rec["full_rows"] += 1
+            rec["max_dlogit"] = max(rec["max_dlogit"], d)
             assert d <= tol, f"seq {b} step {i}: max |dlogit| {d:.3e} > {tol}"
             if gpu_tok[b, i] != ref_tok[b, i]:
-                m = top2_margin(ref_lg[b, i])
-                assert m <= 2 * seen, f"seq {b} step {i}: token {gpu_tok[b, i]} != {ref_tok[b, i]}, margin {m:.3e}"
-                rep["near_ties"].append((b, i, m))
-                if rep["first_divergence"] is None:
-                    rep["first_divergence"] = (b, i)
+                check_flip(rec, b, i, top2_margin(ref_lg[b, i]), seen, int(gpu_tok[b, i]), int(ref_tok[b, i]))
                 break   # later steps of this sequence are compared teacher-forced by the caller
-    return rep
+    rec["max_dlogit_full"] = rec["max_dlogit"]
+    # backwards-compatible view for callers that look at the near ties
+    rec["near_ties"] = [(b, i, m) for b, i, m, _ in rec["flips"]]
+    return rec

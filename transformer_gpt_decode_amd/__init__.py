@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libgptdecode.so")
 GD_OK, GD_ERR_INVALID, GD_ERR_NO_DEVICE, GD_ERR_HIP, GD_ERR_OOM, GD_ERR_CTX_FULL, GD_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 ARCH_GPT2, ARCH_LLAMA = 0, 1
 WEIGHT_F32, WEIGHT_BF16 = 0, 1
-OPT_LINEAR_VARIANT, OPT_USE_GRAPH, OPT_PROFILE, OPT_FUSE_ATTN_O, OPT_PERSISTENT, OPT_PERSISTENT_SPIN_US = 1, 2, 3, 4, 5, 6
-OPT_FOLD_NORM, OPT_FUSE_MLP, OPT_ATTN_CHUNKS = 7, 8, 9
+OPT_LINEAR_VARIANT, OPT_USE_GRAPH, OPT_PROFILE, OPT_FUSE_ATTN_O = 1, 2, 3, 4
+OPT_FOLD_NORM, OPT_ATTN_CHUNKS = 7, 9
 NORM_NONE, NORM_LAYER, NORM_RMS = 0, 1, 2
 ACT_NONE, ACT_GELU = 0, 1
 

@@ -295,8 +295,7 @@ __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
 // (the attention is recomputed by every slice of the head: at short contexts its K/V
 // come from cache), normalizes them, and adds their share of the projection,
 // sum over g, d of o[g][d] W[n][(kh G + g) HD + d], to the residual rows n of its
-// slice with float atomics (the bias from kh == 0, which also folds in and clears an
-// accumulator row if one is given). A slice is ROWS consecutive n; its
+// slice with float atomics (the bias from kh == 0). A slice is ROWS consecutive n; its
 // weights (HD/4 lanes per row, float4 or four bf16 each) and bias are loaded first.
 // The atomics of all passes go out together at the end, after the last wait (vector
 // memory operations of a wave complete in issue order: an atomic issued before a later
@@ -306,7 +305,6 @@ struct AttnOParams {
   const float* bias;      // never NULL
   float* y; int ldy;      // residual rows, updated in place
   int N, K;
-  float* zf;              // NULL, or rows [M][ldy] folded into y with the bias and then zeroed
 };
 
 template <int HD>
@@ -341,8 +339,7 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   // K/V loads. Vector loads complete in issue order, so the weights, needed last,
   // arrive first and the wait for the K/V covers them at no cost.
   f32x4 wv[RT::PASSES][G];
-  float bv[RT::PASSES], zv[RT::PASSES];
-  const bool fold = po.zf && kh == 0;   // wave-uniform
+  float bv[RT::PASSES];
 #pragma unroll
   for (int ps = 0; ps < RT::PASSES; ++ps) {
     const int n = min(n0 + ps * RT::PER_PASS + grp, po.N - 1);
@@ -357,7 +354,6 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       }
     }
     bv[ps] = po.bias[n];
-    zv[ps] = fold ? po.zf[(size_t)row * po.ldy + n] : 0.f;
   }
   const AttnRow rm = attn_row<PAGED>(p, row);
   f32x4 q[G];
@@ -378,7 +374,7 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       a = fmaf(wv[ps][g].z, ov.z, a);
       a = fmaf(wv[ps][g].w, ov.w, a);
     }
-    acc[ps] = group_sum<RT::LG>(a) + (kh == 0 ? bv[ps] + zv[ps] : 0.f);
+    acc[ps] = group_sum<RT::LG>(a) + (kh == 0 ? bv[ps] : 0.f);
   }
   // every sum complete before the first atomic (the empty asm takes them as operands):
   // a wait placed after an atomic would wait for that atomic too
@@ -389,13 +385,6 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     const int n = n0 + ps * RT::PER_PASS + grp;
     if (gl == 0 && n < po.N)
       __hip_atomic_fetch_add(po.y + (size_t)row * po.ldy + n, acc[ps], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (fold) {   // each (row, n) of the accumulator was read by this thread alone
-#pragma unroll
-    for (int ps = 0; ps < RT::PASSES; ++ps) {
-      const int n = n0 + ps * RT::PER_PASS + grp;
-      if (gl == 0 && n < po.N) po.zf[(size_t)row * po.ldy + n] = 0.f;
-    }
   }
 }
 

@@ -32,7 +32,6 @@
 
 // Source of the activation rows.
 #define PRO_COPY 0   // x rows as given
-#define PRO_SUM2 1   // x + x2 (the residual and the fused MLP's accumulator)
 #define PRO_ATTN 3   // merge of split-context attention partials
 // Row normalization applied after the source (LinParams::norm).
 #define NORM_NONE 0
@@ -59,7 +58,6 @@ struct LinParams {
   // ---- input rows
   int pro, norm;
   const float* x; int ldx;                  // COPY (and MFMA input)
-  const float* x2;                          // SUM2: added to x (same row stride)
   const float* ng; const float* nb; float eps;
   const float* apart; int Hq;               // ATTN: partials [M][Hq][GD_ATT_NCH][hd + 2]
   int* err;
@@ -176,7 +174,6 @@ __device__ __forceinline__ void epi_store(const LinParams& p, const EpiOps& e, i
 template <int XPT>
 struct RowRegs {
   f32x4 x[XPT];
-  f32x4 x2[XPT];   // PRO_SUM2
 };
 
 template <int XPT, int PRO>
@@ -184,14 +181,13 @@ __device__ __forceinline__ void stage_issue(const LinParams& p, RowRegs<XPT>& rr
   // Loads are unconditional (clamped to the last valid chunk; stage_finish stores only
   // valid ones) and the prologue is fixed at compile time, so the compiler can count
   // them and wait for these alone later, not for the weight loads issued after them.
-  if (PRO != PRO_COPY && PRO != PRO_SUM2) return;
+  if (PRO != PRO_COPY) return;
   const int tid = threadIdx.x, K4 = p.K >> 2;
 #pragma unroll
   for (int j = 0; j < XPT; ++j) {
     const int i = min(tid + GD_WG * j, p.M * K4 - 1);
     const int m = i / K4, k = (i - m * K4) << 2;
     rr.x[j] = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + k);
-    if (PRO == PRO_SUM2) rr.x2[j] = *reinterpret_cast<const f32x4*>(p.x2 + (size_t)m * p.ldx + k);
   }
 }
 
@@ -220,15 +216,11 @@ __device__ __forceinline__ void stage_finish(const LinParams& p, float* xs, cons
   for (int j = 0; j < XPT; ++j) {
     const int i = min(tid + GD_WG * j, M * K4 - 1);
     const int m = i / K4, k = (i - m * K4) << 2;
-    f32x4 v = rr.x[j];
-    if (PRO == PRO_SUM2) v += rr.x2[j];
-    *reinterpret_cast<f32x4*>(xs + m * K + k) = v;
+    *reinterpret_cast<f32x4*>(xs + m * K + k) = rr.x[j];
   }
   for (int i = tid + GD_WG * XPT; i < M * K4; i += GD_WG) {   // rows beyond the register share
     const int m = i / K4, k = (i - m * K4) << 2;
-    f32x4 v = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + k);
-    if (PRO == PRO_SUM2) v += *reinterpret_cast<const f32x4*>(p.x2 + (size_t)m * p.ldx + k);
-    *reinterpret_cast<f32x4*>(xs + m * K + k) = v;
+    *reinterpret_cast<f32x4*>(xs + m * K + k) = *reinterpret_cast<const f32x4*>(p.x + (size_t)m * p.ldx + k);
   }
 }
 

@@ -7,7 +7,6 @@ struct RowParams {
   const int* table; int max_blocks, block_size, nblk, Hkv, hd;  // KV cache addressing
   const void* wte; const void* wpe; int vocab, n_pos, d, emb_bf16;
   float* x;                                                      // [rows][d]
-  float* z0; float* z1;                                          // NULL, or accumulator rows [rows][d] to clear
   int* row_seq; int* row_pos; int* row_tok; long long* row_kvoff;
   const float* rope; float* row_cs;   // RoPE table [n_pos][hd] (cos | sin) and each row's copy
   int* err;
@@ -45,7 +44,6 @@ __device__ void row_setup(const RowParams& r, int b, int seq, int pos, int tok) 
       else v += bf16_lo(reinterpret_cast<const uint16_t*>(r.wpe)[(size_t)ppos * r.d + i]);
     }
     r.x[(size_t)b * r.d + i] = v;
-    if (r.z0) { r.z0[(size_t)b * r.d + i] = 0.f; r.z1[(size_t)b * r.d + i] = 0.f; }
   }
   if (r.rope) {
     const int rp = min(max(pos, 0), r.n_pos - 1);

@@ -23,8 +23,6 @@
 #include "linear.h"
 #include "attention.h"
 #include "misc.h"
-#include "persistent.h"
-#include "mlp.h"
 
 // ------------------------------------------------------------------ errors
 
@@ -184,17 +182,6 @@ static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipSt
     GD_GEMV(1, EPI_PLAIN, PRO_ATTN, NRM_NONE);
     return hipSuccess;
   }
-  if (prm.pro == PRO_SUM2) {   // the residual plus the fused MLP's accumulator (fp32, folded norm)
-    if constexpr (WT == 0) {
-      if (!fold) return hipErrorNotSupported;
-      if (prm.epi == EPI_QKV) GD_GEMV(1, EPI_QKV, PRO_SUM2, NRM_FOLDED);
-      else if (prm.epi == EPI_ARGMAX && lp.rw == 4) GD_GEMV(4, EPI_ARGMAX, PRO_SUM2, NRM_FOLDED);
-      else if (prm.epi == EPI_ARGMAX) GD_GEMV(1, EPI_ARGMAX, PRO_SUM2, NRM_FOLDED);
-      else return hipErrorNotSupported;
-      return hipSuccess;
-    }
-    return hipErrorNotSupported;
-  }
   switch (prm.epi) {
     case EPI_PLAIN: if (nrm) GD_GEMV_N(1, EPI_PLAIN); else GD_GEMV(1, EPI_PLAIN, PRO_COPY, NRM_NONE); break;
     case EPI_GELU: if (nrm) GD_GEMV_N(1, EPI_GELU); else GD_GEMV(1, EPI_GELU, PRO_COPY, NRM_NONE); break;
@@ -292,7 +279,6 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
     p.M = std::min(lp.rows, prm.M - r0);
     if (r0) {
       if (p.x) p.x += (size_t)r0 * p.ldx;
-      if (p.x2) p.x2 += (size_t)r0 * p.ldx;
       p.resid += (size_t)r0 * p.ldr;
       if (p.y) p.y += (size_t)r0 * p.ldy;
       if (p.logits) p.logits += (size_t)r0 * p.ldl;
@@ -321,7 +307,6 @@ struct LayerOff {
   // pre-norm folded into QKV and MLP-up (fp32): weights, bias, row sums (0: none)
   size_t fqkv, fqkv_b, fqkv_s, ffc, ffc_b, ffc_s;
   size_t tfqkv, tffc;   // their tile-major copies
-  size_t pproj;         // W_proj packed for k_mlp (0: none)
 };
 
 struct GraphKey {
@@ -338,6 +323,8 @@ struct GraphKey {
 // Rows of at most this many positions (and few rows) run attention fused with the output
 // projection: every projection slice recomputes the attention from K/V in cache.
 static const int kFusedAttnOMaxT = 256;
+// Decode-step graphs kept per model.
+static const size_t kMaxGraphs = 16;
 
 struct gd_model {
   gd_config c;
@@ -349,12 +336,8 @@ struct gd_model {
   bool fuse_attn_o = true;
   int attn_chunks = 0;   // split-context chunks per row: 0 auto, 1 or GD_ATT_NCH (GD_OPT_ATTN_CHUNKS)
   bool use_fold = true;  // GEMV pre-norms folded into the weights when available (GD_OPT_FOLD_NORM)
-  bool use_mlp = false;  // the MLP block of <= 4 rows in one launch (GD_OPT_FUSE_MLP; measured slower)
-  bool mlp_ok = false;   // k_mlp has an instance for this shape (and the weights are folded)
-  bool use_pk = false;  // single-launch decode step for one sequence (GD_OPT_PERSISTENT; measured slower)
-  long long pk_spin_us = 20000;   // bound of its waits (GD_OPT_PERSISTENT_SPIN_US)
   int dev = 0;
-  int n_cu = 0;         // compute units: workgroups of the single-launch step
+  int n_cu = 0;         // compute units
 
   // derived shapes
   int qdim, kdim, qkvdim, fcN, hdim, wt;
@@ -381,13 +364,6 @@ struct gd_model {
 
   // scratch offsets (bytes)
   size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart, o_zero;
-  size_t o_z[2];   // k_mlp accumulators (alternating layers)
-  // single-launch decode step: exchange words, layer table, abort tag
-  bool pk_ok = false;
-  unsigned pk_tag = 0;
-  size_t o_xb = 0, o_pkabort = 0;
-  long long pk_xl = 0, pk_att = 0, pk_xo = 0, pk_h = 0, pk_xd = 0, pk_rs_att = 0, pk_rs_d = 0, pk_rs_h = 0, pk_arg = 0;
-  size_t pk_words = 0;
   size_t o_rseq, o_rpos, o_rtok, o_rkv, o_rcs, o_pseq, o_ppos, o_ptok, o_pkv, o_pcs, o_len, o_cap, o_sids, o_table, o_err, o_rope;
 
   // host mirror
@@ -398,7 +374,11 @@ struct gd_model {
   hipEvent_t staging_evt = nullptr;
   bool staging_pending = false;
 
-  std::map<GraphKey, hipGraphExec_t> graphs;
+  // Captured decode steps, keyed by (batch, step pointers, context bucket), at most
+  // kMaxGraphs of them: the least recently launched one is dropped first.
+  struct GraphEntry { hipGraphExec_t exec; unsigned long long last_use; };
+  std::map<GraphKey, GraphEntry> graphs;
+  unsigned long long graph_clock = 0;
 
   // per-kernel profiling (GD_OPT_PROFILE)
   bool profile = false;
@@ -444,34 +424,6 @@ static gd_status check_cfg(const gd_config* c) {
     return set_err(GD_ERR_INVALID, "bad paged cache sizes");
   if (!(c->norm_eps > 0.f)) return set_err(GD_ERR_INVALID, "norm_eps must be > 0");
   return GD_OK;
-}
-
-// Weight chunks (16 bytes) per lane of a K-long row in the single-launch step.
-
-// The single-launch decode step handles one sequence of the GPT-2 layout whose shapes
-// match an instantiated kernel and fit its LDS staging.
-static bool pk_supported(const gd_model* m) {
-  const gd_config& c = m->c;
-  if (c.arch != GD_ARCH_GPT2 || m->n_cu < 1 || m->n_cu > PK_MAXWG) return false;
-  if (c.d_model > PK_DMAX || c.d_model % 64 || c.d_ff > PK_INMAX || c.n_ctx > PK_ACH * PK_MAXNCH) return false;
-  if (c.n_head * PK_MAXNCH * (c.head_dim + 2) > PK_INMAX || c.n_head * PK_MAXNCH > m->n_cu) return false;
-  if (iceil(m->qkvdim, m->n_cu) > 2 * PK_CW || iceil(c.d_ff, m->n_cu) > 2 * PK_CW || iceil(c.d_model, m->n_cu) > PK_CW)
-    return false;
-  if (c.kv_block_size > 0 && (c.kv_block_size & (c.kv_block_size - 1))) return false;   // power-of-two blocks
-  if (m->layer_kv_floats() * 4 >= (1ull << 31)) return false;   // 32-bit byte offsets in a pool
-  // every layer's tensors at a constant stride from layer 0's (the kernel adds l x stride)
-  for (int l = 1; l < c.n_layer; ++l) {
-    const LayerOff &a = m->L[l], &z = m->L[0];
-    const size_t st = m->L[1].n1g - z.n1g;
-    const size_t d = (size_t)l * st;
-    if (a.n1g != z.n1g + d || a.n1b != z.n1b + d || a.wqkv != z.wqkv + d || a.bqkv != z.bqkv + d || a.wo != z.wo + d ||
-        a.bo != z.bo + d || a.n2g != z.n2g + d || a.n2b != z.n2b + d || a.wfc != z.wfc + d || a.bfc != z.bfc + d ||
-        a.wproj != z.wproj + d || a.bproj != z.bproj + d)
-      return false;
-  }
-  // instantiated shapes: GPT-2 124M and the tiny decoder
-  return (c.d_model == 768 && c.d_ff == 3072 && c.head_dim == 64) ||
-         (c.d_model == 64 && c.d_ff == 256 && c.head_dim == 16);
 }
 
 static void layout(gd_model* m) {
@@ -547,10 +499,6 @@ static void layout(gd_model* m) {
     m->o_fhead = take(V * d * 4);
     m->o_fhead_b = take(V * 4);
     m->o_fhead_s = take(V * 4);
-    // k_mlp instances: GPT-2 124M (768, 3072) and the tiny decoder (64, 256)
-    m->mlp_ok = c.arch == GD_ARCH_GPT2 && ((d == 768 && ff == 3072) || (d == 64 && ff == 256));
-    if (m->mlp_ok)
-      for (int l = 0; l < c.n_layer; ++l) m->L[l].pproj = take(d * ff * 4);
   }
   m->o_fold_end = off;   // the host fills [o_fold, o_fold_end); k_pack_tiles the rest
   if (m->folded) {
@@ -582,8 +530,6 @@ static void layout(gd_model* m) {
   m->o_amv = take(m->am_parts * R * 4);
   m->o_ami = take(m->am_parts * R * 4);
   m->o_apart = take(R * c.n_head * GD_ATT_NCH * (c.head_dim + 2) * 4);
-  m->o_z[0] = take(R * d * 4);
-  m->o_z[1] = take(R * d * 4);
   // zeros (cleared at bind, never written): the bias or residual of layers that have none
   m->o_zero = take((size_t)std::max({m->qkvdim, m->fcN, (int)d, (int)ff}) * 4);
   m->o_rseq = take(R * 4);
@@ -602,24 +548,6 @@ static void layout(gd_model* m) {
   m->o_table = take((size_t)c.max_seqs * m->max_blocks * 4);
   m->o_err = take(4);
   m->o_rope = c.arch == GD_ARCH_LLAMA ? take((size_t)c.n_ctx * c.head_dim * 4) : 0;
-  // single-launch decode step (one sequence, GPT-2 layout): exchange regions per layer
-  m->pk_ok = pk_supported(m);
-  if (m->pk_ok) {
-    auto r64 = [](long long w) { return (w + 63) / 64 * 64; };   // 512-byte granules
-    const long long d = c.d_model, hd = c.head_dim, H = c.n_head;
-    m->pk_rs_att = r64(H * PK_MAXNCH * (hd + 2));
-    m->pk_rs_d = r64(d);
-    m->pk_rs_h = r64(c.d_ff);
-    m->pk_att = r64(m->qkvdim);
-    m->pk_xo = m->pk_att + PK_NREP * m->pk_rs_att;
-    m->pk_h = m->pk_xo + PK_NREP * m->pk_rs_d;
-    m->pk_xd = m->pk_h + PK_NREP * m->pk_rs_h;
-    m->pk_xl = m->pk_xd + PK_NREP * m->pk_rs_d;
-    m->pk_arg = m->pk_xl * c.n_layer;
-    m->pk_words = (size_t)(m->pk_arg + r64(2 * PK_MAXWG));
-    m->o_xb = take(m->pk_words * 8);
-    m->o_pkabort = take(4);
-  }
   m->s_bytes = off;
 }
 
@@ -670,7 +598,7 @@ extern "C" gd_status gd_create(const gd_config* cfg, void* hip_stream, gd_model*
 extern "C" void gd_destroy(gd_model* m) {
   if (!m) return;
   if (m->stream) (void)hipStreamSynchronize(m->stream);
-  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
   for (auto& r : m->prof_pending)
     for (auto& pr : r.pairs) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
   if (m->gate_evt) (void)hipEventDestroy(m->gate_evt);
@@ -733,11 +661,10 @@ extern "C" gd_status gd_bind_memory(gd_model* m, void* wdev, void* kvdev, void* 
       }
     HIP_TRY(m, hipMemcpyAsync(m->sp<float>(m->o_rope), cs.data(), cs.size() * 4, hipMemcpyHostToDevice, m->stream));
   }
-  m->pk_tag = 0;   // the exchange words were just cleared (tag 0)
   HIP_TRY(m, hipStreamSynchronize(m->stream));
   std::fill(m->len.begin(), m->len.end(), 0);
   m->last_sids.clear();
-  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
   m->graphs.clear();
   m->bound = true;
   m->loaded = false;
@@ -882,21 +809,6 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     }
     fold(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, (int)V, m->o_nfg, m->o_nfb, 0, m->o_fhead, m->o_fhead_b,
          m->o_fhead_s);
-    if (m->mlp_ok) {
-      // W_proj for k_mlp: float4 c of output nl of slice (js, ns) holds
-      // W_proj[ns NSL + nl][js J + 4c .. 4c + 3]
-      const size_t J = ff / 64, CJ = J / 4, NSL = d / MLP_NS;
-      for (int l = 0; l < c.n_layer; ++l) {
-        const float* Wp = rf(m->L[l].wproj);
-        float* P = wf(m->L[l].pproj);
-        for (size_t js = 0; js < 64; ++js)
-          for (size_t ns = 0; ns < MLP_NS; ++ns)
-            for (size_t cc = 0; cc < CJ; ++cc)
-              for (size_t nl = 0; nl < NSL; ++nl)
-                for (size_t q = 0; q < 4; ++q)
-                  P[((((js * MLP_NS + ns) * CJ + cc) * NSL + nl) << 2) + q] = Wp[(ns * NSL + nl) * ff + js * J + 4 * cc + q];
-      }
-    }
     HIP_TRY(m, hipMemcpyAsync(m->w + m->o_fold, fbuf.data(), fbuf.size(), hipMemcpyHostToDevice, m->stream));
   }
   auto pack = [&](size_t src, size_t dst, int N, int K) {
@@ -1014,13 +926,6 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->fuse_attn_o = v != 0;
   } else if (opt == GD_OPT_FOLD_NORM) {
     m->use_fold = v != 0;
-  } else if (opt == GD_OPT_FUSE_MLP) {
-    m->use_mlp = v != 0;
-  } else if (opt == GD_OPT_PERSISTENT) {
-    m->use_pk = v != 0;
-  } else if (opt == GD_OPT_PERSISTENT_SPIN_US) {
-    if (v < 0) return set_err(GD_ERR_INVALID, "spin bound must be >= 0");
-    m->pk_spin_us = v;
   } else if (opt == GD_OPT_ATTN_CHUNKS) {
     if (v != 0 && v != 1 && v != GD_ATT_NCH) return set_err(GD_ERR_INVALID, "attention chunks must be 0, 1 or %d", GD_ATT_NCH);
     m->attn_chunks = v;
@@ -1031,7 +936,7 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
   } else {
     return set_err(GD_ERR_INVALID, "unknown option %d", opt);
   }
-  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
   m->graphs.clear();
   return GD_OK;
 }
@@ -1178,22 +1083,6 @@ static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, boo
   else GD_LAUNCH((k_attention<HD, G, PPG, false, GD_WG>), grid, dim3(GD_WG), 0, st, a);
 }
 
-// The MLP block of M <= 4 rows (k_mlp): reads the residual rows x, adds into z.
-static hipError_t launch_mlp(gd_model* m, hipStream_t st, int l, int M, const float* x, float* z) {
-  const gd_config& c = m->c;
-  const LayerOff& t = m->L[l];
-  MlpParams p;
-  p.x = x; p.ldx = c.d_model; p.M = M; p.K = c.d_model; p.eps = c.norm_eps;
-  p.wfc = m->wf(t.ffc); p.bfc = m->wf(t.ffc_b); p.sfc = m->wf(t.ffc_s);
-  p.wpk = m->wf(t.pproj); p.bproj = m->wf(t.bproj);
-  p.z = z; p.ldz = c.d_model;
-  p.J = c.d_ff / 64; p.JS = 64; p.NSL = c.d_model / MLP_NS;
-  const dim3 g(64 * MLP_NS), b(MLP_WG);
-  if (c.d_model == 768) GD_LAUNCH((k_mlp<3, 6, 12>), g, b, 0, st, p);
-  else GD_LAUNCH((k_mlp<1, 1, 1>), g, b, 0, st, p);
-  return hipGetLastError();
-}
-
 // Row set-up parameters over the row arrays starting at seq/pos/tok/kvoff.
 static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long long* rkv, float* rcs) {
   const gd_config& c = m->c;
@@ -1205,7 +1094,6 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
   r.wpe = c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr;
   r.vocab = c.vocab; r.n_pos = c.n_ctx; r.d = c.d_model; r.emb_bf16 = m->wt == GD_WEIGHT_BF16;
   r.x = m->sp<float>(m->o_x);
-  if (m->mlp_ok && m->use_mlp) { r.z0 = m->sp<float>(m->o_z[0]); r.z1 = m->sp<float>(m->o_z[1]); }
   r.row_seq = rseq; r.row_pos = rpos; r.row_tok = rtok; r.row_kvoff = rkv;
   r.rope = c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rope) : nullptr;
   r.row_cs = rcs;
@@ -1245,13 +1133,6 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
   const bool fold = m->folded && m->use_fold;   // pre-norms folded into QKV, MLP up and the head
-  // The MLP block in one launch (k_mlp) adds its output into accumulator z[l % 2]
-  // instead of the residual x, which its own workgroups read for the norm. Layer l + 1
-  // then reads x + z[l % 2] (QKV prologue), and its fused attention + output projection
-  // folds z[l % 2] into x and clears it for layer l + 2; the head reads x + z[L-1 % 2].
-  // The row set-up clears both accumulators.
-  const bool fmlp = m->mlp_ok && m->use_mlp && fold && fuse_ao && M <= GEMV_MAX_ROWS;
-  float* zacc[2] = {m->sp<float>(m->o_z[0]), m->sp<float>(m->o_z[1])};
 
   double kv_pos = 0;  // attended positions summed over rows (profiling only)
   for (int t : m->prof_T) kv_pos += t;
@@ -1274,7 +1155,6 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.pro = PRO_COPY;
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
-      if (fmlp && l > 0) { p.pro = PRO_SUM2; p.x2 = zacc[(l - 1) & 1]; }
       p.w = m->w + t.wqkv; p.wtl = m->w + t.tqkv; p.N = m->qkvdim; p.K = d;
       if (fold) { p.wf = m->w + t.fqkv; p.wfl = m->w + t.tfqkv; p.bf = m->wf(t.fqkv_b); p.fs = m->wf(t.fqkv_s); }
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
@@ -1303,7 +1183,6 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       AttnOParams po;
       po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
       po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
-      po.zf = fmlp && l > 0 ? zacc[(l - 1) & 1] : nullptr;
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attn_o<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attn_o", kn,
@@ -1320,7 +1199,6 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       AttnOParams po;
       po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
       po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
-      po.zf = nullptr;
       ProfScope ps(m, st, "attn_proj", "k_attn_proj<64>",
                    kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + M * m->qdim * 4.0 + (double)d * m->qdim * m->elt +
                        (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
@@ -1360,13 +1238,6 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
       if ((e = run_linear(m, st, "linear.o", p)) != hipSuccess) return e;
     }
-    if (fmlp) {
-      // pre-norm + FC + GELU + down-projection + bias, added into z[l % 2]
-      ProfScope ps(m, st, "mlp", c.d_model == 768 ? "k_mlp<3, 6, 12>" : "k_mlp<1, 1, 1>",
-                   2.0 * d * ff * 4 + 2.0 * ff * 4 + d * 4.0 + 2.0 * M * d * 4);
-      if ((e = launch_mlp(m, st, l, M, x, zacc[l & 1])) != hipSuccess) return e;
-      continue;
-    }
     // pre-norm + MLP up: GPT-2 FC + bias + clamped tanh-GELU; Llama gate|up + SiLU gate
     {
       LinParams p = base;
@@ -1399,7 +1270,6 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.pro = PRO_COPY;
     p.x = x + (size_t)head_row * d; p.ldx = d;
     p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
-    if (fmlp) { p.pro = PRO_SUM2; p.x2 = zacc[(c.n_layer - 1) & 1] + (size_t)head_row * d; }
     p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
     if (fold) {
       p.wf = m->w + m->o_fhead; p.wfl = m->w + m->o_tfhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s);
@@ -1474,88 +1344,6 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
   return GD_OK;
 }
 
-// ------------------------------------------------- single-launch decode step
-
-template <int WT, int D, int FF, int HD>
-static hipError_t launch_pk(gd_model* m, hipStream_t st, const PKParams& p) {
-  static bool lds_set = false;
-  if (!lds_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode1<WT, D, FF, HD>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, PK_LDS_BYTES);
-    if (e != hipSuccess) return e;
-    lds_set = true;
-  }
-  GD_LAUNCH((k_decode1<WT, D, FF, HD>), dim3(m->n_cu), dim3(PK_WG), PK_LDS_BYTES, st, p);
-  return hipGetLastError();
-}
-
-// Algorithmic bytes of one single-launch step at T attended positions, counted as the
-// kernel chain counts its launches: every weight, bias and norm parameter once, the
-// K/V of every attended position once, activations in and out.
-static double pk_step_bytes(const gd_model* m, int T, bool logits) {
-  const gd_config& c = m->c;
-  const double d = c.d_model, ff = c.d_ff, q = m->qkvdim, e = (double)m->elt, V = c.vocab;
-  double b = d * (2 * e + 4);
-  const double layer = (q * d * e + d * 4 + q * 4 + q * 4 + 2 * d * 4) +
-                       ((double)T * c.n_head * c.head_dim * 8 + 2 * d * 4 + d * d * e + d * 4 + 2 * d * 4) +
-                       (ff * d * e + d * 4 + ff * 4 + ff * 4 + 2 * d * 4) + (d * ff * e + ff * 4 + 3 * d * 4);
-  b += layer * c.n_layer;
-  b += V * d * e + d * 4 + (logits ? V * 4 : 0) + 2 * d * 4 + m->n_cu * 8.0 + 4;
-  return b;
-}
-
-// One decode step of sequence `seq` as a single launch (k_decode1).
-static hipError_t enqueue_pk(gd_model* m, hipStream_t st, int seq, const int* tok, int* next, float* logits) {
-  const gd_config& c = m->c;
-  if (m->pk_tag == 0xffffffffu) {   // tags are about to wrap: clear every exchange word
-    const hipError_t e = hipMemsetAsync(m->s + m->o_xb, 0, m->pk_words * 8, st);
-    if (e != hipSuccess) return e;
-    m->pk_tag = 0;
-  }
-  PKParams p;
-  memset(&p, 0, sizeof(p));
-  {
-    const LayerOff& t = m->L[0];
-    PKLayer& q = p.L0;
-    q.n1g = m->wf(t.n1g); q.n1b = m->wf(t.n1b);
-    q.wqkv = m->w + t.wqkv; q.bqkv = m->wf(t.bqkv);
-    q.wo = m->w + t.wo; q.bo = m->wf(t.bo);
-    q.n2g = m->wf(t.n2g); q.n2b = m->wf(t.n2b);
-    q.wfc = m->w + t.wfc; q.bfc = m->wf(t.bfc);
-    q.wproj = m->w + t.wproj; q.bproj = m->wf(t.bproj);
-    q.kc = m->kpool(0); q.vc = m->vpool(0);
-    p.w_stride = c.n_layer > 1 ? (long long)(m->L[1].n1g - m->L[0].n1g) : 0;
-    p.kv_stride = (long long)m->layer_kv_floats();
-  }
-  p.n_layer = c.n_layer; p.d = c.d_model; p.H = c.n_head; p.ff = c.d_ff; p.vocab = c.vocab; p.qkv = m->qkvdim;
-  p.eps = c.norm_eps; p.scale = 1.0f / std::sqrt((float)c.head_dim);
-  p.wte = m->w + m->o_wte; p.wpe = m->w + m->o_wpe; p.nfg = m->wf(m->o_nfg); p.nfb = m->wf(m->o_nfb);
-  p.paged = c.kv_block_size > 0;
-  p.hd = c.head_dim;
-  p.kv0 = (int)((size_t)seq * c.n_kv_head * m->bsize * c.head_dim);   // contiguous: the sequence's block
-  p.table = m->sp<int>(m->o_table); p.max_blocks = m->max_blocks; p.nblk = m->nblk;
-  p.bs_shift = 0;
-  while ((1 << p.bs_shift) < m->bsize) ++p.bs_shift;
-  p.kv_hstride = m->bsize * c.head_dim;
-  p.seq = seq; p.pos = m->len[seq]; p.nch = iceil(p.pos + 1, PK_ACH);
-  p.tag = ++m->pk_tag;
-  p.spin_ticks = m->pk_spin_us * 100;   // the real-time counter runs at 100 MHz
-  p.tok = tok; p.next = next; p.logits = logits;
-  p.len = m->sp<int>(m->o_len); p.err = m->sp<int>(m->o_err);
-  p.xb = m->sp<uint64_t>(m->o_xb); p.abort_tag = m->sp<unsigned>(m->o_pkabort);
-  p.xl = m->pk_xl; p.x_att = m->pk_att; p.x_xo = m->pk_xo; p.x_h = m->pk_h; p.x_xd = m->pk_xd;
-  p.rs_att = m->pk_rs_att; p.rs_d = m->pk_rs_d; p.rs_h = m->pk_rs_h; p.x_arg = m->pk_arg;
-  char kn[48];
-  snprintf(kn, sizeof(kn), "k_decode1<%d, %d, %d, %d>", m->wt == GD_WEIGHT_F32 ? 0 : 1, c.d_model, c.d_ff, c.head_dim);
-  ProfScope ps(m, st, "decode1", kn, m->profile ? pk_step_bytes(m, p.pos + 1, logits != nullptr) : 0);
-  if (c.head_dim == 16) {
-    if (m->wt == GD_WEIGHT_F32) return launch_pk<0, 64, 256, 16>(m, st, p);
-    return launch_pk<1, 64, 256, 16>(m, st, p);
-  }
-  if (m->wt == GD_WEIGHT_F32) return launch_pk<0, 768, 3072, 64>(m, st, p);
-  return launch_pk<1, 768, 3072, 64>(m, st, p);
-}
-
 static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, int max_T, const int* tok, int* next,
                                  float* logits) {
   RowParams rp = row_params(m, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
@@ -1600,8 +1388,6 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     for (int b = 0; b < B; ++b) m->prof_T.push_back(m->len[sids[b]] + 1);
   int max_T = 0;   // attended positions of the longest row
   for (int b = 0; b < B; ++b) max_T = std::max(max_T, m->len[sids[b]] + 1);
-  // one sequence of the GPT-2 layout: the whole step as one launch
-  const bool single = B == 1 && m->use_pk && m->pk_ok;
   if (m->profile && m->profile_gated) {
     // hold the stream (bounded) while the step is enqueued, then let it run whole
     if (!m->gate_evt) HIP_TRY(m, hipEventCreateWithFlags(&m->gate_evt, hipEventDisableTiming));
@@ -1609,15 +1395,7 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     HIP_TRY(m, hipGetLastError());
     HIP_TRY(m, hipEventRecord(m->gate_evt, m->cap_stream));
     HIP_TRY(m, hipStreamWaitEvent(s, m->gate_evt, 0));
-    hipError_t e = single ? enqueue_pk(m, s, sids[0], tok_dev, next_dev, logits_dev)
-                          : enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
-    if (e != hipSuccess) {
-      m->poisoned = true;
-      return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    }
-  } else if (single) {
-    // the step's tag changes every step, so it is launched directly (one launch anyway)
-    hipError_t e = enqueue_pk(m, s, sids[0], tok_dev, next_dev, logits_dev);
+    hipError_t e = enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
     if (e != hipSuccess) {
       m->poisoned = true;
       return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
@@ -1626,6 +1404,15 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
     GraphKey key{B, tok_dev, next_dev, logits_dev, max_T <= kFusedAttnOMaxT};
     auto it = m->graphs.find(key);
     if (it == m->graphs.end()) {
+      if (m->graphs.size() >= kMaxGraphs) {
+        // drop the least recently launched graph; it may still run on the stream
+        auto lru = m->graphs.begin();
+        for (auto g = m->graphs.begin(); g != m->graphs.end(); ++g)
+          if (g->second.last_use < lru->second.last_use) lru = g;
+        HIP_TRY(m, hipStreamSynchronize(s));
+        HIP_TRY(m, hipGraphExecDestroy(lru->second.exec));
+        m->graphs.erase(lru);
+      }
       hipGraph_t g;
       HIP_TRY(m, hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
       hipError_t e = enqueue_decode(m, m->cap_stream, B, max_T, tok_dev, next_dev, logits_dev);
@@ -1641,9 +1428,10 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
         m->poisoned = true;
         return set_err(GD_ERR_HIP, "graph instantiate failed: %s", hipGetErrorString(e3));
       }
-      it = m->graphs.emplace(key, ex).first;
+      it = m->graphs.emplace(key, gd_model::GraphEntry{ex, 0}).first;
     }
-    HIP_TRY(m, hipGraphLaunch(it->second, s));
+    it->second.last_use = ++m->graph_clock;
+    HIP_TRY(m, hipGraphLaunch(it->second.exec, s));
   } else {
     hipError_t e = enqueue_decode(m, s, B, max_T, tok_dev, next_dev, logits_dev);
     if (e != hipSuccess) {
