@@ -282,6 +282,15 @@ gd_status gd_argmax_workspace(int32_t rows, int32_t vocab, size_t* bytes);
 gd_status gd_argmax(const float* logits, int32_t rows, int32_t vocab, int32_t* out, void* workspace,
                     size_t workspace_bytes, void* hip_stream);
 
+/* gd_argmax without a workspace, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same result as gd_argmax. Its partials and counters live in a static device array
+ * of the library (64 KiB per GPU, kept until the process ends), so it allocates
+ * nothing: 1 <= rows <= 32 and 1 <= vocab <= 2^20, else GD_ERR_INVALID. Every call on
+ * one GPU shares that array: calls that overlap on one GPU (other streams or threads)
+ * race and must not be issued. Enqueued on hip_stream of the current device. */
+gd_status gd_argmax_static(const float* logits, int32_t rows, int32_t vocab, int32_t* out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

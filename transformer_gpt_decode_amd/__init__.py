@@ -28,7 +28,7 @@ ACT_NONE, ACT_GELU = 0, 1
 EXPORTS = ["gd_create", "gd_memory_requirements", "gd_bind_memory", "gd_load_weights", "gd_set_block_table",
            "gd_reset_seq", "gd_truncate_seq", "gd_seq_len", "gd_prefill", "gd_decode_step", "gd_device_errors",
            "gd_set_option", "gd_profile_read", "gd_destroy", "gd_last_error", "gd_linear_workspace", "gd_linear",
-           "gd_argmax_workspace", "gd_argmax"]
+           "gd_argmax_workspace", "gd_argmax", "gd_argmax_static"]
 
 
 class GdError(RuntimeError):
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
                           _i32, _i32, _i32, _i32, _vp, ctypes.c_size_t, _vp],
             "gd_argmax_workspace": [_i32, _i32, _szp],
             "gd_argmax": [_vp, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp],
+            "gd_argmax_static": [_vp, _i32, _i32, _vp, _vp],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -226,4 +227,15 @@ def argmax(logits, stream=None):
     out = torch.empty(rows, dtype=torch.int32, device=logits.device)
     _check(lib().gd_argmax(logits.data_ptr(), rows, vocab, out.data_ptr(), ws.data_ptr(), ws.numel(),
                            _stream_ptr(stream)))
+    return out
+
+
+def argmax_static(logits, out=None, stream=None):
+    """argmax() without a workspace: the library's static scratch holds the partials
+    (calls on one GPU must not overlap). Writes into ``out`` if given."""
+    import torch
+    rows, vocab = logits.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    _check(lib().gd_argmax_static(logits.data_ptr(), rows, vocab, out.data_ptr(), _stream_ptr(stream)))
     return out

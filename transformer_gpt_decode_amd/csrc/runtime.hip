@@ -1533,3 +1533,65 @@ extern "C" gd_status gd_argmax(const float* logits, int32_t rows, int32_t vocab,
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "argmax launch failed: %s", hipGetErrorString(e));
   return GD_OK;
 }
+
+// ------------------------------------------------- argmax without allocation
+//
+// gd_argmax_static keeps the per-chunk partials and the per-row arrival counters of
+// k_argmax_rows in `scratch`, a file-scope device array: one copy per GPU, held until
+// the process ends. Host code never passes `scratch` itself to a kernel (on the host
+// it is only a stand-in for the symbol): the first call on each device looks up that
+// device's copy with hipGetSymbolAddress and keeps the address.
+static const int kStaticArgmaxMaxVocab = 1 << 20;
+static const int kStaticArgmaxChunks = kStaticArgmaxMaxVocab / 4096;   // chunks of k_argmax_rows
+static const size_t kStaticPartBytes = (size_t)GD_MAX_ROWS * kStaticArgmaxChunks * 4;
+static const size_t kStaticScratchBytes = 2 * kStaticPartBytes + 256;   // values, indices, counters
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+static const int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Clears n ints (a fill kernel rather than a memset, so that the call can be captured).
+__global__ void k_zero_ints(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+extern "C" gd_status gd_argmax_static(const float* logits, int32_t rows, int32_t vocab, int32_t* out,
+                                      void* hip_stream) {
+  if (rows < 1 || rows > GD_MAX_ROWS)
+    return set_err(GD_ERR_INVALID, "argmax_static: rows %d outside 1..%d", rows, GD_MAX_ROWS);
+  if (vocab < 1 || vocab > kStaticArgmaxMaxVocab)
+    return set_err(GD_ERR_INVALID, "argmax_static: vocab %d outside 1..%d (the static scratch holds %d chunks "
+                   "per row)", vocab, kStaticArgmaxMaxVocab, kStaticArgmaxChunks);
+  if (!logits || !out) return set_err(GD_ERR_INVALID, "NULL argument");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_err(GD_ERR_NO_DEVICE, "argmax_static: no current device below %d", kMaxDevices);
+  char* base;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* ptr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !ptr)
+        return set_err(GD_ERR_HIP, "argmax_static: hipGetSymbolAddress failed on device %d: %s", dev,
+                       hipGetErrorString(e));
+      g_scratch_ptr[dev] = ptr;
+    }
+    base = static_cast<char*>(g_scratch_ptr[dev]);
+  }
+  float* pv = reinterpret_cast<float*>(base);
+  int* pi = reinterpret_cast<int*>(base + kStaticPartBytes);
+  int* ctr = reinterpret_cast<int*>(base + 2 * kStaticPartBytes);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const int nch = iceil(vocab, 4096);
+  hipLaunchKernelGGL(k_zero_ints, dim3(1), dim3(64), 0, st, ctr, rows);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    GD_LAUNCH(k_argmax_rows, dim3(nch, rows), dim3(GD_WG), 0, st, logits, rows, vocab, nch, pv, pi, ctr, out);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return set_err(GD_ERR_HIP, "argmax_static launch failed: %s", hipGetErrorString(e));
+  return GD_OK;
+}
