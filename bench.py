@@ -4,19 +4,27 @@
 A step is one decode forward of the whole batch (all layers, logits and greedy
 argmax, tokens fed on the device), replayed as one hipGraph. Inputs are the seeded
 synthetic workloads of synth/ (random-init weights of the named shape, random
-prompt ids); prefill is untimed.
+prompt ids); prefill is untimed (reported as time to first token).
 
-Prints ONE JSON line on stdout (everything else goes to stderr):
-  value        decode tokens/s of the headline workload (GPT-2 124M shape, batch 1)
+Every workload of the five configurations is measured (C1 tiny, C2 GPT-2 124M batch
+1, C3 stress init to n_ctx, C4 batch 32 fp32 and bf16, C5 Llama-style paged batch 8):
+  window       K steps from the end of the prompts, timed 5 times (median reported)
+  full         every decode step of the generation, timed 5 times (median)
+  step         algorithmic bytes per step over the step time, against 8 TB/s and a
+               measured device-to-device copy; a synchronous variant (tokens read back
+               and the stream synchronized every step)
   roofline     the dominant kernel (largest share of the step's kernel time):
                algorithmic bytes per launch / mean launch time, from HIP event pairs
                around every launch of a profiled pass whose steps are each enqueued
                whole behind a short hold, so host enqueue gaps fall outside the pairs
-  step         achieved algorithmic GB/s of the whole step against 8 TB/s and against a
-               measured device-to-device copy; a synchronous variant (token read back
-               and stream synchronized every step)
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
-  batch32      the same measurements for 32 sequences (GPT-2 124M shape, fp32)
+  gemm_mfma    per linear role of the batched workloads: 2 M N K / mean launch time
+               against the fp32 matrix peak, the bf16 peak and the attainable roofline
+  tokens       checksum of every generated token, GPU against the oracle
+  cpu_baseline the CPU oracle timed on a bounded sample of the workload (worker
+               processes started before the GPU work, one thread each)
+
+Prints ONE JSON line on stdout (everything else goes to stderr); the top level is the
+C2 workload (GPT-2 124M shape, batch 1, fp32), the others are under "workloads".
 """
 from __future__ import annotations
 
@@ -77,79 +85,85 @@ def rewind(m, tok, first, plen):
     tok.copy_(first)
 
 
-def run_steps(m, tok, first, plen, n_steps, n_decode, seq_ids):
-    """n_steps decode steps; after each full generation (n_decode steps) rewind to the prompt end."""
-    done = 0
-    while done < n_steps:
-        k = min(n_steps - done, n_decode)
-        for _ in range(k):
+def timed_steps(m, tok, first, plen, K, seq_ids, runs):
+    """ms per step of K decode steps from the end of the prompts, timed `runs` times
+    (GPU events around the K graph launches, and the host clock; the larger counts)."""
+    import torch
+    out = []
+    for _ in range(runs):
+        rewind(m, tok, first, plen)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        e0.record()
+        for _ in range(K):
             m.decode_step(seq_ids, tok, tok)
-        done += k
-        if done < n_steps:
-            rewind(m, tok, first, plen)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        out.append(max(e0.elapsed_time(e1), wall * 1e3) / K)
+    return out
 
 
-def measure(wname: str, steps, warmup: int):
+def measure(wname: str, steps, warmup: int, runs: int, full: bool):
     import torch
     import transformer_gpt_decode_amd as gd
     w, W, prompts, m, tok, first, plen, ttft = setup(wname)
-    log(f"[bench] {wname}: prompts prefilled")
+    log(f"[bench] {wname}: prompts prefilled ({ttft:.3f} s)")
     if PROFILE_MODE[0] == 1:
-        # counter runs: every step launched eagerly (under counter collection, runs stalled
-        # inside back-to-back graph replays)
+        # counter runs: every step launched eagerly (see DESIGN.md, measurement)
         m.set_option(gd.OPT_USE_GRAPH, 0)
     n_decode = w.n_generate - 1
-    K = steps if steps else n_decode
+    K = min(steps, n_decode) if steps else n_decode
     seq_ids = list(range(w.batch))
-    # warmup (captures the graph), then rewind to the end of the prompts
-    run_steps(m, tok, first, plen, max(1, warmup), n_decode, seq_ids)
-    rewind(m, tok, first, plen)
+    # warm-up: W steps from the end of the prompts (rewound after each whole generation)
+    left = max(1, warmup)
+    while left > 0:
+        rewind(m, tok, first, plen)
+        for _ in range(min(left, n_decode)):
+            m.decode_step(seq_ids, tok, tok)
+        left -= min(left, n_decode)
     torch.cuda.synchronize()
     log(f"[bench] {wname}: warm-up done")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record()
-    run_steps(m, tok, first, plen, K, n_decode, seq_ids)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = e0.elapsed_time(e1)
-    ms_step = max(gpu_ms, wall * 1e3) / K
+    win = timed_steps(m, tok, first, plen, K, seq_ids, runs)
     assert m.device_errors() == 0
-    log(f"[bench] {wname}: timed run done ({K} steps)")
+    log(f"[bench] {wname}: {runs} timed runs of {K} steps: " + " ".join(f"{x:.4f}" for x in win) + " ms/step")
+    fullg = timed_steps(m, tok, first, plen, n_decode, seq_ids, runs) if (full and n_decode != K) else win
+    if full and n_decode != K:
+        log(f"[bench] {wname}: {runs} timed runs of the whole generation ({n_decode} steps): "
+            + " ".join(f"{x:.4f}" for x in fullg) + " ms/step")
     # synchronous variant: the new tokens read back and the stream synchronized every step
     rewind(m, tok, first, plen)
-    S = min(K, n_decode)
     host = torch.empty(tok.shape, dtype=tok.dtype, pin_memory=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(S):
+    for _ in range(K):
         m.decode_step(seq_ids, tok, tok)
         host.copy_(tok, non_blocking=True)
         torch.cuda.current_stream().synchronize()
-    ms_sync = (time.perf_counter() - t0) * 1e3 / S
+    ms_sync = (time.perf_counter() - t0) * 1e3 / K
     log(f"[bench] {wname}: synchronous run done")
-    # greedy tokens of the first steps after the prompt (for the oracle cross-check)
+    # every generated token (the first from the prompt) for the checksum against the oracle
     rewind(m, tok, first, plen)
     hist = [first.cpu().numpy().copy()]
-    for _ in range(min(n_decode, 24)):
+    for _ in range(n_decode):
         m.decode_step(seq_ids, tok, tok)
-        hist.append(tok.cpu().numpy().copy())
-    gpu_tokens = np.stack(hist, 1)
-    # profiled eager pass over one generation window: per-kernel time and bytes
+        hist.append(tok.clone())
+    gpu_tokens = np.stack([h if isinstance(h, np.ndarray) else h.cpu().numpy() for h in hist], 1)
+    assert m.device_errors() == 0
+    # profiled eager pass over the window: per-kernel time and bytes
     rewind(m, tok, first, plen)
     m.set_option(gd.OPT_PROFILE, PROFILE_MODE[0])
     m.profile_read(reset=True)
-    P = min(K, n_decode)
-    for _ in range(P):
+    for _ in range(K):
         m.decode_step(seq_ids, tok, tok)
     stats = m.profile_read(reset=True)
-    log(f"[bench] {wname}: profiled pass done ({P} steps)")
+    log(f"[bench] {wname}: profiled pass done ({K} steps)")
     m.set_option(gd.OPT_PROFILE, 0)
     m.close()
     torch.cuda.synchronize()
-    return dict(w=w, W=W, prompts=prompts, ms_step=ms_step, K=K, ttft=ttft, stats=stats, P=P,
-                gpu_tokens=gpu_tokens, gpu_ms=gpu_ms, wall_s=wall, ms_sync=ms_sync, S=S)
+    return dict(w=w, prompts=prompts, plen=plen, K=K, win=win, full=fullg, n_decode=n_decode, ttft=ttft,
+                stats=stats, P=K, gpu_tokens=gpu_tokens, ms_sync=ms_sync)
 
 
 def kernel_table(stats, P):
@@ -206,12 +220,15 @@ def gemm_table(stats, P, w):
 
 def gemm_step(gemms, w):
     """All linear layers of one step: their summed kernel time and the step's GEMM flops
-    (2 B x linear and head parameters) over it."""
+    (2 B x linear and head parameters) over it, against the fp32 and bf16 matrix peaks
+    and against the attainable time (each GEMM at its own attainable rate)."""
     us = sum(g["launches_per_step"] * g["avg_us"] for g in gemms)
     flops = sum(g["launches_per_step"] * g["tflops"] * 1e12 * g["avg_us"] * 1e-6 for g in gemms)
+    at_us = sum(g["launches_per_step"] * g["tflops"] * g["avg_us"] / g["attainable_tflops"] for g in gemms)
     tf = flops / (us * 1e-6) / 1e12 if us else 0.0
     return dict(us_per_step=round(us, 1), gflop_per_step=round(flops / 1e9, 3), tflops=round(tf, 2),
-                frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4))
+                frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4), frac_bf16_peak=round(tf / MFMA_BF16_TFLOPS, 5),
+                attainable_us_per_step=round(at_us, 1), frac_attainable=round(at_us / us, 4) if us else 0.0)
 
 
 def kernel_sources_sha256() -> str:
@@ -259,46 +276,150 @@ def roofline(rows, workload: str):
             "bytes_per_launch": round(top["bytes_per_launch"]), "avg_launch_us": top["avg_us"]}
 
 
-def cpu_baseline(res, budget_s: float):
-    """The oracle (single-threaded C) on a bounded sample: prompt prefilled untimed, then
-    single-token decode forwards of sequence 0 until the budget is spent."""
+# Oracle samples (workload: timed decode forwards). The sequence is the one with the
+# shortest prompt (the oracle's untimed prefill grows with it); C1 and C2 time their
+# whole generation, which also gives every token of it for the checksum.
+CPU_SAMPLE_FORWARDS = {"tiny": None, "gpt2_b1": None, "gpt2_stress": 16, "gpt2_b32": 16, "gpt2_b32_bf16": 16,
+                       "llama_b8": 8}
+
+
+def _shortest(w, prompts):
+    return min(range(len(prompts)), key=lambda b: (len(prompts[b]), b))
+
+
+def oracle_sample(wname: str):
+    """Runs in a worker process: the single-threaded oracle prefills one sequence
+    (untimed), then runs its timed decode forwards (see CPU_SAMPLE_FORWARDS)."""
     import oracle
-    w, W, prompts = res["w"], res["W"], res["prompts"]
+    import synth
+    w = synth.WORKLOADS[wname]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    b = _shortest(w, prompts)
+    n = CPU_SAMPLE_FORWARDS[wname] or (w.n_generate - 1)
     om = oracle.Model(w.shape, W)
-    p = prompts[0]
-    s = om.new_seq(len(p) + w.n_generate)
+    s = om.new_seq(len(prompts[b]) + w.n_generate)
+    t0 = time.perf_counter()
     tok = -1
-    for t in p:
+    for t in prompts[b]:
         tok = s.forward(int(t))
+    prefill_s = time.perf_counter() - t0
     toks = [tok]
     t0 = time.perf_counter()
-    n = 0
-    while n < w.n_generate - 1 and (time.perf_counter() - t0) < budget_s:
-        tok = s.forward(toks[-1])
-        toks.append(tok)
-        n += 1
+    for _ in range(n):
+        toks.append(s.forward(toks[-1]))
     dt = time.perf_counter() - t0
-    g = res["gpu_tokens"][0]
-    k = min(len(g), len(toks))
-    return {"value": round(n / dt, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{w.name}: sequence 0, {len(p)}-id prompt prefilled untimed, then {n} single-token decode "
-                      f"forwards ({dt:.1f} s, 1 thread)",
-            "host_cpus": os.cpu_count(), "tokens_match_gpu": bool(np.array_equal(g[:k], np.array(toks[:k]))),
-            "tokens_compared": int(k)}
+    return dict(workload=wname, seq=b, prompt=len(prompts[b]), forwards=n, seconds=dt, prefill_s=prefill_s,
+                tokens=toks)
+
+
+def start_cpu_samples(wnames):
+    """Worker processes for the oracle samples, started before anything touches the GPU
+    (forked from a fresh server process; one thread each)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("forkserver")
+    pool = ctx.Pool(max(1, min(len(wnames), 6)))
+    return pool, {wn: pool.apply_async(oracle_sample, (wn,)) for wn in wnames}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(sample, res, n_workers):
+    w = res["w"]
+    k = len(sample["tokens"])
+    g = res["gpu_tokens"][sample["seq"], :k]
+    unit = "tok/s"
+    return {"value": round(sample["forwards"] / sample["seconds"], 3), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{w.name}: sequence {sample['seq']} ({sample['prompt']}-id prompt, the shortest) prefilled "
+                      f"untimed ({sample['prefill_s']:.1f} s), then {sample['forwards']} single-token decode forwards "
+                      f"({sample['seconds']:.2f} s, 1 thread; {n_workers} such samples ran at once, one per "
+                      f"workload, each on its own core)",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "tokens_match_gpu": bool(np.array_equal(g, np.array(sample["tokens"]))), "tokens_compared": int(k)}
+
+
+def golden_tokens(wname: str):
+    """The oracle's greedy tokens [B][n_generate] of a full-size workload, as written by
+    tests/golden/make_golden.py (None when there is no golden or it came from another
+    oracle source)."""
+    import hashlib
+    path = os.path.join(ROOT, "tests", "golden", f"{wname}.npz")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("oracle.c", "oracle.h"):
+        with open(os.path.join(ROOT, "oracle", f), "rb") as fh:
+            h.update(fh.read())
+    with np.load(path, allow_pickle=False) as z:
+        if str(z["oracle_hash"]) != h.hexdigest()[:16]:
+            return None
+        return z["tokens"].copy(), z["margin"].copy()
+
+
+def token_checksum(tokens) -> str:
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(tokens, dtype=np.int32).tobytes()).hexdigest()[:16]
+
+
+def token_record(res, sample):
+    """Checksum of every generated token of every sequence, GPU and oracle; the oracle's
+    tokens come from the golden file (full-size workloads) or from the oracle sample
+    when it covers the whole generation (C1, C2, one sequence)."""
+    gpu = res["gpu_tokens"]
+    rec = {"gpu_checksum": token_checksum(gpu), "tokens": int(gpu.size)}
+    g = golden_tokens(res["w"].name)
+    ref = None
+    if g is not None:
+        ref, margin = g
+        rec["oracle_source"] = "tests/golden (oracle)"
+    elif sample is not None and res["w"].batch == 1 and len(sample["tokens"]) == gpu.shape[1]:
+        ref, margin = np.array([sample["tokens"]], np.int32), None
+        rec["oracle_source"] = "oracle sample (this run)"
+    if ref is None:
+        rec["oracle_checksum"] = None
+        return rec
+    rec["oracle_checksum"] = token_checksum(ref)
+    rec["identical"] = bool(np.array_equal(gpu, ref))
+    flips = []
+    for b in range(gpu.shape[0]):
+        d = np.nonzero(gpu[b] != ref[b])[0]
+        if len(d):
+            i = int(d[0])
+            flips.append({"seq": b, "step": i, "oracle_margin": None if margin is None else float(margin[b, i])})
+    rec["first_divergence"] = flips
+    return rec
 
 
 def summary(res):
+    import statistics
     rows, step_bytes, kern_us = kernel_table(res["stats"], res["P"])
     w = res["w"]
-    tps = w.batch / (res["ms_step"] * 1e-3)
-    step_gbps = step_bytes / (res["ms_step"] * 1e-3) / 1e9
-    return rows, dict(value=round(tps, 1), ms_per_step=round(res["ms_step"], 4), steps=res["K"],
+    ms = statistics.median(res["win"])
+    ms_full = statistics.median(res["full"])
+    step_gbps = step_bytes / (ms * 1e-3) / 1e9
+    p0, p1 = min(res["plen"]), max(res["plen"])
+    return rows, dict(value=round(w.batch / (ms * 1e-3), 1), ms_per_step=round(ms, 4), steps=res["K"],
+                      runs=len(res["win"]), ms_per_step_runs=[round(x, 4) for x in res["win"]],
+                      window=f"decode steps 1..{res['K']} after the prompts (positions {p0}..{p0 + res['K'] - 1}"
+                             + (f" to {p1}..{p1 + res['K'] - 1}" if p1 != p0 else "") + ")",
                       algo_bytes_per_step=round(step_bytes), step_gbps=round(step_gbps, 1),
                       step_hbm_frac=round(step_gbps / HBM_PEAK_GBPS, 4),
                       copy_gbps=round(COPY_GBPS[0], 1) if COPY_GBPS[0] else None,
                       step_copy_frac=round(step_gbps / COPY_GBPS[0], 4) if COPY_GBPS[0] else None,
                       kernel_us_per_step=round(kern_us, 2), ttft_s=round(res["ttft"], 4),
-                      sync_ms_per_step=round(res["ms_sync"], 4), sync_value=round(w.batch / (res["ms_sync"] * 1e-3), 1))
+                      sync_ms_per_step=round(res["ms_sync"], 4), sync_value=round(w.batch / (res["ms_sync"] * 1e-3), 1),
+                      full_generation=dict(steps=res["n_decode"], ms_per_step=round(ms_full, 4),
+                                           value=round(w.batch / (ms_full * 1e-3), 1),
+                                           ms_per_step_runs=[round(x, 4) for x in res["full"]]))
 
 
 def _short_name(n: str) -> str:
@@ -403,11 +524,12 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
     if bench_json:
         with open(bench_json) as f:
             bench = json.loads(f.read().strip().splitlines()[-1])
-        bench_sets.append({k["kernel"]: k for k in bench.get("kernels", [])})
-        steps = [bench["steps"]]
-        if "batch32" in bench:
-            bench_sets.append({k["kernel"]: k for k in bench["batch32"].get("kernels", [])})
-            steps.append(bench["batch32"]["steps"])
+        entries = bench.get("workloads_order") or [bench["config"]["workload"]]
+        steps = []
+        for name in entries:
+            e = bench["workloads"][name] if "workloads" in bench else bench
+            bench_sets.append({k["kernel"]: k for k in e.get("kernels", [])})
+            steps.append(e["steps"])
     for pi, (lo, hi, nsteps) in enumerate(profiled_regions(rows, steps)):
         d = {}
         for r in rows[lo:hi]:
@@ -459,14 +581,55 @@ def copy_rate():
     return 2.0 * (1 << 30) / (best * 1e-3) / 1e9
 
 
+WORKLOADS = ["gpt2_b1", "tiny", "gpt2_stress", "gpt2_b32", "gpt2_b32_bf16", "llama_b8"]
+SHAPES = {"tiny": "tiny GPT-2 (2x64, 4 heads, ff 256, vocab 512)",
+          "gpt2_b1": "GPT-2 124M (12x768, 12 heads, ff 3072, vocab 50257)",
+          "gpt2_stress": "GPT-2 124M, W_fc ~ N(0, 0.5)",
+          "gpt2_b32": "GPT-2 124M (12x768, 12 heads, ff 3072, vocab 50257)",
+          "gpt2_b32_bf16": "GPT-2 124M, bf16 weights",
+          "llama_b8": "Llama-style (32x960, 15/5 heads, SwiGLU 2560, vocab 49152), paged KV"}
+
+
+def entry(res):
+    rows, summ = summary(res)
+    w = res["w"]
+    e = dict(workload=w.name, shape=SHAPES[w.name], batch=w.batch, weights=w.weight_dtype,
+             prompt_len=list(w.prompt_len), n_generate=w.n_generate, **summ)
+    if w.name == "tiny":
+        # 548 KB of weights stay in cache: the step is launch-bound, a roofline
+        # fraction says nothing about it
+        e["roofline"] = None
+    else:
+        e["roofline"] = roofline(rows, w.name)
+    if w.batch > 1:
+        gemms = gemm_table(res["stats"], res["P"], w)
+        e["gemm_mfma"] = gemms
+        e["gemm_step"] = gemm_step(gemms, w)
+    e["kernels"] = rows
+    return e
+
+
+def log_entry(e):
+    log(f"[bench] {e['workload']}: {e['value']} tok/s, {e['ms_per_step']} ms/step (median of {e['runs']}), "
+        f"whole generation {e['full_generation']['ms_per_step']} ms/step")
+    for r in e["kernels"]:
+        log(f"  {r['kernel']:<34} {str(r['roles']):<28} {r['launches_per_step']:6.1f}/step {r['avg_us']:9.2f} us "
+            f"{r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
+    for g in e.get("gemm_mfma", []):
+        log(f"  {g['role']:<12} {g['avg_us']:8.2f} us {g['tflops']:7.2f} TFLOP/s  "
+            f"{100 * g['frac_fp32_peak']:5.1f}% of fp32 MFMA peak, {100 * g['frac_attainable']:5.1f}% of attainable")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=0, help="timed decode steps (default: one full generation)")
+    ap.add_argument("--steps", type=int, default=20, help="timed decode steps per run (capped at a workload's "
+                    "generation; 0: the whole generation)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gpt2_b1")
-    ap.add_argument("--batch32", default="gpt2_b32", help="second workload reported beside ('' to skip)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle sample budget (0 to skip)")
+    ap.add_argument("--runs", type=int, default=5, help="timed runs per workload (the median is reported)")
+    ap.add_argument("--workloads", default=",".join(WORKLOADS), help="comma-separated; the first is the headline")
+    ap.add_argument("--no-full", action="store_true", help="skip the timed runs of the whole generation")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle samples (CPU baseline)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known traffic that "
                          "scales the HBM byte counters of a rocprofv3 --pmc run)")
@@ -489,7 +652,8 @@ def main():
         steps = None
         if args.bench_json:
             with open(args.bench_json) as f:
-                steps = json.loads(f.read().strip().splitlines()[-1])["steps"]
+                b = json.loads(f.read().strip().splitlines()[-1])
+                steps = b["workloads"][args.traffic_workload]["steps"] if "workloads" in b else b["steps"]
         traffic_json(args.traffic_json[0], args.traffic_json[1], args.calib_mib, args.traffic_cmd,
                      args.traffic_workload, steps)
         return
@@ -500,6 +664,12 @@ def main():
         print("bench.py runs on one GPU only: the decode path has no multi-GPU code (decode would shard "
               "by sequence, one weight copy per GPU); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    wnames = [x for x in args.workloads.split(",") if x]
+    for wn in wnames:
+        if wn not in SHAPES:
+            sys.exit(f"unknown workload {wn}; choose from {','.join(WORKLOADS)}")
+    # the oracle samples start first, in processes that never touch the GPU
+    pool, jobs = (None, {}) if args.no_cpu else start_cpu_samples(wnames)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -516,38 +686,40 @@ def main():
     PROFILE_MODE[0] = args.profile_mode
     COPY_GBPS[0] = copy_rate()
     log(f"[bench] device-to-device copy: {COPY_GBPS[0]:.0f} GB/s (read + write)")
-    log(f"[bench] workload {args.workload}: warmup {args.warmup}, steps {args.steps or 'one generation'}")
-    res = measure(args.workload, args.steps, args.warmup)
-    rows, summ = summary(res)
-    log(f"[bench] {args.workload}: {summ['value']} tok/s, {summ['ms_per_step']} ms/step")
-    for r in rows:
-        log(f"  {r['kernel']:<28} {str(r['roles']):<40} {r['launches_per_step']:6.1f}/step {r['avg_us']:9.2f} us "
-            f"{r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
-    out = {"metric": METRIC, "value": summ["value"], "unit": "tok/s",
-           "n_gpus": 1, "steps": res["K"], "warmup": args.warmup, "ms_per_step": summ["ms_per_step"],
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": res["w"].name, "batch": res["w"].batch, "prompt_len": res["w"].prompt_len[0],
-                      "n_generate": res["w"].n_generate, "shape": "GPT-2 124M (12x768, 12 heads, ff 3072, "
-                      "vocab 50257)", "weights": "f32"},
-           "roofline": roofline(rows, res["w"].name), "step": summ, "kernels": rows}
-    if args.cpu_seconds > 0:
-        log("[bench] oracle CPU baseline ...")
-        out["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
-    if args.batch32:
-        log(f"[bench] workload {args.batch32} ...")
-        r32 = measure(args.batch32, 0, args.warmup)
-        rows32, summ32 = summary(r32)
-        log(f"[bench] {args.batch32}: {summ32['value']} tok/s, {summ32['ms_per_step']} ms/step")
-        for r in rows32:
-            log(f"  {r['kernel']:<28} {str(r['roles']):<40} {r['launches_per_step']:6.1f}/step "
-                f"{r['avg_us']:9.2f} us {r['gbps']:8.1f} GB/s  {100 * r['share']:5.1f}%")
-        gemms = gemm_table(r32["stats"], r32["P"], r32["w"])
-        for g in gemms:
-            log(f"  {g['role']:<12} {g['avg_us']:8.2f} us {g['tflops']:7.2f} TFLOP/s  "
-                f"{100 * g['frac_fp32_peak']:5.1f}% of fp32 MFMA peak, {100 * g['frac_attainable']:5.1f}% of attainable")
-        out["batch32"] = dict(workload=r32["w"].name, dtype=r32["w"].weight_dtype, **summ32,
-                              roofline=roofline(rows32, r32["w"].name), gemm_mfma=gemms, gemm_step=gemm_step(gemms, r32["w"]),
-                              kernels=rows32)
+    results, entries = {}, {}
+    for wn in wnames:
+        log(f"[bench] workload {wn}: warmup {args.warmup}, {args.runs} runs of {args.steps or 'all'} steps")
+        results[wn] = measure(wn, args.steps, args.warmup, args.runs, not args.no_full)
+        entries[wn] = entry(results[wn])
+        log_entry(entries[wn])
+    if pool is not None:
+        log("[bench] waiting for the oracle samples ...")
+        for wn in wnames:
+            smp = jobs[wn].get(900)
+            entries[wn]["cpu_baseline"] = cpu_baseline(smp, results[wn], len(wnames))
+            entries[wn]["tokens"] = token_record(results[wn], smp)
+            log(f"[bench] {wn}: oracle {entries[wn]['cpu_baseline']['value']} tok/s on 1 core; tokens "
+                f"{entries[wn]['tokens']}")
+        pool.terminate()
+        pool.join()
+    else:
+        for wn in wnames:
+            entries[wn]["tokens"] = token_record(results[wn], None)
+    head = entries[wnames[0]]
+    hw = results[wnames[0]]["w"]
+    out = {"metric": METRIC, "value": head["value"], "unit": "tok/s",
+           "n_gpus": 1, "steps": head["steps"], "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32" if hw.weight_dtype == "f32" else "bf16-weights/f32", "data": "synthetic",
+           "config": {"workload": hw.name, "batch": hw.batch, "prompt_len": hw.prompt_len[0],
+                      "n_generate": hw.n_generate, "timed": head["window"], "runs": head["runs"],
+                      "shape": head["shape"], "weights": hw.weight_dtype},
+           "roofline": head["roofline"], "cpu_baseline": head.get("cpu_baseline"), "tokens": head["tokens"],
+           "step": {k: head[k] for k in ("value", "ms_per_step", "ms_per_step_runs", "algo_bytes_per_step",
+                                         "step_gbps", "step_hbm_frac", "copy_gbps", "step_copy_frac",
+                                         "kernel_us_per_step", "ttft_s", "sync_ms_per_step", "sync_value",
+                                         "full_generation")},
+           "workloads_order": wnames, "workloads": entries}
     print(json.dumps(out), flush=True)
 
 
