@@ -23,7 +23,8 @@ class OrcConfig(ctypes.Structure):
     _fields_ = [("arch", ctypes.c_int), ("n_layer", ctypes.c_int), ("d_model", ctypes.c_int),
                 ("n_head", ctypes.c_int), ("n_kv_head", ctypes.c_int), ("head_dim", ctypes.c_int),
                 ("d_ff", ctypes.c_int), ("vocab", ctypes.c_int), ("n_ctx", ctypes.c_int),
-                ("norm_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+                ("norm_eps", ctypes.c_double), ("rope_theta", ctypes.c_double), ("kv_bf16", ctypes.c_int),
+                ("weight_q8", ctypes.c_int)]
 
 
 def lib():
@@ -60,6 +61,15 @@ def lib():
         L.orc_attend.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p]
         L.orc_rope.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         L.orc_set_mutation.argtypes = [ctypes.c_int]
+        L.orc_round_bf16.restype = ctypes.c_float
+        L.orc_round_bf16.argtypes = [ctypes.c_float]
+        L.orc_quantize_q8.argtypes = [_f32p, ctypes.c_int, ctypes.POINTER(ctypes.c_int8), _f32p]
+        _u64p = ctypes.POINTER(ctypes.c_uint64)
+        L.orc_philox4x64.argtypes = [_u64p, _u64p, _u64p]
+        L.orc_uniform.restype = ctypes.c_double
+        L.orc_uniform.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int]
+        L.orc_sample.restype = ctypes.c_int
+        L.orc_sample.argtypes = [_f32p, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_double]
         _lib = L
     return _lib
 
@@ -74,9 +84,9 @@ def _ip(a: np.ndarray):
     return a.ctypes.data_as(_i32p)
 
 
-def config_from_shape(s) -> OrcConfig:
+def config_from_shape(s, kv_bf16: bool = False, weight_q8: bool = False) -> OrcConfig:
     return OrcConfig(s.arch, s.n_layer, s.d_model, s.n_head, s.n_kv_head, s.head_dim, s.d_ff, s.vocab,
-                     s.n_ctx, s.norm_eps, s.rope_theta)
+                     s.n_ctx, s.norm_eps, s.rope_theta, int(kv_bf16), int(weight_q8))
 
 
 def set_mutation(m: int) -> None:
@@ -154,14 +164,46 @@ def argmax(v) -> int:
     return int(lib().orc_argmax(_fp(v), v.size))
 
 
+def round_bf16(x) -> np.ndarray:
+    x = np.asarray(x, np.float32)
+    f = lib().orc_round_bf16
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.float32).reshape(x.shape)
+
+
+def quantize_q8(x):
+    """(q int8 [n], d float32 [n / 32]) of n values (n a multiple of 32)."""
+    x = np.ascontiguousarray(x, np.float32).ravel()
+    q = np.empty(x.size, np.int8)
+    d = np.empty(x.size // 32, np.float32)
+    lib().orc_quantize_q8(_fp(x), x.size, q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), _fp(d))
+    return q, d
+
+
+def philox4x64(ctr, key):
+    c = (ctypes.c_uint64 * 4)(*[int(v) for v in ctr])
+    k = (ctypes.c_uint64 * 2)(*[int(v) for v in key])
+    o = (ctypes.c_uint64 * 4)()
+    lib().orc_philox4x64(c, k, o)
+    return [int(v) for v in o]
+
+
+def uniform(seed: int, seq: int, pos: int) -> float:
+    return float(lib().orc_uniform(int(seed), int(seq), int(pos)))
+
+
+def sample(logits, temperature: float, top_k: int, u: float) -> int:
+    v = np.ascontiguousarray(logits, np.float32)
+    return int(lib().orc_sample(_fp(v), v.size, float(temperature), int(top_k), float(u)))
+
+
 # --------------------------------------------------------------------- model
 
 class Model:
     """The oracle model over a packed canonical float32 weight buffer (kept alive here)."""
 
-    def __init__(self, shape, weights: np.ndarray):
+    def __init__(self, shape, weights: np.ndarray, kv_bf16: bool = False, weight_q8: bool = False):
         self.shape = shape
-        self.cfg = config_from_shape(shape)
+        self.cfg = config_from_shape(shape, kv_bf16, weight_q8)
         self.weights = np.ascontiguousarray(weights, np.float32)
         n = lib().orc_weight_count(ctypes.byref(self.cfg))
         if n != self.weights.size:
@@ -209,33 +251,48 @@ class Seq:
         return int(lib().orc_forward(self.model._h, self._h, int(token), None))
 
 
+def for_workload(w, weights: np.ndarray) -> Model:
+    """The oracle model of a synth workload (its KV and weight precision choices)."""
+    return Model(w.shape, weights, kv_bf16=w.init.kv_bf16, weight_q8=w.init.q8)
+
+
 def generate(model: Model, prompt: Sequence[int], n_generate: int, capacity: Optional[int] = None,
-             want_logits: bool = False, forced: Optional[Sequence[int]] = None):
-    """Greedy generation: prefill the prompt, then feed each argmax back.
+             want_logits: bool = False, forced: Optional[Sequence[int]] = None, sampling=None):
+    """Greedy (or sampled) generation: prefill the prompt, then feed each token back.
 
     Returns (tokens[n_generate], logits[n_generate][V] or None). The first generated
     token comes from the prompt's last position, so there are n_generate - 1 decode
     forwards after the prompt. With ``forced``, the fed tokens are ``forced`` instead
-    of the argmaxes (teacher forcing); the returned tokens are still the argmaxes.
+    of the generated ones (teacher forcing); the returned tokens are still the
+    generated ones. ``sampling`` = (temperature, top_k, seed, slot) samples each token
+    with orc_sample and the uniform of (seed, slot, position of the logits' row)
+    instead of taking the argmax.
     """
     V = model.shape.vocab
     cap = capacity or (len(prompt) + n_generate)
     s = model.new_seq(cap)
     logits = np.empty((n_generate, V), np.float32) if want_logits else None
     buf = np.empty(V, np.float32)
+    def pick(tok, pos):
+        if sampling is None:
+            return tok
+        temp, top_k, seed, slot = sampling
+        return sample(buf, temp, top_k, uniform(seed, slot, pos))
+
     tok = -1
+    keep = want_logits or sampling is not None
     for i, t in enumerate(prompt):
         last = i == len(prompt) - 1
-        tok = s.forward(int(t), buf if (last and want_logits) else None)
-    out: List[int] = [tok]
+        tok = s.forward(int(t), buf if (last and keep) else None)
+    out: List[int] = [pick(tok, len(prompt) - 1)]
     if want_logits:
         logits[0] = buf
     for i in range(1, n_generate):
         feed = out[-1] if forced is None else int(forced[i - 1])
-        tok = s.forward(feed, buf if want_logits else None)
+        tok = s.forward(feed, buf if keep else None)
         if tok < 0:
             raise RuntimeError(f"oracle forward failed rc={tok}")
-        out.append(tok)
+        out.append(pick(tok, len(prompt) + i - 1))
         if want_logits:
             logits[i] = buf
     return np.array(out, np.int32), logits

@@ -10,13 +10,17 @@
  *   [BF]   "batch_forge" README: component status table, the GELU/tanh paragraph,
  *          the KV-cache roadmap item.
  *   [RVM]  "rvllm Metal backend" post: "What the kernels do", "Things that were
- *          problematic", "How I know it's correct".
+ *          problematic", "How I know it's correct", "What's basic about it" and
+ *          "What's next" (the F32 KV cache and 1-byte Q8_0 weights as next steps).
+ *   [BF] status table also lists int8 dequantization and sampling (greedy,
+ *          temperature, top-k), and the temperature 0.7 demo.
  * Where the pages give no formula, the reading used is stated at the function.
  */
 #include "oracle.h"
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -31,12 +35,18 @@ static int g_mut = 0;
  *  7 GQA maps query head h to KV head h mod n_kv
  *  8 argmax ties go to the highest index
  *  9 stateless causal mask lets each row see one future position
- * 10 linear layers drop the bias                                                   */
+ * 10 linear layers drop the bias
+ * 11 bfloat16 rounding of K/V truncates instead of rounding to nearest even
+ * 12 8-bit quantization truncates toward zero instead of rounding
+ * 13 8-bit quantization scale max|x| / 128
+ * 14 sampling ignores the temperature
+ * 15 sampling keeps one candidate more than top_k                                   */
 void orc_set_mutation(int m) { g_mut = m; }
 
 struct orc_model {
   orc_config c;
   const float* w;
+  float* own;   /* weight_q8: the dequantized copy w points to */
   /* offsets (in floats) into w */
   size_t wte, wpe, lnf_g, lnf_b, rmsf, w_head;
   size_t* layer; /* n_layer entries: offset of the layer's first tensor */
@@ -61,6 +71,7 @@ static int cfg_ok(const orc_config* c) {
   } else {
     if (c->n_kv_head <= 0 || c->n_head % c->n_kv_head != 0 || (c->head_dim % 2) != 0) return 0;
   }
+  if (c->weight_q8 && (c->d_model % 32 || c->d_ff % 32 || (c->n_head * c->head_dim) % 32)) return 0;
   return 1;
 }
 
@@ -82,6 +93,20 @@ size_t orc_weight_count(const orc_config* c) {
   return n;
 }
 
+/* In place: every row of the [rows][cols] matrix at w replaced by the dequantization
+ * q * d of its 8-bit block quantization. */
+static void q8_matrix(float* w, size_t rows, int cols) {
+  signed char* q = (signed char*)malloc((size_t)cols);
+  float* d = (float*)malloc(sizeof(float) * (size_t)(cols / 32));
+  for (size_t r = 0; r < rows; ++r) {
+    float* x = w + r * (size_t)cols;
+    orc_quantize_q8(x, cols, q, d);
+    for (int i = 0; i < cols; ++i) x[i] = (float)q[i] * d[i / 32];
+  }
+  free(q);
+  free(d);
+}
+
 orc_model* orc_model_create(const orc_config* c, const float* w, size_t n) {
   if (!cfg_ok(c) || !w || n != orc_weight_count(c)) return NULL;
   orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
@@ -100,11 +125,44 @@ orc_model* orc_model_create(const orc_config* c, const float* w, size_t n) {
     m->rmsf = off; off += d;
     m->w_head = off; off += V * d;
   }
+  if (c->weight_q8) {
+    /* every weight matrix (embeddings and head included) through the 8-bit blocks of
+     * its rows; norm parameters and biases stay float */
+    m->own = (float*)malloc(sizeof(float) * n);
+    if (!m->own) { orc_model_free(m); return NULL; }
+    memcpy(m->own, w, sizeof(float) * n);
+    m->w = m->own;
+    size_t ff = (size_t)c->d_ff, hq = (size_t)c->n_head * c->head_dim, hk = (size_t)c->n_kv_head * c->head_dim;
+    q8_matrix(m->own + m->wte, V, (int)d);
+    if (c->arch == ORC_ARCH_GPT2) {
+      q8_matrix(m->own + m->wpe, (size_t)c->n_ctx, (int)d);
+      for (int l = 0; l < c->n_layer; ++l) {
+        float* p = m->own + m->layer[l] + 2 * d;   /* after ln1_g, ln1_b */
+        q8_matrix(p, 3 * d, (int)d); p += 3 * d * d + 3 * d;
+        q8_matrix(p, d, (int)d); p += d * d + d + 2 * d;
+        q8_matrix(p, ff, (int)d); p += ff * d + ff;
+        q8_matrix(p, d, (int)ff);
+      }
+    } else {
+      for (int l = 0; l < c->n_layer; ++l) {
+        float* p = m->own + m->layer[l] + d;       /* after rms1 */
+        q8_matrix(p, hq, (int)d); p += hq * d;
+        q8_matrix(p, hk, (int)d); p += hk * d;
+        q8_matrix(p, hk, (int)d); p += hk * d;
+        q8_matrix(p, d, (int)hq); p += d * hq + d;
+        q8_matrix(p, ff, (int)d); p += ff * d;
+        q8_matrix(p, ff, (int)d); p += ff * d;
+        q8_matrix(p, d, (int)ff);
+      }
+      q8_matrix(m->own + m->w_head, V, (int)d);
+    }
+  }
   return m;
 }
 
 void orc_model_free(orc_model* m) {
   if (!m) return;
+  free(m->own);
   free(m->layer);
   free(m);
 }
@@ -262,6 +320,119 @@ int orc_argmax(const float* v, int n) {
   return n > 0 ? best : -1;
 }
 
+/* bfloat16 keeps the top 16 bits of a float. Rounding to nearest, ties to even, on the
+ * bit pattern: add 0x7fff plus the lowest kept bit, then clear the low 16 bits (the
+ * carry may round up into the exponent, which is the correct result up to infinity).
+ * [RVM] "What's basic about it" names the F32 KV cache as the basic choice; the
+ * 16-bit cache is the reading of the half-size KV step. */
+float orc_round_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return x;   /* NaN */
+  if (g_mut == 11) u &= 0xffff0000u;
+  else u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+  float y;
+  memcpy(&y, &u, 4);
+  return y;
+}
+
+/* 8-bit blocks as in the Q8_0 format [RVM] names ("What's basic about it": one byte
+ * per weight; [BF] status table: int8 dequantization): per block of 32 values, the
+ * scale d = max|x| / 127 and q = round(x / d), evaluated as x * (1 / d) in float and
+ * rounded half away from zero; d is kept as a float. */
+void orc_quantize_q8(const float* x, int n, signed char* q, float* d) {
+  for (int b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      float a = fabsf(xb[i]);
+      if (a > amax) amax = a;
+    }
+    float db = amax / (g_mut == 13 ? 128.0f : 127.0f);
+    float id = db != 0.0f ? 1.0f / db : 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      float t = xb[i] * id;
+      float r = (g_mut == 12) ? truncf(t) : roundf(t);
+      q[32 * b + i] = (signed char)r;
+    }
+    d[b] = db;
+  }
+}
+
+/* Philox4x64-10 (Salmon, Moraes, Dror, Shaw: "Parallel random numbers: as easy as 1, 2,
+ * 3", SC 2011): ten rounds of two 64 x 64 -> 128-bit products of counter words with
+ * the round multipliers, the high halves xored with the other counter words and the
+ * key, the key advanced by the Weyl increments after each round. */
+void orc_philox4x64(const unsigned long long ctr[4], const unsigned long long key[2], unsigned long long out[4]) {
+  const unsigned long long M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const unsigned long long W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  unsigned long long c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
+    unsigned long long hi0 = (unsigned long long)(p0 >> 64), lo0 = (unsigned long long)p0;
+    unsigned long long hi1 = (unsigned long long)(p1 >> 64), lo1 = (unsigned long long)p1;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+double orc_uniform(unsigned long long seed, int seq, int pos) {
+  unsigned long long ctr[4] = {(unsigned long long)pos, (unsigned long long)seq, 0, 0}, key[2] = {seed, 0};
+  unsigned long long out[4];
+  orc_philox4x64(ctr, key, out);
+  return (double)(out[0] >> 40) * (1.0 / 16777216.0);
+}
+
+static const float* g_sort_keys;
+/* descending logit, ties to the lower index */
+static int by_logit_desc(const void* a, const void* b) {
+  int i = *(const int*)a, j = *(const int*)b;
+  float x = g_sort_keys[i], y = g_sort_keys[j];
+  if (x > y) return -1;
+  if (x < y) return 1;
+  return i < j ? -1 : (i > j);
+}
+
+/* [BF] status table: sampling by greedy, temperature and top-k ("--temperature 0.7" in
+ * its demo). The pages print no rule; the reading: keep the top_k largest logits
+ * (ties to the lower index), weight them by exp((l - l_max) / temperature) and return
+ * the first candidate, in that order, whose cumulative weight exceeds u times the
+ * total. */
+int orc_sample(const float* logits, int n, double temperature, int top_k, double u) {
+  if (n <= 0) return -1;
+  for (int i = 0; i < n; ++i)
+    if (isnan(logits[i])) return i;
+  if (temperature <= 0.0 || top_k == 1) return orc_argmax(logits, n);
+  int k = (top_k <= 0 || top_k > n) ? n : top_k;
+  if (g_mut == 15 && k < n) k += 1;
+  int* idx = (int*)malloc(sizeof(int) * (size_t)n);
+  for (int i = 0; i < n; ++i) idx[i] = i;
+  g_sort_keys = logits;
+  qsort(idx, (size_t)n, sizeof(int), by_logit_desc);
+  double t = (g_mut == 14) ? 1.0 : temperature;
+  double top = (double)logits[idx[0]];
+  double* w = (double*)malloc(sizeof(double) * (size_t)k);
+  double total = 0.0;
+  for (int r = 0; r < k; ++r) {
+    w[r] = exp(((double)logits[idx[r]] - top) / t);
+    total += w[r];
+  }
+  double target = u * total, cum = 0.0;
+  int pick = idx[k - 1];
+  for (int r = 0; r < k; ++r) {
+    cum += w[r];
+    if (target < cum) { pick = idx[r]; break; }
+  }
+  free(w);
+  free(idx);
+  return pick;
+}
+
 /* ---------------------------------------------------------- layer tensors */
 
 typedef struct {
@@ -378,11 +549,15 @@ int orc_forward(const orc_model* m, orc_seq* s, int token, float* logits_out) {
       for (int h = 0; h < H; ++h) orc_rope(q + h * hd, hd, p, c->rope_theta);
       for (int h = 0; h < Hk; ++h) orc_rope(k + h * hd, hd, p, c->rope_theta);
     }
-    /* append this position's K and V: [BML] "What got built" (a real KV cache) */
+    /* append this position's K and V: [BML] "What got built" (a real KV cache); with
+     * kv_bf16 the cache holds them rounded to bfloat16 */
     for (int h = 0; h < Hk; ++h) {
       size_t base = (((size_t)l * Hk + h) * s->cap + p) * hd;
-      memcpy(s->K + base, k + h * hd, sizeof(float) * (size_t)hd);
-      memcpy(s->V + base, v + h * hd, sizeof(float) * (size_t)hd);
+      for (int i = 0; i < hd; ++i) {
+        float kk = k[h * hd + i], vv = v[h * hd + i];
+        s->K[base + i] = c->kv_bf16 ? orc_round_bf16(kk) : kk;
+        s->V[base + i] = c->kv_bf16 ? orc_round_bf16(vv) : vv;
+      }
     }
     int T = (g_mut == 5) ? p : p + 1;
     for (int h = 0; h < H; ++h) {
@@ -477,6 +652,9 @@ int orc_forward_stateless(const orc_model* m, const int* tokens, int T, float* l
         for (int h = 0; h < H; ++h) orc_rope(qr + h * hd, hd, r, c->rope_theta);
         for (int h = 0; h < Hk; ++h) orc_rope(qr + qdim + h * hd, hd, r, c->rope_theta);
       }
+      /* the keys and values attention reads (bfloat16-rounded with kv_bf16) */
+      if (c->kv_bf16)
+        for (int i = qdim; i < wq; ++i) qr[i] = orc_round_bf16(qr[i]);
     }
     for (int h = 0; h < H; ++h) {
       int kh = (g_mut == 7) ? h % Hk : h / group;

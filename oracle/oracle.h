@@ -44,6 +44,10 @@ typedef struct {
   int n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab, n_ctx;
   double norm_eps;
   double rope_theta;
+  int kv_bf16;    /* 1: K and V are rounded to bfloat16 (nearest, ties to even) as they
+                   * enter the cache; attention reads the rounded values */
+  int weight_q8;  /* 1: every weight matrix is replaced by its 8-bit block quantization
+                   * (orc_quantize_q8 on each row's blocks of 32), dequantized to float */
 } orc_config;
 
 typedef struct orc_model orc_model;
@@ -85,6 +89,29 @@ void orc_linear(const float* x, const float* W, const float* b, int n_out, int n
 void orc_attend(const float* q, const float* K, const float* V, int T, int hd, int ld, float* o);
 /* Rotate-half RoPE of one head vector v[hd] at position pos (pairs i, i + hd/2). */
 void orc_rope(float* v, int hd, int pos, double theta);
+
+/* bfloat16 rounding of a float (nearest, ties to even; NaN stays NaN), returned as float. */
+float orc_round_bf16(float x);
+
+/* 8-bit block quantization of n values (n a multiple of 32), blocks of 32: scale
+ * d = max|x| / 127, q = round-half-away(x / d) in [-127, 127] (x * (1/d) in float),
+ * d = 0 and q = 0 for an all-zero block. Writes q[n] and d[n / 32]. */
+void orc_quantize_q8(const float* x, int n, signed char* q, float* d);
+
+/* Philox4x64-10 block of counter ctr[4] and key key[2] into out[4]. */
+void orc_philox4x64(const unsigned long long ctr[4], const unsigned long long key[2], unsigned long long out[4]);
+
+/* The uniform number in [0, 1) that drives sampling of the token after position pos of
+ * sequence slot seq: the top 24 bits of the first word of Philox4x64-10 with counter
+ * (pos, seq, 0, 0) and key (seed, 0), times 2^-24. */
+double orc_uniform(unsigned long long seed, int seq, int pos);
+
+/* Temperature / top-k sampling of one row of logits with the uniform u: the top_k
+ * largest logits (ties to the lower index; top_k <= 0 or > n: all), weights
+ * exp((l - l_max) / temperature), the first candidate in that order whose cumulative
+ * weight exceeds u times the total. temperature <= 0 or top_k == 1: the greedy argmax.
+ * A NaN among the logits gives the first NaN's index. */
+int orc_sample(const float* logits, int n, double temperature, int top_k, double u);
 
 /* Planted mistakes for mutation tests of the pins (0 = none). See oracle.c. */
 void orc_set_mutation(int m);

@@ -19,6 +19,11 @@ Workloads (sizes as named by the model shapes they stand in for):
                    SiLU-gated MLP 2560, RMSNorm, RoPE theta 1e5, vocab 49152, untied
                    head, bf16 weights; paged KV (block 16, shuffled tables); batch 8,
                    prompt lengths uniform in [32, 1024], 256 generated tokens.
+* ``gpt2_b32_kv16`` the batch-32 GPT-2 workload with a bfloat16 KV cache.
+* ``llama_long``   the Llama-style shape at n_ctx 4096 with a bfloat16 paged KV cache:
+                   batch 4, prompt lengths uniform in [1536, 3840], 128 generated.
+* ``gpt2_b1_q8``   the batch-1 GPT-2 workload with 8-bit block-quantized weights.
+* ``gpt2_b1_sample`` the batch-1 GPT-2 workload sampled at temperature 0.7, top-k 40.
 
 Draw rules: ``numpy.random.default_rng(seed)`` (PCG64) for weights, drawn in the
 canonical tensor order below with ``standard_normal(dtype=float32) * sigma``;
@@ -72,6 +77,8 @@ class Init:
     resid_sigma: Optional[float] = None   # sigma of w_o / w_proj (GPT-2 residual scaling)
     fc_sigma: Optional[float] = None      # sigma of w_fc (activation-stress init)
     bf16: bool = False                    # weight matrices rounded to bf16 (RNE)
+    q8: bool = False                      # weight matrices in 8-bit blocks of 32 (quantized by each side)
+    kv_bf16: bool = False                 # K and V rounded to bf16 as they enter the cache
 
 
 @dataclasses.dataclass(frozen=True)
@@ -84,16 +91,18 @@ class Workload:
     prompt_len: Tuple[int, int]           # closed range [lo, hi]; lo == hi means fixed
     n_generate: int                       # generated tokens per sequence (argmax count)
     kv_block: int = 0                     # 0: contiguous per-sequence cache; else paged
+    sampling: Optional[Tuple[float, int, int]] = None   # (temperature, top_k, seed); None: greedy
 
     @property
     def weight_dtype(self) -> str:
-        return "bf16" if self.init.bf16 else "f32"
+        return "bf16" if self.init.bf16 else ("q8" if self.init.q8 else "f32")
 
 
 GPT2_124M = Shape(ARCH_GPT2, 12, 768, 12, 12, 64, 3072, 50257, 1024)
 TINY = Shape(ARCH_GPT2, 2, 64, 4, 4, 16, 256, 512, 64)
 # n_ctx of the Llama-style shape: longest prompt (1024) plus 256 generated tokens.
 LLAMA_360M = Shape(ARCH_LLAMA, 32, 960, 15, 5, 64, 2560, 49152, 1280, 1e-5, 1e5)
+LLAMA_360M_4K = Shape(ARCH_LLAMA, 32, 960, 15, 5, 64, 2560, 49152, 4096, 1e-5, 1e5)
 
 _RESID = 0.02 / math.sqrt(24.0)
 
@@ -106,6 +115,13 @@ WORKLOADS: Dict[str, Workload] = {
     "gpt2_b32_bf16": Workload("gpt2_b32_bf16", GPT2_124M, Init(resid_sigma=_RESID, bf16=True), 4, 32,
                               (16, 512), 256),
     "llama_b8": Workload("llama_b8", LLAMA_360M, Init(bf16=True), 5, 8, (32, 1024), 256, kv_block=16),
+    "gpt2_b32_kv16": Workload("gpt2_b32_kv16", GPT2_124M, Init(resid_sigma=_RESID, kv_bf16=True), 4, 32,
+                              (16, 512), 256),
+    "llama_long": Workload("llama_long", LLAMA_360M_4K, Init(bf16=True, kv_bf16=True), 6, 4, (1536, 3840), 128,
+                           kv_block=16),
+    "gpt2_b1_q8": Workload("gpt2_b1_q8", GPT2_124M, Init(resid_sigma=_RESID, q8=True), 2, 1, (8, 8), 128),
+    "gpt2_b1_sample": Workload("gpt2_b1_sample", GPT2_124M, Init(resid_sigma=_RESID), 2, 1, (8, 8), 128,
+                               sampling=(0.7, 40, 2024)),
 }
 
 

@@ -36,7 +36,7 @@ import synth  # noqa: E402
 TOPK = 8
 NPROBE = 24
 FULL_SEQ_STEPS = 3
-WORKLOADS = ["gpt2_stress", "gpt2_b32", "gpt2_b32_bf16", "llama_b8"]
+WORKLOADS = ["gpt2_stress", "gpt2_b32", "gpt2_b32_bf16", "llama_b8", "gpt2_b32_kv16", "llama_long"]
 
 _W = None
 
@@ -51,7 +51,7 @@ def _one(args):
     b, prompt, probe, full_steps = args
     w, W = _W
     t0 = time.time()
-    m = oracle.Model(w.shape, W)
+    m = oracle.for_workload(w, W)
     toks, lg = oracle.generate(m, prompt, w.n_generate, want_logits=True)
     order = np.argsort(-lg.astype(np.float64), axis=1, kind="stable")[:, :TOPK]
     top_val = np.take_along_axis(lg, order, axis=1)

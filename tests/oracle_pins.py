@@ -352,8 +352,136 @@ def check_llama_block_closed_forms():
         assert np.max(np.abs(buf - ref)) < 2e-5, t
 
 
+def check_round_bf16():
+    """bfloat16 rounding (nearest, ties to even) against torch's float32 -> bfloat16
+    conversion, a library routine the oracle does not use."""
+    import torch
+    vals = [0.0, -0.0, 1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -7, -1.0 - 2.0 ** -8, 3.39e38, 3.4e38,
+            1e-40, -1e-40, 6e-39, 65504.0, 1.0 / 3.0]
+    x = np.concatenate([np.array(vals, np.float32)] +
+                       [(RNG.standard_normal(4000) * s).astype(np.float32) for s in (1e-3, 1.0, 1e3, 1e30)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = oracle.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(oracle.round_bf16(np.array([np.nan], np.float32))[0])
+
+
+def check_kv_bf16_model():
+    """With the bfloat16 KV cache: the cached path equals the stateless matrix form (both
+    read rounded K and V), K/V that are exactly zero make it equal the float cache, and
+    random K/V make it differ (the rounding is applied)."""
+    for shape, seed in ((_tiny_gpt2(), 31), (_tiny_llama(), 32)):
+        W = synth.make_weights(shape, synth.Init(), seed)
+        m = oracle.Model(shape, W, kv_bf16=True)
+        m32 = oracle.Model(shape, W)
+        toks = np.random.default_rng(seed).integers(0, shape.vocab, size=16).astype(np.int32)
+        st = m.stateless(toks)
+        s = m.new_seq(32)
+        buf = np.empty(shape.vocab, np.float32)
+        for i, t in enumerate(toks):
+            s.forward(int(t), buf)
+            assert np.max(np.abs(buf - st[i])) < 1e-5, (shape.arch, i)
+        assert np.max(np.abs(m32.stateless(toks) - st)) > 1e-6
+    sh = _tiny_gpt2()
+    W = synth.make_weights(sh, synth.Init(), 33)
+    off = synth.offsets(sh)
+    d = sh.d_model
+    for l in range(sh.n_layer):
+        o, _ = off[f"h{l}.w_qkv"]
+        W[o + d * d:o + 3 * d * d] = 0.0   # k and v rows (their biases are zero)
+    toks = [3, 9, 27, 81]
+    assert np.array_equal(oracle.Model(sh, W, kv_bf16=True).stateless(toks), oracle.Model(sh, W).stateless(toks))
+
+
+def check_quantize_q8():
+    """8-bit blocks of 32: codes in [-127, 127], the largest magnitude of a block at 127,
+    reconstruction within half a step, exact for values that are codes times a power of
+    two, sign symmetry, all-zero blocks."""
+    for sc in (1e-3, 0.02, 1.0, 50.0):
+        x = (RNG.standard_normal(32 * 64) * sc).astype(np.float32)
+        q, d = oracle.quantize_q8(x)
+        assert q.min() >= -127 and q.max() <= 127
+        qb = q.reshape(-1, 32).astype(np.int32)
+        assert np.all(np.abs(qb).max(axis=1) == 127)
+        err = np.abs(x.reshape(-1, 32).astype(np.float64) - qb * d[:, None].astype(np.float64))
+        assert np.all(err <= 0.5 * d[:, None] * (1 + 1e-5) + 1e-12)
+        q2, d2 = oracle.quantize_q8(-x)
+        assert np.array_equal(q2, -q) and np.array_equal(d2, d)
+    codes = RNG.integers(-127, 128, size=(8, 32)).astype(np.int32)
+    codes[:, 5] = 127
+    scale = 2.0 ** RNG.integers(-12, 4, size=8).astype(np.float64)
+    x = (codes * scale[:, None]).astype(np.float32)
+    q, d = oracle.quantize_q8(x)
+    assert np.array_equal(q.reshape(8, 32), codes) and np.array_equal(d, scale.astype(np.float32))
+    q, d = oracle.quantize_q8(np.zeros(64, np.float32))
+    assert not q.any() and not d.any()
+
+
+def check_q8_model():
+    """The 8-bit model equals the float model run on weights whose every matrix (and
+    only the matrices) is replaced row by row, block by block, by its dequantization."""
+    for shape, seed in ((_tiny_gpt2(), 41), (_tiny_llama(d=64, H=8, Hk=2, hd=8, ff=96), 42)):
+        W = synth.make_weights(shape, synth.Init(), seed)
+        Wd = W.copy()
+        off = 0
+        for name, shp, kind in synth.tensor_list(shape):
+            n = int(np.prod(shp))
+            if kind == "w":
+                rows = W[off:off + n].reshape(shp)
+                q, d = oracle.quantize_q8(rows)
+                Wd[off:off + n] = (q.astype(np.float32).reshape(-1, 32) * d[:, None]).reshape(-1)
+            off += n
+        toks = [1, 17, 200, 42, 7]
+        a = oracle.Model(shape, W, weight_q8=True).stateless(toks)
+        b = oracle.Model(shape, Wd).stateless(toks)
+        assert np.array_equal(a, b)
+        assert np.max(np.abs(a - oracle.Model(shape, W).stateless(toks))) > 1e-6
+
+
+def check_sampling():
+    """Philox4x64-10 against numpy's implementation (which advances the counter before a
+    block); the sampling rule against scipy's softmax of the top-k logits over a fine
+    grid of uniforms; its greedy special cases."""
+    from scipy.special import softmax
+    for key, ctr in (((0, 0), (0, 0, 0, 0)), ((7, 0), (1022, 31, 0, 0)), ((2 ** 63 + 5, 3), (2 ** 40, 9, 8, 7))):
+        bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                              counter=np.array([ctr[0] - 1 if ctr[0] else 2 ** 64 - 1, ctr[1], ctr[2], ctr[3]]
+                                               if ctr[0] else [2 ** 64 - 1, (ctr[1] - 1) % 2 ** 64, ctr[2], ctr[3]],
+                                               dtype=np.uint64))
+        want = [int(v) for v in bg.random_raw(4)]
+        if ctr[0] == 0 and ctr[1] == 0:
+            # the block before (0, 0, 0, 0) wraps words 0 and 1 and borrows from word 2
+            bg = np.random.Philox(key=np.array(key, dtype=np.uint64),
+                                  counter=np.array([2 ** 64 - 1, 2 ** 64 - 1, 2 ** 64 - 1, 2 ** 64 - 1], dtype=np.uint64))
+            want = [int(v) for v in bg.random_raw(4)]
+        assert oracle.philox4x64(ctr, key) == want, (ctr, key)
+    for seed, seq, pos in ((0, 0, 0), (12345, 3, 511), (2 ** 40 + 1, 31, 1023)):
+        bg = np.random.Philox(key=np.array([seed, 0], dtype=np.uint64),
+                              counter=np.array([pos - 1 if pos else 2 ** 64 - 1, seq if pos else seq - 1, 0, 0]
+                                               if (pos or seq) else [2 ** 64 - 1] * 4, dtype=np.uint64))
+        w0 = int(bg.random_raw(1)[0])
+        assert oracle.uniform(seed, seq, pos) == (w0 >> 40) / 2.0 ** 24
+    logits = (RNG.standard_normal(12) * 2).astype(np.float32)
+    order = sorted(range(12), key=lambda i: (-float(logits[i]), i))
+    assert oracle.sample(logits, 0.7, 1, 0.9) == order[0]
+    assert oracle.sample(logits, 0.0, 5, 0.9) == order[0]
+    assert oracle.sample(logits, 0.7, 5, 0.0) == order[0]
+    for T, k in ((0.7, 4), (1.3, 0), (0.25, 12), (2.0, 7)):
+        kk = 12 if k == 0 else k
+        p = softmax(logits[order[:kk]].astype(np.float64) / T)
+        n = 20000
+        picks = np.array([oracle.sample(logits, T, k, (i + 0.5) / n) for i in range(n)])
+        assert set(picks.tolist()) <= set(order[:kk])
+        freq = np.array([np.mean(picks == order[r]) for r in range(kk)])
+        assert np.max(np.abs(freq - p)) <= 1.5 / n + 1e-9, (T, k)
+    tie = np.array([1.0, 1.0], np.float32)
+    assert oracle.sample(tie, 1.0, 0, 0.49) == 0 and oracle.sample(tie, 1.0, 0, 0.51) == 1
+    nan = np.array([0.0, np.nan, 5.0, np.nan], np.float32)
+    assert oracle.sample(nan, 1.0, 0, 0.3) == 1
+
+
 COMPONENT_CHECKS = [check_softmax, check_layernorm, check_rmsnorm, check_gelu, check_silu, check_linear,
-                    check_attention, check_rope, check_argmax]
+                    check_attention, check_rope, check_argmax, check_round_bf16, check_quantize_q8, check_sampling]
 MODEL_CHECKS = [check_cached_equals_stateless, check_zero_layers_closed_form, check_gpt2_block_closed_forms,
-                check_llama_block_closed_forms]
+                check_llama_block_closed_forms, check_kv_bf16_model, check_q8_model]
 ALL_CHECKS = COMPONENT_CHECKS + MODEL_CHECKS

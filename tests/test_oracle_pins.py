@@ -27,6 +27,11 @@ MUTATIONS = {
     8: "argmax ties to highest index",
     9: "stateless mask leaks one future position",
     10: "linear drops the bias",
+    11: "bfloat16 K/V rounding truncates",
+    12: "8-bit quantization truncates",
+    13: "8-bit quantization scale max/128",
+    14: "sampling ignores the temperature",
+    15: "sampling keeps top_k + 1 candidates",
 }
 
 
