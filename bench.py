@@ -56,7 +56,7 @@ def setup(wname: str):
     w = synth.WORKLOADS[wname]
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
-    kw = dict(max_seqs=w.batch, max_batch=w.batch)
+    kw = dict(max_seqs=w.batch, max_batch=w.batch, kv_dtype=gd.KV_BF16 if w.init.kv_bf16 else gd.KV_F32)
     tables = None
     if w.kv_block:
         tables, pool = synth.make_block_tables(w, prompts)
@@ -297,7 +297,7 @@ def oracle_sample(wname: str):
     prompts = synth.make_prompts(w)
     b = _shortest(w, prompts)
     n = CPU_SAMPLE_FORWARDS[wname] or (w.n_generate - 1)
-    om = oracle.Model(w.shape, W)
+    om = oracle.for_workload(w, W)
     s = om.new_seq(len(prompts[b]) + w.n_generate)
     t0 = time.perf_counter()
     tok = -1

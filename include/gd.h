@@ -30,8 +30,9 @@
  *   - Errors: every call returns a gd_status; gd_last_error() gives a message for
  *     the calling thread. A HIP failure poisons the model: every later call on it
  *     returns GD_ERR_HIP. A model is not thread-safe.
- *   - Activations, accumulation and the KV cache are float32. Weight matrices are
- *     stored float32 or bfloat16 (weight_dtype); norm parameters and biases float32.
+ *   - Activations and accumulation are float32; the KV cache float32 or bfloat16
+ *     (kv_dtype). Weight matrices are stored float32 or bfloat16 (weight_dtype); norm
+ *     parameters and biases float32.
  */
 #ifndef GD_H
 #define GD_H
@@ -59,6 +60,12 @@ typedef enum {
 #define GD_WEIGHT_F32 0
 #define GD_WEIGHT_BF16 1
 
+#define GD_KV_F32 0   /* the KV cache holds float32 */
+#define GD_KV_BF16 1  /* K and V are rounded to bfloat16 (nearest, ties to even) as they enter
+                       * the cache and widened to float32 when attention reads them: half the
+                       * cache bytes ("rvllm Metal backend", "What's basic about it": the F32
+                       * KV cache as the basic choice) */
+
 typedef struct {
   int32_t arch;           /* GD_ARCH_* */
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab;   /* d_model, d_ff: multiples of 8, <= 2^20 */
@@ -70,6 +77,7 @@ typedef struct {
   int32_t max_batch;      /* rows of one decode step (<= 32) */
   int32_t kv_block_size;  /* 0: contiguous cache, n_ctx positions per slot; else paged */
   int32_t kv_num_blocks;  /* paged: blocks in the pool */
+  int32_t kv_dtype;       /* GD_KV_* */
 } gd_config;
 
 typedef struct gd_model gd_model;

@@ -19,7 +19,8 @@ def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, varia
              chunks=0):
     import transformer_gpt_decode_amd as gd
     s = workload.shape
-    kw = dict(max_seqs=max_seqs or workload.batch, max_batch=max_batch or workload.batch)
+    kw = dict(max_seqs=max_seqs or workload.batch, max_batch=max_batch or workload.batch,
+              kv_dtype=gd.KV_BF16 if workload.init.kv_bf16 else gd.KV_F32)
     if workload.kv_block:
         kw.update(kv_block_size=workload.kv_block, kv_num_blocks=pool_blocks)
     m = gd.Model.from_shape(s, gd.WEIGHT_BF16 if workload.init.bf16 else gd.WEIGHT_F32, **kw)
@@ -93,11 +94,13 @@ def gpu_generate(m, prompts, n_generate, tables=None, want_logits=True, forced=N
 
 
 def oracle_generate(workload, W, prompts, n_generate=None, forced=None):
-    om = oracle.Model(workload.shape, W)
+    om = oracle.for_workload(workload, W)
     n = n_generate or workload.n_generate
     toks, lgs = [], []
     for b, p in enumerate(prompts):
-        t, lg = oracle.generate(om, p, n, want_logits=True, forced=None if forced is None else forced[b])
+        smp = None if workload.sampling is None else (*workload.sampling[:2], workload.sampling[2], b)
+        t, lg = oracle.generate(om, p, n, want_logits=True, forced=None if forced is None else forced[b],
+                                sampling=smp)
         toks.append(t)
         lgs.append(lg)
     return np.stack(toks), np.stack(lgs)

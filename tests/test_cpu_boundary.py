@@ -43,14 +43,14 @@ def test_library_carries_gfx950_code_object(tmp_path):
 def _cfg(**kw):
     base = dict(arch=0, n_layer=2, d_model=64, n_head=4, n_kv_head=4, head_dim=16, d_ff=256, vocab=512, n_ctx=64,
                 norm_eps=1e-5, rope_theta=0.0, weight_dtype=0, max_seqs=1, max_batch=1, kv_block_size=0,
-                kv_num_blocks=0)
+                kv_num_blocks=0, kv_dtype=0)
     base.update(kw)
     return gd.GdConfig(**base)
 
 
 @pytest.mark.parametrize("bad", [dict(arch=7), dict(head_dim=32, d_model=128), dict(max_batch=33),
                                  dict(n_kv_head=2), dict(weight_dtype=3), dict(norm_eps=0.0),
-                                 dict(d_model=60, head_dim=15)])
+                                 dict(d_model=60, head_dim=15), dict(kv_dtype=2)])
 def test_create_rejects_bad_config(bad):
     h = ctypes.c_void_p()
     st = gd.lib().gd_create(ctypes.byref(_cfg(**bad)), None, ctypes.byref(h))

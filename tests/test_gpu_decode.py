@@ -68,16 +68,21 @@ def test_tiny_llama_paged(shuffled):
     _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool)
 
 
-@pytest.mark.parametrize("batch", [2, 6], ids=["fused_attn_o", "split_context"])
-def test_llama_hd64_gqa_paged(batch):
-    """Up to 4 rows at contexts of at most 256 positions run attention fused with the
-    output projection; more rows run split-context attention, a merge and the MFMA
-    projection. Both at head_dim 64, 3 query heads per KV head, paged, bf16 weights."""
-    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 11, batch, (5, 60), 10, kv_block=16)
+@pytest.mark.parametrize("mode", ["fused_attn_o", "gemv_split_context", "mfma_split_context"])
+def test_llama_hd64_gqa_paged(mode):
+    """head_dim 64, 3 query heads per KV head, paged, bf16 weights. Rows at contexts of at
+    most 256 positions whose projections run on the GEMV take attention fused with the
+    output projection; with the GEMV forced, 8 rows at 250-310 positions run
+    split-context attention whose partials the GEMV projection (two launches of 4 rows)
+    merges in its prologue; with the MFMA forced, a merge launch and the MFMA projection
+    follow the split-context attention."""
+    batch, plen, variant = {"fused_attn_o": (2, (5, 60), 0), "gemv_split_context": (8, (250, 300), 1),
+                            "mfma_split_context": (6, (5, 60), 2)}[mode]
+    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 11, batch, plen, 10, kv_block=16)
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
     tab, pool = synth.make_block_tables(w, prompts)
-    _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool)
+    _run_and_compare(w, W, prompts, 2e-2, variant=variant, tables=tab, pool=pool, config=f"llama_hd64 ({mode})")
 
 
 def test_llama_hd64_gqa_paged_one_chunk():
@@ -304,3 +309,57 @@ def test_gpt2_124m_prenorm_outlier_rows(outlier, mean, fold):
                                  config=f"gpt2_b1 pre-norm rows (outlier {outlier:g}, mean {mean:g}, "
                                         f"{'folded' if fold else 'applied'})")
     assert not rep["flips"], rep["flips"]
+
+
+# ------------------------------------------------------------- bfloat16 KV cache
+
+@pytest.mark.parametrize("variant", [0, 2], ids=["auto", "mfma"])
+def test_tiny_gpt2_kv_bf16(variant):
+    """K and V rounded to bf16 as they enter the cache (the oracle rounds the same
+    values): contiguous cache, GEMV and MFMA QKV epilogues, fused and split attention."""
+    w = synth.Workload("tiny_kv16", synth.TINY, synth.Init(kv_bf16=True), 1, 4, (1, 40), 16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 2e-2, variant, config=f"tiny kv bf16 (variant {variant})")
+    assert not rep["flips"]
+
+
+@pytest.mark.parametrize("mode", ["fused_attn_o", "one_chunk", "eight_chunks"])
+def test_llama_hd64_kv_bf16_paged(mode):
+    """bf16 KV on a shuffled paged cache with 3 query heads per KV head: the fused
+    short-context attention, and split-context attention with one or eight chunks."""
+    batch, plen, variant, chunks = {"fused_attn_o": (2, (5, 60), 0, 0), "one_chunk": (6, (5, 200), 2, 1),
+                                    "eight_chunks": (6, (5, 200), 2, 8)}[mode]
+    w = synth.Workload("llama_hd64_kv16", LLAMA_HD64, synth.Init(bf16=True, kv_bf16=True), 15, batch, plen, 10,
+                       kv_block=16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    _run_and_compare(w, W, prompts, 2e-2, variant=variant, tables=tab, pool=pool, chunks=chunks,
+                     config=f"llama_hd64 kv bf16 ({mode})")
+
+
+@pytest.mark.parametrize("chunks", [1, 8], ids=["one_chunk", "eight_chunks"])
+def test_long_contexts_kv_bf16(chunks):
+    """bf16 KV at ragged contexts up to ~900 positions on the contiguous cache, the
+    one-chunk attention fused with the output projection and the eight-chunk scan."""
+    w = synth.Workload("gpt2_hd64_long_kv16", GPT2_HD64_LONG, synth.Init(kv_bf16=True), 16, 5, (1, 880), 6)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    _run_and_compare(w, W, prompts, 2e-2, variant=2, chunks=chunks, config=f"gpt2_hd64_long kv bf16 ({chunks} chunks)")
+
+
+# A small Llama-style model with contexts far past 1280 positions
+LLAMA_LONG_SMALL = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 4096, 1e-5, 1e5)
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_llama_contexts_past_1280(kv):
+    """Split-context paged attention at 1300-3800 positions (n_ctx 4096), float or bf16
+    KV, shuffled block tables; the rows at different lengths share each step."""
+    w = synth.Workload("llama_long_small", LLAMA_LONG_SMALL, synth.Init(bf16=True, kv_bf16=kv == "bf16"), 17, 2,
+                       (1300, 3800), 6, kv_block=16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool, config=f"llama long contexts ({kv} KV)")

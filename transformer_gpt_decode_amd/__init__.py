@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgptdecode.so")
 GD_OK, GD_ERR_INVALID, GD_ERR_NO_DEVICE, GD_ERR_HIP, GD_ERR_OOM, GD_ERR_CTX_FULL, GD_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 ARCH_GPT2, ARCH_LLAMA = 0, 1
 WEIGHT_F32, WEIGHT_BF16 = 0, 1
+KV_F32, KV_BF16 = 0, 1
 OPT_LINEAR_VARIANT, OPT_USE_GRAPH, OPT_PROFILE, OPT_FUSE_ATTN_O = 1, 2, 3, 4
 OPT_FOLD_NORM, OPT_ATTN_CHUNKS = 7, 9
 NORM_NONE, NORM_LAYER, NORM_RMS = 0, 1, 2
@@ -43,7 +44,7 @@ class GdConfig(ctypes.Structure):
                 ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32), ("n_ctx", ctypes.c_int32),
                 ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("weight_dtype", ctypes.c_int32),
                 ("max_seqs", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("kv_block_size", ctypes.c_int32),
-                ("kv_num_blocks", ctypes.c_int32)]
+                ("kv_num_blocks", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
 
 
 class KernelStat(ctypes.Structure):
@@ -119,10 +120,10 @@ class Model:
     def __init__(self, arch: int, n_layer: int, d_model: int, n_head: int, n_kv_head: int, head_dim: int,
                  d_ff: int, vocab: int, n_ctx: int, norm_eps: float = 1e-5, rope_theta: float = 0.0,
                  weight_dtype: int = WEIGHT_F32, max_seqs: int = 1, max_batch: int = 1, kv_block_size: int = 0,
-                 kv_num_blocks: int = 0, stream=None):
+                 kv_num_blocks: int = 0, kv_dtype: int = KV_F32, stream=None):
         import torch
         self.cfg = GdConfig(arch, n_layer, d_model, n_head, n_kv_head, head_dim, d_ff, vocab, n_ctx, norm_eps,
-                            rope_theta, weight_dtype, max_seqs, max_batch, kv_block_size, kv_num_blocks)
+                            rope_theta, weight_dtype, max_seqs, max_batch, kv_block_size, kv_num_blocks, kv_dtype)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         h = _vp()
         _check(lib().gd_create(ctypes.byref(self.cfg), _stream_ptr(self.stream), ctypes.byref(h)))

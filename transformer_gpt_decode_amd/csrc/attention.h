@@ -27,7 +27,7 @@
 
 struct AttnParams {
   const float* q; int ldq;            // [M][ldq]; query head h at h*HD (post-RoPE)
-  const float* kc; const float* vc;   // this layer's pools [nblk][Hkv][B][HD]
+  const void* kc; const void* vc;     // this layer's pools [nblk][Hkv][B][HD]: float, or bf16 bits
   const int* table; int max_blocks;   // [slots][max_blocks] (paged)
   int block_size, nblk;
   int Hq, Hkv;
@@ -84,13 +84,34 @@ __device__ __forceinline__ AttnRow attn_row(const AttnParams& p, int row) {
 // Weight of a partial with max m in a merge whose max is mm (0 when both are -inf).
 __device__ __forceinline__ float attn_rescale(float m, float mm) { return mm == -INFINITY ? 0.f : expf(m - mm); }
 
+// Four consecutive cache elements at element offset e, widened to float: a 16-byte
+// load of a float cache or an 8-byte load of a bf16 cache (STREAM: non-temporal).
+template <bool KV16, bool STREAM>
+__device__ __forceinline__ f32x4 kv_load4(const void* base, size_t e) {
+  if constexpr (KV16) {
+    const uint2* p = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + e);
+    uint2 u;
+    if constexpr (STREAM) {
+      u.x = __builtin_nontemporal_load(&p->x);
+      u.y = __builtin_nontemporal_load(&p->y);
+    } else {
+      u = *p;
+    }
+    return (f32x4){bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + e);
+    if constexpr (STREAM) return __builtin_nontemporal_load(p);
+    return *p;
+  }
+}
+
 // Loads are unconditional (a position past the range is clamped to its last position,
 // an invalid cache block to block 0) and masked afterwards, so that the compiler keeps
 // them where they are issued instead of sinking them into branches.
 // STREAM: each K/V element is read by one workgroup of the launch, so the contiguous
 // loads carry the non-temporal hint (they then displace less of what other workgroups
 // share in L2: the output projection's weights, the query rows).
-template <int HD, int G, int PPG, bool PAGED, int NT = GD_WG, bool STREAM = false>
+template <int HD, int G, int PPG, bool PAGED, bool KV16, int NT = GD_WG, bool STREAM = false>
 __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0, int p1, const f32x4 (&q)[G],
                           AttnScanLds<HD, G, PPG, NT>& sh, float& m_out, float& l_out, float& o_out) {
   constexpr int LG = HD / 4;            // lanes per position group
@@ -101,15 +122,12 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
   const int grp = tid / LG, gl = tid % LG;
   const int pos = rm.pos;
 
-  const float* kbase = nullptr;
-  const float* vbase = nullptr;
+  size_t cbase = 0;   // contiguous: element offset of position 0 of this head (+ this lane's 4)
   const int* tab = nullptr;
   if (PAGED) {
     tab = p.table + (size_t)rm.seq * p.max_blocks;
   } else {
-    const long long base = rm.kvoff - (long long)pos * HD + (long long)kh * p.block_size * HD;
-    kbase = p.kc + base + gl * 4;
-    vbase = p.vc + base + gl * 4;
+    cbase = (size_t)(rm.kvoff - (long long)pos * HD + (long long)kh * p.block_size * HD) + gl * 4;
   }
 
   float mx[G], l[G];
@@ -132,18 +150,11 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
         const bool valid = (unsigned)blk < (unsigned)p.nblk;
         ok[j] = ok[j] && valid;
         off = (((size_t)(valid ? blk : 0) * p.Hkv + kh) * p.block_size + (ps - bi * p.block_size)) * HD + gl * 4;
-        kv[j] = *reinterpret_cast<const f32x4*>(p.kc + off);
-        vv[j] = *reinterpret_cast<const f32x4*>(p.vc + off);
+        kv[j] = kv_load4<KV16, false>(p.kc, off);
+        vv[j] = kv_load4<KV16, false>(p.vc, off);
       } else {
-        const f32x4* kp = reinterpret_cast<const f32x4*>(kbase + (size_t)ps * HD);
-        const f32x4* vp = reinterpret_cast<const f32x4*>(vbase + (size_t)ps * HD);
-        if constexpr (STREAM) {
-          kv[j] = __builtin_nontemporal_load(kp);
-          vv[j] = __builtin_nontemporal_load(vp);
-        } else {
-          kv[j] = *kp;
-          vv[j] = *vp;
-        }
+        kv[j] = kv_load4<KV16, STREAM>(p.kc, cbase + (size_t)ps * HD);
+        vv[j] = kv_load4<KV16, STREAM>(p.vc, cbase + (size_t)ps * HD);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // all of this step's loads go out before any arithmetic
@@ -266,7 +277,7 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
 
 // NT threads: 512 for one chunk per row, so that a long context scanned by one
 // workgroup keeps twice the positions in flight.
-template <int HD, int G, int PPG, bool PAGED, int NT>
+template <int HD, int G, int PPG, bool PAGED, int NT, bool KV16>
 __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
   __shared__ AttnScanLds<HD, G, PPG, NT> sh;
   const int c = blockIdx.x, kh = blockIdx.y, row = blockIdx.z;
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
   const int L = (T + C - 1) / C;
   const int p0 = min(T, c * L), p1 = min(T, p0 + L);
   float m, l, o;
-  attn_scan<HD, G, PPG, PAGED, NT, true>(p, rm, kh, p0, p1, q, sh, m, l, o);
+  attn_scan<HD, G, PPG, PAGED, KV16, NT, true>(p, rm, kh, p0, p1, q, sh, m, l, o);
   if (threadIdx.x < G * HD) {
     const int g = threadIdx.x / HD, d = threadIdx.x % HD;
     if (C == 1) {   // the whole context: l > 0 (the row's own position is in it)
@@ -311,7 +322,7 @@ template <int HD>
 struct AttnORows { static constexpr int LG = HD / 4, PER_PASS = GD_WG / LG, PASSES = HD == 64 ? 3 : 1,
                    ROWS = PER_PASS * PASSES; };
 
-template <int HD, int G, int PPG, bool PAGED, int WT>
+template <int HD, int G, int PPG, bool PAGED, int WT, bool KV16>
 __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_attn_o(AttnParams p, AttnOParams po) {
   using RT = AttnORows<HD>;
   __shared__ AttnScanLds<HD, G, PPG> sh;
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   f32x4 q[G];
   attn_load_q<HD, G>(p, row, kh, q);
   float m, l, o;
-  attn_scan<HD, G, PPG, PAGED>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
+  attn_scan<HD, G, PPG, PAGED, KV16>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
   if (tid < G * HD) s_o[tid / HD][tid % HD] = l > 0.f ? o / l : 0.f;
   __syncthreads();
   float acc[RT::PASSES];
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 // reads its weights in groups of HD/4 lanes per output (float4 or four bf16 each), NP
 // passes of NT / (HD/4) outputs, all issued at once after the scan; the sums go
 // through LDS so that every atomic is issued after the last wait.
-template <int HD, bool PAGED, int WT, int NT, int NP>
+template <int HD, bool PAGED, int WT, int NT, int NP, bool KV16>
 __global__ __launch_bounds__(NT) void k_attn_proj(AttnParams p, AttnOParams po) {
   constexpr int PPG = 4, LG = HD / 4, RPP = NT / LG;
   static_assert(HD == 64, "head_dim 64");
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(NT) void k_attn_proj(AttnParams p, AttnOParams po) 
   f32x4 q[1];
   attn_load_q<HD, 1>(p, row, kh, q);
   float m, l, o;
-  attn_scan<HD, 1, PPG, PAGED, NT, true>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
+  attn_scan<HD, 1, PPG, PAGED, KV16, NT, true>(p, rm, kh, 0, rm.pos + 1, q, sh, m, l, o);
   if (tid < HD) s_o[tid] = o / l;   // l > 0: the row's own position is in its context
   // this head's weight columns, every pass at once (clamped rows past N are never added)
   f32x4 wv[NP];

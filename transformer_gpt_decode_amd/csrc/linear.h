@@ -79,21 +79,25 @@ struct LinParams {
   float* logits; int ldl;
   int qdim, kdim, hd, kv_hstride;           // QKV: head g of a slot at + g * kv_hstride
   const float* rope_cs;                     // [M][hd]: each row's cos | sin of pair i (NULL: no RoPE)
-  float* kc; float* vc;
+  void* kc; void* vc;                       // K / V pools of the layer: float, or bf16 bits if kv16
+  int kv16;
 };
 
 // ------------------------------------------------------------ shared pieces
 
-// Destination of QKV output column n of row m: q columns go to y, k and v columns
-// into this layer's cache slot of the row (none if the slot is invalid).
-__device__ __forceinline__ float* qkv_dst(const LinParams& p, int m, int n, long long kvoff) {
-  if (n < p.qdim) return p.y + (size_t)m * p.ldy + n;
-  if (kvoff < 0) return nullptr;
+// Stores QKV output column n of row m: q columns go to y, k and v columns into this
+// layer's cache slot of the row (nothing if the slot is invalid), as float or, with a
+// bf16 cache, rounded to bf16.
+__device__ __forceinline__ void qkv_store(const LinParams& p, int m, int n, long long kvoff, float v) {
+  if (n < p.qdim) { p.y[(size_t)m * p.ldy + n] = v; return; }
+  if (kvoff < 0) return;
   int kn = n - p.qdim;
-  float* base = p.kc;
+  void* base = p.kc;
   if (kn >= p.kdim) { kn -= p.kdim; base = p.vc; }
   const int g = kn / p.hd, d = kn - g * p.hd;
-  return base + kvoff + (size_t)g * p.kv_hstride + d;
+  const size_t e = (size_t)kvoff + (size_t)g * p.kv_hstride + d;
+  if (p.kv16) reinterpret_cast<uint16_t*>(base)[e] = bf16_rne(v);
+  else reinterpret_cast<float*>(base)[e] = v;
 }
 
 template <int EPI>
@@ -154,11 +158,9 @@ __device__ __forceinline__ void epi_store(const LinParams& p, const EpiOps& e, i
         v0 = a * e.c - b * e.s;
         v1 = a * e.s + b * e.c;
       }
-      float* d1 = qkv_dst(p, m, n + 1, e.kvoff);
-      if (d1) *d1 = v1;
+      qkv_store(p, m, n + 1, e.kvoff, v1);
     }
-    float* d0 = qkv_dst(p, m, n, e.kvoff);
-    if (d0) *d0 = v0;
+    qkv_store(p, m, n, e.kvoff, v0);
   } else {
     v0 += e.b0;
     if (EPI == EPI_GELU) v0 = gelu_clamped(v0);

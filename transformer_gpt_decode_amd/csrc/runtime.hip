@@ -343,6 +343,8 @@ struct gd_model {
   int qdim, kdim, qkvdim, fcN, hdim, wt;
   int nblk, bsize, max_blocks;
   size_t elt;  // bytes per weight element
+  bool kv16 = false;   // the KV cache holds bf16 (GD_KV_BF16)
+  size_t kv_elt = 4;   // bytes per KV cache element
 
   // sizes
   size_t w_bytes = 0, kv_bytes = 0, s_bytes = 0;
@@ -351,7 +353,7 @@ struct gd_model {
 
   // bound memory
   char* w = nullptr;
-  float* kv = nullptr;
+  char* kv = nullptr;
   char* s = nullptr;
   bool bound = false, loaded = false;
 
@@ -395,9 +397,10 @@ struct gd_model {
   template <class T>
   const T* wp(size_t off) const { return reinterpret_cast<const T*>(w + off); }
   const float* wf(size_t off) const { return reinterpret_cast<const float*>(w + off); }
-  float* kpool(int l) const { return kv + (size_t)l * layer_kv_floats(); }
-  float* vpool(int l) const { return kv + (size_t)(c.n_layer + l) * layer_kv_floats(); }
-  size_t layer_kv_floats() const { return (size_t)nblk * c.n_kv_head * bsize * c.head_dim; }
+  // K pools of all layers, then V pools; elements of kv_elt bytes (float or bf16)
+  void* kpool(int l) const { return kv + (size_t)l * layer_kv_elems() * kv_elt; }
+  void* vpool(int l) const { return kv + (size_t)(c.n_layer + l) * layer_kv_elems() * kv_elt; }
+  size_t layer_kv_elems() const { return (size_t)nblk * c.n_kv_head * bsize * c.head_dim; }
 };
 
 static gd_status check_cfg(const gd_config* c) {
@@ -418,6 +421,7 @@ static gd_status check_cfg(const gd_config* c) {
   if ((c->n_head * c->head_dim) % 8) return set_err(GD_ERR_INVALID, "n_head*head_dim must be a multiple of 8");
   if (c->weight_dtype != GD_WEIGHT_F32 && c->weight_dtype != GD_WEIGHT_BF16)
     return set_err(GD_ERR_INVALID, "bad weight_dtype");
+  if (c->kv_dtype != GD_KV_F32 && c->kv_dtype != GD_KV_BF16) return set_err(GD_ERR_INVALID, "bad kv_dtype");
   if (c->max_seqs < 1 || c->max_batch < 1 || c->max_batch > GD_MAX_ROWS)
     return set_err(GD_ERR_INVALID, "max_seqs >= 1 and 1 <= max_batch <= 32 required");
   if (c->kv_block_size < 0 || (c->kv_block_size > 0 && c->kv_num_blocks < 1))
@@ -431,6 +435,8 @@ static void layout(gd_model* m) {
   const size_t d = c.d_model, ff = c.d_ff, V = c.vocab;
   m->wt = c.weight_dtype;
   m->elt = m->wt == GD_WEIGHT_F32 ? 4 : 2;
+  m->kv16 = c.kv_dtype == GD_KV_BF16;
+  m->kv_elt = m->kv16 ? 2 : 4;
   m->qdim = c.n_head * c.head_dim;
   m->kdim = c.n_kv_head * c.head_dim;
   m->qkvdim = m->qdim + 2 * m->kdim;
@@ -512,7 +518,7 @@ static void layout(gd_model* m) {
   m->w_bytes = off;
 
   // KV cache: K pools for all layers, then V pools
-  m->kv_bytes = 2 * (size_t)c.n_layer * m->layer_kv_floats() * sizeof(float);
+  m->kv_bytes = 2 * (size_t)c.n_layer * m->layer_kv_elems() * m->kv_elt;
 
   // argmax partials: the head's widest grid over both kernels
   m->am_parts = 0;
@@ -639,7 +645,7 @@ extern "C" gd_status gd_bind_memory(gd_model* m, void* wdev, void* kvdev, void* 
   if ((reinterpret_cast<uintptr_t>(wdev) | reinterpret_cast<uintptr_t>(kvdev) | reinterpret_cast<uintptr_t>(sdev)) & 255)
     return set_err(GD_ERR_INVALID, "device buffers must be 256-byte aligned");
   m->w = static_cast<char*>(wdev);
-  m->kv = static_cast<float*>(kvdev);
+  m->kv = static_cast<char*>(kvdev);
   m->s = static_cast<char*>(sdev);
   HIP_TRY(m, hipMemsetAsync(m->s, 0, m->s_bytes, m->stream));
   const gd_config& c = m->c;
@@ -1048,39 +1054,60 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
   return e;
 }
 
-template <int HD, int G>
-static void launch_attn_o(hipStream_t st, const AttnParams& a, const AttnOParams& po, bool paged, int wt, int M,
-                          int Hkv) {
+template <int HD, int G, bool KV16>
+static void launch_attn_o_kv(hipStream_t st, const AttnParams& a, const AttnOParams& po, bool paged, int wt, int M,
+                             int Hkv) {
   constexpr int PPG = HD == 64 ? 4 : 1;   // 64 positions per load round (measured: 8 and 2 slower)
   const dim3 grid(iceil(po.N, AttnORows<HD>::ROWS), Hkv, M), b(GD_WG);
   if (paged) {
-    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, true, 0>), grid, b, 0, st, a, po);
-    else GD_LAUNCH((k_attn_o<HD, G, PPG, true, 1>), grid, b, 0, st, a, po);
+    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, true, 0, KV16>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_o<HD, G, PPG, true, 1, KV16>), grid, b, 0, st, a, po);
   } else {
-    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, false, 0>), grid, b, 0, st, a, po);
-    else GD_LAUNCH((k_attn_o<HD, G, PPG, false, 1>), grid, b, 0, st, a, po);
+    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, false, 0, KV16>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_o<HD, G, PPG, false, 1, KV16>), grid, b, 0, st, a, po);
   }
+}
+
+template <int HD, int G>
+static void launch_attn_o(hipStream_t st, const AttnParams& a, const AttnOParams& po, bool paged, int wt, int M,
+                          int Hkv, bool kv16) {
+  if (kv16) launch_attn_o_kv<HD, G, true>(st, a, po, paged, wt, M, Hkv);
+  else launch_attn_o_kv<HD, G, false>(st, a, po, paged, wt, M, Hkv);
 }
 
 // Outputs of k_attn_proj: NP passes of 32 (512 threads, 16 lanes per output).
 static const int kAttnProjPasses = 24;
 
-static void launch_attn_proj(hipStream_t st, const AttnParams& a, const AttnOParams& po, int wt, int M, int Hkv) {
+static void launch_attn_proj(hipStream_t st, const AttnParams& a, const AttnOParams& po, int wt, int M, int Hkv,
+                             bool kv16) {
   const dim3 grid(1, Hkv, M), b(2 * GD_WG);
-  if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_proj<64, false, 0, 2 * GD_WG, kAttnProjPasses>), grid, b, 0, st, a, po);
-  else GD_LAUNCH((k_attn_proj<64, false, 1, 2 * GD_WG, kAttnProjPasses>), grid, b, 0, st, a, po);
+  constexpr int NT = 2 * GD_WG, NP = kAttnProjPasses;
+  if (kv16) {
+    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_proj<64, false, 0, NT, NP, true>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_proj<64, false, 1, NT, NP, true>), grid, b, 0, st, a, po);
+  } else {
+    if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_proj<64, false, 0, NT, NP, false>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_proj<64, false, 1, NT, NP, false>), grid, b, 0, st, a, po);
+  }
 }
 
-template <int HD, int G>
-static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, bool paged) {
+template <int HD, int G, bool KV16>
+static void launch_attention_kv(dim3 grid, hipStream_t st, const AttnParams& a, bool paged) {
   static_assert(HD == 64 || HD == 16, "head_dim");
   // 64 positions per load round: at batch 32 the kernel runs 40 % faster than with 128
   // (fewer registers, more workgroups resident per CU); 32 and 16 measure slightly slower
   // One chunk per row: 512 threads, twice the positions in flight for the longest rows.
   constexpr int PPG = HD == 64 ? 4 : 1;
-  if (grid.x == 1 && !paged) GD_LAUNCH((k_attention<HD, G, PPG, false, 2 * GD_WG>), grid, dim3(2 * GD_WG), 0, st, a);
-  else if (paged) GD_LAUNCH((k_attention<HD, G, PPG, true, GD_WG>), grid, dim3(GD_WG), 0, st, a);
-  else GD_LAUNCH((k_attention<HD, G, PPG, false, GD_WG>), grid, dim3(GD_WG), 0, st, a);
+  if (grid.x == 1 && !paged)
+    GD_LAUNCH((k_attention<HD, G, PPG, false, 2 * GD_WG, KV16>), grid, dim3(2 * GD_WG), 0, st, a);
+  else if (paged) GD_LAUNCH((k_attention<HD, G, PPG, true, GD_WG, KV16>), grid, dim3(GD_WG), 0, st, a);
+  else GD_LAUNCH((k_attention<HD, G, PPG, false, GD_WG, KV16>), grid, dim3(GD_WG), 0, st, a);
+}
+
+template <int HD, int G>
+static void launch_attention(dim3 grid, hipStream_t st, const AttnParams& a, bool paged, bool kv16) {
+  if (kv16) launch_attention_kv<HD, G, true>(grid, st, a, paged);
+  else launch_attention_kv<HD, G, false>(grid, st, a, paged);
 }
 
 // Row set-up parameters over the row arrays starting at seq/pos/tok/kvoff.
@@ -1162,7 +1189,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.y = q; p.ldy = m->qdim;
       p.qdim = m->qdim; p.kdim = m->kdim;
       p.rope_cs = rp.row_cs;
-      p.kc = m->kpool(l); p.vc = m->vpool(l);
+      p.kc = m->kpool(l); p.vc = m->vpool(l); p.kv16 = m->kv16;
       p.kv_hstride = m->bsize * c.head_dim;
       if ((e = run_linear(m, st, "linear.qkv", p)) != hipSuccess) return e;
     }
@@ -1186,12 +1213,12 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attn_o<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attn_o", kn,
-                   kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4 +
+                   kv_pos * c.n_kv_head * c.head_dim * m->kv_elt * 2 + 2.0 * M * m->qdim * 4 +
                        (double)d * m->qdim * m->elt + (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
-      if (c.head_dim == 64 && G == 1) launch_attn_o<64, 1>(st, a, po, paged, m->wt, M, c.n_kv_head);
-      else if (c.head_dim == 64) launch_attn_o<64, 3>(st, a, po, paged, m->wt, M, c.n_kv_head);
-      else if (G == 1) launch_attn_o<16, 1>(st, a, po, paged, m->wt, M, c.n_kv_head);
-      else launch_attn_o<16, 3>(st, a, po, paged, m->wt, M, c.n_kv_head);
+      if (c.head_dim == 64 && G == 1) launch_attn_o<64, 1>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
+      else if (c.head_dim == 64) launch_attn_o<64, 3>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
+      else if (G == 1) launch_attn_o<16, 1>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
+      else launch_attn_o<16, 3>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (fuse_ap) {
       // attention + output projection + bias + residual (in place on x), one workgroup
@@ -1200,20 +1227,20 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
       po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
       ProfScope ps(m, st, "attn_proj", "k_attn_proj<64>",
-                   kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + M * m->qdim * 4.0 + (double)d * m->qdim * m->elt +
+                   kv_pos * c.n_kv_head * c.head_dim * m->kv_elt * 2 + M * m->qdim * 4.0 + (double)d * m->qdim * m->elt +
                        (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
-      launch_attn_proj(st, a, po, m->wt, M, c.n_kv_head);
+      launch_attn_proj(st, a, po, m->wt, M, c.n_kv_head, m->kv16);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
       // causal attention of every row against its sequence's cache (split-context partials)
       dim3 grid(nch, c.n_kv_head, M);
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attention<%d, %d>", c.head_dim, G);
-      ProfScope ps(m, st, "attention", kn, kv_pos * c.n_kv_head * c.head_dim * 4.0 * 2 + 2.0 * M * m->qdim * 4);
-      if (c.head_dim == 64 && G == 1) launch_attention<64, 1>(grid, st, a, paged);
-      else if (c.head_dim == 64) launch_attention<64, 3>(grid, st, a, paged);
-      else if (G == 1) launch_attention<16, 1>(grid, st, a, paged);
-      else launch_attention<16, 3>(grid, st, a, paged);
+      ProfScope ps(m, st, "attention", kn, kv_pos * c.n_kv_head * c.head_dim * m->kv_elt * 2 + 2.0 * M * m->qdim * 4);
+      if (c.head_dim == 64 && G == 1) launch_attention<64, 1>(grid, st, a, paged, m->kv16);
+      else if (c.head_dim == 64) launch_attention<64, 3>(grid, st, a, paged, m->kv16);
+      else if (G == 1) launch_attention<16, 1>(grid, st, a, paged, m->kv16);
+      else launch_attention<16, 3>(grid, st, a, paged, m->kv16);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // output projection + bias + residual (in place on x); the gemv kernel merges the
