@@ -61,7 +61,8 @@ def setup(wname: str):
     if w.kv_block:
         tables, pool = synth.make_block_tables(w, prompts)
         kw.update(kv_block_size=w.kv_block, kv_num_blocks=pool)
-    m = gd.Model.from_shape(w.shape, gd.WEIGHT_BF16 if w.init.bf16 else gd.WEIGHT_F32, **kw)
+    wdt = gd.WEIGHT_BF16 if w.init.bf16 else (gd.WEIGHT_Q8 if w.init.q8 else gd.WEIGHT_F32)
+    m = gd.Model.from_shape(w.shape, wdt, **kw)
     m.load_weights(W)
     if tables is not None:
         for b in range(w.batch):
@@ -280,7 +281,9 @@ def roofline(rows, workload: str):
 # shortest prompt (the oracle's untimed prefill grows with it); C1 and C2 time their
 # whole generation, which also gives every token of it for the checksum.
 CPU_SAMPLE_FORWARDS = {"tiny": None, "gpt2_b1": None, "gpt2_stress": 16, "gpt2_b32": 16, "gpt2_b32_bf16": 16,
-                       "llama_b8": 8}
+                       "llama_b8": 8, "gpt2_b32_kv16": 16, "gpt2_b1_q8": None}
+# no oracle sample: its untimed prefill of a 2976-id prompt alone takes the oracle ~20 min
+NO_CPU_SAMPLE = {"llama_long": "the oracle's untimed prefill of the shortest (2976-id) prompt takes ~20 minutes"}
 
 
 def _shortest(w, prompts):
@@ -318,8 +321,9 @@ def start_cpu_samples(wnames):
     (forked from a fresh server process; one thread each)."""
     import multiprocessing as mp
     ctx = mp.get_context("forkserver")
-    pool = ctx.Pool(max(1, min(len(wnames), 6)))
-    return pool, {wn: pool.apply_async(oracle_sample, (wn,)) for wn in wnames}
+    todo = [wn for wn in wnames if wn not in NO_CPU_SAMPLE]
+    pool = ctx.Pool(max(1, min(len(todo), 8)))
+    return pool, {wn: pool.apply_async(oracle_sample, (wn,)) for wn in todo}
 
 
 def cpu_model():
@@ -581,13 +585,17 @@ def copy_rate():
     return 2.0 * (1 << 30) / (best * 1e-3) / 1e9
 
 
-WORKLOADS = ["gpt2_b1", "tiny", "gpt2_stress", "gpt2_b32", "gpt2_b32_bf16", "llama_b8"]
+WORKLOADS = ["gpt2_b1", "tiny", "gpt2_stress", "gpt2_b32", "gpt2_b32_bf16", "llama_b8", "gpt2_b32_kv16",
+             "llama_long", "gpt2_b1_q8"]
 SHAPES = {"tiny": "tiny GPT-2 (2x64, 4 heads, ff 256, vocab 512)",
           "gpt2_b1": "GPT-2 124M (12x768, 12 heads, ff 3072, vocab 50257)",
           "gpt2_stress": "GPT-2 124M, W_fc ~ N(0, 0.5)",
           "gpt2_b32": "GPT-2 124M (12x768, 12 heads, ff 3072, vocab 50257)",
           "gpt2_b32_bf16": "GPT-2 124M, bf16 weights",
-          "llama_b8": "Llama-style (32x960, 15/5 heads, SwiGLU 2560, vocab 49152), paged KV"}
+          "llama_b8": "Llama-style (32x960, 15/5 heads, SwiGLU 2560, vocab 49152), paged KV",
+          "gpt2_b32_kv16": "GPT-2 124M, bf16 KV cache",
+          "llama_long": "Llama-style, n_ctx 4096, bf16 weights, bf16 paged KV",
+          "gpt2_b1_q8": "GPT-2 124M, 8-bit block weights"}
 
 
 def entry(res):
@@ -695,8 +703,12 @@ def main():
     if pool is not None:
         log("[bench] waiting for the oracle samples ...")
         for wn in wnames:
+            if wn not in jobs:
+                entries[wn]["cpu_baseline"] = {"value": None, "note": NO_CPU_SAMPLE[wn]}
+                entries[wn]["tokens"] = token_record(results[wn], None)
+                continue
             smp = jobs[wn].get(900)
-            entries[wn]["cpu_baseline"] = cpu_baseline(smp, results[wn], len(wnames))
+            entries[wn]["cpu_baseline"] = cpu_baseline(smp, results[wn], len(jobs))
             entries[wn]["tokens"] = token_record(results[wn], smp)
             log(f"[bench] {wn}: oracle {entries[wn]['cpu_baseline']['value']} tok/s on 1 core; tokens "
                 f"{entries[wn]['tokens']}")

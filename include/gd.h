@@ -59,6 +59,15 @@ typedef enum {
 
 #define GD_WEIGHT_F32 0
 #define GD_WEIGHT_BF16 1
+#define GD_WEIGHT_Q8 2 /* 8-bit blocks: every weight matrix quantized at gd_load_weights, per
+                        * row and block of 32 inputs, as in the Q8_0 format (scale
+                        * max|x| / 127 kept as float32, codes round(x / scale), half away
+                        * from zero): one byte per weight plus 4 bytes per 32 ("rvllm Metal
+                        * backend", "What's basic about it" and "What's next": Q8_0 weights
+                        * as the decode speed-up; "batch_forge" README, status table: int8
+                        * dequantization). The linear layers run on the VALU GEMV (launches
+                        * of up to 4 rows); d_model, d_ff and n_head*head_dim must be
+                        * multiples of 32 */
 
 #define GD_KV_F32 0   /* the KV cache holds float32 */
 #define GD_KV_BF16 1  /* K and V are rounded to bfloat16 (nearest, ties to even) as they enter
@@ -122,7 +131,8 @@ gd_status gd_bind_memory(gd_model* m, void* weights_dev, void* kv_dev, void* scr
  *          w_v[Hkv*hd][d], w_o[d][Hq*hd], rms2[d], w_gate[ff][d], w_up[ff][d],
  *          w_down[d][ff]; then rmsf[d], w_head[V][d].
  * Matrices are [out][in] (y = x . W^T + b). With GD_WEIGHT_BF16 the matrices are
- * rounded to bfloat16 (nearest, ties to even). Repacks into the device layout and
+ * rounded to bfloat16 (nearest, ties to even); with GD_WEIGHT_Q8 quantized to 8-bit blocks
+ * (see GD_WEIGHT_Q8). Repacks into the device layout and
  * waits for the copy. n_floats must equal the canonical count (else GD_ERR_INVALID);
  * GD_ERR_STATE before gd_bind_memory. The host buffer is only read during the call. */
 gd_status gd_load_weights(gd_model* m, const float* host_weights, size_t n_floats);
@@ -175,6 +185,18 @@ gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens_host, int32
  * ids), GD_ERR_STATE (an empty sequence), GD_ERR_CTX_FULL (a full one). */
 gd_status gd_decode_step(gd_model* m, int32_t batch, const int32_t* seq_ids_host,
                          const int32_t* tokens_dev, int32_t* next_tokens_dev, float* logits_dev);
+
+/* Temperature / top-k sampling instead of the greedy argmax for every later prefill
+ * and decode step ("batch_forge" README, status table: greedy, temperature and top-k
+ * sampling; its demo samples at temperature 0.7). The token after position p of
+ * sequence slot s keeps the top_k largest logits (ties to the lower index), weights
+ * them by exp((l - l_max) / temperature) in that order, and takes the first whose
+ * cumulative weight exceeds u times the total, u being the top 24 bits of the first
+ * word of Philox4x64-10 (counter (p, s, 0, 0), key (seed, 0)) times 2^-24; a NaN logit
+ * gives the first NaN's index. temperature <= 0 or top_k == 1: greedy (the default).
+ * Otherwise 2 <= top_k <= min(256, vocab) and vocab <= 65536, else GD_ERR_INVALID.
+ * Drops the captured graphs; host-side only. */
+gd_status gd_set_sampling(gd_model* m, float temperature, int32_t top_k, uint64_t seed);
 
 /* Waits for the stream and returns the device error flags (bit 0: token id out of
  * range; bit 1: position beyond a sequence's capacity; bit 2: block table entry out

@@ -8,7 +8,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FULLSIZE_TESTS = {"test_c3_gpt2_stress_full_context": "gpt2_stress", "test_c4_gpt2_batch32_fp32": "gpt2_b32",
-                  "test_c4_gpt2_batch32_bf16": "gpt2_b32_bf16", "test_c5_llama_paged_batch8": "llama_b8"}
+                  "test_c4_gpt2_batch32_bf16": "gpt2_b32_bf16", "test_c5_llama_paged_batch8": "llama_b8",
+                  "test_c4_gpt2_batch32_kv_bf16": "gpt2_b32_kv16"}
 
 
 def pytest_configure(config):

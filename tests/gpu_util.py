@@ -23,12 +23,15 @@ def gd_model(workload, W, max_seqs=None, max_batch=None, pool_blocks=None, varia
               kv_dtype=gd.KV_BF16 if workload.init.kv_bf16 else gd.KV_F32)
     if workload.kv_block:
         kw.update(kv_block_size=workload.kv_block, kv_num_blocks=pool_blocks)
-    m = gd.Model.from_shape(s, gd.WEIGHT_BF16 if workload.init.bf16 else gd.WEIGHT_F32, **kw)
+    wdt = gd.WEIGHT_BF16 if workload.init.bf16 else (gd.WEIGHT_Q8 if workload.init.q8 else gd.WEIGHT_F32)
+    m = gd.Model.from_shape(s, wdt, **kw)
     m.load_weights(W)
     m.set_option(gd.OPT_LINEAR_VARIANT, variant)
     m.set_option(gd.OPT_USE_GRAPH, 1 if graph else 0)
     m.set_option(gd.OPT_FOLD_NORM, 1 if fold else 0)
     m.set_option(gd.OPT_ATTN_CHUNKS, chunks)
+    if workload.sampling is not None:
+        m.set_sampling(*workload.sampling)
     return m
 
 
@@ -157,11 +160,35 @@ def check_flip(rec: dict, b: int, i: int, margin: float, seen: float, gpu_t: int
     rec["flips"].append((b, i, margin, seen))
 
 
-def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run"):
-    """Parity bar: identical greedy tokens and |dlogit| <= tol over every vocabulary
-    entry at every step of every sequence. A flip passes only as a known near tie
-    (check_flip); the caller then compares that sequence teacher-forced. Returns the
-    parity record (also kept in RECORDS)."""
+# A sampled token may differ from the oracle's only where the oracle's uniform lies
+# within this of a cumulative-weight boundary between the two picks (the GPU's weights
+# come from logits that differ from the oracle's by well under 1e-5).
+SAMPLE_TIE = 1e-4
+
+
+def check_sample_flip(rec, b, i, logits, sampling, u, gpu_t, ref_t):
+    """A sampled token differs from the oracle's: it passes only if both are top-k
+    candidates and u is within SAMPLE_TIE of a cumulative-weight boundary between them."""
+    temp, top_k = sampling[0], sampling[1]
+    lg = logits.astype(np.float64)
+    order = sorted(range(lg.size), key=lambda j: (-lg[j], j))[:top_k]
+    w = np.exp((lg[order] - lg[order[0]]) / temp)
+    c = np.cumsum(w) / w.sum()
+    assert gpu_t in order, f"{rec['config']} seq {b} step {i}: sampled {gpu_t} is not a top-{top_k} candidate"
+    lo, hi = sorted((order.index(gpu_t), order.index(ref_t)))
+    gap = float(np.min(np.abs(u - c[lo:hi])))
+    assert gap <= SAMPLE_TIE, (f"{rec['config']} seq {b} step {i}: sampled {gpu_t} != oracle {ref_t}, u {u:.6f} is "
+                              f"{gap:.2e} from the nearest boundary between them")
+    rec["flips"].append((b, i, gap, 0.0))
+
+
+def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run", sampling=None, plens=None):
+    """Parity bar: identical tokens and |dlogit| <= tol over every vocabulary entry at
+    every step of every sequence. A greedy flip passes only as a known near tie
+    (check_flip), a sampled one only at a cumulative-weight boundary (check_sample_flip);
+    the caller then compares that sequence teacher-forced. ``sampling`` = (temperature,
+    top_k, seed) of a sampled run, ``plens`` its prompt lengths. Returns the parity
+    record (also kept in RECORDS)."""
     B, n = ref_tok.shape
     rec = new_record(config, B, n, tol)
     rec["tok_gpu"], rec["tok_ref"] = token_checksum(gpu_tok), token_checksum(ref_tok)
@@ -175,7 +202,11 @@ def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run"):
             rec["max_dlogit"] = max(rec["max_dlogit"], d)
             assert d <= tol, f"seq {b} step {i}: max |dlogit| {d:.3e} > {tol}"
             if gpu_tok[b, i] != ref_tok[b, i]:
-                check_flip(rec, b, i, top2_margin(ref_lg[b, i]), seen, int(gpu_tok[b, i]), int(ref_tok[b, i]))
+                if sampling is not None:
+                    u = oracle.uniform(sampling[2], b, plens[b] + i - 1)
+                    check_sample_flip(rec, b, i, ref_lg[b, i], sampling, u, int(gpu_tok[b, i]), int(ref_tok[b, i]))
+                else:
+                    check_flip(rec, b, i, top2_margin(ref_lg[b, i]), seen, int(gpu_tok[b, i]), int(ref_tok[b, i]))
                 break   # later steps of this sequence are compared teacher-forced by the caller
     rec["max_dlogit_full"] = rec["max_dlogit"]
     # backwards-compatible view for callers that look at the near ties

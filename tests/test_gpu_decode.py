@@ -28,7 +28,8 @@ def _run_and_compare(w, W, prompts, tol, variant=0, graph=True, tables=None, poo
     m = gd_model(w, W, max_seqs=max_seqs, pool_blocks=pool, variant=variant, graph=graph, fold=fold, chunks=chunks)
     tok, lg = gpu_generate(m, prompts, w.n_generate, tables=tables, logits_slices=logits_slices)
     assert m.device_errors() == 0
-    rep = compare_generation(tok, lg, ref_tok, ref_lg, tol, config or w.name)
+    rep = compare_generation(tok, lg, ref_tok, ref_lg, tol, config or w.name, sampling=w.sampling,
+                             plens=[len(p) for p in prompts])
     if rep["flips"]:
         # continue teacher-forced with the oracle's tokens; logits must still meet the bar
         tok2, lg2 = gpu_generate(m, prompts, w.n_generate, tables=tables, forced=ref_tok)
@@ -363,3 +364,108 @@ def test_llama_contexts_past_1280(kv):
     prompts = synth.make_prompts(w)
     tab, pool = synth.make_block_tables(w, prompts)
     _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool, config=f"llama long contexts ({kv} KV)")
+
+
+# ----------------------------------------------------------------- 8-bit weights
+
+@pytest.mark.parametrize("batch", [1, 3, 6])
+def test_tiny_gpt2_q8(batch):
+    """8-bit block weights (quantized at load by the library; the oracle quantizes the
+    same float weights itself): every matrix including the tied embedding and the
+    position table, one launch of up to 4 rows or two."""
+    w = synth.Workload("tiny_q8", synth.TINY, synth.Init(q8=True), 1, batch, (1, 30), 16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, config=f"tiny q8 (batch {batch})")
+    assert not rep["flips"]
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_llama_hd64_q8_paged(kv):
+    """8-bit weights in the Llama layout (RoPE row pairs and gate/up rows interleaved at
+    load, untied head), 3 query heads per KV head, shuffled paged cache."""
+    w = synth.Workload("llama_hd64_q8", LLAMA_HD64, synth.Init(q8=True, kv_bf16=kv == "bf16"), 18, 3, (5, 300), 8,
+                       kv_block=16)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    _run_and_compare(w, W, prompts, 1e-3 if kv == "f32" else 2e-2, tables=tab, pool=pool,
+                     config=f"llama_hd64 q8 ({kv} KV)")
+
+
+def test_gpt2_124m_q8_batch1():
+    """GPT-2 124M shape with 8-bit weights, batch 1, 8 prompt ids, 128 tokens: every
+    logit of every step against the oracle."""
+    w = synth.WORKLOADS["gpt2_b1_q8"]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, config="gpt2_b1_q8")
+    assert not rep["flips"], rep["flips"]
+
+
+# ---------------------------------------------------------------------- sampling
+
+@pytest.mark.parametrize("temp,top_k", [(0.8, 20), (1.5, 256), (0.3, 2)])
+def test_tiny_gpt2_sampling(temp, top_k):
+    """Temperature / top-k draws on the GPU (Philox4x64-10 uniforms keyed by seed,
+    sequence slot and position) against the oracle's, token by token; three sequences
+    decoded together, the first token drawn from the prefill's last row."""
+    w = synth.Workload("tiny_sample", synth.TINY, synth.Init(), 1, 3, (1, 30), 24, sampling=(temp, top_k, 99))
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    rep, tok, _ = _run_and_compare(w, W, prompts, 1e-3, config=f"tiny sampled (T {temp}, top-{top_k})")
+    assert len(set(tok.ravel().tolist())) > 3   # the draws spread over several tokens
+
+
+def test_sampling_greedy_special_cases_and_nan():
+    """top_k == 1 or temperature 0 is the greedy argmax; a NaN logit wins (first NaN)."""
+    import torch
+    import transformer_gpt_decode_amd as gd
+    w = synth.WORKLOADS["tiny"]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    ref_tok, _ = oracle_generate(w, W, prompts)
+    for temp, k in ((0.7, 1), (0.0, 40)):
+        m = gd_model(w, W)
+        m.set_sampling(temp, k, 5)
+        tok, _ = gpu_generate(m, prompts, w.n_generate)
+        assert np.array_equal(tok, ref_tok)
+        m.close()
+    m = gd_model(w, W)
+    for bad in ((0.7, 0), (0.7, 257), (float("nan"), 5)):
+        with pytest.raises(gd.GdError) as e:
+            m.set_sampling(*bad, 1)
+        assert e.value.status == gd.GD_ERR_INVALID
+    # NaN among the logits: an embedding row of NaNs through a 1-layer model is not
+    # needed; the sampler's NaN rule is reached with NaN weights in the head instead
+    Wn = W.copy()
+    o, shp = synth.offsets(w.shape)["wte"]
+    Wn[o + 77 * shp[1]:o + 78 * shp[1]] = np.nan   # row 77 of the tied embedding: logit 77 is NaN
+    m2 = gd_model(w, Wn)
+    m2.set_sampling(0.9, 30, 1)
+    dev = device()
+    t = torch.zeros(1, dtype=torch.int32, device=dev)
+    m2.prefill(0, [1, 2, 3], t)
+    torch.cuda.synchronize()
+    assert int(t.item()) == 77
+    m.close()
+    m2.close()
+
+
+def test_gpt2_124m_sampled_batch1():
+    """GPT-2 124M shape, batch 1, temperature 0.7, top-k 40 (the batch_forge demo's
+    temperature): 128 sampled tokens against the oracle's draws."""
+    w = synth.WORKLOADS["gpt2_b1_sample"]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    _run_and_compare(w, W, prompts, 1e-3, config="gpt2_b1 sampled (T 0.7, top-40)")
+
+
+def test_llama_hd64_sampled_paged():
+    """Sampling on the Llama layout (untied head, paged cache, 5 sequences)."""
+    w = synth.Workload("llama_hd64_sample", LLAMA_HD64, synth.Init(bf16=True), 19, 5, (5, 100), 12, kv_block=16,
+                       sampling=(1.0, 50, 7))
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool, config="llama_hd64 sampled (T 1, top-50)")

@@ -106,7 +106,7 @@ def _run(name, tol):
     top2, probe2 = _sampled(lg2, g)
     d_top = float(np.abs(top2 - g["top_val"]).max())
     d_probe = float(np.abs(probe2 - g["probe_val"]).max())
-    d_full = max(float(np.abs(lg2[b] - live[b][1]).max()) for b in full)
+    d_full = max([float(np.abs(lg2[b] - live[b][1]).max()) for b in full], default=0.0)
     worst = max(d_top, d_probe, d_full)
     rec["forced_max_dlogit"] = worst
     rec["max_dlogit_full"] = d_full
@@ -138,3 +138,15 @@ def test_c4_gpt2_batch32_bf16():
 def test_c5_llama_paged_batch8():
     """Llama-style 32 layers, GQA 15/5, RoPE, SwiGLU, paged KV (block 16, shuffled tables)."""
     _run("llama_b8", 2e-2)
+
+
+def test_c4_gpt2_batch32_kv_bf16():
+    """C4 (fp32 weights) with the bf16 KV cache (K and V rounded as they enter it)."""
+    _run("gpt2_b32_kv16", 2e-2)
+
+
+def test_llama_long_contexts_kv_bf16():
+    """Llama-style C5 shape at n_ctx 4096, bf16 weights and bf16 paged KV: 4 sequences
+    with prompts of 2976-3714 ids, 128 tokens each (sampled golden entries only: the
+    oracle needs over ten minutes per sequence)."""
+    _run("llama_long", 2e-2)

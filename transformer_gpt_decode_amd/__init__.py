@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgptdecode.so")
 
 GD_OK, GD_ERR_INVALID, GD_ERR_NO_DEVICE, GD_ERR_HIP, GD_ERR_OOM, GD_ERR_CTX_FULL, GD_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 ARCH_GPT2, ARCH_LLAMA = 0, 1
-WEIGHT_F32, WEIGHT_BF16 = 0, 1
+WEIGHT_F32, WEIGHT_BF16, WEIGHT_Q8 = 0, 1, 2
 KV_F32, KV_BF16 = 0, 1
 OPT_LINEAR_VARIANT, OPT_USE_GRAPH, OPT_PROFILE, OPT_FUSE_ATTN_O = 1, 2, 3, 4
 OPT_FOLD_NORM, OPT_ATTN_CHUNKS = 7, 9
@@ -29,7 +29,7 @@ ACT_NONE, ACT_GELU = 0, 1
 EXPORTS = ["gd_create", "gd_memory_requirements", "gd_bind_memory", "gd_load_weights", "gd_set_block_table",
            "gd_reset_seq", "gd_truncate_seq", "gd_seq_len", "gd_prefill", "gd_decode_step", "gd_device_errors",
            "gd_set_option", "gd_profile_read", "gd_destroy", "gd_last_error", "gd_linear_workspace", "gd_linear",
-           "gd_argmax_workspace", "gd_argmax", "gd_argmax_static"]
+           "gd_argmax_workspace", "gd_argmax", "gd_argmax_static", "gd_set_sampling"]
 
 
 class GdError(RuntimeError):
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "gd_argmax_workspace": [_i32, _i32, _szp],
             "gd_argmax": [_vp, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp],
             "gd_argmax_static": [_vp, _i32, _i32, _vp, _vp],
+            "gd_set_sampling": [_vp, ctypes.c_float, _i32, ctypes.c_uint64],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -199,6 +200,10 @@ class Model:
 
     def set_option(self, opt: int, value: int) -> None:
         _check(lib().gd_set_option(self._h, opt, value))
+
+    def set_sampling(self, temperature: float, top_k: int, seed: int) -> None:
+        """Temperature / top-k sampling for later steps (temperature <= 0 or top_k == 1: greedy)."""
+        _check(lib().gd_set_sampling(self._h, float(temperature), int(top_k), int(seed)))
 
 
 def linear(x, W, weight_dtype: int = WEIGHT_F32, bias=None, norm: int = NORM_NONE, norm_g=None, norm_b=None,

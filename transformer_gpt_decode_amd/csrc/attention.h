@@ -312,7 +312,8 @@ __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
 // memory operations of a wave complete in issue order: an atomic issued before a later
 // wait would be waited for).
 struct AttnOParams {
-  const void* w;          // W_o [N][K] (K = Hq * HD), fp32 or bf16 bits
+  const void* w;          // W_o [N][K] (K = Hq * HD): fp32, bf16 bits, or int8 codes
+  const float* wsc;       // int8 codes: block scales [N][K / 32]
   const float* bias;      // never NULL
   float* y; int ldy;      // residual rows, updated in place
   int N, K;
@@ -359,9 +360,12 @@ __global__ __launch_bounds__(GD_WG) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       const size_t off = (size_t)n * po.K + (kh * G + g) * HD + gl * 4;
       if constexpr (WT == 0) {
         wv[ps][g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(po.w) + off);
-      } else {
+      } else if constexpr (WT == 1) {
         const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(po.w) + off);
         wv[ps][g] = (f32x4){bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+      } else {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const int8_t*>(po.w) + off);
+        wv[ps][g] = q8x4(u, po.wsc[off >> 5]);
       }
     }
     bv[ps] = po.bias[n];

@@ -19,6 +19,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Signed byte j (0..3) of a word, as float (8-bit block weights).
+__device__ __forceinline__ float q8_at(uint32_t w, int j) { return (float)((int32_t)(w << (24 - 8 * j)) >> 24); }
+// Four int8 codes of a word times the block scale.
+__device__ __forceinline__ f32x4 q8x4(uint32_t w, float s) {
+  return (f32x4){q8_at(w, 0) * s, q8_at(w, 1) * s, q8_at(w, 2) * s, q8_at(w, 3) * s};
+}
 // float -> bfloat16 bits, rounded to nearest with ties to even (NaN kept a NaN).
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);

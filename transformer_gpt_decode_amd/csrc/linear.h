@@ -64,6 +64,7 @@ struct LinParams {
   const long long* row_kvoff;               // element offset of each row's K/V slot in a layer pool (-1: none)
   // ---- weights
   const void* w; int M, N, K;               // [N][K] row-major (VALU kernel)
+  const float* wsc;                         // 8-bit weights: the block scales [N][K / 32]
   const void* wtl;                          // the same, tile-major (matrix-core kernel; see k_pack_tiles)
   // ---- the pre-norm folded into the layer (fp32 weights; NULL: not available). With
   // LN(x)_k = (x_k - mu) r g_k + b_k the layer is y_n = r sum_k (x_k - mu) g_k W_nk +
@@ -232,6 +233,23 @@ template <>
 struct WChunk<0> { typedef f32x4 T; static constexpr int CE = 4; };
 template <>
 struct WChunk<1> { typedef u32x4 T; static constexpr int CE = 8; };
+template <>
+struct WChunk<2> { typedef u32x4 T; static constexpr int CE = 16; };   // 16 int8 codes, one block scale
+
+// The sum over one 16-code chunk of 8-bit weights against its 16 activations a[0..3],
+// times the chunk's block scale.
+__device__ __forceinline__ float q8_chunk_dot(const u32x4& w, const f32x4* a, float sc) {
+  float t = 0.f;
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t = fmaf(q8_at(ws[j], 0), a[j].x, t);
+    t = fmaf(q8_at(ws[j], 1), a[j].y, t);
+    t = fmaf(q8_at(ws[j], 2), a[j].z, t);
+    t = fmaf(q8_at(ws[j], 3), a[j].w, t);
+  }
+  return t * sc;
+}
 
 // ------------------------------------------------------------------ GEMV
 
@@ -288,8 +306,19 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
       // products skip them) and rows past N are never stored
       const int k = min((lane + 64 * i) * CE, K - CE);
       w[r][i] = __builtin_nontemporal_load(reinterpret_cast<const VT*>(
-          reinterpret_cast<const char*>(p.w) + ((size_t)min(n, N - 1) * K + k) * (WT == 0 ? 4 : 2)));
+          reinterpret_cast<const char*>(p.w) + ((size_t)min(n, N - 1) * K + k) * (WT == 0 ? 4 : WT == 1 ? 2 : 1)));
     }
+  }
+  // 8-bit weights: each chunk's block scale (blocks of 32: two chunks per scale)
+  float wsc[RW][NC];
+  if constexpr (WT == 2) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int k = min((lane + 64 * i) * CE, K - CE);
+        wsc[r][i] = p.wsc[(size_t)min(nw0 + r, N - 1) * (K >> 5) + (k >> 5)];
+      }
   }
   // 2. epilogue operands of this lane's output (lane m * RW + r), or pair (lane m)
   constexpr bool PAIR = EpiTraits<EPI>::pair;
@@ -320,6 +349,13 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   auto dot_row = [&](int m, const f32x4 (&xv)[NC][CE / 4]) {
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
+      if constexpr (WT == 2) {
+        if ((lane + 64 * i) * CE < K) {
+#pragma unroll
+          for (int r = 0; r < RW; ++r) acc[r][m] += q8_chunk_dot(w[r][i], xv[i], wsc[r][i]);
+        }
+        continue;
+      }
       if ((lane + 64 * i) * CE < K) {
         const f32x4 a = xv[i][0];
 #pragma unroll
@@ -369,6 +405,13 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
         for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
           if (m < M) {
             const float* xr = xs + m * K + k;
+            if constexpr (WT == 2) {
+              const f32x4 a4[4] = {*reinterpret_cast<const f32x4*>(xr), *reinterpret_cast<const f32x4*>(xr + 4),
+                                   *reinterpret_cast<const f32x4*>(xr + 8), *reinterpret_cast<const f32x4*>(xr + 12)};
+#pragma unroll
+              for (int r = 0; r < RW; ++r) acc[r][m] += q8_chunk_dot(w[r][i], a4, wsc[r][i]);
+              continue;
+            }
             const f32x4 a = *reinterpret_cast<const f32x4*>(xr);
 #pragma unroll
             for (int r = 0; r < RW; ++r) {

@@ -98,7 +98,7 @@ static const int kNcChoices[] = {1, 2, 3, 4, 6, 8, 12};
 
 // Smallest instantiated chunk count covering K (-1: K too long for the gemv kernel).
 static int gemv_nc(int K, int wt) {
-  const int ce = wt == GD_WEIGHT_F32 ? 4 : 8;
+  const int ce = wt == GD_WEIGHT_F32 ? 4 : wt == GD_WEIGHT_BF16 ? 8 : 16;
   const int need = iceil(iceil(K, ce), 64);
   for (int c : kNcChoices)
     if (c >= need) return c;
@@ -109,6 +109,8 @@ static int gemv_nc(int K, int wt) {
 // norm: the prologue normalizes the rows (LDS for statistics, gain and shift).
 static int gemv_rows_per_wave(int epi, int N) {
   if (epi == EPI_SWIGLU || epi == EPI_QKV_ROPE) return 2;   // both rows of a pair in one wave
+  // a wide head: four rows per wave (8-bit heads with 16 rows per wave measured 61 us
+  // against 21 us at GPT-2 124M: each wave then serializes 16 cross-lane sums)
   if (epi == EPI_ARGMAX && N >= 16384) return 4;
   return 1;
 }
@@ -125,9 +127,10 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
   LinPlan p;
   memset(&p, 0, sizeof(p));
   p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= GEMV_MAX_ROWS ? 0 : 1);
+  if (wt == GD_WEIGHT_Q8) p.var = 0;   // 8-bit weights: the VALU kernel only (launches of <= 4 rows)
   p.nc = gemv_nc(K, wt);
   if (p.var == 1 && norm && K > MM_KC) p.var = 0;   // the norm needs whole rows in one register pass
-  if (p.var == 0 && p.nc < 0) p.var = 1;
+  if (p.var == 0 && p.nc < 0 && wt != GD_WEIGHT_Q8) p.var = 1;
   if (p.var == 0) {
     p.rw = gemv_rows_per_wave(epi, N);
     p.rows = std::min(M, GEMV_MAX_ROWS);
@@ -136,7 +139,7 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
     // the activation rows (a pre-norm is applied in registers)
     const size_t xs = ((size_t)p.rows * K + 3) & ~(size_t)3;
     p.lds = xs * sizeof(float);
-    if (p.lds > kGemvLdsMax && !(norm && K > MM_KC)) p.var = 1;   // rows too long to stage
+    if (p.lds > kGemvLdsMax && !(norm && K > MM_KC) && wt != GD_WEIGHT_Q8) p.var = 1;   // rows too long to stage
   }
   if (p.var == 1) {
     const int ntiles = iceil(N, GD_TILE_N), nb = iceil(K, 32);
@@ -261,7 +264,9 @@ static hipError_t launch_mm(const LinPlan& lp, const LinParams& prm, hipStream_t
 // One launch of one plan over prm.M rows (prm.M <= lp.rows).
 static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st) {
   if (lp.var == 0) {
-    const hipError_t e = wt == GD_WEIGHT_F32 ? launch_gemv<0>(lp, prm, st) : launch_gemv<1>(lp, prm, st);
+    const hipError_t e = wt == GD_WEIGHT_F32    ? launch_gemv<0>(lp, prm, st)
+                         : wt == GD_WEIGHT_BF16 ? launch_gemv<1>(lp, prm, st)
+                                                : launch_gemv<2>(lp, prm, st);
     if (e != hipSuccess) return e;
   } else {
     const hipError_t e = wt == GD_WEIGHT_F32 ? launch_mm<0>(lp, prm, st) : launch_mm<1>(lp, prm, st);
@@ -303,6 +308,7 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
 
 struct LayerOff {
   size_t n1g, n1b, wqkv, bqkv, wo, bo, n2g, n2b, wfc, bfc, wproj, bproj;
+  size_t sqkv, so, sfc, sproj;   // 8-bit weights: block scales of the matrices (0: none)
   size_t tqkv, to, tfc, tproj;   // tile-major copies of the matrices (matrix-core kernel)
   // pre-norm folded into QKV and MLP-up (fp32): weights, bias, row sums (0: none)
   size_t fqkv, fqkv_b, fqkv_s, ffc, ffc_b, ffc_s;
@@ -336,6 +342,11 @@ struct gd_model {
   bool fuse_attn_o = true;
   int attn_chunks = 0;   // split-context chunks per row: 0 auto, 1 or GD_ATT_NCH (GD_OPT_ATTN_CHUNKS)
   bool use_fold = true;  // GEMV pre-norms folded into the weights when available (GD_OPT_FOLD_NORM)
+  // temperature / top-k sampling instead of the greedy argmax (gd_set_sampling)
+  bool sample = false;
+  int top_k = 1;
+  float inv_temp = 1.f;
+  unsigned long long seed = 0;
   int dev = 0;
   int n_cu = 0;         // compute units
 
@@ -359,6 +370,7 @@ struct gd_model {
 
   // weight offsets (bytes)
   size_t o_wte = 0, o_wpe = 0, o_nfg = 0, o_nfb = 0, o_head = 0, o_thead = 0;
+  size_t o_swte = 0, o_swpe = 0, o_shead = 0;   // 8-bit weights: block scales of the tables and head
   size_t o_fhead = 0, o_fhead_b = 0, o_fhead_s = 0, o_fold = 0;   // folded final norm + head
   size_t o_tfhead = 0, o_fold_end = 0;   // tile-major folded head; end of the row-major folded part
   bool folded = false;   // the folded copies exist (fp32 weights)
@@ -366,6 +378,7 @@ struct gd_model {
 
   // scratch offsets (bytes)
   size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart, o_zero;
+  size_t o_slog = 0;   // logits rows the sampler reads when the caller asks for none
   size_t o_rseq, o_rpos, o_rtok, o_rkv, o_rcs, o_pseq, o_ppos, o_ptok, o_pkv, o_pcs, o_len, o_cap, o_sids, o_table, o_err, o_rope;
 
   // host mirror
@@ -419,8 +432,10 @@ static gd_status check_cfg(const gd_config* c) {
   int G = c->n_head / c->n_kv_head;
   if (G != 1 && G != 3) return set_err(GD_ERR_INVALID, "query heads per KV head must be 1 or 3");
   if ((c->n_head * c->head_dim) % 8) return set_err(GD_ERR_INVALID, "n_head*head_dim must be a multiple of 8");
-  if (c->weight_dtype != GD_WEIGHT_F32 && c->weight_dtype != GD_WEIGHT_BF16)
+  if (c->weight_dtype != GD_WEIGHT_F32 && c->weight_dtype != GD_WEIGHT_BF16 && c->weight_dtype != GD_WEIGHT_Q8)
     return set_err(GD_ERR_INVALID, "bad weight_dtype");
+  if (c->weight_dtype == GD_WEIGHT_Q8 && (c->d_model % 32 || c->d_ff % 32 || (c->n_head * c->head_dim) % 32))
+    return set_err(GD_ERR_INVALID, "8-bit weights need d_model, d_ff and n_head*head_dim multiples of 32");
   if (c->kv_dtype != GD_KV_F32 && c->kv_dtype != GD_KV_BF16) return set_err(GD_ERR_INVALID, "bad kv_dtype");
   if (c->max_seqs < 1 || c->max_batch < 1 || c->max_batch > GD_MAX_ROWS)
     return set_err(GD_ERR_INVALID, "max_seqs >= 1 and 1 <= max_batch <= 32 required");
@@ -434,7 +449,8 @@ static void layout(gd_model* m) {
   const gd_config& c = m->c;
   const size_t d = c.d_model, ff = c.d_ff, V = c.vocab;
   m->wt = c.weight_dtype;
-  m->elt = m->wt == GD_WEIGHT_F32 ? 4 : 2;
+  m->elt = m->wt == GD_WEIGHT_F32 ? 4 : m->wt == GD_WEIGHT_BF16 ? 2 : 1;
+  const bool q8 = m->wt == GD_WEIGHT_Q8;
   m->kv16 = c.kv_dtype == GD_KV_BF16;
   m->kv_elt = m->kv16 ? 2 : 4;
   m->qdim = c.n_head * c.head_dim;
@@ -456,38 +472,47 @@ static void layout(gd_model* m) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   const size_t e = m->elt;
-  m->o_wte = take(V * d * e);
-  if (c.arch == GD_ARCH_GPT2) m->o_wpe = take((size_t)c.n_ctx * d * e);
+  // a matrix of R rows by K: its elements, then (8-bit weights) its block scales
+  auto mat = [&](size_t R, size_t K, size_t& sc) {
+    const size_t o = take(R * K * e);
+    sc = q8 ? take(R * (K / 32) * 4) : 0;
+    return o;
+  };
+  m->o_wte = mat(V, d, m->o_swte);
+  if (c.arch == GD_ARCH_GPT2) m->o_wpe = mat((size_t)c.n_ctx, d, m->o_swpe);
   m->L.resize(c.n_layer);
   for (int l = 0; l < c.n_layer; ++l) {
     LayerOff& t = m->L[l];
     t.n1g = take(d * 4);
     t.n1b = c.arch == GD_ARCH_GPT2 ? take(d * 4) : 0;
-    t.wqkv = take((size_t)m->qkvdim * d * e);
+    t.wqkv = mat((size_t)m->qkvdim, d, t.sqkv);
     t.bqkv = c.arch == GD_ARCH_GPT2 ? take((size_t)m->qkvdim * 4) : 0;
-    t.wo = take(d * m->qdim * e);
+    t.wo = mat(d, (size_t)m->qdim, t.so);
     t.bo = c.arch == GD_ARCH_GPT2 ? take(d * 4) : 0;
     t.n2g = take(d * 4);
     t.n2b = c.arch == GD_ARCH_GPT2 ? take(d * 4) : 0;
-    t.wfc = take((size_t)m->fcN * d * e);
+    t.wfc = mat((size_t)m->fcN, d, t.sfc);
     t.bfc = c.arch == GD_ARCH_GPT2 ? take(ff * 4) : 0;
-    t.wproj = take(d * ff * e);
+    t.wproj = mat(d, ff, t.sproj);
     t.bproj = c.arch == GD_ARCH_GPT2 ? take(d * 4) : 0;
   }
   m->o_nfg = take(d * 4);
   if (c.arch == GD_ARCH_GPT2) m->o_nfb = take(d * 4);
-  else m->o_head = take(V * d * e);
-  // tile-major copies for the matrix-core kernel (filled from the row-major matrices)
+  else m->o_head = mat(V, d, m->o_shead);
+  // tile-major copies for the matrix-core kernel (filled from the row-major matrices;
+  // none for 8-bit weights, which run on the VALU kernel only)
   m->w_rowmajor_bytes = off;
   const int wt = m->wt == GD_WEIGHT_F32 ? 0 : 1;
-  for (int l = 0; l < c.n_layer; ++l) {
-    LayerOff& t = m->L[l];
-    t.tqkv = take(mm_packed_bytes(wt, m->qkvdim, (int)d));
-    t.to = take(mm_packed_bytes(wt, (int)d, m->qdim));
-    t.tfc = take(mm_packed_bytes(wt, m->fcN, (int)d));
-    t.tproj = take(mm_packed_bytes(wt, (int)d, (int)ff));
+  if (!q8) {
+    for (int l = 0; l < c.n_layer; ++l) {
+      LayerOff& t = m->L[l];
+      t.tqkv = take(mm_packed_bytes(wt, m->qkvdim, (int)d));
+      t.to = take(mm_packed_bytes(wt, (int)d, m->qdim));
+      t.tfc = take(mm_packed_bytes(wt, m->fcN, (int)d));
+      t.tproj = take(mm_packed_bytes(wt, (int)d, (int)ff));
+    }
+    m->o_thead = take(mm_packed_bytes(wt, (int)V, (int)d));
   }
-  m->o_thead = take(mm_packed_bytes(wt, (int)V, (int)d));
   // the pre-norms folded into the layers that follow them (fp32 weights only: a bf16
   // copy of g_k W_nk would round the weights a second time)
   m->folded = m->wt == GD_WEIGHT_F32;
@@ -536,6 +561,7 @@ static void layout(gd_model* m) {
   m->o_amv = take(m->am_parts * R * 4);
   m->o_ami = take(m->am_parts * R * 4);
   m->o_apart = take(R * c.n_head * GD_ATT_NCH * (c.head_dim + 2) * 4);
+  m->o_slog = take(R * (size_t)c.vocab * 4);
   // zeros (cleared at bind, never written): the bias or residual of layers that have none
   m->o_zero = take((size_t)std::max({m->qkvdim, m->fcN, (int)d, (int)ff}) * 4);
   m->o_rseq = take(R * 4);
@@ -694,6 +720,33 @@ static void put_mat(const gd_model* m, std::vector<char>& dst, size_t off, const
   }
 }
 
+// 8-bit blocks of one row of K values (K a multiple of 32), as in the Q8_0 format: per
+// block of 32, the scale s = max|x| / 127 and the codes round(x * (1 / s)), rounded half
+// away from zero, in [-127, 127]; s = 0 and codes 0 for an all-zero block.
+static void quantize_q8_row(const float* x, size_t K, int8_t* q, float* sc) {
+  for (size_t b = 0; b < K / 32; ++b) {
+    float amax = 0.f;
+    for (size_t i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(x[32 * b + i]));
+    const float s = amax / 127.0f;
+    const float inv = s != 0.f ? 1.0f / s : 0.f;
+    for (size_t i = 0; i < 32; ++i) q[32 * b + i] = (int8_t)std::round(x[32 * b + i] * inv);
+    sc[b] = s;
+  }
+}
+
+// Rows [row0, row0 + nrows) of a [rows][K] matrix stored at byte offset off (8-bit
+// weights: its block scales at sc_off), from nrows float rows at src.
+static void put_rows(const gd_model* m, std::vector<char>& dst, size_t off, size_t sc_off, size_t row0,
+                     const float* src, size_t nrows, size_t K) {
+  if (m->wt == GD_WEIGHT_Q8) {
+    int8_t* q = reinterpret_cast<int8_t*>(dst.data() + off) + row0 * K;
+    float* sc = reinterpret_cast<float*>(dst.data() + sc_off) + row0 * (K / 32);
+    for (size_t r = 0; r < nrows; ++r) quantize_q8_row(src + r * K, K, q + r * K, sc + r * (K / 32));
+    return;
+  }
+  put_mat(m, dst, off + row0 * K * m->elt, src, nrows * K);
+}
+
 static void put_vec(std::vector<char>& dst, size_t off, const float* src, size_t n) {
   memcpy(dst.data() + off, src, n * 4);
 }
@@ -721,27 +774,27 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
   if (!m->bound) return set_err(GD_ERR_STATE, "memory not bound");
   const gd_config& c = m->c;
   if (n != canonical_count(c)) return set_err(GD_ERR_INVALID, "weight count %zu, expected %zu", n, canonical_count(c));
-  const size_t d = c.d_model, ff = c.d_ff, V = c.vocab, e = m->elt;
+  const size_t d = c.d_model, ff = c.d_ff, V = c.vocab;
   std::vector<char> buf(m->w_rowmajor_bytes, 0);
   const float* p = hw;
-  put_mat(m, buf, m->o_wte, p, V * d);
+  put_rows(m, buf, m->o_wte, m->o_swte, 0, p, V, d);
   p += V * d;
   if (c.arch == GD_ARCH_GPT2) {
-    put_mat(m, buf, m->o_wpe, p, (size_t)c.n_ctx * d);
+    put_rows(m, buf, m->o_wpe, m->o_swpe, 0, p, (size_t)c.n_ctx, d);
     p += (size_t)c.n_ctx * d;
     for (int l = 0; l < c.n_layer; ++l) {
       const LayerOff& t = m->L[l];
       put_vec(buf, t.n1g, p, d); p += d;
       put_vec(buf, t.n1b, p, d); p += d;
-      put_mat(m, buf, t.wqkv, p, 3 * d * d); p += 3 * d * d;
+      put_rows(m, buf, t.wqkv, t.sqkv, 0, p, 3 * d, d); p += 3 * d * d;
       put_vec(buf, t.bqkv, p, 3 * d); p += 3 * d;
-      put_mat(m, buf, t.wo, p, d * d); p += d * d;
+      put_rows(m, buf, t.wo, t.so, 0, p, d, d); p += d * d;
       put_vec(buf, t.bo, p, d); p += d;
       put_vec(buf, t.n2g, p, d); p += d;
       put_vec(buf, t.n2b, p, d); p += d;
-      put_mat(m, buf, t.wfc, p, ff * d); p += ff * d;
+      put_rows(m, buf, t.wfc, t.sfc, 0, p, ff, d); p += ff * d;
       put_vec(buf, t.bfc, p, ff); p += ff;
-      put_mat(m, buf, t.wproj, p, d * ff); p += d * ff;
+      put_rows(m, buf, t.wproj, t.sproj, 0, p, d, ff); p += d * ff;
       put_vec(buf, t.bproj, p, d); p += d;
     }
     put_vec(buf, m->o_nfg, p, d); p += d;
@@ -750,34 +803,34 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
     const size_t hq = m->qdim, hk = m->kdim, hd = c.head_dim, half = hd / 2;
     // q and k rows are stored so that each RoPE pair (i, i + hd/2) of a head sits in
     // adjacent rows (2i, 2i + 1); q.k is unchanged because both use the same order.
-    auto put_rope_rows = [&](size_t dst, const float* src, size_t heads) {
+    auto put_rope_rows = [&](const LayerOff& t, size_t row_base, const float* src, size_t heads) {
       for (size_t h = 0; h < heads; ++h)
         for (size_t i = 0; i < half; ++i) {
-          put_mat(m, buf, dst + ((h * hd + 2 * i) * d) * e, src + (h * hd + i) * d, d);
-          put_mat(m, buf, dst + ((h * hd + 2 * i + 1) * d) * e, src + (h * hd + half + i) * d, d);
+          put_rows(m, buf, t.wqkv, t.sqkv, row_base + h * hd + 2 * i, src + (h * hd + i) * d, 1, d);
+          put_rows(m, buf, t.wqkv, t.sqkv, row_base + h * hd + 2 * i + 1, src + (h * hd + half + i) * d, 1, d);
         }
     };
     for (int l = 0; l < c.n_layer; ++l) {
       const LayerOff& t = m->L[l];
       put_vec(buf, t.n1g, p, d); p += d;
       // fused [w_q; w_k; w_v]
-      put_rope_rows(t.wqkv, p, c.n_head); p += hq * d;
-      put_rope_rows(t.wqkv + hq * d * e, p, c.n_kv_head); p += hk * d;
-      put_mat(m, buf, t.wqkv + (hq + hk) * d * e, p, hk * d); p += hk * d;
-      put_mat(m, buf, t.wo, p, d * hq); p += d * hq;
+      put_rope_rows(t, 0, p, c.n_head); p += hq * d;
+      put_rope_rows(t, hq, p, c.n_kv_head); p += hk * d;
+      put_rows(m, buf, t.wqkv, t.sqkv, hq + hk, p, hk, d); p += hk * d;
+      put_rows(m, buf, t.wo, t.so, 0, p, d, hq); p += d * hq;
       put_vec(buf, t.n2g, p, d); p += d;
       // gate and up interleaved by row: row 2j = gate j, row 2j + 1 = up j
       const float* g = p;
       const float* u = p + ff * d;
       for (size_t j = 0; j < ff; ++j) {
-        put_mat(m, buf, t.wfc + (2 * j) * d * e, g + j * d, d);
-        put_mat(m, buf, t.wfc + (2 * j + 1) * d * e, u + j * d, d);
+        put_rows(m, buf, t.wfc, t.sfc, 2 * j, g + j * d, 1, d);
+        put_rows(m, buf, t.wfc, t.sfc, 2 * j + 1, u + j * d, 1, d);
       }
       p += 2 * ff * d;
-      put_mat(m, buf, t.wproj, p, d * ff); p += d * ff;
+      put_rows(m, buf, t.wproj, t.sproj, 0, p, d, ff); p += d * ff;
     }
     put_vec(buf, m->o_nfg, p, d); p += d;
-    put_mat(m, buf, m->o_head, p, V * d); p += V * d;
+    put_rows(m, buf, m->o_head, m->o_shead, 0, p, V, d); p += V * d;
   }
   HIP_TRY(m, hipMemcpyAsync(m->w, buf.data(), buf.size(), hipMemcpyHostToDevice, m->stream));
   std::vector<char> fbuf;
@@ -820,14 +873,15 @@ extern "C" gd_status gd_load_weights(gd_model* m, const float* hw, size_t n) {
   auto pack = [&](size_t src, size_t dst, int N, int K) {
     return launch_pack(m->w + src, m->wt, N, K, m->w + dst, m->stream);
   };
-  for (int l = 0; l < c.n_layer; ++l) {
+  for (int l = 0; l < c.n_layer && m->wt != GD_WEIGHT_Q8; ++l) {
     const LayerOff& t = m->L[l];
     HIP_TRY(m, pack(t.wqkv, t.tqkv, m->qkvdim, (int)d));
     HIP_TRY(m, pack(t.wo, t.to, (int)d, m->qdim));
     HIP_TRY(m, pack(t.wfc, t.tfc, m->fcN, (int)d));
     HIP_TRY(m, pack(t.wproj, t.tproj, (int)d, (int)ff));
   }
-  HIP_TRY(m, pack(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, m->o_thead, (int)V, (int)d));
+  if (m->wt != GD_WEIGHT_Q8)
+    HIP_TRY(m, pack(c.arch == GD_ARCH_GPT2 ? m->o_wte : m->o_head, m->o_thead, (int)V, (int)d));
   if (m->folded) {
     for (int l = 0; l < c.n_layer; ++l) {
       const LayerOff& t = m->L[l];
@@ -947,6 +1001,26 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
   return GD_OK;
 }
 
+extern "C" gd_status gd_set_sampling(gd_model* m, float temperature, int32_t top_k, uint64_t seed) {
+  if (!m) return set_err(GD_ERR_INVALID, "model is NULL");
+  if (!(temperature == temperature)) return set_err(GD_ERR_INVALID, "temperature is NaN");
+  if (temperature <= 0.f || top_k == 1) {
+    m->sample = false;
+  } else {
+    if (m->c.vocab > GD_SAMPLE_NT * GD_SAMPLE_VPT)
+      return set_err(GD_ERR_INVALID, "sampling needs vocab <= %d", GD_SAMPLE_NT * GD_SAMPLE_VPT);
+    if (top_k < 2 || top_k > GD_SAMPLE_MAX_K || top_k > m->c.vocab)
+      return set_err(GD_ERR_INVALID, "top_k %d outside 1..min(%d, vocab)", top_k, GD_SAMPLE_MAX_K);
+    m->sample = true;
+    m->top_k = top_k;
+    m->inv_temp = 1.0f / temperature;
+    m->seed = seed;
+  }
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second.exec);
+  m->graphs.clear();
+  return GD_OK;
+}
+
 extern "C" gd_status gd_device_errors(gd_model* m, int32_t* flags) {
   if (!m || !flags) return set_err(GD_ERR_INVALID, "NULL argument");
   if (!m->bound) return set_err(GD_ERR_STATE, "memory not bound");
@@ -1009,7 +1083,7 @@ struct ProfScope {
 
 static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, bool fold, int pro, char* buf,
                                       size_t n) {
-  const int w = wt == GD_WEIGHT_F32 ? 0 : 1;
+  const int w = wt == GD_WEIGHT_F32 ? 0 : wt == GD_WEIGHT_BF16 ? 1 : 2;
   // as rocprofv3 prints the instantiation
   if (lp.var == 0)
     snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %d>", w, lp.nc, lp.rw, epi, pro,
@@ -1025,6 +1099,7 @@ static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool n
 static double linear_bytes(const gd_model* m, const LinParams& p) {
   const int n_out = p.epi == EPI_SWIGLU ? p.N / 2 : (p.epi == EPI_ARGMAX ? (p.logits ? p.N : 0) : p.N);
   double b = (double)p.N * p.K * m->elt + (double)p.M * p.K * 4 + (double)p.M * n_out * 4;
+  if (m->wt == GD_WEIGHT_Q8) b += (double)p.N * (p.K / 32) * 4;   // block scales
   const float* zero = m->sp<float>(m->o_zero);
   if (p.bias && p.bias != zero) b += (double)p.N * 4;
   if (p.norm) b += (double)p.K * 4 * (p.nb ? 2 : 1);
@@ -1061,10 +1136,12 @@ static void launch_attn_o_kv(hipStream_t st, const AttnParams& a, const AttnOPar
   const dim3 grid(iceil(po.N, AttnORows<HD>::ROWS), Hkv, M), b(GD_WG);
   if (paged) {
     if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, true, 0, KV16>), grid, b, 0, st, a, po);
-    else GD_LAUNCH((k_attn_o<HD, G, PPG, true, 1, KV16>), grid, b, 0, st, a, po);
+    else if (wt == GD_WEIGHT_BF16) GD_LAUNCH((k_attn_o<HD, G, PPG, true, 1, KV16>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_o<HD, G, PPG, true, 2, KV16>), grid, b, 0, st, a, po);
   } else {
     if (wt == GD_WEIGHT_F32) GD_LAUNCH((k_attn_o<HD, G, PPG, false, 0, KV16>), grid, b, 0, st, a, po);
-    else GD_LAUNCH((k_attn_o<HD, G, PPG, false, 1, KV16>), grid, b, 0, st, a, po);
+    else if (wt == GD_WEIGHT_BF16) GD_LAUNCH((k_attn_o<HD, G, PPG, false, 1, KV16>), grid, b, 0, st, a, po);
+    else GD_LAUNCH((k_attn_o<HD, G, PPG, false, 2, KV16>), grid, b, 0, st, a, po);
   }
 }
 
@@ -1120,6 +1197,11 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
   r.wte = m->w + m->o_wte;
   r.wpe = c.arch == GD_ARCH_GPT2 ? (const void*)(m->w + m->o_wpe) : nullptr;
   r.vocab = c.vocab; r.n_pos = c.n_ctx; r.d = c.d_model; r.emb_bf16 = m->wt == GD_WEIGHT_BF16;
+  r.emb_q8 = m->wt == GD_WEIGHT_Q8;
+  if (r.emb_q8) {
+    r.wte_sc = m->wf(m->o_swte);
+    r.wpe_sc = c.arch == GD_ARCH_GPT2 ? m->wf(m->o_swpe) : nullptr;
+  }
   r.x = m->sp<float>(m->o_x);
   r.row_seq = rseq; r.row_pos = rpos; r.row_tok = rtok; r.row_kvoff = rkv;
   r.rope = c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rope) : nullptr;
@@ -1155,7 +1237,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   // With one chunk per row (contiguous cache, head_dim 64, one query head per KV head,
   // d_model <= 768) the attention workgroups also apply the output projection.
   const bool fuse_ap = m->fuse_attn_o && !fuse_ao && nch == 1 && c.kv_block_size == 0 && c.head_dim == 64 &&
-                       c.n_head == c.n_kv_head && c.d_model <= kAttnProjPasses * 32;
+                       c.n_head == c.n_kv_head && c.d_model <= kAttnProjPasses * 32 && m->wt != GD_WEIGHT_Q8;
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
   const int nrm = gpt2 ? NORM_LN : NORM_RMS;
   const int G = c.n_head / c.n_kv_head;
@@ -1183,6 +1265,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n1g); p.nb = t.n1b ? m->wf(t.n1b) : nullptr;
       p.w = m->w + t.wqkv; p.wtl = m->w + t.tqkv; p.N = m->qkvdim; p.K = d;
+      if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(t.sqkv);
       if (fold) { p.wf = m->w + t.fqkv; p.wfl = m->w + t.tfqkv; p.bf = m->wf(t.fqkv_b); p.fs = m->wf(t.fqkv_s); }
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
       p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
@@ -1209,12 +1292,13 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       // attention + output projection + bias + residual (in place on x), one launch
       AttnOParams po;
       po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
+      po.wsc = m->wt == GD_WEIGHT_Q8 ? m->wf(t.so) : nullptr;
       po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
       char kn[48];
       snprintf(kn, sizeof(kn), "k_attn_o<%d, %d>", c.head_dim, G);
       ProfScope ps(m, st, "attn_o", kn,
                    kv_pos * c.n_kv_head * c.head_dim * m->kv_elt * 2 + 2.0 * M * m->qdim * 4 +
-                       (double)d * m->qdim * m->elt + (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
+                       (double)d * m->qdim * m->elt + (m->wt == GD_WEIGHT_Q8 ? d * (m->qdim / 32) * 4.0 : 0.0) + (t.bo ? d * 4.0 : 0.0) + 2.0 * M * d * 4);
       if (c.head_dim == 64 && G == 1) launch_attn_o<64, 1>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
       else if (c.head_dim == 64) launch_attn_o<64, 3>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
       else if (G == 1) launch_attn_o<16, 1>(st, a, po, paged, m->wt, M, c.n_kv_head, m->kv16);
@@ -1225,6 +1309,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       // per (KV head, row)
       AttnOParams po;
       po.w = m->w + t.wo; po.bias = t.bo ? m->wf(t.bo) : zero;
+      po.wsc = m->wt == GD_WEIGHT_Q8 ? m->wf(t.so) : nullptr;
       po.y = x; po.ldy = d; po.N = d; po.K = m->qdim;
       ProfScope ps(m, st, "attn_proj", "k_attn_proj<64>",
                    kv_pos * c.n_kv_head * c.head_dim * m->kv_elt * 2 + M * m->qdim * 4.0 + (double)d * m->qdim * m->elt +
@@ -1260,6 +1345,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
         p.x = attn; p.ldx = m->qdim;
       }
       p.w = m->w + t.wo; p.wtl = m->w + t.to; p.N = d; p.K = m->qdim;
+      if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(t.so);
       p.epi = EPI_PLAIN;
       p.bias = t.bo ? m->wf(t.bo) : zero;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
@@ -1272,6 +1358,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.x = x; p.ldx = d;
       p.norm = nrm; p.ng = m->wf(t.n2g); p.nb = t.n2b ? m->wf(t.n2b) : nullptr;
       p.w = m->w + t.wfc; p.wtl = m->w + t.tfc; p.N = m->fcN; p.K = d;
+      if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(t.sfc);
       if (fold) { p.wf = m->w + t.ffc; p.wfl = m->w + t.tffc; p.bf = m->wf(t.ffc_b); p.fs = m->wf(t.ffc_s); }
       p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
       p.bias = t.bfc ? m->wf(t.bfc) : zero;
@@ -1285,6 +1372,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.pro = PRO_COPY;
       p.x = h; p.ldx = ff;
       p.w = m->w + t.wproj; p.wtl = m->w + t.tproj; p.N = d; p.K = ff;
+      if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(t.sproj);
       p.epi = EPI_PLAIN;
       p.bias = t.bproj ? m->wf(t.bproj) : zero;
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
@@ -1298,6 +1386,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.x = x + (size_t)head_row * d; p.ldx = d;
     p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
     p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
+    if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(gpt2 ? m->o_swte : m->o_shead);
     if (fold) {
       p.wf = m->w + m->o_fhead; p.wfl = m->w + m->o_tfhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s);
     }
@@ -1306,8 +1395,21 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     p.row_kvoff = rp.row_kvoff + head_row;
     p.rope_cs = nullptr;
     p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
-    p.logits = logits; p.ldl = c.vocab;
+    // the sampler reads whole logit rows: the caller's, or the scratch rows
+    p.logits = logits ? logits : (m->sample ? m->sp<float>(m->o_slog) : nullptr);
+    p.ldl = c.vocab;
     if ((e = run_linear(m, st, "linear.head", p, head_out)) != hipSuccess) return e;
+    if (m->sample) {
+      // temperature / top-k draw over each head row (replaces the greedy token)
+      SampleParams sp;
+      sp.logits = p.logits; sp.ldl = c.vocab; sp.V = c.vocab; sp.top_k = m->top_k;
+      sp.inv_temp = m->inv_temp; sp.seed = m->seed;
+      sp.row_seq = rp.row_seq + head_row; sp.row_pos = rp.row_pos + head_row;
+      sp.out = head_out;
+      ProfScope ps(m, st, "sample", "k_sample", (double)head_rows * c.vocab * 4);
+      GD_LAUNCH(k_sample, dim3(head_rows), dim3(GD_SAMPLE_NT), 0, st, sp);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
