@@ -617,6 +617,89 @@ def entry(res):
     return e
 
 
+# Prompt workloads: (workload whose weights and prompts are used, sequence)
+PREFILL = [("gpt2_stress", 0), ("llama_b8", 4)]
+
+
+def measure_prefill(wname: str, seq: int, runs: int):
+    """Prompt throughput of one sequence's prompt: the tiled prompt pass (median of
+    `runs`), the same prompt through the decode kernels (32 rows per pass), and a
+    profiled pass giving each GEMM's 2 M N K over its mean time."""
+    import statistics
+    import torch
+    import synth
+    import transformer_gpt_decode_amd as gd
+    w = synth.WORKLOADS[wname]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    P = prompts[seq]
+    kw = dict(max_seqs=w.batch, max_batch=w.batch, kv_dtype=gd.KV_BF16 if w.init.kv_bf16 else gd.KV_F32)
+    if w.kv_block:
+        tables, pool = synth.make_block_tables(w, prompts)
+        kw.update(kv_block_size=w.kv_block, kv_num_blocks=pool)
+    wdt = gd.WEIGHT_BF16 if w.init.bf16 else (gd.WEIGHT_Q8 if w.init.q8 else gd.WEIGHT_F32)
+    m = gd.Model.from_shape(w.shape, wdt, **kw)
+    m.load_weights(W)
+    if w.kv_block:
+        m.set_block_table(seq, tables[seq][tables[seq] >= 0])
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run(tiled, n):
+        m.set_option(gd.OPT_TILED_PREFILL, 1 if tiled else 0)
+        out = []
+        for _ in range(n + 1):   # the first run is a warm-up
+            m.reset_seq(seq)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            m.prefill(seq, P, tok)
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return out[1:], int(tok.item())
+
+    tiled, t1 = run(True, runs)
+    untiled, t2 = run(False, runs)
+    m.set_option(gd.OPT_TILED_PREFILL, 1)
+    m.reset_seq(seq)
+    m.set_option(gd.OPT_PROFILE, 1)
+    m.profile_read(reset=True)
+    m.prefill(seq, P, tok)
+    stats = m.profile_read(reset=True)
+    m.set_option(gd.OPT_PROFILE, 0)
+    m.close()
+    n = len(P)
+    s = w.shape
+    qdim, kdim = s.n_head * s.head_dim, s.n_kv_head * s.head_dim
+    fc_n = s.d_ff if s.arch == 0 else 2 * s.d_ff
+    nk = {"pf.qkv": (qdim + 2 * kdim, s.d_model), "pf.o": (s.d_model, qdim), "pf.fc": (fc_n, s.d_model),
+          "pf.down": (s.d_model, s.d_ff)}
+    gemms, g_us, g_fl = [], 0.0, 0.0
+    chunks = -(-n // 512)   # launches per role = layers x 512-row chunks; the chunks cover the n rows once
+    for st in stats:
+        if st["role"] not in nk:
+            continue
+        N, K = nk[st["role"]]
+        flops = 2.0 * n * N * K * st["launches"] / chunks
+        tf = flops / (st["total_us"] * 1e-6) / 1e12
+        g_us += st["total_us"]
+        g_fl += flops
+        gemms.append(dict(role=st["role"], kernel=st["kernel"], launches=st["launches"],
+                          avg_us=round(st["total_us"] / st["launches"], 2), tflops=round(tf, 2),
+                          frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4)))
+    other = {st["role"]: round(st["total_us"], 1) for st in stats if st["role"] not in nk}
+    med = statistics.median(tiled)
+    tf = g_fl / (g_us * 1e-6) / 1e12 if g_us else 0.0
+    return dict(workload=wname, sequence=seq, prompt_len=n, weights=w.weight_dtype,
+                ms=round(med, 3), ms_runs=[round(x, 3) for x in tiled], tok_s=round(n / (med * 1e-3), 1),
+                untiled_ms=round(statistics.median(untiled), 3),
+                untiled_tok_s=round(n / (statistics.median(untiled) * 1e-3), 1),
+                same_first_token=t1 == t2, gemm=gemms,
+                gemm_total=dict(us=round(g_us, 1), gflop=round(g_fl / 1e9, 2), tflops=round(tf, 2),
+                                frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4)),
+                other_us=other)
+
+
 def log_entry(e):
     log(f"[bench] {e['workload']}: {e['value']} tok/s, {e['ms_per_step']} ms/step (median of {e['runs']}), "
         f"whole generation {e['full_generation']['ms_per_step']} ms/step")
@@ -638,6 +721,7 @@ def main():
     ap.add_argument("--workloads", default=",".join(WORKLOADS), help="comma-separated; the first is the headline")
     ap.add_argument("--no-full", action="store_true", help="skip the timed runs of the whole generation")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle samples (CPU baseline)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-throughput measurements")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known traffic that "
                          "scales the HBM byte counters of a rocprofv3 --pmc run)")
@@ -700,6 +784,13 @@ def main():
         results[wn] = measure(wn, args.steps, args.warmup, args.runs, not args.no_full)
         entries[wn] = entry(results[wn])
         log_entry(entries[wn])
+    prefill = []
+    if not args.no_prefill:
+        for pw, ps in PREFILL:
+            r = measure_prefill(pw, ps, args.runs)
+            prefill.append(r)
+            log(f"[bench] prefill {pw} seq {ps} ({r['prompt_len']} ids): {r['ms']} ms = {r['tok_s']} tok/s "
+                f"(decode kernels: {r['untiled_ms']} ms); GEMMs {r['gemm_total']}")
     if pool is not None:
         log("[bench] waiting for the oracle samples ...")
         for wn in wnames:
@@ -731,7 +822,7 @@ def main():
                                          "step_gbps", "step_hbm_frac", "copy_gbps", "step_copy_frac",
                                          "kernel_us_per_step", "ttft_s", "sync_ms_per_step", "sync_value",
                                          "full_generation")},
-           "workloads_order": wnames, "workloads": entries}
+           "workloads_order": wnames, "workloads": entries, "prefill": prefill}
     print(json.dumps(out), flush=True)
 
 

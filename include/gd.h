@@ -238,6 +238,12 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                              * output projection is the VALU GEMV (at most 4 rows, or any
                              * row count with GD_OPT_LINEAR_VARIANT = 1) the split-context
                              * attention always uses 8 (the GEMV's prologue merges them) */
+#define GD_OPT_TILED_PREFILL 10 /* 1 (default): prompts of at least 64 tokens run the tiled
+                                * prompt pass (512 rows at a time: 64 x 64 matrix-core GEMM
+                                * tiles with the decode epilogues, tiled causal attention with
+                                * K/V tiles in LDS) when the weights are float or bf16 and
+                                * head_dim is 64; 0: every prompt runs the decode kernels over
+                                * 32 rows at a time */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

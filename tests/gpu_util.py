@@ -124,18 +124,24 @@ def token_checksum(tokens: np.ndarray) -> str:
 
 # A greedy token may flip only at a step whose oracle top-2 margin is below this, the
 # known near ties (every such step of the full-size workloads is listed in the design doc),
-# and at most twice the largest logit difference seen so far in the sequence. The GPU
-# logits of every configuration differ from the oracle's by well under 5e-5 (fp32
-# sums in another order), so a wider gap cannot flip a token.
+# and at most twice the largest logit difference seen so far in the sequence. With a
+# float KV cache the GPU logits differ from the oracle's by under 1e-5 (fp32 sums in
+# another order); with a bf16 cache, K/V values that fall on either side of a bf16
+# rounding boundary on the two sides move logits by up to ~5e-4, hence the wider bound.
 NEAR_TIE_MARGIN = 1e-4
+NEAR_TIE_MARGIN_KV16 = 1e-3
+
+
+def near_tie_margin(workload) -> float:
+    return NEAR_TIE_MARGIN_KV16 if workload.init.kv_bf16 else NEAR_TIE_MARGIN
 
 # Parity records of the end-to-end runs of this session (printed in the terminal
 # summary by conftest.py).
 RECORDS = []
 
 
-def new_record(config: str, B: int, n: int, tol: float) -> dict:
-    rec = {"config": config, "seqs": B, "steps": n, "tol": tol, "flips": [], "max_dlogit": 0.0,
+def new_record(config: str, B: int, n: int, tol: float, tie: float = NEAR_TIE_MARGIN) -> dict:
+    rec = {"config": config, "seqs": B, "steps": n, "tol": tol, "tie": tie, "flips": [], "max_dlogit": 0.0,
            "max_dlogit_full": 0.0, "full_rows": 0, "sampled_rows": 0, "tok_gpu": "", "tok_ref": "",
            "forced_max_dlogit": None}
     RECORDS.append(rec)
@@ -153,9 +159,9 @@ def format_record(r: dict) -> str:
 
 def check_flip(rec: dict, b: int, i: int, margin: float, seen: float, gpu_t: int, ref_t: int) -> None:
     """A flipped greedy token passes only as a known near tie (see NEAR_TIE_MARGIN)."""
-    assert margin <= NEAR_TIE_MARGIN and margin <= 2 * seen, (
+    assert margin <= rec["tie"] and margin <= 2 * seen, (
         f"{rec['config']} seq {b} step {i}: token {gpu_t} != oracle {ref_t} with oracle top-2 margin "
-        f"{margin:.3e} (known near ties are below {NEAR_TIE_MARGIN:g}; twice the max |dlogit| so far is "
+        f"{margin:.3e} (known near ties are below {rec['tie']:g}; twice the max |dlogit| so far is "
         f"{2 * seen:.3e})")
     rec["flips"].append((b, i, margin, seen))
 
@@ -182,7 +188,8 @@ def check_sample_flip(rec, b, i, logits, sampling, u, gpu_t, ref_t):
     rec["flips"].append((b, i, gap, 0.0))
 
 
-def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run", sampling=None, plens=None):
+def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run", sampling=None, plens=None,
+                       tie=NEAR_TIE_MARGIN):
     """Parity bar: identical tokens and |dlogit| <= tol over every vocabulary entry at
     every step of every sequence. A greedy flip passes only as a known near tie
     (check_flip), a sampled one only at a cumulative-weight boundary (check_sample_flip);
@@ -190,7 +197,7 @@ def compare_generation(gpu_tok, gpu_lg, ref_tok, ref_lg, tol, config="run", samp
     top_k, seed) of a sampled run, ``plens`` its prompt lengths. Returns the parity
     record (also kept in RECORDS)."""
     B, n = ref_tok.shape
-    rec = new_record(config, B, n, tol)
+    rec = new_record(config, B, n, tol, tie)
     rec["tok_gpu"], rec["tok_ref"] = token_checksum(gpu_tok), token_checksum(ref_tok)
     for b in range(B):
         seen = 0.0

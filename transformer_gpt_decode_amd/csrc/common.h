@@ -82,15 +82,15 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Maximum over aligned groups of G lanes (G = 8 or 64).
+// Maximum over aligned groups of G lanes (G = 8, 16 or 64).
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-  static_assert(G == 8 || G == 64, "group size");
+  static_assert(G == 8 || G == 16 || G == 64, "group size");
   v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
   v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
   v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  if (G >= 16) v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
   if (G == 64) {
-    v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
     const int b = __float_as_int(v);
     v = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));

@@ -239,12 +239,23 @@ __global__ __launch_bounds__(GD_SAMPLE_NT) void k_sample(SampleParams p) {
   __syncthreads();
   uint32_t key[GD_SAMPLE_VPT];
   int nan_i = 0x7fffffff;
+  if (i0 + GD_SAMPLE_VPT <= V) {
+    // a whole span: loads at immediate offsets from one base address
+    const float* b = L + i0;
 #pragma unroll
-  for (int j = 0; j < GD_SAMPLE_VPT; ++j) {
-    const int i = i0 + j;
-    const float f = L[min(i, V - 1)];
-    key[j] = (i < V && f == f) ? sample_key(f) : 0u;
-    if (i < V && f != f) nan_i = min(nan_i, i);
+    for (int j = 0; j < GD_SAMPLE_VPT; ++j) {
+      const float f = b[j];
+      key[j] = f == f ? sample_key(f) : 0u;
+      if (f != f) nan_i = min(nan_i, i0 + j);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < GD_SAMPLE_VPT; ++j) {
+      const int i = i0 + j;
+      const float f = i < V ? L[i] : 0.f;
+      key[j] = (i < V && f == f) ? sample_key(f) : 0u;
+      if (i < V && f != f) nan_i = min(nan_i, i);
+    }
   }
   if (nan_i != 0x7fffffff) atomicMin(&s_nan, nan_i);
   // radix select of the k-th largest key, 8 bits at a time from the top

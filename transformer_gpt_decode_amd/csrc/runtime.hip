@@ -23,6 +23,7 @@
 #include "linear.h"
 #include "attention.h"
 #include "misc.h"
+#include "prefill.h"
 
 // ------------------------------------------------------------------ errors
 
@@ -331,6 +332,10 @@ struct GraphKey {
 static const int kFusedAttnOMaxT = 256;
 // Decode-step graphs kept per model.
 static const size_t kMaxGraphs = 16;
+// Prompts of at least kPrefillMinRows tokens run the tiled prompt pass, kPrefillChunk
+// rows at a time; shorter ones run the decode kernels over <= 32 rows per pass.
+static const int kPrefillMinRows = 64;
+static const int kPrefillChunk = 512;
 
 struct gd_model {
   gd_config c;
@@ -342,6 +347,7 @@ struct gd_model {
   bool fuse_attn_o = true;
   int attn_chunks = 0;   // split-context chunks per row: 0 auto, 1 or GD_ATT_NCH (GD_OPT_ATTN_CHUNKS)
   bool use_fold = true;  // GEMV pre-norms folded into the weights when available (GD_OPT_FOLD_NORM)
+  bool use_pf = true;    // long prompts take the tiled prompt pass (GD_OPT_TILED_PREFILL)
   // temperature / top-k sampling instead of the greedy argmax (gd_set_sampling)
   bool sample = false;
   int top_k = 1;
@@ -379,6 +385,10 @@ struct gd_model {
   // scratch offsets (bytes)
   size_t o_x, o_q, o_attn, o_h, o_amv, o_ami, o_apart, o_zero;
   size_t o_slog = 0;   // logits rows the sampler reads when the caller asks for none
+  // the tiled prompt pass (kPrefillChunk rows): residual, normalized rows, queries,
+  // attention output, MLP hidden
+  bool pf_ok = false;
+  size_t o_px = 0, o_pxn = 0, o_pq = 0, o_pattn = 0, o_ph = 0;
   size_t o_rseq, o_rpos, o_rtok, o_rkv, o_rcs, o_pseq, o_ppos, o_ptok, o_pkv, o_pcs, o_len, o_cap, o_sids, o_table, o_err, o_rope;
 
   // host mirror
@@ -562,6 +572,17 @@ static void layout(gd_model* m) {
   m->o_ami = take(m->am_parts * R * 4);
   m->o_apart = take(R * c.n_head * GD_ATT_NCH * (c.head_dim + 2) * 4);
   m->o_slog = take(R * (size_t)c.vocab * 4);
+  // the tiled prompt pass: float or bf16 weights, head_dim 64, widths multiples of 32
+  m->pf_ok = m->wt != GD_WEIGHT_Q8 && c.head_dim == 64 && c.d_model % 32 == 0 && c.d_ff % 32 == 0 &&
+             m->qdim % 32 == 0 && c.d_model <= PF_NT * 16 && (c.n_head % c.n_kv_head) == 0;
+  if (m->pf_ok) {
+    const size_t P = kPrefillChunk;
+    m->o_px = take(P * d * 4);
+    m->o_pxn = take(P * d * 4);
+    m->o_pq = take(P * (size_t)m->qdim * 4);
+    m->o_pattn = take(P * (size_t)m->qdim * 4);
+    m->o_ph = take(P * ff * 4);
+  }
   // zeros (cleared at bind, never written): the bias or residual of layers that have none
   m->o_zero = take((size_t)std::max({m->qkvdim, m->fcN, (int)d, (int)ff}) * 4);
   m->o_rseq = take(R * 4);
@@ -986,6 +1007,8 @@ extern "C" gd_status gd_set_option(gd_model* m, int32_t opt, int32_t v) {
     m->fuse_attn_o = v != 0;
   } else if (opt == GD_OPT_FOLD_NORM) {
     m->use_fold = v != 0;
+  } else if (opt == GD_OPT_TILED_PREFILL) {
+    m->use_pf = v != 0;
   } else if (opt == GD_OPT_ATTN_CHUNKS) {
     if (v != 0 && v != 1 && v != GD_ATT_NCH) return set_err(GD_ERR_INVALID, "attention chunks must be 0, 1 or %d", GD_ATT_NCH);
     m->attn_chunks = v;
@@ -1210,6 +1233,57 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
   return r;
 }
 
+// Final norm + logits (tied embedding or untied head) + the greedy argmax (or the
+// sampled token) of rows [head_row, head_row + head_rows) of the residual rows x.
+static hipError_t enqueue_head(gd_model* m, hipStream_t st, const RowParams& rp, const float* x, int head_row,
+                               int head_rows, int* head_out, float* logits) {
+  const gd_config& c = m->c;
+  const int d = c.d_model;
+  const bool gpt2 = c.arch == GD_ARCH_GPT2;
+  const int nrm = gpt2 ? NORM_LN : NORM_RMS;
+  const bool fold = m->folded && m->use_fold;
+  hipError_t e;
+  LinParams base;
+  memset(&base, 0, sizeof(base));
+  base.eps = c.norm_eps;
+  base.err = m->sp<int>(m->o_err);
+  base.hd = c.head_dim;
+  base.Hq = c.n_head;
+  {
+    // final norm + logits (tied embedding or untied head) + greedy argmax partials
+    LinParams p = base;
+    p.pro = PRO_COPY;
+    p.x = x + (size_t)head_row * d; p.ldx = d;
+    p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
+    p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
+    if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(gpt2 ? m->o_swte : m->o_shead);
+    if (fold) {
+      p.wf = m->w + m->o_fhead; p.wfl = m->w + m->o_tfhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s);
+    }
+    p.epi = EPI_ARGMAX;
+    p.M = head_rows;
+    p.row_kvoff = rp.row_kvoff + head_row;
+    p.rope_cs = nullptr;
+    p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
+    // the sampler reads whole logit rows: the caller's, or the scratch rows
+    p.logits = logits ? logits : (m->sample ? m->sp<float>(m->o_slog) : nullptr);
+    p.ldl = c.vocab;
+    if ((e = run_linear(m, st, "linear.head", p, head_out)) != hipSuccess) return e;
+    if (m->sample) {
+      // temperature / top-k draw over each head row (replaces the greedy token)
+      SampleParams sp;
+      sp.logits = p.logits; sp.ldl = c.vocab; sp.V = c.vocab; sp.top_k = m->top_k;
+      sp.inv_temp = m->inv_temp; sp.seed = m->seed;
+      sp.row_seq = rp.row_seq + head_row; sp.row_pos = rp.row_pos + head_row;
+      sp.out = head_out;
+      ProfScope ps(m, st, "sample", "k_sample", (double)head_rows * c.vocab * 4);
+      GD_LAUNCH(k_sample, dim3(head_rows), dim3(GD_SAMPLE_NT), 0, st, sp);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 // Enqueues the forward pass of M (<= 32) rows with device-resident row metadata.
 // If head_out is not NULL, computes logits/argmax for rows [head_row, head_row + head_rows).
 static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp, int M, int max_T, int head_row,
@@ -1379,38 +1453,139 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       if ((e = run_linear(m, st, "linear.down", p)) != hipSuccess) return e;
     }
   }
-  if (head_out) {
-    // final norm + logits (tied embedding or untied head) + greedy argmax partials
-    LinParams p = base;
-    p.pro = PRO_COPY;
-    p.x = x + (size_t)head_row * d; p.ldx = d;
-    p.norm = nrm; p.ng = m->wf(m->o_nfg); p.nb = gpt2 ? m->wf(m->o_nfb) : nullptr;
-    p.w = m->w + (gpt2 ? m->o_wte : m->o_head); p.wtl = m->w + m->o_thead; p.N = c.vocab; p.K = d;
-    if (m->wt == GD_WEIGHT_Q8) p.wsc = m->wf(gpt2 ? m->o_swte : m->o_shead);
-    if (fold) {
-      p.wf = m->w + m->o_fhead; p.wfl = m->w + m->o_tfhead; p.bf = m->wf(m->o_fhead_b); p.fs = m->wf(m->o_fhead_s);
+  if (head_out) return enqueue_head(m, st, rp, x, head_row, head_rows, head_out, logits);
+  return hipSuccess;
+}
+
+// ------------------------------------------------------------ tiled prompt pass
+
+template <int WT>
+static void launch_gemm_pf(hipStream_t st, const LinParams& p) {
+  const dim3 g(iceil(p.N, PF_BN), iceil(p.M, PF_BM)), b(PF_NT);
+  switch (p.epi) {
+    case EPI_PLAIN: GD_LAUNCH((k_gemm_pf<WT, EPI_PLAIN>), g, b, 0, st, p); break;
+    case EPI_GELU: GD_LAUNCH((k_gemm_pf<WT, EPI_GELU>), g, b, 0, st, p); break;
+    case EPI_SWIGLU: GD_LAUNCH((k_gemm_pf<WT, EPI_SWIGLU>), g, b, 0, st, p); break;
+    case EPI_QKV: GD_LAUNCH((k_gemm_pf<WT, EPI_QKV>), g, b, 0, st, p); break;
+    default: GD_LAUNCH((k_gemm_pf<WT, EPI_QKV_ROPE>), g, b, 0, st, p); break;
+  }
+}
+
+// One GEMM of the prompt pass (profiled as role `role`: 2 M N K flops, the bytes of
+// the weights, the rows in and out).
+static hipError_t run_gemm_pf(gd_model* m, hipStream_t st, const char* role, const LinParams& p) {
+  char kn[48];
+  snprintf(kn, sizeof(kn), "k_gemm_pf<%d, %d>", m->wt == GD_WEIGHT_F32 ? 0 : 1, p.epi);
+  ProfScope ps(m, st, role, kn, (double)p.N * p.K * m->elt + 4.0 * p.M * (p.K + p.N));
+  if (m->wt == GD_WEIGHT_F32) launch_gemm_pf<0>(st, p);
+  else launch_gemm_pf<1>(st, p);
+  return hipGetLastError();
+}
+
+static hipError_t run_rownorm(gd_model* m, hipStream_t st, const float* x, const float* g, const float* b, float* y,
+                              int M) {
+  const gd_config& c = m->c;
+  ProfScope ps(m, st, "pf.norm", "k_rownorm", (double)M * c.d_model * 8.0);
+  if (c.arch == GD_ARCH_GPT2)
+    GD_LAUNCH(k_rownorm<NORM_LN>, dim3(M), dim3(PF_NT), 0, st, x, c.d_model, g, b, c.norm_eps, c.d_model, y, c.d_model);
+  else
+    GD_LAUNCH(k_rownorm<NORM_RMS>, dim3(M), dim3(PF_NT), 0, st, x, c.d_model, g, g, c.norm_eps, c.d_model, y,
+              c.d_model);
+  return hipGetLastError();
+}
+
+// The prompt pass over M (<= kPrefillChunk) rows of sequence `seq` at positions
+// p0 .. p0 + M - 1, whose metadata rp holds (rp.x = the prompt pass's residual rows):
+// pre-norm, QKV GEMM (K/V appended), tiled causal attention, output projection GEMM,
+// pre-norm, MLP GEMMs; then, if head_out is given, the head of the last row.
+static hipError_t enqueue_prefill_tiled(gd_model* m, hipStream_t st, const RowParams& rp, int seq, int M, int p0,
+                                        int* head_out, float* logits) {
+  const gd_config& c = m->c;
+  const int d = c.d_model, ff = c.d_ff;
+  const bool gpt2 = c.arch == GD_ARCH_GPT2;
+  float* x = m->sp<float>(m->o_px);
+  float* xn = m->sp<float>(m->o_pxn);
+  float* q = m->sp<float>(m->o_pq);
+  float* att = m->sp<float>(m->o_pattn);
+  float* h = m->sp<float>(m->o_ph);
+  const float* zero = m->sp<float>(m->o_zero);
+  hipError_t e;
+  LinParams base;
+  memset(&base, 0, sizeof(base));
+  base.err = m->sp<int>(m->o_err);
+  base.hd = c.head_dim;
+  base.Hq = c.n_head;
+  base.row_kvoff = rp.row_kvoff;
+  base.M = M;
+  base.pro = PRO_COPY;
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& t = m->L[l];
+    if ((e = run_rownorm(m, st, x, m->wf(t.n1g), t.n1b ? m->wf(t.n1b) : nullptr, xn, M)) != hipSuccess) return e;
+    {
+      LinParams p = base;
+      p.x = xn; p.ldx = d;
+      p.w = m->w + t.wqkv; p.N = m->qkvdim; p.K = d;
+      p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
+      p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
+      p.y = q; p.ldy = m->qdim;
+      p.qdim = m->qdim; p.kdim = m->kdim;
+      p.rope_cs = rp.row_cs;
+      p.kc = m->kpool(l); p.vc = m->vpool(l); p.kv16 = m->kv16;
+      p.kv_hstride = m->bsize * c.head_dim;
+      if ((e = run_gemm_pf(m, st, "pf.qkv", p)) != hipSuccess) return e;
     }
-    p.epi = EPI_ARGMAX;
-    p.M = head_rows;
-    p.row_kvoff = rp.row_kvoff + head_row;
-    p.rope_cs = nullptr;
-    p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
-    // the sampler reads whole logit rows: the caller's, or the scratch rows
-    p.logits = logits ? logits : (m->sample ? m->sp<float>(m->o_slog) : nullptr);
-    p.ldl = c.vocab;
-    if ((e = run_linear(m, st, "linear.head", p, head_out)) != hipSuccess) return e;
-    if (m->sample) {
-      // temperature / top-k draw over each head row (replaces the greedy token)
-      SampleParams sp;
-      sp.logits = p.logits; sp.ldl = c.vocab; sp.V = c.vocab; sp.top_k = m->top_k;
-      sp.inv_temp = m->inv_temp; sp.seed = m->seed;
-      sp.row_seq = rp.row_seq + head_row; sp.row_pos = rp.row_pos + head_row;
-      sp.out = head_out;
-      ProfScope ps(m, st, "sample", "k_sample", (double)head_rows * c.vocab * 4);
-      GD_LAUNCH(k_sample, dim3(head_rows), dim3(GD_SAMPLE_NT), 0, st, sp);
+    {
+      PfAttnParams a;
+      a.q = q; a.ldq = m->qdim;
+      a.kc = m->kpool(l); a.vc = m->vpool(l);
+      const bool paged = c.kv_block_size > 0;
+      a.table = paged ? m->sp<int>(m->o_table) + (size_t)seq * m->max_blocks : nullptr;
+      a.kv0 = paged ? 0 : (long long)seq * c.n_kv_head * m->bsize * c.head_dim;
+      a.block_size = m->bsize; a.nblk = m->nblk; a.Hq = c.n_head; a.Hkv = c.n_kv_head; a.M = M; a.p0 = p0;
+      a.scale = 1.0f / std::sqrt((float)c.head_dim);
+      a.out = att; a.ldo = m->qdim;
+      const dim3 g(iceil(M, 64), c.n_head), b(PF_NT);
+      // K/V of every attended position: each query tile reads its keys once
+      double kvb = 0;
+      for (int r0 = 0; r0 < M; r0 += 64) kvb += (double)(p0 + std::min(r0 + 64, M)) * c.n_head * c.head_dim * m->kv_elt * 2;
+      ProfScope ps(m, st, "pf.attention", "k_attn_prefill", kvb + 8.0 * M * m->qdim);
+      if (paged && m->kv16) GD_LAUNCH((k_attn_prefill<64, true, true>), g, b, 0, st, a);
+      else if (paged) GD_LAUNCH((k_attn_prefill<64, true, false>), g, b, 0, st, a);
+      else if (m->kv16) GD_LAUNCH((k_attn_prefill<64, false, true>), g, b, 0, st, a);
+      else GD_LAUNCH((k_attn_prefill<64, false, false>), g, b, 0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    {
+      LinParams p = base;
+      p.x = att; p.ldx = m->qdim;
+      p.w = m->w + t.wo; p.N = d; p.K = m->qdim;
+      p.epi = EPI_PLAIN;
+      p.bias = t.bo ? m->wf(t.bo) : zero;
+      p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
+      if ((e = run_gemm_pf(m, st, "pf.o", p)) != hipSuccess) return e;
+    }
+    if ((e = run_rownorm(m, st, x, m->wf(t.n2g), t.n2b ? m->wf(t.n2b) : nullptr, xn, M)) != hipSuccess) return e;
+    {
+      LinParams p = base;
+      p.x = xn; p.ldx = d;
+      p.w = m->w + t.wfc; p.N = m->fcN; p.K = d;
+      p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
+      p.bias = t.bfc ? m->wf(t.bfc) : zero;
+      p.resid = zero; p.ldr = 0;
+      p.y = h; p.ldy = ff;
+      if ((e = run_gemm_pf(m, st, "pf.fc", p)) != hipSuccess) return e;
+    }
+    {
+      LinParams p = base;
+      p.x = h; p.ldx = ff;
+      p.w = m->w + t.wproj; p.N = d; p.K = ff;
+      p.epi = EPI_PLAIN;
+      p.bias = t.bproj ? m->wf(t.bproj) : zero;
+      p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
+      if ((e = run_gemm_pf(m, st, "pf.down", p)) != hipSuccess) return e;
+    }
   }
+  if (head_out) return enqueue_head(m, st, rp, x, M - 1, 1, head_out, logits);
   return hipSuccess;
 }
 
@@ -1447,6 +1622,30 @@ extern "C" gd_status gd_prefill(gd_model* m, int32_t seq, const int32_t* tokens,
   HIP_TRY(m, hipMemcpyAsync(m->sp<int>(m->o_ptok), ht, (size_t)n * 4, hipMemcpyHostToDevice, s));
   HIP_TRY(m, hipMemcpyAsync(m->sp<int>(m->o_len) + seq, hs + 3 * n, 4, hipMemcpyHostToDevice, s));
   if ((st = staging_done(m)) != GD_OK) return st;
+  if (m->pf_ok && m->use_pf && n >= kPrefillMinRows) {
+    for (int r0 = 0; r0 < n; r0 += kPrefillChunk) {
+      const int M = std::min(kPrefillChunk, n - r0);
+      const bool last = r0 + M == n;
+      RowParams rp = row_params(m, m->sp<int>(m->o_pseq) + r0, m->sp<int>(m->o_ppos) + r0,
+                                m->sp<int>(m->o_ptok) + r0, m->sp<long long>(m->o_pkv) + r0,
+                                c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_pcs) + (size_t)r0 * c.head_dim : nullptr);
+      rp.x = m->sp<float>(m->o_px);
+      hipError_t e;
+      {
+        ProfScope ps(m, s, "setup", "k_setup_rows", (double)M * c.d_model * (m->elt * 2 + 4));
+        GD_LAUNCH(k_setup_rows, dim3(M), dim3(GD_WG), 0, s, rp);
+        e = hipGetLastError();
+      }
+      if (e == hipSuccess)
+        e = enqueue_prefill_tiled(m, s, rp, seq, M, p0 + r0, last ? next_dev : nullptr, last ? logits_dev : nullptr);
+      if (e != hipSuccess) {
+        m->poisoned = true;
+        return set_err(GD_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+      }
+    }
+    m->len[seq] = p0 + n;
+    return GD_OK;
+  }
   for (int r0 = 0; r0 < n; r0 += GD_MAX_ROWS) {
     int M = std::min(GD_MAX_ROWS, n - r0);
     bool last = r0 + M == n;
