@@ -45,8 +45,11 @@ MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix peak
 METRIC = "decode tok/s at GPT-2-124M shape, batch 1 and 32; achieved HBM GB/s"
 
 
+T0 = time.perf_counter()
+
+
 def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+    print(f"{time.perf_counter() - T0:8.2f}s", *a, file=sys.stderr, flush=True)
 
 
 def setup(wname: str):
@@ -133,24 +136,28 @@ def measure(wname: str, steps, warmup: int, runs: int, full: bool):
     if full and n_decode != K:
         log(f"[bench] {wname}: {runs} timed runs of the whole generation ({n_decode} steps): "
             + " ".join(f"{x:.4f}" for x in fullg) + " ms/step")
-    # synchronous variant: the new tokens read back and the stream synchronized every step
-    rewind(m, tok, first, plen)
-    host = torch.empty(tok.shape, dtype=tok.dtype, pin_memory=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        m.decode_step(seq_ids, tok, tok)
-        host.copy_(tok, non_blocking=True)
-        torch.cuda.current_stream().synchronize()
-    ms_sync = (time.perf_counter() - t0) * 1e3 / K
-    log(f"[bench] {wname}: synchronous run done")
-    # every generated token (the first from the prompt) for the checksum against the oracle
-    rewind(m, tok, first, plen)
-    hist = [first.cpu().numpy().copy()]
-    for _ in range(n_decode):
-        m.decode_step(seq_ids, tok, tok)
-        hist.append(tok.clone())
-    gpu_tokens = np.stack([h if isinstance(h, np.ndarray) else h.cpu().numpy() for h in hist], 1)
+    if PROFILE_MODE[0] == 1:
+        # counter runs collect per dispatch, serialized: only the passes they profile
+        ms_sync, gpu_tokens = float("nan"), first.cpu().numpy()[:, None]
+    else:
+        # synchronous variant: the new tokens read back and the stream synchronized every step
+        rewind(m, tok, first, plen)
+        host = torch.empty(tok.shape, dtype=tok.dtype, pin_memory=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            m.decode_step(seq_ids, tok, tok)
+            host.copy_(tok, non_blocking=True)
+            torch.cuda.current_stream().synchronize()
+        ms_sync = (time.perf_counter() - t0) * 1e3 / K
+        log(f"[bench] {wname}: synchronous run done")
+        # every generated token (the first from the prompt) for the checksum against the oracle
+        rewind(m, tok, first, plen)
+        hist = [first.cpu().numpy().copy()]
+        for _ in range(n_decode):
+            m.decode_step(seq_ids, tok, tok)
+            hist.append(tok.clone())
+        gpu_tokens = np.stack([h if isinstance(h, np.ndarray) else h.cpu().numpy() for h in hist], 1)
     assert m.device_errors() == 0
     # profiled eager pass over the window: per-kernel time and bytes
     rewind(m, tok, first, plen)
@@ -621,10 +628,10 @@ def entry(res):
 PREFILL = [("gpt2_stress", 0), ("llama_b8", 4)]
 
 
-def measure_prefill(wname: str, seq: int, runs: int):
+def measure_prefill(wname: str, seq: int, runs: int, untiled: bool = True):
     """Prompt throughput of one sequence's prompt: the tiled prompt pass (median of
-    `runs`), the same prompt through the decode kernels (32 rows per pass), and a
-    profiled pass giving each GEMM's 2 M N K over its mean time."""
+    `runs`), the same prompt through the decode kernels (32 rows per pass; skipped with
+    untiled=False), and a profiled pass giving each GEMM's 2 M N K over its mean time."""
     import statistics
     import torch
     import synth
@@ -659,7 +666,7 @@ def measure_prefill(wname: str, seq: int, runs: int):
         return out[1:], int(tok.item())
 
     tiled, t1 = run(True, runs)
-    untiled, t2 = run(False, runs)
+    untiled, t2 = run(False, runs) if untiled else ([float("nan")], t1)
     m.set_option(gd.OPT_TILED_PREFILL, 1)
     m.reset_seq(seq)
     m.set_option(gd.OPT_PROFILE, 1)
@@ -722,6 +729,7 @@ def main():
     ap.add_argument("--no-full", action="store_true", help="skip the timed runs of the whole generation")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle samples (CPU baseline)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prompt-throughput measurements")
+    ap.add_argument("--no-decode", action="store_true", help="measure the prompt pass only (no decode workload)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known traffic that "
                          "scales the HBM byte counters of a rocprofv3 --pmc run)")
@@ -761,7 +769,7 @@ def main():
         if wn not in SHAPES:
             sys.exit(f"unknown workload {wn}; choose from {','.join(WORKLOADS)}")
     # the oracle samples start first, in processes that never touch the GPU
-    pool, jobs = (None, {}) if args.no_cpu else start_cpu_samples(wnames)
+    pool, jobs = (None, {}) if (args.no_cpu or args.no_decode) else start_cpu_samples(wnames)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -779,6 +787,13 @@ def main():
     COPY_GBPS[0] = copy_rate()
     log(f"[bench] device-to-device copy: {COPY_GBPS[0]:.0f} GB/s (read + write)")
     results, entries = {}, {}
+    if args.no_decode:
+        prefill = [measure_prefill(pw, ps, args.runs, untiled=PROFILE_MODE[0] != 1) for pw, ps in PREFILL]
+        for r in prefill:
+            log(f"[bench] prefill {r['workload']} seq {r['sequence']} ({r['prompt_len']} ids): {r['ms']} ms = "
+                f"{r['tok_s']} tok/s; GEMMs {r['gemm_total']}")
+        print(json.dumps({"prefill": prefill}), flush=True)
+        return
     for wn in wnames:
         log(f"[bench] workload {wn}: warmup {args.warmup}, {args.runs} runs of {args.steps or 'all'} steps")
         results[wn] = measure(wn, args.steps, args.warmup, args.runs, not args.no_full)

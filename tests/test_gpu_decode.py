@@ -487,6 +487,18 @@ def test_tiled_prefill_gpt2(wdt, kv):
                      config=f"tiled prefill gpt2 ({wdt} weights, {kv} KV)")
 
 
+def test_tiled_prefill_split_edges():
+    """Prompt lengths at the key-tile edges of the tiled pass: 64 ids (one key tile, the
+    attention written unsplit), 65 and 128 (two tiles: one query tile's second split
+    empty), 191 (three tiles, ragged last query tile)."""
+    w = synth.Workload("gpt2_hd64_prefill_edges", GPT2_HD64_LONG, synth.Init(), 23, 4, (191, 191), 6)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    full = synth.make_prompts(w)
+    prompts = [full[0][:64], full[1][:65], full[2][:128], full[3][:191]]
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, config="tiled prefill gpt2 (64, 65, 128, 191 ids)")
+    assert not rep["flips"]
+
+
 def test_tiled_prefill_llama_long_paged():
     """Llama layout (RoPE in the QKV GEMM epilogue, 3 query heads per KV head, SwiGLU),
     shuffled paged bf16 cache, prompts of 600-2000 ids: up to four 512-row chunks, each
