@@ -538,3 +538,109 @@ def test_prefill_in_two_calls():
     rep = compare_generation(got, lg.cpu().numpy()[None], ref_tok, ref_lg, 1e-3, "prefill in two calls")
     assert not rep["flips"]
     m.close()
+
+
+# ------------------------------------------------------- replays and the NaN rule
+
+def _replay_logits(m, plens, toks, n, dev):
+    """Logits of the same decode step (every sequence rewound to its prompt end and fed
+    the same token) replayed n times, as one [n][B][V] array."""
+    import torch
+    B = len(plens)
+    out = []
+    tok = torch.tensor(toks, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    lg = torch.empty((B, m.cfg.vocab), dtype=torch.float32, device=dev)
+    for _ in range(n):
+        for b, p in enumerate(plens):
+            m.truncate_seq(b, p)
+        m.decode_step(list(range(B)), tok, nxt, lg)
+        out.append(lg.cpu().numpy().copy())
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("fuse", [0, 1], ids=["unfused", "fused"])
+def test_replay_determinism_batch1(fuse):
+    """GPT-2 124M shape, batch 1: one decode step replayed 100 times (one hipGraph). With
+    attention and the output projection in separate launches no float atomic is left and
+    the logits must be bitwise identical; the fused attention adds the heads' shares of
+    the projection with atomics in any order, so replays may differ in the last bits
+    (bounded here by 1e-5)."""
+    import transformer_gpt_decode_amd as gd
+    w = synth.WORKLOADS["gpt2_b1"]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    m = gd_model(w, W)
+    m.set_option(gd.OPT_FUSE_ATTN_O, fuse)
+    dev = device()
+    import torch
+    t = torch.zeros(1, dtype=torch.int32, device=dev)
+    m.prefill(0, prompts[0], t)
+    lg = _replay_logits(m, [len(prompts[0])], [int(t.item())], 100, dev)
+    assert m.device_errors() == 0 and np.all(np.isfinite(lg))
+    d = float(np.max(np.abs(lg - lg[0])))
+    print(f"batch-1 replays (fuse {fuse}): max |dlogit| across 100 replays {d:.3e}", flush=True)
+    if fuse == 0:
+        assert d == 0.0, d
+    else:
+        assert d <= 1e-5, d
+    m.close()
+
+
+def test_replay_spread_batch32():
+    """GPT-2 124M shape, 32 sequences: one decode step replayed 20 times. The split-K
+    matrix-core GEMMs and the fused attention + projection add with float atomics, so
+    replays may differ in the last bits; the spread is bounded (1e-5) and the greedy
+    tokens equal in every replay."""
+    w = synth.WORKLOADS["gpt2_b32"]
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    m = gd_model(w, W)
+    dev = device()
+    import torch
+    t = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    for b, p in enumerate(prompts):
+        m.prefill(b, p, t[b:b + 1])
+    lg = _replay_logits(m, [len(p) for p in prompts], t.cpu().tolist(), 20, dev)
+    assert m.device_errors() == 0 and np.all(np.isfinite(lg))
+    d = float(np.max(np.abs(lg - lg[0])))
+    print(f"batch-32 replays: max |dlogit| across 20 replays {d:.3e}", flush=True)
+    assert d <= 1e-5, d
+    am = np.argmax(lg, axis=2)
+    assert np.all(am == am[0])
+    m.close()
+
+
+def test_greedy_head_nan_rule():
+    """Row 77 of the tied embedding set to NaN makes logit 77 NaN in every row: the greedy
+    argmax of the fused head returns 77 for one row (GEMV head, decode-kernel prefill),
+    for six rows fed finite tokens (matrix-core head) and after a 70-id prompt (tiled
+    prompt pass); a row whose logits are all NaN (token 77 fed back) returns index 0, the
+    first NaN."""
+    import torch
+    w = synth.Workload("gpt2_hd64_nan", GPT2_HD64_LONG, synth.Init(), 24, 6, (70, 70), 2)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    o, shp = synth.offsets(w.shape)["wte"]
+    W[o + 77 * shp[1]:o + 78 * shp[1]] = np.nan
+    prompts = [[78 if x == 77 else int(x) for x in p] for p in synth.make_prompts(w)]   # finite embeddings
+    m = gd_model(w, W)
+    dev = device()
+    t = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    m.prefill(0, prompts[0][:5], t[0:1])          # decode kernels, one row
+    m.prefill(1, prompts[1], t[1:2])              # tiled prompt pass (70 ids)
+    for b in range(2, w.batch):
+        m.prefill(b, prompts[b][:3 + b], t[b:b + 1])
+    torch.cuda.synchronize()
+    assert t.cpu().tolist() == [77] * w.batch
+    # six rows fed finite tokens: the matrix-core head
+    feed = torch.tensor([1, 2, 3, 4, 5, 6], dtype=torch.int32, device=dev)
+    nxt = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    m.decode_step(list(range(w.batch)), feed, nxt)
+    torch.cuda.synchronize()
+    assert nxt.cpu().tolist() == [77] * w.batch
+    # token 77 fed back: its NaN embedding makes every logit NaN -> the first NaN, 0
+    m.decode_step([0], nxt[0:1], nxt[0:1])
+    torch.cuda.synchronize()
+    assert int(nxt[0].item()) == 0
+    assert m.device_errors() == 0
+    m.close()
