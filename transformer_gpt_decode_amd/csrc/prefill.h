@@ -203,14 +203,26 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
 // Causal attention of M prompt rows (positions p0 .. p0 + M - 1 of one sequence)
 // against the cache, which already holds their K/V. Workgroup (query tile t, query
 // head h, split s): 64 query rows against key tiles [s kt, (s + 1) kt) of the 64-position
-// tiles the query tile reaches; each key tile staged in LDS (float, widened from a bf16
-// cache), scores of a 4 x 4 block per thread, the online softmax per row over the 16
-// threads that share it, then P V for a 4-row x 4-dim block per thread. Positions after
-// a row's own are masked (never weighted). With one split (S = 1) the output o [M][ldo]
-// is written normalized at the head's columns; with S > 1 every split writes its
-// partial (running max, sum of weights, weighted V) per row and head, and
-// k_attn_pf_merge combines them. Splitting the key range gives the launch enough
-// workgroups for the CUs: one per (query tile, head) is 96 for a 512-row GPT-2 chunk.
+// tiles the query tile reaches, on the fp32 matrix cores. Wave w owns queries
+// 16 w .. 16 w + 15 of the tile and computes, per key tile, the transposed scores
+// S^T = K Q^T (keys as rows) and then O^T += V^T P^T:
+//  - v_mfma_f32_16x16x4f32 number s of a 16-key block contracts head dims 16 q + s, so
+//    lane l = 16 q + c holds K[key c][16 q .. 16 q + 15] (LDS) and Q[query c][same dims]
+//    (registers, loaded once);
+//  - the score accumulator of key block b holds S^T[keys 16 b + 4 q + v][query c], which
+//    is exactly the second product's operand P^T[k = q][n = c] for the key chunk
+//    {16 b + 4 q + v}, so P never goes through LDS; the matching V^T values come from a
+//    transposed copy of the V tile in LDS (4 consecutive keys per 16-byte read);
+//  - every value a lane holds belongs to its query c, so the online softmax rescales the
+//    output accumulators per lane; the running max is reduced over the four lanes of a
+//    query each key tile, the running sum only at the end.
+// Each key tile is staged in LDS (float, widened from a bf16 cache) while the next one
+// is loaded into registers. Positions after a row's own are masked (never weighted).
+// With one split (S = 1) the output o [M][ldo] is written normalized at the head's
+// columns; with S > 1 every split writes its partial (running max, sum of weights,
+// weighted V) per row and head, and k_attn_pf_merge combines them. Splitting the key
+// range gives the launch enough workgroups for the CUs: one per (query tile, head) is
+// 96 for a 512-row GPT-2 chunk.
 #define PF_MAXS 8          // key-range splits at most
 #define PF_PSTRIDE 68      // floats per partial: max, sum, 2 pad, 64 weighted-V values
 struct PfAttnParams {
@@ -225,149 +237,151 @@ struct PfAttnParams {
   float* part;                            // S > 1: partials [M][Hq][S][PF_PSTRIDE]
 };
 
+__device__ __forceinline__ float f4_at(const f32x4& v, int u) {
+  return u == 0 ? v.x : u == 1 ? v.y : u == 2 ? v.z : v.w;
+}
+
 template <int HD, bool PAGED, bool KV16>
 __global__ __launch_bounds__(PF_NT) void k_attn_prefill(PfAttnParams p) {
   static_assert(HD == 64, "head_dim 64");
-  constexpr int BQ = 64, BKV = 64, LS = HD + 4;   // LDS row stride (16-byte aligned)
-  __shared__ __align__(16) float sQ[BQ * LS];
-  __shared__ __align__(16) float sK[BKV * LS];
-  __shared__ __align__(16) float sV[BKV * LS];
-  __shared__ __align__(16) float sP[BQ * (BKV + 4)];
-  const int tid = threadIdx.x;
+  constexpr int BQ = 64, BKV = 64, LS = HD + 4;   // LDS row strides (16-byte aligned rows)
+  __shared__ __align__(16) float sK[BKV * LS];    // [key][dim]
+  __shared__ __align__(16) float sVt[HD * LS];    // [dim][key]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c = lane & 15;
   const int qt = blockIdx.x, h = blockIdx.y, kh = h / (p.Hq / p.Hkv), sp = blockIdx.z;
-  const int r0 = qt * BQ;                  // first row of the tile
-  const int ti = tid >> 4, tj = tid & 15;  // this thread: rows 4 ti .., keys (or dims) 4 tj ..
+  const int r0 = qt * BQ;
   const int last_pos = p.p0 + min(r0 + BQ, p.M) - 1;   // the tile's last query position
   const int kt0 = sp * p.kt, kt1 = min(last_pos / BKV + 1, kt0 + p.kt);   // this split's key tiles
-  // the partial of row 4 ti + a of the tile (S > 1)
-  auto part_at = [&](int a) {
-    return p.part + (((size_t)(r0 + 4 * ti + a) * p.Hq + h) * p.S + sp) * PF_PSTRIDE;
-  };
+  const int row = r0 + 16 * wave + c;                  // this lane's query (rows >= M never stored)
+  float* pp = p.part + (((size_t)row * p.Hq + h) * p.S + sp) * PF_PSTRIDE;
   if (kt0 >= kt1) {   // no key tile of this query tile falls in the split: an empty partial
+    if (row < p.M) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      if (r0 + 4 * ti + a < p.M) {
-        float* pp = part_at(a);
-        *reinterpret_cast<f32x4*>(pp + 4 + 4 * tj) = (f32x4){0.f, 0.f, 0.f, 0.f};
-        if (tj == 0) { pp[0] = -INFINITY; pp[1] = 0.f; }
-      }
+      for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(pp + 4 + 16 * dt + 4 * q4) = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (q4 == 0) { pp[0] = -INFINITY; pp[1] = 0.f; }
     }
     return;
   }
-  // the query tile (rows past M read as the last row; never stored)
-  for (int e = tid; e < BQ * (HD / 4); e += PF_NT) {
-    const int r = e / (HD / 4), d4 = e % (HD / 4);
-    const int row = min(r0 + r, p.M - 1);
-    *reinterpret_cast<f32x4*>(sQ + r * LS + 4 * d4) =
-        *reinterpret_cast<const f32x4*>(p.q + (size_t)row * p.ldq + h * HD + 4 * d4);
-  }
-  float mrow[4], lrow[4], o[4][4];
+  const int qpos = p.p0 + row;
+  // this lane's query values: dims 16 q4 .. 16 q4 + 15 of its row
+  f32x4 qv[4];
+  {
+    const float* src = p.q + (size_t)min(row, p.M - 1) * p.ldq + h * HD + 16 * q4;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    mrow[a] = -INFINITY;
-    lrow[a] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[a][d] = 0.f;
+    for (int u = 0; u < 4; ++u) qv[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
   }
+  // key tile loads: K unit e = tid + 256 u is (key e / 16, dims 4 (e % 16) ..), V unit
+  // is (key e % 64, dims 4 (e / 64) ..), so that the transposed V stores of a wave fall
+  // on 64 consecutive LDS words
+  f32x4 kr[4], vr[4];
+  auto kv_off = [&](int pos) -> size_t {
+    if (PAGED) {
+      const int bi = pos / p.block_size;
+      int blk = p.table[bi];
+      blk = (unsigned)blk < (unsigned)p.nblk ? blk : 0;
+      return (((size_t)blk * p.Hkv + kh) * p.block_size + (pos - bi * p.block_size)) * HD;
+    }
+    return (size_t)p.kv0 + ((size_t)kh * p.block_size + pos) * HD;
+  };
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + PF_NT * u;
+      const int pk = min(kt * BKV + (e >> 4), last_pos), pv = min(kt * BKV + (e & 63), last_pos);
+      kr[u] = kv_load4<KV16, false>(p.kc, kv_off(pk) + 4 * (e & 15));
+      vr[u] = kv_load4<KV16, false>(p.vc, kv_off(pv) + 4 * (e >> 6));
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + PF_NT * u;
+      *reinterpret_cast<f32x4*>(sK + (e >> 4) * LS + 4 * (e & 15)) = kr[u];
+      float* vt = sVt + (4 * (e >> 6)) * LS + (e & 63);
+      vt[0] = vr[u].x; vt[LS] = vr[u].y; vt[2 * LS] = vr[u].z; vt[3 * LS] = vr[u].w;
+    }
+  };
+  f32x4 oacc[4];   // O^T[dims 16 dt + 4 q4 + v][query c]
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+  load_tile(kt0);
   for (int kt = kt0; kt < kt1; ++kt) {
-    __syncthreads();   // the previous tile's K, V and P are no longer read
-    for (int e = tid; e < BKV * (HD / 4); e += PF_NT) {
-      const int r = e / (HD / 4), d4 = e % (HD / 4);
-      const int pos = min(kt * BKV + r, last_pos);
-      size_t off;
-      if (PAGED) {
-        const int bi = pos / p.block_size;
-        int blk = p.table[bi];
-        blk = (unsigned)blk < (unsigned)p.nblk ? blk : 0;
-        off = (((size_t)blk * p.Hkv + kh) * p.block_size + (pos - bi * p.block_size)) * HD + 4 * d4;
-      } else {
-        off = (size_t)p.kv0 + ((size_t)kh * p.block_size + pos) * HD + 4 * d4;
-      }
-      *reinterpret_cast<f32x4*>(sK + r * LS + 4 * d4) = kv_load4<KV16, false>(p.kc, off);
-      *reinterpret_cast<f32x4*>(sV + r * LS + 4 * d4) = kv_load4<KV16, false>(p.vc, off);
-    }
+    __syncthreads();   // the previous tile is no longer read
+    store_tile();
     __syncthreads();
-    // scores of rows 4 ti + a against keys 4 tj + b
-    float s[4][4];
+    if (kt + 1 < kt1) load_tile(kt + 1);   // in flight during this tile's MFMAs
+    // S^T for the four 16-key blocks
+    f32x4 st[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 4; ++b) {
+      f32x4 kv[4];
+      const float* src = sK + (16 * b + c) * LS + 16 * q4;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) s[a][b] = 0.f;
-#pragma unroll 4
-    for (int d = 0; d < HD; d += 4) {
-      f32x4 qa[4], kb[4];
+      for (int u = 0; u < 4; ++u) kv[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
+      st[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int a = 0; a < 4; ++a) qa[a] = *reinterpret_cast<const f32x4*>(sQ + (4 * ti + a) * LS + d);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) kb[b] = *reinterpret_cast<const f32x4*>(sK + (4 * tj + b) * LS + d);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          float t = s[a][b];
-          t = fmaf(qa[a].x, kb[b].x, t);
-          t = fmaf(qa[a].y, kb[b].y, t);
-          t = fmaf(qa[a].z, kb[b].z, t);
-          t = fmaf(qa[a].w, kb[b].w, t);
-          s[a][b] = t;
-        }
+      for (int s = 0; s < 16; ++s)
+        st[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(kv[s >> 2], s & 3), f4_at(qv[s >> 2], s & 3), st[b], 0, 0, 0);
     }
-    // online softmax per row: its 64 keys sit on the 16 threads tj of row group ti
+    // scale and mask; the tile's max over the query's 64 keys (this lane's 16 and the
+    // other three lanes of the query)
+    float sv[4][4];
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int qpos = p.p0 + r0 + 4 * ti + a;
-      float mx = -INFINITY;
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int kpos = kt * BKV + 4 * tj + b;
-        s[a][b] = kpos <= qpos ? s[a][b] * p.scale : -INFINITY;
-        mx = fmaxf(mx, s[a][b]);
+      for (int v = 0; v < 4; ++v) {
+        const int kpos = kt * BKV + 16 * b + 4 * q4 + v;
+        sv[b][v] = kpos <= qpos ? f4_at(st[b], v) * p.scale : -INFINITY;
+        tmax = fmaxf(tmax, sv[b][v]);
       }
-      mx = group_max<16>(mx);
-      // -inf only while every key so far is after the row (never in split 0, which holds
-      // key 0); then every weight below is 0 and the row stays empty
-      const float nm = fmaxf(mrow[a], mx);
-      const float sc = attn_rescale(mrow[a], nm);
-      float ls = 0.f;
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // -inf only while every key so far is after the query (never in split 0, which
+    // holds key 0); then every weight below is 0 and the query stays empty
+    const float nm = fmaxf(m_run, tmax);
+    const float alpha = attn_rescale(m_run, nm);
+    m_run = nm;
+    l_lane *= alpha;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float e = s[a][b] == -INFINITY ? 0.f : expf(s[a][b] - nm);
-        sP[(4 * ti + a) * (BKV + 4) + 4 * tj + b] = e;
-        ls += e;
-      }
-      lrow[a] = lrow[a] * sc + group_sum<16>(ls);
-      mrow[a] = nm;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) o[a][d] *= sc;
+    for (int dt = 0; dt < 4; ++dt) {
+      oacc[dt].x *= alpha; oacc[dt].y *= alpha; oacc[dt].z *= alpha; oacc[dt].w *= alpha;
     }
-    __syncthreads();
-    // o[rows 4 ti + a][dims 4 tj + d] += P . V
-#pragma unroll 4
-    for (int j = 0; j < BKV; ++j) {
-      const f32x4 vv = *reinterpret_cast<const f32x4*>(sV + j * LS + 4 * tj);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float pa = sP[(4 * ti + a) * (BKV + 4) + j];
-        o[a][0] = fmaf(pa, vv.x, o[a][0]);
-        o[a][1] = fmaf(pa, vv.y, o[a][1]);
-        o[a][2] = fmaf(pa, vv.z, o[a][2]);
-        o[a][3] = fmaf(pa, vv.w, o[a][3]);
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float e = sv[b][v] == -INFINITY ? 0.f : expf(sv[b][v] - nm);
+        sv[b][v] = e;
+        l_lane += e;
       }
-    }
+    // O^T += V^T P^T over the 16 key chunks {16 b + 4 q + v}
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const f32x4 vt = *reinterpret_cast<const f32x4*>(sVt + (16 * dt + c) * LS + 16 * b + 4 * q4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(vt, v), sv[b][v], oacc[dt], 0, 0, 0);
+      }
   }
+  float l = l_lane + __shfl_xor(l_lane, 16);
+  l += __shfl_xor(l, 32);
+  if (row >= p.M) return;
+  if (p.S == 1) {   // the whole key range: l > 0 (key 0 is visible to every row)
+    const float inv = 1.0f / l;
+    float* dst = p.out + (size_t)row * p.ldo + h * HD + 4 * q4;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int row = r0 + 4 * ti + a;
-    if (row >= p.M) continue;
-    if (p.S == 1) {   // the whole key range: l > 0 (key 0 is visible to every row)
-      const float inv = 1.0f / lrow[a];
-      *reinterpret_cast<f32x4*>(p.out + (size_t)row * p.ldo + h * HD + 4 * tj) =
-          (f32x4){o[a][0] * inv, o[a][1] * inv, o[a][2] * inv, o[a][3] * inv};
-    } else {
-      float* pp = part_at(a);
-      *reinterpret_cast<f32x4*>(pp + 4 + 4 * tj) = (f32x4){o[a][0], o[a][1], o[a][2], o[a][3]};
-      if (tj == 0) { pp[0] = mrow[a]; pp[1] = lrow[a]; }
-    }
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<f32x4*>(dst + 16 * dt) =
+          (f32x4){oacc[dt].x * inv, oacc[dt].y * inv, oacc[dt].z * inv, oacc[dt].w * inv};
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(pp + 4 + 16 * dt + 4 * q4) = oacc[dt];
+    if (q4 == 0) { pp[0] = m_run; pp[1] = l; }
   }
 }
 
