@@ -93,10 +93,22 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
   const int n0 = blockIdx.x * PF_BN, m0 = blockIdx.y * PF_BM;
   const int M = p.M, N = p.N, K = p.K;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  // this thread's share of a tile: row lr, columns 8 lc .. 8 lc + 7
-  const int lr = tid >> 2, lc = tid & 3;
-  const int am = min(m0 + lr, M - 1), wr = min(n0 + lr, N - 1);
-  const float* a_src = p.x + (size_t)am * p.ldx + 8 * lc;
+  // Tile loads shaped for the memory pipeline: each wave instruction reads whole tile
+  // rows, eight 128-byte lines for fp32 (lane l: row 8 u + l / 8 of the wave's 16,
+  // float4 l % 8) or sixteen 64-byte rows of bf16 W (row l / 4, eight values l % 4);
+  // spread over 16 rows at 32 bytes each, the same bytes reach a CU far more slowly.
+  const int ar = 16 * wave + (lane >> 3), ac = 4 * (lane & 7);   // fp32 unit u: row ar + 8 u
+  const int br = 16 * wave + (lane >> 2), bc = 8 * (lane & 3);   // bf16 W unit
+  const float* a_src[2];
+  const void* w_src[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    a_src[u] = p.x + (size_t)min(m0 + ar + 8 * u, M - 1) * p.ldx + ac;
+    if constexpr (WT == 0)
+      w_src[u] = reinterpret_cast<const float*>(p.w) + (size_t)min(n0 + ar + 8 * u, N - 1) * K + ac;
+    else
+      w_src[u] = reinterpret_cast<const uint16_t*>(p.w) + (size_t)min(n0 + br, N - 1) * K + bc;
+  }
   f32x4 ra[PF_PD][2], rw[PF_PD][2];
   const int nk = K / PF_BK, S = gridDim.z, z = blockIdx.z;
   // this split's groups of PD steps (the last group of the last split may reach past K)
@@ -104,27 +116,32 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
   const int g0 = z * ng / S, g1 = (z + 1) * ng / S;   // g0 < g1: S <= ng
   auto load = [&](int i, int st) {   // step st (clamped to the last one) into slot i
     const int k0 = min(st, nk - 1) * PF_BK;
-    ra[i][0] = *reinterpret_cast<const f32x4*>(a_src + k0);
-    ra[i][1] = *reinterpret_cast<const f32x4*>(a_src + k0 + 4);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) ra[i][u] = *reinterpret_cast<const f32x4*>(a_src[u] + k0);
     if constexpr (WT == 0) {
-      const float* w = reinterpret_cast<const float*>(p.w) + (size_t)wr * K + k0 + 8 * lc;
-      rw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w));
-      rw[i][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w) + 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        rw[i][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(w_src[u]) + k0));
     } else {
-      const uint16_t* w = reinterpret_cast<const uint16_t*>(p.w) + (size_t)wr * K + k0 + 8 * lc;
-      const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w));
-      rw[i][0] = (f32x4){bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
-      rw[i][1] = (f32x4){bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(w_src[0]) + k0));
+      rw[i][0] = (f32x4){bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+      rw[i][1] = (f32x4){bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
     }
   };
   auto store = [&](int i, bool valid) {   // slot i into LDS buffer i % 2 (zeros past K)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-    float* a = sA[i & 1] + lr * PF_LDS + 8 * lc;
-    float* w = sW[i & 1] + lr * PF_LDS + 8 * lc;
-    *reinterpret_cast<f32x4*>(a) = valid ? ra[i][0] : z4;
-    *reinterpret_cast<f32x4*>(a + 4) = valid ? ra[i][1] : z4;
-    *reinterpret_cast<f32x4*>(w) = valid ? rw[i][0] : z4;
-    *reinterpret_cast<f32x4*>(w + 4) = valid ? rw[i][1] : z4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<f32x4*>(sA[i & 1] + (ar + 8 * u) * PF_LDS + ac) = valid ? ra[i][u] : z4;
+    if constexpr (WT == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<f32x4*>(sW[i & 1] + (ar + 8 * u) * PF_LDS + ac) = valid ? rw[i][u] : z4;
+    } else {
+      float* w = sW[i & 1] + br * PF_LDS + bc;
+      *reinterpret_cast<f32x4*>(w) = valid ? rw[i][0] : z4;
+      *reinterpret_cast<f32x4*>(w + 4) = valid ? rw[i][1] : z4;
+    }
   };
   f32x4 acc[2][2];
 #pragma unroll
