@@ -570,6 +570,64 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
                 print(f"| `{k}` | {len(v)} | {mean:.2f} | {b['avg_us'] if b else '-'} |")
 
 
+def counter_table(csv_paths, clock_ghz: float = 2.4):
+    """Markdown table of rocprofv3 --pmc CSVs of the same command (one per counter pass):
+    per kernel and grid size, the number of dispatches, the mean of every counter per
+    dispatch, the dispatch's mean duration in that run, and what follows from them where
+    the counters are present: MFMA busy cycles per SIMD (1024 SIMDs) and as a share of
+    the duration at clock_ghz, L2 hit rate, mean L2 read latency (cycles per request),
+    and the shares of wave time spent waiting and issuing VALU and LDS instructions."""
+    import csv
+    import statistics
+
+    agg = {}
+    for path in csv_paths:
+        per = {}
+        for r in csv.DictReader(open(path)):
+            k = _short_name(r["Kernel_Name"])
+            if "at::native" in k or "rocclr" in k or k == "k_gate":
+                continue
+            key = (k, int(r["Grid_Size"]))
+            d = per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        for key, ds in per.items():
+            a = agg.setdefault(key, {"n": len(ds)})
+            for c in {c for d in ds.values() for c in d}:
+                a[c] = statistics.mean(d[c] for d in ds.values() if c in d)
+    counters = sorted({c for a in agg.values() for c in a if c not in ("n", "_us")})
+    cols = ["kernel", "grid", "dispatches", "mean us (under collection)"] + [c.replace("_sum", "") for c in counters]
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+        derived += ["MFMA busy cycles / SIMD", "MFMA busy % of duration"]
+    if "TCC_HIT_sum" in counters:
+        derived += ["L2 hit %"]
+    if "TCP_TCC_READ_REQ_LATENCY_sum" in counters:
+        derived += ["L2 read latency (cycles / request)"]
+    if "SQ_WAVE_CYCLES" in counters:
+        derived += ["wait % of wave time", "VALU % of wave time", "LDS % of wave time"]
+    print("| " + " | ".join(cols + derived) + " |")
+    print("|" + "---|" * (len(cols) + len(derived)))
+    for key in sorted(agg, key=lambda k: -agg[k]["n"] * agg[k].get("_us", 0.0)):
+        a = agg[key]
+        row = [f"`{key[0]}`", str(key[1]), str(a["n"]), f"{a.get('_us', 0.0):.2f}"]
+        row += [f"{a[c]:.4g}" if c in a else "-" for c in counters]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+            b = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024
+            row += [f"{b:.0f}", f"{100 * b / (a['_us'] * clock_ghz * 1e3):.1f}" if a.get("_us") else "-"]
+        if "TCC_HIT_sum" in counters:
+            h, m = a.get("TCC_HIT_sum", 0.0), a.get("TCC_MISS_sum", 0.0)
+            row += [f"{100 * h / (h + m):.1f}" if h + m else "-"]
+        if "TCP_TCC_READ_REQ_LATENCY_sum" in counters:
+            q = a.get("TCP_TCC_READ_REQ_sum", 0.0)
+            row += [f"{a.get('TCP_TCC_READ_REQ_LATENCY_sum', 0.0) / q:.0f}" if q else "-"]
+        if "SQ_WAVE_CYCLES" in counters:
+            w = a.get("SQ_WAVE_CYCLES", 0.0)
+            row += [f"{100 * a.get(c, 0.0) / w:.1f}" if w else "-"
+                    for c in ("SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS")]
+        print("| " + " | ".join(row) + " |")
+
+
 COPY_GBPS = [None]   # measured device-to-device copy rate (read + write bytes / time)
 PROFILE_MODE = [2]   # GD_OPT_PROFILE of the per-kernel pass (--profile-mode)
 
@@ -741,6 +799,8 @@ def main():
     ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/hbm_traffic.json from the two --pmc CSVs (with --calib-mib) and exit")
     ap.add_argument("--traffic-cmd", action="append", default=[], help="with --traffic-json: a command to record")
+    ap.add_argument("--counter-table", nargs="+", metavar="CSV", help="print a markdown table of rocprofv3 --pmc "
+                    "CSVs of one command (one per counter pass): counters and derived figures per kernel")
     ap.add_argument("--traffic-workload", default="gpt2_b1", help="with --traffic-json: the profiled workload")
     ap.add_argument("--profile-mode", type=int, choices=(1, 2), default=2,
                     help="per-kernel timing pass: 2 holds each step behind a gate kernel on a helper stream so "
@@ -756,6 +816,9 @@ def main():
                 steps = b["workloads"][args.traffic_workload]["steps"] if "workloads" in b else b["steps"]
         traffic_json(args.traffic_json[0], args.traffic_json[1], args.calib_mib, args.traffic_cmd,
                      args.traffic_workload, steps)
+        return
+    if args.counter_table:
+        counter_table(args.counter_table)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json, args.calib_mib)

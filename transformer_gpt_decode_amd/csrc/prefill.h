@@ -90,7 +90,19 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
   __shared__ __align__(16) float sW[2][PF_BN * PF_LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c = lane & 15;
-  const int n0 = blockIdx.x * PF_BN, m0 = blockIdx.y * PF_BM;
+  // Workgroups are placed round-robin over the 8 XCDs (each with its own L2) in launch
+  // order; the launch index is renumbered so that an XCD gets a run of consecutive
+  // logical tiles, ordered row tile fastest, then column tile, then K split: the tiles
+  // of one XCD then share their W columns and K range, and each slice of A and W comes
+  // from HBM about once instead of once per XCD. L = 8 k + x (x < 8) becomes x per + k
+  // for the first 8 per indices (per = total / 8); the remainder keeps its index.
+  const int GX = gridDim.x, GY = gridDim.y;
+  const int lid = [&] {
+    const int total = GX * GY * gridDim.z, L = blockIdx.x + GX * (blockIdx.y + GY * blockIdx.z), per = total >> 3;
+    return L < 8 * per ? (L & 7) * per + (L >> 3) : L;
+  }();
+  const int ty = lid % GY, tx = (lid / GY) % GX;
+  const int n0 = tx * PF_BN, m0 = ty * PF_BM;
   const int M = p.M, N = p.N, K = p.K;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   // Tile loads shaped for the memory pipeline: each wave instruction reads whole tile
@@ -110,7 +122,7 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
       w_src[u] = reinterpret_cast<const uint16_t*>(p.w) + (size_t)min(n0 + br, N - 1) * K + bc;
   }
   f32x4 ra[PF_PD][2], rw[PF_PD][2];
-  const int nk = K / PF_BK, S = gridDim.z, z = blockIdx.z;
+  const int nk = K / PF_BK, S = gridDim.z, z = lid / (GX * GY);
   // this split's groups of PD steps (the last group of the last split may reach past K)
   const int ng = (nk + PF_PD - 1) / PF_PD;
   const int g0 = z * ng / S, g1 = (z + 1) * ng / S;   // g0 < g1: S <= ng
