@@ -510,14 +510,16 @@ def traffic_json(fetch_csv: str, write_csv: str, calib_mib: int, commands, workl
     print(f"wrote {path}: {workload}, {len(rec['workloads'][workload]['kernels'])} kernels")
 
 
-def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
+def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0, run_json: str | None = None):
     """Markdown summary of a rocprofv3 CSV of a bench.py run (--kernel-trace, or --pmc with
     one counter): per kernel, over the dispatches of each profiled pass (the steps that
     follow a k_gate hold; these are the launches bench.py times), the mean execution time
     or the mean counter value. A counter in KiB is scaled to bytes by the first
     __amd_rocclr_copyBuffer dispatch, the copy of calib_mib MiB each way that
     `bench.py --copy-mib` runs first. With the bench's JSON line, its mean time and
-    algorithmic bytes per launch are shown beside."""
+    algorithmic bytes per launch are shown beside. run_json, the JSON line of the traced
+    run itself when it measured a subset of bench_json's workloads, gives the order and
+    step counts of its profiled passes (workloads are matched by name)."""
     import csv
     import statistics
 
@@ -531,16 +533,20 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
         factor = calib_mib * 1024.0 / float(cp["Counter_Value"])
         print(f"{counter}: the calibration copy ({calib_mib} MiB read, {calib_mib} MiB written) counts "
               f"{float(cp['Counter_Value']):.1f} KiB, so bytes = {counter} x {factor:.3f} KiB")
-    bench_sets, steps = [], None
+    bench_sets, steps, names = [], None, []
     if bench_json:
-        with open(bench_json) as f:
-            bench = json.loads(f.read().strip().splitlines()[-1])
-        entries = bench.get("workloads_order") or [bench["config"]["workload"]]
+        def last_json(path):
+            with open(path) as f:
+                return json.loads(f.read().strip().splitlines()[-1])
+        bench = last_json(bench_json)
+        run = last_json(run_json) if run_json else bench
+        entries = run.get("workloads_order") or [run["config"]["workload"]]
         steps = []
         for name in entries:
             e = bench["workloads"][name] if "workloads" in bench else bench
             bench_sets.append({k["kernel"]: k for k in e.get("kernels", [])})
-            steps.append(e["steps"])
+            steps.append((run["workloads"][name] if "workloads" in run else run)["steps"])
+            names.append(name)
     for pi, (lo, hi, nsteps) in enumerate(profiled_regions(rows, steps)):
         d = {}
         for r in rows[lo:hi]:
@@ -550,7 +556,8 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0):
             v = float(r["Counter_Value"]) if counter else (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
             d.setdefault(k, []).append(v)
         bs = bench_sets[pi] if pi < len(bench_sets) else {}
-        print(f"\nProfiled pass {pi + 1}: {nsteps} steps, dispatches {lo}..{hi}\n")
+        label = f" ({names[pi]})" if pi < len(names) else ""
+        print(f"\nProfiled pass {pi + 1}{label}: {nsteps} steps, dispatches {lo}..{hi}\n")
         if counter:
             print(f"| kernel | dispatches | mean {counter} KiB | MB per dispatch | bench.py algorithmic MB | ratio |")
             print("|---|---|---|---|---|---|")
@@ -587,16 +594,19 @@ def counter_table(csv_paths, clock_ghz: float = 2.4):
             k = _short_name(r["Kernel_Name"])
             if "at::native" in k or "rocclr" in k or k == "k_gate":
                 continue
-            key = (k, int(r["Grid_Size"]))
+            grid = int(r["Grid_Size"]) if "Grid_Size" in r else (
+                int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+            key = (k, grid)
             d = per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
-            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            if "Counter_Name" in r:
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
             d["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
         for key, ds in per.items():
             a = agg.setdefault(key, {"n": len(ds)})
             for c in {c for d in ds.values() for c in d}:
                 a[c] = statistics.mean(d[c] for d in ds.values() if c in d)
     counters = sorted({c for a in agg.values() for c in a if c not in ("n", "_us")})
-    cols = ["kernel", "grid", "dispatches", "mean us (under collection)"] + [c.replace("_sum", "") for c in counters]
+    cols = ["kernel", "grid", "dispatches", "mean us"] + [c.replace("_sum", "") for c in counters]
     derived = []
     if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
         derived += ["MFMA busy cycles / SIMD", "MFMA busy % of duration"]
@@ -794,6 +804,8 @@ def main():
     ap.add_argument("--trace-summary", metavar="CSV", help="print a markdown summary of a rocprofv3 kernel trace "
                     "of a bench.py run (no GPU needed) and exit")
     ap.add_argument("--bench-json", metavar="FILE", help="with --trace-summary: the bench's JSON line to compare")
+    ap.add_argument("--run-json", metavar="FILE", help="with --trace-summary: the traced run's own JSON line (its "
+                    "workloads and step counts, when it measured a subset of --bench-json's)")
     ap.add_argument("--calib-mib", type=int, default=0, help="with --trace-summary of a --pmc CSV: the size of the "
                     "--copy-mib calibration copy")
     ap.add_argument("--traffic-json", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -821,7 +833,7 @@ def main():
         counter_table(args.counter_table)
         return
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.bench_json, args.calib_mib)
+        trace_summary(args.trace_summary, args.bench_json, args.calib_mib, args.run_json)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the decode path has no multi-GPU code (decode would shard "
