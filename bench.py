@@ -577,13 +577,14 @@ def trace_summary(csv_path: str, bench_json: str | None, calib_mib: int = 0, run
                 print(f"| `{k}` | {len(v)} | {mean:.2f} | {b['avg_us'] if b else '-'} |")
 
 
-def counter_table(csv_paths, clock_ghz: float = 2.4):
+def counter_table(csv_paths, clock_ghz: float = 2.4, top: int = 16):
     """Markdown table of rocprofv3 --pmc CSVs of the same command (one per counter pass):
     per kernel and grid size, the number of dispatches, the mean of every counter per
     dispatch, the dispatch's mean duration in that run, and what follows from them where
     the counters are present: MFMA busy cycles per SIMD (1024 SIMDs) and as a share of
     the duration at clock_ghz, L2 hit rate, mean L2 read latency (cycles per request),
-    and the shares of wave time spent waiting and issuing VALU and LDS instructions."""
+    and the shares of wave time spent waiting and issuing VALU and LDS instructions. The
+    `top` kernels by total duration are listed."""
     import csv
     import statistics
 
@@ -618,7 +619,7 @@ def counter_table(csv_paths, clock_ghz: float = 2.4):
         derived += ["wait % of wave time", "VALU % of wave time", "LDS % of wave time"]
     print("| " + " | ".join(cols + derived) + " |")
     print("|" + "---|" * (len(cols) + len(derived)))
-    for key in sorted(agg, key=lambda k: -agg[k]["n"] * agg[k].get("_us", 0.0)):
+    for key in sorted(agg, key=lambda k: -agg[k]["n"] * agg[k].get("_us", 0.0))[:top]:
         a = agg[key]
         row = [f"`{key[0]}`", str(key[1]), str(a["n"]), f"{a.get('_us', 0.0):.2f}"]
         row += [f"{a[c]:.4g}" if c in a else "-" for c in counters]
@@ -813,6 +814,7 @@ def main():
     ap.add_argument("--traffic-cmd", action="append", default=[], help="with --traffic-json: a command to record")
     ap.add_argument("--counter-table", nargs="+", metavar="CSV", help="print a markdown table of rocprofv3 --pmc "
                     "CSVs of one command (one per counter pass): counters and derived figures per kernel")
+    ap.add_argument("--counter-top", type=int, default=16, help="with --counter-table: kernels listed (by total time)")
     ap.add_argument("--traffic-workload", default="gpt2_b1", help="with --traffic-json: the profiled workload")
     ap.add_argument("--profile-mode", type=int, choices=(1, 2), default=2,
                     help="per-kernel timing pass: 2 holds each step behind a gate kernel on a helper stream so "
@@ -830,7 +832,7 @@ def main():
                      args.traffic_workload, steps)
         return
     if args.counter_table:
-        counter_table(args.counter_table)
+        counter_table(args.counter_table, top=args.counter_top)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.bench_json, args.calib_mib, args.run_json)
