@@ -760,9 +760,15 @@ def measure_prefill(wname: str, seq: int, runs: int, untiled: bool = True):
         tf = flops / (st["total_us"] * 1e-6) / 1e12
         g_us += st["total_us"]
         g_fl += flops
+        # k_gemm_pf<..., true>: the products in bf16 parts on the bf16 matrix cores (3 bf16
+        # MFMA products per product with bf16 weights, 6 with fp32 weights)
+        parts = st["kernel"].endswith("true>")
+        issued = (3 if w.init.bf16 else 6) if parts else 1
         gemms.append(dict(role=st["role"], kernel=st["kernel"], launches=st["launches"],
                           avg_us=round(st["total_us"] / st["launches"], 2), tflops=round(tf, 2),
-                          frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4)))
+                          frac_fp32_peak=round(tf / MFMA_FP32_TFLOPS, 4),
+                          mfma="bf16 parts" if parts else "fp32", issued_tflops=round(tf * issued, 2),
+                          frac_issued_peak=round(tf * issued / (MFMA_BF16_TFLOPS if parts else MFMA_FP32_TFLOPS), 4)))
     other = {st["role"]: round(st["total_us"], 1) for st in stats if st["role"] not in nk}
     med = statistics.median(tiled)
     tf = g_fl / (g_us * 1e-6) / 1e12 if g_us else 0.0

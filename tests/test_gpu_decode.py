@@ -282,7 +282,7 @@ def test_context_edges_and_errors():
     assert m.device_errors() == 0
     # option values outside the documented sets are refused on the host
     for opt, bad in ((gd.OPT_ATTN_CHUNKS, 2), (gd.OPT_ATTN_CHUNKS, -1), (gd.OPT_ATTN_CHUNKS, 16),
-                     (gd.OPT_LINEAR_VARIANT, 3), (gd.OPT_PROFILE, 5), (99, 0)):
+                     (gd.OPT_LINEAR_VARIANT, 3), (gd.OPT_PROFILE, 5), (gd.OPT_PREFILL_BF16_PARTS, 3), (99, 0)):
         with pytest.raises(gd.GdError) as e:
             m.set_option(opt, bad)
         assert e.value.status == gd.GD_ERR_INVALID
@@ -487,16 +487,28 @@ def test_tiled_prefill_gpt2(wdt, kv):
                      config=f"tiled prefill gpt2 ({wdt} weights, {kv} KV)")
 
 
-def test_tiled_prefill_split_edges():
+@pytest.mark.parametrize("parts", [2, 0], ids=["bf16_parts", "fp32_mfma"])
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+def test_tiled_prefill_split_edges(wdt, parts):
     """Prompt lengths at the key-tile edges of the tiled pass: 64 ids (one key tile, the
     attention written unsplit), 65 and 128 (two tiles: one query tile's second split
-    empty), 191 (three tiles, ragged last query tile)."""
-    w = synth.Workload("gpt2_hd64_prefill_edges", GPT2_HD64_LONG, synth.Init(), 23, 4, (191, 191), 6)
+    empty), 191 (three tiles, ragged last query tile); the GEMM products in bf16 parts
+    (the default) and on the fp32 matrix cores."""
+    import transformer_gpt_decode_amd as gd
+    w = synth.Workload("gpt2_hd64_prefill_edges", GPT2_HD64_LONG, synth.Init(bf16=wdt == "bf16"), 23, 4, (191, 191), 6)
     W = synth.make_weights(w.shape, w.init, w.seed)
     full = synth.make_prompts(w)
     prompts = [full[0][:64], full[1][:65], full[2][:128], full[3][:191]]
-    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, config="tiled prefill gpt2 (64, 65, 128, 191 ids)")
+    ref_tok, ref_lg = oracle_generate(w, W, prompts)
+    m = gd_model(w, W)
+    m.set_option(gd.OPT_PREFILL_BF16_PARTS, parts)
+    tok, lg = gpu_generate(m, prompts, w.n_generate)
+    assert m.device_errors() == 0
+    rep = compare_generation(tok, lg, ref_tok, ref_lg, 1e-3 if wdt == "f32" else 2e-2,
+                             f"tiled prefill gpt2 ({wdt} weights, {'bf16 parts' if parts else 'fp32 MFMA'}; 64, 65, 128, 191 ids)",
+                             plens=[len(p) for p in prompts], tie=near_tie_margin(w))
     assert not rep["flips"]
+    m.close()
 
 
 def test_tiled_prefill_llama_long_paged():

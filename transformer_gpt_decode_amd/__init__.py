@@ -21,7 +21,7 @@ ARCH_GPT2, ARCH_LLAMA = 0, 1
 WEIGHT_F32, WEIGHT_BF16, WEIGHT_Q8 = 0, 1, 2
 KV_F32, KV_BF16 = 0, 1
 OPT_LINEAR_VARIANT, OPT_USE_GRAPH, OPT_PROFILE, OPT_FUSE_ATTN_O = 1, 2, 3, 4
-OPT_FOLD_NORM, OPT_ATTN_CHUNKS, OPT_TILED_PREFILL = 7, 9, 10
+OPT_FOLD_NORM, OPT_ATTN_CHUNKS, OPT_TILED_PREFILL, OPT_PREFILL_BF16_PARTS = 7, 9, 10, 11
 NORM_NONE, NORM_LAYER, NORM_RMS = 0, 1, 2
 ACT_NONE, ACT_GELU = 0, 1
 

@@ -83,11 +83,53 @@ __global__ __launch_bounds__(PF_NT) void k_rownorm(const float* __restrict__ x, 
 // epilogue whose output is the residual, updated in place (p.y == p.resid): each split
 // adds its partial sums to it with float atomics, the bias coming from split 0, so the
 // summation order of the S partials is not fixed.
+//
+// SPLIT: the products run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, 16 times
+// the fp32 rate) without losing fp32 accuracy. An fp32 value is the exact sum of three
+// bf16 parts (each the nearest bf16 to what the previous parts left: 8 + 8 + 8
+// significant bits), and a product of two bf16 values is exact in fp32, so
+//   a w = sum over the part pairs (i, j) of a_i w_j.
+// bf16 weights are one part already: three MFMAs per product. fp32 weights are split as
+// well and the six pairs with i + j <= 2 (parts numbered from 0) are kept; the three
+// dropped terms are below 2^-24 of the product, the size of an fp32 rounding. The parts
+// are formed once per workgroup when a tile is stored into LDS (one LDS plane each), and
+// the sums accumulate in fp32 as before. Lane l = 16 q + c then holds eight consecutive
+// k values of row c of each operand.
 #define PF_PD 4   // K steps in flight
-template <int WT, int EPI>
+#define PF_LDB 40 // LDS row stride of the bf16 part planes (elements; 16-byte aligned rows)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 bits, rounded to nearest even (element 0 in the low half).
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){x, y}, bf16x2_t));
+}
+
+// Four floats as three packed bf16 parts: a = hi + mid + lo.
+__device__ __forceinline__ void split3(const f32x4& a, uint2& hi, uint2& mid, uint2& lo) {
+  hi = make_uint2(pk_bf16(a.x, a.y), pk_bf16(a.z, a.w));
+  float r0 = a.x - bf16_lo(hi.x), r1 = a.y - bf16_hi(hi.x), r2 = a.z - bf16_lo(hi.y), r3 = a.w - bf16_hi(hi.y);
+  mid = make_uint2(pk_bf16(r0, r1), pk_bf16(r2, r3));
+  r0 -= bf16_lo(mid.x); r1 -= bf16_hi(mid.x); r2 -= bf16_lo(mid.y); r3 -= bf16_hi(mid.y);
+  lo = make_uint2(pk_bf16(r0, r1), pk_bf16(r2, r3));
+}
+
+template <int WT, bool SPLIT>
+struct PfLds;
+template <int WT>
+struct PfLds<WT, false> {
+  float a[2][PF_BM * PF_LDS];
+  float w[2][PF_BN * PF_LDS];
+};
+template <int WT>
+struct PfLds<WT, true> {
+  uint16_t a[2][3][PF_BM * PF_LDB];                   // [buffer][part][row][k]
+  uint16_t w[2][WT == 0 ? 3 : 1][PF_BN * PF_LDB];
+};
+
+template <int WT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
-  __shared__ __align__(16) float sA[2][PF_BM * PF_LDS];
-  __shared__ __align__(16) float sW[2][PF_BN * PF_LDS];
+  __shared__ __align__(16) PfLds<WT, SPLIT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c = lane & 15;
   // Workgroups are placed round-robin over the 8 XCDs (each with its own L2) in launch
@@ -121,7 +163,8 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
     else
       w_src[u] = reinterpret_cast<const uint16_t*>(p.w) + (size_t)min(n0 + br, N - 1) * K + bc;
   }
-  f32x4 ra[PF_PD][2], rw[PF_PD][2];
+  f32x4 ra[PF_PD][2], rw[PF_PD][2];   // fp32 tiles in flight (SPLIT bf16 W: raw bits in rb)
+  u32x4 rb[PF_PD];
   const int nk = K / PF_BK, S = gridDim.z, z = lid / (GX * GY);
   // this split's groups of PD steps (the last group of the last split may reach past K)
   const int ng = (nk + PF_PD - 1) / PF_PD;
@@ -136,23 +179,48 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
         rw[i][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(w_src[u]) + k0));
     } else {
       const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(w_src[0]) + k0));
-      rw[i][0] = (f32x4){bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
-      rw[i][1] = (f32x4){bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+      if constexpr (SPLIT) {
+        rb[i] = v;
+      } else {
+        rw[i][0] = (f32x4){bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+        rw[i][1] = (f32x4){bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+      }
     }
   };
   auto store = [&](int i, bool valid) {   // slot i into LDS buffer i % 2 (zeros past K)
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const int b = i & 1;
+    if constexpr (SPLIT) {
+      const uint2 z2 = make_uint2(0u, 0u);
+      auto put3 = [&](uint16_t (*planes)[PF_BM * PF_LDB], int row, const f32x4& v) {
+        uint2 h, m, l;
+        split3(v, h, m, l);
+        *reinterpret_cast<uint2*>(planes[0] + row * PF_LDB + ac) = valid ? h : z2;
+        *reinterpret_cast<uint2*>(planes[1] + row * PF_LDB + ac) = valid ? m : z2;
+        *reinterpret_cast<uint2*>(planes[2] + row * PF_LDB + ac) = valid ? l : z2;
+      };
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<f32x4*>(sA[i & 1] + (ar + 8 * u) * PF_LDS + ac) = valid ? ra[i][u] : z4;
-    if constexpr (WT == 0) {
+      for (int u = 0; u < 2; ++u) put3(sm.a[b], ar + 8 * u, ra[i][u]);
+      if constexpr (WT == 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) put3(sm.w[b], ar + 8 * u, rw[i][u]);
+      } else {
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(sm.w[b][0] + br * PF_LDB + bc) = valid ? rb[i] : z4;
+      }
+    } else {
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<f32x4*>(sW[i & 1] + (ar + 8 * u) * PF_LDS + ac) = valid ? rw[i][u] : z4;
-    } else {
-      float* w = sW[i & 1] + br * PF_LDS + bc;
-      *reinterpret_cast<f32x4*>(w) = valid ? rw[i][0] : z4;
-      *reinterpret_cast<f32x4*>(w + 4) = valid ? rw[i][1] : z4;
+        *reinterpret_cast<f32x4*>(sm.a[b] + (ar + 8 * u) * PF_LDS + ac) = valid ? ra[i][u] : z4;
+      if constexpr (WT == 0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          *reinterpret_cast<f32x4*>(sm.w[b] + (ar + 8 * u) * PF_LDS + ac) = valid ? rw[i][u] : z4;
+      } else {
+        float* w = sm.w[b] + br * PF_LDS + bc;
+        *reinterpret_cast<f32x4*>(w) = valid ? rw[i][0] : z4;
+        *reinterpret_cast<f32x4*>(w + 4) = valid ? rw[i][1] : z4;
+      }
     }
   };
   f32x4 acc[2][2];
@@ -163,26 +231,55 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
   // A step's 32 K columns: MFMA t (0..7) contracts k = 8 q + t, so each lane reads its
   // eight operand values of a row with two 16-byte LDS loads, all before the MFMAs
   auto mfma = [&](int b) {
-    F8 a[2], w[2];
+    if constexpr (SPLIT) {
+      constexpr int NW = WT == 0 ? 3 : 1;
+      u32x4 a[3][2], w[NW][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float* src = sA[b] + (wm + 16 * i + c) * PF_LDS + 8 * q;
-      a[i].a = *reinterpret_cast<const f32x4*>(src);
-      a[i].b = *reinterpret_cast<const f32x4*>(src + 4);
-    }
+      for (int pa = 0; pa < 3; ++pa)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float* src = sW[b] + (wn + 16 * j + c) * PF_LDS + 8 * q;
-      w[j].a = *reinterpret_cast<const f32x4*>(src);
-      w[j].b = *reinterpret_cast<const f32x4*>(src + 4);
-    }
+        for (int i = 0; i < 2; ++i)
+          a[pa][i] = *reinterpret_cast<const u32x4*>(sm.a[b][pa] + (wm + 16 * i + c) * PF_LDB + 8 * q);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int pw = 0; pw < NW; ++pw)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f8_at(a[i], t), f8_at(w[j], t), acc[i][j], 0, 0, 0);
+          w[pw][j] = *reinterpret_cast<const u32x4*>(sm.w[b][pw] + (wn + 16 * j + c) * PF_LDB + 8 * q);
+      // the part pairs (pa, pw) with pa + pw <= 2, smallest terms first
+#pragma unroll
+      for (int s = 2; s >= 0; --s)
+#pragma unroll
+        for (int pa = 0; pa <= s; ++pa) {
+          const int pw = s - pa;
+          if (pw >= NW) continue;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[pa][i]),
+                                                                 __builtin_bit_cast(bf16x8_t, w[pw][j]), acc[i][j], 0, 0, 0);
+        }
+    } else {
+      F8 a[2], w[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float* src = sm.a[b] + (wm + 16 * i + c) * PF_LDS + 8 * q;
+        a[i].a = *reinterpret_cast<const f32x4*>(src);
+        a[i].b = *reinterpret_cast<const f32x4*>(src + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float* src = sm.w[b] + (wn + 16 * j + c) * PF_LDS + 8 * q;
+        w[j].a = *reinterpret_cast<const f32x4*>(src);
+        w[j].b = *reinterpret_cast<const f32x4*>(src + 4);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f8_at(a[i], t), f8_at(w[j], t), acc[i][j], 0, 0, 0);
+    }
   };
 #pragma unroll
   for (int i = 0; i < PF_PD; ++i) load(i, g0 * PF_PD + i);
