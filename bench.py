@@ -760,9 +760,9 @@ def measure_prefill(wname: str, seq: int, runs: int, untiled: bool = True):
         tf = flops / (st["total_us"] * 1e-6) / 1e12
         g_us += st["total_us"]
         g_fl += flops
-        # k_gemm_pf<..., true>: the products in bf16 parts on the bf16 matrix cores (3 bf16
+        # k_gemm_pf<w, epi, true, nrm>: the products in bf16 parts on the bf16 matrix cores (3 bf16
         # MFMA products per product with bf16 weights, 6 with fp32 weights)
-        parts = st["kernel"].endswith("true>")
+        parts = ", true" in st["kernel"]
         issued = (3 if w.init.bf16 else 6) if parts else 1
         gemms.append(dict(role=st["role"], kernel=st["kernel"], launches=st["launches"],
                           avg_us=round(st["total_us"] / st["launches"], 2), tflops=round(tf, 2),

@@ -224,8 +224,11 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                            * (QKV, MLP up, head) reads copies of its weights with the
                            * norm's gain folded in (and the shift in its bias), made at
                            * gd_load_weights, and applies the row statistics in its
-                           * epilogue; 0: the norm's gain and shift are applied to the
-                           * row first */
+                           * epilogue; the tiled prompt pass applies its pre-norms inside
+                           * the QKV and MLP-up GEMMs (LayerNorm through those folded
+                           * copies, RMSNorm with any weights: gains applied as the rows
+                           * are staged, the row scale in the epilogue). 0: the norm's
+                           * gain and shift are applied to the rows first */
 #define GD_OPT_ATTN_CHUNKS 9 /* context chunks per row of the split-context attention
                              * (rows that do not take the short-context fused attention):
                              * 1 (one workgroup per row and KV head over the whole context:

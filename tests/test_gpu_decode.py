@@ -656,3 +656,28 @@ def test_greedy_head_nan_rule():
     assert int(nxt[0].item()) == 0
     assert m.device_errors() == 0
     m.close()
+
+
+@pytest.mark.parametrize("fold", [True, False], ids=["in_gemm", "rownorm"])
+@pytest.mark.parametrize("arch", ["gpt2", "llama"])
+def test_tiled_prefill_prenorm(arch, fold):
+    """The tiled prompt pass with its pre-norms inside the GEMMs (LayerNorm through the
+    folded fp32 weights, RMSNorm with the gains applied as the tiles are staged) and
+    applied to the rows first (k_rownorm): random norm gains, shifts and biases, and
+    residual rows with a far-off first element and a large common offset (the folded
+    LayerNorm shifts by the first element); 96- and 200-id prompts."""
+    if arch == "gpt2":
+        w = synth.Workload("gpt2_hd64_prefill_norm", GPT2_HD64_LONG, synth.Init(), 25, 2, (96, 200), 4)
+    else:
+        w = synth.Workload("llama_prefill_norm", LLAMA_HD64, synth.Init(), 25, 2, (96, 200), 4)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 26)
+    name = "wpe" if arch == "gpt2" else "wte"
+    off, shp = synth.offsets(w.shape)[name]
+    tab = W[off:off + int(np.prod(shp))].reshape(shp)
+    tab += np.float32(5.0)
+    tab[:, 0] += np.float32(20.0)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, fold=fold,
+                                 config=f"tiled prefill {arch} pre-norm ({'in the GEMMs' if fold else 'rownorm'}, "
+                                        f"random norms, offset rows)")
+    assert not rep["flips"], rep["flips"]

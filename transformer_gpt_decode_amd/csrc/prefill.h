@@ -127,9 +127,24 @@ struct PfLds<WT, true> {
   uint16_t w[2][WT == 0 ? 3 : 1][PF_BN * PF_LDB];
 };
 
-template <int WT, int EPI, bool SPLIT>
+// NRM: the pre-norm of the rows, applied inside the GEMM (QKV and MLP up, never split
+// in K, so each workgroup sees whole rows over its K loop):
+//  PFN_RMS:  RMSNorm: each staged value is multiplied by its column's gain (p.ng), the
+//            row's sum of squares accumulates as the tiles pass, and the epilogue scales
+//            by r = 1 / sqrt(mean(x^2) + eps);
+//  PFN_FOLD: LayerNorm folded into fp32 weights (p.w = g W, p.fs its row sums, p.bias the
+//            folded bias): the rows are staged shifted by their first element,
+//            d = x - x_0, whose moments accumulate; the epilogue forms
+//            r (acc - mean(d) s_n), as the decode kernels do.
+#define PFN_NONE 0
+#define PFN_RMS 1
+#define PFN_FOLD 2
+
+template <int WT, int EPI, bool SPLIT, int NRM = PFN_NONE>
 __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
+  static_assert(NRM != PFN_FOLD || WT == 0, "folded weights are fp32");
   __shared__ __align__(16) PfLds<WT, SPLIT> sm;
+  __shared__ float s_r[PF_BM], s_mu[PF_BM];   // NRM: each tile row's r and mean(d)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, c = lane & 15;
   // Workgroups are placed round-robin over the 8 XCDs (each with its own L2) in launch
@@ -165,6 +180,13 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
   }
   f32x4 ra[PF_PD][2], rw[PF_PD][2];   // fp32 tiles in flight (SPLIT bf16 W: raw bits in rb)
   u32x4 rb[PF_PD];
+  f32x4 gv[PF_PD];                    // PFN_RMS: the gains of this thread's 4 columns
+  float x0[2] = {0.f, 0.f};           // PFN_FOLD: each unit row's first element
+  float st1[2] = {0.f, 0.f}, st2[2] = {0.f, 0.f};   // the unit rows' running sum and sum of squares
+  if constexpr (NRM == PFN_FOLD) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) x0[u] = *(a_src[u] - ac);
+  }
   const int nk = K / PF_BK, S = gridDim.z, z = lid / (GX * GY);
   // this split's groups of PD steps (the last group of the last split may reach past K)
   const int ng = (nk + PF_PD - 1) / PF_PD;
@@ -173,6 +195,7 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
     const int k0 = min(st, nk - 1) * PF_BK;
 #pragma unroll
     for (int u = 0; u < 2; ++u) ra[i][u] = *reinterpret_cast<const f32x4*>(a_src[u] + k0);
+    if constexpr (NRM == PFN_RMS) gv[i] = *reinterpret_cast<const f32x4*>(p.ng + k0 + ac);
     if constexpr (WT == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -189,6 +212,20 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
   };
   auto store = [&](int i, bool valid) {   // slot i into LDS buffer i % 2 (zeros past K)
     const int b = i & 1;
+    if constexpr (NRM != PFN_NONE) {
+      // the pre-norm's share of this step: statistics of the real columns, then the
+      // values the MFMAs see (x g for RMSNorm, x - x_0 for the folded LayerNorm)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4& a = ra[i][u];
+        if constexpr (NRM == PFN_FOLD) { a.x -= x0[u]; a.y -= x0[u]; a.z -= x0[u]; a.w -= x0[u]; }
+        const float s1 = (a.x + a.y) + (a.z + a.w);
+        const float s2 = fmaf(a.x, a.x, a.y * a.y) + fmaf(a.z, a.z, a.w * a.w);
+        st1[u] += valid ? s1 : 0.f;
+        st2[u] += valid ? s2 : 0.f;
+        if constexpr (NRM == PFN_RMS) { a.x *= gv[i].x; a.y *= gv[i].y; a.z *= gv[i].z; a.w *= gv[i].w; }
+      }
+    }
     if constexpr (SPLIT) {
       const uint2 z2 = make_uint2(0u, 0u);
       auto put3 = [&](uint16_t (*planes)[PF_BM * PF_LDB], int row, const f32x4& v) {
@@ -300,6 +337,20 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
     __syncthreads();
     mfma(i & 1);
   }
+  if constexpr (NRM != PFN_NONE) {
+    // each row's statistics: the 8 lanes that staged it, then LDS for the epilogue
+    const float invK = 1.0f / (float)K;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float s1 = group_sum<8>(st1[u]), s2 = group_sum<8>(st2[u]);
+      const float mu = NRM == PFN_FOLD ? s1 * invK : 0.f;
+      if ((lane & 7) == 0) {
+        s_r[ar + 8 * u] = rsqrtf(fmaxf(s2 * invK - mu * mu, 0.f) + p.eps);
+        s_mu[ar + 8 * u] = mu;
+      }
+    }
+    __syncthreads();
+  }
   // epilogue: this lane holds rows m0 + wm + 16 i + 4 q + v of column n0 + wn + 16 j + c
   constexpr bool PAIR = EpiTraits<EPI>::pair;
 #pragma unroll
@@ -307,11 +358,15 @@ __global__ __launch_bounds__(PF_NT) void k_gemm_pf(LinParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn + 16 * j + c;
+      const float f0 = NRM == PFN_FOLD ? p.fs[min(n, N - 1)] : 0.f;   // folded row sum of this column
       const float vv[4] = {acc[i][j].x, acc[i][j].y, acc[i][j].z, acc[i][j].w};
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wm + 16 * i + 4 * q + v;
-        const float v0 = vv[v];
+        const int rl = wm + 16 * i + 4 * q + v;
+        float v0 = vv[v];
+        if (NRM == PFN_RMS) v0 *= s_r[rl];
+        if (NRM == PFN_FOLD) v0 = s_r[rl] * (v0 - s_mu[rl] * f0);
         const float v1 = __shfl_xor(v0, 1);   // the odd neighbour's column (pairs)
         const bool own = m < M && (PAIR ? ((c & 1) == 0 && n + 1 < N) : n < N);
         if (EPI == EPI_PLAIN && S > 1) {

@@ -1476,35 +1476,57 @@ static int gemm_pf_splits(const gd_model* m, const LinParams& p) {
   return std::max(1, std::min({want, PF_MAXS, p.K / PF_BK / 4}));
 }
 
+// nrm: PFN_NONE, PFN_RMS (SwiGLU and QKV + RoPE: the Llama layout) or PFN_FOLD (GELU
+// and QKV with fp32 weights).
 template <int WT, bool SPLIT>
-static void launch_gemm_pf(hipStream_t st, const LinParams& p, int S) {
+static void launch_gemm_pf(hipStream_t st, const LinParams& p, int S, int nrm) {
   const dim3 g(iceil(p.N, PF_BN), iceil(p.M, PF_BM), S), b(PF_NT);
+#define PF_GO(E, N) GD_LAUNCH((k_gemm_pf<WT, E, SPLIT, N>), g, b, 0, st, p)
   switch (p.epi) {
-    case EPI_PLAIN: GD_LAUNCH((k_gemm_pf<WT, EPI_PLAIN, SPLIT>), g, b, 0, st, p); break;
-    case EPI_GELU: GD_LAUNCH((k_gemm_pf<WT, EPI_GELU, SPLIT>), g, b, 0, st, p); break;
-    case EPI_SWIGLU: GD_LAUNCH((k_gemm_pf<WT, EPI_SWIGLU, SPLIT>), g, b, 0, st, p); break;
-    case EPI_QKV: GD_LAUNCH((k_gemm_pf<WT, EPI_QKV, SPLIT>), g, b, 0, st, p); break;
-    default: GD_LAUNCH((k_gemm_pf<WT, EPI_QKV_ROPE, SPLIT>), g, b, 0, st, p); break;
+    case EPI_PLAIN: PF_GO(EPI_PLAIN, PFN_NONE); break;
+    case EPI_GELU:
+    case EPI_QKV:
+      if constexpr (WT == 0) {
+        if (nrm == PFN_FOLD) {
+          if (p.epi == EPI_GELU) PF_GO(EPI_GELU, PFN_FOLD);
+          else PF_GO(EPI_QKV, PFN_FOLD);
+          break;
+        }
+      }
+      if (p.epi == EPI_GELU) PF_GO(EPI_GELU, PFN_NONE);
+      else PF_GO(EPI_QKV, PFN_NONE);
+      break;
+    case EPI_SWIGLU:
+      if (nrm == PFN_RMS) PF_GO(EPI_SWIGLU, PFN_RMS);
+      else PF_GO(EPI_SWIGLU, PFN_NONE);
+      break;
+    default:
+      if (nrm == PFN_RMS) PF_GO(EPI_QKV_ROPE, PFN_RMS);
+      else PF_GO(EPI_QKV_ROPE, PFN_NONE);
+      break;
   }
+#undef PF_GO
 }
 
 // One GEMM of the prompt pass (profiled as role `role`: 2 M N K flops, the bytes of
 // the weights, the rows in and out).
-static hipError_t run_gemm_pf(gd_model* m, hipStream_t st, const char* role, const LinParams& p) {
+static hipError_t run_gemm_pf(gd_model* m, hipStream_t st, const char* role, const LinParams& p,
+                              int nrm = PFN_NONE) {
   char kn[48];
   // bf16 parts: the default for bf16 weights (three products per weight, 1.3-1.8x
   // faster); for fp32 weights (six products, the weights split too) only on request:
   // the narrow split-K GEMMs measured slower that way and the wide ones faster
   const bool parts = m->wt == GD_WEIGHT_F32 ? m->pf_parts == 2 : m->pf_parts >= 1;
-  snprintf(kn, sizeof(kn), "k_gemm_pf<%d, %d, %s>", m->wt == GD_WEIGHT_F32 ? 0 : 1, p.epi, parts ? "true" : "false");
+  snprintf(kn, sizeof(kn), "k_gemm_pf<%d, %d, %s, %d>", m->wt == GD_WEIGHT_F32 ? 0 : 1, p.epi, parts ? "true" : "false",
+           nrm);
   ProfScope ps(m, st, role, kn, (double)p.N * p.K * m->elt + 4.0 * p.M * (p.K + p.N));
   const int S = gemm_pf_splits(m, p);
   if (m->wt == GD_WEIGHT_F32) {
-    if (parts) launch_gemm_pf<0, true>(st, p, S);
-    else launch_gemm_pf<0, false>(st, p, S);
+    if (parts) launch_gemm_pf<0, true>(st, p, S, nrm);
+    else launch_gemm_pf<0, false>(st, p, S, nrm);
   } else {
-    if (parts) launch_gemm_pf<1, true>(st, p, S);
-    else launch_gemm_pf<1, false>(st, p, S);
+    if (parts) launch_gemm_pf<1, true>(st, p, S, nrm);
+    else launch_gemm_pf<1, false>(st, p, S, nrm);
   }
   return hipGetLastError();
 }
@@ -1545,21 +1567,29 @@ static hipError_t enqueue_prefill_tiled(gd_model* m, hipStream_t st, const RowPa
   base.row_kvoff = rp.row_kvoff;
   base.M = M;
   base.pro = PRO_COPY;
+  base.eps = c.norm_eps;
+  // the pre-norms inside the QKV and MLP-up GEMMs: RMSNorm (any weights), LayerNorm
+  // through the folded fp32 weights; otherwise k_rownorm normalizes the rows first
+  const int nrm = !m->use_fold ? PFN_NONE : !gpt2 ? PFN_RMS : m->folded ? PFN_FOLD : PFN_NONE;
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& t = m->L[l];
-    if ((e = run_rownorm(m, st, x, m->wf(t.n1g), t.n1b ? m->wf(t.n1b) : nullptr, xn, M)) != hipSuccess) return e;
+    if (nrm == PFN_NONE &&
+        (e = run_rownorm(m, st, x, m->wf(t.n1g), t.n1b ? m->wf(t.n1b) : nullptr, xn, M)) != hipSuccess)
+      return e;
     {
       LinParams p = base;
-      p.x = xn; p.ldx = d;
-      p.w = m->w + t.wqkv; p.N = m->qkvdim; p.K = d;
+      p.x = nrm == PFN_NONE ? xn : x; p.ldx = d;
+      p.w = m->w + (nrm == PFN_FOLD ? t.fqkv : t.wqkv); p.N = m->qkvdim; p.K = d;
       p.epi = gpt2 ? EPI_QKV : EPI_QKV_ROPE;
-      p.bias = t.bqkv ? m->wf(t.bqkv) : zero;
+      p.bias = nrm == PFN_FOLD ? m->wf(t.fqkv_b) : t.bqkv ? m->wf(t.bqkv) : zero;
+      p.fs = nrm == PFN_FOLD ? m->wf(t.fqkv_s) : nullptr;
+      p.ng = m->wf(t.n1g);
       p.y = q; p.ldy = m->qdim;
       p.qdim = m->qdim; p.kdim = m->kdim;
       p.rope_cs = rp.row_cs;
       p.kc = m->kpool(l); p.vc = m->vpool(l); p.kv16 = m->kv16;
       p.kv_hstride = m->bsize * c.head_dim;
-      if ((e = run_gemm_pf(m, st, "pf.qkv", p)) != hipSuccess) return e;
+      if ((e = run_gemm_pf(m, st, "pf.qkv", p, nrm)) != hipSuccess) return e;
     }
     {
       PfAttnParams a;
@@ -1605,16 +1635,20 @@ static hipError_t enqueue_prefill_tiled(gd_model* m, hipStream_t st, const RowPa
       p.resid = x; p.ldr = d; p.y = x; p.ldy = d;
       if ((e = run_gemm_pf(m, st, "pf.o", p)) != hipSuccess) return e;
     }
-    if ((e = run_rownorm(m, st, x, m->wf(t.n2g), t.n2b ? m->wf(t.n2b) : nullptr, xn, M)) != hipSuccess) return e;
+    if (nrm == PFN_NONE &&
+        (e = run_rownorm(m, st, x, m->wf(t.n2g), t.n2b ? m->wf(t.n2b) : nullptr, xn, M)) != hipSuccess)
+      return e;
     {
       LinParams p = base;
-      p.x = xn; p.ldx = d;
-      p.w = m->w + t.wfc; p.N = m->fcN; p.K = d;
+      p.x = nrm == PFN_NONE ? xn : x; p.ldx = d;
+      p.w = m->w + (nrm == PFN_FOLD ? t.ffc : t.wfc); p.N = m->fcN; p.K = d;
       p.epi = gpt2 ? EPI_GELU : EPI_SWIGLU;
-      p.bias = t.bfc ? m->wf(t.bfc) : zero;
+      p.bias = nrm == PFN_FOLD ? m->wf(t.ffc_b) : t.bfc ? m->wf(t.bfc) : zero;
+      p.fs = nrm == PFN_FOLD ? m->wf(t.ffc_s) : nullptr;
+      p.ng = m->wf(t.n2g);
       p.resid = zero; p.ldr = 0;
       p.y = h; p.ldy = ff;
-      if ((e = run_gemm_pf(m, st, "pf.fc", p)) != hipSuccess) return e;
+      if ((e = run_gemm_pf(m, st, "pf.fc", p, nrm)) != hipSuccess) return e;
     }
     {
       LinParams p = base;
