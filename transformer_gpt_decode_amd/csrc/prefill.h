@@ -1,14 +1,16 @@
 // prefill.h -- the prompt pass for many rows at once: a pre-norm kernel, a tiled
-// matrix-core GEMM with the decode epilogues, and tiled causal attention.
+// matrix-core GEMM with the decode epilogues (and the pre-norm inside), and tiled
+// causal attention with its merge.
 //
 // A prompt of P tokens runs the same layer as a decode step, but on P rows at a time
 // ("rvllm Metal backend", "The matmul pain story": prefill is where the tiled GEMM
 // pays; "Numbers": prompt processing speed and time to first token). The linear
 // layers are real matrix products there (M = P rows), so they run as 64 x 64 output
-// tiles on the fp32 matrix cores, every weight tile read once per 64 rows. Attention
-// over the prompt is causal: query tile i of 64 rows attends to key tiles 0..i (and
-// every cached position before the prompt), with the K/V tiles staged in LDS and
-// shared by the 64 queries, and an online softmax per query row.
+// tiles on the matrix cores (fp32, or bf16 in exact parts for bf16 weights), every
+// weight tile read once per 64 rows. Attention over the prompt is causal: query tile i
+// of 64 rows attends to key tiles 0..i (and every cached position before the prompt),
+// with the K/V tiles staged in LDS and shared by the 64 queries, and an online softmax
+// per query row.
 #pragma once
 #include "common.h"
 #include "linear.h"
