@@ -237,10 +237,13 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                              * GD_OPT_FUSE_ATTN_O) or 8 (partials merged by the output
                              * projection's prologue or a merge launch); 0 (default): 1
                              * when rows x KV heads >= the CU count and the output
-                             * projection would be a matrix-core launch, else 8. When the
-                             * output projection is the VALU GEMV (at most 4 rows, or any
-                             * row count with GD_OPT_LINEAR_VARIANT = 1) the split-context
-                             * attention always uses 8 (the GEMV's prologue merges them) */
+                             * projection would be a matrix-core launch, 32 (merged by a
+                             * launch of their own) when some row attends to 1024 or more
+                             * positions and rows x KV heads x 8 < the CU count, else 8.
+                             * Below that context length, when the output projection is
+                             * the VALU GEMV (at most 4 rows, or any row count with
+                             * GD_OPT_LINEAR_VARIANT = 1) the split-context attention
+                             * always uses 8 (the GEMV's prologue merges them) */
 #define GD_OPT_TILED_PREFILL 10 /* 1 (default): prompts of at least 64 tokens run the tiled
                                 * prompt pass (512 rows at a time: 64 x 64 matrix-core GEMM
                                 * tiles with the decode epilogues, tiled causal attention with

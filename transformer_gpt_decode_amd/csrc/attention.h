@@ -10,7 +10,7 @@
 // (grouped-query attention).
 //
 // Decomposition (split context): one workgroup per (row, KV head, chunk). A row's
-// T = pos + 1 positions are cut into C <= GD_ATT_NCH chunks of ceil(T / C) positions
+// T = pos + 1 positions are cut into C chunks of ceil(T / C) positions (C = 1, GD_ATT_NCH or GD_ATT_NCH_LONG)
 // (C = the grid's x extent), so the number of partials per row is fixed and their
 // consumer can load all of them without first reading the row's position. Inside a
 // chunk, groups of HD/4 lanes take one position per step (float4 of K and V per lane,
@@ -35,7 +35,7 @@ struct AttnParams {
   const long long* row_kvoff;         // contiguous: the row's own slot offset
   int M;
   float scale;
-  float* part;                        // [M][Hq][GD_ATT_NCH][HD + 2]: max, sum, o[HD]
+  float* part;                        // [M][Hq][C][HD + 2]: max, sum, o[HD] (C chunks per row)
   float* out; int ldo;                // one chunk per row: the normalized output [M][ldo]
 };
 
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
     if (C == 1) {   // the whole context: l > 0 (the row's own position is in it)
       p.out[(size_t)row * p.ldo + (kh * G + g) * HD + d] = o / l;
     } else {
-      float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * GD_ATT_NCH + c) * (HD + 2);
+      float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * C + c) * (HD + 2);
       pp[2 + d] = o;
       if (d == 0) { pp[0] = m; pp[1] = l; }
     }
@@ -576,6 +576,34 @@ __device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd,
   MergeRegs<EPT> r;
   attn_merge_issue<EPT>(apart, Hq, hd, M, r, nthr);
   attn_merge_finish<EPT>(apart, Hq, hd, M, r, dst, ldd, s_w, nthr);
+}
+
+// Merge of C <= GD_ATT_NCH_LONG chunk partials (the long-context split) into
+// o[M][Hq*HD]: one wave per (query head, row). Every load is issued at once (indices
+// clamped to the last chunk, extra chunks weighted 0), so the merge costs one memory
+// round trip: lane c takes chunk c's (max, sum), lane d the C values of dimension d;
+// the chunk weights e^(max_c - max) are shared by lane exchanges. Empty chunks (max
+// -inf) weigh 0; chunk 0 holds position 0, so max is finite.
+__global__ __launch_bounds__(64) void k_attn_merge_n(const float* part, int Hq, int hd, int C, float* out, int ldo) {
+  const int h = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+  const int stride = hd + 2, d = min(lane, hd - 1);
+  const float* pp = part + ((size_t)m * Hq + h) * C * stride;
+  const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)min(lane, C - 1) * stride);   // stride is even
+  float ov[GD_ATT_NCH_LONG];
+#pragma unroll
+  for (int c = 0; c < GD_ATT_NCH_LONG; ++c) ov[c] = pp[(size_t)min(c, C - 1) * stride + 2 + d];
+  // keeps the loads above where they are (the pointers are not restrict-qualified, so
+  // the clobber binds them): left alone, the compiler moves the value loads below the
+  // reductions, after a wait for the (max, sum) pairs (two round trips)
+  asm volatile("" ::: "memory");
+  const float mc = lane < C ? ml.x : -INFINITY;
+  const float mx = wave_max(mc);
+  const float w = attn_rescale(mc, mx);   // 0 for lanes >= C
+  const float l = wave_sum((lane < C ? ml.y : 0.f) * w);
+  float o = 0.f;
+#pragma unroll
+  for (int c = 0; c < GD_ATT_NCH_LONG; ++c) o = fmaf(__shfl(w, c), ov[c], o);
+  if (lane < hd) out[(size_t)m * ldo + h * hd + lane] = o / l;
 }
 
 // Merge of the chunk partials into o[M][Hq*HD] (rows handled by the matrix-core

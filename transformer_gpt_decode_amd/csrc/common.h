@@ -7,6 +7,7 @@
 #define GD_MAX_ROWS 32     // rows (sequences or prompt positions) per forward call
 #define GD_TILE_N 16       // output columns per linear tile
 #define GD_ATT_NCH 8       // context chunks (attention workgroups) per row and KV head
+#define GD_ATT_NCH_LONG 32 // chunks for long contexts with few rows (merged by a launch of their own)
 #define GD_MAX_HEADS 32    // query heads per layer
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

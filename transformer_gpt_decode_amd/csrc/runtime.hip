@@ -322,14 +322,19 @@ struct GraphKey {
   void* next;
   void* logits;
   bool short_ctx;   // every row attends to at most kFusedAttnOMaxT positions
+  bool long_ctx;    // some row attends to at least kLongCtxT positions
   bool operator<(const GraphKey& o) const {
-    return std::tie(batch, tok, next, logits, short_ctx) < std::tie(o.batch, o.tok, o.next, o.logits, o.short_ctx);
+    return std::tie(batch, tok, next, logits, short_ctx, long_ctx) <
+           std::tie(o.batch, o.tok, o.next, o.logits, o.short_ctx, o.long_ctx);
   }
 };
 
 // Rows of at most this many positions (and few rows) run attention fused with the output
 // projection: every projection slice recomputes the attention from K/V in cache.
 static const int kFusedAttnOMaxT = 256;
+// From this many attended positions, launches with few (row, KV head) pairs split each
+// context into GD_ATT_NCH_LONG chunks (merged by k_attn_merge_n) instead of GD_ATT_NCH.
+static const int kLongCtxT = 1024;
 // Decode-step graphs kept per model.
 static const size_t kMaxGraphs = 16;
 // Prompts of at least kPrefillMinRows tokens run the tiled prompt pass, kPrefillChunk
@@ -571,7 +576,7 @@ static void layout(gd_model* m) {
   m->o_h = take(R * ff * 4);
   m->o_amv = take(m->am_parts * R * 4);
   m->o_ami = take(m->am_parts * R * 4);
-  m->o_apart = take(R * c.n_head * GD_ATT_NCH * (c.head_dim + 2) * 4);
+  m->o_apart = take(R * c.n_head * GD_ATT_NCH_LONG * (c.head_dim + 2) * 4);
   m->o_slog = take(R * (size_t)c.vocab * 4);
   // the tiled prompt pass: float or bf16 weights, head_dim 64, widths multiples of 32
   m->pf_ok = m->wt != GD_WEIGHT_Q8 && c.head_dim == 64 && c.d_model % 32 == 0 && c.d_ff % 32 == 0 &&
@@ -1312,7 +1317,16 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   // Split-context chunks per row: one when the rows and KV heads alone give every CU a
   // workgroup (the kernel then writes the normalized output and no merge launch
   // follows); the gemv O-projection's prologue merges GD_ATT_NCH partials.
-  const int nch = o_gemv ? GD_ATT_NCH
+  // Long contexts with few (row, KV head) pairs: 32 chunks, so that the scan spreads over
+  // the GPU (8 chunks of a 3700-position context leave 160 workgroups walking 460
+  // positions each: 18.5 -> 11.7 us, plus a 4.2 us merge, while the projection no longer
+  // merges in its prologue: 9.2 -> 4.1 us), merged by a launch of their own. With 8
+  // chunks already giving the CUs a workgroup each (8 rows x 5 KV heads), 32 measured
+  // slightly slower.
+  const bool long_split = !m->attn_chunks && max_T >= kLongCtxT && !fuse_ao &&
+                          M * c.n_kv_head * GD_ATT_NCH < m->n_cu;
+  const int nch = long_split ? GD_ATT_NCH_LONG
+                  : o_gemv ? GD_ATT_NCH
                   : m->attn_chunks ? m->attn_chunks
                   : (M * c.n_kv_head >= m->n_cu ? 1 : GD_ATT_NCH);
   // With one chunk per row (contiguous cache, head_dim 64, one query head per KV head,
@@ -1413,7 +1427,15 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
     // attention partials in its prologue, the mfma path merges them in a kernel first
     if (!fuse_ao && !fuse_ap) {
       LinParams p = base;
-      if (o_gemv) {
+      if (long_split) {
+        ProfScope ps(m, st, "attn_merge", "k_attn_merge_n",
+                     (double)M * c.n_head * (GD_ATT_NCH_LONG * (c.head_dim + 2) + c.head_dim) * 4.0);
+        GD_LAUNCH(k_attn_merge_n, dim3(c.n_head, M), dim3(64), 0, st, apart, c.n_head, c.head_dim, GD_ATT_NCH_LONG, attn,
+                  m->qdim);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        p.pro = PRO_COPY;
+        p.x = attn; p.ldx = m->qdim;
+      } else if (o_gemv) {
         p.pro = PRO_ATTN;
         p.apart = apart;
       } else {
@@ -1804,7 +1826,7 @@ extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids,
       return set_err(GD_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     }
   } else if (m->use_graph && !m->profile) {
-    GraphKey key{B, tok_dev, next_dev, logits_dev, max_T <= kFusedAttnOMaxT};
+    GraphKey key{B, tok_dev, next_dev, logits_dev, max_T <= kFusedAttnOMaxT, max_T >= kLongCtxT};
     auto it = m->graphs.find(key);
     if (it == m->graphs.end()) {
       if (m->graphs.size() >= kMaxGraphs) {
