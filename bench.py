@@ -275,8 +275,19 @@ def measured_traffic(kernel: str, workload: str):
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
 
 
+def dominant(rows):
+    """The kernel with the largest share of the step's kernel time. Shares within 2 % of
+    the largest are measurement noise between kernels of the same length (the batch-1
+    step runs four kernels of ~4.2 us per layer, whose order changes from run to run), so
+    among those the one that moves the most bytes per step is taken: the choice then
+    follows the workload, not the run."""
+    top = rows[0]["share"]
+    near = [r for r in rows if r["share"] >= 0.98 * top]
+    return max(near, key=lambda r: (r["bytes_per_launch"] * r["launches_per_step"], r["share"]))
+
+
 def roofline(rows, workload: str):
-    top = rows[0]
+    top = dominant(rows)
     ach = top["bytes_per_launch"] / (top["avg_us"] * 1e-6) / 1e9
     tr = measured_traffic(top["kernel"], workload)
     return {"bound": "hbm", "kernel": top["kernel"], "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
