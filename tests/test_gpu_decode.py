@@ -75,8 +75,8 @@ def test_llama_hd64_gqa_paged(mode):
     most 256 positions whose projections run on the GEMV take attention fused with the
     output projection; with the GEMV forced, 8 rows at 250-310 positions run
     split-context attention whose partials the GEMV projection (two launches of 4 rows)
-    merges in its prologue; with the MFMA forced, a merge launch and the MFMA projection
-    follow the split-context attention."""
+    merges in its prologue; with the MFMA forced, the MFMA projection merges the
+    split-context partials of its 6 rows while staging them."""
     batch, plen, variant = {"fused_attn_o": (2, (5, 60), 0), "gemv_split_context": (8, (250, 300), 1),
                             "mfma_split_context": (6, (5, 60), 2)}[mode]
     w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 11, batch, plen, 10, kv_block=16)
@@ -97,17 +97,19 @@ def test_llama_hd64_gqa_paged_one_chunk():
     _run_and_compare(w, W, prompts, 2e-2, variant=2, tables=tab, pool=pool, chunks=1)
 
 
-@pytest.mark.parametrize("mode", ["fused_attn_o", "one_chunk", "eight_chunks"])
+@pytest.mark.parametrize("mode", ["fused_attn_o", "one_chunk", "eight_chunks", "eight_chunks_20_rows"])
 def test_llama_hd64_gqa_contiguous(mode):
     """3 query heads per KV head on a contiguous cache (no block table): 2 rows at short
     contexts take the fused attention + output projection; 6 rows run split-context
-    attention with one or eight chunks per row and the matrix-core output projection."""
+    attention with one or eight chunks per row and the matrix-core output projection
+    (which merges the eight chunks while staging its rows); 20 rows with eight chunks
+    take the merge launch and then the 32-row matrix-core projection."""
     fused = mode == "fused_attn_o"
-    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 14, 2 if fused else 6,
-                       (5, 120 if fused else 200), 10)
+    w = synth.Workload("llama_hd64", LLAMA_HD64, synth.Init(bf16=True), 14,
+                       2 if fused else 20 if mode == "eight_chunks_20_rows" else 6, (5, 120 if fused else 200), 10)
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
-    _run_and_compare(w, W, prompts, 2e-2, variant=0 if fused else 2, chunks=8 if mode == "eight_chunks" else
+    _run_and_compare(w, W, prompts, 2e-2, variant=0 if fused else 2, chunks=8 if mode.startswith("eight_chunks") else
                      (1 if mode == "one_chunk" else 0))
 
 
@@ -132,7 +134,8 @@ def test_long_contexts_attention_chunks(variant, chunks):
     """Ragged contexts of 1..~900 positions: the scan runs 1..15 load rounds of 64
     positions, odd and even counts. With the matrix-core output projection and one
     chunk per row the attention writes its normalized output itself; with eight chunks
-    the partials are merged (the gemv projection always merges eight)."""
+    the partials are merged while the projection stages its rows (the gemv projection
+    always merges eight)."""
     w = synth.Workload("gpt2_hd64_long", GPT2_HD64_LONG, synth.Init(), 13, 5, (1, 880), 6)
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)

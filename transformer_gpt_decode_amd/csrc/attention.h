@@ -35,7 +35,7 @@ struct AttnParams {
   const long long* row_kvoff;         // contiguous: the row's own slot offset
   int M;
   float scale;
-  float* part;                        // [M][Hq][C][HD + 2]: max, sum, o[HD] (C chunks per row)
+  float* part;                        // [M][Hq][C][gd_apart_stride(HD)]: max, sum, -, -, o[HD] (C chunks per row)
   float* out; int ldo;                // one chunk per row: the normalized output [M][ldo]
 };
 
@@ -310,8 +310,8 @@ __global__ __launch_bounds__(NT) void k_attention(AttnParams p) {
     if (C == 1) {   // the whole context: l > 0 (the row's own position is in it)
       p.out[(size_t)row * p.ldo + (kh * G + g) * HD + d] = o / l;
     } else {
-      float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * C + c) * (HD + 2);
-      pp[2 + d] = o;
+      float* pp = p.part + (((size_t)row * p.Hq + kh * G + g) * C + c) * gd_apart_stride(HD);
+      pp[GD_APART_O + d] = o;
       if (d == 0) { pp[0] = m; pp[1] = l; }
     }
   }
@@ -512,14 +512,14 @@ template <int EPT>
 __device__ __forceinline__ void attn_merge_issue(const float* __restrict__ apart, int Hq, int hd, int M,
                                                  MergeRegs<EPT>& r, int nthr) {
   static_assert(GD_ATT_NCH == 8, "one chunk per lane of an 8-lane group");
-  const int tid = threadIdx.x, K = Hq * hd, stride = hd + 2;
+  const int tid = threadIdx.x, K = Hq * hd, stride = gd_apart_stride(hd);
   const int total = M * K, npair = M * Hq * GD_ATT_NCH;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int i = min(tid + nthr * j, total - 1);
     const int m = i / K, k = i - m * K;
     const int h = k / hd, d = k - h * hd;
-    const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + 2 + d;
+    const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + GD_APART_O + d;
 #pragma unroll
     for (int c = 0; c < GD_ATT_NCH; ++c) r.oc[j][c] = pp[(size_t)c * stride];
   }
@@ -531,7 +531,7 @@ __device__ __forceinline__ void attn_merge_issue(const float* __restrict__ apart
 template <int EPT>
 __device__ void attn_merge_finish(const float* __restrict__ apart, int Hq, int hd, int M, const MergeRegs<EPT>& r,
                                   float* dst, int ldd, float* s_w, int nthr) {
-  const int tid = threadIdx.x, K = Hq * hd, stride = hd + 2;
+  const int tid = threadIdx.x, K = Hq * hd, stride = gd_apart_stride(hd);
   const int total = M * K, npair = M * Hq * GD_ATT_NCH;
   for (int q0 = 0; q0 < npair; q0 += nthr) {   // npair is a multiple of 8: groups never straddle
     float mc = r.mc, lc = r.lc;
@@ -561,7 +561,7 @@ __device__ void attn_merge_finish(const float* __restrict__ apart, int Hq, int h
   for (int i = tid + nthr * EPT; i < total; i += nthr) {   // elements beyond the register share
     const int m = i / K, k = i - m * K;
     const int h = k / hd, d = k - h * hd;
-    const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + 2 + d;
+    const float* pp = apart + ((size_t)m * Hq + h) * GD_ATT_NCH * stride + GD_APART_O + d;
     const float* w = s_w + ((size_t)m * Hq + h) * GD_ATT_NCH;
     float o = 0.f;
 #pragma unroll
@@ -586,12 +586,12 @@ __device__ void attn_merge_rows(const float* __restrict__ apart, int Hq, int hd,
 // -inf) weigh 0; chunk 0 holds position 0, so max is finite.
 __global__ __launch_bounds__(64) void k_attn_merge_n(const float* part, int Hq, int hd, int C, float* out, int ldo) {
   const int h = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
-  const int stride = hd + 2, d = min(lane, hd - 1);
+  const int stride = gd_apart_stride(hd), d = min(lane, hd - 1);
   const float* pp = part + ((size_t)m * Hq + h) * C * stride;
-  const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)min(lane, C - 1) * stride);   // stride is even
+  const float2 ml = *reinterpret_cast<const float2*>(pp + (size_t)min(lane, C - 1) * stride);
   float ov[GD_ATT_NCH_LONG];
 #pragma unroll
-  for (int c = 0; c < GD_ATT_NCH_LONG; ++c) ov[c] = pp[(size_t)min(c, C - 1) * stride + 2 + d];
+  for (int c = 0; c < GD_ATT_NCH_LONG; ++c) ov[c] = pp[(size_t)min(c, C - 1) * stride + GD_APART_O + d];
   // keeps the loads above where they are (the pointers are not restrict-qualified, so
   // the clobber binds them): left alone, the compiler moves the value loads below the
   // reductions, after a wait for the (max, sum) pairs (two round trips)
@@ -612,6 +612,6 @@ __global__ __launch_bounds__(GD_WG) void k_attn_merge(const float* __restrict__ 
                                                       int ldo) {
   __shared__ float s_w[GD_MAX_HEADS * GD_ATT_NCH];
   const int m = blockIdx.x;
-  attn_merge_rows<4>(part + (size_t)m * Hq * GD_ATT_NCH * (hd + 2), Hq, hd, 1, out + (size_t)m * ldo, ldo, s_w,
+  attn_merge_rows<4>(part + (size_t)m * Hq * GD_ATT_NCH * gd_apart_stride(hd), Hq, hd, 1, out + (size_t)m * ldo, ldo, s_w,
                      GD_WG);
 }

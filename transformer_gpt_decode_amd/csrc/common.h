@@ -9,6 +9,11 @@
 #define GD_ATT_NCH 8       // context chunks (attention workgroups) per row and KV head
 #define GD_ATT_NCH_LONG 32 // chunks for long contexts with few rows (merged by a launch of their own)
 #define GD_MAX_HEADS 32    // query heads per layer
+// Split-context attention partials, per (row, query head, chunk): the running max, the
+// sum of weights, two unused words (so that the values start 16-byte aligned) and the
+// hd unnormalized weighted sums of V.
+#define GD_APART_O 4
+__host__ __device__ constexpr int gd_apart_stride(int hd) { return hd + GD_APART_O; }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -19,7 +19,9 @@
 //   (gain and shift loaded) or folded into the weights (see NRM_FOLDED). Dot products
 //   are reduced across the wave.
 // k_mm (5..32 rows): fp32 matrix-core tiles of 16 columns, activation rows held in
-//   registers in the MFMA operand layout; see the MFMA section below.
+//   registers in the MFMA operand layout; its prologue copies the rows or (output
+//   projection, up to 16 rows) merges the split-context attention partials into them;
+//   see the MFMA section below.
 //
 // Epilogues: bias, clamped tanh-GELU, residual add; SiLU-gated pairs (gate and up
 // rows interleaved, gate at even rows); QKV scatter (q to a buffer, k and v into the
@@ -59,7 +61,7 @@ struct LinParams {
   int pro, norm;
   const float* x; int ldx;                  // COPY (and MFMA input)
   const float* ng; const float* nb; float eps;
-  const float* apart; int Hq;               // ATTN: partials [M][Hq][GD_ATT_NCH][hd + 2]
+  const float* apart; int Hq, nch;          // ATTN: partials [M][Hq][nch][hd + 2] (k_gemv: nch = GD_ATT_NCH)
   int* err;
   const long long* row_kvoff;               // element offset of each row's K/V slot in a layer pool (-1: none)
   // ---- weights
@@ -677,9 +679,22 @@ __host__ __device__ constexpr int mm_lds_floats(int R) { return R * MM_LDX; }
 // element by element. Elsewhere the slots past a row's range hold a copy of its last
 // chunk, which only ever meets zero weight columns (the packed copy is zero past K), and
 // rows >= M hold copies of row M - 1, whose outputs are never stored.
-template <int WT, int MT, int EPI, int NRM, bool MP>
+//
+// PRO: PRO_COPY stages the rows of p.x; PRO_ATTN (the output projection behind
+// split-context attention, no norm, one register pass) forms them from the attention
+// partials p.apart [M][Hq][nch][gd_apart_stride(hd)] (per chunk: running max, sum of
+// weights and the unnormalized weighted sum of V), so that no merge launch precedes the
+// projection. Each lane loads, for its float4 of every real staged row, the float4 of
+// all nch (<= GD_ATT_NCH) chunks, and lane c of each aligned group of 8 the (max, sum)
+// of chunk c (the group's 32 columns lie in one head: hd is a multiple of 32); all at
+// once, before the weights (one memory round trip). The chunk weights e_c = exp(max_c -
+// max) / sum_c' e_c' sum_c' are formed as k_attn_merge forms them and shared within the
+// group by lane exchanges. A split spans at most 256 columns (one float4 slot per lane);
+// the host plans the splits so.
+template <int WT, int MT, int EPI, int NRM, bool MP, int PRO>
 __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   static_assert(!(NRM != NRM_NONE && MP), "the norm needs whole rows in one pass");
+  static_assert(PRO == PRO_COPY || (NRM == NRM_NONE && !MP && EPI == EPI_PLAIN), "merged rows: projection only");
   constexpr int R = MT * 16;          // activation rows of the tile (rows >= M discarded)
   constexpr int RPW = R / MM_NW;      // rows staged per wave
   constexpr int RS = 17;              // padded row stride of a partial tile in LDS
@@ -714,10 +729,30 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   // normalizes, writes the rows to LDS and reads this wave's operand blocks into xr.
   F8 xr[MM_JB][MT];
   f32x4 v[RPW][MM_JB], g[MM_JB], bb[MM_JB];
+  f32x4 ao[RPW][GD_ATT_NCH];    // PRO_ATTN: the chunks' values of this lane's float4
+  float2 aml[RPW];              // and chunk (lane & 7)'s (max, sum)
   auto stage_issue = [&](int cb, int ce) {
     const int ka = cb * 32;
     const int kq = (min(ce * 32, K) - ka) >> 2;   // float4 chunks of real columns per row
     const int pc = ((ce - cb) * 8 + 63) >> 6;     // chunks per lane (padded range)
+    if constexpr (PRO == PRO_ATTN) {
+      // slot 0 only (a split spans <= 256 columns); rows >= M (wave-uniform) are not
+      // loaded; chunks past nch repeat the last one and get weight 0
+      const int hd = p.hd, stride = gd_apart_stride(hd), C = p.nch;
+      const int col = ka + 4 * min(lane, kq - 1);
+      const int hh = col / hd, dd = col - hh * hd;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        if (wave + MM_NW * i < M) {
+          const float* pp = p.apart + ((size_t)(wave + MM_NW * i) * p.Hq + hh) * C * stride;
+          aml[i] = *reinterpret_cast<const float2*>(pp + (size_t)min(lane & 7, C - 1) * stride);
+#pragma unroll
+          for (int c = 0; c < GD_ATT_NCH; ++c)
+            ao[i][c] = *reinterpret_cast<const f32x4*>(pp + (size_t)min(c, C - 1) * stride + GD_APART_O + dd);
+        }
+      }
+      return;
+    }
     // Without a norm only the slots of the range's padded blocks are loaded (j < pc, a
     // wave-uniform test: the load pipeline of a CU is the bottleneck there); with a
     // norm every slot is, which keeps the statistics free of branches. Lanes past the
@@ -787,6 +822,33 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
     const int kq = (min(ce * 32, K) - cb * 32) >> 2;
     const int kqp = (ce - cb) * 8;
     const int pc = (kqp + 63) >> 6;
+    if constexpr (PRO == PRO_ATTN) {
+      // each real row: chunk weights within each 8-lane group (lane c: chunk c), then
+      // the weighted values in chunk order; rows >= M stage zeros
+      static_assert(GD_ATT_NCH == 8, "one chunk per lane of an 8-lane group");
+      const int gb = lane & ~7;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        f32x4 o = f4_zero();
+        if (wave + MM_NW * i < M) {
+          const bool live = (lane & 7) < p.nch;
+          const float mc = live ? aml[i].x : -INFINITY;
+          const float mx = group_max<GD_ATT_NCH>(mc);
+          const float e = expf(mc - mx);
+          const float l = group_sum<GD_ATT_NCH>((live ? aml[i].y : 0.f) * e);
+          const float w = e / l;
+#pragma unroll
+          for (int c = 0; c < GD_ATT_NCH; ++c) {
+            const float wc = __shfl(w, gb + c);
+            o.x = fmaf(wc, ao[i][c].x, o.x);
+            o.y = fmaf(wc, ao[i][c].y, o.y);
+            o.z = fmaf(wc, ao[i][c].z, o.z);
+            o.w = fmaf(wc, ao[i][c].w, o.w);
+          }
+        }
+        v[i][0] = o;
+      }
+    }
     if constexpr (NRM == NRM_FOLDED) {
       // shift each row by its first element (lane 0, slot 0): the shifted row is what the
       // MFMAs see; then its moments
@@ -840,7 +902,7 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
         const int ch = lane + 64 * j;
-        if (j < pc) *reinterpret_cast<f32x4*>(xs + m * MM_LDX + 4 * ch) = v[i][j];
+        if (j < pc && (PRO == PRO_COPY || j == 0)) *reinterpret_cast<f32x4*>(xs + m * MM_LDX + 4 * ch) = v[i][j];
       }
     }
     (void)kqp;
@@ -872,6 +934,7 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   // loads each just before its first use, inside the branch that uses it)
   asm volatile("" ::"s"(p.x), "s"(p.ldx), "s"(p.ng), "s"(p.nb), "s"(p.norm), "s"(p.eps), "s"(p.wtl), "s"(p.bias),
                "s"(p.resid), "s"(p.ldr), "s"(p.y), "s"(p.ldy));
+  if constexpr (PRO == PRO_ATTN) asm volatile("" ::"s"(p.apart), "s"(p.Hq), "s"(p.hd), "s"(p.nch));
   W8<WT> wa[MM_JB], wb[MM_JB];   // this tile's weights and the next tile's
   int t = wg;
   if constexpr (!MP) {

@@ -123,8 +123,11 @@ static const int kMaxK = 1 << 20;
 static const int kMmTargetWgs = 256;   // one matrix-core workgroup per CU
 
 // splittable: linear epilogue whose output is the residual, updated in place (the
-// K splits are then summed with atomics into it).
-static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bool norm, bool splittable = false) {
+// K splits are then summed with atomics into it). attn_rows: the rows are merged from
+// split-context attention partials (PRO_ATTN), which the matrix-core kernel does for
+// up to 16 rows with splits of at most 256 columns (head_dim a multiple of 32).
+static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bool norm, bool splittable = false,
+                           bool attn_rows = false) {
   LinPlan p;
   memset(&p, 0, sizeof(p));
   p.var = variant == 1 ? 0 : variant == 2 ? 1 : (M <= GEMV_MAX_ROWS ? 0 : 1);
@@ -153,6 +156,7 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
     if (splittable && !norm && epi == EPI_PLAIN) {
       p.splits = std::max(1, std::min(nb, kMmTargetWgs / ntiles));
       p.splits = std::max(p.splits, iceil(nb, MM_KC / 32));   // one register pass per split
+      if (attn_rows) p.splits = std::max(p.splits, iceil(nb, 8));   // one float4 slot per lane
     }
     p.passes = iceil(iceil(nb, p.splits) * 32, MM_KC);
     // at most one workgroup per CU; wider layers stream several tiles per workgroup
@@ -229,12 +233,22 @@ static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm0, hipStre
     prm.wtl = prm0.wfl;
     prm.bias = prm0.bf;
   }
-#define GD_MM(EPI, NRM, MP) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, MP>), g, b, 0, st, prm)
+#define GD_MM(EPI, NRM, MP) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, MP, PRO_COPY>), g, b, 0, st, prm)
 #define GD_MM_N(EPI)                                   \
   do {                                                 \
     if (fold) GD_MM(EPI, NRM_FOLDED, false);           \
     else GD_MM(EPI, NRM_EXPLICIT, false);              \
   } while (0)
+  if (prm.pro == PRO_ATTN) {   // the output projection behind split-context attention (<= 16 rows)
+    if constexpr (MT == 1) {
+      if (nrm || prm.epi != EPI_PLAIN || lp.passes > 1 || prm.nch < 1 || prm.nch > GD_ATT_NCH || prm.hd % 32 ||
+          iceil(iceil(prm.K, 32), lp.splits) > 8)
+        return hipErrorNotSupported;
+      GD_LAUNCH((k_mm<WT, MT, EPI_PLAIN, NRM_NONE, false, PRO_ATTN>), g, b, 0, st, prm);
+      return hipSuccess;
+    }
+    return hipErrorNotSupported;
+  }
   if (lp.passes > 1) {   // K range wider than one pass: plain or GELU epilogue, no norm
     if (nrm) return hipErrorNotSupported;
     if (prm.epi == EPI_PLAIN) GD_MM(EPI_PLAIN, NRM_NONE, true);
@@ -290,7 +304,7 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
       if (p.logits) p.logits += (size_t)r0 * p.ldl;
       if (p.row_kvoff) p.row_kvoff += r0;
       if (p.rope_cs) p.rope_cs += (size_t)r0 * p.hd;
-      if (p.apart) p.apart += (size_t)r0 * p.Hq * GD_ATT_NCH * (p.hd + 2);
+      if (p.apart) p.apart += (size_t)r0 * p.Hq * p.nch * gd_apart_stride(p.hd);
     }
     hipError_t e = launch_linear(wt, lp, p, st);
     if (e != hipSuccess) return e;
@@ -576,7 +590,7 @@ static void layout(gd_model* m) {
   m->o_h = take(R * ff * 4);
   m->o_amv = take(m->am_parts * R * 4);
   m->o_ami = take(m->am_parts * R * 4);
-  m->o_apart = take(R * c.n_head * GD_ATT_NCH_LONG * (c.head_dim + 2) * 4);
+  m->o_apart = take(R * c.n_head * GD_ATT_NCH_LONG * gd_apart_stride(c.head_dim) * 4);
   m->o_slog = take(R * (size_t)c.vocab * 4);
   // the tiled prompt pass: float or bf16 weights, head_dim 64, widths multiples of 32
   m->pf_ok = m->wt != GD_WEIGHT_Q8 && c.head_dim == 64 && c.d_model % 32 == 0 && c.d_ff % 32 == 0 &&
@@ -1122,8 +1136,8 @@ static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool n
     snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %d>", w, lp.nc, lp.rw, epi, pro,
              !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT);
   else
-    snprintf(buf, n, "k_mm<%d, %d, %d, %d, %s>", w, lp.mt, epi,
-             !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT, lp.passes > 1 ? "true" : "false");
+    snprintf(buf, n, "k_mm<%d, %d, %d, %d, %s, %d>", w, lp.mt, epi,
+             !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT, lp.passes > 1 ? "true" : "false", pro);
   return buf;
 }
 
@@ -1131,7 +1145,9 @@ static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool n
 // parameter once, the activation rows in, the outputs out (and the residual read).
 static double linear_bytes(const gd_model* m, const LinParams& p) {
   const int n_out = p.epi == EPI_SWIGLU ? p.N / 2 : (p.epi == EPI_ARGMAX ? (p.logits ? p.N : 0) : p.N);
-  double b = (double)p.N * p.K * m->elt + (double)p.M * p.K * 4 + (double)p.M * n_out * 4;
+  // rows in: as given, or the attention partials they are merged from
+  const double rows_in = p.pro == PRO_ATTN ? (double)p.M * p.Hq * p.nch * (p.hd + 2) * 4 : (double)p.M * p.K * 4;
+  double b = (double)p.N * p.K * m->elt + rows_in + (double)p.M * n_out * 4;
   if (m->wt == GD_WEIGHT_Q8) b += (double)p.N * (p.K / 32) * 4;   // block scales
   const float* zero = m->sp<float>(m->o_zero);
   if (p.bias && p.bias != zero) b += (double)p.N * 4;
@@ -1144,7 +1160,7 @@ static double linear_bytes(const gd_model* m, const LinParams& p) {
 static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, const LinParams& p,
                              int* am_out = nullptr) {
   const bool inplace = p.resid == p.y && p.ldr == p.ldy;
-  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE, inplace);
+  LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE, inplace, p.pro == PRO_ATTN);
   char kn[64];
   std::vector<std::pair<hipEvent_t, hipEvent_t>> fin;
   hipError_t e;
@@ -1310,8 +1326,10 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const float* zero = m->sp<float>(m->o_zero);
   int* err = m->sp<int>(m->o_err);
   hipError_t e;
-  // the gemv O-projection merges the attention partials in its prologue
+  // the gemv O-projection merges the attention partials in its prologue, and so does
+  // the matrix-core one for up to 16 rows
   const bool o_gemv = plan_linear(M, c.d_model, m->qdim, m->wt, m->variant, EPI_PLAIN, false).var == 0;
+  const bool o_mm_merge = !o_gemv && M <= 16 && c.head_dim % 32 == 0;
   // few rows at short contexts: attention fused with the output projection
   const bool fuse_ao = m->fuse_attn_o && o_gemv && max_T <= kFusedAttnOMaxT;
   // Split-context chunks per row: one when the rows and KV heads alone give every CU a
@@ -1435,9 +1453,10 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
         if ((e = hipGetLastError()) != hipSuccess) return e;
         p.pro = PRO_COPY;
         p.x = attn; p.ldx = m->qdim;
-      } else if (o_gemv) {
+      } else if (o_gemv || (o_mm_merge && nch == GD_ATT_NCH)) {
         p.pro = PRO_ATTN;
         p.apart = apart;
+        p.nch = GD_ATT_NCH;
       } else {
         if (nch > 1) {
           ProfScope ps(m, st, "attn_merge", "k_attn_merge", (double)M * c.n_head * (c.head_dim + 2) * 4.0 * 2);
