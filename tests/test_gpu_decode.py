@@ -357,16 +357,18 @@ def test_long_contexts_kv_bf16(chunks):
 LLAMA_LONG_SMALL = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 256, 300, 4096, 1e-5, 1e5)
 
 
-@pytest.mark.parametrize("kv", ["f32", "bf16"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "q8_weights"])
 def test_llama_contexts_past_1280(kv):
     """Split-context paged attention at 1300-3800 positions (n_ctx 4096), float or bf16
-    KV, shuffled block tables; the rows at different lengths share each step."""
-    w = synth.Workload("llama_long_small", LLAMA_LONG_SMALL, synth.Init(bf16=True, kv_bf16=kv == "bf16"), 17, 2,
-                       (1300, 3800), 6, kv_block=16)
+    KV, or 8-bit weights; shuffled block tables; the rows at different lengths share
+    each step (32 chunks per row, merged by a launch of their own)."""
+    q8 = kv == "q8_weights"
+    init = synth.Init(q8=True) if q8 else synth.Init(bf16=True, kv_bf16=kv == "bf16")
+    w = synth.Workload("llama_long_small", LLAMA_LONG_SMALL, init, 17, 2, (1300, 3800), 6, kv_block=16)
     W = synth.make_weights(w.shape, w.init, w.seed)
     prompts = synth.make_prompts(w)
     tab, pool = synth.make_block_tables(w, prompts)
-    _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool, config=f"llama long contexts ({kv} KV)")
+    _run_and_compare(w, W, prompts, 1e-3 if q8 else 2e-2, tables=tab, pool=pool, config=f"llama long contexts ({kv})")
 
 
 # ----------------------------------------------------------------- 8-bit weights

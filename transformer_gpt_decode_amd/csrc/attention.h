@@ -46,11 +46,15 @@ struct AttnParams {
 // exchanges and the waves through LDS. On return (after a barrier) thread
 // tid < G * HD holds, for query head g = tid / HD and dimension d = tid % HD, the
 // range's max, sum and weighted V (max -inf and zeros for an empty range).
+// A paged scan stages the block-table entries of its range in LDS, GD_ATT_TABN blocks
+// (a segment of the range) at a time.
+#define GD_ATT_TABN 256
 template <int HD, int G, int PPG, int NT = GD_WG>
 struct AttnScanLds {
   static constexpr int NW = NT / 64;
   float m[NW][G], l[NW][G];
   __align__(16) float o[NW][G][HD];
+  int tab[GD_ATT_TABN];   // paged: cache blocks of the current segment
 };
 
 // This lane's query values (lanes gl of every position group: dims 4 gl .. 4 gl + 3
@@ -124,6 +128,10 @@ __device__ __forceinline__ f32x4 kv_load4(const void* base, size_t e) {
 // Loads are unconditional (a position past the range is clamped to its last position,
 // an invalid cache block to block 0) and masked afterwards, so that the compiler keeps
 // them where they are issued instead of sinking them into branches.
+// Both caches run the same two-deep pipeline of steps. A paged range is scanned in
+// segments of at most GD_ATT_TABN cache blocks whose block-table entries are first
+// staged in LDS (one memory round trip per segment), so that a step's K/V addresses
+// come from LDS and the next step's loads can be in flight while one is consumed.
 // STREAM: each K/V element is read by one workgroup of the launch, so the contiguous
 // loads carry the non-temporal hint (they then displace less of what other workgroups
 // share in L2: the output projection's weights, the query rows).
@@ -140,6 +148,7 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
 
   size_t cbase = 0;   // contiguous: element offset of position 0 of this head (+ this lane's 4)
   const int* tab = nullptr;
+  int tb0 = 0;        // paged: first block of the current segment (sh.tab[0])
   if (PAGED) {
     tab = p.table + (size_t)rm.seq * p.max_blocks;
   } else {
@@ -153,16 +162,16 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
 
   f32x4 kv[PPG], vv[PPG], kv2[PPG], vv2[PPG];
   bool ok[PPG], ok2[PPG];
-  auto issue = [&](int s0, f32x4 (&kv)[PPG], f32x4 (&vv)[PPG], bool (&ok)[PPG]) {
+  auto issue = [&](int s0, int pe, f32x4 (&kv)[PPG], f32x4 (&vv)[PPG], bool (&ok)[PPG]) {
 #pragma unroll
     for (int j = 0; j < PPG; ++j) {
       const int pr = s0 + grp + NG * j;
-      const int ps = min(pr, p1 - 1);
-      ok[j] = pr < p1;
+      const int ps = min(pr, pe - 1);
+      ok[j] = pr < pe;
       size_t off;
       if (PAGED) {
         const int bi = ps / p.block_size;
-        const int blk = tab[bi];
+        const int blk = sh.tab[bi - tb0];
         const bool valid = (unsigned)blk < (unsigned)p.nblk;
         ok[j] = ok[j] && valid;
         off = (((size_t)(valid ? blk : 0) * p.Hkv + kh) * p.block_size + (ps - bi * p.block_size)) * HD + gl * 4;
@@ -209,30 +218,23 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
       mx[g] = nm;
     }
   };
-  if constexpr (PAGED) {
-    // the block-table read of a step feeds its own K/V addresses, so a step is waited
-    // for before the next one is issued
-    for (int s0 = p0; s0 < p1; s0 += STEP) {
-      issue(s0, kv, vv, ok);
-      consume(kv, vv, ok);
-    }
-  } else if (p0 < p1) {
-    // Two register sets: step i + 1 is in flight while step i is consumed (the wait
-    // before a consume covers only the older set: loads complete in issue order). Every
-    // path into the loop head has exactly the newer set in flight (an issue or exit
-    // between the halves would make the compiler wait for every load there); the last
-    // one or two steps are peeled off below the loop, so no load is issued past the range.
-    const int n = (p1 - p0 + STEP - 1) / STEP;
-    issue(p0, kv, vv, ok);
+  // Two register sets: step i + 1 is in flight while step i is consumed (the wait
+  // before a consume covers only the older set: loads complete in issue order). Every
+  // path into the loop head has exactly the newer set in flight (an issue or exit
+  // between the halves would make the compiler wait for every load there); the last
+  // one or two steps are peeled off below the loop, so no load is issued past the range.
+  auto scan_range = [&](int a, int b) {
+    const int n = (b - a + STEP - 1) / STEP;
+    issue(a, b, kv, vv, ok);
     int i = 0;
     for (; i + 2 < n; i += 2) {
-      issue(p0 + (i + 1) * STEP, kv2, vv2, ok2);
+      issue(a + (i + 1) * STEP, b, kv2, vv2, ok2);
       consume(kv, vv, ok);
-      issue(p0 + (i + 2) * STEP, kv, vv, ok);
+      issue(a + (i + 2) * STEP, b, kv, vv, ok);
       consume(kv2, vv2, ok2);
     }
     if (i + 1 < n) {
-      issue(p0 + (i + 1) * STEP, kv2, vv2, ok2);
+      issue(a + (i + 1) * STEP, b, kv2, vv2, ok2);
       // passing the older set through empty asm makes this branch's arithmetic differ
       // from the other's, which the compiler would otherwise hoist above the issue
 #pragma unroll
@@ -242,6 +244,23 @@ __device__ void attn_scan(const AttnParams& p, const AttnRow& rm, int kh, int p0
     } else {
       consume(kv, vv, ok);
     }
+  };
+  if constexpr (PAGED) {
+    // segments of at most GD_ATT_TABN blocks (p0, p1 and the block size are uniform, so
+    // every thread takes the same path through the barriers)
+    const int bs = p.block_size;
+    for (int a = p0; a < p1;) {
+      tb0 = a / bs;
+      const int b = min(p1, (tb0 + GD_ATT_TABN) * bs);
+      const int nbk = (b - 1) / bs - tb0 + 1;
+      if (a != p0) __syncthreads();   // the previous segment's entries have been read
+      for (int k = tid; k < nbk; k += NT) sh.tab[k] = tab[tb0 + k];
+      __syncthreads();
+      scan_range(a, b);
+      a = b;
+    }
+  } else if (p0 < p1) {
+    scan_range(p0, p1);
   }
   // merge the groups of each wave (lanes gl + LG r) by exchanges between lanes
 #pragma unroll
