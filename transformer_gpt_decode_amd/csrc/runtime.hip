@@ -1334,7 +1334,8 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
   const bool fuse_ao = m->fuse_attn_o && o_gemv && max_T <= kFusedAttnOMaxT;
   // Split-context chunks per row: one when the rows and KV heads alone give every CU a
   // workgroup (the kernel then writes the normalized output and no merge launch
-  // follows); the gemv O-projection's prologue merges GD_ATT_NCH partials.
+  // follows); else GD_ATT_NCH, whose partials the O-projection merges as it stages its
+  // rows (gemv, or matrix-core up to 16 rows) or a merge launch does.
   // Long contexts with few (row, KV head) pairs: 32 chunks, so that the scan spreads over
   // the GPU (8 chunks of a 3700-position context leave 160 workgroups walking 460
   // positions each: 18.5 -> 11.7 us, plus a 4.2 us merge, while the projection no longer
@@ -1441,8 +1442,9 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       else launch_attention<16, 3>(grid, st, a, paged, m->kv16);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // output projection + bias + residual (in place on x); the gemv kernel merges the
-    // attention partials in its prologue, the mfma path merges them in a kernel first
+    // output projection + bias + residual (in place on x); the attention partials are
+    // merged as the projection stages its rows (gemv; matrix-core up to 16 rows), else
+    // by a merge launch first
     if (!fuse_ao && !fuse_ap) {
       LinParams p = base;
       if (long_split) {
