@@ -543,15 +543,23 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
 
 // ------------------------------------------------------------------- MFMA
 //
-// k_mm (1..32 rows): 16-column tiles on v_mfma_f32_16x16x4f32 (bf16 weights widened
-// to fp32 in registers). Grid (G, S): workgroup (g, s) owns the 32-column K blocks
+// k_mm (1..32 rows): 16-column tiles on v_mfma_f32_16x16x4f32 (bf16 weights widened to
+// fp32 in registers) or, for workgroups that stream several tiles (PT), on the bf16
+// matrix cores (v_mfma_f32_16x16x32_bf16, 16 times the fp32 rate) in exact parts: the
+// staged activations are split once into three bf16 parts, fp32 weights as they arrive
+// (per block) as well; a product is then the sum of the part products with i + j <= 2
+// (six for fp32 weights: the dropped terms lie below 2^-24 of the product; three for
+// bf16 weights, which are one part: exact), smallest first, accumulated in fp32. With
+// one tile per workgroup the split of the activations outweighs the faster products.
+// Grid (G, S): workgroup (g, s) owns the 32-column K blocks
 // [s nb / S, (s + 1) nb / S) and the column tiles g, g + G, g + 2G, ...; S > 1 only for
 // a linear epilogue whose output is the residual, updated in place: each split adds
 // its partial sums to it with float atomics, the bias coming from split 0.
 //
 // Operand layout: lane l = 16 q + c holds W[n0 + c][kk + 8q .. +8] and
-// X[m0 + c][kk + 8q .. +8] for the 32-column block kk; MFMA step t of 8 feeds element t
-// of both, so one instruction contracts the k-values kk + 8q + t for A and B alike.
+// X[m0 + c][kk + 8q .. +8] for the 32-column block kk; fp32 MFMA step t of 8 feeds
+// element t of both, so one instruction contracts the k-values kk + 8q + t for A and B
+// alike (PT: eight bf16 values per part, one MFMA per part pair for the whole block).
 // D[i][j]: lane l holds column j = l % 16 and rows 4q + v.
 //
 // Loads are shaped for the memory pipeline rather than for that layout: a load
@@ -610,6 +618,36 @@ __global__ __launch_bounds__(GD_WG) void k_pack_tiles(const void* __restrict__ W
     if (n < N && k < K) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(W) + (size_t)n * K + k);
   }
   reinterpret_cast<u32x4*>(dst)[u] = v;
+}
+
+// bf16 parts of fp32 values (the matrix-core kernels): an fp32 value is the exact sum of
+// three bf16 parts, each the nearest bf16 to what the previous ones left (8 + 8 + 8
+// significant bits), and a product of two bf16 values is exact in fp32.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 bits, rounded to nearest even (element 0 in the low half).
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){x, y}, bf16x2_t));
+}
+
+// Four floats as three packed bf16 parts: a = hi + mid + lo.
+__device__ __forceinline__ void split3(const f32x4& a, uint2& hi, uint2& mid, uint2& lo) {
+  hi = make_uint2(pk_bf16(a.x, a.y), pk_bf16(a.z, a.w));
+  float r0 = a.x - bf16_lo(hi.x), r1 = a.y - bf16_hi(hi.x), r2 = a.z - bf16_lo(hi.y), r3 = a.w - bf16_hi(hi.y);
+  mid = make_uint2(pk_bf16(r0, r1), pk_bf16(r2, r3));
+  r0 -= bf16_lo(mid.x); r1 -= bf16_hi(mid.x); r2 -= bf16_lo(mid.y); r3 -= bf16_hi(mid.y);
+  lo = make_uint2(pk_bf16(r0, r1), pk_bf16(r2, r3));
+}
+
+// Eight consecutive fp32 values (two float4) as three bf16x8 parts.
+__device__ __forceinline__ void split3x8(const f32x4& a, const f32x4& b, u32x4 (&pt)[3]) {
+  uint2 ha, ma, la, hb, mb, lb;
+  split3(a, ha, ma, la);
+  split3(b, hb, mb, lb);
+  pt[0] = (u32x4){ha.x, ha.y, hb.x, hb.y};
+  pt[1] = (u32x4){ma.x, ma.y, mb.x, mb.y};
+  pt[2] = (u32x4){la.x, la.y, lb.x, lb.y};
 }
 
 template <int WT> struct W8;   // eight weights of one lane and block, as stored
@@ -691,7 +729,7 @@ __host__ __device__ constexpr int mm_lds_floats(int R) { return R * MM_LDX; }
 // max) / sum_c' e_c' sum_c' are formed as k_attn_merge forms them and shared within the
 // group by lane exchanges. A split spans at most 256 columns (one float4 slot per lane);
 // the host plans the splits so.
-template <int WT, int MT, int EPI, int NRM, bool MP, int PRO>
+template <int WT, int MT, int EPI, int NRM, bool MP, int PRO, bool PT>
 __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   static_assert(!(NRM != NRM_NONE && MP), "the norm needs whole rows in one pass");
   static_assert(PRO == PRO_COPY || (NRM == NRM_NONE && !MP && EPI == EPI_PLAIN), "merged rows: projection only");
@@ -727,7 +765,8 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
   // gain and shift); it runs before the weight loads, so that waiting for the rows does
   // not wait for the weights (vector loads complete in issue order). stage_finish
   // normalizes, writes the rows to LDS and reads this wave's operand blocks into xr.
-  F8 xr[MM_JB][MT];
+  F8 xr[MM_JB][MT];          // this wave's operand blocks (fp32 products)
+  u32x4 xp[MM_JB][MT][3];    // the same as three bf16 parts (PT)
   f32x4 v[RPW][MM_JB], g[MM_JB], bb[MM_JB];
   f32x4 ao[RPW][GD_ATT_NCH];    // PRO_ATTN: the chunks' values of this lane's float4
   float2 aml[RPW];              // and chunk (lane & 7)'s (max, sum)
@@ -914,8 +953,12 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const float* src = xs + (mt * 16 + c) * MM_LDX + blk * 32 + 8 * q;
-        xr[j][mt].a = *reinterpret_cast<const f32x4*>(src);
-        xr[j][mt].b = *reinterpret_cast<const f32x4*>(src + 4);
+        if constexpr (PT) {
+          split3x8(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4), xp[j][mt]);
+        } else {
+          xr[j][mt].a = *reinterpret_cast<const f32x4*>(src);
+          xr[j][mt].b = *reinterpret_cast<const f32x4*>(src + 4);
+        }
       }
     }
     __syncthreads();   // the staging area is reused for the partial tiles
@@ -970,12 +1013,30 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
       }
 #pragma unroll
       for (int j = 0; j < MM_JB; ++j) {
-        if (cb + wave + MM_NW * j < ce) {   // wave-uniform: MFMAs run with the whole wave
+        if (cb + wave + MM_NW * j < ce && !PT) {   // wave-uniform: MFMAs run with the whole wave
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int u = 0; u < 8; ++u)
               acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f8_at(xr[j][mt], u), w8_at<WT>(w[j], u), acc[mt], 0, 0, 0);
+        }
+        if (cb + wave + MM_NW * j < ce && PT) {
+          constexpr int NW = WT == 0 ? 3 : 1;   // parts of a weight
+          u32x4 wp[3];
+          if constexpr (WT == 0) split3x8(w[j].a, w[j].b, wp);
+          else wp[0] = w[j].a;
+          // the part pairs (pa, pw) with pa + pw <= 2, smallest terms first
+#pragma unroll
+          for (int sp = 2; sp >= 0; --sp)
+#pragma unroll
+            for (int pa = 0; pa <= sp; ++pa) {
+              const int pw = sp - pa;
+              if (pw >= NW) continue;
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xp[j][mt][pa]),
+                                                                  __builtin_bit_cast(bf16x8_t, wp[pw]), acc[mt], 0, 0, 0);
+            }
         }
       }
     }

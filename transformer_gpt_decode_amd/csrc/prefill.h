@@ -99,23 +99,6 @@ __global__ __launch_bounds__(PF_NT) void k_rownorm(const float* __restrict__ x, 
 // k values of row c of each operand.
 #define PF_PD 4   // K steps in flight
 #define PF_LDB 40 // LDS row stride of the bf16 part planes (elements; 16-byte aligned rows)
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Two floats to packed bf16 bits, rounded to nearest even (element 0 in the low half).
-__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){x, y}, bf16x2_t));
-}
-
-// Four floats as three packed bf16 parts: a = hi + mid + lo.
-__device__ __forceinline__ void split3(const f32x4& a, uint2& hi, uint2& mid, uint2& lo) {
-  hi = make_uint2(pk_bf16(a.x, a.y), pk_bf16(a.z, a.w));
-  float r0 = a.x - bf16_lo(hi.x), r1 = a.y - bf16_hi(hi.x), r2 = a.z - bf16_lo(hi.y), r3 = a.w - bf16_hi(hi.y);
-  mid = make_uint2(pk_bf16(r0, r1), pk_bf16(r2, r3));
-  r0 -= bf16_lo(mid.x); r1 -= bf16_hi(mid.x); r2 -= bf16_lo(mid.y); r3 -= bf16_hi(mid.y);
-  lo = make_uint2(pk_bf16(r0, r1), pk_bf16(r2, r3));
-}
-
 template <int WT, bool SPLIT>
 struct PfLds;
 template <int WT>

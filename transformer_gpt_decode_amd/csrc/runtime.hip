@@ -221,6 +221,15 @@ static hipError_t launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream
   }
 }
 
+// Whether a matrix-core launch multiplies on the bf16 matrix cores in parts: when its
+// workgroups stream several tiles (the head; the SwiGLU up-projection with the norm
+// applied to the rows), where the faster products outweigh splitting the activations
+// (with one tile per workgroup they measured slower).
+static bool mm_parts(const LinPlan& lp, int N, int epi, bool fold) {
+  if (lp.var != 1 || lp.passes != 1 || iceil(N, GD_TILE_N) <= lp.grid) return false;
+  return epi == EPI_ARGMAX || (epi == EPI_SWIGLU && !fold);
+}
+
 // A pre-norm whose folded form is given (fp32 weights, prm.wfl) runs as NRM_FOLDED on
 // the folded tile-major weights, bias and row sums.
 template <int WT, int MT>
@@ -233,7 +242,9 @@ static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm0, hipStre
     prm.wtl = prm0.wfl;
     prm.bias = prm0.bf;
   }
-#define GD_MM(EPI, NRM, MP) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, MP, PRO_COPY>), g, b, 0, st, prm)
+#define GD_MM(EPI, NRM, MP) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, MP, PRO_COPY, false>), g, b, 0, st, prm)
+  const bool pt = mm_parts(lp, prm.N, prm.epi, fold);
+#define GD_MM_PT(EPI, NRM) GD_LAUNCH((k_mm<WT, MT, EPI, NRM, false, PRO_COPY, true>), g, b, 0, st, prm)
 #define GD_MM_N(EPI)                                   \
   do {                                                 \
     if (fold) GD_MM(EPI, NRM_FOLDED, false);           \
@@ -244,7 +255,7 @@ static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm0, hipStre
       if (nrm || prm.epi != EPI_PLAIN || lp.passes > 1 || prm.nch < 1 || prm.nch > GD_ATT_NCH || prm.hd % 32 ||
           iceil(iceil(prm.K, 32), lp.splits) > 8)
         return hipErrorNotSupported;
-      GD_LAUNCH((k_mm<WT, MT, EPI_PLAIN, NRM_NONE, false, PRO_ATTN>), g, b, 0, st, prm);
+      GD_LAUNCH((k_mm<WT, MT, EPI_PLAIN, NRM_NONE, false, PRO_ATTN, false>), g, b, 0, st, prm);
       return hipSuccess;
     }
     return hipErrorNotSupported;
@@ -260,13 +271,23 @@ static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm0, hipStre
     case EPI_PLAIN: if (nrm) GD_MM_N(EPI_PLAIN); else GD_MM(EPI_PLAIN, NRM_NONE, false); break;
     case EPI_GELU: if (nrm) GD_MM_N(EPI_GELU); else GD_MM(EPI_GELU, NRM_NONE, false); break;
     // the remaining epilogues always follow a pre-norm
-    case EPI_SWIGLU: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_SWIGLU); break;
-    case EPI_ARGMAX: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_ARGMAX); break;
+    case EPI_SWIGLU:
+      if (!nrm) return hipErrorNotSupported;
+      if (pt) GD_MM_PT(EPI_SWIGLU, NRM_EXPLICIT);
+      else GD_MM_N(EPI_SWIGLU);
+      break;
+    case EPI_ARGMAX:
+      if (!nrm) return hipErrorNotSupported;
+      if (pt && fold) GD_MM_PT(EPI_ARGMAX, NRM_FOLDED);
+      else if (pt) GD_MM_PT(EPI_ARGMAX, NRM_EXPLICIT);
+      else GD_MM_N(EPI_ARGMAX);
+      break;
     case EPI_QKV: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_QKV); break;
     case EPI_QKV_ROPE: if (!nrm) return hipErrorNotSupported; GD_MM_N(EPI_QKV_ROPE); break;
     default: return hipErrorNotSupported;
   }
 #undef GD_MM_N
+#undef GD_MM_PT
 #undef GD_MM
   return hipSuccess;
 }
@@ -1128,16 +1149,17 @@ struct ProfScope {
   }
 };
 
-static const char* linear_kernel_name(int wt, const LinPlan& lp, int epi, bool norm, bool fold, int pro, char* buf,
-                                      size_t n) {
+static const char* linear_kernel_name(int wt, const LinPlan& lp, int N, int epi, bool norm, bool fold, int pro,
+                                      char* buf, size_t n) {
   const int w = wt == GD_WEIGHT_F32 ? 0 : wt == GD_WEIGHT_BF16 ? 1 : 2;
   // as rocprofv3 prints the instantiation
   if (lp.var == 0)
     snprintf(buf, n, "k_gemv<%d, %d, %d, %d, %d, %d>", w, lp.nc, lp.rw, epi, pro,
              !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT);
   else
-    snprintf(buf, n, "k_mm<%d, %d, %d, %d, %s, %d>", w, lp.mt, epi,
-             !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT, lp.passes > 1 ? "true" : "false", pro);
+    snprintf(buf, n, "k_mm<%d, %d, %d, %d, %s, %d, %s>", w, lp.mt, epi,
+             !norm ? NRM_NONE : (fold && w == 0) ? NRM_FOLDED : NRM_EXPLICIT, lp.passes > 1 ? "true" : "false", pro,
+             mm_parts(lp, N, epi, norm && fold && w == 0) ? "true" : "false");
   return buf;
 }
 
@@ -1166,7 +1188,7 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
   hipError_t e;
   {
     ProfScope ps(m, st, role,
-                 linear_kernel_name(m->wt, lp, p.epi, p.norm != NORM_NONE, p.wf != nullptr, p.pro, kn, sizeof(kn)),
+                 linear_kernel_name(m->wt, lp, p.N, p.epi, p.norm != NORM_NONE, p.wf != nullptr, p.pro, kn, sizeof(kn)),
                  m->profile ? linear_bytes(m, p) : 0);
     t_prof_fin = &fin;
     e = run_linear_rows(m->wt, lp, p, st, am_out);
