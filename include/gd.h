@@ -254,11 +254,13 @@ gd_status gd_device_errors(gd_model* m, int32_t* flags);
                                       * products. 1 (default): with bf16 weights on the
                                       * bf16 matrix cores, every fp32 activation split into
                                       * three bf16 parts (exact: three products per
-                                      * weight); with fp32 weights on the fp32 matrix
-                                      * cores. 2: bf16 parts for fp32 weights as well (the
-                                      * six largest of the nine part products, the dropped
-                                      * ones below 2^-24 of the product). 0: fp32 matrix
-                                      * cores for both. GD_ERR_INVALID for other values */
+                                      * weight); with fp32 weights the same for the GEMMs
+                                      * not split in K (QKV and MLP up: the weights split
+                                      * too, the six largest of the nine part products, the
+                                      * dropped ones below 2^-24 of the product) and the
+                                      * fp32 matrix cores for the split ones. 2: bf16 parts
+                                      * for every fp32 GEMM. 0: fp32 matrix cores for all.
+                                      * GD_ERR_INVALID for other values */
 #define GD_OPT_PROFILE 3 /* launch eagerly and time every kernel with a HIP event pair.
                           * 1: as enqueued (host enqueue gaps fall inside short pairs);
                           * 2: each decode step waits behind a 3 ms hold on a helper

@@ -1578,14 +1578,15 @@ static void launch_gemm_pf(hipStream_t st, const LinParams& p, int S, int nrm) {
 static hipError_t run_gemm_pf(gd_model* m, hipStream_t st, const char* role, const LinParams& p,
                               int nrm = PFN_NONE) {
   char kn[48];
+  const int S = gemm_pf_splits(m, p);
   // bf16 parts: the default for bf16 weights (three products per weight, 1.3-1.8x
-  // faster); for fp32 weights (six products, the weights split too) only on request:
-  // the narrow split-K GEMMs measured slower that way and the wide ones faster
-  const bool parts = m->wt == GD_WEIGHT_F32 ? m->pf_parts == 2 : m->pf_parts >= 1;
+  // faster); for fp32 weights (six products, the weights split too) by default only
+  // for the unsplit GEMMs (the wide QKV and MLP-up): the narrow split-K ones measured
+  // slower that way
+  const bool parts = m->wt == GD_WEIGHT_F32 ? (m->pf_parts == 2 || (m->pf_parts == 1 && S == 1)) : m->pf_parts >= 1;
   snprintf(kn, sizeof(kn), "k_gemm_pf<%d, %d, %s, %d>", m->wt == GD_WEIGHT_F32 ? 0 : 1, p.epi, parts ? "true" : "false",
            nrm);
   ProfScope ps(m, st, role, kn, (double)p.N * p.K * m->elt + 4.0 * p.M * (p.K + p.N));
-  const int S = gemm_pf_splits(m, p);
   if (m->wt == GD_WEIGHT_F32) {
     if (parts) launch_gemm_pf<0, true>(st, p, S, nrm);
     else launch_gemm_pf<0, false>(st, p, S, nrm);
