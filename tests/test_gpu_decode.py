@@ -224,6 +224,36 @@ def test_gpt2_124m_random_norms_and_biases():
     assert not rep["flips"], rep["flips"]
 
 
+@pytest.mark.parametrize("fold", [True, False], ids=["folded_norm", "norm_applied"])
+def test_gpt2_124m_batched_random_norms_head_parts(fold):
+    """GPT-2 124M shape, 6 sequences (matrix-core GEMMs), random norm parameters and
+    biases: the head's 3142 column tiles stream through 256 workgroups, which multiply in
+    exact bf16 parts, with the final norm folded into the tied embedding or applied to
+    the rows."""
+    w = dataclasses.replace(synth.WORKLOADS["gpt2_b32"], batch=6, prompt_len=(2, 30), n_generate=6)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 105)
+    prompts = synth.make_prompts(w)
+    rep, _, _ = _run_and_compare(w, W, prompts, 1e-3, fold=fold,
+                                 config=f"gpt2 124M batch 6, random norms ({'folded' if fold else 'applied'})")
+    assert not rep["flips"], rep["flips"]
+
+
+# Llama layout, small but with a SwiGLU up-projection and a head wide enough (320 and 512
+# column tiles) for their workgroups to stream several tiles (bf16 parts)
+LLAMA_WIDE_FF = synth.Shape(synth.ARCH_LLAMA, 2, 192, 3, 1, 64, 2560, 8192, 256, 1e-5, 1e5)
+
+
+def test_llama_wide_mlp_and_head_parts():
+    """bf16 weights, 6 rows, paged: the SwiGLU up-projection (5120 rows) and the head
+    (8192 rows) run in bf16 parts on the matrix cores, with random norm gains."""
+    w = synth.Workload("llama_wide_ff", LLAMA_WIDE_FF, synth.Init(bf16=True), 19, 6, (5, 120), 8, kv_block=16)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 106)
+    prompts = synth.make_prompts(w)
+    tab, pool = synth.make_block_tables(w, prompts)
+    rep, _, _ = _run_and_compare(w, W, prompts, 2e-2, tables=tab, pool=pool, config="llama wide MLP and head (bf16 parts)")
+    assert not rep["flips"], rep["flips"]
+
+
 @pytest.mark.parametrize("wdt", ["f32", "bf16"])
 def test_gpt2_124m_batched_short(wdt):
     """GPT-2 124M shape, 5 sequences with ragged prompts, MFMA path for the linears."""
