@@ -18,10 +18,11 @@
 //   (LayerNorm or RMSNorm) is taken per wave in registers, either applied to the row
 //   (gain and shift loaded) or folded into the weights (see NRM_FOLDED). Dot products
 //   are reduced across the wave.
-// k_mm (5..32 rows): fp32 matrix-core tiles of 16 columns, activation rows held in
-//   registers in the MFMA operand layout; its prologue copies the rows or (output
-//   projection, up to 16 rows) merges the split-context attention partials into them;
-//   see the MFMA section below.
+// k_mm (5..32 rows): matrix-core tiles of 16 columns (fp32 products, or exact bf16
+//   parts where a workgroup streams several tiles), activation rows held in registers in
+//   the MFMA operand layout; its prologue copies the rows or (output projection, up to 16
+//   rows) merges the split-context attention partials into them; see the MFMA section
+//   below.
 //
 // Epilogues: bias, clamped tanh-GELU, residual add; SiLU-gated pairs (gate and up
 // rows interleaved, gate at even rows); QKV scatter (q to a buffer, k and v into the
@@ -61,7 +62,7 @@ struct LinParams {
   int pro, norm;
   const float* x; int ldx;                  // COPY (and MFMA input)
   const float* ng; const float* nb; float eps;
-  const float* apart; int Hq, nch;          // ATTN: partials [M][Hq][nch][hd + 2] (k_gemv: nch = GD_ATT_NCH)
+  const float* apart; int Hq, nch;          // ATTN: partials [M][Hq][nch][gd_apart_stride(hd)] (k_gemv: nch = GD_ATT_NCH)
   int* err;
   const long long* row_kvoff;               // element offset of each row's K/V slot in a layer pool (-1: none)
   // ---- weights
