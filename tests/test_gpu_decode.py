@@ -201,6 +201,50 @@ def test_tiny_gpt2_batches_interleaved():
     m.close()
 
 
+def test_set_up_in_qkv_and_set_up_launch_alternate():
+    """Steps of up to 4 rows run the step's set-up (embedding, row metadata) inside the
+    first QKV launch and advance the sequence lengths in the argmax finalize; steps of 6
+    rows stage their rows through the set-up launch, which advances them itself. Six
+    sequences decoded alternately as one batch of 6 and as batches of 4 and 2 (slots
+    reordered) must match the oracle at every step."""
+    import torch
+    w = dataclasses.replace(synth.WORKLOADS["tiny"], batch=6, prompt_len=(2, 24), n_generate=14)
+    W = perturb_norms_and_biases(w.shape, synth.make_weights(w.shape, w.init, w.seed), 105)
+    prompts = synth.make_prompts(w)
+    ref_tok, ref_lg = oracle_generate(w, W, prompts)
+    m = gd_model(w, W)
+    dev = device()
+    V = w.shape.vocab
+    tok = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    out = torch.zeros((w.batch, w.n_generate), dtype=torch.int32, device=dev)
+    lg = torch.empty((w.batch, w.n_generate, V), dtype=torch.float32, device=dev)
+    for b, p in enumerate(prompts):
+        m.reset_seq(b)
+        m.prefill(b, p, tok[b:b + 1], lg[b, 0])
+        out[b, 0] = tok[b]
+    step_lg = torch.empty((w.batch, V), dtype=torch.float32, device=dev)
+    for i in range(1, w.n_generate):
+        groups = [[0, 1, 2, 3, 4, 5]] if i % 2 else [[5, 3, 1, 0], [2, 4]]
+        for g in groups:
+            t_in = torch.stack([tok[b] for b in g])
+            t_out = torch.zeros(len(g), dtype=torch.int32, device=dev)
+            m.decode_step(g, t_in, t_out, step_lg[:len(g)])
+            for k, b in enumerate(g):
+                tok[b] = t_out[k]
+                out[b, i] = t_out[k]
+                lg[b, i] = step_lg[k]
+    torch.cuda.synchronize()
+    assert m.device_errors() == 0
+    rep = compare_generation(out.cpu().numpy(), lg.cpu().numpy(), ref_tok, ref_lg, 1e-3,
+                             "tiny (set-up in QKV / set-up launch alternating)")
+    assert not rep["flips"], rep
+    # (a device length out of step with the host's would have moved the attended
+    # positions and the logits above)
+    for b, p in enumerate(prompts):
+        assert m.seq_len(b) == len(p) + w.n_generate - 1
+    m.close()
+
+
 @pytest.mark.parametrize("fold", [True, False], ids=["folded", "applied"])
 @pytest.mark.parametrize("variant", [0, 2], ids=["auto", "mfma"])
 def test_tiny_gpt2_random_norms_and_biases(variant, fold):

@@ -32,10 +32,12 @@
 #pragma once
 #include "common.h"
 #include "attention.h"
+#include "misc.h"
 
 // Source of the activation rows.
-#define PRO_COPY 0   // x rows as given
-#define PRO_ATTN 3   // merge of split-context attention partials
+#define PRO_COPY 0    // x rows as given
+#define PRO_ATTN 3    // merge of split-context attention partials
+#define PRO_EMBED 4   // the decode rows' input embeddings (k_gemv, QKV: the step's set-up folded in)
 // Row normalization applied after the source (LinParams::norm).
 #define NORM_NONE 0
 #define NORM_LN 1    // (x - mean) / sqrt(var + eps) * g + b, biased variance
@@ -85,6 +87,14 @@ struct LinParams {
   const float* rope_cs;                     // [M][hd]: each row's cos | sin of pair i (NULL: no RoPE)
   void* kc; void* vc;                       // K / V pools of the layer: float, or bf16 bits if kv16
   int kv16;
+  // ---- EMBED: row b < M is token e_tok[b] of sequence slot e_sids[b] at that
+  // sequence's length e_len[.], as k_setup_decode takes it; erp addresses the tables,
+  // the cache's block table and the rows' metadata that workgroup 0 stores
+  RowParams erp;
+  const int* e_sids; const int* e_tok; const int* e_len; const int* e_cap;
+  // ---- host side: the argmax finalize behind this launch advances len[adv_seq[b]] to
+  // adv_pos[b] + 1 (NULL: it does not)
+  int* adv_len; const int* adv_seq; const int* adv_pos;
 };
 
 // ------------------------------------------------------------ shared pieces
@@ -118,7 +128,9 @@ struct EpiOps {
   long long kvoff;    // the row's cache slot (QKV)
 };
 
-template <int EPI, bool FOLD = false>
+// META: the row's cache slot and RoPE row come from p.row_kvoff / p.rope_cs (else the
+// caller fills them in).
+template <int EPI, bool FOLD = false, bool META = true>
 __device__ __forceinline__ EpiOps epi_prefetch(const LinParams& p, int m, int n) {
   EpiOps e;
   e.b0 = e.b1 = e.r0 = 0.f;
@@ -135,15 +147,17 @@ __device__ __forceinline__ EpiOps epi_prefetch(const LinParams& p, int m, int n)
     e.r0 = p.resid[(size_t)m * p.ldr + n];
   } else if (EPI == EPI_QKV) {
     e.b0 = p.bias[n];
-    e.kvoff = p.row_kvoff[m];
+    if (META) e.kvoff = p.row_kvoff[m];
   } else if (EPI == EPI_QKV_ROPE) {
     e.b0 = p.bias[n];
     e.b1 = p.bias[n + 1];
-    e.kvoff = p.row_kvoff[m];
-    const int i = (n % p.hd) >> 1;
-    const float* cs = p.rope_cs + (size_t)m * p.hd;
-    e.c = cs[i];
-    e.s = cs[(p.hd >> 1) + i];
+    if (META) {
+      e.kvoff = p.row_kvoff[m];
+      const int i = (n % p.hd) >> 1;
+      const float* cs = p.rope_cs + (size_t)m * p.hd;
+      e.c = cs[i];
+      e.s = cs[(p.hd >> 1) + i];
+    }
   }
   return e;
 }
@@ -230,6 +244,216 @@ __device__ __forceinline__ void stage_finish(const LinParams& p, float* xs, cons
   }
 }
 
+// ---- PRO_EMBED: the decode step's set-up done by its first QKV launch (a GEMV).
+// Every workgroup takes the rows' (sequence, position, token) as k_setup_decode does
+// (the position is the sequence's length, kept below its capacity; a token or learned
+// position out of range is replaced by 0) and forms x_b = wte[t] (+ wpe[p]) itself
+// ("bare-metal-llm", "What got built": token and learned position embeddings).
+// Workgroup 0 also stores the rows, their metadata and the error flags for the later
+// launches of the step. The step's argmax finalize advances the lengths, after every
+// workgroup here has read them.
+struct EmbMeta {
+  int vseq, vtok;   // lane m < M: row m's sequence slot and token as loaded
+  int seq[GEMV_MAX_ROWS], pos[GEMV_MAX_ROWS], tok[GEMV_MAX_ROWS], ppos[GEMV_MAX_ROWS], flags[GEMV_MAX_ROWS];
+};
+
+// v[m] of a row index m < GEMV_MAX_ROWS held in a register (no indexed register array)
+__device__ __forceinline__ int sel_row(int m, const int (&v)[GEMV_MAX_ROWS]) {
+  return m == 0 ? v[0] : m == 1 ? v[1] : m == 2 ? v[2] : v[3];
+}
+
+// Issued before the weights (vector loads complete in issue order, so waiting for
+// these does not wait for the weight stream): lane m loads row m's sequence slot and
+// token.
+__device__ __forceinline__ void emb_meta_issue(const LinParams& p, EmbMeta& em) {
+  const int lm = min((int)(threadIdx.x & 63), p.M - 1);
+  em.vseq = p.e_sids[lm];
+  em.vtok = p.e_tok[lm];
+}
+
+// After the weights: the tokens (an out-of-range one is replaced by 0) ...
+__device__ __forceinline__ void emb_meta_tokens(const LinParams& p, EmbMeta& em) {
+#pragma unroll
+  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+    const int tok = __builtin_amdgcn_readlane(em.vtok, m);
+    const bool ok = tok >= 0 && tok < p.erp.vocab;
+    em.tok[m] = ok ? tok : 0;
+    em.flags[m] = ok ? 0 : GD_DERR_TOKEN;
+    em.seq[m] = __builtin_amdgcn_readlane(em.vseq, m);
+  }
+}
+
+// ... then the sequences' lengths and capacities (scalar loads), clamped as
+// k_setup_decode does.
+__device__ __forceinline__ void emb_meta_finish(const LinParams& p, EmbMeta& em) {
+  const RowParams& r = p.erp;
+  int len[GEMV_MAX_ROWS], cap[GEMV_MAX_ROWS];
+#pragma unroll
+  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+    len[m] = p.e_len[em.seq[m]];
+    cap[m] = p.e_cap[em.seq[m]];
+  }
+#pragma unroll
+  for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
+    int pos = len[m];
+    int fl = em.flags[m];
+    if (pos >= cap[m]) { fl |= GD_DERR_POS; pos = cap[m] - 1; }
+    int ppos = pos;
+    if (r.wpe && (ppos < 0 || ppos >= r.n_pos)) { fl |= GD_DERR_POS; ppos = 0; }
+    em.pos[m] = pos;
+    em.ppos[m] = ppos;
+    em.flags[m] = fl;
+  }
+}
+
+// Four consecutive elements of an embedding table (the weights' type): float4, four
+// bf16, four int8 codes (with their block scale).
+template <int WT>
+struct EmbChunk;
+template <>
+struct EmbChunk<0> { typedef f32x4 T; };
+template <>
+struct EmbChunk<1> { typedef uint2 T; };
+template <>
+struct EmbChunk<2> { typedef uint32_t T; };
+
+template <int WT>
+struct EmbLoad {
+  typename EmbChunk<WT>::T a, b;   // wte, wpe
+  float sa, sb;                    // 8-bit: block scales
+};
+
+// Chunk (m, k) of wte[t] (needs the tokens only) ...
+template <int WT>
+__device__ __forceinline__ void emb_load_te(const LinParams& p, const EmbMeta& em, int m, int k, EmbLoad<WT>& l) {
+  typedef typename EmbChunk<WT>::T ET;
+  constexpr int ES = WT == 0 ? 4 : WT == 1 ? 2 : 1;
+  const RowParams& r = p.erp;
+  const size_t et = (size_t)sel_row(m, em.tok) * r.d + k;
+  l.a = *reinterpret_cast<const ET*>(reinterpret_cast<const char*>(r.wte) + et * ES);
+  l.sa = 1.f;
+  if constexpr (WT == 2) l.sa = r.wte_sc[et >> 5];
+}
+
+// ... and of wpe[p] (the positions).
+template <int WT>
+__device__ __forceinline__ void emb_load_pe(const LinParams& p, const EmbMeta& em, int m, int k, EmbLoad<WT>& l) {
+  typedef typename EmbChunk<WT>::T ET;
+  constexpr int ES = WT == 0 ? 4 : WT == 1 ? 2 : 1;
+  const RowParams& r = p.erp;
+  const size_t ep = (size_t)sel_row(m, em.ppos) * r.d + k;
+  l.b = *reinterpret_cast<const ET*>(reinterpret_cast<const char*>(r.wpe) + ep * ES);
+  l.sb = 1.f;
+  if constexpr (WT == 2) l.sb = r.wpe_sc[ep >> 5];
+}
+
+// x = wte[t][k..k+3] (+ wpe[p][k..k+3]), as k_setup_decode sums them.
+template <int WT>
+__device__ __forceinline__ f32x4 emb_value(const EmbLoad<WT>& l, bool pe) {
+  f32x4 v;
+  if constexpr (WT == 0) {
+    v = l.a;
+    if (pe) { v.x += l.b.x; v.y += l.b.y; v.z += l.b.z; v.w += l.b.w; }
+  } else if constexpr (WT == 1) {
+    v = (f32x4){bf16_lo(l.a.x), bf16_hi(l.a.x), bf16_lo(l.a.y), bf16_hi(l.a.y)};
+    if (pe) { v.x += bf16_lo(l.b.x); v.y += bf16_hi(l.b.x); v.z += bf16_lo(l.b.y); v.w += bf16_hi(l.b.y); }
+  } else {
+    v = (f32x4){q8_at(l.a, 0) * l.sa, q8_at(l.a, 1) * l.sa, q8_at(l.a, 2) * l.sa, q8_at(l.a, 3) * l.sa};
+    if (pe) {
+      v.x += q8_at(l.b, 0) * l.sb; v.y += q8_at(l.b, 1) * l.sb;
+      v.z += q8_at(l.b, 2) * l.sb; v.w += q8_at(l.b, 3) * l.sb;
+    }
+  }
+  return v;
+}
+
+// This thread's chunks of all rows: chunk j is i = tid + GD_WG j of the M K / 4; XE
+// covers GEMV_MAX_ROWS rows, and the chunks past the M rows are not loaded.
+template <int WT, int XE>
+__device__ __forceinline__ void emb_issue_te(const LinParams& p, const EmbMeta& em, EmbLoad<WT> (&el)[XE]) {
+  const int tid = threadIdx.x, K4 = p.K >> 2, MK4 = p.M * K4;
+#pragma unroll
+  for (int j = 0; j < XE; ++j) {
+    const int i = tid + GD_WG * j;
+    if (i < MK4) {
+      const int m = i / K4, k = (i - m * K4) << 2;
+      emb_load_te<WT>(p, em, m, k, el[j]);
+    }
+  }
+}
+
+template <int WT, int XE>
+__device__ __forceinline__ void emb_issue_pe(const LinParams& p, const EmbMeta& em, EmbLoad<WT> (&el)[XE]) {
+  const int tid = threadIdx.x, K4 = p.K >> 2, MK4 = p.M * K4;
+#pragma unroll
+  for (int j = 0; j < XE; ++j) {
+    const int i = tid + GD_WG * j;
+    if (i < MK4) {
+      const int m = i / K4, k = (i - m * K4) << 2;
+      emb_load_pe<WT>(p, em, m, k, el[j]);
+    }
+  }
+}
+
+// The rows into LDS xs[m * K + k].
+template <int WT, int XE>
+__device__ __forceinline__ void emb_finish(const LinParams& p, const EmbLoad<WT> (&el)[XE], float* xs) {
+  const int tid = threadIdx.x, K = p.K, K4 = K >> 2, MK4 = p.M * K4;
+  const bool pe = p.erp.wpe != nullptr;
+#pragma unroll
+  for (int j = 0; j < XE; ++j) {
+    const int i = tid + GD_WG * j;
+    if (i < MK4) {
+      const int m = i / K4, k = (i - m * K4) << 2;
+      *reinterpret_cast<f32x4*>(xs + m * K + k) = emb_value<WT>(el[j], pe);
+    }
+  }
+}
+
+// The row's K/V slot (kv_slot_offset with the block-table load unconditional).
+__device__ __forceinline__ long long emb_kvoff(const RowParams& r, int seq, int pos) {
+  const int bi = max(pos, 0) / r.block_size;
+  const int blk = r.table[(size_t)seq * r.max_blocks + min(bi, r.max_blocks - 1)];
+  if (pos < 0 || bi >= r.max_blocks || (unsigned)blk >= (unsigned)r.nblk) return -1;
+  return ((long long)blk * r.Hkv * r.block_size + (pos - bi * r.block_size)) * r.hd;
+}
+
+// The QKV epilogue's row metadata of output (m, n) from the embedding prologue.
+template <int EPI>
+__device__ __forceinline__ void emb_epi_ops(const LinParams& p, const EmbMeta& em, int m, int n, EpiOps& e) {
+  const RowParams& r = p.erp;
+  const int pos = sel_row(m, em.pos);
+  e.kvoff = emb_kvoff(r, sel_row(m, em.seq), pos);
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    const int i = (n % p.hd) >> 1;
+    const float* cs = r.rope + (size_t)min(max(pos, 0), r.n_pos - 1) * p.hd;
+    e.c = cs[i];
+    e.s = cs[(p.hd >> 1) + i];
+  }
+}
+
+// Workgroup 0: the rows' metadata (lane m < M of wave 0, which owns row m's output and
+// holds its slot in e), error flags and RoPE rows, as k_setup_decode leaves them.
+template <int EPI>
+__device__ __forceinline__ void emb_publish(const LinParams& p, const EmbMeta& em, const EpiOps& e) {
+  const RowParams& r = p.erp;
+  const int tid = threadIdx.x;
+  if (tid < p.M) {
+    r.row_seq[tid] = sel_row(tid, em.seq);
+    r.row_pos[tid] = sel_row(tid, em.pos);
+    r.row_tok[tid] = sel_row(tid, em.tok);
+    r.row_kvoff[tid] = e.kvoff;
+    const int fl = sel_row(tid, em.flags) | (e.kvoff < 0 ? GD_DERR_BLOCK : 0);
+    if (fl) atomicOr(p.err, fl);
+  }
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    for (int i = tid; i < p.M * p.hd; i += GD_WG) {
+      const int m = i / p.hd, j = i - m * p.hd;
+      r.row_cs[i] = r.rope[(size_t)min(max(sel_row(m, em.pos), 0), r.n_pos - 1) * p.hd + j];
+    }
+  }
+}
+
 template <int WT>
 struct WChunk;
 template <>
@@ -283,11 +507,16 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
   stage_issue<XPT, PRO>(p, rr);
   MergeRegs<4> ar;
   stage_issue_attn<PRO>(p, ar);
+  const float* bsrc = p.nb ? p.nb : p.ng;
+  EmbMeta em;
+  if constexpr (PRO == PRO_EMBED) {
+    emb_meta_issue(p, em);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // the norm's gain and shift at this lane's chunks (RMSNorm: no shift; the gain is
   // loaded in its place so that the number of loads stays fixed)
   f32x4 gn[NC][CE / 4], bn[NC][CE / 4];
   if constexpr (NRM == NRM_EXPLICIT) {
-    const float* bsrc = p.nb ? p.nb : p.ng;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int k = min((lane + 64 * i) * CE, K - CE);
@@ -323,22 +552,47 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
         wsc[r][i] = p.wsc[(size_t)min(nw0 + r, N - 1) * (K >> 5) + (k >> 5)];
       }
   }
+  // embedding rows (PRO_EMBED), loaded after the weights: the token rows once the rows'
+  // slots and tokens (loaded before the weights) are in, the position rows after one
+  // more scalar round trip (the sequences' lengths); both overlap the weight stream
+  constexpr int XE = PRO == PRO_EMBED ? GEMV_MAX_ROWS * XPT : 1;
+  EmbLoad<WT> el[XE];
+  if constexpr (PRO == PRO_EMBED) {
+    __builtin_amdgcn_sched_barrier(0);
+    emb_meta_tokens(p, em);
+    emb_issue_te<WT, XE>(p, em, el);
+    emb_meta_finish(p, em);
+    if (p.erp.wpe) emb_issue_pe<WT, XE>(p, em, el);
+  }
   // 2. epilogue operands of this lane's output (lane m * RW + r), or pair (lane m)
   constexpr bool PAIR = EpiTraits<EPI>::pair;
   static_assert(!PAIR || RW == 2, "pair epilogues need both rows of the pair in one wave");
+  static_assert(PRO != PRO_EMBED || EPI == EPI_QKV || EPI == EPI_QKV_ROPE, "embedding rows: the QKV launch only");
   const int om = PAIR ? lane : lane / RW, orr = PAIR ? 0 : lane % RW;
   const int on = nw0 + orr;
   const bool own = EPI != EPI_ARGMAX && om < M && (PAIR ? nw0 + 1 < N : (lane < M * RW && on < N));
   // argmax: lane m * RW + r finishes output (m, nw0 + r)
   const int an = min(nw0 + lane % RW, N - 1);
-  EpiOps eo = EPI == EPI_ARGMAX ? epi_prefetch<EPI, NRM == NRM_FOLDED>(p, 0, an)
-                                : epi_prefetch<EPI, NRM == NRM_FOLDED>(p, own ? om : 0, own ? on : 0);
+  constexpr bool META = PRO != PRO_EMBED;
+  EpiOps eo = EPI == EPI_ARGMAX ? epi_prefetch<EPI, NRM == NRM_FOLDED, META>(p, 0, an)
+                                : epi_prefetch<EPI, NRM == NRM_FOLDED, META>(p, own ? om : 0, own ? on : 0);
+  if constexpr (PRO == PRO_EMBED) emb_epi_ops<EPI>(p, em, own ? om : 0, own ? on : 0, eo);
   // every load above is issued here, in this order: the scheduler may not move any of
   // them below the waits for the rows
   __builtin_amdgcn_sched_barrier(0);
   // 3. activation rows into LDS
-  stage_finish<XPT, PRO>(p, xs, rr, ar, s_aw);
+  if constexpr (PRO == PRO_EMBED) emb_finish<WT, XE>(p, el, xs);
+  else stage_finish<XPT, PRO>(p, xs, rr, ar, s_aw);
   __syncthreads();
+  if constexpr (PRO == PRO_EMBED) {
+    if (blockIdx.x == 0) {   // the residual rows for the rest of the step
+      const int K4 = K >> 2;
+      for (int i = tid; i < M * K4; i += GD_WG) {
+        const int m = i / K4, k = (i - m * K4) << 2;
+        *reinterpret_cast<f32x4*>(p.erp.x + (size_t)m * p.erp.d + k) = *reinterpret_cast<const f32x4*>(xs + m * K + k);
+      }
+    }
+  }
   // 4. dot products. With a pre-norm every row is normalized on the fly: the lanes of a
   //    wave hold the row's whole K range (chunks lane + 64 i), so each wave forms the
   //    row's statistics itself (one-pass moments shifted by the row's first element,
@@ -524,6 +778,9 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
       p.am_idx[(size_t)blockIdx.x * M + tid] = bi;
     }
     return;
+  }
+  if constexpr (PRO == PRO_EMBED) {
+    if (blockIdx.x == 0) emb_publish<EPI>(p, em, eo);
   }
   if (!own) return;
   float v0 = 0.f, v1 = 0.f;
@@ -1110,11 +1367,19 @@ __global__ __launch_bounds__(64 * MM_NW) void k_mm(LinParams p) {
 // Every thread loads all of its partials before comparing, so the reduction costs
 // one memory round trip. nparts <= GD_WG * AM_FIN_PER.
 #define AM_FIN_PER 16
+// With adv_len (a decode step whose set-up ran in its QKV launch) it also advances the
+// row's sequence length: adv_len[adv_seq[m]] = adv_pos[m] + 1.
 __global__ __launch_bounds__(GD_WG) void k_argmax_finalize(const float* __restrict__ val, const int* __restrict__ idx,
-                                                           int nparts, int M, int* out) {
+                                                           int nparts, int M, int* out, const int* __restrict__ adv_seq,
+                                                           const int* __restrict__ adv_pos, int* adv_len) {
   __shared__ float sv[GD_WG / 64];
   __shared__ int si[GD_WG / 64];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int aseq = 0, apos = 0;
+  if (adv_len) {
+    aseq = adv_seq[m];
+    apos = adv_pos[m];
+  }
   float v[AM_FIN_PER];
   int ix[AM_FIN_PER];
 #pragma unroll
@@ -1142,5 +1407,6 @@ __global__ __launch_bounds__(GD_WG) void k_argmax_finalize(const float* __restri
     for (int w = 1; w < GD_WG / 64; ++w)
       if (si[w] != 0x7fffffff && (i0 == 0x7fffffff || am_better(sv[w], si[w], v0, i0))) { v0 = sv[w]; i0 = si[w]; }
     out[m] = i0;
+    if (adv_len) adv_len[aseq] = apos + 1;
   }
 }

@@ -190,6 +190,19 @@ static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipSt
     GD_GEMV(1, EPI_PLAIN, PRO_ATTN, NRM_NONE);
     return hipSuccess;
   }
+  if (prm.pro == PRO_EMBED) {   // the decode step's first QKV launch, its set-up included
+    if (!nrm || lp.rows < prm.M) return hipErrorNotSupported;
+    if (prm.epi == EPI_QKV) {
+      if (fold) GD_GEMV(1, EPI_QKV, PRO_EMBED, NRM_FOLDED);
+      else GD_GEMV(1, EPI_QKV, PRO_EMBED, NRM_EXPLICIT);
+    } else if (prm.epi == EPI_QKV_ROPE) {
+      if (fold) GD_GEMV(2, EPI_QKV_ROPE, PRO_EMBED, NRM_FOLDED);
+      else GD_GEMV(2, EPI_QKV_ROPE, PRO_EMBED, NRM_EXPLICIT);
+    } else {
+      return hipErrorNotSupported;
+    }
+    return hipSuccess;
+  }
   switch (prm.epi) {
     case EPI_PLAIN: if (nrm) GD_GEMV_N(1, EPI_PLAIN); else GD_GEMV(1, EPI_PLAIN, PRO_COPY, NRM_NONE); break;
     case EPI_GELU: if (nrm) GD_GEMV_N(1, EPI_GELU); else GD_GEMV(1, EPI_GELU, PRO_COPY, NRM_NONE); break;
@@ -250,6 +263,7 @@ static hipError_t launch_mm_mt(const LinPlan& lp, const LinParams& prm0, hipStre
     if (fold) GD_MM(EPI, NRM_FOLDED, false);           \
     else GD_MM(EPI, NRM_EXPLICIT, false);              \
   } while (0)
+  if (prm.pro == PRO_EMBED) return hipErrorNotSupported;   // embedding rows: the GEMV only
   if (prm.pro == PRO_ATTN) {   // the output projection behind split-context attention (<= 16 rows)
     if constexpr (MT == 1) {
       if (nrm || prm.epi != EPI_PLAIN || lp.passes > 1 || prm.nch < 1 || prm.nch > GD_ATT_NCH || prm.hd % 32 ||
@@ -318,6 +332,7 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
   for (int r0 = 0; r0 < prm.M; r0 += lp.rows) {
     LinParams p = prm;
     p.M = std::min(lp.rows, prm.M - r0);
+    if (r0 && prm.pro == PRO_EMBED) return hipErrorNotSupported;   // its rows' arrays do not advance
     if (r0) {
       if (p.x) p.x += (size_t)r0 * p.ldx;
       p.resid += (size_t)r0 * p.ldr;
@@ -332,7 +347,8 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
     if (p.epi == EPI_ARGMAX) {
       auto* keep = t_prof_pairs;
       if (t_prof_pairs) t_prof_pairs = t_prof_fin;
-      GD_LAUNCH(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.parts, p.M, am_out + r0);
+      GD_LAUNCH(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.parts, p.M, am_out + r0,
+                p.adv_len ? p.adv_seq + r0 : nullptr, p.adv_len ? p.adv_pos + r0 : nullptr, p.adv_len);
       t_prof_pairs = keep;
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1167,8 +1183,11 @@ static const char* linear_kernel_name(int wt, const LinPlan& lp, int N, int epi,
 // parameter once, the activation rows in, the outputs out (and the residual read).
 static double linear_bytes(const gd_model* m, const LinParams& p) {
   const int n_out = p.epi == EPI_SWIGLU ? p.N / 2 : (p.epi == EPI_ARGMAX ? (p.logits ? p.N : 0) : p.N);
-  // rows in: as given, or the attention partials they are merged from
-  const double rows_in = p.pro == PRO_ATTN ? (double)p.M * p.Hq * p.nch * (p.hd + 2) * 4 : (double)p.M * p.K * 4;
+  // rows in: as given, the attention partials they are merged from, or the embedding
+  // rows they are summed from (stored once as the residual rows)
+  const double rows_in = p.pro == PRO_ATTN    ? (double)p.M * p.Hq * p.nch * (p.hd + 2) * 4
+                         : p.pro == PRO_EMBED ? (double)p.M * p.K * (m->elt * (p.erp.wpe ? 2 : 1) + 4)
+                                              : (double)p.M * p.K * 4;
   double b = (double)p.N * p.K * m->elt + rows_in + (double)p.M * n_out * 4;
   if (m->wt == GD_WEIGHT_Q8) b += (double)p.N * (p.K / 32) * 4;   // block scales
   const float* zero = m->sp<float>(m->o_zero);
@@ -1285,8 +1304,10 @@ static RowParams row_params(gd_model* m, int* rseq, int* rpos, int* rtok, long l
 
 // Final norm + logits (tied embedding or untied head) + the greedy argmax (or the
 // sampled token) of rows [head_row, head_row + head_rows) of the residual rows x.
+// adv_len: the finalize advances the rows' sequence lengths (a decode step whose
+// set-up ran in its first QKV launch).
 static hipError_t enqueue_head(gd_model* m, hipStream_t st, const RowParams& rp, const float* x, int head_row,
-                               int head_rows, int* head_out, float* logits) {
+                               int head_rows, int* head_out, float* logits, int* adv_len = nullptr) {
   const gd_config& c = m->c;
   const int d = c.d_model;
   const bool gpt2 = c.arch == GD_ARCH_GPT2;
@@ -1315,6 +1336,7 @@ static hipError_t enqueue_head(gd_model* m, hipStream_t st, const RowParams& rp,
     p.row_kvoff = rp.row_kvoff + head_row;
     p.rope_cs = nullptr;
     p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
+    if (adv_len) { p.adv_len = adv_len; p.adv_seq = rp.row_seq + head_row; p.adv_pos = rp.row_pos + head_row; }
     // the sampler reads whole logit rows: the caller's, or the scratch rows
     p.logits = logits ? logits : (m->sample ? m->sp<float>(m->o_slog) : nullptr);
     p.ldl = c.vocab;
@@ -1336,8 +1358,15 @@ static hipError_t enqueue_head(gd_model* m, hipStream_t st, const RowParams& rp,
 
 // Enqueues the forward pass of M (<= 32) rows with device-resident row metadata.
 // If head_out is not NULL, computes logits/argmax for rows [head_row, head_row + head_rows).
+// The decode step's set-up folded into its first QKV launch: the rows' sequence slots
+// and tokens, and the sequences' lengths (advanced by the step's argmax finalize) and
+// capacities.
+struct StepEmbed {
+  const int* sids; const int* tok; int* len; const int* cap;
+};
+
 static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp, int M, int max_T, int head_row,
-                               int head_rows, int* head_out, float* logits) {
+                               int head_rows, int* head_out, float* logits, const StepEmbed* se = nullptr) {
   const gd_config& c = m->c;
   const int d = c.d_model, ff = c.d_ff;
   float* x = m->sp<float>(m->o_x);
@@ -1410,6 +1439,13 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.rope_cs = rp.row_cs;
       p.kc = m->kpool(l); p.vc = m->vpool(l); p.kv16 = m->kv16;
       p.kv_hstride = m->bsize * c.head_dim;
+      if (l == 0 && se) {
+        // the rows are the step's input embeddings, formed by this launch
+        p.pro = PRO_EMBED;
+        p.x = nullptr;
+        p.erp = rp;
+        p.e_sids = se->sids; p.e_tok = se->tok; p.e_len = se->len; p.e_cap = se->cap;
+      }
       if ((e = run_linear(m, st, "linear.qkv", p)) != hipSuccess) return e;
     }
     AttnParams a;
@@ -1525,7 +1561,7 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       if ((e = run_linear(m, st, "linear.down", p)) != hipSuccess) return e;
     }
   }
-  if (head_out) return enqueue_head(m, st, rp, x, head_row, head_rows, head_out, logits);
+  if (head_out) return enqueue_head(m, st, rp, x, head_row, head_rows, head_out, logits, se ? se->len : nullptr);
   return hipSuccess;
 }
 
@@ -1818,14 +1854,20 @@ static hipError_t enqueue_decode(gd_model* m, hipStream_t st, int B, int max_T, 
   RowParams rp = row_params(m, m->sp<int>(m->o_rseq), m->sp<int>(m->o_rpos), m->sp<int>(m->o_rtok),
                             m->sp<long long>(m->o_rkv),
                             m->c.arch == GD_ARCH_LLAMA ? m->sp<float>(m->o_rcs) : nullptr);
-  {
-    ProfScope ps(m, st, "setup", "k_setup_decode", (double)B * m->c.d_model * (m->elt * 2 + 4));
-    GD_LAUNCH(k_setup_decode, dim3(B), dim3(GD_WG), 0, st, rp, m->sp<int>(m->o_sids), tok,
-                       m->sp<int>(m->o_len), m->sp<int>(m->o_cap));
+  // With a GEMV QKV launch (<= 4 rows) the set-up runs inside it (one launch fewer);
+  // the matrix-core one stages its rows from the set-up launch's output.
+  const gd_config& c = m->c;
+  const int qkv_epi = c.arch == GD_ARCH_GPT2 ? EPI_QKV : EPI_QKV_ROPE;
+  const StepEmbed se{m->sp<int>(m->o_sids), tok, m->sp<int>(m->o_len), m->sp<int>(m->o_cap)};
+  const LinPlan qp = plan_linear(B, m->qkvdim, c.d_model, m->wt, m->variant, qkv_epi, true);
+  const bool embed = next != nullptr && qp.var == 0 && qp.rows >= B;   // one launch over all rows
+  if (!embed) {
+    ProfScope ps(m, st, "setup", "k_setup_decode", (double)B * c.d_model * (m->elt * 2 + 4));
+    GD_LAUNCH(k_setup_decode, dim3(B), dim3(GD_WG), 0, st, rp, se.sids, tok, se.len, se.cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return enqueue_rows(m, st, rp, B, max_T, 0, B, next, logits);
+  return enqueue_rows(m, st, rp, B, max_T, 0, B, next, logits, embed ? &se : nullptr);
 }
 
 extern "C" gd_status gd_decode_step(gd_model* m, int32_t B, const int32_t* sids, const int32_t* tok_dev,
