@@ -87,15 +87,24 @@ struct LinParams {
   const float* rope_cs;                     // [M][hd]: each row's cos | sin of pair i (NULL: no RoPE)
   void* kc; void* vc;                       // K / V pools of the layer: float, or bf16 bits if kv16
   int kv16;
-  // ---- EMBED: row b < M is token e_tok[b] of sequence slot e_sids[b] at that
-  // sequence's length e_len[.], as k_setup_decode takes it; erp addresses the tables,
-  // the cache's block table and the rows' metadata that workgroup 0 stores
-  RowParams erp;
-  const int* e_sids; const int* e_tok; const int* e_len; const int* e_cap;
-  // ---- host side: the argmax finalize behind this launch advances len[adv_seq[b]] to
-  // adv_pos[b] + 1 (NULL: it does not)
-  int* adv_len; const int* adv_seq; const int* adv_pos;
 };
+
+// The embedding prologue's sources (PRO_EMBED): row b < M is token tok[b] of sequence
+// slot sids[b] at that sequence's length len[.], as k_setup_decode takes it; erp
+// addresses the tables, the cache's block table and the rows' metadata that workgroup
+// 0 stores. A kernel argument type of its own, so that every other launch keeps the
+// smaller argument block of LinParams.
+struct EmbSrc {
+  RowParams erp;
+  const int* sids; const int* tok; const int* len; const int* cap;
+};
+struct LinEmbParams : LinParams {
+  EmbSrc e;
+};
+template <int PRO>
+struct GemvArgs { typedef LinParams T; };
+template <>
+struct GemvArgs<PRO_EMBED> { typedef LinEmbParams T; };
 
 // ------------------------------------------------------------ shared pieces
 
@@ -265,18 +274,18 @@ __device__ __forceinline__ int sel_row(int m, const int (&v)[GEMV_MAX_ROWS]) {
 // Issued before the weights (vector loads complete in issue order, so waiting for
 // these does not wait for the weight stream): lane m loads row m's sequence slot and
 // token.
-__device__ __forceinline__ void emb_meta_issue(const LinParams& p, EmbMeta& em) {
+__device__ __forceinline__ void emb_meta_issue(const LinEmbParams& p, EmbMeta& em) {
   const int lm = min((int)(threadIdx.x & 63), p.M - 1);
-  em.vseq = p.e_sids[lm];
-  em.vtok = p.e_tok[lm];
+  em.vseq = p.e.sids[lm];
+  em.vtok = p.e.tok[lm];
 }
 
 // After the weights: the tokens (an out-of-range one is replaced by 0) ...
-__device__ __forceinline__ void emb_meta_tokens(const LinParams& p, EmbMeta& em) {
+__device__ __forceinline__ void emb_meta_tokens(const LinEmbParams& p, EmbMeta& em) {
 #pragma unroll
   for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
     const int tok = __builtin_amdgcn_readlane(em.vtok, m);
-    const bool ok = tok >= 0 && tok < p.erp.vocab;
+    const bool ok = tok >= 0 && tok < p.e.erp.vocab;
     em.tok[m] = ok ? tok : 0;
     em.flags[m] = ok ? 0 : GD_DERR_TOKEN;
     em.seq[m] = __builtin_amdgcn_readlane(em.vseq, m);
@@ -285,13 +294,13 @@ __device__ __forceinline__ void emb_meta_tokens(const LinParams& p, EmbMeta& em)
 
 // ... then the sequences' lengths and capacities (scalar loads), clamped as
 // k_setup_decode does.
-__device__ __forceinline__ void emb_meta_finish(const LinParams& p, EmbMeta& em) {
-  const RowParams& r = p.erp;
+__device__ __forceinline__ void emb_meta_finish(const LinEmbParams& p, EmbMeta& em) {
+  const RowParams& r = p.e.erp;
   int len[GEMV_MAX_ROWS], cap[GEMV_MAX_ROWS];
 #pragma unroll
   for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
-    len[m] = p.e_len[em.seq[m]];
-    cap[m] = p.e_cap[em.seq[m]];
+    len[m] = p.e.len[em.seq[m]];
+    cap[m] = p.e.cap[em.seq[m]];
   }
 #pragma unroll
   for (int m = 0; m < GEMV_MAX_ROWS; ++m) {
@@ -325,10 +334,10 @@ struct EmbLoad {
 
 // Chunk (m, k) of wte[t] (needs the tokens only) ...
 template <int WT>
-__device__ __forceinline__ void emb_load_te(const LinParams& p, const EmbMeta& em, int m, int k, EmbLoad<WT>& l) {
+__device__ __forceinline__ void emb_load_te(const LinEmbParams& p, const EmbMeta& em, int m, int k, EmbLoad<WT>& l) {
   typedef typename EmbChunk<WT>::T ET;
   constexpr int ES = WT == 0 ? 4 : WT == 1 ? 2 : 1;
-  const RowParams& r = p.erp;
+  const RowParams& r = p.e.erp;
   const size_t et = (size_t)sel_row(m, em.tok) * r.d + k;
   l.a = *reinterpret_cast<const ET*>(reinterpret_cast<const char*>(r.wte) + et * ES);
   l.sa = 1.f;
@@ -337,10 +346,10 @@ __device__ __forceinline__ void emb_load_te(const LinParams& p, const EmbMeta& e
 
 // ... and of wpe[p] (the positions).
 template <int WT>
-__device__ __forceinline__ void emb_load_pe(const LinParams& p, const EmbMeta& em, int m, int k, EmbLoad<WT>& l) {
+__device__ __forceinline__ void emb_load_pe(const LinEmbParams& p, const EmbMeta& em, int m, int k, EmbLoad<WT>& l) {
   typedef typename EmbChunk<WT>::T ET;
   constexpr int ES = WT == 0 ? 4 : WT == 1 ? 2 : 1;
-  const RowParams& r = p.erp;
+  const RowParams& r = p.e.erp;
   const size_t ep = (size_t)sel_row(m, em.ppos) * r.d + k;
   l.b = *reinterpret_cast<const ET*>(reinterpret_cast<const char*>(r.wpe) + ep * ES);
   l.sb = 1.f;
@@ -370,7 +379,7 @@ __device__ __forceinline__ f32x4 emb_value(const EmbLoad<WT>& l, bool pe) {
 // This thread's chunks of all rows: chunk j is i = tid + GD_WG j of the M K / 4; XE
 // covers GEMV_MAX_ROWS rows, and the chunks past the M rows are not loaded.
 template <int WT, int XE>
-__device__ __forceinline__ void emb_issue_te(const LinParams& p, const EmbMeta& em, EmbLoad<WT> (&el)[XE]) {
+__device__ __forceinline__ void emb_issue_te(const LinEmbParams& p, const EmbMeta& em, EmbLoad<WT> (&el)[XE]) {
   const int tid = threadIdx.x, K4 = p.K >> 2, MK4 = p.M * K4;
 #pragma unroll
   for (int j = 0; j < XE; ++j) {
@@ -383,7 +392,7 @@ __device__ __forceinline__ void emb_issue_te(const LinParams& p, const EmbMeta& 
 }
 
 template <int WT, int XE>
-__device__ __forceinline__ void emb_issue_pe(const LinParams& p, const EmbMeta& em, EmbLoad<WT> (&el)[XE]) {
+__device__ __forceinline__ void emb_issue_pe(const LinEmbParams& p, const EmbMeta& em, EmbLoad<WT> (&el)[XE]) {
   const int tid = threadIdx.x, K4 = p.K >> 2, MK4 = p.M * K4;
 #pragma unroll
   for (int j = 0; j < XE; ++j) {
@@ -397,9 +406,9 @@ __device__ __forceinline__ void emb_issue_pe(const LinParams& p, const EmbMeta& 
 
 // The rows into LDS xs[m * K + k].
 template <int WT, int XE>
-__device__ __forceinline__ void emb_finish(const LinParams& p, const EmbLoad<WT> (&el)[XE], float* xs) {
+__device__ __forceinline__ void emb_finish(const LinEmbParams& p, const EmbLoad<WT> (&el)[XE], float* xs) {
   const int tid = threadIdx.x, K = p.K, K4 = K >> 2, MK4 = p.M * K4;
-  const bool pe = p.erp.wpe != nullptr;
+  const bool pe = p.e.erp.wpe != nullptr;
 #pragma unroll
   for (int j = 0; j < XE; ++j) {
     const int i = tid + GD_WG * j;
@@ -420,8 +429,8 @@ __device__ __forceinline__ long long emb_kvoff(const RowParams& r, int seq, int 
 
 // The QKV epilogue's row metadata of output (m, n) from the embedding prologue.
 template <int EPI>
-__device__ __forceinline__ void emb_epi_ops(const LinParams& p, const EmbMeta& em, int m, int n, EpiOps& e) {
-  const RowParams& r = p.erp;
+__device__ __forceinline__ void emb_epi_ops(const LinEmbParams& p, const EmbMeta& em, int m, int n, EpiOps& e) {
+  const RowParams& r = p.e.erp;
   const int pos = sel_row(m, em.pos);
   e.kvoff = emb_kvoff(r, sel_row(m, em.seq), pos);
   if constexpr (EPI == EPI_QKV_ROPE) {
@@ -435,8 +444,8 @@ __device__ __forceinline__ void emb_epi_ops(const LinParams& p, const EmbMeta& e
 // Workgroup 0: the rows' metadata (lane m < M of wave 0, which owns row m's output and
 // holds its slot in e), error flags and RoPE rows, as k_setup_decode leaves them.
 template <int EPI>
-__device__ __forceinline__ void emb_publish(const LinParams& p, const EmbMeta& em, const EpiOps& e) {
-  const RowParams& r = p.erp;
+__device__ __forceinline__ void emb_publish(const LinEmbParams& p, const EmbMeta& em, const EpiOps& e) {
+  const RowParams& r = p.e.erp;
   const int tid = threadIdx.x;
   if (tid < p.M) {
     r.row_seq[tid] = sel_row(tid, em.seq);
@@ -491,7 +500,7 @@ __device__ __forceinline__ float q8_chunk_dot(const u32x4& w, const f32x4* a, fl
 // statistics, and the result is r (d . w_n - a s_n) + bias_n with a = mean(d) (this
 // equals r (x - mu) . w_n) and r = 1 / sqrt(var + eps). RMSNorm: no shift, a = 0.
 template <int WT, int NC, int RW, int EPI, int PRO, int NRM>
-__global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
+__global__ __launch_bounds__(GD_WG) void k_gemv(typename GemvArgs<PRO>::T p) {
   typedef typename WChunk<WT>::T VT;
   constexpr int CE = WChunk<WT>::CE;
   extern __shared__ __align__(16) float xs[];   // [M][K] rows
@@ -562,7 +571,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
     emb_meta_tokens(p, em);
     emb_issue_te<WT, XE>(p, em, el);
     emb_meta_finish(p, em);
-    if (p.erp.wpe) emb_issue_pe<WT, XE>(p, em, el);
+    if (p.e.erp.wpe) emb_issue_pe<WT, XE>(p, em, el);
   }
   // 2. epilogue operands of this lane's output (lane m * RW + r), or pair (lane m)
   constexpr bool PAIR = EpiTraits<EPI>::pair;
@@ -589,7 +598,7 @@ __global__ __launch_bounds__(GD_WG) void k_gemv(LinParams p) {
       const int K4 = K >> 2;
       for (int i = tid; i < M * K4; i += GD_WG) {
         const int m = i / K4, k = (i - m * K4) << 2;
-        *reinterpret_cast<f32x4*>(p.erp.x + (size_t)m * p.erp.d + k) = *reinterpret_cast<const f32x4*>(xs + m * K + k);
+        *reinterpret_cast<f32x4*>(p.e.erp.x + (size_t)m * p.e.erp.d + k) = *reinterpret_cast<const f32x4*>(xs + m * K + k);
       }
     }
   }

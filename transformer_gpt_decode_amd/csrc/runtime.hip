@@ -168,9 +168,10 @@ static LinPlan plan_linear(int M, int N, int K, int wt, int variant, int epi, bo
 }
 
 // With a pre-norm whose folded form is given (fp32 weights, prm.wf), the folded
-// weights, bias and row sums replace the layer's own (NRM_FOLDED).
+// weights, bias and row sums replace the layer's own (NRM_FOLDED). es: the embedding
+// prologue's sources (prm.pro == PRO_EMBED).
 template <int WT, int NC>
-static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipStream_t st) {
+static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipStream_t st, const EmbSrc* es) {
   const dim3 g(lp.grid), b(GD_WG);
   const bool nrm = prm0.norm != NORM_NONE;
   const bool fold = WT == 0 && nrm && prm0.wf;
@@ -191,16 +192,21 @@ static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipSt
     return hipSuccess;
   }
   if (prm.pro == PRO_EMBED) {   // the decode step's first QKV launch, its set-up included
-    if (!nrm || lp.rows < prm.M) return hipErrorNotSupported;
+    if (!nrm || !es || lp.rows < prm.M) return hipErrorNotSupported;
+    LinEmbParams eprm;
+    static_cast<LinParams&>(eprm) = prm;
+    eprm.e = *es;
+#define GD_GEMV_E(RW, EPI, NRM) GD_LAUNCH((k_gemv<WT, NC, RW, EPI, PRO_EMBED, NRM>), g, b, lp.lds, st, eprm)
     if (prm.epi == EPI_QKV) {
-      if (fold) GD_GEMV(1, EPI_QKV, PRO_EMBED, NRM_FOLDED);
-      else GD_GEMV(1, EPI_QKV, PRO_EMBED, NRM_EXPLICIT);
+      if (fold) GD_GEMV_E(1, EPI_QKV, NRM_FOLDED);
+      else GD_GEMV_E(1, EPI_QKV, NRM_EXPLICIT);
     } else if (prm.epi == EPI_QKV_ROPE) {
-      if (fold) GD_GEMV(2, EPI_QKV_ROPE, PRO_EMBED, NRM_FOLDED);
-      else GD_GEMV(2, EPI_QKV_ROPE, PRO_EMBED, NRM_EXPLICIT);
+      if (fold) GD_GEMV_E(2, EPI_QKV_ROPE, NRM_FOLDED);
+      else GD_GEMV_E(2, EPI_QKV_ROPE, NRM_EXPLICIT);
     } else {
       return hipErrorNotSupported;
     }
+#undef GD_GEMV_E
     return hipSuccess;
   }
   switch (prm.epi) {
@@ -222,15 +228,15 @@ static hipError_t launch_gemv_nc(const LinPlan& lp, const LinParams& prm0, hipSt
 }
 
 template <int WT>
-static hipError_t launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+static hipError_t launch_gemv(const LinPlan& lp, const LinParams& prm, hipStream_t st, const EmbSrc* es) {
   switch (lp.nc) {
-    case 1: return launch_gemv_nc<WT, 1>(lp, prm, st);
-    case 2: return launch_gemv_nc<WT, 2>(lp, prm, st);
-    case 3: return launch_gemv_nc<WT, 3>(lp, prm, st);
-    case 4: return launch_gemv_nc<WT, 4>(lp, prm, st);
-    case 6: return launch_gemv_nc<WT, 6>(lp, prm, st);
-    case 8: return launch_gemv_nc<WT, 8>(lp, prm, st);
-    default: return launch_gemv_nc<WT, 12>(lp, prm, st);
+    case 1: return launch_gemv_nc<WT, 1>(lp, prm, st, es);
+    case 2: return launch_gemv_nc<WT, 2>(lp, prm, st, es);
+    case 3: return launch_gemv_nc<WT, 3>(lp, prm, st, es);
+    case 4: return launch_gemv_nc<WT, 4>(lp, prm, st, es);
+    case 6: return launch_gemv_nc<WT, 6>(lp, prm, st, es);
+    case 8: return launch_gemv_nc<WT, 8>(lp, prm, st, es);
+    default: return launch_gemv_nc<WT, 12>(lp, prm, st, es);
   }
 }
 
@@ -312,11 +318,11 @@ static hipError_t launch_mm(const LinPlan& lp, const LinParams& prm, hipStream_t
 }
 
 // One launch of one plan over prm.M rows (prm.M <= lp.rows).
-static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st) {
+static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st, const EmbSrc* es) {
   if (lp.var == 0) {
-    const hipError_t e = wt == GD_WEIGHT_F32    ? launch_gemv<0>(lp, prm, st)
-                         : wt == GD_WEIGHT_BF16 ? launch_gemv<1>(lp, prm, st)
-                                                : launch_gemv<2>(lp, prm, st);
+    const hipError_t e = wt == GD_WEIGHT_F32    ? launch_gemv<0>(lp, prm, st, es)
+                         : wt == GD_WEIGHT_BF16 ? launch_gemv<1>(lp, prm, st, es)
+                                                : launch_gemv<2>(lp, prm, st, es);
     if (e != hipSuccess) return e;
   } else {
     const hipError_t e = wt == GD_WEIGHT_F32 ? launch_mm<0>(lp, prm, st) : launch_mm<1>(lp, prm, st);
@@ -325,10 +331,17 @@ static hipError_t launch_linear(int wt, const LinPlan& lp, const LinParams& prm,
   return hipGetLastError();
 }
 
+// A decode step whose set-up ran in its first QKV launch: the head's argmax finalize
+// advances len[seq[b]] to pos[b] + 1 for its rows b.
+struct AdvLen {
+  int* len; const int* seq; const int* pos;
+};
+
 // Runs a linear layer over prm.M rows, as several launches of at most lp.rows rows when
 // needed (every per-row pointer advances with the row group). With EPI_ARGMAX each
 // group's per-workgroup partials are reduced into am_out[rows of the group].
-static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st, int* am_out) {
+static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& prm, hipStream_t st, int* am_out,
+                                  const EmbSrc* es, const AdvLen* adv) {
   for (int r0 = 0; r0 < prm.M; r0 += lp.rows) {
     LinParams p = prm;
     p.M = std::min(lp.rows, prm.M - r0);
@@ -342,13 +355,13 @@ static hipError_t run_linear_rows(int wt, const LinPlan& lp, const LinParams& pr
       if (p.rope_cs) p.rope_cs += (size_t)r0 * p.hd;
       if (p.apart) p.apart += (size_t)r0 * p.Hq * p.nch * gd_apart_stride(p.hd);
     }
-    hipError_t e = launch_linear(wt, lp, p, st);
+    hipError_t e = launch_linear(wt, lp, p, st, es);
     if (e != hipSuccess) return e;
     if (p.epi == EPI_ARGMAX) {
       auto* keep = t_prof_pairs;
       if (t_prof_pairs) t_prof_pairs = t_prof_fin;
       GD_LAUNCH(k_argmax_finalize, dim3(p.M), dim3(GD_WG), 0, st, p.am_val, p.am_idx, lp.parts, p.M, am_out + r0,
-                p.adv_len ? p.adv_seq + r0 : nullptr, p.adv_len ? p.adv_pos + r0 : nullptr, p.adv_len);
+                adv ? adv->seq + r0 : nullptr, adv ? adv->pos + r0 : nullptr, adv ? adv->len : nullptr);
       t_prof_pairs = keep;
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1186,7 +1199,7 @@ static double linear_bytes(const gd_model* m, const LinParams& p) {
   // rows in: as given, the attention partials they are merged from, or the embedding
   // rows they are summed from (stored once as the residual rows)
   const double rows_in = p.pro == PRO_ATTN    ? (double)p.M * p.Hq * p.nch * (p.hd + 2) * 4
-                         : p.pro == PRO_EMBED ? (double)p.M * p.K * (m->elt * (p.erp.wpe ? 2 : 1) + 4)
+                         : p.pro == PRO_EMBED ? (double)p.M * p.K * (m->elt * (m->c.arch == GD_ARCH_GPT2 ? 2 : 1) + 4)
                                               : (double)p.M * p.K * 4;
   double b = (double)p.N * p.K * m->elt + rows_in + (double)p.M * n_out * 4;
   if (m->wt == GD_WEIGHT_Q8) b += (double)p.N * (p.K / 32) * 4;   // block scales
@@ -1197,9 +1210,10 @@ static double linear_bytes(const gd_model* m, const LinParams& p) {
   return b;
 }
 
-// Launches one linear layer (profiled when enabled).
+// Launches one linear layer (profiled when enabled). es: the embedding prologue's
+// sources (p.pro == PRO_EMBED); adv: the lengths the argmax finalize advances.
 static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, const LinParams& p,
-                             int* am_out = nullptr) {
+                             int* am_out = nullptr, const EmbSrc* es = nullptr, const AdvLen* adv = nullptr) {
   const bool inplace = p.resid == p.y && p.ldr == p.ldy;
   LinPlan lp = plan_linear(p.M, p.N, p.K, m->wt, m->variant, p.epi, p.norm != NORM_NONE, inplace, p.pro == PRO_ATTN);
   char kn[64];
@@ -1210,7 +1224,7 @@ static hipError_t run_linear(gd_model* m, hipStream_t st, const char* role, cons
                  linear_kernel_name(m->wt, lp, p.N, p.epi, p.norm != NORM_NONE, p.wf != nullptr, p.pro, kn, sizeof(kn)),
                  m->profile ? linear_bytes(m, p) : 0);
     t_prof_fin = &fin;
-    e = run_linear_rows(m->wt, lp, p, st, am_out);
+    e = run_linear_rows(m->wt, lp, p, st, am_out, es, adv);
     t_prof_fin = nullptr;
   }
   if (m->profile && !fin.empty())
@@ -1336,11 +1350,11 @@ static hipError_t enqueue_head(gd_model* m, hipStream_t st, const RowParams& rp,
     p.row_kvoff = rp.row_kvoff + head_row;
     p.rope_cs = nullptr;
     p.am_val = m->sp<float>(m->o_amv); p.am_idx = m->sp<int>(m->o_ami);
-    if (adv_len) { p.adv_len = adv_len; p.adv_seq = rp.row_seq + head_row; p.adv_pos = rp.row_pos + head_row; }
     // the sampler reads whole logit rows: the caller's, or the scratch rows
     p.logits = logits ? logits : (m->sample ? m->sp<float>(m->o_slog) : nullptr);
     p.ldl = c.vocab;
-    if ((e = run_linear(m, st, "linear.head", p, head_out)) != hipSuccess) return e;
+    const AdvLen adv{adv_len, rp.row_seq + head_row, rp.row_pos + head_row};
+    if ((e = run_linear(m, st, "linear.head", p, head_out, nullptr, adv_len ? &adv : nullptr)) != hipSuccess) return e;
     if (m->sample) {
       // temperature / top-k draw over each head row (replaces the greedy token)
       SampleParams sp;
@@ -1439,14 +1453,14 @@ static hipError_t enqueue_rows(gd_model* m, hipStream_t st, const RowParams& rp,
       p.rope_cs = rp.row_cs;
       p.kc = m->kpool(l); p.vc = m->vpool(l); p.kv16 = m->kv16;
       p.kv_hstride = m->bsize * c.head_dim;
+      EmbSrc es;
       if (l == 0 && se) {
         // the rows are the step's input embeddings, formed by this launch
         p.pro = PRO_EMBED;
         p.x = nullptr;
-        p.erp = rp;
-        p.e_sids = se->sids; p.e_tok = se->tok; p.e_len = se->len; p.e_cap = se->cap;
+        es = EmbSrc{rp, se->sids, se->tok, se->len, se->cap};
       }
-      if ((e = run_linear(m, st, "linear.qkv", p)) != hipSuccess) return e;
+      if ((e = run_linear(m, st, "linear.qkv", p, nullptr, p.pro == PRO_EMBED ? &es : nullptr)) != hipSuccess) return e;
     }
     AttnParams a;
     memset(&a, 0, sizeof(a));
@@ -2014,7 +2028,7 @@ extern "C" gd_status gd_linear(const float* x, int32_t ldx, const void* W, int32
     if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
     p.wtl = packed;
   }
-  e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr);
+  e = run_linear_rows(wdt, lp, p, reinterpret_cast<hipStream_t>(stream), nullptr, nullptr, nullptr);
   if (e != hipSuccess) return set_err(GD_ERR_HIP, "linear launch failed: %s", hipGetErrorString(e));
   return GD_OK;
 }
