@@ -1384,11 +1384,6 @@ __global__ __launch_bounds__(GD_WG) void k_argmax_finalize(const float* __restri
   __shared__ float sv[GD_WG / 64];
   __shared__ int si[GD_WG / 64];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int aseq = 0, apos = 0;
-  if (adv_len) {
-    aseq = adv_seq[m];
-    apos = adv_pos[m];
-  }
   float v[AM_FIN_PER];
   int ix[AM_FIN_PER];
 #pragma unroll
@@ -1396,6 +1391,14 @@ __global__ __launch_bounds__(GD_WG) void k_argmax_finalize(const float* __restri
     const int q = tid + GD_WG * j;
     v[j] = q < nparts ? val[(size_t)q * M + m] : 0.f;
     ix[j] = q < nparts ? idx[(size_t)q * M + m] : 0x7fffffff;
+  }
+  // the row's slot and position after the partials are issued (a wait for them then
+  // does not hold the partials back)
+  __builtin_amdgcn_sched_barrier(0);
+  int aseq = 0, apos = 0;
+  if (adv_len) {
+    aseq = adv_seq[m];
+    apos = adv_pos[m];
   }
   float bv = v[0];
   int bi = ix[0];
