@@ -308,6 +308,50 @@ def test_gpt2_124m_batched_short(wdt):
     _run_and_compare(w, W, prompts, 1e-3 if wdt == "f32" else 2e-2)
 
 
+def test_out_of_range_tokens_on_both_set_up_paths():
+    """A token id outside the vocabulary fed on the device is flagged and replaced by 0,
+    both where the step's set-up runs inside the QKV launch (2 rows) and where it runs
+    as a launch of its own (6 rows); the other rows of the step are unaffected and the
+    next steps run normally."""
+    import torch
+    dev = device()
+    w = dataclasses.replace(synth.WORKLOADS["tiny"], batch=6, prompt_len=(3, 12), n_generate=4)
+    W = synth.make_weights(w.shape, w.init, w.seed)
+    prompts = synth.make_prompts(w)
+    V = w.shape.vocab
+    om = oracle.Model(w.shape, W)
+    m = gd_model(w, W)
+    tok = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    ref_next = []
+    for b, p in enumerate(prompts):
+        m.reset_seq(b)
+        m.prefill(b, p, tok[b:b + 1])
+        s = om.new_seq(len(p) + 4)
+        ref = np.empty(V, np.float32)
+        for t in p:
+            s.forward(int(t), ref)
+        ref_next.append((s, ref))
+    torch.cuda.synchronize()
+    assert m.device_errors() == 0
+    for rows, bad in (([1, 4], 1), ([0, 1, 2, 3, 4, 5], 3)):
+        feed = torch.tensor([int(tok[b]) for b in rows], dtype=torch.int32, device=dev)
+        feed[bad] = V + 5 if len(rows) == 2 else -3
+        out = torch.zeros(len(rows), dtype=torch.int32, device=dev)
+        lg = torch.empty((len(rows), V), dtype=torch.float32, device=dev)
+        m.decode_step(rows, feed, out, lg)
+        torch.cuda.synchronize()
+        assert m.device_errors() & 1, rows
+        assert m.device_errors() == 0
+        for k, b in enumerate(rows):
+            s, ref = ref_next[b]
+            fed = 0 if k == bad else int(feed[k])      # the replaced id
+            nxt = s.forward(fed, ref)
+            assert np.max(np.abs(lg[k].cpu().numpy() - ref)) <= 1e-3, (rows, b)
+            assert int(out[k]) == nxt
+            tok[b] = out[k]
+    m.close()
+
+
 def test_context_edges_and_errors():
     """Position n_ctx-1 runs; one more is refused on the host; bad ids are rejected."""
     import torch
