@@ -14,7 +14,9 @@
 // k_gemv (1..4 rows, VALU): each wave owns RW weight rows; lane l holds chunks
 //   c = l + 64 i (16 bytes each: 4 fp32 or 8 bf16 weights) of each row in registers,
 //   loaded first. Meanwhile the workgroup stages the activation rows in LDS through a
-//   prologue (a copy, or the merge of split-context attention partials). A pre-norm
+//   prologue (a copy, the merge of split-context attention partials, or, in the first
+//   QKV launch of a decode step, the rows' input embeddings formed from the step's
+//   tokens and positions, so that the step needs no set-up launch). A pre-norm
 //   (LayerNorm or RMSNorm) is taken per wave in registers, either applied to the row
 //   (gain and shift loaded) or folded into the weights (see NRM_FOLDED). Dot products
 //   are reduced across the wave.

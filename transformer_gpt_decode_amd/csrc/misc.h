@@ -57,6 +57,9 @@ __device__ void row_setup(const RowParams& r, int b, int seq, int pos, int tok) 
 
 // Decode step set-up, on the device so the step replays as one graph: row b runs
 // slot seq_ids[b] at its current length, which is then advanced. One workgroup per row.
+// Steps whose first QKV launch is a GEMV (at most 4 rows) do the same inside that
+// launch instead (PRO_EMBED in linear.h), and their argmax finalize advances the
+// lengths.
 __global__ __launch_bounds__(GD_WG) void k_setup_decode(RowParams r, const int* __restrict__ seq_ids,
                                                         const int* __restrict__ tokens, int* len,
                                                         const int* __restrict__ cap) {
