@@ -122,9 +122,10 @@ def token_checksum(tokens: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(tokens, dtype=np.int32).tobytes()).hexdigest()[:16]
 
 
-# A greedy token may flip only at a step whose oracle top-2 margin is below this, the
-# known near ties (every such step of the full-size workloads is listed in the design doc),
-# and at most twice the largest logit difference seen so far in the sequence. With a
+# A greedy token may flip only at a step whose oracle top-2 margin is below this (the
+# known near ties: the full-size goldens hold a handful of such steps, each computable
+# from its stored logits) and at most twice the largest logit difference seen so far in
+# the sequence. With a
 # float KV cache the GPU logits differ from the oracle's by under 1e-5 (fp32 sums in
 # another order); with a bf16 cache, K/V values that fall on either side of a bf16
 # rounding boundary on the two sides move logits by up to ~5e-4, hence the wider bound.

@@ -11,8 +11,8 @@ Two oracle sources, both CPU-only (oracle/ + synth/), neither touched by the GPU
     32, 2 of C5's 8).
 
 Bar: identical greedy tokens running free (a flip passes only at a known near tie:
-oracle top-2 margin below gpu_util.near_tie_margin of the workload, every such step
-listed in the design doc, and at most twice the largest logit difference seen so far); fed the
+oracle top-2 margin below gpu_util.near_tie_margin of the workload, a handful of steps
+per golden, and at most twice the largest logit difference seen so far); fed the
 oracle's tokens (teacher forcing), every compared logit within 1e-3 (fp32 weights) or
 2e-2 (bf16 weights) at every step, and the argmax equal to the oracle's token except at
 known near ties. The decode steps run as hipGraph replays, as in bench.py.
